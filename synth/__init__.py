@@ -1,0 +1,9 @@
+"""Seeded synthetic inputs shared by the oracle tests and the HIP path.
+
+This package only draws random numbers and describes workload shapes; it holds
+none of the backward pass's arithmetic.  Both sides of every parity test take
+their inputs from here (directly, or after the oracle's float64 forward turns
+the draws into consistent saved activations).
+"""
+from .configs import CONFIGS, LayerConfig, get_config  # noqa: F401
+from .gen import draw_layer, draw_timing_layer, stream, TENSOR_IDS  # noqa: F401

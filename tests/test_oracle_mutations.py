@@ -1,0 +1,148 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+the pins catch every one: a dropped term, a wrong sign, a wrong index, a
+transposed operand, a wrong constant.
+
+Each mutation rewrites one expression of oracle/backward.py, loads the result
+as a throw-away module, and runs the pin checks against it; at least one check
+must fail.
+"""
+import os
+import types
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import forward as F
+from oracle import fd
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "backward.py")
+
+MUTATIONS = [
+    # (old, new) - each old string must occur in oracle/backward.py
+    ("return (g - x * dot / (n * r * r)) / r", "return g / r"),                      # dropped term
+    ("return (g - x * dot / (n * r * r)) / r", "return (g - x * dot / (n * r)) / r"),  # wrong power
+    ("dx[..., half:] = -lo * s + hi * c", "dx[..., half:] = lo * s + hi * c"),      # sign
+    ("dx[..., :half] = lo * c + hi * s", "dx[..., :half] = lo * c - hi * s"),       # forward rotation
+    ("inv_freq = np.power(float(base), -2.0 * d / head_dim)",
+     "inv_freq = np.power(float(base), -1.0 * d / head_dim)"),                      # constant
+    ("return dh * up * 2.0 * r, dh * r * r", "return dh * up * r, dh * r * r"),     # factor 2
+    ("dsilu = sig * (1.0 + gate - silu)", "dsilu = sig * (1.0 - silu)"),            # dropped term
+    ("return P * (dA - delta)", "return P * dA"),                                    # no delta
+    ("g = h // grp", "g = h % n_kv_heads"),                                          # GQA map
+    ("dQ[:, h * D:(h + 1) * D] = scale * (dS @ Kg)", "dQ[:, h * D:(h + 1) * D] = dS @ Kg"),
+    ("dV[:, g * D:(g + 1) * D] += P[h].T @ dC", "dV[:, g * D:(g + 1) * D] += P[h] @ dC"),
+    ("g = s * (dy @ B)", "g = dy @ B"),                                              # dropped scaling
+    ("dB = s * (dy.T @ h)", "dB = s * (h.T @ dy).T * 0 + s * (dy.T @ h) / 2"),       # halved
+    ("v = beta2 * v + (1.0 - beta2) * g * g", "v = beta2 * v + (1.0 - beta2) * g"),
+    ("p = p - lr * ((m * bc1) / (np.sqrt(v * bc2) + eps) + wd * p)",
+     "p = p - lr * ((m * bc1) / (np.sqrt(v * bc2) + eps)) - wd * p"),               # decay not scaled by lr
+    ("dh1 = d_out + rmsnorm_bwd(resid1, gamma_ffn, dn2, eps)",
+     "dh1 = rmsnorm_bwd(resid1, gamma_ffn, dn2, eps)"),                              # dropped residual
+    ("dn2 = dgate @ np.asarray(W_gate, np.float64) + dup @ np.asarray(W_up, np.float64)",
+     "dn2 = dgate @ np.asarray(W_up, np.float64) + dup @ np.asarray(W_gate, np.float64)"),
+    ("dq_pre = rope_bwd(dq, cfg.n_heads, cfg.head_dim, cfg.pos0 + np.arange(rows),",
+     "dq_pre = rope_bwd(dq, cfg.n_heads, cfg.head_dim, np.arange(rows),"),           # positions
+    ('res["gnorm_sq"] += float(np.sum(dA * dA))',
+     'res["gnorm_sq"] += float(np.sum(dA * dA) + np.sum(dB * dB))'),                 # gnorm of B too
+]
+
+
+def _load_mutant(old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, old
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new, 1), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def _checks(B):
+    """Pin checks that do not depend on which module is under test; each
+    returns True when the module passes."""
+    cfg = synth.get_config("tiny")
+    out = []
+    # golden-style closed forms
+    x = np.array([[3.0, 4.0]])
+    out.append(np.allclose(B.rmsnorm_bwd(x, np.ones(2), np.array([[1.0, 0.0]]), 0.0)[0],
+                           [0.18101933598375617, -0.13576450198781713], atol=1e-15))
+    out.append(np.allclose(B.rope_bwd(np.array([[1.0, 0, 0, 0]]), 1, 4, [1], 100.0)[0],
+                           [np.cos(1.0), 0, -np.sin(1.0), 0], atol=1e-15))
+    out.append(np.allclose(B.rope_bwd(np.array([[0, 0, 0, 1.0]]), 1, 4, [1], 100.0)[0],
+                           [0, np.sin(0.1), 0, np.cos(0.1)], atol=1e-15))
+    dg, du = B.relu2_mul_bwd(np.array([-1, 0, 0.5, 2.0]), np.array([3, 1, -2, 0.5]),
+                             np.array([1, 1, 1, 2.0]))
+    out.append(np.array_equal(dg, [0, 0, -2, 4]) and np.array_equal(du, [0, 0, 0.25, 8]))
+    out.append(np.array_equal(B.softmax_bwd(np.array([0.5, 0.5, 0]), np.array([1.0, 3, 7])),
+                              [-0.5, 0.5, 0]))
+    p, m, v = B.adamw(0.5, 0.2, 0.0, 0.0, 1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    out.append(abs(p - 0.49899500004999997) < 1e-15 and abs(v - 4e-5) < 1e-18)
+    # whole-layer finite differences (SwiGLU + LoRA)
+    d = synth.draw_layer(cfg)
+    w, saved, lora = F.make_layer(cfg, d)
+    res = B.layer_bwd(cfg, w, saved, d["d_out"], lora)
+    x0 = d["x"]
+
+    def L(**kw):
+        o, _ = F.layer_forward(cfg, w, kw.pop("x", x0), x_attn=x0, **kw)
+        return float(np.sum(d["d_out"] * o))
+    idx = range(0, x0.size, 37)
+    num = fd.grad(lambda z: L(x=z, lora=lora), x0, idx=idx)
+    out.append(fd.rel_err(res["d_hidden"].reshape(-1)[list(idx)], num.reshape(-1)[list(idx)]) < 1e-5)
+    for k in ("A_q", "B_q", "A_v", "B_v"):
+        def Lk(z, k=k):
+            l2 = dict(lora)
+            l2[k] = z
+            return L(lora=l2)
+        ii = range(0, lora[k].size, 5)
+        num = fd.grad(Lk, lora[k], idx=ii, rel_step=1e-5)
+        out.append(fd.rel_err(res["d" + k].reshape(-1)[list(ii)], num.reshape(-1)[list(ii)]) < 1e-5)
+    # A-only gradient norm and the AdamW step-1 closed form on B (LoRA+)
+    out.append(abs(res["gnorm_sq"] - float(np.sum(res["dA_q"] ** 2) + np.sum(res["dA_v"] ** 2)))
+               <= 1e-15 * res["gnorm_sq"])
+    g = res["dB_q"]
+    want = lora["B_q"] - cfg.lr_b * (g / (np.abs(g) + cfg.adam_eps) + cfg.weight_decay * lora["B_q"])
+    out.append(np.allclose(res["B_q"], want, rtol=1e-13))
+    # GQA attention FD with 4 query heads on 2 KV heads
+    r = np.random.default_rng(3)
+    q = r.standard_normal((5, 4 * 4))
+    kk = r.standard_normal((5, 2 * 4))
+    vv = r.standard_normal((5, 2 * 4))
+    P, ctx = F.attention(q, kk, vv, 4, 2, 4, 0.5, True)
+    dctx = r.standard_normal(ctx.shape)
+    dq, dv = B.attention_bwd(dctx, P, kk, vv, 4, 2, 0.5)
+    out.append(fd.rel_err(dq, fd.grad(lambda z: float(np.sum(dctx * F.attention(z, kk, vv, 4, 2, 4, 0.5, True)[1])), q)) < 1e-7)
+    out.append(fd.rel_err(dv, fd.grad(lambda z: float(np.sum(dctx * F.attention(q, kk, z, 4, 2, 4, 0.5, True)[1])), vv)) < 1e-7)
+    # decode-like layer (pos0 = 11, ReLU^2 x up, sub-norms): FD of dQpre and dX
+    cd = synth.get_config("decode").with_(hidden=16, ffn=24, n_heads=2, n_kv_heads=1,
+                                         head_dim=8, kv_len=12, pos0=11)
+    dd = synth.draw_layer(cd)
+    wd_, sd_, _ = F.make_layer(cd, dd)
+    rd = B.layer_bwd(cd, wd_, sd_, dd["d_out"], None)
+
+    def Ld(**kw):
+        o, _ = F.layer_forward(cd, wd_, kw.pop("x", dd["x"]), x_attn=dd["x"], **kw)
+        return float(np.sum(dd["d_out"] * o))
+    out.append(fd.rel_err(rd["dq_pre"], fd.grad(lambda z: Ld(q_pre=z), sd_["q_pre"])) < 1e-5)
+    out.append(fd.rel_err(rd["d_hidden"], fd.grad(lambda z: Ld(x=z), dd["x"])) < 1e-5)
+    # multi-step AdamW v update against its definition through a second step
+    p2, m2, v2 = B.adamw(np.array([1.0]), np.array([0.5]), np.array([0.1]), np.array([0.04]),
+                         1e-3, 0.9, 0.999, 1e-8, 0.0, 2)
+    out.append(abs(v2[0] - (0.999 * 0.04 + 0.001 * 0.25)) < 1e-15)
+    return out
+
+
+def test_unmutated_oracle_passes_all_checks():
+    from oracle import backward as B
+    assert all(_checks(B))
+
+
+@pytest.mark.parametrize("i", range(len(MUTATIONS)))
+def test_mutation_is_caught(i):
+    old, new = MUTATIONS[i]
+    B = _load_mutant(old, new)
+    try:
+        ok = all(_checks(B))
+    except (ValueError, IndexError):  # a shape error also exposes the mistake
+        ok = False
+    assert not ok, "mutation not caught: %r -> %r" % (old, new)

@@ -1,0 +1,502 @@
+// C ABI of the lorabwd library: argument validation (always before any HIP
+// call, so a rejected call enqueues nothing), workspace sizing, and the
+// composition of the FFN and whole-layer backward from the kernels.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/lorabwd.h"
+#include "kernels.h"
+
+using namespace lbp;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t up(size_t b) { return (b + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool dtype_ok(int dt) { return dt == LORABWD_F32 || dt == LORABWD_BF16; }
+inline size_t esize(int dt) { return dt == LORABWD_BF16 ? 2 : 4; }
+inline bool feat_ok(int64_t n) { return n > 0 && n % 8 == 0; }
+inline bool head_dim_ok(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+inline bool finite(float x) { return isfinite(x); }
+
+// Byte ranges [a, a+na) and [b, b+nb) intersect.
+inline bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// Carves aligned sub-buffers out of a workspace.
+struct Carver {
+  char* p;
+  size_t used = 0;
+  explicit Carver(void* base) : p((char*)base) {}
+  template <typename T>
+  T* take(size_t bytes) {
+    T* r = (T*)(p ? p + used : nullptr);
+    used += up(bytes);
+    return r;
+  }
+};
+
+#define LBP_CHECK(cond, code) \
+  do {                        \
+    if (!(cond)) return (code); \
+  } while (0)
+
+#define LBP_HIP(expr)                                   \
+  do {                                                  \
+    if ((expr) != hipSuccess) return LORABWD_ERR_HIP;   \
+  } while (0)
+
+// ---------------------------------------------------------------- FFN
+struct FfnPlan {
+  float *dhid, *dn2, *partials;
+  void* dgu;
+  size_t bytes;
+};
+
+FfnPlan ffn_plan(void* ws, int64_t rows, int64_t dim, int64_t ffn, int dt) {
+  Carver c(ws);
+  FfnPlan p;
+  const bool vec = rows == 1;
+  const int gu_dt = vec ? F32 : dt;
+  p.dhid = c.take<float>((size_t)rows * ffn * 4);
+  p.dgu = c.take<void>((size_t)rows * 2 * ffn * esize(gu_dt));
+  p.dn2 = c.take<float>((size_t)rows * dim * 4);
+  size_t part;
+  if (vec) {
+    const size_t a = gemv_partial_bytes(ffn, dim), b = gemv_partial_bytes(dim, 2 * ffn);
+    part = a > b ? a : b;
+  } else {
+    const size_t a = gemm_partial_bytes(rows, ffn, dim, dt);
+    const size_t b = gemm_partial_bytes(rows, dim, 2 * ffn, dt);
+    part = a > b ? a : b;
+  }
+  p.partials = c.take<float>(part);
+  p.bytes = c.used;
+  return p;
+}
+
+int ffn_validate(int64_t rows, int64_t dim, int64_t ffn, int act, const float* d_out,
+                 const void* w_down, const void* w_gate, const void* w_up, const void* gate,
+                 const void* up_, const void* hidden_pre, const float* gamma_sub,
+                 const void* resid1, const float* gamma_ffn, float* d_resid, float eps, int dt) {
+  LBP_CHECK(dtype_ok(dt), LORABWD_ERR_DTYPE);
+  LBP_CHECK(act == LORABWD_ACT_SWIGLU || act == LORABWD_ACT_RELU2, LORABWD_ERR_DTYPE);
+  LBP_CHECK(rows >= 0 && feat_ok(dim) && feat_ok(ffn), LORABWD_ERR_SHAPE);
+  LBP_CHECK(finite(eps) && eps >= 0.f, LORABWD_ERR_ARG);
+  if (rows == 0) return LORABWD_OK;
+  LBP_CHECK(d_out && w_down && w_gate && w_up && gate && up_ && resid1 && gamma_ffn && d_resid,
+            LORABWD_ERR_NULL);
+  LBP_CHECK((hidden_pre == nullptr) == (gamma_sub == nullptr), LORABWD_ERR_NULL);
+  const void* ptrs[] = {d_out, w_down, w_gate, w_up, gate, up_, resid1, gamma_ffn, d_resid,
+                        hidden_pre, gamma_sub};
+  for (const void* q : ptrs) LBP_CHECK(aligned16(q), LORABWD_ERR_ALIGN);
+  const size_t nres = (size_t)rows * dim * 4;
+  LBP_CHECK(d_resid == d_out || !overlap(d_resid, nres, d_out, nres), LORABWD_ERR_ALIAS);
+  const size_t es = esize(dt);
+  const void* ins[] = {w_down, w_gate, w_up, gate, up_, resid1, hidden_pre};
+  const size_t ns[] = {(size_t)dim * ffn * es, (size_t)dim * ffn * es, (size_t)dim * ffn * es,
+                       (size_t)rows * ffn * es, (size_t)rows * ffn * es, (size_t)rows * dim * es,
+                       (size_t)rows * ffn * es};
+  for (int i = 0; i < 7; ++i) LBP_CHECK(!overlap(d_resid, nres, ins[i], ns[i]), LORABWD_ERR_ALIAS);
+  LBP_CHECK(!overlap(d_resid, nres, gamma_ffn, (size_t)dim * 4), LORABWD_ERR_ALIAS);
+  return LORABWD_OK;
+}
+
+hipError_t ffn_run(int64_t rows, int64_t dim, int64_t ffn, int act, const float* d_out,
+                   const void* w_down, const void* w_gate, const void* w_up, const void* gate,
+                   const void* up_, const void* hidden_pre, const float* gamma_sub,
+                   const void* resid1, const float* gamma_ffn, float* d_resid, float eps, int dt,
+                   void* ws, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  FfnPlan p = ffn_plan(ws, rows, dim, ffn, dt);
+  hipError_t e;
+  const bool vec = rows == 1;
+  // 1. dHid = d_out W_down
+  if (vec)
+    e = launch_gemv(ffn, dim, d_out, w_down, nullptr, dim, dt, p.dhid, p.partials, s);
+  else
+    e = launch_gemm(rows, ffn, dim, d_out, F32, dim, w_down, nullptr, dim, dt, ffn, p.dhid, ffn,
+                    p.partials, s);
+  if (e != hipSuccess) return e;
+  // 2. sub-norm backward
+  if (hidden_pre) {
+    e = launch_rmsnorm_bwd(rows, ffn, hidden_pre, dt, gamma_sub, p.dhid, p.dhid, eps, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  // 3. gated activation backward -> [dGate | dUp]
+  const int gu_dt = vec ? F32 : dt;
+  e = launch_act_bwd(rows, ffn, act, gate, up_, dt, p.dhid, p.dgu, gu_dt, s);
+  if (e != hipSuccess) return e;
+  // 4. dN2 = [dGate | dUp] [W_gate; W_up]
+  if (vec)
+    e = launch_gemv(dim, 2 * ffn, (const float*)p.dgu, w_gate, w_up, ffn, dt, p.dn2, p.partials,
+                    s);
+  else
+    e = launch_gemm(rows, dim, 2 * ffn, p.dgu, gu_dt, 2 * ffn, w_gate, w_up, ffn, dt, dim, p.dn2,
+                    dim, p.partials, s);
+  if (e != hipSuccess) return e;
+  // 5. d_resid += rmsnorm_bwd(resid1, gamma_ffn, dN2)
+  return launch_rmsnorm_bwd(rows, dim, resid1, dt, gamma_ffn, p.dn2, d_resid, eps, 1, s);
+}
+
+// ---------------------------------------------------------------- LoRA
+int lora_validate(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank, const float* dy,
+                  const void* x, const void* h, float* A, float* B, float* m_a, float* v_a,
+                  float* m_b, float* v_b, float* grad_a, float* grad_b, float* gnorm_sq,
+                  float alpha, float lr_a, float lr_b, float beta1, float beta2, float eps,
+                  float wd, int step, int dt) {
+  LBP_CHECK(dtype_ok(dt), LORABWD_ERR_DTYPE);
+  LBP_CHECK(rows >= 0 && feat_ok(in_dim) && out_dim > 0 && rank >= 1 && rank <= 64,
+            LORABWD_ERR_SHAPE);
+  LBP_CHECK(step >= 1, LORABWD_ERR_STEP);
+  LBP_CHECK(finite(alpha) && finite(lr_a) && finite(lr_b) && finite(wd) && finite(eps) &&
+                eps >= 0.f && beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f,
+            LORABWD_ERR_ARG);
+  LBP_CHECK(A && B && m_a && v_a && m_b && v_b, LORABWD_ERR_NULL);
+  if (rows > 0) LBP_CHECK(dy && x && h, LORABWD_ERR_NULL);
+  const void* ptrs[] = {dy, x, h, A, B, m_a, v_a, m_b, v_b, grad_a, grad_b};
+  for (const void* q : ptrs) LBP_CHECK(aligned16(q), LORABWD_ERR_ALIGN);
+  LBP_CHECK(((uintptr_t)gnorm_sq & 3u) == 0, LORABWD_ERR_ALIGN);
+  const size_t na = (size_t)rank * in_dim * 4, nb = (size_t)out_dim * rank * 4;
+  float* outs[] = {A, m_a, v_a, grad_a, B, m_b, v_b, grad_b};
+  const size_t ns[] = {na, na, na, na, nb, nb, nb, nb};
+  for (int i = 0; i < 8; ++i)
+    for (int j = i + 1; j < 8; ++j)
+      LBP_CHECK(!overlap(outs[i], ns[i], outs[j], ns[j]), LORABWD_ERR_ALIAS);
+  for (int i = 0; i < 8; ++i) {
+    LBP_CHECK(!overlap(outs[i], ns[i], dy, (size_t)rows * out_dim * 4), LORABWD_ERR_ALIAS);
+    LBP_CHECK(!overlap(outs[i], ns[i], x, (size_t)rows * in_dim * esize(dt)), LORABWD_ERR_ALIAS);
+    LBP_CHECK(!overlap(outs[i], ns[i], h, (size_t)rows * rank * esize(dt)), LORABWD_ERR_ALIAS);
+    LBP_CHECK(!overlap(outs[i], ns[i], gnorm_sq, 4), LORABWD_ERR_ALIAS);
+  }
+  return LORABWD_OK;
+}
+
+AdamHP make_hp(float lr_a, float lr_b, float beta1, float beta2, float eps, float wd, int step) {
+  AdamHP hp;
+  hp.lr_a = lr_a;
+  hp.lr_b = lr_b;
+  hp.beta1 = beta1;
+  hp.beta2 = beta2;
+  hp.eps = eps;
+  hp.wd = wd;
+  // bias corrections 1/(1 - beta^step), formed in float64 once per call
+  hp.bc1 = (float)(1.0 / (1.0 - pow((double)beta1, (double)step)));
+  hp.bc2 = (float)(1.0 / (1.0 - pow((double)beta2, (double)step)));
+  return hp;
+}
+
+// ---------------------------------------------------------------- attention
+int attn_validate(int64_t s_q, int64_t s_kv, int64_t Hq, int64_t Hkv, int64_t D,
+                  const float* dctx, const void* P, const void* K, const void* V,
+                  const void* ctx, float* dq, float* dv, float scale, int causal, int dt) {
+  LBP_CHECK(dtype_ok(dt), LORABWD_ERR_DTYPE);
+  LBP_CHECK(s_q >= 0 && s_kv >= 0 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0 && head_dim_ok(D),
+            LORABWD_ERR_SHAPE);
+  LBP_CHECK(causal == 0 || causal == 1, LORABWD_ERR_ARG);
+  LBP_CHECK(!causal || s_q <= s_kv, LORABWD_ERR_SHAPE);
+  LBP_CHECK(s_q == 0 || s_kv >= 1, LORABWD_ERR_SHAPE);
+  LBP_CHECK(finite(scale), LORABWD_ERR_ARG);
+  if (s_q == 0 && (dv == nullptr || s_kv == 0)) return LORABWD_OK;
+  if (s_q > 0) LBP_CHECK(dctx && P && K && V && dq, LORABWD_ERR_NULL);
+  const void* ptrs[] = {dctx, P, K, V, ctx, dq, dv};
+  for (const void* q : ptrs) LBP_CHECK(aligned16(q), LORABWD_ERR_ALIGN);
+  const size_t es = esize(dt);
+  const size_t nq = (size_t)s_q * Hq * D, nkv = (size_t)s_kv * Hkv * D;
+  const void* ins[] = {dctx, P, K, V, ctx};
+  const size_t ns[] = {nq * 4, (size_t)Hq * s_q * s_kv * es, nkv * es, nkv * es, nq * es};
+  for (int i = 0; i < 5; ++i) {
+    LBP_CHECK(!overlap(dq, nq * 4, ins[i], ns[i]), LORABWD_ERR_ALIAS);
+    LBP_CHECK(!overlap(dv, nkv * 4, ins[i], ns[i]), LORABWD_ERR_ALIAS);
+  }
+  LBP_CHECK(!overlap(dq, nq * 4, dv, nkv * 4), LORABWD_ERR_ALIAS);
+  return LORABWD_OK;
+}
+
+}  // namespace
+
+// =========================================================================
+extern "C" {
+
+const char* lorabwd_status_string(int status) {
+  switch (status) {
+    case LORABWD_OK: return "ok";
+    case LORABWD_ERR_NULL: return "required pointer is NULL";
+    case LORABWD_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case LORABWD_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case LORABWD_ERR_DTYPE: return "unknown dtype or activation";
+    case LORABWD_ERR_WORKSPACE: return "workspace missing or too small";
+    case LORABWD_ERR_STEP: return "AdamW step must be >= 1";
+    case LORABWD_ERR_ALIAS: return "buffers overlap where not allowed";
+    case LORABWD_ERR_HIP: return "HIP launch failed";
+    case LORABWD_ERR_ARG: return "scalar argument out of range";
+    default: return "unknown status";
+  }
+}
+
+int lorabwd_abi_version(void) { return 1; }
+
+int lorabwd_rmsnorm_backward(int64_t rows, int64_t n, const void* x, const float* gamma,
+                             const float* dy, float* dx, float eps, int accumulate, int dtype,
+                             hipStream_t stream) {
+  LBP_CHECK(dtype_ok(dtype), LORABWD_ERR_DTYPE);
+  LBP_CHECK(rows >= 0 && feat_ok(n), LORABWD_ERR_SHAPE);
+  LBP_CHECK(finite(eps) && eps >= 0.f && (accumulate == 0 || accumulate == 1), LORABWD_ERR_ARG);
+  if (rows == 0) return LORABWD_OK;
+  LBP_CHECK(x && gamma && dy && dx, LORABWD_ERR_NULL);
+  LBP_CHECK(aligned16(x) && aligned16(gamma) && aligned16(dy) && aligned16(dx), LORABWD_ERR_ALIGN);
+  const size_t nb = (size_t)rows * n * 4;
+  LBP_CHECK(dx == dy || !overlap(dx, nb, dy, nb), LORABWD_ERR_ALIAS);
+  LBP_CHECK(!overlap(dx, nb, x, (size_t)rows * n * esize(dtype)), LORABWD_ERR_ALIAS);
+  LBP_CHECK(!overlap(dx, nb, gamma, (size_t)n * 4), LORABWD_ERR_ALIAS);
+  LBP_HIP(launch_rmsnorm_bwd(rows, n, x, dtype, gamma, dy, dx, eps, accumulate, stream));
+  return LORABWD_OK;
+}
+
+int lorabwd_rope_backward(int64_t rows, int64_t n_heads, int64_t head_dim, const float* dy,
+                          float* dx, int64_t pos0, float base, hipStream_t stream) {
+  LBP_CHECK(rows >= 0 && n_heads >= 1 && head_dim_ok(head_dim) && pos0 >= 0, LORABWD_ERR_SHAPE);
+  LBP_CHECK(finite(base) && base > 0.f, LORABWD_ERR_ARG);
+  if (rows == 0) return LORABWD_OK;
+  LBP_CHECK(dy && dx, LORABWD_ERR_NULL);
+  LBP_CHECK(aligned16(dy) && aligned16(dx), LORABWD_ERR_ALIGN);
+  const size_t nb = (size_t)rows * n_heads * head_dim * 4;
+  LBP_CHECK(dx == dy || !overlap(dx, nb, dy, nb), LORABWD_ERR_ALIAS);
+  LBP_HIP(launch_rope_bwd(rows, n_heads, head_dim, dy, dx, pos0, base, stream));
+  return LORABWD_OK;
+}
+
+size_t lorabwd_attn_workspace_size(int64_t s_q, int64_t s_kv, int64_t n_heads,
+                                   int64_t n_kv_heads, int64_t head_dim, int dtype) {
+  (void)dtype;
+  if (s_q < 0 || s_kv < 0 || n_heads < 1) return 0;
+  return up(attn_ws_bytes(s_q, s_kv, n_heads, n_kv_heads, head_dim));
+}
+
+int lorabwd_attn_backward(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_kv_heads,
+                          int64_t head_dim, const float* dctx, const void* P, const void* K,
+                          const void* V, const void* ctx, float* dq, float* dv, float scale,
+                          int causal, int dtype, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  int st = attn_validate(s_q, s_kv, n_heads, n_kv_heads, head_dim, dctx, P, K, V, ctx, dq, dv,
+                         scale, causal, dtype);
+  if (st != LORABWD_OK) return st;
+  if (s_q == 0 && (dv == nullptr || s_kv == 0)) return LORABWD_OK;
+  const size_t need = lorabwd_attn_workspace_size(s_q, s_kv, n_heads, n_kv_heads, head_dim, dtype);
+  LBP_CHECK(workspace_bytes >= need && (need == 0 || workspace != nullptr), LORABWD_ERR_WORKSPACE);
+  LBP_CHECK(aligned16(workspace), LORABWD_ERR_ALIGN);
+  LBP_HIP(launch_attn_bwd(s_q, s_kv, n_heads, n_kv_heads, head_dim, dctx, P, K, V, ctx, dtype, dq,
+                          dv, scale, causal, workspace, stream));
+  return LORABWD_OK;
+}
+
+size_t lorabwd_ffn_workspace_size(int64_t rows, int64_t dim, int64_t ffn_dim, int dtype) {
+  if (rows <= 0 || dim <= 0 || ffn_dim <= 0) return 0;
+  return ffn_plan(nullptr, rows, dim, ffn_dim, dtype).bytes;
+}
+
+int lorabwd_ffn_backward(int64_t rows, int64_t dim, int64_t ffn_dim, int act, const float* d_out,
+                         const void* w_down, const void* w_gate, const void* w_up,
+                         const void* gate, const void* up_, const void* hidden_pre,
+                         const float* gamma_sub, const void* resid1, const float* gamma_ffn,
+                         float* d_resid, float eps, int dtype, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  int st = ffn_validate(rows, dim, ffn_dim, act, d_out, w_down, w_gate, w_up, gate, up_,
+                        hidden_pre, gamma_sub, resid1, gamma_ffn, d_resid, eps, dtype);
+  if (st != LORABWD_OK || rows == 0) return st;
+  const size_t need = lorabwd_ffn_workspace_size(rows, dim, ffn_dim, dtype);
+  LBP_CHECK(workspace && workspace_bytes >= need, LORABWD_ERR_WORKSPACE);
+  LBP_CHECK(aligned16(workspace), LORABWD_ERR_ALIGN);
+  LBP_HIP(ffn_run(rows, dim, ffn_dim, act, d_out, w_down, w_gate, w_up, gate, up_, hidden_pre,
+                  gamma_sub, resid1, gamma_ffn, d_resid, eps, dtype, workspace, stream));
+  return LORABWD_OK;
+}
+
+size_t lorabwd_lora_workspace_size(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank) {
+  if (rows < 0 || in_dim <= 0 || out_dim <= 0 || rank <= 0) return 0;
+  return up(lora_ws_bytes(rows, in_dim, out_dim, rank));
+}
+
+int lorabwd_lora_grad_adamw(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank,
+                            const float* dy, const void* x, const void* h, float* A, float* B,
+                            float* m_a, float* v_a, float* m_b, float* v_b, float* grad_a,
+                            float* grad_b, float* gnorm_sq, float alpha, float lr_a, float lr_b,
+                            float beta1, float beta2, float eps, float weight_decay, int step,
+                            int dtype, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  int st = lora_validate(rows, in_dim, out_dim, rank, dy, x, h, A, B, m_a, v_a, m_b, v_b, grad_a,
+                         grad_b, gnorm_sq, alpha, lr_a, lr_b, beta1, beta2, eps, weight_decay,
+                         step, dtype);
+  if (st != LORABWD_OK) return st;
+  const size_t need = lorabwd_lora_workspace_size(rows, in_dim, out_dim, rank);
+  LBP_CHECK(workspace && workspace_bytes >= need, LORABWD_ERR_WORKSPACE);
+  LBP_CHECK(aligned16(workspace), LORABWD_ERR_ALIGN);
+  const AdamHP hp = make_hp(lr_a, lr_b, beta1, beta2, eps, weight_decay, step);
+  LBP_HIP(launch_lora_adamw(rows, in_dim, out_dim, rank, dy, x, h, dtype, A, B, m_a, v_a, m_b,
+                            v_b, grad_a, grad_b, gnorm_sq, alpha / (float)rank, hp, workspace,
+                            stream));
+  return LORABWD_OK;
+}
+
+// ---------------------------------------------------------------- layer
+namespace {
+
+struct LayerPlan {
+  float *dctx, *dq, *dv;
+  void* scratch;
+  size_t bytes;
+};
+
+bool has_lora(const lorabwd_lora_state* s) { return s != nullptr && s->rank > 0; }
+
+LayerPlan layer_plan(void* ws, const lorabwd_layer_desc* d, int64_t rq, int64_t rv) {
+  const int64_t S = d->seq, L = d->kv_len, H = d->hidden;
+  const int64_t qd = d->n_heads * d->head_dim, kvd = d->n_kv_heads * d->head_dim;
+  Carver c(ws);
+  LayerPlan p;
+  p.dctx = c.take<float>((size_t)S * qd * 4);
+  p.dq = c.take<float>((size_t)S * qd * 4);
+  p.dv = c.take<float>((size_t)L * kvd * 4);
+  size_t sc = ffn_plan(nullptr, S, H, d->ffn, d->dtype).bytes;
+  const size_t o = S == 1 ? gemv_partial_bytes(qd, H) : gemm_partial_bytes(S, qd, H, d->dtype);
+  const size_t a = up(attn_ws_bytes(S, L, d->n_heads, d->n_kv_heads, d->head_dim));
+  const size_t lq = rq > 0 ? up(lora_ws_bytes(S, H, qd, rq)) : 0;
+  const size_t lv = rv > 0 ? up(lora_ws_bytes(S, H, kvd, rv)) : 0;
+  for (size_t v : {o, a, lq, lv})
+    if (v > sc) sc = v;
+  p.scratch = c.take<void>(sc);
+  p.bytes = c.used;
+  return p;
+}
+
+int desc_validate(const lorabwd_layer_desc* d) {
+  LBP_CHECK(d != nullptr, LORABWD_ERR_NULL);
+  LBP_CHECK(dtype_ok(d->dtype), LORABWD_ERR_DTYPE);
+  LBP_CHECK(d->act == LORABWD_ACT_SWIGLU || d->act == LORABWD_ACT_RELU2, LORABWD_ERR_DTYPE);
+  LBP_CHECK(d->seq >= 0 && d->kv_len >= d->seq && d->kv_len >= 1 && feat_ok(d->hidden) &&
+                feat_ok(d->ffn) && d->n_heads >= 1 && d->n_kv_heads >= 1 &&
+                d->n_heads % d->n_kv_heads == 0 && head_dim_ok(d->head_dim) && d->pos0 >= 0,
+            LORABWD_ERR_SHAPE);
+  LBP_CHECK((d->sub_norms == 0 || d->sub_norms == 1) && (d->causal == 0 || d->causal == 1),
+            LORABWD_ERR_ARG);
+  LBP_CHECK(finite(d->eps) && d->eps >= 0.f && finite(d->rope_base) && d->rope_base > 0.f &&
+                finite(d->attn_scale) && finite(d->lora_alpha),
+            LORABWD_ERR_ARG);
+  return LORABWD_OK;
+}
+
+}  // namespace
+
+size_t lorabwd_layer_workspace_size(const lorabwd_layer_desc* d) {
+  if (desc_validate(d) != LORABWD_OK) return 0;
+  // sized for the largest adapter rank the library accepts, so the size does
+  // not depend on the adapter states
+  return layer_plan(nullptr, d, 64, 64).bytes;
+}
+
+int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w,
+                           const lorabwd_layer_saved* a, lorabwd_lora_state* qs,
+                           lorabwd_lora_state* vs, const lorabwd_adamw* hp, float* d_hidden,
+                           float* dq_pre_out, float* dv_out, float* gnorm_sq, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  int st = desc_validate(d);
+  if (st != LORABWD_OK) return st;
+  LBP_CHECK(w && a, LORABWD_ERR_NULL);
+  const int64_t S = d->seq, L = d->kv_len, H = d->hidden, I = d->ffn;
+  const int64_t Hq = d->n_heads, Hkv = d->n_kv_heads, D = d->head_dim;
+  const int64_t qd = Hq * D, kvd = Hkv * D;
+  const int dt = d->dtype;
+  const bool sub = d->sub_norms != 0;
+  const bool lq = has_lora(qs), lv = has_lora(vs);
+  LBP_CHECK(!(qs && qs->rank < 0) && !(vs && vs->rank < 0), LORABWD_ERR_SHAPE);
+  if (lq || lv) {
+    LBP_CHECK(hp != nullptr, LORABWD_ERR_NULL);
+    LBP_CHECK(hp->step >= 1, LORABWD_ERR_STEP);
+    LBP_CHECK(a->attn_input != nullptr, LORABWD_ERR_NULL);
+  }
+  if (lq) LBP_CHECK(a->lora_q_h != nullptr, LORABWD_ERR_NULL);
+  if (lv) LBP_CHECK(a->lora_v_h != nullptr, LORABWD_ERR_NULL);
+  if (sub) LBP_CHECK(w->gamma_fsub && w->gamma_asub && a->hidden_pre && a->ctx, LORABWD_ERR_NULL);
+  if (S == 0) return LORABWD_OK;
+  LBP_CHECK(d_hidden && w->w_o, LORABWD_ERR_NULL);
+  st = ffn_validate(S, H, I, d->act, d_hidden, w->w_down, w->w_gate, w->w_up, a->gate, a->up,
+                    sub ? a->hidden_pre : nullptr, sub ? w->gamma_fsub : nullptr, a->resid1,
+                    w->gamma_ffn, d_hidden, d->eps, dt);
+  if (st != LORABWD_OK) return st;
+  LBP_CHECK(aligned16(w->w_o) && aligned16(w->gamma_asub) && aligned16(dq_pre_out) &&
+                aligned16(dv_out) && aligned16(a->attn_input) && aligned16(a->lora_q_h) &&
+                aligned16(a->lora_v_h),
+            LORABWD_ERR_ALIGN);
+  const LayerPlan plan = layer_plan(workspace, d, lq ? qs->rank : 0, lv ? vs->rank : 0);
+  LBP_CHECK(workspace && workspace_bytes >= lorabwd_layer_workspace_size(d),
+            LORABWD_ERR_WORKSPACE);
+  LBP_CHECK(aligned16(workspace), LORABWD_ERR_ALIGN);
+  float* dv = dv_out ? dv_out : plan.dv;
+  float* dqp = dq_pre_out ? dq_pre_out : plan.dq;
+  st = attn_validate(S, L, Hq, Hkv, D, plan.dctx, a->P, a->K, a->V, a->ctx, plan.dq, dv,
+                     d->attn_scale, d->causal, dt);
+  if (st != LORABWD_OK) return st;
+  LBP_CHECK(!overlap(dq_pre_out, (size_t)S * qd * 4, d_hidden, (size_t)S * H * 4) &&
+                !overlap(dv_out, (size_t)L * kvd * 4, d_hidden, (size_t)S * H * 4) &&
+                !overlap(dq_pre_out, (size_t)S * qd * 4, dv_out, (size_t)L * kvd * 4),
+            LORABWD_ERR_ALIAS);
+  const float lr_a = hp ? hp->lr_a : 0.f, lr_b = hp ? hp->lr_b : 0.f;
+  const int step = hp ? hp->step : 1;
+  if (lq) {
+    st = lora_validate(S, H, qd, qs->rank, dqp, a->attn_input, a->lora_q_h, qs->A, qs->B,
+                       qs->m_a, qs->v_a, qs->m_b, qs->v_b, nullptr, nullptr, gnorm_sq,
+                       d->lora_alpha, lr_a, lr_b, hp->beta1, hp->beta2, hp->eps,
+                       hp->weight_decay, step, dt);
+    if (st != LORABWD_OK) return st;
+  }
+  if (lv) {
+    st = lora_validate(S, H, kvd, vs->rank, dv + (L - S) * kvd, a->attn_input, a->lora_v_h,
+                       vs->A, vs->B, vs->m_a, vs->v_a, vs->m_b, vs->v_b, nullptr, nullptr,
+                       gnorm_sq, d->lora_alpha, lr_a, lr_b, hp->beta1, hp->beta2, hp->eps,
+                       hp->weight_decay, step, dt);
+    if (st != LORABWD_OK) return st;
+  }
+
+  // ---- all arguments valid: enqueue
+  // FFN half, residual-stream gradient in place: d_hidden <- dH1
+  LBP_HIP(ffn_run(S, H, I, d->act, d_hidden, w->w_down, w->w_gate, w->w_up, a->gate, a->up,
+                  sub ? a->hidden_pre : nullptr, sub ? w->gamma_fsub : nullptr, a->resid1,
+                  w->gamma_ffn, d_hidden, d->eps, dt, plan.scratch, stream));
+  // O-projection backward: dCtx = dH1 W_o
+  if (S == 1)
+    LBP_HIP(launch_gemv(qd, H, d_hidden, w->w_o, nullptr, H, dt, plan.dctx, (float*)plan.scratch,
+                        stream));
+  else
+    LBP_HIP(launch_gemm(S, qd, H, d_hidden, F32, H, w->w_o, nullptr, H, dt, qd, plan.dctx, qd,
+                        (float*)plan.scratch, stream));
+  if (sub)
+    LBP_HIP(launch_rmsnorm_bwd(S, qd, a->ctx, dt, w->gamma_asub, plan.dctx, plan.dctx, d->eps, 0,
+                               stream));
+  LBP_HIP(launch_attn_bwd(S, L, Hq, Hkv, D, plan.dctx, a->P, a->K, a->V, a->ctx, dt, plan.dq, dv,
+                          d->attn_scale, d->causal, plan.scratch, stream));
+  LBP_HIP(launch_rope_bwd(S, Hq, D, plan.dq, dqp, d->pos0, d->rope_base, stream));
+  if (lq) {
+    const AdamHP h = make_hp(lr_a, lr_b, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, step);
+    LBP_HIP(launch_lora_adamw(S, H, qd, qs->rank, dqp, a->attn_input, a->lora_q_h, dt, qs->A,
+                              qs->B, qs->m_a, qs->v_a, qs->m_b, qs->v_b, nullptr, nullptr,
+                              gnorm_sq, d->lora_alpha / (float)qs->rank, h, plan.scratch,
+                              stream));
+  }
+  if (lv) {
+    // the adapter sees the value rows of the current tokens: the last S of
+    // the kv_len rows (all of them when kv_len == seq)
+    const AdamHP h = make_hp(lr_a, lr_b, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, step);
+    LBP_HIP(launch_lora_adamw(S, H, kvd, vs->rank, dv + (L - S) * kvd, a->attn_input,
+                              a->lora_v_h, dt, vs->A, vs->B, vs->m_a, vs->v_a, vs->m_b, vs->v_b,
+                              nullptr, nullptr, gnorm_sq, d->lora_alpha / (float)vs->rank, h,
+                              plan.scratch, stream));
+  }
+  return LORABWD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal launchers of the lorabwd kernels.  Each launcher only enqueues
+// work on `stream`; arguments were validated by the C-ABI layer (api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lbp {
+
+enum DType { F32 = 0, BF16 = 1 };
+enum ActKind { SWIGLU = 0, RELU2 = 1 };
+
+// ---- row-wise kernels (rowwise.hip)
+hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, const float* gamma,
+                              const float* dy, float* dx, float eps, int accumulate,
+                              hipStream_t s);
+hipError_t launch_rope_bwd(int64_t rows, int64_t n_heads, int64_t head_dim, const float* dy,
+                           float* dx, int64_t pos0, float base, hipStream_t s);
+// dgu[r, 0:I] = dGate, dgu[r, I:2I] = dUp; out_dt selects float or bf16 output.
+hipError_t launch_act_bwd(int64_t rows, int64_t ffn, int act, const void* gate, const void* up,
+                          int in_dt, const float* dhid, void* dgu, int out_dt, hipStream_t s);
+// p[0:n] = 0 (a kernel, not a memset, so the call can sit in a captured graph)
+hipError_t launch_fill_zero(int64_t n, float* p, hipStream_t s);
+// dst = bf16(src), n elements (n % 8 == 0)
+hipError_t launch_to_bf16(int64_t n, const float* src, void* dst, hipStream_t s);
+
+// ---- products (gemm.hip)
+// C[M,N] = A[M,K] B[K,N]; B rows k < K1 come from B1 (row k), rows k >= K1
+// from B2 (row k - K1).  A is float or bf16 (a_dt), B is float or bf16
+// (b_dt).  bf16 B runs on bf16 matrix cores (A rounded to bf16).
+// split-K writes partial sums to `partials` ([splits, M, N]) and reduces
+// them in order; partial_bytes must cover gemm_partial_bytes().
+int gemm_splits(int64_t M, int64_t N, int64_t K, int b_dt);
+size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K, int b_dt);
+hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt, int64_t lda,
+                       const void* B1, const void* B2, int64_t K1, int b_dt, int64_t ldb,
+                       float* C, int64_t ldc, float* partials, hipStream_t s);
+
+// y[N] = x[K] W[K,N] with the same two-source rule; single vector.
+int gemv_splits(int64_t N, int64_t K);
+size_t gemv_partial_bytes(int64_t N, int64_t K);
+hipError_t launch_gemv(int64_t N, int64_t K, const float* x, const void* W1, const void* W2,
+                       int64_t K1, int w_dt, float* y, float* partials, hipStream_t s);
+
+// ---- attention (attn.hip)
+size_t attn_ws_bytes(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_kv_heads,
+                     int64_t head_dim);
+hipError_t launch_attn_bwd(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_kv_heads,
+                           int64_t head_dim, const float* dctx, const void* P, const void* K,
+                           const void* V, const void* ctx, int dt, float* dq, float* dv,
+                           float scale, int causal, void* ws, hipStream_t s);
+
+// ---- LoRA + AdamW (lora.hip)
+size_t lora_ws_bytes(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank);
+struct AdamHP {
+  float lr_a, lr_b, beta1, beta2, eps, wd, bc1, bc2;
+};
+hipError_t launch_lora_adamw(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank,
+                             const float* dy, const void* x, const void* h, int dt, float* A,
+                             float* B, float* m_a, float* v_a, float* m_b, float* v_b,
+                             float* grad_a, float* grad_b, float* gnorm_sq, float scaling,
+                             const AdamHP& hp, void* ws, hipStream_t s);
+
+}  // namespace lbp

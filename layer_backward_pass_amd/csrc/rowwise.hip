@@ -1,0 +1,244 @@
+// Row-wise and elementwise backward kernels: RMSNorm backward, inverse NeoX
+// RoPE, and the gated-activation (SwiGLU, ReLU^2 x up) backward.  All are
+// HBM-bound: each element is read once and written once, with float4 /
+// 8-byte bf16 vector accesses.
+#include "common.h"
+#include "kernels.h"
+
+namespace lbp {
+
+// ---------------------------------------------------------------------------
+// RMSNorm backward, one 256-thread workgroup per row.  Hesper "Attention
+// Backward GPU Kernels", section "RMSNorm Backward":
+//   dx = (1/r) (dy*gamma - x <dy*gamma, x> / (n r^2)),  r = sqrt(mean(x^2)+eps)
+// Pass 1 reduces sum(x^2) and <dy*gamma, x> over the row; pass 2 writes dx
+// (or adds to it).  Each thread re-reads only the elements it read in pass
+// 1, so dx may alias dy.
+template <typename T, int ACC>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int64_t n, const T* __restrict__ x,
+                                                          const float* __restrict__ gamma,
+                                                          const float* dy, float* dx,
+                                                          float eps) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const T* xr = x + row * n;
+  const float* dyr = dy + row * n;
+  float* dxr = dx + row * n;
+  float ss = 0.f, dot = 0.f;
+  for (int64_t i = (int64_t)threadIdx.x * 4; i < n; i += 1024) {
+    float4 xv = Act<T>::ld4(xr, i);
+    float4 gv = *reinterpret_cast<const float4*>(gamma + i);
+    float4 dv = *reinterpret_cast<const float4*>(dyr + i);
+    ss += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
+    dot += dv.x * gv.x * xv.x + dv.y * gv.y * xv.y + dv.z * gv.z * xv.z + dv.w * gv.w * xv.w;
+  }
+  ss = block_sum<4>(ss, red);
+  dot = block_sum<4>(dot, red);
+  const float nf = (float)n;
+  const float r2 = ss / nf + eps;
+  const float inv_r = 1.0f / sqrtf(r2);
+  const float c = dot / (nf * r2);
+  for (int64_t i = (int64_t)threadIdx.x * 4; i < n; i += 1024) {
+    float4 xv = Act<T>::ld4(xr, i);
+    float4 gv = *reinterpret_cast<const float4*>(gamma + i);
+    float4 dv = *reinterpret_cast<const float4*>(dyr + i);
+    float4 o;
+    o.x = (dv.x * gv.x - xv.x * c) * inv_r;
+    o.y = (dv.y * gv.y - xv.y * c) * inv_r;
+    o.z = (dv.z * gv.z - xv.z * c) * inv_r;
+    o.w = (dv.w * gv.w - xv.w * c) * inv_r;
+    float4* dp = reinterpret_cast<float4*>(dxr + i);
+    if (ACC) {
+      float4 p = *dp;
+      o.x += p.x;
+      o.y += p.y;
+      o.z += p.z;
+      o.w += p.w;
+    }
+    *dp = o;
+  }
+}
+
+hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, const float* gamma,
+                              const float* dy, float* dx, float eps, int accumulate,
+                              hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  dim3 grid((unsigned)rows), block(256);
+  if (xdt == F32) {
+    if (accumulate)
+      rmsnorm_bwd_kernel<float, 1><<<grid, block, 0, s>>>(n, (const float*)x, gamma, dy, dx, eps);
+    else
+      rmsnorm_bwd_kernel<float, 0><<<grid, block, 0, s>>>(n, (const float*)x, gamma, dy, dx, eps);
+  } else {
+    if (accumulate)
+      rmsnorm_bwd_kernel<bf16, 1><<<grid, block, 0, s>>>(n, (const bf16*)x, gamma, dy, dx, eps);
+    else
+      rmsnorm_bwd_kernel<bf16, 0><<<grid, block, 0, s>>>(n, (const bf16*)x, gamma, dy, dx, eps);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Inverse NeoX RoPE.  Hesper "Attention Backward GPU Kernels", section "RoPE
+// Backward (inverse rotation)".  One workgroup per row; thread (d, hg)
+// forms theta_d = pos * base^(-2d/D) and its cosine and sine in float64 once,
+// then rotates the (d, d+half) pair of every head hg, hg+HG, ...  The angle
+// of a late position needs float64: at pos ~2e3 one float32 ulp of theta is
+// ~1e-4 rad.
+__global__ __launch_bounds__(256) void rope_bwd_kernel(int64_t n_heads, int head_dim,
+                                                       const float* dy, float* dx, int64_t pos0,
+                                                       double log2_base) {
+  const int half = head_dim >> 1;
+  const int d = threadIdx.x % half;
+  const int hg = threadIdx.x / half;
+  const int HG = blockDim.x / half;
+  const int64_t row = blockIdx.x;
+  const double pos = (double)(pos0 + row);
+  const double inv_freq = exp2(-(2.0 * d / head_dim) * log2_base);
+  double sn, cs;
+  sincos(pos * inv_freq, &sn, &cs);
+  const float c = (float)cs, s = (float)sn;
+  const int64_t base = row * n_heads * head_dim;
+  for (int64_t h = hg; h < n_heads; h += HG) {
+    const int64_t i = base + h * head_dim + d;
+    const float lo = dy[i], hi = dy[i + half];
+    dx[i] = lo * c + hi * s;
+    dx[i + half] = -lo * s + hi * c;
+  }
+}
+
+hipError_t launch_rope_bwd(int64_t rows, int64_t n_heads, int64_t head_dim, const float* dy,
+                           float* dx, int64_t pos0, float base, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int half = (int)head_dim / 2;
+  int threads = 256 / half * half;
+  if ((int64_t)(threads / half) > n_heads) threads = (int)n_heads * half;
+  rope_bwd_kernel<<<dim3((unsigned)rows), dim3(threads), 0, s>>>(n_heads, (int)head_dim, dy, dx,
+                                                                   pos0, log2((double)base));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Gated activation backward, 4 elements per thread.
+//   SwiGLU (entrenar wgpu_backward.rs, "SiLU backward"): s = sigmoid(g),
+//     dGate = dH up s (1 + g (1 - s)),  dUp = dH g s
+//   ReLU^2 x up (Hesper "FFN Backward GPU Kernels", "ReLU²×Mul Backward"):
+//     dGate = dH up 2 max(0,g),  dUp = dH max(0,g)^2
+// Output row r is [dGate(0:I) | dUp(0:I)] so the next product runs over
+// K = 2I against the stacked [W_gate; W_up].
+template <int ACT>
+__device__ __forceinline__ void act_bwd1(float g, float u, float dh, float& dg, float& du) {
+  if (ACT == SWIGLU) {
+    const float sg = 1.0f / (1.0f + expf(-g));
+    dg = dh * u * sg * (1.0f + g * (1.0f - sg));
+    du = dh * g * sg;
+  } else {
+    const float r = fmaxf(g, 0.0f);
+    dg = dh * u * 2.0f * r;
+    du = dh * r * r;
+  }
+}
+
+template <typename T, int ACT, int OUT_BF16>
+__global__ __launch_bounds__(256) void act_bwd_kernel(int64_t rows, int64_t ffn,
+                                                      const T* __restrict__ gate,
+                                                      const T* __restrict__ up,
+                                                      const float* __restrict__ dhid, void* dgu) {
+  const int64_t q = ffn / 4;
+  const int64_t total = rows * q;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = t / q;
+    const int64_t c = (t - r * q) * 4;
+    const int64_t i = r * ffn + c;
+    const float4 g = Act<T>::ld4(gate, i);
+    const float4 u = Act<T>::ld4(up, i);
+    const float4 dh = *reinterpret_cast<const float4*>(dhid + i);
+    float4 dg, du;
+    act_bwd1<ACT>(g.x, u.x, dh.x, dg.x, du.x);
+    act_bwd1<ACT>(g.y, u.y, dh.y, dg.y, du.y);
+    act_bwd1<ACT>(g.z, u.z, dh.z, dg.z, du.z);
+    act_bwd1<ACT>(g.w, u.w, dh.w, dg.w, du.w);
+    const int64_t og = r * 2 * ffn + c, ou = og + ffn;
+    if (OUT_BF16) {
+      uint16_t* o = (uint16_t*)dgu;
+      uint2 a, b;
+      a.x = (uint32_t)f2bf(dg.x) | ((uint32_t)f2bf(dg.y) << 16);
+      a.y = (uint32_t)f2bf(dg.z) | ((uint32_t)f2bf(dg.w) << 16);
+      b.x = (uint32_t)f2bf(du.x) | ((uint32_t)f2bf(du.y) << 16);
+      b.y = (uint32_t)f2bf(du.z) | ((uint32_t)f2bf(du.w) << 16);
+      *reinterpret_cast<uint2*>(o + og) = a;
+      *reinterpret_cast<uint2*>(o + ou) = b;
+    } else {
+      float* o = (float*)dgu;
+      *reinterpret_cast<float4*>(o + og) = dg;
+      *reinterpret_cast<float4*>(o + ou) = du;
+    }
+  }
+}
+
+template <typename T, int ACT>
+static void act_launch(int64_t rows, int64_t ffn, const void* gate, const void* up,
+                       const float* dhid, void* dgu, int out_dt, hipStream_t s) {
+  const int64_t total = rows * (ffn / 4);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (out_dt == BF16)
+    act_bwd_kernel<T, ACT, 1><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+        rows, ffn, (const T*)gate, (const T*)up, dhid, dgu);
+  else
+    act_bwd_kernel<T, ACT, 0><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+        rows, ffn, (const T*)gate, (const T*)up, dhid, dgu);
+}
+
+hipError_t launch_act_bwd(int64_t rows, int64_t ffn, int act, const void* gate, const void* up,
+                          int in_dt, const float* dhid, void* dgu, int out_dt, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (in_dt == F32) {
+    if (act == SWIGLU) act_launch<float, SWIGLU>(rows, ffn, gate, up, dhid, dgu, out_dt, s);
+    else act_launch<float, RELU2>(rows, ffn, gate, up, dhid, dgu, out_dt, s);
+  } else {
+    if (act == SWIGLU) act_launch<bf16, SWIGLU>(rows, ffn, gate, up, dhid, dgu, out_dt, s);
+    else act_launch<bf16, RELU2>(rows, ffn, gate, up, dhid, dgu, out_dt, s);
+  }
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void to_bf16_kernel(int64_t n, const float* __restrict__ src,
+                                                      uint16_t* __restrict__ dst) {
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8; i < n;
+       i += (int64_t)gridDim.x * blockDim.x * 8) {
+    const float4 a = *reinterpret_cast<const float4*>(src + i);
+    const float4 b = *reinterpret_cast<const float4*>(src + i + 4);
+    uint4 o;
+    o.x = (uint32_t)f2bf(a.x) | ((uint32_t)f2bf(a.y) << 16);
+    o.y = (uint32_t)f2bf(a.z) | ((uint32_t)f2bf(a.w) << 16);
+    o.z = (uint32_t)f2bf(b.x) | ((uint32_t)f2bf(b.y) << 16);
+    o.w = (uint32_t)f2bf(b.z) | ((uint32_t)f2bf(b.w) << 16);
+    *reinterpret_cast<uint4*>(dst + i) = o;
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(int64_t n, float* __restrict__ p) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.f;
+}
+
+hipError_t launch_fill_zero(int64_t n, float* p, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  fill_zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(n, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_bf16(int64_t n, const float* src, void* dst, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n / 8 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  to_bf16_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(n, src, (uint16_t*)dst);
+  return hipGetLastError();
+}
+
+}  // namespace lbp

@@ -1,0 +1,177 @@
+"""Shared helpers of the GPU parity tests and the smoke check.
+
+Seeded draws (synth) go through the oracle's float64 forward to become
+consistent saved activations; those are cast to the storage dtype on the
+GPU, and the oracle then runs on exactly the values the GPU received (read
+back and widened to float64).  GPU results come through the C-ABI binding.
+
+Error measure, per output tensor: ||gpu - oracle||_inf / ||oracle||_inf.
+Bound: 1e-4 for float32 inputs, 2e-2 for bf16 inputs.
+
+AdamW after one step is p - lr (sign(g) + wd p) up to eps, which jumps where
+g crosses zero; an element whose oracle gradient is within the gradient
+tolerance of zero may take either sign.  Updated parameters are therefore
+compared at the bound on elements with |g| >= 1e-3 ||g||_inf, and within
+2 lr + bound elsewhere.  Moments m, v (continuous in g) use the plain bound.
+"""
+import numpy as np
+
+import synth
+from oracle import backward as OB
+from oracle import forward as OF
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def tdtype(cfg):
+    torch = _torch()
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+def dev(a, dtype, device):
+    torch = _torch()
+    return torch.from_numpy(np.ascontiguousarray(a, np.float64)).to(device=device, dtype=dtype)
+
+
+def host(t):
+    """Device tensor -> float64 numpy (exactly the values the GPU holds)."""
+    return t.detach().to(dtype=_torch().float64).cpu().numpy()
+
+
+def rel_err(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = float(np.max(np.abs(b))) if b.size else 0.0
+    num = float(np.max(np.abs(a - b))) if b.size else 0.0
+    return num / den if den > 0 else num
+
+
+def update_err(p_gpu, p_or, g_or, lr, tol):
+    """Error of an AdamW-updated tensor, scaled so that <= tol passes (see
+    the module docstring)."""
+    p_gpu = np.asarray(p_gpu, np.float64)
+    p_or = np.asarray(p_or, np.float64)
+    g_or = np.asarray(g_or, np.float64)
+    scale = max(float(np.max(np.abs(p_or))), 1e-30)
+    gmax = float(np.max(np.abs(g_or))) if g_or.size else 0.0
+    diff = np.abs(p_gpu - p_or)
+    firm = np.abs(g_or) >= 1e-3 * gmax
+    e1 = float(np.max(diff[firm])) / scale if firm.any() else 0.0
+    loose = ~firm
+    e2 = 0.0
+    if loose.any():
+        e2 = float(np.max(diff[loose])) / (2.0 * lr + tol * scale) * tol
+    return max(e1, e2)
+
+
+WEIGHTS = ("W_o", "W_gate", "W_up", "W_down")
+SAVED = ("attn_input", "resid1", "gate", "up", "hidden_pre", "ctx", "P", "K", "V",
+         "lora_q_h", "lora_v_h")
+
+
+class DeviceLayer:
+    """One layer's weights, saved activations and LoRA state on the GPU, plus
+    the float64 copies the oracle reads."""
+
+    def __init__(self, cfg, layer=0, device="cuda:0"):
+        torch = _torch()
+        self.cfg = cfg
+        draws = synth.draw_layer(cfg, layer)
+        w, saved, lora = OF.make_layer(cfg, draws)
+        dt = tdtype(cfg)
+        f32 = torch.float32
+        self.w = {k.lower(): dev(w[k], dt, device) for k in WEIGHTS}
+        for k in ("gamma_ffn", "gamma_fsub", "gamma_asub"):
+            if k in w:
+                self.w[k] = dev(w[k], f32, device)
+        self.saved = {k: dev(saved[k], dt, device) for k in SAVED if k in saved}
+        self.d_out = dev(draws["d_out"], f32, device)
+        self.lora = None
+        if lora is not None:
+            self.lora = {}
+            for tag in ("q", "v"):
+                self.lora[tag] = {
+                    "A": dev(lora["A_" + tag], f32, device), "B": dev(lora["B_" + tag], f32, device),
+                    "m_a": dev(lora["m_A_" + tag], f32, device),
+                    "v_a": dev(lora["v_A_" + tag], f32, device),
+                    "m_b": dev(lora["m_B_" + tag], f32, device),
+                    "v_b": dev(lora["v_B_" + tag], f32, device)}
+        # oracle copies: exactly what the GPU holds
+        self.o_w = {("W_" + k[2:] if k.startswith("w_") else k): host(v)
+                    for k, v in self.w.items()}
+        self.o_saved = {k: host(v) for k, v in self.saved.items()}
+        self.o_dout = host(self.d_out)
+        self.o_lora = None
+        if self.lora is not None:
+            self.o_lora = {}
+            for tag, st in self.lora.items():
+                self.o_lora["A_" + tag] = host(st["A"])
+                self.o_lora["B_" + tag] = host(st["B"])
+                self.o_lora["m_A_" + tag] = host(st["m_a"])
+                self.o_lora["v_A_" + tag] = host(st["v_a"])
+                self.o_lora["m_B_" + tag] = host(st["m_b"])
+                self.o_lora["v_B_" + tag] = host(st["v_b"])
+
+    def desc(self):
+        import layer_backward_pass_amd as lbp
+        c = self.cfg
+        return lbp.make_desc(c.seq, c.kv_len, c.hidden, c.ffn, c.n_heads, c.n_kv_heads,
+                             c.head_dim, act=lbp.ACT_SWIGLU if c.act == "swiglu" else lbp.ACT_RELU2,
+                             sub_norms=c.sub_norms, causal=c.causal,
+                             dtype=lbp.BF16 if c.dtype == "bf16" else lbp.F32, pos0=c.pos0,
+                             eps=c.eps, rope_base=c.rope_base, attn_scale=c.scale,
+                             lora_alpha=c.alpha)
+
+    def adamw(self):
+        import layer_backward_pass_amd as lbp
+        c = self.cfg
+        return lbp.AdamW(c.lr, c.lr_b, c.beta1, c.beta2, c.adam_eps, c.weight_decay, c.step)
+
+    def run_gpu(self, d_hidden, dq_pre=None, dv=None, gnorm=None):
+        import layer_backward_pass_amd as lbp
+        return lbp.lorabwd_layer_backward(
+            self.desc(), self.w, self.saved, d_hidden,
+            q_state=self.lora["q"] if self.lora else None,
+            v_state=self.lora["v"] if self.lora else None,
+            adamw=self.adamw() if self.lora else None, dq_pre_out=dq_pre, dv_out=dv,
+            gnorm_sq=gnorm)
+
+    def run_oracle(self, d_out):
+        return OB.layer_bwd(self.cfg, self.o_w, self.o_saved, d_out, self.o_lora)
+
+
+def compare_lora(cfg, dl, ref, tol):
+    """Errors of the updated LoRA tensors of one layer against the oracle."""
+    errs = {}
+    for tag in ("q", "v"):
+        st = dl.lora[tag]
+        errs["A_" + tag] = update_err(host(st["A"]), ref["A_" + tag], ref["dA_" + tag], cfg.lr, tol)
+        errs["B_" + tag] = update_err(host(st["B"]), ref["B_" + tag], ref["dB_" + tag], cfg.lr_b, tol)
+        for k, rk in (("m_a", "m_A_"), ("v_a", "v_A_"), ("m_b", "m_B_"), ("v_b", "v_B_")):
+            errs[k + "_" + tag] = rel_err(host(st[k]), ref[rk + tag])
+    return errs
+
+
+def layer_parity(cfg, device="cuda:0", layer=0):
+    """Run one layer on the GPU and on the oracle; returns {output: rel err}."""
+    torch = _torch()
+    dl = DeviceLayer(cfg, layer, device)
+    ref = dl.run_oracle(dl.o_dout)
+    d_hidden = dl.d_out.clone()
+    dq_pre = torch.empty(cfg.seq, cfg.q_dim, device=device)
+    dv = torch.empty(cfg.kv_len, cfg.kv_dim, device=device)
+    gnorm = torch.zeros(1, device=device)
+    dl.run_gpu(d_hidden, dq_pre, dv, gnorm)
+    torch.cuda.synchronize()
+    errs = {"d_hidden": rel_err(host(d_hidden), ref["d_hidden"]),
+            "dq_pre": rel_err(host(dq_pre), ref["dq_pre"]),
+            "dv": rel_err(host(dv), ref["dv"])}
+    if dl.lora is not None:
+        errs.update(compare_lora(cfg, dl, ref, TOL[cfg.dtype]))
+        errs["gnorm_sq"] = rel_err(host(gnorm), np.array([ref["gnorm_sq"]]))
+    return errs

@@ -1,0 +1,199 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function
+include/lorabwd.h declares, and rejects bad arguments with the documented
+status codes before any HIP call.
+
+Every call below carries at least one invalid argument, so none reaches a
+kernel launch (the fake pointers are never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import layer_backward_pass_amd as lbp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lorabwd.h")
+
+OK, ENULL, ESHAPE, EALIGN, EDTYPE, EWS, ESTEP, EALIAS, EHIP, EARG = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+
+# fake, 16-byte-aligned, non-overlapping "device" addresses (never touched)
+BASE = 1 << 40
+SPAN = 1 << 32
+
+
+def fake(i):
+    return BASE + i * SPAN
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lbp.lib_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return lbp.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(lorabwd_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_six_entry_points():
+    names = declared_functions()
+    for f in ("lorabwd_attn_backward", "lorabwd_ffn_backward", "lorabwd_rmsnorm_backward",
+              "lorabwd_rope_backward", "lorabwd_lora_grad_adamw", "lorabwd_layer_backward"):
+        assert f in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(lbp.EXPORTS) <= set(names)
+
+
+def test_status_strings_and_version(lib):
+    assert lib.lorabwd_abi_version() == 1
+    for code in (OK, ENULL, ESHAPE, EALIGN, EDTYPE, EWS, ESTEP, EALIAS, EHIP, EARG):
+        s = lib.lorabwd_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.lorabwd_status_string(12345).decode() == "unknown status"
+
+
+# ---------------------------------------------------------------- RMSNorm
+def test_rmsnorm_validation(lib):
+    f = lib.lorabwd_rmsnorm_backward
+    x, g, dy, dx = fake(0), fake(1), fake(2), fake(3)
+    assert f(4, 64, x, g, dy, dx, 1e-6, 0, 7, None) == EDTYPE
+    assert f(4, 60, x, g, dy, dx, 1e-6, 0, 0, None) == ESHAPE       # n % 8
+    assert f(-1, 64, x, g, dy, dx, 1e-6, 0, 0, None) == ESHAPE
+    assert f(4, 64, x, g, dy, dx, -1.0, 0, 0, None) == EARG
+    assert f(4, 64, x, g, dy, dx, float("nan"), 0, 0, None) == EARG
+    assert f(4, 64, x, g, dy, dx, 1e-6, 2, 0, None) == EARG
+    assert f(4, 64, None, g, dy, dx, 1e-6, 0, 0, None) == ENULL
+    assert f(4, 64, x + 4, g, dy, dx, 1e-6, 0, 0, None) == EALIGN
+    assert f(4, 64, x, g, dy, dy + 16, 1e-6, 0, 0, None) == EALIAS   # partial overlap
+    assert f(4, 64, x, g, dy, x, 1e-6, 0, 0, None) == EALIAS         # dx over x
+    assert f(0, 64, None, None, None, None, 1e-6, 0, 0, None) == OK  # empty: no-op
+
+
+def test_rope_validation(lib):
+    f = lib.lorabwd_rope_backward
+    a, b = fake(0), fake(1)
+    assert f(2, 4, 24, a, b, 0, 1e4, None) == ESHAPE    # head_dim not supported
+    assert f(2, 0, 16, a, b, 0, 1e4, None) == ESHAPE
+    assert f(2, 4, 16, a, b, -1, 1e4, None) == ESHAPE
+    assert f(2, 4, 16, a, b, 0, 0.0, None) == EARG
+    assert f(2, 4, 16, None, b, 0, 1e4, None) == ENULL
+    assert f(2, 4, 16, a, a + 64, 0, 1e4, None) == EALIAS
+    assert f(2, 4, 16, a, b + 8, 0, 1e4, None) == EALIGN
+    assert f(0, 4, 16, None, None, 0, 1e4, None) == OK
+
+
+def test_attn_validation(lib):
+    f = lib.lorabwd_attn_backward
+    p = [fake(i) for i in range(8)]
+    ws = lib.lorabwd_attn_workspace_size(64, 64, 4, 2, 64, 0)
+    assert ws > 0
+
+    def call(s_q=64, s_kv=64, hq=4, hkv=2, d=64, dctx=p[0], P=p[1], K=p[2], V=p[3], ctx=p[4],
+             dq=p[5], dv=p[6], scale=0.125, causal=1, dt=0, w=p[7], wsb=ws):
+        return f(s_q, s_kv, hq, hkv, d, dctx, P, K, V, ctx, dq, dv, scale, causal, dt, w, wsb, None)
+    assert call(hq=4, hkv=3) == ESHAPE              # Hq % Hkv
+    assert call(d=48) == ESHAPE
+    assert call(s_q=65, s_kv=64) == ESHAPE          # causal needs s_q <= s_kv
+    assert call(dt=3) == EDTYPE
+    assert call(causal=2) == EARG
+    assert call(scale=float("inf")) == EARG
+    assert call(K=None) == ENULL
+    assert call(dq=None) == ENULL
+    assert call(V=p[3] + 2) == EALIGN
+    assert call(dq=p[1]) == EALIAS                  # dq over P
+    assert call(dv=p[5] + 256) == EALIAS            # dv over dq
+    assert call(wsb=ws - 1) == EWS
+    assert call(w=None) == EWS
+    assert call(s_q=0, dv=None) == OK               # nothing to do
+
+
+def test_ffn_validation(lib):
+    f = lib.lorabwd_ffn_backward
+    p = [fake(i) for i in range(14)]
+    ws = lib.lorabwd_ffn_workspace_size(16, 64, 256, 0)
+    assert ws > 0
+
+    def call(rows=16, dim=64, ffn=256, act=0, d_out=p[0], wd=p[1], wg=p[2], wu=p[3], g=p[4],
+             u=p[5], hp=None, gs=None, r1=p[6], gf=p[7], dres=p[8], eps=1e-6, dt=0, w=p[9],
+             wsb=ws):
+        return f(rows, dim, ffn, act, d_out, wd, wg, wu, g, u, hp, gs, r1, gf, dres, eps, dt, w,
+                 wsb, None)
+    assert call(act=5) == EDTYPE
+    assert call(dt=9) == EDTYPE
+    assert call(ffn=250) == ESHAPE
+    assert call(eps=-1.0) == EARG
+    assert call(wg=None) == ENULL
+    assert call(hp=p[10]) == ENULL                  # sub-norm input without its gamma
+    assert call(g=p[4] + 4) == EALIGN
+    assert call(dres=p[0] + 16) == EALIAS           # partial overlap with d_out
+    assert call(dres=p[6]) == EALIAS                # over resid1
+    assert call(wsb=ws - 256) == EWS
+    assert call(w=None) == EWS
+    assert call(rows=0) == OK
+
+
+def test_lora_validation(lib):
+    f = lib.lorabwd_lora_grad_adamw
+    p = [fake(i) for i in range(13)]
+    ws = lib.lorabwd_lora_workspace_size(16, 64, 64, 4)
+
+    def call(rows=16, i=64, o=64, r=4, dy=p[0], x=p[1], h=p[2], A=p[3], B=p[4], ma=p[5], va=p[6],
+             mb=p[7], vb=p[8], ga=None, gb=None, gn=None, alpha=8.0, lra=1e-4, lrb=1.6e-3,
+             b1=0.9, b2=0.999, eps=1e-8, wd=0.01, step=1, dt=0, w=p[9], wsb=ws):
+        return f(rows, i, o, r, dy, x, h, A, B, ma, va, mb, vb, ga, gb, gn, alpha, lra, lrb, b1, b2,
+                 eps, wd, step, dt, w, wsb, None)
+    assert call(step=0) == ESTEP
+    assert call(r=0) == ESHAPE
+    assert call(r=65) == ESHAPE
+    assert call(dt=2) == EDTYPE
+    assert call(b1=1.0) == EARG
+    assert call(lra=float("nan")) == EARG
+    assert call(B=None) == ENULL
+    assert call(dy=None) == ENULL
+    assert call(ma=p[5] + 8) == EALIGN
+    assert call(va=p[5]) == EALIAS                  # v_a over m_a
+    assert call(ga=p[0]) == EALIAS                  # grad_a over dy
+    assert call(gn=p[3] + 16) == EALIAS             # gnorm inside A
+    assert call(wsb=ws - 1) == EWS
+
+
+def test_layer_validation(lib):
+    d = lbp.make_desc(16, 16, 64, 256, 4, 2, 16, lora_alpha=8.0)
+    ws = lib.lorabwd_layer_workspace_size(ctypes.byref(d))
+    assert ws > 0
+    bad = lbp.make_desc(16, 16, 64, 256, 4, 3, 16)
+    assert lib.lorabwd_layer_workspace_size(ctypes.byref(bad)) == 0
+    w = lbp.LayerWeights(*[fake(i) for i in range(4)], fake(4), None, None)
+    a = lbp.LayerSaved(*[fake(10 + i) for i in range(11)])
+    st = lbp.LoraState(4, *[fake(30 + i) for i in range(6)])
+    hp = lbp.AdamW(1e-4, 1.6e-3, 0.9, 0.999, 1e-8, 0.01, 0)
+    f = lib.lorabwd_layer_backward
+    r = ctypes.byref
+    dh = fake(50)
+    assert f(r(bad), r(w), r(a), None, None, None, dh, None, None, None, fake(60), ws, None) == ESHAPE
+    assert f(r(d), r(w), r(a), r(st), None, r(hp), dh, None, None, None, fake(60), ws, None) == ESTEP
+    hp.step = 1
+    assert f(r(d), r(w), r(a), r(st), None, None, dh, None, None, None, fake(60), ws, None) == ENULL
+    sub = lbp.make_desc(16, 16, 64, 256, 4, 2, 16, sub_norms=True)
+    assert f(r(sub), r(w), r(a), None, None, None, dh, None, None, None, fake(60), ws, None) == ENULL
+    assert f(r(d), r(w), r(a), r(st), None, r(hp), dh, None, None, None, fake(60), ws - 1, None) == EWS
+    assert f(r(d), r(w), r(a), r(st), None, r(hp), dh, fake(50) + 64, None, None, fake(60), ws,
+             None) == EALIAS
+    d.kv_len = 8                                  # kv_len < seq
+    assert f(r(d), r(w), r(a), None, None, None, dh, None, None, None, fake(60), ws, None) == ESHAPE
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(OSError):
+        lbp.load_library(str(tmp_path / "missing.so"))

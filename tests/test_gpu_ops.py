@@ -1,0 +1,242 @@
+"""GPU parity of each C-ABI entry point against the float64 oracle, at small
+shapes that span several tiles and ragged tails, plus edge cases."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import backward as OB
+from tests import harness as Hn
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+DEV = "cuda:0"
+F32 = torch.float32
+BF16 = torch.bfloat16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import layer_backward_pass_amd as lbp
+    lbp.load_library()
+
+
+def lbp():
+    import layer_backward_pass_amd as m
+    return m
+
+
+def rnd(seed, shape, std=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * std
+
+
+def tol(dt):
+    return 2e-2 if dt == BF16 else 1e-4
+
+
+# ------------------------------------------------------------------ RMSNorm
+@pytest.mark.parametrize("rows,n,acc,dt", [
+    (1, 8, 0, F32), (3, 2560, 0, F32), (37, 1000, 1, F32), (5, 6912, 0, F32),
+    (17, 2560, 1, BF16), (2, 9728, 0, BF16)])
+def test_rmsnorm(rows, n, acc, dt):
+    print("rmsnorm", rows, n, acc, dt, flush=True)
+    x = Hn.dev(rnd(1, (rows, n)), dt, DEV)
+    g = Hn.dev(1 + 0.1 * rnd(2, n), F32, DEV)
+    dy = Hn.dev(rnd(3, (rows, n)), F32, DEV)
+    dx0 = rnd(4, (rows, n))
+    dx = Hn.dev(dx0, F32, DEV)
+    lbp().lorabwd_rmsnorm_backward(x, g, dy, dx, eps=1e-6, accumulate=bool(acc))
+    torch.cuda.synchronize()
+    want = OB.rmsnorm_bwd(Hn.host(x), Hn.host(g), Hn.host(dy), 1e-6) + (dx0 if acc else 0)
+    assert Hn.rel_err(Hn.host(dx), want) <= 1e-4
+
+
+def test_rmsnorm_in_place():
+    x = Hn.dev(rnd(1, (4, 64)), F32, DEV)
+    g = Hn.dev(1 + 0.1 * rnd(2, 64), F32, DEV)
+    dy = Hn.dev(rnd(3, (4, 64)), F32, DEV)
+    want = OB.rmsnorm_bwd(Hn.host(x), Hn.host(g), Hn.host(dy), 1e-6)
+    lbp().lorabwd_rmsnorm_backward(x, g, dy, dy)
+    torch.cuda.synchronize()
+    assert Hn.rel_err(Hn.host(dy), want) <= 1e-4
+
+
+# ------------------------------------------------------------------ RoPE
+@pytest.mark.parametrize("rows,H,D,pos0", [(1, 20, 128, 511), (33, 4, 16, 0), (2048, 2, 128, 0),
+                                           (7, 3, 64, 100000), (5, 9, 32, 3)])
+def test_rope(rows, H, D, pos0):
+    print("rope", rows, H, D, pos0, flush=True)
+    dy = Hn.dev(rnd(5, (rows, H * D)), F32, DEV)
+    dx = torch.empty_like(dy)
+    lbp().lorabwd_rope_backward(dy, dx, H, D, pos0=pos0, base=10000.0)
+    torch.cuda.synchronize()
+    want = OB.rope_bwd(Hn.host(dy), H, D, pos0 + np.arange(rows), 10000.0)
+    assert Hn.rel_err(Hn.host(dx), want) <= 1e-4
+    # in place
+    lbp().lorabwd_rope_backward(dy, dy, H, D, pos0=pos0, base=10000.0)
+    torch.cuda.synchronize()
+    assert Hn.rel_err(Hn.host(dy), want) <= 1e-4
+
+
+# ------------------------------------------------------------------ attention
+def _attn_inputs(seed, s_q, s_kv, Hq, Hkv, D, causal, dt):
+    from oracle import forward as OF
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((s_q, Hq * D))
+    k = r.standard_normal((s_kv, Hkv * D))
+    v = r.standard_normal((s_kv, Hkv * D))
+    P, ctx = OF.attention(q, k, v, Hq, Hkv, D, D ** -0.5, causal)
+    dctx = r.standard_normal((s_q, Hq * D))
+    return [Hn.dev(a, t, DEV) for a, t in ((dctx, F32), (P, dt), (k, dt), (v, dt), (ctx, dt))]
+
+
+@pytest.mark.parametrize("s_q,s_kv,Hq,Hkv,D,causal,use_ctx,dt", [
+    (16, 16, 4, 2, 16, 1, 1, F32),
+    (100, 100, 4, 2, 64, 1, 1, F32),      # ragged: not a multiple of 64 or 32
+    (130, 130, 4, 1, 128, 1, 0, F32),     # page-form delta (no ctx)
+    (70, 70, 2, 2, 32, 0, 1, F32),        # non-causal
+    (40, 97, 8, 2, 128, 1, 1, F32),       # fewer queries than keys
+    (1, 512, 20, 5, 128, 1, 1, F32),      # decode
+    (1, 77, 4, 2, 16, 1, 0, F32),         # decode, ragged cache
+    (96, 96, 8, 2, 128, 1, 1, BF16),
+    (1, 300, 8, 4, 64, 0, 0, BF16),
+])
+def test_attention(s_q, s_kv, Hq, Hkv, D, causal, use_ctx, dt):
+    print("attn", s_q, s_kv, Hq, Hkv, D, causal, use_ctx, dt, flush=True)
+    dctx, P, K, V, ctx = _attn_inputs(7, s_q, s_kv, Hq, Hkv, D, bool(causal), dt)
+    dq = torch.empty(s_q, Hq * D, device=DEV)
+    dv = torch.empty(s_kv, Hkv * D, device=DEV)
+    lbp().lorabwd_attn_backward(dctx, P, K, V, ctx if use_ctx else None, dq, dv, Hq, Hkv, D,
+                                causal=bool(causal))
+    torch.cuda.synchronize()
+    wq, wv = OB.attention_bwd(Hn.host(dctx), Hn.host(P), Hn.host(K), Hn.host(V), Hq, Hkv,
+                              D ** -0.5)
+    assert Hn.rel_err(Hn.host(dq), wq) <= tol(dt)
+    assert Hn.rel_err(Hn.host(dv), wv) <= tol(dt)
+
+
+def test_attention_without_dv_and_empty_queries():
+    dctx, P, K, V, ctx = _attn_inputs(8, 20, 20, 4, 2, 16, True, F32)
+    dq = torch.empty(20, 64, device=DEV)
+    lbp().lorabwd_attn_backward(dctx, P, K, V, ctx, dq, None, 4, 2, 16)
+    torch.cuda.synchronize()
+    wq, _ = OB.attention_bwd(Hn.host(dctx), Hn.host(P), Hn.host(K), Hn.host(V), 4, 2, 0.25)
+    assert Hn.rel_err(Hn.host(dq), wq) <= 1e-4
+    # zero query rows: dV is all zeros
+    dv = torch.full((20, 32), 7.0, device=DEV)
+    e = torch.empty(0, 64, device=DEV)
+    lbp().lorabwd_attn_backward(e, torch.empty(4, 0, 20, device=DEV), K, V, None,
+                                torch.empty(0, 64, device=DEV), dv, 4, 2, 16, causal=False)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dv).item() == 0
+
+
+# ------------------------------------------------------------------ FFN
+@pytest.mark.parametrize("rows,dim,ffn,act,sub,dt", [
+    (16, 64, 256, "swiglu", False, F32),
+    (1, 64, 96, "relu2", True, F32),        # decode GEMV path
+    (133, 192, 320, "swiglu", False, F32),  # ragged tiles
+    (1, 2560, 6912, "relu2", True, F32),    # decode layer shape
+    (70, 256, 512, "relu2", True, BF16),
+    (300, 128, 256, "swiglu", False, BF16),
+])
+def test_ffn(rows, dim, ffn, act, sub, dt):
+    print("ffn", rows, dim, ffn, act, sub, dt, flush=True)
+    r = np.random.default_rng(11)
+    t = lambda a, d=dt: Hn.dev(a, d, DEV)  # noqa: E731
+    d_out = t(r.standard_normal((rows, dim)), F32)
+    w_down = t(r.standard_normal((dim, ffn)) * 0.02)
+    w_gate = t(r.standard_normal((ffn, dim)) * 0.02)
+    w_up = t(r.standard_normal((ffn, dim)) * 0.02)
+    gate = t(r.standard_normal((rows, ffn)))
+    up = t(r.standard_normal((rows, ffn)))
+    resid1 = t(r.standard_normal((rows, dim)))
+    gffn = t(1 + 0.1 * r.standard_normal(dim), F32)
+    hp = t(r.standard_normal((rows, ffn))) if sub else None
+    gsub = t(1 + 0.1 * r.standard_normal(ffn), F32) if sub else None
+    d_resid = d_out.clone()
+    m = lbp()
+    m.lorabwd_ffn_backward(d_out, w_down, w_gate, w_up, gate, up, resid1, gffn, d_resid,
+                           act=m.ACT_SWIGLU if act == "swiglu" else m.ACT_RELU2,
+                           hidden_pre=hp, gamma_sub=gsub)
+    torch.cuda.synchronize()
+    H = Hn.host
+    want = OB.ffn_bwd(H(d_out), H(w_down), H(w_gate), H(w_up), H(gate), H(up), H(resid1),
+                      H(gffn), 1e-6, act, hidden_pre=H(hp) if sub else None,
+                      gamma_fsub=H(gsub) if sub else None)
+    assert Hn.rel_err(H(d_resid), want) <= tol(dt)
+
+
+# ------------------------------------------------------------------ LoRA
+@pytest.mark.parametrize("rows,H,out,rank,step,dt", [
+    (16, 64, 64, 4, 1, F32), (300, 256, 96, 16, 1, F32), (129, 64, 40, 7, 5, F32),
+    (200, 128, 64, 16, 1, BF16), (0, 64, 32, 4, 2, F32)])
+def test_lora_adamw(rows, H, out, rank, step, dt):
+    print("lora", rows, H, out, rank, step, dt, flush=True)
+    r = np.random.default_rng(12)
+    x = r.standard_normal((rows, H))
+    A = r.standard_normal((rank, H)) * 0.02
+    Bm = r.standard_normal((out, rank)) * 0.02
+    dy = r.standard_normal((rows, out))
+    cfg = synth.get_config("tiny")
+    m_a, v_a = synth.gen.draw_adam_state(cfg, 0, A.shape, 0) if step > 1 else (0 * A, 0 * A)
+    m_b, v_b = synth.gen.draw_adam_state(cfg, 0, Bm.shape, 1) if step > 1 else (0 * Bm, 0 * Bm)
+    tx = Hn.dev(x, dt, DEV)
+    th = Hn.dev(x @ A.T, dt, DEV)
+    T = {k: Hn.dev(v, F32, DEV) for k, v in dict(A=A, B=Bm, m_a=m_a, v_a=v_a, m_b=m_b, v_b=v_b).items()}
+    tdy = Hn.dev(dy, F32, DEV)
+    ga = torch.empty(rank, H, device=DEV)
+    gb = torch.empty(out, rank, device=DEV)
+    gn = torch.full((1,), 0.5, device=DEV)
+    alpha, lr, lr_b = 2.0 * rank, 1e-3, 1.6e-2
+    lbp().lorabwd_lora_grad_adamw(tdy, tx, th, T["A"], T["B"], T["m_a"], T["v_a"], T["m_b"],
+                                  T["v_b"], alpha, lr, lr_b, step=step, grad_a=ga, grad_b=gb,
+                                  gnorm_sq=gn)
+    torch.cuda.synchronize()
+    hx, hh = Hn.host(tx), Hn.host(th)
+    dA, dB = OB.lora_grads(dy if rows else np.zeros((0, out)), hh, hx, Bm, alpha, rank)
+    tl = tol(dt)
+    if rows:
+        assert Hn.rel_err(Hn.host(ga), dA) <= tl
+        assert Hn.rel_err(Hn.host(gb), dB) <= tl
+    nA, mA, vA = OB.adamw(A, dA, m_a, v_a, lr, 0.9, 0.999, 1e-8, 0.01, step)
+    nB, mB, vB = OB.adamw(Bm, dB, m_b, v_b, lr_b, 0.9, 0.999, 1e-8, 0.01, step)
+    assert Hn.update_err(Hn.host(T["A"]), nA, dA, lr, tl) <= tl
+    assert Hn.update_err(Hn.host(T["B"]), nB, dB, lr_b, tl) <= tl
+    for k, w in (("m_a", mA), ("v_a", vA), ("m_b", mB), ("v_b", vB)):
+        assert Hn.rel_err(Hn.host(T[k]), w) <= tl or np.max(np.abs(w)) == 0
+    assert Hn.rel_err(Hn.host(gn), [0.5 + np.sum(dA * dA)]) <= tl
+
+
+# ------------------------------------------------------------------ whole layer, small
+@pytest.mark.parametrize("name,over", [
+    ("tiny", {}),
+    ("tiny", {"seq": 45, "kv_len": 45}),                          # ragged
+    ("tiny", {"dtype": "bf16"}),
+    ("decode", {"hidden": 128, "ffn": 256, "n_heads": 4, "n_kv_heads": 2, "head_dim": 32,
+                "kv_len": 70, "pos0": 69}),
+    ("seq512", {"seq": 80, "kv_len": 80, "hidden": 256, "ffn": 512, "n_heads": 4,
+                "n_kv_heads": 1, "head_dim": 64, "rank": 8, "alpha": 16.0}),
+])
+def test_layer_small(name, over):
+    cfg = synth.get_config(name).with_(**over)
+    print("layer", cfg, flush=True)
+    errs = Hn.layer_parity(cfg, DEV)
+    bad = {k: v for k, v in errs.items() if not v <= Hn.TOL[cfg.dtype]}
+    assert not bad, bad
+
+
+def test_layer_deterministic():
+    cfg = synth.get_config("tiny").with_(seq=70, kv_len=70)
+    outs = []
+    for _ in range(2):
+        dl = Hn.DeviceLayer(cfg, 0, DEV)
+        d = dl.d_out.clone()
+        g = torch.zeros(1, device=DEV)
+        dl.run_gpu(d, gnorm=g)
+        torch.cuda.synchronize()
+        outs.append((d.cpu(), g.cpu(), dl.lora["q"]["A"].cpu(), dl.lora["v"]["B"].cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)

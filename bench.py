@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of the LoRA layer backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one whole backward of the workload through the C-ABI library:
+the residual-stream gradient is reset from the upstream gradient (one small
+device copy) and lorabwd_layer_backward runs every step of the path (FFN
+backward, O-projection backward, attention backward, inverse RoPE, and, where
+the workload has adapters, LoRA gradients with AdamW) - for `stack36`, all
+36 layers in reverse order.  Inputs are resident in HBM before timing starts;
+each input copy's step is captured once as a HIP graph and replayed.  Steps
+rotate over enough input copies that HBM-bound work cannot be served from
+the 256 MB Infinity Cache.
+
+Workloads (default: decode):
+  decode       one token, 512-slot K/V cache, hidden 2560, ffn 6912, 20/5 heads
+               of 128, ReLU^2 x up with sub-norms, ternary fp32 weights
+  seq512       512 tokens, hidden 2560, ffn 9728, 32/8 heads, SwiGLU, LoRA r16, fp32
+  seq2048bf16  the seq512 layer at 2048 tokens with bf16 activations/weights
+  stack36      36 seq512-shaped layers at 1024 tokens, fp32
+  tiny         hidden 64, 16 tokens (launch-bound; parity-size case)
+
+Prints ONE JSON line.  `roofline` describes the kernel with the largest
+share of the step, timed with HIP events recorded on the library's stream
+right after each kernel (lorabwd_layer_backward_timed); its algorithmic
+bytes / flops come from the library.  `cpu_baseline` times the float64
+oracle on the host on a bounded sample of the same workload.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK = {  # MI355X published peaks (dense)
+    "hbm_GBps": 8000.0,
+    "f32_TFLOPs": 157.3,
+    "bf16_TFLOPs": 2516.6,
+}
+COPIES = {"decode": 3, "tiny": 1, "seq512": 2, "seq2048bf16": 2, "stack36": 1}
+DEFAULT_STEPS = {"decode": 2000, "tiny": 2000, "seq512": 200, "seq2048bf16": 100, "stack36": 5}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode", choices=sorted(COPIES))
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline sample budget")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ HIP events via ctypes
+class Hip:
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            e = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[i] = e.value
+        return arr
+
+    def record(self, ev, stream):
+        if self.lib.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        out = ctypes.c_float()
+        self.lib.hipEventSynchronize(b)
+        if self.lib.hipEventElapsedTime(ctypes.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+
+# ------------------------------------------------------------------ workload
+def layer_call(lbp, cfg, d, d_hidden, **kw):
+    desc = lbp.make_desc(cfg.seq, cfg.kv_len, cfg.hidden, cfg.ffn, cfg.n_heads, cfg.n_kv_heads,
+                         cfg.head_dim,
+                         act=lbp.ACT_SWIGLU if cfg.act == "swiglu" else lbp.ACT_RELU2,
+                         sub_norms=cfg.sub_norms, causal=cfg.causal,
+                         dtype=lbp.BF16 if cfg.dtype == "bf16" else lbp.F32, pos0=cfg.pos0,
+                         eps=cfg.eps, rope_base=cfg.rope_base, attn_scale=cfg.scale,
+                         lora_alpha=cfg.alpha)
+    lora = d["lora"]
+    hp = lbp.AdamW(cfg.lr, cfg.lr_b, cfg.beta1, cfg.beta2, cfg.adam_eps, cfg.weight_decay,
+                   cfg.step) if lora else None
+    return lbp.lorabwd_layer_backward(desc, d["weights"], d["saved"], d_hidden,
+                                      q_state=lora["q"] if lora else None,
+                                      v_state=lora["v"] if lora else None, adamw=hp,
+                                      gnorm_sq=kw.pop("gnorm", None), **kw)
+
+
+def build_copies(cfg, n_copies, torch):
+    from synth.device import draw_timing_layer_device
+    copies = []
+    for c in range(n_copies):
+        layers = [draw_timing_layer_device(cfg, c * cfg.n_layers + l) for l in range(cfg.n_layers)]
+        copies.append({"layers": layers, "d_out": layers[-1]["d_out"],
+                       "d_hidden": torch.empty_like(layers[-1]["d_out"]),
+                       "gnorm": torch.zeros(1, device="cuda:0")})
+    return copies
+
+
+def run_step(lbp, cfg, cp):
+    """One step: reset the residual-stream gradient, then the layers in
+    reverse order (a single layer for one-layer workloads)."""
+    cp["d_hidden"].copy_(cp["d_out"])
+    for d in reversed(cp["layers"]):
+        layer_call(lbp, cfg, d, cp["d_hidden"], gnorm=cp["gnorm"])
+
+
+# ------------------------------------------------------------------ roofline
+def kernel_profile(lbp, hip, cfg, copies, torch, reps):
+    """Per-kernel average duration (ms), from events recorded right after each
+    kernel by lorabwd_layer_backward_timed, over `reps` eager steps."""
+    cap = 128
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = hip.events(cap + 1)
+    recs = (lbp.KernelRecord * cap)()
+    stats = {}
+    for r in range(reps):
+        cp = copies[r % len(copies)]
+        cp["d_hidden"].copy_(cp["d_out"])
+        for li, d in enumerate(reversed(cp["layers"])):
+            hip.record(ev[cap], stream)
+            n = layer_call(lbp, cfg, d, cp["d_hidden"], gnorm=cp["gnorm"],
+                           timing=(ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)), recs))
+            torch.cuda.synchronize()
+            prev = ev[cap]
+            for i in range(min(n, cap)):
+                ms = hip.elapsed_ms(prev, ev[i])
+                prev = ev[i]
+                key = (i, recs[i].name.decode())
+                s = stats.setdefault(key, {"ms": 0.0, "n": 0, "bytes": recs[i].alg_bytes,
+                                           "flops": recs[i].alg_flops})
+                s["ms"] += ms
+                s["n"] += 1
+    out = []
+    for (i, name), s in sorted(stats.items()):
+        out.append({"index": i, "name": name, "avg_ms": s["ms"] / s["n"],
+                    "alg_bytes": s["bytes"], "alg_flops": s["flops"]})
+    return out
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "layer_backward_pass_amd", "csrc"))):
+        with open(os.path.join(ROOT, "layer_backward_pass_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def roofline(cfg, kernels):
+    """The dominant kernel (largest time per step, launches of the same
+    kernel at the same shape counted together) against its roofline."""
+    groups = {}
+    for k in kernels:
+        key = (k["name"], k["alg_bytes"], k["alg_flops"])
+        g = groups.setdefault(key, {"ms": 0.0, "launches": 0, "avg": []})
+        g["ms"] += k["avg_ms"]
+        g["launches"] += 1
+        g["avg"].append(k["avg_ms"])
+    (name, nbytes, flops), g = max(groups.items(), key=lambda kv: kv[1]["ms"])
+    avg_s = sum(g["avg"]) / len(g["avg"]) / 1e3
+    intensity = flops / nbytes if nbytes else float("inf")
+    mfma_peak = PEAK["bf16_TFLOPs"] if "bf16" in name else PEAK["f32_TFLOPs"]
+    ridge = mfma_peak * 1e12 / (PEAK["hbm_GBps"] * 1e9)
+    if "mfma" in name and intensity > ridge:
+        achieved = flops / avg_s / 1e12
+        rl = {"bound": "mfma", "achieved": round(achieved, 2), "peak": mfma_peak,
+              "unit": "TFLOP/s", "frac": round(achieved / mfma_peak, 4)}
+    else:
+        achieved = nbytes / avg_s / 1e9
+        rl = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_GBps"],
+              "unit": "GB/s", "frac": round(achieved / PEAK["hbm_GBps"], 4)}
+    rl.update({"kernel": name, "avg_us": round(avg_s * 1e6, 2), "launches_per_step": g["launches"],
+               "alg_bytes": nbytes, "alg_flops": flops, "traffic": traffic_for(cfg, name)})
+    return rl
+
+
+def traffic_for(cfg, kernel):
+    """Measured HBM bytes per launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(cfg.name, {}).get(kernel)
+    if not ent or ent.get("source_digest") != source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(cfg, budget_s):
+    """The float64 oracle's layer backward on the host, timed on a bounded
+    sample: whole layers of the same workload, repeated until the budget is
+    used (at least once); for the stack, one of its 36 layers."""
+    import numpy as np
+    import synth
+    from oracle import backward as OB
+    one = cfg.with_(n_layers=1)
+    t = synth.draw_timing_layer(one, 0)
+    f64 = lambda a: np.asarray(a, np.float64)  # noqa: E731
+    w = {k: f64(v) for k, v in t.items() if k.startswith("W_") or k.startswith("gamma_")}
+    saved = {k: f64(t[k]) for k in ("attn_input", "resid1", "gate", "up", "ctx", "P", "K", "V",
+                                    "hidden_pre", "lora_q_h", "lora_v_h") if k in t}
+    lora = None
+    if cfg.rank > 0:
+        lora = {k: f64(v) for k, v in t.items()
+                if k[:2] in ("A_", "B_") or k[:4] in ("m_A_", "m_B_", "v_A_", "v_B_")}
+    d_out = f64(t["d_out"])
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        OB.layer_bwd(one, w, saved, d_out, lora)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or (runs >= 1 and el * (runs + 1) / runs > 3 * budget_s):
+            break
+    per_layer = el / runs
+    per_step = per_layer * cfg.n_layers
+    return {"value": round(cfg.seq / per_step, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d whole-layer backward(s) of the %s workload (%s), %.1f s%s" % (
+                runs, cfg.name, "float64 NumPy", el,
+                "; stack = 36 x one layer" if cfg.n_layers > 1 else "")}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU; --gpus %d is not supported (the multi-GPU "
+              "path is design-only)" % args.gpus, file=sys.stderr)
+        return 2
+    import torch
+    import synth
+    import layer_backward_pass_amd as lbp
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    lbp.load_library()
+    cfg = synth.get_config(args.workload)
+    steps = args.steps or DEFAULT_STEPS[cfg.name]
+    warmup = args.warmup if args.warmup is not None else max(3, steps // 10)
+    hip = Hip()
+    torch.cuda.set_device(0)
+    copies = build_copies(cfg, COPIES[cfg.name], torch)
+    # eager warm-up: sizes the workspace, loads the code objects
+    for cp in copies:
+        run_step(lbp, cfg, cp)
+    torch.cuda.synchronize()
+    graphs = []
+    if not args.no_graph:
+        for cp in copies:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_step(lbp, cfg, cp)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def step(i):
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            run_step(lbp, cfg, copies[i % len(copies)])
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = hip.events(2)
+    hip.record(ev[0], stream)
+    for i in range(steps):
+        step(i)
+    hip.record(ev[1], stream)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(ev[0], ev[1])
+    ms_per_step = ms / steps
+    tokens = cfg.seq * steps
+    value = tokens / (ms / 1e3)
+
+    kernels = kernel_profile(lbp, hip, cfg, copies, torch,
+                             reps=max(3, min(20, steps // 10)) if cfg.n_layers == 1 else 1)
+    rl = roofline(cfg, kernels)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, args.cpu_seconds)
+    out = {
+        "metric": "layer-backward tokens/s",
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens_per_step": cfg.seq, "kv_len": cfg.kv_len,
+                   "hidden": cfg.hidden, "ffn": cfg.ffn, "heads": cfg.n_heads,
+                   "kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "act": cfg.act,
+                   "sub_norms": cfg.sub_norms, "lora_rank": cfg.rank, "layers": cfg.n_layers,
+                   "input_copies": len(copies), "hip_graph": bool(graphs),
+                   "kernels_per_step": len(kernels) * (cfg.n_layers if cfg.n_layers > 1 else 1)},
+        "roofline": rl,
+        "cpu_baseline": cpu,
+        "kernels": [{"name": k["name"], "avg_us": round(k["avg_ms"] * 1e3, 2)} for k in kernels],
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -260,6 +260,31 @@ int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weig
                            float* d_hidden, float* dq_pre_out, float* dv_out, float* gnorm_sq,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement variant of lorabwd_layer_backward: the same work on the same
+ * stream, and right after the i-th kernel it enqueues (i < capacity) it
+ * records the caller-created HIP event events[i] on `stream` and fills
+ * records[i] with the kernel's name and the algorithmic HBM bytes and
+ * floating-point operations that kernel's step of the method has to move /
+ * perform at this shape (masked attention pairs, split-K partial sums and
+ * other implementation traffic are not counted).  *n_kernels receives the
+ * number of kernels enqueued.  With an event recorded just before the call,
+ * consecutive events bracket each kernel.
+ * ---------------------------------------------------------------------- */
+typedef struct lorabwd_kernel_record {
+  const char* name;  /* static string */
+  double alg_bytes;
+  double alg_flops;
+} lorabwd_kernel_record;
+
+int lorabwd_layer_backward_timed(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w,
+                                 const lorabwd_layer_saved* a, lorabwd_lora_state* q_state,
+                                 lorabwd_lora_state* v_state, const lorabwd_adamw* hp,
+                                 float* d_hidden, float* dq_pre_out, float* dv_out,
+                                 float* gnorm_sq, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream, hipEvent_t* events,
+                                 lorabwd_kernel_record* records, int capacity, int* n_kernels);
+
 #ifdef __cplusplus
 }
 #endif

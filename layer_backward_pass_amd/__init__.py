@@ -19,6 +19,7 @@ __all__ = [
     "lorabwd_ffn_backward", "lorabwd_lora_grad_adamw", "lorabwd_layer_backward",
     "lorabwd_attn_workspace_size", "lorabwd_ffn_workspace_size",
     "lorabwd_lora_workspace_size", "lorabwd_layer_workspace_size", "lorabwd_status_string",
+    "lorabwd_layer_backward_timed", "KernelRecord", "make_desc",
     "F32", "BF16", "ACT_SWIGLU", "ACT_RELU2",
 ]
 
@@ -30,7 +31,7 @@ EXPORTS = [
     "lorabwd_attn_workspace_size", "lorabwd_attn_backward",
     "lorabwd_ffn_workspace_size", "lorabwd_ffn_backward",
     "lorabwd_lora_workspace_size", "lorabwd_lora_grad_adamw",
-    "lorabwd_layer_workspace_size", "lorabwd_layer_backward",
+    "lorabwd_layer_workspace_size", "lorabwd_layer_backward", "lorabwd_layer_backward_timed",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -70,6 +71,11 @@ class LayerSaved(ctypes.Structure):
                 ("lora_q_h", c_vp), ("lora_v_h", c_vp)]
 
 
+class KernelRecord(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("alg_bytes", ctypes.c_double),
+                ("alg_flops", ctypes.c_double)]
+
+
 class LoraState(ctypes.Structure):
     _fields_ = [("rank", c_i64), ("A", c_vp), ("B", c_vp), ("m_a", c_vp), ("v_a", c_vp),
                 ("m_b", c_vp), ("v_b", c_vp)]
@@ -104,6 +110,11 @@ _SIGS = {
                                        ctypes.POINTER(LayerSaved), ctypes.POINTER(LoraState),
                                        ctypes.POINTER(LoraState), ctypes.POINTER(AdamW), c_vp,
                                        c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "lorabwd_layer_backward_timed": (c_int, [
+        ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), ctypes.POINTER(LayerSaved),
+        ctypes.POINTER(LoraState), ctypes.POINTER(LoraState), ctypes.POINTER(AdamW), c_vp, c_vp,
+        c_vp, c_vp, c_vp, c_size, c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(KernelRecord), c_int,
+        ctypes.POINTER(c_int)]),
 }
 
 
@@ -326,6 +337,10 @@ def lorabwd_lora_grad_adamw(dy, x, h, A, B, m_a, v_a, m_b, v_b, alpha, lr_a, lr_
         lr_b, beta1, beta2, eps, weight_decay, step, dt, _ptr(ws), wsb, _stream(stream)))
 
 
+def lorabwd_layer_backward_timed(desc, weights, saved, d_hidden, events, records, **kw):
+    return lorabwd_layer_backward(desc, weights, saved, d_hidden, timing=(events, records), **kw)
+
+
 def lorabwd_layer_workspace_size(desc):
     return load_library().lorabwd_layer_workspace_size(ctypes.byref(desc))
 
@@ -340,10 +355,14 @@ def make_desc(seq, kv_len, hidden, ffn, n_heads, n_kv_heads, head_dim, act=ACT_S
 
 def lorabwd_layer_backward(desc, weights, saved, d_hidden, q_state=None, v_state=None,
                            adamw=None, dq_pre_out=None, dv_out=None, gnorm_sq=None,
-                           stream=None):
+                           stream=None, timing=None):
     """desc: LayerDesc; weights / saved: dicts of tensors keyed like the C
     structs; q_state / v_state: dicts with A, B, m_a, v_a, m_b, v_b (or None);
-    adamw: AdamW or None.  d_hidden is updated in place."""
+    adamw: AdamW or None.  d_hidden is updated in place.
+
+    timing: None, or (events, records) = (ctypes array of hipEvent_t,
+    ctypes array of KernelRecord) to call lorabwd_layer_backward_timed; the
+    number of kernels enqueued is then returned."""
     d = desc
     tdt = _torch().bfloat16 if d.dtype == BF16 else _torch().float32
     S, L, H, I = d.seq, d.kv_len, d.hidden, d.ffn
@@ -386,11 +405,17 @@ def lorabwd_layer_backward(desc, weights, saved, d_hidden, q_state=None, v_state
     lib = load_library()
     need = lib.lorabwd_layer_workspace_size(ctypes.byref(d))
     ws, wsb = _workspace(need, d_hidden.device)
-    _check("lorabwd_layer_backward", lib.lorabwd_layer_backward(
-        ctypes.byref(d), ctypes.byref(w), ctypes.byref(a),
-        ctypes.byref(qs) if qs is not None else None,
-        ctypes.byref(vs) if vs is not None else None,
-        ctypes.byref(adamw) if adamw is not None else None,
-        _ptr(d_hidden), _ptr(dq_pre_out), _ptr(dv_out), _ptr(gnorm_sq), _ptr(ws), wsb,
-        _stream(stream)))
-    return d_hidden
+    args = (ctypes.byref(d), ctypes.byref(w), ctypes.byref(a),
+            ctypes.byref(qs) if qs is not None else None,
+            ctypes.byref(vs) if vs is not None else None,
+            ctypes.byref(adamw) if adamw is not None else None,
+            _ptr(d_hidden), _ptr(dq_pre_out), _ptr(dv_out), _ptr(gnorm_sq), _ptr(ws), wsb,
+            _stream(stream))
+    if timing is None:
+        _check("lorabwd_layer_backward", lib.lorabwd_layer_backward(*args))
+        return d_hidden
+    events, records = timing
+    n = ctypes.c_int(0)
+    _check("lorabwd_layer_backward_timed", lib.lorabwd_layer_backward_timed(
+        *args, events, records, len(records), ctypes.byref(n)))
+    return n.value

@@ -9,6 +9,30 @@
 
 using namespace lbp;
 
+namespace lbp {
+
+struct Recorder {
+  hipEvent_t* events;
+  lorabwd_kernel_record* records;
+  int capacity;
+  int count;
+};
+static thread_local Recorder* tl_recorder = nullptr;
+
+void mark(const char* name, double alg_bytes, double alg_flops, hipStream_t s) {
+  Recorder* r = tl_recorder;
+  if (r == nullptr) return;
+  if (r->count < r->capacity) {
+    (void)hipEventRecord(r->events[r->count], s);
+    r->records[r->count].name = name;
+    r->records[r->count].alg_bytes = alg_bytes;
+    r->records[r->count].alg_flops = alg_flops;
+  }
+  ++r->count;
+}
+
+}  // namespace lbp
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -497,6 +521,24 @@ int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weig
                               plan.scratch, stream));
   }
   return LORABWD_OK;
+}
+
+int lorabwd_layer_backward_timed(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w,
+                                 const lorabwd_layer_saved* a, lorabwd_lora_state* q_state,
+                                 lorabwd_lora_state* v_state, const lorabwd_adamw* hp,
+                                 float* d_hidden, float* dq_pre_out, float* dv_out,
+                                 float* gnorm_sq, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream, hipEvent_t* events,
+                                 lorabwd_kernel_record* records, int capacity, int* n_kernels) {
+  LBP_CHECK(capacity >= 0, LORABWD_ERR_ARG);
+  LBP_CHECK(capacity == 0 || (events != nullptr && records != nullptr), LORABWD_ERR_NULL);
+  Recorder rec{events, records, capacity, 0};
+  tl_recorder = &rec;
+  const int st = lorabwd_layer_backward(d, w, a, q_state, v_state, hp, d_hidden, dq_pre_out,
+                                        dv_out, gnorm_sq, workspace, workspace_bytes, stream);
+  tl_recorder = nullptr;
+  if (n_kernels) *n_kernels = rec.count;
+  return st;
 }
 
 }  // extern "C"

@@ -319,35 +319,54 @@ static hipError_t attn_launch(int64_t s_q, int64_t s_kv, int Hq, int Hkv, const 
                               const T* P, const T* K, const T* V, const T* ctx, float* dq,
                               float* dv, float scale, int causal, float* ws, hipStream_t s) {
   const int grp = Hq / Hkv;
+  const double es = sizeof(T);
   dim3 block(256);
   const size_t sm1 = ((size_t)grp * D + 64 * (D + 1)) * sizeof(float);
   const size_t sm2 = ((size_t)s_kv + 256) * sizeof(float);
   if (s_q == 1 && sm1 <= 64 * 1024 && sm2 <= 64 * 1024) {
     attn_dec_dadv_kernel<T, D><<<dim3((unsigned)((s_kv + 63) / 64), (unsigned)Hkv), block, sm1,
                                  s>>>(s_kv, Hq, grp, dctx, P, V, ws, dv);
+    mark("attn_dec_dadv",
+         (double)s_kv * Hkv * D * es + (double)Hq * s_kv * (es + 4) + (double)Hq * D * 4 +
+             (dv ? (double)s_kv * Hkv * D * 4 : 0.0),
+         4.0 * D * Hq * s_kv, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     attn_dec_dq_kernel<T, D><<<dim3((unsigned)Hq), block, sm2, s>>>(s_kv, Hq, grp, P, K, ws, dq,
                                                                      scale);
+    mark("attn_dec_dq",
+         (double)Hq * s_kv * (es + 4) + (double)s_kv * Hkv * D * es + (double)Hq * D * 4,
+         2.0 * D * Hq * s_kv, s);
     return hipGetLastError();
   }
+  // unmasked (query, key) pairs per head: the work the method must do
+  const double pairs = causal ? (double)s_q * (s_kv - s_q) + 0.5 * (double)s_q * (s_q + 1)
+                              : (double)s_q * s_kv;
+  const double pbytes = pairs * Hq * es, qbytes = (double)s_q * Hq * D;
+  const double kvbytes = (double)s_kv * Hkv * D;
   dim3 gq((unsigned)((s_q + AQ - 1) / AQ), (unsigned)Hq);
   if (ctx != nullptr) {
     attn_dq_kernel<T, D, 1><<<gq, block, 0, s>>>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, nullptr,
                                                   dq, scale, causal);
+    mark("attn_dq_mfma", pbytes + qbytes * (8 + es) + 2 * kvbytes * es, 4.0 * D * pairs * Hq, s);
   } else {
     attn_delta_kernel<T, D><<<dim3((unsigned)((s_q + 3) / 4), (unsigned)Hq), block, 0, s>>>(
         s_q, s_kv, Hq, grp, dctx, P, V, ws, causal);
+    mark("attn_delta", pbytes + qbytes * 4 + kvbytes * es + (double)Hq * s_q * 4,
+         2.0 * D * pairs * Hq, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     attn_dq_kernel<T, D, 0><<<gq, block, 0, s>>>(s_q, s_kv, Hq, grp, dctx, P, K, V, nullptr, ws,
                                                   dq, scale, causal);
+    mark("attn_dq_mfma", pbytes + qbytes * 8 + 2 * kvbytes * es + (double)Hq * s_q * 4,
+         4.0 * D * pairs * Hq, s);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || dv == nullptr) return e;
   constexpr int KB = 16 * (D >= 32 ? 2 : 4);
   attn_dv_kernel<T, D><<<dim3((unsigned)((s_kv + KB - 1) / KB), (unsigned)Hkv), block, 0, s>>>(
       s_q, s_kv, Hq, grp, dctx, P, dv, causal);
+  mark("attn_dv_mfma", pbytes + qbytes * 4 + kvbytes * 4, 2.0 * D * pairs * Hq, s);
   return hipGetLastError();
 }
 

@@ -279,10 +279,15 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
                                                       K1, ldb, out, ldo, kps, sstride);
   }
   hipError_t e = hipGetLastError();
+  mark(b_dt == F32 ? "gemm_f32_mfma" : "gemm_bf16_mfma",
+       (double)M * K * (a_dt == F32 ? 4 : 2) + (double)K * N * (b_dt == F32 ? 4 : 2) +
+           (double)M * N * 4,
+       2.0 * M * N * K, s);
   if (e != hipSuccess || nsp == 1) return e;
   int64_t blocks = cdiv(M * (N / 4), 256);
   if (blocks > 4096) blocks = 4096;
   splitk_reduce_kernel<<<dim3((unsigned)blocks), block, 0, s>>>(M, N, nsp, partials, C, ldc);
+  mark("splitk_reduce", 0, 0, s);
   return hipGetLastError();
 }
 
@@ -393,8 +398,10 @@ hipError_t launch_gemv(int64_t N, int64_t K, const float* x, const void* W1, con
     gemv_partial_kernel<bf16><<<grid, block, 0, s>>>(N, K, x, (const bf16*)W1, (const bf16*)W2,
                                                      K1, partials);
   hipError_t e = hipGetLastError();
+  mark("gemv_partial", (double)K * N * (w_dt == F32 ? 4 : 2) + K * 4.0 + N * 4.0, 2.0 * K * N, s);
   if (e != hipSuccess) return e;
   gemv_reduce_kernel<<<dim3((unsigned)cdiv(N, 256)), block, 0, s>>>(N, splits, partials, y);
+  mark("gemv_reduce", 0, 0, s);
   return hipGetLastError();
 }
 

@@ -9,6 +9,12 @@
 namespace lbp {
 
 enum DType { F32 = 0, BF16 = 1 };
+
+// Measurement hook: after each kernel launch a launcher calls mark() with the
+// kernel's name and its algorithmic HBM bytes and flops.  It does nothing
+// unless the calling thread is inside lorabwd_layer_backward_timed, which
+// then records a caller-owned event on the stream.
+void mark(const char* name, double alg_bytes, double alg_flops, hipStream_t s);
 enum ActKind { SWIGLU = 0, RELU2 = 1 };
 
 // ---- row-wise kernels (rowwise.hip)

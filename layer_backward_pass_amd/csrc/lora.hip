@@ -202,15 +202,20 @@ hipError_t launch_lora_adamw(int64_t rows, int64_t in_dim, int64_t out_dim, int6
   hipError_t e;
   if (rows > 0) {
     lora_g_kernel<<<dim3((unsigned)rows), block, 0, s>>>(out_dim, r, dy, B, scaling, g);
+    mark("lora_g", (double)rows * out_dim * 4 + (double)out_dim * rank * 4 + (double)rows * rank * 4,
+         2.0 * rows * out_dim * rank, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     lora_db_part_kernel<<<dim3((unsigned)cdiv(out_dim, 64), (unsigned)chunks), block, 0, s>>>(
         rows, out_dim, r, dy, h, dt, part);
+    mark("lora_db_part", (double)rows * out_dim * 4 + (double)rows * rank * (dt == F32 ? 4 : 2),
+         2.0 * rows * out_dim * rank, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // with no token rows the gradients are zero: a single zero "chunk"
   const int nb = (int)(rows > 0 ? chunks : 0);
   lora_db_update_kernel<<<dim3((unsigned)cdiv(out_dim * rank, 256)), block, 0, s>>>(
       out_dim * rank, nb, part, scaling, B, m_b, v_b, grad_b, hp);
+  mark("lora_adamw_b", (double)out_dim * rank * 4 * (6 + (grad_b ? 1 : 0)), 12.0 * out_dim * rank, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (rows > 0) {
     if (dt == F32)
@@ -219,14 +224,18 @@ hipError_t launch_lora_adamw(int64_t rows, int64_t in_dim, int64_t out_dim, int6
     else
       lora_da_part_kernel<bf16><<<dim3((unsigned)cdiv(in_dim, 64), (unsigned)chunks), block, 0,
                                   s>>>(rows, in_dim, r, g, (const bf16*)x, part);
+    mark("lora_da_part", (double)rows * in_dim * (dt == F32 ? 4 : 2) + (double)rows * rank * 4,
+         2.0 * rows * in_dim * rank, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int nsq = (int)cdiv(rank * in_dim, 256);
   lora_da_update_kernel<<<dim3((unsigned)nsq), block, 0, s>>>(rank * in_dim, nb, part, A, m_a,
                                                               v_a, grad_a, sq, hp);
+  mark("lora_adamw_a", (double)rank * in_dim * 4 * (6 + (grad_a ? 1 : 0)), 14.0 * rank * in_dim, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (gnorm_sq != nullptr) {
     lora_gnorm_kernel<<<dim3(1), dim3(64), 0, s>>>(nsq, sq, gnorm_sq);
+    mark("lora_gnorm", 8, (double)nsq, s);
     e = hipGetLastError();
   }
   return e;

@@ -75,6 +75,8 @@ hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, c
     else
       rmsnorm_bwd_kernel<bf16, 0><<<grid, block, 0, s>>>(n, (const bf16*)x, gamma, dy, dx, eps);
   }
+  mark("rmsnorm_bwd", (double)rows * n * ((xdt == F32 ? 4 : 2) + 8 + (accumulate ? 4 : 0)) + n * 4.0,
+       (double)rows * n * 8, s);
   return hipGetLastError();
 }
 
@@ -115,6 +117,7 @@ hipError_t launch_rope_bwd(int64_t rows, int64_t n_heads, int64_t head_dim, cons
   if ((int64_t)(threads / half) > n_heads) threads = (int)n_heads * half;
   rope_bwd_kernel<<<dim3((unsigned)rows), dim3(threads), 0, s>>>(n_heads, (int)head_dim, dy, dx,
                                                                    pos0, log2((double)base));
+  mark("rope_bwd", (double)rows * n_heads * head_dim * 8, (double)rows * n_heads * head_dim * 3, s);
   return hipGetLastError();
 }
 
@@ -201,6 +204,8 @@ hipError_t launch_act_bwd(int64_t rows, int64_t ffn, int act, const void* gate, 
     if (act == SWIGLU) act_launch<bf16, SWIGLU>(rows, ffn, gate, up, dhid, dgu, out_dt, s);
     else act_launch<bf16, RELU2>(rows, ffn, gate, up, dhid, dgu, out_dt, s);
   }
+  mark("act_bwd", (double)rows * ffn * (2 * (in_dt == F32 ? 4 : 2) + 4 + 2 * (out_dt == F32 ? 4 : 2)),
+       (double)rows * ffn * 12, s);
   return hipGetLastError();
 }
 
@@ -230,6 +235,7 @@ hipError_t launch_fill_zero(int64_t n, float* p, hipStream_t s) {
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   fill_zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(n, p);
+  mark("fill_zero", (double)n * 4, 0, s);
   return hipGetLastError();
 }
 
@@ -238,6 +244,7 @@ hipError_t launch_to_bf16(int64_t n, const float* src, void* dst, hipStream_t s)
   int64_t blocks = (n / 8 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   to_bf16_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(n, src, (uint16_t*)dst);
+  mark("to_bf16", (double)n * 6, 0, s);
   return hipGetLastError();
 }
 

@@ -121,10 +121,13 @@ def draw_timing_layer(cfg, layer=0):
     def n(name, shape, std=1.0):
         return (stream(cfg.index, layer, name).standard_normal(shape, dtype=f) * f(std))
 
+    wshapes = {"W_o": (H, qd), "W_gate": (I, H), "W_up": (I, H), "W_down": (H, I)}
+    if cfg.ternary:
+        weights = {k: ternary(cfg, layer, k, shp).astype(f) for k, shp in wshapes.items()}
+    else:
+        weights = {k: n(k, shp, 0.02) for k, shp in wshapes.items()}
     t = {
-        "d_out": n("d_out", (S, H)),
-        "W_o": n("W_o", (H, qd), 0.02), "W_gate": n("W_gate", (I, H), 0.02),
-        "W_up": n("W_up", (I, H), 0.02), "W_down": n("W_down", (H, I), 0.02),
+        "d_out": n("d_out", (S, H)), **weights,
         "gamma_ffn": (1 + n("gamma_ffn", (H,), 0.1)).astype(f),
         "attn_input": n("t_attn_input", (S, H)), "resid1": n("t_resid1", (S, H)),
         "gate": n("t_gate", (S, I)), "up": n("t_up", (S, I)),
@@ -132,9 +135,6 @@ def draw_timing_layer(cfg, layer=0):
         "P": causal_rows(stream(cfg.index, layer, "t_P"), cfg.n_heads, S, L, cfg.causal),
         "K": n("t_K", (L, kvd)), "V": n("t_V", (L, kvd)),
     }
-    if cfg.ternary:
-        for k, shp in (("W_o", (H, qd)), ("W_gate", (I, H)), ("W_up", (I, H)), ("W_down", (H, I))):
-            t[k] = ternary(cfg, layer, k, shp).astype(f)
     if cfg.sub_norms:
         t["hidden_pre"] = n("t_hidden_pre", (S, I))
         t["gamma_fsub"] = (1 + n("gamma_fsub", (I,), 0.1)).astype(f)

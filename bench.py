@@ -138,10 +138,20 @@ def kernel_profile(lbp, hip, cfg, copies, torch, reps):
     ev = hip.events(cap + 1)
     recs = (lbp.KernelRecord * cap)()
     stats = {}
+    # A read of 2 GiB enqueued ahead of each measured call keeps the GPU busy
+    # while the host enqueues the layer, so consecutive events bracket kernels
+    # that ran back to back (not host launch gaps).  It also evicts the
+    # Infinity Cache without leaving dirty lines behind (a write-filler would
+    # make the next kernel pay for its write-backs), so every kernel starts
+    # cold, as in the rotated timed loop.
+    filler = torch.zeros(1 << 29, dtype=torch.float32, device="cuda:0")
+    sink = torch.empty((), dtype=torch.float32, device="cuda:0")
+    torch.cuda.synchronize()
     for r in range(reps):
         cp = copies[r % len(copies)]
         cp["d_hidden"].copy_(cp["d_out"])
         for li, d in enumerate(reversed(cp["layers"])):
+            torch.sum(filler, dim=(0,), out=sink)
             hip.record(ev[cap], stream)
             n = layer_call(lbp, cfg, d, cp["d_hidden"], gnorm=cp["gnorm"],
                            timing=(ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)), recs))
@@ -155,10 +165,22 @@ def kernel_profile(lbp, hip, cfg, copies, torch, reps):
                                            "flops": recs[i].alg_flops})
                 s["ms"] += ms
                 s["n"] += 1
+    # cost of one event record between two kernels, measured the same way
+    # with no kernel in between; subtracted from every kernel's interval
+    gaps = []
+    for _ in range(20):
+        torch.sum(filler, dim=(0,), out=sink)
+        hip.record(ev[cap], stream)
+        hip.record(ev[0], stream)
+        hip.record(ev[1], stream)
+        torch.cuda.synchronize()
+        gaps.append(hip.elapsed_ms(ev[0], ev[1]))
+    gap = sorted(gaps)[len(gaps) // 2]
+    del filler, sink
     out = []
     for (i, name), s in sorted(stats.items()):
-        out.append({"index": i, "name": name, "avg_ms": s["ms"] / s["n"],
-                    "alg_bytes": s["bytes"], "alg_flops": s["flops"]})
+        out.append({"index": i, "name": name, "avg_ms": max(s["ms"] / s["n"] - gap, 1e-6),
+                    "alg_bytes": s["bytes"], "alg_flops": s["flops"], "event_gap_ms": gap})
     return out
 
 
@@ -194,6 +216,7 @@ def roofline(cfg, kernels):
         rl = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_GBps"],
               "unit": "GB/s", "frac": round(achieved / PEAK["hbm_GBps"], 4)}
     rl.update({"kernel": name, "avg_us": round(avg_s * 1e6, 2), "launches_per_step": g["launches"],
+               "event_gap_us": round(kernels[0]["event_gap_ms"] * 1e3, 2),
                "alg_bytes": nbytes, "alg_flops": flops, "traffic": traffic_for(cfg, name)})
     return rl
 

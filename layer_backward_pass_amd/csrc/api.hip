@@ -77,29 +77,31 @@ struct Carver {
 
 // ---------------------------------------------------------------- FFN
 struct FfnPlan {
-  float *dhid, *dn2, *partials;
+  float *dhid, *dn2, *partials;          // rows > 1
   void* dgu;
+  float *part1, *part2, *x2, *scal1, *scal2;  // rows == 1
   size_t bytes;
 };
 
+// rows == 1 runs the single-token GEMV chain (decode.hip); more rows run
+// the MFMA products with the elementwise kernels between them.
 FfnPlan ffn_plan(void* ws, int64_t rows, int64_t dim, int64_t ffn, int dt) {
   Carver c(ws);
-  FfnPlan p;
-  const bool vec = rows == 1;
-  const int gu_dt = vec ? F32 : dt;
-  p.dhid = c.take<float>((size_t)rows * ffn * 4);
-  p.dgu = c.take<void>((size_t)rows * 2 * ffn * esize(gu_dt));
-  p.dn2 = c.take<float>((size_t)rows * dim * 4);
-  size_t part;
-  if (vec) {
-    const size_t a = gemv_partial_bytes(ffn, dim), b = gemv_partial_bytes(dim, 2 * ffn);
-    part = a > b ? a : b;
+  FfnPlan p{};
+  if (rows == 1) {
+    p.part1 = c.take<float>(dgemv_part_bytes(ffn, dim));
+    p.part2 = c.take<float>(dgemv_part_bytes(dim, 2 * ffn));
+    p.x2 = c.take<float>((size_t)2 * ffn * 4);
+    p.scal1 = c.take<float>((size_t)2 * dgemv_nscal(ffn, dim) * 4);
+    p.scal2 = c.take<float>((size_t)2 * dgemv_nscal(dim, 2 * ffn) * 4);
   } else {
+    p.dhid = c.take<float>((size_t)rows * ffn * 4);
+    p.dgu = c.take<void>((size_t)rows * 2 * ffn * esize(dt));
+    p.dn2 = c.take<float>((size_t)rows * dim * 4);
     const size_t a = gemm_partial_bytes(rows, ffn, dim, dt);
     const size_t b = gemm_partial_bytes(rows, dim, 2 * ffn, dt);
-    part = a > b ? a : b;
+    p.partials = c.take<float>(a > b ? a : b);
   }
-  p.partials = c.take<float>(part);
   p.bytes = c.used;
   return p;
 }
@@ -139,13 +141,66 @@ hipError_t ffn_run(int64_t rows, int64_t dim, int64_t ffn, int act, const float*
   if (rows == 0) return hipSuccess;
   FfnPlan p = ffn_plan(ws, rows, dim, ffn, dt);
   hipError_t e;
-  const bool vec = rows == 1;
+  if (rows == 1) {
+    // 1. part1 = d_out W_down (+ the FFN sub-norm's row-sum shares)
+    GemvArgs g{};
+    g.N = ffn;
+    g.K = dim;
+    g.W1 = w_down;
+    g.x = d_out;
+    g.part = p.part1;
+    if (hidden_pre) {
+      g.ng = gamma_sub;
+      g.nx = hidden_pre;
+      g.scal = p.scal1;
+    }
+    if ((e = launch_dgemv(dt, dt, g, s)) != hipSuccess) return e;
+    // 2-3. dHid, sub-norm backward, activation backward -> [dGate | dUp]
+    RedArgs r{};
+    r.N = ffn;
+    r.splits = (int)dgemv_splits(ffn, dim);
+    r.part = p.part1;
+    r.y = p.x2;
+    if (hidden_pre) {
+      r.scal = p.scal1;
+      r.nscal = dgemv_nscal(ffn, dim);
+      r.nx = hidden_pre;
+      r.ngam = gamma_sub;
+      r.eps = eps;
+    }
+    r.gate = gate;
+    r.up = up_;
+    r.act = act;
+    if ((e = launch_dgemv_red(RED_ACT, dt, r, s)) != hipSuccess) return e;
+    // 4. part2 = [dGate | dUp] [W_gate; W_up] (+ the FFN norm's row-sum shares)
+    g = GemvArgs{};
+    g.N = dim;
+    g.K = 2 * ffn;
+    g.K1 = ffn;
+    g.W1 = w_gate;
+    g.W2 = w_up;
+    g.x = p.x2;
+    g.part = p.part2;
+    g.ng = gamma_ffn;
+    g.nx = resid1;
+    g.scal = p.scal2;
+    if ((e = launch_dgemv(dt, dt, g, s)) != hipSuccess) return e;
+    // 5. d_resid += rmsnorm_bwd(resid1, gamma_ffn, dN2)
+    r = RedArgs{};
+    r.N = dim;
+    r.splits = (int)dgemv_splits(dim, 2 * ffn);
+    r.part = p.part2;
+    r.y = d_resid;
+    r.scal = p.scal2;
+    r.nscal = dgemv_nscal(dim, 2 * ffn);
+    r.nx = resid1;
+    r.ngam = gamma_ffn;
+    r.eps = eps;
+    return launch_dgemv_red(RED_ACCUM, dt, r, s);
+  }
   // 1. dHid = d_out W_down
-  if (vec)
-    e = launch_gemv(ffn, dim, d_out, w_down, nullptr, dim, dt, p.dhid, p.partials, s);
-  else
-    e = launch_gemm(rows, ffn, dim, d_out, F32, dim, w_down, nullptr, dim, dt, ffn, p.dhid, ffn,
-                    p.partials, s);
+  e = launch_gemm(rows, ffn, dim, d_out, F32, dim, w_down, nullptr, dim, dt, ffn, p.dhid, ffn,
+                  p.partials, s);
   if (e != hipSuccess) return e;
   // 2. sub-norm backward
   if (hidden_pre) {
@@ -153,16 +208,11 @@ hipError_t ffn_run(int64_t rows, int64_t dim, int64_t ffn, int act, const float*
     if (e != hipSuccess) return e;
   }
   // 3. gated activation backward -> [dGate | dUp]
-  const int gu_dt = vec ? F32 : dt;
-  e = launch_act_bwd(rows, ffn, act, gate, up_, dt, p.dhid, p.dgu, gu_dt, s);
+  e = launch_act_bwd(rows, ffn, act, gate, up_, dt, p.dhid, p.dgu, dt, s);
   if (e != hipSuccess) return e;
   // 4. dN2 = [dGate | dUp] [W_gate; W_up]
-  if (vec)
-    e = launch_gemv(dim, 2 * ffn, (const float*)p.dgu, w_gate, w_up, ffn, dt, p.dn2, p.partials,
-                    s);
-  else
-    e = launch_gemm(rows, dim, 2 * ffn, p.dgu, gu_dt, 2 * ffn, w_gate, w_up, ffn, dt, dim, p.dn2,
-                    dim, p.partials, s);
+  e = launch_gemm(rows, dim, 2 * ffn, p.dgu, dt, 2 * ffn, w_gate, w_up, ffn, dt, dim, p.dn2, dim,
+                  p.partials, s);
   if (e != hipSuccess) return e;
   // 5. d_resid += rmsnorm_bwd(resid1, gamma_ffn, dN2)
   return launch_rmsnorm_bwd(rows, dim, resid1, dt, gamma_ffn, p.dn2, d_resid, eps, 1, s);
@@ -372,30 +422,165 @@ namespace {
 
 struct LayerPlan {
   float *dctx, *dq, *dv;
+  float *part2, *x2, *scal1, *scal2, *scal3, *dA;  // single-token chain only
   void* scratch;
   size_t bytes;
 };
 
 bool has_lora(const lorabwd_lora_state* s) { return s != nullptr && s->rank > 0; }
 
+// One token whose attention fits the decode kernels runs the fused GEMV
+// chain of decode.hip; everything else runs the general composition.
+bool use_decode_chain(const lorabwd_layer_desc* d) {
+  return d->seq == 1 && dec_attn_fits(d->kv_len, d->n_heads, d->n_kv_heads, d->head_dim);
+}
+
 LayerPlan layer_plan(void* ws, const lorabwd_layer_desc* d, int64_t rq, int64_t rv) {
-  const int64_t S = d->seq, L = d->kv_len, H = d->hidden;
+  const int64_t S = d->seq, L = d->kv_len, H = d->hidden, I = d->ffn;
   const int64_t qd = d->n_heads * d->head_dim, kvd = d->n_kv_heads * d->head_dim;
   Carver c(ws);
-  LayerPlan p;
+  LayerPlan p{};
   p.dctx = c.take<float>((size_t)S * qd * 4);
   p.dq = c.take<float>((size_t)S * qd * 4);
   p.dv = c.take<float>((size_t)L * kvd * 4);
-  size_t sc = ffn_plan(nullptr, S, H, d->ffn, d->dtype).bytes;
-  const size_t o = S == 1 ? gemv_partial_bytes(qd, H) : gemm_partial_bytes(S, qd, H, d->dtype);
-  const size_t a = up(attn_ws_bytes(S, L, d->n_heads, d->n_kv_heads, d->head_dim));
   const size_t lq = rq > 0 ? up(lora_ws_bytes(S, H, qd, rq)) : 0;
   const size_t lv = rv > 0 ? up(lora_ws_bytes(S, H, kvd, rv)) : 0;
-  for (size_t v : {o, a, lq, lv})
-    if (v > sc) sc = v;
+  size_t sc = lq > lv ? lq : lv;
+  if (use_decode_chain(d)) {
+    p.part2 = c.take<float>(dgemv_part_bytes(H, 2 * I));
+    p.x2 = c.take<float>((size_t)2 * I * 4);
+    p.scal1 = c.take<float>((size_t)2 * dgemv_nscal(I, H) * 4);
+    p.scal2 = c.take<float>((size_t)2 * dgemv_nscal(H, 2 * I) * 4);
+    p.scal3 = c.take<float>((size_t)2 * dgemv_nscal(qd, H) * 4);
+    p.dA = c.take<float>(dec_attn_ws_bytes(L, d->n_heads, d->head_dim));
+    // part1 and part3 share the scratch region (part1 is dead once the
+    // second stream has reduced it), and so do the adapters afterwards
+    for (size_t v : {dgemv_part_bytes(I, H), dgemv_part_bytes(qd, H)})
+      if (v > sc) sc = v;
+  } else {
+    const size_t f = ffn_plan(nullptr, S, H, I, d->dtype).bytes;
+    const size_t o = S == 1 ? dgemv_part_bytes(qd, H) : gemm_partial_bytes(S, qd, H, d->dtype);
+    const size_t a = up(attn_ws_bytes(S, L, d->n_heads, d->n_kv_heads, d->head_dim));
+    for (size_t v : {f, o, a})
+      if (v > sc) sc = v;
+  }
   p.scratch = c.take<void>(sc);
   p.bytes = c.used;
   return p;
+}
+
+// The single-token layer: three weight streams, each followed by a light
+// reduction that also applies the elementwise step after it (decode.hip).
+hipError_t decode_chain(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w,
+                        const lorabwd_layer_saved* a, const LayerPlan& p, float* d_hidden,
+                        float* dqp, float* dv, hipStream_t s) {
+  const int64_t L = d->kv_len, H = d->hidden, I = d->ffn;
+  const int64_t qd = d->n_heads * d->head_dim;
+  const int dt = d->dtype;
+  const bool sub = d->sub_norms != 0;
+  float* part13 = (float*)p.scratch;
+  hipError_t e;
+  // part1 = d_out W_down, with the FFN sub-norm's row-sum shares
+  GemvArgs g{};
+  g.N = I;
+  g.K = H;
+  g.W1 = w->w_down;
+  g.x = d_hidden;
+  g.part = part13;
+  if (sub) {
+    g.ng = w->gamma_fsub;
+    g.nx = a->hidden_pre;
+    g.scal = p.scal1;
+  }
+  if ((e = launch_dgemv(dt, dt, g, s)) != hipSuccess) return e;
+  // dHid -> sub-norm backward -> activation backward -> x2 = [dGate | dUp]
+  RedArgs r{};
+  r.N = I;
+  r.splits = (int)dgemv_splits(I, H);
+  r.part = part13;
+  r.y = p.x2;
+  if (sub) {
+    r.scal = p.scal1;
+    r.nscal = dgemv_nscal(I, H);
+    r.nx = a->hidden_pre;
+    r.ngam = w->gamma_fsub;
+    r.eps = d->eps;
+  }
+  r.gate = a->gate;
+  r.up = a->up;
+  r.act = d->act;
+  if ((e = launch_dgemv_red(RED_ACT, dt, r, s)) != hipSuccess) return e;
+  // part2 = x2 [W_gate; W_up], with the FFN norm's row-sum shares
+  g = GemvArgs{};
+  g.N = H;
+  g.K = 2 * I;
+  g.K1 = I;
+  g.W1 = w->w_gate;
+  g.W2 = w->w_up;
+  g.x = p.x2;
+  g.part = p.part2;
+  g.ng = w->gamma_ffn;
+  g.nx = a->resid1;
+  g.scal = p.scal2;
+  if ((e = launch_dgemv(dt, dt, g, s)) != hipSuccess) return e;
+  // d_hidden = d_out + rmsnorm_bwd(resid1, gamma_ffn, dN2)   (dH1, in place)
+  r = RedArgs{};
+  r.N = H;
+  r.splits = (int)dgemv_splits(H, 2 * I);
+  r.part = p.part2;
+  r.y = d_hidden;
+  r.scal = p.scal2;
+  r.nscal = dgemv_nscal(H, 2 * I);
+  r.nx = a->resid1;
+  r.ngam = w->gamma_ffn;
+  r.eps = d->eps;
+  if ((e = launch_dgemv_red(RED_ACCUM, dt, r, s)) != hipSuccess) return e;
+  // part3 = dH1 W_o, with the attention sub-norm's row-sum shares
+  g = GemvArgs{};
+  g.N = qd;
+  g.K = H;
+  g.W1 = w->w_o;
+  g.x = d_hidden;
+  g.part = part13;
+  if (sub) {
+    g.ng = w->gamma_asub;
+    g.nx = a->ctx;
+    g.scal = p.scal3;
+  }
+  if ((e = launch_dgemv(dt, dt, g, s)) != hipSuccess) return e;
+  // dCtx (sub-norm backward applied)
+  r = RedArgs{};
+  r.N = qd;
+  r.splits = (int)dgemv_splits(qd, H);
+  r.part = part13;
+  r.y = p.dctx;
+  if (sub) {
+    r.scal = p.scal3;
+    r.nscal = dgemv_nscal(qd, H);
+    r.nx = a->ctx;
+    r.ngam = w->gamma_asub;
+    r.eps = d->eps;
+  }
+  if ((e = launch_dgemv_red(RED_STORE, dt, r, s)) != hipSuccess) return e;
+  // attention backward, inverse RoPE at the token's position
+  DecAttnArgs at{};
+  at.s_kv = L;
+  at.Hq = (int)d->n_heads;
+  at.grp = (int)(d->n_heads / d->n_kv_heads);
+  at.dctx = p.dctx;
+  at.P = a->P;
+  at.K = a->K;
+  at.V = a->V;
+  at.ctx = a->ctx;
+  at.dA = p.dA;
+  at.dq_part = p.dA;
+  at.dv = dv;
+  at.dq = dqp;
+  at.scale = d->attn_scale;
+  at.rope = 1;
+  at.pos = d->pos0;
+  at.log2_base = log2((double)d->rope_base);
+  return launch_dec_attn(dt, (int)d->head_dim, at, s);
 }
 
 int desc_validate(const lorabwd_layer_desc* d) {
@@ -418,6 +603,7 @@ int desc_validate(const lorabwd_layer_desc* d) {
 
 size_t lorabwd_layer_workspace_size(const lorabwd_layer_desc* d) {
   if (desc_validate(d) != LORABWD_OK) return 0;
+  if (d->seq == 0) return 0;
   // sized for the largest adapter rank the library accepts, so the size does
   // not depend on the adapter states
   return layer_plan(nullptr, d, 64, 64).bytes;
@@ -487,23 +673,39 @@ int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weig
   }
 
   // ---- all arguments valid: enqueue
-  // FFN half, residual-stream gradient in place: d_hidden <- dH1
-  LBP_HIP(ffn_run(S, H, I, d->act, d_hidden, w->w_down, w->w_gate, w->w_up, a->gate, a->up,
-                  sub ? a->hidden_pre : nullptr, sub ? w->gamma_fsub : nullptr, a->resid1,
-                  w->gamma_ffn, d_hidden, d->eps, dt, plan.scratch, stream));
-  // O-projection backward: dCtx = dH1 W_o
-  if (S == 1)
-    LBP_HIP(launch_gemv(qd, H, d_hidden, w->w_o, nullptr, H, dt, plan.dctx, (float*)plan.scratch,
-                        stream));
-  else
-    LBP_HIP(launch_gemm(S, qd, H, d_hidden, F32, H, w->w_o, nullptr, H, dt, qd, plan.dctx, qd,
-                        (float*)plan.scratch, stream));
-  if (sub)
-    LBP_HIP(launch_rmsnorm_bwd(S, qd, a->ctx, dt, w->gamma_asub, plan.dctx, plan.dctx, d->eps, 0,
-                               stream));
-  LBP_HIP(launch_attn_bwd(S, L, Hq, Hkv, D, plan.dctx, a->P, a->K, a->V, a->ctx, dt, plan.dq, dv,
-                          d->attn_scale, d->causal, plan.scratch, stream));
-  LBP_HIP(launch_rope_bwd(S, Hq, D, plan.dq, dqp, d->pos0, d->rope_base, stream));
+  if (use_decode_chain(d)) {
+    LBP_HIP(decode_chain(d, w, a, plan, d_hidden, dqp, dv, stream));
+  } else {
+    // FFN half, residual-stream gradient in place: d_hidden <- dH1
+    LBP_HIP(ffn_run(S, H, I, d->act, d_hidden, w->w_down, w->w_gate, w->w_up, a->gate, a->up,
+                    sub ? a->hidden_pre : nullptr, sub ? w->gamma_fsub : nullptr, a->resid1,
+                    w->gamma_ffn, d_hidden, d->eps, dt, plan.scratch, stream));
+    // O-projection backward: dCtx = dH1 W_o
+    if (S == 1) {
+      GemvArgs g{};
+      g.N = qd;
+      g.K = H;
+      g.W1 = w->w_o;
+      g.x = d_hidden;
+      g.part = (float*)plan.scratch;
+      LBP_HIP(launch_dgemv(dt, dt, g, stream));
+      RedArgs r{};
+      r.N = qd;
+      r.splits = (int)dgemv_splits(qd, H);
+      r.part = (float*)plan.scratch;
+      r.y = plan.dctx;
+      LBP_HIP(launch_dgemv_red(RED_STORE, dt, r, stream));
+    } else {
+      LBP_HIP(launch_gemm(S, qd, H, d_hidden, F32, H, w->w_o, nullptr, H, dt, qd, plan.dctx, qd,
+                          (float*)plan.scratch, stream));
+    }
+    if (sub)
+      LBP_HIP(launch_rmsnorm_bwd(S, qd, a->ctx, dt, w->gamma_asub, plan.dctx, plan.dctx, d->eps, 0,
+                                 stream));
+    LBP_HIP(launch_attn_bwd(S, L, Hq, Hkv, D, plan.dctx, a->P, a->K, a->V, a->ctx, dt, plan.dq, dv,
+                            d->attn_scale, d->causal, plan.scratch, stream));
+    LBP_HIP(launch_rope_bwd(S, Hq, D, plan.dq, dqp, d->pos0, d->rope_base, stream));
+  }
   if (lq) {
     const AdamHP h = make_hp(lr_a, lr_b, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, step);
     LBP_HIP(launch_lora_adamw(S, H, qd, qs->rank, dqp, a->attn_input, a->lora_q_h, dt, qs->A,

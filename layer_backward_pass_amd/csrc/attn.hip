@@ -18,9 +18,7 @@
 //                   see those keys.
 //   attn_delta_kernel  delta = rowsum(P o dA) formed from P directly, for
 //                   callers that do not pass ctx.
-// Decode path (s_q = 1): attn_dec_dadv_kernel (dA and dV per block of 64
-// cache slots and KV head; the group's heads share each V row read) and
-// attn_dec_dq_kernel (delta, dS and dQ per head).
+// One query row (decode) goes to the kernels in decode.hip.
 #include "common.h"
 #include "kernels.h"
 
@@ -229,89 +227,11 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(int64_t s_q, int64_t s_
   if (lane == 0) delta[(int64_t)h * s_q + i] = s;
 }
 
-// Decode, step 1: dA[h, j] = dCtx_h . V_g[j] and dV[j, g] = sum_{h in g}
-// P[h, j] dCtx_h for a block of 64 cache slots of KV head g.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_dec_dadv_kernel(int64_t s_kv, int Hq, int grp,
-                                                            const float* __restrict__ dctx,
-                                                            const T* __restrict__ P,
-                                                            const T* __restrict__ V,
-                                                            float* __restrict__ dA,
-                                                            float* __restrict__ dv) {
-  extern __shared__ float smem[];
-  float* dC = smem;              // [grp][D]
-  float* Vs = smem + grp * D;    // [64][D + 1]
-  const int t = threadIdx.x;
-  const int g = blockIdx.y;
-  const int64_t k0 = (int64_t)blockIdx.x * 64;
-  const int64_t ldk = (int64_t)(Hq / grp) * D;
-  for (int e = t; e < grp * D; e += 256) dC[e] = dctx[(int64_t)g * grp * D + e];
-  for (int e = t; e < 64 * D; e += 256) {
-    const int kr = e / D, d = e - kr * D;
-    const int64_t key = k0 + kr;
-    Vs[kr * (D + 1) + d] = key < s_kv ? Act<T>::ld(V, key * ldk + g * D + d) : 0.f;
-  }
-  __syncthreads();
-  for (int pr = t; pr < grp * 64; pr += 256) {
-    const int hh = pr / 64, kr = pr - hh * 64;
-    const int64_t key = k0 + kr;
-    float s = 0.f;
-    for (int d = 0; d < D; ++d) s += dC[hh * D + d] * Vs[kr * (D + 1) + d];
-    if (key < s_kv) dA[(int64_t)(g * grp + hh) * s_kv + key] = s;
-  }
-  if (dv == nullptr) return;
-  for (int e = t; e < 64 * D; e += 256) {
-    const int kr = e / D, d = e - kr * D;
-    const int64_t key = k0 + kr;
-    if (key >= s_kv) continue;
-    float s = 0.f;
-    for (int hh = 0; hh < grp; ++hh)
-      s += Act<T>::ld(P, (int64_t)(g * grp + hh) * s_kv + key) * dC[hh * D + d];
-    dv[key * ldk + g * D + d] = s;
-  }
-}
-
-// Decode, step 2 (one workgroup per head): delta = sum_j P dA, dS = P (dA -
-// delta), dq = scale sum_j dS[j] K_g[j].
-template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_dec_dq_kernel(int64_t s_kv, int Hq, int grp,
-                                                          const T* __restrict__ P,
-                                                          const T* __restrict__ K,
-                                                          const float* __restrict__ dA,
-                                                          float* __restrict__ dq, float scale) {
-  extern __shared__ float smem[];
-  float* dS = smem;            // [s_kv]
-  float* part = smem + s_kv;   // [256]
-  __shared__ float red[4];
-  const int t = threadIdx.x;
-  const int h = blockIdx.x, g = h / grp;
-  const int64_t ldk = (int64_t)(Hq / grp) * D;
-  const T* Ph = P + (int64_t)h * s_kv;
-  const float* dAh = dA + (int64_t)h * s_kv;
-  float s = 0.f;
-  for (int64_t j = t; j < s_kv; j += 256) s += Act<T>::ld(Ph, j) * dAh[j];
-  const float delta = block_sum<4>(s, red);
-  for (int64_t j = t; j < s_kv; j += 256) dS[j] = Act<T>::ld(Ph, j) * (dAh[j] - delta);
-  __syncthreads();
-  constexpr int NP = 256 / D;
-  const int d = t % D, pi = t / D;
-  float a = 0.f;
-  for (int64_t j = pi; j < s_kv; j += NP) a += dS[j] * Act<T>::ld(K, j * ldk + g * D + d);
-  part[t] = a;
-  __syncthreads();
-  if (t < D) {
-    float o = 0.f;
-    for (int p = 0; p < NP; ++p) o += part[p * D + t];
-    dq[(int64_t)h * D + t] = scale * o;
-  }
-}
-
 size_t attn_ws_bytes(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_kv_heads,
                      int64_t head_dim) {
   (void)n_kv_heads;
-  (void)head_dim;
-  const int64_t n = s_q == 1 ? s_kv : s_q;
-  return (size_t)n_heads * n * sizeof(float);
+  if (s_q == 1) return dec_attn_ws_bytes(s_kv, n_heads, head_dim);
+  return (size_t)n_heads * s_q * sizeof(float);
 }
 
 template <typename T, int D>
@@ -321,24 +241,6 @@ static hipError_t attn_launch(int64_t s_q, int64_t s_kv, int Hq, int Hkv, const 
   const int grp = Hq / Hkv;
   const double es = sizeof(T);
   dim3 block(256);
-  const size_t sm1 = ((size_t)grp * D + 64 * (D + 1)) * sizeof(float);
-  const size_t sm2 = ((size_t)s_kv + 256) * sizeof(float);
-  if (s_q == 1 && sm1 <= 64 * 1024 && sm2 <= 64 * 1024) {
-    attn_dec_dadv_kernel<T, D><<<dim3((unsigned)((s_kv + 63) / 64), (unsigned)Hkv), block, sm1,
-                                 s>>>(s_kv, Hq, grp, dctx, P, V, ws, dv);
-    mark("attn_dec_dadv",
-         (double)s_kv * Hkv * D * es + (double)Hq * s_kv * (es + 4) + (double)Hq * D * 4 +
-             (dv ? (double)s_kv * Hkv * D * 4 : 0.0),
-         4.0 * D * Hq * s_kv, s);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    attn_dec_dq_kernel<T, D><<<dim3((unsigned)Hq), block, sm2, s>>>(s_kv, Hq, grp, P, K, ws, dq,
-                                                                     scale);
-    mark("attn_dec_dq",
-         (double)Hq * s_kv * (es + 4) + (double)s_kv * Hkv * D * es + (double)Hq * D * 4,
-         2.0 * D * Hq * s_kv, s);
-    return hipGetLastError();
-  }
   // unmasked (query, key) pairs per head: the work the method must do
   const double pairs = causal ? (double)s_q * (s_kv - s_q) + 0.5 * (double)s_q * (s_q + 1)
                               : (double)s_q * s_kv;
@@ -397,6 +299,23 @@ hipError_t launch_attn_bwd(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n
   if (s_q == 0) {
     if (dv != nullptr) return launch_fill_zero(s_kv * n_kv_heads * head_dim, dv, s);
     return hipSuccess;
+  }
+  if (s_q == 1 && dec_attn_fits(s_kv, n_heads, n_kv_heads, head_dim)) {
+    DecAttnArgs a{};
+    a.s_kv = s_kv;
+    a.Hq = (int)n_heads;
+    a.grp = (int)(n_heads / n_kv_heads);
+    a.dctx = dctx;
+    a.P = P;
+    a.K = K;
+    a.V = V;
+    a.ctx = ctx;
+    a.dA = (float*)ws;
+    a.dq_part = (float*)ws;
+    a.dv = dv;
+    a.dq = dq;
+    a.scale = scale;
+    return launch_dec_attn(dt, (int)head_dim, a, s);
   }
   if (dt == F32)
     return attn_dispatch_d<float>(s_q, s_kv, (int)n_heads, (int)n_kv_heads, (int)head_dim, dctx,

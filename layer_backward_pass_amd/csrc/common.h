@@ -80,4 +80,22 @@ __device__ __forceinline__ floatx4 mfma16x16x32bf16(ushortx8 a, ushortx8 b, floa
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Gated activation backward of one element.
+//   SwiGLU (entrenar wgpu_backward.rs, "SiLU backward"): s = sigmoid(g),
+//     dGate = dH up s (1 + g (1 - s)),  dUp = dH g s
+//   ReLU^2 x up (Hesper "FFN Backward GPU Kernels", "ReLU²×Mul Backward"):
+//     dGate = dH up 2 max(0,g),  dUp = dH max(0,g)^2
+template <int ACT>
+__device__ __forceinline__ void act_bwd1(float g, float u, float dh, float& dg, float& du) {
+  if (ACT == 0) {
+    const float sg = 1.0f / (1.0f + expf(-g));
+    dg = dh * u * sg * (1.0f + g * (1.0f - sg));
+    du = dh * g * sg;
+  } else {
+    const float r = fmaxf(g, 0.0f);
+    dg = dh * u * 2.0f * r;
+    du = dh * r * r;
+  }
+}
+
 }  // namespace lbp

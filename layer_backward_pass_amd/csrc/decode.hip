@@ -1,0 +1,758 @@
+// Single-token (decode) backward.  Every transposed product is a GEMV over
+// a weight matrix streamed from HBM once, so the layer is organised around
+// the three weight streams (W_down, [W_gate; W_up], W_o) and everything
+// elementwise rides along with them:
+//
+//   dgemv<PLAIN>  part1 = d_out W_down over row chunks; every workgroup also
+//                 emits its share of <dHid*gamma_fsub, hidden_pre> (the
+//                 FFN sub-norm's row sum is linear in dHid) and, for the
+//                 first chunk, of sum hidden_pre^2
+//   dgemv<ACT>    prologue: dHid for its rows from part1, sub-norm backward,
+//                 ReLU^2 / SwiGLU backward; part2 = [dGate|dUp][W_gate;W_up]
+//                 plus the FFN-norm shares over resid1
+//   dgemv<RESID>  prologue: dN2 for its rows from part2, dH1 = d_out +
+//                 rmsnorm_bwd(resid1, gamma_ffn, dN2); part3 = dH1 W_o plus
+//                 the attention sub-norm shares over ctx
+//   dgemv_red     dCtx = sum of part3, attention sub-norm backward applied;
+//                 dH1 copied to the caller's d_hidden
+//   dec_attn1     dA = dCtx V^T and dV = P^T dCtx per block of keys
+//   dec_attn2     per head: delta, dS = P (dA - delta), dq = scale dS K and
+//                 the inverse RoPE rotation at the token's position
+//
+// Hesper "FFN Backward GPU Kernels" (the five steps of "Backward
+// (reverse)", "ReLU²×Mul Backward") and "Attention Backward GPU Kernels"
+// ("Gradient Flow", "RMSNorm Backward", "Attention Apply Backward",
+// "Softmax Backward", "Attention Score Backward", "RoPE Backward").
+//
+// GEMV layout: a workgroup owns 256 adjacent output columns (one float4 per
+// lane) and a chunk of rows; its four waves split the rows, keep 8 rows of
+// 16-byte loads in flight each, and add their results in a fixed order.
+// Every reduction has a fixed order, so results are bitwise reproducible.
+#include "common.h"
+#include "kernels.h"
+
+namespace lbp {
+
+constexpr int DG_COLS = 256;
+constexpr int DG_U = 8;
+constexpr int DR_COLS = 64;      // columns per reduce workgroup (16 lanes x float4)
+constexpr int DG_STAGE = 8192;   // floats of LDS staging for the prologue reduction
+
+static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+__device__ __forceinline__ void fma4(float4& a, float x, const float4& w) {
+  a.x += x * w.x;
+  a.y += x * w.y;
+  a.z += x * w.z;
+  a.w += x * w.w;
+}
+
+// RMSNorm constants from per-workgroup shares sc[2*i] (dot), sc[2*i+1]
+// (sum of squares), i < n: every thread gets inv_r = 1/sqrt(ss/len + eps)
+// and c = dot / (len r^2).  Fixed order: strided per-thread sums (8 loads in
+// flight), then the block tree.  All 256 threads must call it.
+__device__ __forceinline__ void norm_consts_block(const float* sc, int64_t n, int64_t len,
+                                                  float eps, float* red, float& inv_r,
+                                                  float& c) {
+  float dot = 0.f, ss = 0.f;
+  for (int64_t i0 = threadIdx.x; i0 < n; i0 += 2048) {
+    float2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = i0 + 256 * u;
+      v[u] = i < n ? *reinterpret_cast<const float2*>(sc + 2 * i) : make_float2(0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      dot += v[u].x;
+      ss += v[u].y;
+    }
+  }
+  dot = block_sum<4>(dot, red);
+  ss = block_sum<4>(ss, red);
+  const float nf = (float)len;
+  const float r2 = ss / nf + eps;
+  inv_r = 1.0f / sqrtf(r2);
+  c = dot / (nf * r2);
+}
+
+template <typename TW, typename TA>
+__global__ __launch_bounds__(256) void dgemv_kernel(GemvArgs a) {
+  extern __shared__ float xs[];  // [kc] the input vector of this chunk
+  __shared__ float4 red4[3][64];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int64_t kb = (int64_t)blockIdx.y * a.kc;
+  const int64_t ke = min(a.K, kb + a.kc);
+  const int R = (int)(ke - kb);
+  const int64_t n = (int64_t)blockIdx.x * DG_COLS + lane * 4;
+  const int64_t per = (R + 3) / 4;
+  const int64_t r0 = kb + w * per, r1 = min(ke, r0 + per);
+  const bool nok = n < a.N;
+  // two named register buffers (indices known at compile time): the next
+  // 8 rows are in flight while the current 8 are multiplied
+  float4 wa[DG_U], wb[DG_U];
+  auto fetch = [&](float4 (&wv)[DG_U], int64_t r) {
+#pragma unroll
+    for (int u = 0; u < DG_U; ++u) {
+      const int64_t rr = r + u;
+      if (nok && rr < r1) {
+        const TW* wp = rr < a.K1 ? (const TW*)a.W1 + rr * a.N : (const TW*)a.W2 + (rr - a.K1) * a.N;
+        wv[u] = Act<TW>::ld4(wp, n);
+      } else {
+        wv[u] = make_float4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto consume = [&](const float4 (&wv)[DG_U], int64_t r, float4& acc) {
+#pragma unroll
+    for (int u = 0; u < DG_U; ++u) {
+      const float xv = (r + u < r1) ? xs[r + u - kb] : 0.f;
+      fma4(acc, xv, wv[u]);
+    }
+  };
+  // the first rows are in flight before the input vector arrives
+  fetch(wa, r0);
+  for (int r = t; r < R; r += 256) xs[r] = a.x[kb + r];
+  __syncthreads();
+  float4 acc = make_float4(0, 0, 0, 0);
+  for (int64_t r = r0; r < r1; r += 2 * DG_U) {
+    if (r + DG_U < r1) fetch(wb, r + DG_U);
+    consume(wa, r, acc);
+    if (r + DG_U < r1) {
+      if (r + 2 * DG_U < r1) fetch(wa, r + 2 * DG_U);
+      consume(wb, r + DG_U, acc);
+    }
+  }
+  if (w > 0) red4[w - 1][lane] = acc;
+  __syncthreads();
+  if (w == 0) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      acc.x += red4[i][lane].x;
+      acc.y += red4[i][lane].y;
+      acc.z += red4[i][lane].z;
+      acc.w += red4[i][lane].w;
+    }
+    if (nok) *reinterpret_cast<float4*>(a.part + (int64_t)blockIdx.y * a.N + n) = acc;
+    if (a.ng != nullptr) {
+      // this workgroup's share of the row sums of the norm that consumes y
+      float dot = 0.f, ss = 0.f;
+      if (nok) {
+        const float4 x = Act<TA>::ld4((const TA*)a.nx, n);
+        const float4 g = *reinterpret_cast<const float4*>(a.ng + n);
+        dot = acc.x * g.x * x.x + acc.y * g.y * x.y + acc.z * g.z * x.z + acc.w * g.w * x.w;
+        if (blockIdx.y == 0) ss = x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+      }
+      dot = wave_sum(dot);
+      ss = wave_sum(ss);
+      if (lane == 0) {
+        const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+        a.scal[2 * wg] = dot;
+        a.scal[2 * wg + 1] = ss;
+      }
+    }
+  }
+}
+
+// y = sum over row chunks of part (a tile of up to 128 chunks in flight per
+// 16-thread group; chunk order fixed), then the elementwise step of the
+// path at that point (see RedMode), with RMSNorm constants from the
+// producer's per-workgroup shares.  A workgroup owns 64 columns.
+template <typename TA, int MODE>
+__global__ __launch_bounds__(256) void dgemv_red_kernel(RedArgs a) {
+  __shared__ float4 red[16][16];
+  __shared__ float rs[2][4];
+  const int t = threadIdx.x, c = t & 15, g = t >> 4;
+  const int64_t n = (int64_t)blockIdx.x * DR_COLS + c * 4;
+  const bool nok = n < a.N;
+  const bool norm = a.scal != nullptr;
+  // ---- every global load first: partial sums, norm shares, elementwise inputs
+  float4 v[8];
+  float2 sv[8];
+  float4 xin = make_float4(0, 0, 0, 0), gin = xin, gt = xin, upv = xin, prev = xin;
+  const int first_tile = a.splits < 128 ? a.splits : 128;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int i = g + 16 * u;
+    v[u] = (nok && i < first_tile) ? *reinterpret_cast<const float4*>(a.part + (int64_t)i * a.N + n)
+                                   : make_float4(0, 0, 0, 0);
+  }
+  if (norm) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = t + 256 * u;
+      sv[u] = i < a.nscal ? *reinterpret_cast<const float2*>(a.scal + 2 * i) : make_float2(0.f, 0.f);
+    }
+  }
+  if (t < 16 && nok) {
+    if (norm) {
+      xin = Act<TA>::ld4((const TA*)a.nx, n);
+      gin = *reinterpret_cast<const float4*>(a.ngam + n);
+    }
+    if (MODE == RED_ACT) {
+      gt = Act<TA>::ld4((const TA*)a.gate, n);
+      upv = Act<TA>::ld4((const TA*)a.up, n);
+    }
+    if (MODE == RED_ACCUM) prev = *reinterpret_cast<const float4*>(a.y + n);
+  }
+  // ---- partial sums over row chunks (first tile in flight above)
+  float4 s = make_float4(0, 0, 0, 0);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    s.x += v[u].x;
+    s.y += v[u].y;
+    s.z += v[u].z;
+    s.w += v[u].w;
+  }
+  for (int i0 = g + 128; i0 < a.splits; i0 += 128) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + 16 * u;
+      v[u] = (nok && i < a.splits) ? *reinterpret_cast<const float4*>(a.part + (int64_t)i * a.N + n)
+                                   : make_float4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      s.x += v[u].x;
+      s.y += v[u].y;
+      s.z += v[u].z;
+      s.w += v[u].w;
+    }
+  }
+  red[g][c] = s;
+  float inv_r = 1.f, cc = 0.f;
+  if (norm) {
+    float dot = 0.f, ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      dot += sv[u].x;
+      ss += sv[u].y;
+    }
+    for (int64_t i0 = t + 2048; i0 < a.nscal; i0 += 2048) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = i0 + 256 * u;
+        sv[u] = i < a.nscal ? *reinterpret_cast<const float2*>(a.scal + 2 * i) : make_float2(0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        dot += sv[u].x;
+        ss += sv[u].y;
+      }
+    }
+    dot = block_sum<4>(dot, rs[0]);
+    ss = block_sum<4>(ss, rs[1]);
+    const float nf = (float)a.N;
+    const float r2 = ss / nf + a.eps;
+    inv_r = 1.0f / sqrtf(r2);
+    cc = dot / (nf * r2);
+  } else {
+    __syncthreads();
+  }
+  if (t < 16 && nok) {
+    float4 y = red[0][t];
+    for (int i = 1; i < 16; ++i) {
+      y.x += red[i][t].x;
+      y.y += red[i][t].y;
+      y.z += red[i][t].z;
+      y.w += red[i][t].w;
+    }
+    float o[4] = {y.x, y.y, y.z, y.w};
+    if (norm) {
+      const float xv[4] = {xin.x, xin.y, xin.z, xin.w}, gv[4] = {gin.x, gin.y, gin.z, gin.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = (o[q] * gv[q] - xv[q] * cc) * inv_r;
+    }
+    if (MODE == RED_ACT) {
+      // o = dHid: gated activation backward -> y[n] = dGate, y[N + n] = dUp
+      const float gv[4] = {gt.x, gt.y, gt.z, gt.w}, uv[4] = {upv.x, upv.y, upv.z, upv.w};
+      float dg[4], du[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (a.act == SWIGLU) act_bwd1<SWIGLU>(gv[q], uv[q], o[q], dg[q], du[q]);
+        else act_bwd1<RELU2>(gv[q], uv[q], o[q], dg[q], du[q]);
+      }
+      *reinterpret_cast<float4*>(a.y + n) = make_float4(dg[0], dg[1], dg[2], dg[3]);
+      *reinterpret_cast<float4*>(a.y + a.N + n) = make_float4(du[0], du[1], du[2], du[3]);
+    } else {
+      if (MODE == RED_ACCUM) {
+        o[0] += prev.x;
+        o[1] += prev.y;
+        o[2] += prev.z;
+        o[3] += prev.w;
+      }
+      *reinterpret_cast<float4*>(a.y + n) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+// Rows per workgroup: ~1000-1500 workgroups so the tail where some CUs run
+// out of work is short; every wave streams a multiple of 8 rows.
+int64_t dgemv_kc(int64_t N, int64_t K) {
+  const int64_t cb = cdiv(N, DG_COLS);
+  int64_t splits = cdiv(1536, cb);
+  if (splits < 1) splits = 1;
+  int64_t kc = cdiv(cdiv(K, splits), 32) * 32;
+  if (kc < 64) kc = 64;
+  if (kc > 256) kc = 256;
+  return kc;
+}
+
+int64_t dgemv_splits(int64_t N, int64_t K) { return cdiv(K, dgemv_kc(N, K)); }
+
+size_t dgemv_part_bytes(int64_t N, int64_t K) {
+  return (size_t)dgemv_splits(N, K) * N * sizeof(float);
+}
+
+int64_t dgemv_nscal(int64_t N, int64_t K) { return dgemv_splits(N, K) * cdiv(N, DG_COLS); }
+
+hipError_t launch_dgemv(int w_dt, int a_dt, GemvArgs a, hipStream_t s) {
+  a.kc = dgemv_kc(a.N, a.K);
+  if (a.W2 == nullptr) {
+    a.W2 = a.W1;
+    a.K1 = a.K;
+  }
+  dim3 grid((unsigned)cdiv(a.N, DG_COLS), (unsigned)cdiv(a.K, a.kc)), block(256);
+  const size_t sm = (size_t)a.kc * sizeof(float);
+  if (w_dt == F32) {
+    if (a_dt == F32) dgemv_kernel<float, float><<<grid, block, sm, s>>>(a);
+    else dgemv_kernel<float, bf16><<<grid, block, sm, s>>>(a);
+  } else {
+    if (a_dt == F32) dgemv_kernel<bf16, float><<<grid, block, sm, s>>>(a);
+    else dgemv_kernel<bf16, bf16><<<grid, block, sm, s>>>(a);
+  }
+  const double es = w_dt == F32 ? 4 : 2;
+  mark("dgemv", (double)a.K * a.N * es + a.K * 4.0 + a.N * 4.0, 2.0 * a.K * a.N, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_dgemv_red(int mode, int a_dt, RedArgs a, hipStream_t s) {
+  dim3 grid((unsigned)cdiv(a.N, DR_COLS)), block(256);
+#define LBP_RED(TA)                                                        \
+  do {                                                                     \
+    if (mode == RED_ACT) dgemv_red_kernel<TA, RED_ACT><<<grid, block, 0, s>>>(a);     \
+    else if (mode == RED_ACCUM) dgemv_red_kernel<TA, RED_ACCUM><<<grid, block, 0, s>>>(a); \
+    else dgemv_red_kernel<TA, RED_STORE><<<grid, block, 0, s>>>(a);                 \
+  } while (0)
+  if (a_dt == F32) LBP_RED(float);
+  else LBP_RED(bf16);
+#undef LBP_RED
+  const double es = a_dt == F32 ? 4 : 2;
+  double bytes = (double)a.N * 4;  // the result
+  if (a.scal) bytes += (double)a.N * (es + 4);
+  if (mode == RED_ACT) bytes += (double)a.N * (2 * es + 4);
+  if (mode == RED_ACCUM) bytes += (double)a.N * 4;
+  mark(mode == RED_ACT ? "dgemv_red_act" : mode == RED_ACCUM ? "dgemv_red_resid" : "dgemv_red",
+       bytes, 0, s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Decode attention (one query row), two kernels with no serial chains:
+//   dec_attn1  workgroup = (32 keys, KV head g): V rows staged in LDS;
+//              dA[h, j] = dCtx_h . V_g[j] as 8 partial dots per (h, j)
+//              summed across waves in a fixed order; dV[j] = sum_h P dCtx_h.
+//   dec_attn2  workgroup = head, 16 waves: delta = sum_j P dA, dS = P (dA -
+//              delta), dq = scale sum_j dS[j] K_g[j] with the waves taking
+//              interleaved keys (partials added in order), then optionally
+//              the inverse RoPE rotation.
+constexpr int DA_KC = 32;   // keys per dec_attn1 workgroup
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void dec_attn1_kernel(DecAttnArgs a) {
+  constexpr int NP = 8;            // partial dots per (head, key)
+  constexpr int DP = D / NP;       // head dims per partial
+  extern __shared__ float sm[];
+  const int grp = a.grp;
+  float* Vs = sm;                          // [DA_KC][D + 1]
+  float* dC = Vs + DA_KC * (D + 1);        // [grp][D]
+  float* Ps = dC + grp * D;                // [grp][DA_KC]
+  float* red = Ps + grp * DA_KC;           // [NP][grp][DA_KC]
+  const int t = threadIdx.x;
+  const int g = blockIdx.y;
+  const int64_t k0 = (int64_t)blockIdx.x * DA_KC;
+  const int64_t ldk = (int64_t)(a.Hq / grp) * D;
+  {
+    // all global loads of the block first, then the LDS stores
+    constexpr int NV = DA_KC * D / 1024;  // float4 of V per thread (>= 1 for D >= 32)
+    float4 v[NV > 0 ? NV : 1];
+#pragma unroll
+    for (int u = 0; u < (NV > 0 ? NV : 1); ++u) {
+      const int e = t * 4 + 1024 * u;
+      const int kr = e / D, d = e - kr * D;
+      const int64_t key = k0 + kr;
+      v[u] = (e < DA_KC * D && key < a.s_kv) ? Act<T>::ld4((const T*)a.V, key * ldk + g * D + d)
+                                             : make_float4(0, 0, 0, 0);
+    }
+    for (int e = t; e < grp * D; e += 256) dC[e] = a.dctx[(int64_t)g * grp * D + e];
+    for (int e = t; e < grp * DA_KC; e += 256) {
+      const int hh = e / DA_KC, kr = e - hh * DA_KC;
+      const int64_t key = k0 + kr;
+      Ps[e] = key < a.s_kv ? Act<T>::ld((const T*)a.P, (int64_t)(g * grp + hh) * a.s_kv + key) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < (NV > 0 ? NV : 1); ++u) {
+      const int e = t * 4 + 1024 * u;
+      if (e < DA_KC * D) {
+        const int kr = e / D, d = e - kr * D;
+        float* vr = Vs + kr * (D + 1) + d;
+        vr[0] = v[u].x;
+        vr[1] = v[u].y;
+        vr[2] = v[u].z;
+        vr[3] = v[u].w;
+      }
+    }
+  }
+  __syncthreads();
+  {
+    // thread (key kr = t % 32, part p = t / 32) over dims [p*DP, p*DP+DP)
+    const int kr = t % DA_KC, p = t / DA_KC;
+    for (int hh = 0; hh < grp; ++hh) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < DP; ++i) acc += dC[hh * D + p * DP + i] * Vs[kr * (D + 1) + p * DP + i];
+      red[(p * grp + hh) * DA_KC + kr] = acc;
+    }
+  }
+  __syncthreads();
+  for (int e = t; e < grp * DA_KC; e += 256) {
+    const int hh = e / DA_KC, kr = e - hh * DA_KC;
+    const int64_t key = k0 + kr;
+    float o = 0.f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) o += red[(p * grp + hh) * DA_KC + kr];
+    if (key < a.s_kv) a.dA[(int64_t)(g * grp + hh) * a.s_kv + key] = o;
+  }
+  if (a.dv != nullptr) {
+    for (int e = t; e < DA_KC * D; e += 256) {
+      const int kr = e / D, d = e - kr * D;
+      const int64_t key = k0 + kr;
+      if (key >= a.s_kv) break;
+      float o = 0.f;
+      for (int hh = 0; hh < grp; ++hh) o += Ps[hh * DA_KC + kr] * dC[hh * D + d];
+      a.dv[key * ldk + g * D + d] = o;
+    }
+  }
+}
+
+template <typename T, int VPL>
+__device__ __forceinline__ void ldv(const T* p, int64_t i, float (&v)[VPL]) {
+  if constexpr (VPL == 2 && sizeof(T) == 4) {
+    const float2 x = *reinterpret_cast<const float2*>((const float*)p + i);
+    v[0] = x.x;
+    v[1] = x.y;
+  } else {
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) v[j] = Act<T>::ld(p, i + j);
+  }
+}
+
+constexpr int DQ_W = 16;   // waves per dec_attn2 workgroup
+
+template <typename T, int D>
+__global__ __launch_bounds__(1024) void dec_attn2_kernel(DecAttnArgs a) {
+  constexpr int VPL = D >= 64 ? D / 64 : 1;
+  constexpr int NL = D / VPL;
+  extern __shared__ float sm[];
+  float* dS = sm;                  // [s_kv]
+  float* accs = sm + a.s_kv;       // [DQ_W][D]
+  float* o = accs + DQ_W * D;      // [D]
+  __shared__ float rs[DQ_W];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int h = blockIdx.x, g = h / a.grp;
+  const int64_t ldk = (int64_t)(a.Hq / a.grp) * D;
+  const T* Ph = (const T*)a.P + (int64_t)h * a.s_kv;
+  const float* dAh = a.dA + (int64_t)h * a.s_kv;
+  const bool lok = lane < NL;
+  const int d0 = lane * VPL;
+  constexpr int UK = 16;  // keys in flight per wave
+  // the first UK keys of this wave are fetched before delta is known
+  float k[UK][VPL];
+  auto fetch = [&](int64_t j0) {
+#pragma unroll
+    for (int u = 0; u < UK; ++u) {
+      const int64_t j = j0 + DQ_W * u;
+      if (lok && j < a.s_kv) {
+        ldv<T, VPL>((const T*)a.K, j * ldk + g * D + d0, k[u]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < VPL; ++q) k[u][q] = 0.f;
+      }
+    }
+  };
+  fetch(w);
+  float s = 0.f;
+  for (int64_t j = t; j < a.s_kv; j += 1024) s += Act<T>::ld(Ph, j) * dAh[j];
+  const float delta = block_sum<DQ_W>(s, rs);
+  for (int64_t j = t; j < a.s_kv; j += 1024) dS[j] = Act<T>::ld(Ph, j) * (dAh[j] - delta);
+  __syncthreads();
+  float acc[VPL];
+#pragma unroll
+  for (int q = 0; q < VPL; ++q) acc[q] = 0.f;
+  for (int64_t j0 = w; j0 < a.s_kv; j0 += UK * DQ_W) {
+    if (j0 != w) fetch(j0);
+#pragma unroll
+    for (int u = 0; u < UK; ++u) {
+      const int64_t j = j0 + DQ_W * u;
+      const float ds = j < a.s_kv ? dS[j] : 0.f;
+#pragma unroll
+      for (int q = 0; q < VPL; ++q) acc[q] += ds * k[u][q];
+    }
+  }
+  if (lok) {
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) accs[w * D + d0 + q] = acc[q];
+  }
+  __syncthreads();
+  if (t < D) {
+    float v = accs[t];
+    for (int i = 1; i < DQ_W; ++i) v += accs[i * D + t];
+    o[t] = a.scale * v;
+  }
+  __syncthreads();
+  constexpr int HALF = D / 2;
+  if (!a.rope) {
+    if (t < D) a.dq[(int64_t)h * D + t] = o[t];
+  } else if (t < HALF) {
+    const double inv_freq = exp2(-(2.0 * t / D) * a.log2_base);
+    double sn, cs;
+    sincos((double)a.pos * inv_freq, &sn, &cs);
+    const float cf = (float)cs, sf = (float)sn;
+    const float lo = o[t], hi = o[t + HALF];
+    a.dq[(int64_t)h * D + t] = lo * cf + hi * sf;
+    a.dq[(int64_t)h * D + t + HALF] = -lo * sf + hi * cf;
+  }
+}
+
+// With ctx (= P V, the forward attention output) available, delta_h =
+// <dCtx_h, ctx_h> is known up front, so one pass over each key block does
+// everything: dA, dV, dS = P (dA - delta) and this block's share of dq.
+//   dec_attn1c   workgroup = (32 keys, KV head g); K and V rows staged in LDS
+//   dec_attn_dqc workgroup = head: dq = scale * sum of the block shares (in
+//                order), then optionally the inverse RoPE rotation
+template <typename T, int D>
+__global__ __launch_bounds__(256) void dec_attn1c_kernel(DecAttnArgs a) {
+  constexpr int NP = 8;            // partial dots per (head, key)
+  constexpr int DP = D / NP;
+  constexpr int NKG = 256 / D;     // key groups in the dq share
+  constexpr int KPG = DA_KC / NKG; // keys per key group
+  extern __shared__ float sm[];
+  const int grp = a.grp;
+  float* Vs = sm;                          // [DA_KC][D + 1]
+  float* Ks = Vs + DA_KC * (D + 1);        // [DA_KC][D + 1]
+  float* dC = Ks + DA_KC * (D + 1);        // [grp][D]
+  float* Ps = dC + grp * D;                // [grp][DA_KC]
+  float* red = Ps + grp * DA_KC;           // [NP][grp][DA_KC]
+  float* dS = red + NP * grp * DA_KC;      // [grp][DA_KC]
+  float* prod = dS + grp * DA_KC;          // [grp][D]
+  float* dqs = prod + grp * D;             // [NKG][grp][D]
+  __shared__ float delta[64];
+  const int t = threadIdx.x;
+  const int g = blockIdx.y;
+  const int64_t k0 = (int64_t)blockIdx.x * DA_KC;
+  const int64_t ldk = (int64_t)(a.Hq / grp) * D;
+  {
+    constexpr int NV = DA_KC * D / 1024 > 0 ? DA_KC * D / 1024 : 1;
+    float4 v[NV], k[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int e = t * 4 + 1024 * u;
+      const int kr = e / D, d = e - kr * D;
+      const int64_t key = k0 + kr;
+      const bool ok = e < DA_KC * D && key < a.s_kv;
+      v[u] = ok ? Act<T>::ld4((const T*)a.V, key * ldk + g * D + d) : make_float4(0, 0, 0, 0);
+      k[u] = ok ? Act<T>::ld4((const T*)a.K, key * ldk + g * D + d) : make_float4(0, 0, 0, 0);
+    }
+    for (int e = t; e < grp * D; e += 256) {
+      const int64_t qi = (int64_t)g * grp * D + e;
+      const float dc = a.dctx[qi];
+      dC[e] = dc;
+      prod[e] = dc * Act<T>::ld((const T*)a.ctx, qi);
+    }
+    for (int e = t; e < grp * DA_KC; e += 256) {
+      const int hh = e / DA_KC, kr = e - hh * DA_KC;
+      const int64_t key = k0 + kr;
+      Ps[e] = key < a.s_kv ? Act<T>::ld((const T*)a.P, (int64_t)(g * grp + hh) * a.s_kv + key) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int e = t * 4 + 1024 * u;
+      if (e < DA_KC * D) {
+        const int kr = e / D, d = e - kr * D;
+        float* vr = Vs + kr * (D + 1) + d;
+        float* kq = Ks + kr * (D + 1) + d;
+        vr[0] = v[u].x;
+        vr[1] = v[u].y;
+        vr[2] = v[u].z;
+        vr[3] = v[u].w;
+        kq[0] = k[u].x;
+        kq[1] = k[u].y;
+        kq[2] = k[u].z;
+        kq[3] = k[u].w;
+      }
+    }
+  }
+  __syncthreads();
+  // delta_h = <dCtx_h, ctx_h>: wave w reduces heads w, w+4, ... (fixed
+  // lane order, then the butterfly); partial dots for dA
+  {
+    const int lane = t & 63, w = t >> 6;
+    for (int hh = w; hh < grp; hh += 4) {
+      float s = 0.f;
+      for (int d = lane; d < D; d += 64) s += prod[hh * D + d];
+      s = wave_sum(s);
+      if (lane == 0) delta[hh] = s;
+    }
+  }
+  {
+    const int kr = t % DA_KC, p = t / DA_KC;
+    for (int hh = 0; hh < grp; ++hh) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < DP; ++i) acc += dC[hh * D + p * DP + i] * Vs[kr * (D + 1) + p * DP + i];
+      red[(p * grp + hh) * DA_KC + kr] = acc;
+    }
+  }
+  __syncthreads();
+  for (int e = t; e < grp * DA_KC; e += 256) {
+    const int hh = e / DA_KC, kr = e - hh * DA_KC;
+    float o = 0.f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) o += red[(p * grp + hh) * DA_KC + kr];
+    dS[e] = Ps[e] * (o - delta[hh]);
+  }
+  if (a.dv != nullptr) {
+    for (int e = t; e < DA_KC * D; e += 256) {
+      const int kr = e / D, d = e - kr * D;
+      const int64_t key = k0 + kr;
+      if (key >= a.s_kv) break;
+      float o = 0.f;
+      for (int hh = 0; hh < grp; ++hh) o += Ps[hh * DA_KC + kr] * dC[hh * D + d];
+      a.dv[key * ldk + g * D + d] = o;
+    }
+  }
+  __syncthreads();
+  {
+    // this block's share of dq: thread (d, key group kg)
+    const int d = t % D, kg = t / D;
+    for (int hh = 0; hh < grp; ++hh) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < KPG; ++i) {
+        const int kr = kg * KPG + i;
+        acc += dS[hh * DA_KC + kr] * Ks[kr * (D + 1) + d];
+      }
+      dqs[(kg * grp + hh) * D + d] = acc;
+    }
+  }
+  __syncthreads();
+  for (int e = t; e < grp * D; e += 256) {
+    const int hh = e / D, d = e - hh * D;
+    float o = 0.f;
+#pragma unroll
+    for (int kg = 0; kg < NKG; ++kg) o += dqs[(kg * grp + hh) * D + d];
+    a.dq_part[((int64_t)(g * grp + hh) * gridDim.x + blockIdx.x) * D + d] = o;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void dec_attn_dqc_kernel(DecAttnArgs a, int nchunks) {
+  __shared__ float o[D];
+  const int t = threadIdx.x, h = blockIdx.x;
+  const float* src = a.dq_part + (int64_t)h * nchunks * D + t;
+  float v = 0.f;
+  for (int c0 = 0; c0 < nchunks; c0 += 16) {
+    float x[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) x[u] = c0 + u < nchunks ? src[(int64_t)(c0 + u) * D] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v += x[u];
+  }
+  o[t] = a.scale * v;
+  __syncthreads();
+  constexpr int HALF = D / 2;
+  if (!a.rope) {
+    a.dq[(int64_t)h * D + t] = o[t];
+  } else if (t < HALF) {
+    const double inv_freq = exp2(-(2.0 * t / D) * a.log2_base);
+    double sn, cs;
+    sincos((double)a.pos * inv_freq, &sn, &cs);
+    const float cf = (float)cs, sf = (float)sn;
+    const float lo = o[t], hi = o[t + HALF];
+    a.dq[(int64_t)h * D + t] = lo * cf + hi * sf;
+    a.dq[(int64_t)h * D + t + HALF] = -lo * sf + hi * cf;
+  }
+}
+
+static size_t dec_attn1c_smem(int64_t grp, int64_t D) {
+  return ((size_t)2 * DA_KC * (D + 1) + 2 * grp * D + 10 * grp * DA_KC + (256 / D) * grp * D) *
+         sizeof(float);
+}
+
+static size_t dec_attn1_smem(int64_t grp, int64_t D) {
+  return ((size_t)DA_KC * (D + 1) + grp * D + grp * DA_KC + 8 * grp * DA_KC) * sizeof(float);
+}
+
+static size_t dec_attn2_smem(int64_t s_kv, int64_t D) {
+  return ((size_t)s_kv + (DQ_W + 1) * D) * sizeof(float);
+}
+
+template <typename T, int D>
+static hipError_t dec_attn_launch(const DecAttnArgs& a, hipStream_t s) {
+  const int Hkv = a.Hq / a.grp;
+  const double es = sizeof(T);
+  const int nch = (int)cdiv(a.s_kv, DA_KC);
+  hipError_t e;
+  if (a.ctx != nullptr && a.grp <= 64 && dec_attn1c_smem(a.grp, D) <= 64 * 1024) {
+    dec_attn1c_kernel<T, D><<<dim3((unsigned)nch, (unsigned)Hkv), dim3(256),
+                              dec_attn1c_smem(a.grp, D), s>>>(a);
+    mark("dec_attn1c",
+         2.0 * a.s_kv * Hkv * D * es + (double)a.Hq * a.s_kv * es + (double)a.Hq * D * (4 + es) +
+             (a.dv ? (double)a.s_kv * Hkv * D * 4 : 0.0) + (double)a.Hq * nch * D * 4,
+         6.0 * D * a.Hq * a.s_kv, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    dec_attn_dqc_kernel<D><<<dim3((unsigned)a.Hq), dim3(D), 0, s>>>(a, nch);
+    mark("dec_attn_dqc", (double)a.Hq * nch * D * 4 + (double)a.Hq * D * 4, 0, s);
+    return hipGetLastError();
+  }
+  dec_attn1_kernel<T, D><<<dim3((unsigned)nch, (unsigned)Hkv), dim3(256),
+                           dec_attn1_smem(a.grp, D), s>>>(a);
+  mark("dec_attn1",
+       (double)a.s_kv * Hkv * D * es + (double)a.Hq * a.s_kv * (es + 4) + (double)a.Hq * D * 4 +
+           (a.dv ? (double)a.s_kv * Hkv * D * 4 : 0.0),
+       4.0 * D * a.Hq * a.s_kv, s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  dec_attn2_kernel<T, D><<<dim3((unsigned)a.Hq), dim3(1024), dec_attn2_smem(a.s_kv, D), s>>>(a);
+  mark("dec_attn2",
+       (double)a.Hq * a.s_kv * (es + 4) + (double)a.s_kv * Hkv * D * es + (double)a.Hq * D * 4,
+       2.0 * D * a.Hq * a.s_kv, s);
+  return hipGetLastError();
+}
+
+bool dec_attn_fits(int64_t s_kv, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim) {
+  return dec_attn1_smem(n_heads / n_kv_heads, head_dim) <= 64 * 1024 &&
+         dec_attn2_smem(s_kv, head_dim) <= 64 * 1024;
+}
+
+size_t dec_attn_ws_bytes(int64_t s_kv, int64_t n_heads, int64_t head_dim) {
+  // dA [Hq, s_kv] for the two-pass path, or the dq shares [Hq, blocks, D]
+  const size_t a = (size_t)n_heads * s_kv, b = (size_t)n_heads * cdiv(s_kv, DA_KC) * head_dim;
+  return (a > b ? a : b) * sizeof(float);
+}
+
+hipError_t launch_dec_attn(int dt, int head_dim, const DecAttnArgs& a, hipStream_t s) {
+#define LBP_DA(DD)                                                                 \
+  case DD:                                                                         \
+    return dt == F32 ? dec_attn_launch<float, DD>(a, s) : dec_attn_launch<bf16, DD>(a, s);
+  switch (head_dim) {
+    LBP_DA(16)
+    LBP_DA(32)
+    LBP_DA(64)
+    LBP_DA(128)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef LBP_DA
+}
+
+}  // namespace lbp

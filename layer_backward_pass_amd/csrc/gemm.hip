@@ -3,7 +3,6 @@
 //   * fp32 weights: v_mfma_f32_16x16x4_f32, 128x128x16 workgroup tiles
 //   * bf16 weights: v_mfma_f32_16x16x32_bf16, 128x128x32 tiles, the
 //     gradient operand rounded to bf16 when staged in LDS
-//   * M = 1 (single-token decode): an HBM-streaming GEMV with 16-byte loads
 // Split-K partial sums go to caller scratch and are reduced in a fixed
 // order (no float atomics), so results are bitwise reproducible.
 #include "common.h"
@@ -288,120 +287,6 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
   if (blocks > 4096) blocks = 4096;
   splitk_reduce_kernel<<<dim3((unsigned)blocks), block, 0, s>>>(M, N, nsp, partials, C, ldc);
   mark("splitk_reduce", 0, 0, s);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Decode GEMV: y[n] = sum_k x[k] W[k, n].  Workgroup (column block of 1024,
-// row chunk of GV_KC); each thread streams 4 adjacent columns of its rows
-// with 16-byte loads, 8 rows in flight.  Partial sums [splits, N] are then
-// reduced in a fixed order.
-constexpr int GV_COLS = 1024, GV_KC = 64;
-
-template <typename TW>
-__global__ __launch_bounds__(256) void gemv_partial_kernel(int64_t N, int64_t K,
-                                                           const float* __restrict__ x,
-                                                           const TW* __restrict__ W1,
-                                                           const TW* __restrict__ W2, int64_t K1,
-                                                           float* __restrict__ part) {
-  const int64_t n = (int64_t)blockIdx.x * GV_COLS + threadIdx.x * 4;
-  const int64_t k0 = (int64_t)blockIdx.y * GV_KC;
-  const int64_t k1 = min(K, k0 + GV_KC);
-  float4 acc = make_float4(0, 0, 0, 0);
-  if (n < N) {
-    int64_t k = k0;
-    for (; k + 8 <= k1; k += 8) {
-      float4 wv[8];
-      float xv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t kk = k + u;
-        const TW* wp = kk < K1 ? W1 + kk * N : W2 + (kk - K1) * N;
-        wv[u] = Act<TW>::ld4(wp, n);
-        xv[u] = x[kk];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        acc.x += xv[u] * wv[u].x;
-        acc.y += xv[u] * wv[u].y;
-        acc.z += xv[u] * wv[u].z;
-        acc.w += xv[u] * wv[u].w;
-      }
-    }
-    for (; k < k1; ++k) {
-      const TW* wp = k < K1 ? W1 + k * N : W2 + (k - K1) * N;
-      const float4 wv = Act<TW>::ld4(wp, n);
-      const float xv = x[k];
-      acc.x += xv * wv.x;
-      acc.y += xv * wv.y;
-      acc.z += xv * wv.z;
-      acc.w += xv * wv.w;
-    }
-    *reinterpret_cast<float4*>(part + (int64_t)blockIdx.y * N + n) = acc;
-  }
-}
-
-// y[n] = sum_s part[s, n]: four split groups of 64 threads sum interleaved
-// splits in order, then the four group sums are added in order.
-__global__ __launch_bounds__(256) void gemv_reduce_kernel(int64_t N, int splits,
-                                                          const float* __restrict__ part,
-                                                          float* __restrict__ y) {
-  __shared__ float4 red[4][64];
-  const int g = threadIdx.x >> 6, c = threadIdx.x & 63;
-  const int64_t n = (int64_t)blockIdx.x * 256 + c * 4;
-  float4 s = make_float4(0, 0, 0, 0);
-  if (n < N)
-    for (int i = g; i < splits; i += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)i * N + n);
-      s.x += v.x;
-      s.y += v.y;
-      s.z += v.z;
-      s.w += v.w;
-    }
-  red[g][c] = s;
-  __syncthreads();
-  if (g == 0 && n < N) {
-    float4 o = red[0][c];
-#pragma unroll
-    for (int i = 1; i < 4; ++i) {
-      o.x += red[i][c].x;
-      o.y += red[i][c].y;
-      o.z += red[i][c].z;
-      o.w += red[i][c].w;
-    }
-    *reinterpret_cast<float4*>(y + n) = o;
-  }
-}
-
-int gemv_splits(int64_t N, int64_t K) {
-  (void)N;
-  return (int)cdiv(K, GV_KC);
-}
-
-size_t gemv_partial_bytes(int64_t N, int64_t K) {
-  return (size_t)gemv_splits(N, K) * N * sizeof(float);
-}
-
-hipError_t launch_gemv(int64_t N, int64_t K, const float* x, const void* W1, const void* W2,
-                       int64_t K1, int w_dt, float* y, float* partials, hipStream_t s) {
-  if (N == 0) return hipSuccess;
-  if (W2 == nullptr) {
-    W2 = W1;
-    K1 = K;
-  }
-  const int splits = gemv_splits(N, K);
-  dim3 grid((unsigned)cdiv(N, GV_COLS), (unsigned)splits), block(256);
-  if (w_dt == F32)
-    gemv_partial_kernel<float><<<grid, block, 0, s>>>(N, K, x, (const float*)W1,
-                                                      (const float*)W2, K1, partials);
-  else
-    gemv_partial_kernel<bf16><<<grid, block, 0, s>>>(N, K, x, (const bf16*)W1, (const bf16*)W2,
-                                                     K1, partials);
-  hipError_t e = hipGetLastError();
-  mark("gemv_partial", (double)K * N * (w_dt == F32 ? 4 : 2) + K * 4.0 + N * 4.0, 2.0 * K * N, s);
-  if (e != hipSuccess) return e;
-  gemv_reduce_kernel<<<dim3((unsigned)cdiv(N, 256)), block, 0, s>>>(N, splits, partials, y);
-  mark("gemv_reduce", 0, 0, s);
   return hipGetLastError();
 }
 

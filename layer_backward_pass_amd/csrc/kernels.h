@@ -43,11 +43,76 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
                        const void* B1, const void* B2, int64_t K1, int b_dt, int64_t ldb,
                        float* C, int64_t ldc, float* partials, hipStream_t s);
 
-// y[N] = x[K] W[K,N] with the same two-source rule; single vector.
-int gemv_splits(int64_t N, int64_t K);
-size_t gemv_partial_bytes(int64_t N, int64_t K);
-hipError_t launch_gemv(int64_t N, int64_t K, const float* x, const void* W1, const void* W2,
-                       int64_t K1, int w_dt, float* y, float* partials, hipStream_t s);
+// ---- single-token (decode) kernels (decode.hip)
+// part[chunk, N] = x[K] W[K, N] over row chunks of kc rows (W rows k < K1
+// from W1, the rest from W2).  With ng set, every workgroup also writes its
+// share of the row sums of the RMSNorm that consumes y = sum of parts:
+// scal[2*wg] = <y_part*ng, nx> over its columns and scal[2*wg+1] = sum nx^2
+// over them (first row chunk only), wg = chunk * column_blocks + block.
+struct GemvArgs {
+  int64_t N, K, K1, kc;
+  const void* W1;
+  const void* W2;
+  const float* x;
+  float* part;
+  float* scal;
+  const void* nx;
+  const float* ng;
+};
+
+// y = sum over `splits` chunks of part, then:
+//   scal set: z = rmsnorm_bwd(nx, ngam, y) with row sums from the nscal
+//             shares in scal; else z = y
+//   RED_STORE  y_out[n] = z
+//   RED_ACCUM  y_out[n] += z                      (residual skip)
+//   RED_ACT    y_out[n] = dGate(z), y_out[N + n] = dUp(z) from gate, up
+enum RedMode { RED_STORE = 0, RED_ACCUM = 1, RED_ACT = 2 };
+struct RedArgs {
+  int64_t N;
+  int splits;
+  const float* part;
+  float* y;
+  const float* scal;
+  int64_t nscal;
+  const void* nx;
+  const float* ngam;
+  float eps;
+  const void* gate;
+  const void* up;
+  int act;
+};
+
+int64_t dgemv_kc(int64_t N, int64_t K);
+int64_t dgemv_splits(int64_t N, int64_t K);
+size_t dgemv_part_bytes(int64_t N, int64_t K);
+int64_t dgemv_nscal(int64_t N, int64_t K);
+hipError_t launch_dgemv(int w_dt, int a_dt, GemvArgs a, hipStream_t s);
+hipError_t launch_dgemv_red(int mode, int a_dt, RedArgs a, hipStream_t s);
+
+// One query row against s_kv keys.  With ctx: dec_attn1c (per key block:
+// dA, dv, dS with delta = <dctx, ctx>, a share of dq) then dec_attn_dqc
+// (sum of shares, scale, inverse RoPE when rope is set).  Without ctx:
+// dec_attn1 (dA, dv) then dec_attn2 (delta = sum P dA, dS, dq, RoPE).
+struct DecAttnArgs {
+  int64_t s_kv;
+  int Hq, grp;
+  const float* dctx;
+  const void* P;
+  const void* K;
+  const void* V;
+  const void* ctx;  // P V (forward attention output) or NULL
+  float* dA;        // scratch, dec_attn_ws_bytes (dA, or the dq shares when ctx is set)
+  float* dq_part;   // same scratch as dA
+  float* dv;
+  float* dq;
+  float scale;
+  int rope;
+  int64_t pos;
+  double log2_base;
+};
+bool dec_attn_fits(int64_t s_kv, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim);
+size_t dec_attn_ws_bytes(int64_t s_kv, int64_t n_heads, int64_t head_dim);
+hipError_t launch_dec_attn(int dt, int head_dim, const DecAttnArgs& a, hipStream_t s);
 
 // ---- attention (attn.hip)
 size_t attn_ws_bytes(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_kv_heads,

@@ -129,19 +129,6 @@ hipError_t launch_rope_bwd(int64_t rows, int64_t n_heads, int64_t head_dim, cons
 //     dGate = dH up 2 max(0,g),  dUp = dH max(0,g)^2
 // Output row r is [dGate(0:I) | dUp(0:I)] so the next product runs over
 // K = 2I against the stacked [W_gate; W_up].
-template <int ACT>
-__device__ __forceinline__ void act_bwd1(float g, float u, float dh, float& dg, float& du) {
-  if (ACT == SWIGLU) {
-    const float sg = 1.0f / (1.0f + expf(-g));
-    dg = dh * u * sg * (1.0f + g * (1.0f - sg));
-    du = dh * g * sg;
-  } else {
-    const float r = fmaxf(g, 0.0f);
-    dg = dh * u * 2.0f * r;
-    du = dh * r * r;
-  }
-}
-
 template <typename T, int ACT, int OUT_BF16>
 __global__ __launch_bounds__(256) void act_bwd_kernel(int64_t rows, int64_t ffn,
                                                       const T* __restrict__ gate,

@@ -100,6 +100,9 @@ def _attn_inputs(seed, s_q, s_kv, Hq, Hkv, D, causal, dt):
     (40, 97, 8, 2, 128, 1, 1, F32),       # fewer queries than keys
     (1, 512, 20, 5, 128, 1, 1, F32),      # decode
     (1, 77, 4, 2, 16, 1, 0, F32),         # decode, ragged cache
+    (1, 77, 4, 2, 16, 1, 1, F32),         # decode, delta from ctx
+    (1, 300, 8, 4, 64, 0, 1, BF16),
+    (1, 1000, 32, 4, 32, 1, 1, F32),
     (96, 96, 8, 2, 128, 1, 1, BF16),
     (1, 300, 8, 4, 64, 0, 0, BF16),
 ])

@@ -89,6 +89,20 @@ def attention(q, k, v, n_heads, n_kv_heads, head_dim, scale, causal):
     return P, ctx
 
 
+def context(P, V, n_heads, n_kv_heads):
+    """The attention output ctx_h = P_h V_g (the apply step of the forward),
+    for saved softmax weights P [Hq, s_q, s_kv] and values V [s_kv, Hkv*D]."""
+    P = np.asarray(P, np.float64)
+    V = np.asarray(V, np.float64)
+    D = V.shape[1] // n_kv_heads
+    grp = n_heads // n_kv_heads
+    ctx = np.zeros((P.shape[1], n_heads * D))
+    for h in range(n_heads):
+        g = h // grp
+        ctx[:, h * D:(h + 1) * D] = P[h] @ V[:, g * D:(g + 1) * D]
+    return ctx
+
+
 def layer_forward(cfg, w, x_res, x_attn=None, lora=None, q_pre=None, v_in=None):
     """Returns (out, saved).  lora: dict with A_q, B_q, A_v, B_v (or None).
     q_pre / v_in override the Q projection output (pre-RoPE) and the value

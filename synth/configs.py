@@ -52,11 +52,13 @@ class LayerConfig:
 
     @property
     def scale(self):
-        return 1.0 / float(self.head_dim) ** 0.5
+        s = self.__dict__.get("_scale")
+        return s if s is not None else 1.0 / float(self.head_dim) ** 0.5
 
     @property
     def lr_b(self):
-        return self.lr * self.lr_b_ratio
+        s = self.__dict__.get("_lr_b")
+        return s if s is not None else self.lr * self.lr_b_ratio
 
     def with_(self, **kw):
         return replace(self, **kw)

@@ -2,8 +2,9 @@
 
 Every tensor has its own PCG64 stream seeded from
 SeedSequence([0, config index, layer index, tensor id]), so any tensor of any
-layer can be regenerated on its own, in any order.  Values are float64; casting
-to the storage dtype is left to the caller.
+layer can be regenerated on its own, in any order.  Large tensors are drawn as
+float32 (N(0,1) ziggurat in single precision); casting to the storage dtype
+is left to the caller.
 
 Distributions (the workload recipe):
   * layer input x, upstream gradient d_out, decode K/V cache: N(0, 1)
@@ -33,7 +34,11 @@ def stream(cfg_index, layer, tensor):
 
 
 def normal(cfg, layer, name, shape, std=1.0):
-    return stream(cfg.index, layer, name).standard_normal(shape) * std
+    """N(0, std^2) draws, generated in float32 (values widen exactly)."""
+    a = stream(cfg.index, layer, name).standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    return a
 
 
 def ternary(cfg, layer, name, shape, scale=0.02):
@@ -42,7 +47,7 @@ def ternary(cfg, layer, name, shape, scale=0.02):
 
 
 def gamma(cfg, layer, name, n):
-    return 1.0 + 0.1 * stream(cfg.index, layer, name).standard_normal(n)
+    return 1.0 + 0.1 * stream(cfg.index, layer, name).standard_normal(n)  # float64, small
 
 
 def _weight(cfg, layer, name, shape):

@@ -1,0 +1,51 @@
+"""GPU parity at the full workload shapes, through the same entry point and
+launch configuration the benchmark times (lorabwd_layer_backward), against
+the float64 oracle on exactly the values the GPU holds.
+
+Bounds (per-tensor max-norm relative error): 1e-4 for float32 inputs, 2e-2
+for bf16 inputs; AdamW-updated tensors use the sign-flip allowance described
+in tests/harness.py.
+"""
+import time
+
+import pytest
+
+import synth
+from tests import harness as Hn
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "seq512", "seq2048bf16"])
+def test_full_size_layer(name):
+    cfg = synth.get_config(name)
+    t0 = time.time()
+    _log("full-size layer %s" % name)
+    errs = Hn.layer_parity(cfg, "cuda:0")
+    _log("  %s: %.1f s, errors %s" % (name, time.time() - t0,
+                                      {k: float("%.3g" % v) for k, v in errs.items()}))
+    bad = {k: v for k, v in errs.items() if not v <= Hn.TOL[cfg.dtype]}
+    assert not bad, bad
+
+
+@pytest.mark.timeout(1500)
+def test_stack36_full():
+    cfg = synth.get_config("stack36")
+    t0 = time.time()
+    errs = Hn.stack_parity(cfg, "cuda:0", log=_log)
+    _log("  stack36: %.1f s, errors %s" % (time.time() - t0,
+                                         {k: float("%.3g" % v) for k, v in errs.items()}))
+    bad = {k: v for k, v in errs.items() if not v <= Hn.TOL[cfg.dtype]}
+    assert not bad, bad

@@ -101,7 +101,8 @@ def _checks(B):
     out.append(abs(res["gnorm_sq"] - float(np.sum(res["dA_q"] ** 2) + np.sum(res["dA_v"] ** 2)))
                <= 1e-15 * res["gnorm_sq"])
     g = res["dB_q"]
-    want = lora["B_q"] - cfg.lr_b * (g / (np.abs(g) + cfg.adam_eps) + cfg.weight_decay * lora["B_q"])
+    b0 = np.asarray(lora["B_q"], np.float64)
+    want = b0 - cfg.lr_b * (g / (np.abs(g) + cfg.adam_eps) + cfg.weight_decay * b0)
     out.append(np.allclose(res["B_q"], want, rtol=1e-13))
     # GQA attention FD with 4 query heads on 2 KV heads
     r = np.random.default_rng(3)

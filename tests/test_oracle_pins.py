@@ -355,8 +355,8 @@ def test_layer_adamw_uses_lora_plus_and_a_only_gnorm(tiny):
     gsq = float(np.sum(res["dA_q"] ** 2) + np.sum(res["dA_v"] ** 2))
     assert res["gnorm_sq"] == pytest.approx(gsq, rel=1e-15)
     g = res["dB_q"]
-    want = lora["B_q"] - tiny.lr * 16 * (g / (np.abs(g) + tiny.adam_eps)
-                                         + tiny.weight_decay * lora["B_q"])
+    b0 = np.asarray(lora["B_q"], np.float64)
+    want = b0 - tiny.lr * 16 * (g / (np.abs(g) + tiny.adam_eps) + tiny.weight_decay * b0)
     np.testing.assert_allclose(res["B_q"], want, rtol=1e-13)
 
 

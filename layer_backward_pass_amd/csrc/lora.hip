@@ -2,159 +2,262 @@
 //
 // entrenar wgpu_backward.rs, backward_through_layers, LoRA Q and V blocks,
 // and cpu_adamw.  With s = alpha/rank and saved h = x A^T:
-//   g  = s dy B       (lora_g_kernel; reads B before it is updated)
-//   dB = s dy^T h     -> AdamW on B with lr_b   (lora_db_kernel)
-//   dA = g^T x        -> AdamW on A with lr_a   (lora_da_kernel)
-//   gnorm_sq += ||dA||^2, per-workgroup partials summed in a fixed order
-// The three reductions run over the token rows (dB, dA) or the output
-// features (g); all are deterministic.  The rows are split over several
-// workgroups and the partial sums reduced in order before the update.
+//   g  = s dy B       [rows, rank]  (B read before it is updated)
+//   dB = s dy^T h     [out, rank]   -> AdamW on B with lr_b
+//   dA = g^T x        [rank, in]    -> AdamW on A with lr_a
+//   gnorm_sq += ||dA||^2
+//
+// Two MFMA passes carry the work.  lora_dy_kernel reads each element of dy
+// once from HBM and forms both g (contraction over the output features) and
+// dB (contraction over the token rows); lora_da_kernel reads x once for dA.
+// Each workgroup owns 256 columns (4 waves x 64) and one slice of the rows;
+// the per-slice partial sums are reduced in a fixed order by the update
+// kernels, so every result is deterministic.  Ranks are padded to a multiple
+// of 16 (the MFMA tile width) with zeros.
 #include "common.h"
 #include "kernels.h"
 
 namespace lbp {
 
-constexpr int LR_MAX = 64;   // largest supported rank
-constexpr int L_ROWS = 128;  // token rows per partial-sum chunk
+constexpr int LW_COLS = 64;    // columns per wave
+constexpr int LG_COLS = 256;   // columns per workgroup
+constexpr int L_TARGET = 256;  // workgroups aimed for per pass
 
-// g[i, r] = s sum_o dy[i, o] B[o, r]; one workgroup per token row.
-__global__ __launch_bounds__(256) void lora_g_kernel(int64_t out_dim, int rank,
-                                                     const float* __restrict__ dy,
-                                                     const float* __restrict__ B, float s,
-                                                     float* __restrict__ g) {
-  __shared__ float red[4][LR_MAX];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int64_t i = blockIdx.x;
-  float acc[LR_MAX];
-#pragma unroll
-  for (int r = 0; r < LR_MAX; ++r) acc[r] = 0.f;
-  const float* dyr = dy + i * out_dim;
-  for (int64_t o = t; o < out_dim; o += 256) {
-    const float d = dyr[o];
-    const float* br = B + o * rank;
-#pragma unroll
-    for (int r = 0; r < LR_MAX; ++r)
-      if (r < rank) acc[r] += d * br[r];
+static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Four consecutive floats of row `row` starting at column `c`, zero outside
+// [0, rows) x [0, ncol).  VEC: ncol % 4 == 0 and c % 4 == 0, one 16-byte load.
+template <bool VEC>
+__device__ __forceinline__ float4 ld4f(const float* p, int64_t row, int64_t rows, int64_t c,
+                                       int64_t ncol) {
+  float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (row >= rows) return r;
+  const float* q = p + row * ncol + c;
+  if (VEC) {
+    if (c < ncol) r = *reinterpret_cast<const float4*>(q);
+  } else {
+    if (c < ncol) r.x = q[0];
+    if (c + 1 < ncol) r.y = q[1];
+    if (c + 2 < ncol) r.z = q[2];
+    if (c + 3 < ncol) r.w = q[3];
   }
-#pragma unroll
-  for (int r = 0; r < LR_MAX; ++r) {
-    if (r < rank) {
-      const float v = wave_sum(acc[r]);
-      if (lane == 0) red[w][r] = v;
-    }
-  }
-  __syncthreads();
-  if (t < rank) g[i * rank + t] = s * (((red[0][t] + red[1][t]) + red[2][t]) + red[3][t]);
+  return r;
 }
 
-__device__ __forceinline__ float adamw1(float& p, float gr, float& m, float& v, float lr,
-                                        const AdamHP& hp) {
+__device__ __forceinline__ float f4get(const float4& v, int j) {
+  return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ float ld_h(const void* h, int hdt, int64_t e) {
+  return hdt == F32 ? ((const float*)h)[e] : bf2f(((const uint16_t*)h)[e]);
+}
+
+// One pass over dy [rows, out].  Wave w of workgroup (bx, by) owns the output
+// features o0 .. o0+63 (o0 = 256 bx + 64 w) and the row slice by.
+//   g part:  gpart[bx][i][r]  = sum_{o in workgroup} dy[i,o] B[o,r]
+//   dB part: dbpart[by][o][r] = sum_{i in slice} dy[i,o] h[i,r]
+// MFMA 16x16x4 f32 layouts: operand lane l holds (row l%16, k l/16); result
+// lane l, register v holds (row 4(l/16)+v, col l%16).
+// g:  rows = 16 tokens, k = features; lane loads dy[i0+l%16][o0+16c+4(l/16)+j]
+// dB: rows = 16 features (tile j: o0 + 4m + j), k = tokens; lane loads
+//     dy[i0+4q+l/16][o0+4(l%16)+j].
+template <int RB, bool VEC>
+__global__ __launch_bounds__(256) void lora_dy_kernel(int64_t rows, int64_t out_dim, int rank,
+                                                      int64_t rs, const float* __restrict__ dy,
+                                                      const void* __restrict__ h, int hdt,
+                                                      const float* __restrict__ Bm,
+                                                      float* __restrict__ gpart,
+                                                      float* __restrict__ dbpart) {
+  constexpr int RP = 16 * RB;
+  __shared__ float gs[4][16][RP + 1];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int l16 = lane & 15, l4 = lane >> 4;
+  const int64_t o0 = (int64_t)blockIdx.x * LG_COLS + w * LW_COLS;
+  const int64_t i_beg = (int64_t)blockIdx.y * rs;
+  const int64_t i_end = min(rows, i_beg + rs);
+
+  float bv[4][4][RB];  // B operand of g: B[o0+16c+4 l4+j][16b+l16]
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        const int64_t o = o0 + 16 * c + 4 * l4 + j;
+        const int r = 16 * b + l16;
+        bv[c][j][b] = (o < out_dim && r < rank) ? Bm[o * rank + r] : 0.f;
+      }
+  floatx4 accb[4][RB];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int b = 0; b < RB; ++b) accb[j][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t i0 = i_beg; i0 < i_end; i0 += 16) {
+    float4 ga[4], da[4];
+    float hv[4][RB];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ga[c] = ld4f<VEC>(dy, i0 + l16, rows, o0 + 16 * c + 4 * l4, out_dim);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t i = i0 + 4 * q + l4;
+      da[q] = ld4f<VEC>(dy, i, rows, o0 + 4 * l16, out_dim);
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        const int r = 16 * b + l16;
+        hv[q][b] = (i < rows && r < rank) ? ld_h(h, hdt, i * rank + r) : 0.f;
+      }
+    }
+    floatx4 accg[RB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) accg[b] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int b = 0; b < RB; ++b) accg[b] = mfma16x16x4(f4get(ga[c], j), bv[c][j][b], accg[b]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int b = 0; b < RB; ++b) accb[j][b] = mfma16x16x4(f4get(da[q], j), hv[q][b], accb[j][b]);
+    // sum the four waves' g tiles in a fixed order
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) gs[w][4 * l4 + v][16 * b + l16] = accg[b][v];
+    __syncthreads();
+    for (int e = t; e < 16 * RP; e += 256) {
+      const int row = e / RP, col = e % RP;
+      if (i0 + row < rows)
+        gpart[((int64_t)blockIdx.x * rows + i0 + row) * RP + col] =
+            ((gs[0][row][col] + gs[1][row][col]) + gs[2][row][col]) + gs[3][row][col];
+    }
+    __syncthreads();
+  }
+  // dB tile j, register v: feature o0 + 4(4 l4 + v) + j, rank 16b + l16
+  float* dp = dbpart + (int64_t)blockIdx.y * out_dim * rank;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t o = o0 + 4 * (4 * l4 + v) + j;
+        const int r = 16 * b + l16;
+        if (o < out_dim && r < rank) dp[o * rank + r] = accb[j][b][v];
+      }
+}
+
+// Four consecutive activations of x as float (in_dim % 8 == 0, c % 4 == 0).
+template <typename T>
+__device__ __forceinline__ float4 ld4x(const T* x, int64_t row, int64_t rows, int64_t c,
+                                       int64_t ncol) {
+  if (row >= rows || c >= ncol) return make_float4(0.f, 0.f, 0.f, 0.f);
+  return Act<T>::ld4(x, row * ncol + c);
+}
+
+// One pass over x [rows, in]: dapart[by][r][k] = sum_{i in slice} g[i,r] x[i,k].
+// Result rows = rank (16 per block b), cols = features (tile j: k0 + 4n + j),
+// k = tokens.  g is [rows, 16 RB], already scaled and zero-padded.
+template <int RB, typename T>
+__global__ __launch_bounds__(256) void lora_da_kernel(int64_t rows, int64_t in_dim, int rank,
+                                                      int64_t rs, const float* __restrict__ g,
+                                                      const T* __restrict__ x,
+                                                      float* __restrict__ dapart) {
+  constexpr int RP = 16 * RB;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int l16 = lane & 15, l4 = lane >> 4;
+  const int64_t k0 = (int64_t)blockIdx.x * LG_COLS + w * LW_COLS;
+  const int64_t i_beg = (int64_t)blockIdx.y * rs;
+  const int64_t i_end = min(rows, i_beg + rs);
+  floatx4 acc[4][RB];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int b = 0; b < RB; ++b) acc[j][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t i0 = i_beg; i0 < i_end; i0 += 16) {
+    float4 xa[4];
+    float gv[4][RB];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t i = i0 + 4 * q + l4;
+      xa[q] = ld4x<T>(x, i, rows, k0 + 4 * l16, in_dim);
+#pragma unroll
+      for (int b = 0; b < RB; ++b) gv[q][b] = i < rows ? g[i * RP + 16 * b + l16] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int b = 0; b < RB; ++b) acc[j][b] = mfma16x16x4(gv[q][b], f4get(xa[q], j), acc[j][b]);
+  }
+  // tile j, register v: rank 16b + 4 l4 + v, feature k0 + 4 l16 + j
+  float* dp = dapart + (int64_t)blockIdx.y * rank * in_dim;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = 16 * b + 4 * l4 + v;
+        const int64_t k = k0 + 4 * l16 + j;
+        if (r < rank && k < in_dim) dp[(int64_t)r * in_dim + k] = acc[j][b][v];
+      }
+}
+
+__device__ __forceinline__ void adamw1(float& p, float gr, float& m, float& v, float lr,
+                                       const AdamHP& hp) {
   m = hp.beta1 * m + (1.0f - hp.beta1) * gr;
   v = hp.beta2 * v + (1.0f - hp.beta2) * gr * gr;
   const float mh = m * hp.bc1, vh = v * hp.bc2;
   p -= lr * (mh / (sqrtf(vh) + hp.eps) + hp.wd * p);
-  return p;
 }
 
-// Partial dB over one chunk of L_ROWS token rows: thread (o, r-group) owns
-// outputs (o, r) for r = rg, rg+4, ...  part[chunk][o][r].
-__global__ __launch_bounds__(256) void lora_db_part_kernel(int64_t rows, int64_t out_dim,
-                                                           int rank,
-                                                           const float* __restrict__ dy,
-                                                           const void* __restrict__ hv, int hdt,
-                                                           float* __restrict__ part) {
-  const int t = threadIdx.x;
-  const int64_t o = (int64_t)blockIdx.x * 64 + (t & 63);
-  const int rg = t >> 6;
-  const int64_t i0 = (int64_t)blockIdx.y * L_ROWS;
-  const int64_t i1 = min(rows, i0 + L_ROWS);
-  float acc[LR_MAX / 4];
-#pragma unroll
-  for (int j = 0; j < LR_MAX / 4; ++j) acc[j] = 0.f;
-  if (o < out_dim) {
-    for (int64_t i = i0; i < i1; ++i) {
-      const float d = dy[i * out_dim + o];
-#pragma unroll
-      for (int j = 0; j < LR_MAX / 4; ++j) {
-        const int r = rg + 4 * j;
-        if (r < rank) {
-          const float hh = hdt == F32 ? ((const float*)hv)[i * rank + r]
-                                      : bf2f(((const uint16_t*)hv)[i * rank + r]);
-          acc[j] += d * hh;
-        }
-      }
-    }
-    float* pp = part + ((int64_t)blockIdx.y * out_dim + o) * rank;
-#pragma unroll
-    for (int j = 0; j < LR_MAX / 4; ++j) {
-      const int r = rg + 4 * j;
-      if (r < rank) pp[r] = acc[j];
-    }
-  }
-}
-
-// dB = s sum_chunks part, then AdamW on B (lr_b).
-__global__ __launch_bounds__(256) void lora_db_update_kernel(int64_t n, int chunks,
-                                                             const float* __restrict__ part,
-                                                             float s, float* B, float* m,
-                                                             float* v, float* grad_b, AdamHP hp) {
+// Elements [0, nb): dB = s sum_slices dbpart, then AdamW on B (lr_b).
+// Elements [nb, nb + ng): g = s sum_groups gpart (ng = rows * 16 RB).
+__global__ __launch_bounds__(256) void lora_b_update_kernel(int64_t nb, int slices,
+                                                            const float* __restrict__ dbpart,
+                                                            int64_t ng, int groups,
+                                                            const float* __restrict__ gpart,
+                                                            float* __restrict__ g, float s,
+                                                            float* B, float* m, float* v,
+                                                            float* grad_b, AdamHP hp) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= n) return;
-  float d = 0.f;
-  for (int c = 0; c < chunks; ++c) d += part[(int64_t)c * n + e];
-  d *= s;
-  if (grad_b) grad_b[e] = d;
-  float p = B[e], mm = m[e], vv = v[e];
-  adamw1(p, d, mm, vv, hp.lr_b, hp);
-  B[e] = p;
-  m[e] = mm;
-  v[e] = vv;
-}
-
-// Partial dA over one chunk of token rows: thread (k, r-group) owns (r, k).
-template <typename T>
-__global__ __launch_bounds__(256) void lora_da_part_kernel(int64_t rows, int64_t in_dim,
-                                                           int rank, const float* __restrict__ g,
-                                                           const T* __restrict__ x,
-                                                           float* __restrict__ part) {
-  const int t = threadIdx.x;
-  const int64_t k = (int64_t)blockIdx.x * 64 + (t & 63);
-  const int rg = t >> 6;
-  const int64_t i0 = (int64_t)blockIdx.y * L_ROWS;
-  const int64_t i1 = min(rows, i0 + L_ROWS);
-  float acc[LR_MAX / 4];
-#pragma unroll
-  for (int j = 0; j < LR_MAX / 4; ++j) acc[j] = 0.f;
-  if (k < in_dim) {
-    for (int64_t i = i0; i < i1; ++i) {
-      const float xv = Act<T>::ld(x, i * in_dim + k);
-#pragma unroll
-      for (int j = 0; j < LR_MAX / 4; ++j) {
-        const int r = rg + 4 * j;
-        if (r < rank) acc[j] += g[i * rank + r] * xv;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < LR_MAX / 4; ++j) {
-      const int r = rg + 4 * j;
-      if (r < rank) part[((int64_t)blockIdx.y * rank + r) * in_dim + k] = acc[j];
-    }
+  if (e < nb) {
+    float d = 0.f;
+    for (int c = 0; c < slices; ++c) d += dbpart[(int64_t)c * nb + e];
+    d *= s;
+    if (grad_b) grad_b[e] = d;
+    float p = B[e], mm = m[e], vv = v[e];
+    adamw1(p, d, mm, vv, hp.lr_b, hp);
+    B[e] = p;
+    m[e] = mm;
+    v[e] = vv;
+  } else if (e < nb + ng) {
+    const int64_t f = e - nb;
+    float d = 0.f;
+    for (int c = 0; c < groups; ++c) d += gpart[(int64_t)c * ng + f];
+    g[f] = s * d;
   }
 }
 
-// dA = sum_chunks part, AdamW on A (lr_a), per-workgroup sum of dA^2.
-__global__ __launch_bounds__(256) void lora_da_update_kernel(int64_t n, int chunks,
-                                                             const float* __restrict__ part,
-                                                             float* A, float* m, float* v,
-                                                             float* grad_a,
-                                                             float* __restrict__ sq_part,
-                                                             AdamHP hp) {
+// dA = sum_slices dapart, AdamW on A (lr_a), per-workgroup sum of dA^2.
+__global__ __launch_bounds__(256) void lora_a_update_kernel(int64_t n, int slices,
+                                                            const float* __restrict__ dapart,
+                                                            float* A, float* m, float* v,
+                                                            float* grad_a,
+                                                            float* __restrict__ sq_part,
+                                                            AdamHP hp) {
   __shared__ float red[4];
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   float sq = 0.f;
   if (e < n) {
     float d = 0.f;
-    for (int c = 0; c < chunks; ++c) d += part[(int64_t)c * n + e];
+    for (int c = 0; c < slices; ++c) d += dapart[(int64_t)c * n + e];
     if (grad_a) grad_a[e] = d;
     sq = d * d;
     float p = A[e], mm = m[e], vv = v[e];
@@ -167,24 +270,85 @@ __global__ __launch_bounds__(256) void lora_da_update_kernel(int64_t n, int chun
   if (threadIdx.x == 0) sq_part[blockIdx.x] = sq;
 }
 
-__global__ void lora_gnorm_kernel(int nparts, const float* __restrict__ sq_part,
-                                  float* gnorm_sq) {
-  if (threadIdx.x != 0) return;
+// gnorm_sq += sum of the per-workgroup partials, in index order.
+__global__ __launch_bounds__(64) void lora_gnorm_kernel(int nparts,
+                                                        const float* __restrict__ sq_part,
+                                                        float* gnorm_sq) {
+  const int lane = threadIdx.x;
   float s = 0.f;
-  for (int i = 0; i < nparts; ++i) s += sq_part[i];
-  *gnorm_sq += s;
+  for (int i = lane; i < nparts; i += 64) s += sq_part[i];
+  s = wave_sum(s);
+  if (lane == 0) *gnorm_sq += s;
 }
 
-static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+namespace {
+
+// Row slicing of one pass: `cols` columns in groups of 256, rows cut into
+// slices of a multiple of 16 rows so that about L_TARGET workgroups run.
+struct Slicing {
+  int64_t groups, rs, slices;
+};
+Slicing slicing(int64_t rows, int64_t cols) {
+  Slicing s;
+  s.groups = cdiv(cols, LG_COLS);
+  if (rows <= 0) {
+    s.rs = 16;
+    s.slices = 0;
+    return s;
+  }
+  int64_t want = cdiv(L_TARGET, s.groups);
+  want = want < 1 ? 1 : want;
+  s.rs = cdiv(cdiv(rows, want), 16) * 16;
+  s.slices = cdiv(rows, s.rs);
+  return s;
+}
+
+// Workspace carve-up, in floats: g | gpart | part (dB, then dA) | sq.
+struct LoraWs {
+  int64_t g, gpart, part, sq, end;
+};
+LoraWs lora_ws(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank) {
+  const int64_t rp = cdiv(rank, 16) * 16;
+  const Slicing sy = slicing(rows, out_dim), sa = slicing(rows, in_dim);
+  const int64_t pb = sy.slices * out_dim * rank, pa = sa.slices * rank * in_dim;
+  LoraWs w;
+  w.g = 0;
+  w.gpart = w.g + cdiv(rows * rp, 64) * 64;
+  w.part = w.gpart + cdiv(sy.groups * rows * rp, 64) * 64;
+  w.sq = w.part + cdiv(pb > pa ? pb : pa, 64) * 64;
+  w.end = w.sq + cdiv(cdiv(rank * in_dim, 256), 64) * 64;
+  return w;
+}
+
+template <int RB>
+void launch_dy(int64_t rows, int64_t out_dim, int rank, const Slicing& sl, const float* dy,
+               const void* h, int hdt, const float* B, float* gpart, float* dbpart,
+               hipStream_t s) {
+  const dim3 grid((unsigned)sl.groups, (unsigned)sl.slices);
+  if (out_dim % 4 == 0)
+    lora_dy_kernel<RB, true><<<grid, 256, 0, s>>>(rows, out_dim, rank, sl.rs, dy, h, hdt, B,
+                                                  gpart, dbpart);
+  else
+    lora_dy_kernel<RB, false><<<grid, 256, 0, s>>>(rows, out_dim, rank, sl.rs, dy, h, hdt, B,
+                                                   gpart, dbpart);
+}
+
+template <int RB>
+void launch_da(int64_t rows, int64_t in_dim, int rank, const Slicing& sl, const float* g,
+               const void* x, int dt, float* dapart, hipStream_t s) {
+  const dim3 grid((unsigned)sl.groups, (unsigned)sl.slices);
+  if (dt == F32)
+    lora_da_kernel<RB, float><<<grid, 256, 0, s>>>(rows, in_dim, rank, sl.rs, g,
+                                                   (const float*)x, dapart);
+  else
+    lora_da_kernel<RB, bf16><<<grid, 256, 0, s>>>(rows, in_dim, rank, sl.rs, g,
+                                                  (const bf16*)x, dapart);
+}
+
+}  // namespace
 
 size_t lora_ws_bytes(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank) {
-  const int64_t chunks = cdiv(rows, L_ROWS);
-  const int64_t g = rows * rank;
-  const int64_t pb = chunks * out_dim * rank;
-  const int64_t pa = chunks * rank * in_dim;
-  const int64_t sq = cdiv(rank * in_dim, 256);
-  const int64_t n = g + (pb > pa ? pb : pa) + sq + 64;
-  return (size_t)n * sizeof(float);
+  return (size_t)lora_ws(rows, in_dim, out_dim, rank).end * sizeof(float);
 }
 
 hipError_t launch_lora_adamw(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank,
@@ -192,50 +356,53 @@ hipError_t launch_lora_adamw(int64_t rows, int64_t in_dim, int64_t out_dim, int6
                              float* B, float* m_a, float* v_a, float* m_b, float* v_b,
                              float* grad_a, float* grad_b, float* gnorm_sq, float scaling,
                              const AdamHP& hp, void* ws, hipStream_t s) {
-  const int64_t chunks = cdiv(rows, L_ROWS);
-  float* g = (float*)ws;
-  float* part = g + rows * rank;
-  const int64_t pb = chunks * out_dim * rank, pa = chunks * rank * in_dim;
-  float* sq = part + (pb > pa ? pb : pa);
-  const int r = (int)rank;
-  dim3 block(256);
+  const LoraWs o = lora_ws(rows, in_dim, out_dim, rank);
+  float* const base = (float*)ws;
+  struct {
+    float *g, *gpart, *part, *sq;
+  } w = {base + o.g, base + o.gpart, base + o.part, base + o.sq};
+  const Slicing sy = slicing(rows, out_dim), sa = slicing(rows, in_dim);
+  const int r = (int)rank, rb = (int)cdiv(rank, 16);
+  const int64_t rp = 16 * rb;
+  const double esz = dt == F32 ? 4.0 : 2.0;
   hipError_t e;
   if (rows > 0) {
-    lora_g_kernel<<<dim3((unsigned)rows), block, 0, s>>>(out_dim, r, dy, B, scaling, g);
-    mark("lora_g", (double)rows * out_dim * 4 + (double)out_dim * rank * 4 + (double)rows * rank * 4,
-         2.0 * rows * out_dim * rank, s);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    lora_db_part_kernel<<<dim3((unsigned)cdiv(out_dim, 64), (unsigned)chunks), block, 0, s>>>(
-        rows, out_dim, r, dy, h, dt, part);
-    mark("lora_db_part", (double)rows * out_dim * 4 + (double)rows * rank * (dt == F32 ? 4 : 2),
-         2.0 * rows * out_dim * rank, s);
+    switch (rb) {
+      case 1: launch_dy<1>(rows, out_dim, r, sy, dy, h, dt, B, w.gpart, w.part, s); break;
+      case 2: launch_dy<2>(rows, out_dim, r, sy, dy, h, dt, B, w.gpart, w.part, s); break;
+      case 3: launch_dy<3>(rows, out_dim, r, sy, dy, h, dt, B, w.gpart, w.part, s); break;
+      default: launch_dy<4>(rows, out_dim, r, sy, dy, h, dt, B, w.gpart, w.part, s); break;
+    }
+    mark("lora_dy", (double)rows * out_dim * 4 + (double)rows * rank * esz + (double)out_dim * rank * 4,
+         4.0 * rows * out_dim * rank, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // with no token rows the gradients are zero: a single zero "chunk"
-  const int nb = (int)(rows > 0 ? chunks : 0);
-  lora_db_update_kernel<<<dim3((unsigned)cdiv(out_dim * rank, 256)), block, 0, s>>>(
-      out_dim * rank, nb, part, scaling, B, m_b, v_b, grad_b, hp);
-  mark("lora_adamw_b", (double)out_dim * rank * 4 * (6 + (grad_b ? 1 : 0)), 12.0 * out_dim * rank, s);
+  // with no token rows the gradients are zero: no slices, no groups
+  const int64_t nb = out_dim * rank, ng = rows > 0 ? rows * rp : 0;
+  lora_b_update_kernel<<<dim3((unsigned)cdiv(nb + ng, 256)), 256, 0, s>>>(
+      nb, (int)sy.slices, w.part, ng, (int)sy.groups, w.gpart, w.g, scaling, B, m_b, v_b, grad_b,
+      hp);
+  mark("lora_adamw_b", (double)nb * 4 * (6 + (grad_b ? 1 : 0)) + (double)ng * 4, 12.0 * nb, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (rows > 0) {
-    if (dt == F32)
-      lora_da_part_kernel<float><<<dim3((unsigned)cdiv(in_dim, 64), (unsigned)chunks), block, 0,
-                                   s>>>(rows, in_dim, r, g, (const float*)x, part);
-    else
-      lora_da_part_kernel<bf16><<<dim3((unsigned)cdiv(in_dim, 64), (unsigned)chunks), block, 0,
-                                  s>>>(rows, in_dim, r, g, (const bf16*)x, part);
-    mark("lora_da_part", (double)rows * in_dim * (dt == F32 ? 4 : 2) + (double)rows * rank * 4,
+    switch (rb) {
+      case 1: launch_da<1>(rows, in_dim, r, sa, w.g, x, dt, w.part, s); break;
+      case 2: launch_da<2>(rows, in_dim, r, sa, w.g, x, dt, w.part, s); break;
+      case 3: launch_da<3>(rows, in_dim, r, sa, w.g, x, dt, w.part, s); break;
+      default: launch_da<4>(rows, in_dim, r, sa, w.g, x, dt, w.part, s); break;
+    }
+    mark("lora_da", (double)rows * in_dim * esz + (double)rows * rank * 4,
          2.0 * rows * in_dim * rank, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int nsq = (int)cdiv(rank * in_dim, 256);
-  lora_da_update_kernel<<<dim3((unsigned)nsq), block, 0, s>>>(rank * in_dim, nb, part, A, m_a,
-                                                              v_a, grad_a, sq, hp);
+  lora_a_update_kernel<<<dim3((unsigned)nsq), 256, 0, s>>>(rank * in_dim, (int)sa.slices, w.part,
+                                                            A, m_a, v_a, grad_a, w.sq, hp);
   mark("lora_adamw_a", (double)rank * in_dim * 4 * (6 + (grad_a ? 1 : 0)), 14.0 * rank * in_dim, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (gnorm_sq != nullptr) {
-    lora_gnorm_kernel<<<dim3(1), dim3(64), 0, s>>>(nsq, sq, gnorm_sq);
-    mark("lora_gnorm", 8, (double)nsq, s);
+    lora_gnorm_kernel<<<dim3(1), dim3(64), 0, s>>>(nsq, w.sq, gnorm_sq);
+    mark("lora_gnorm", 4.0 * nsq + 8, (double)nsq, s);
     e = hipGetLastError();
   }
   return e;

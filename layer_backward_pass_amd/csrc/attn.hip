@@ -5,24 +5,292 @@
 // Score Backward" (dQ = scale dS K); entrenar wgpu_backward.rs attention
 // backward for dV = P^T dCtx.  Query head h reads KV head h / grp.
 //
-// Sequence path (s_q > 1), v_mfma_f32_16x16x4_f32 throughout:
-//   attn_dq_kernel  one workgroup per (64 query rows, head); each wave owns
-//                   16 rows, keeps its dCtx rows in registers, and walks the
-//                   key blocks up to the causal limit: dA on the matrix
-//                   cores, P read straight into the accumulator layout, dS
-//                   formed in registers, transposed through LDS and
-//                   multiplied by the K block.  delta comes from
-//                   <dCtx, ctx> (ctx = P V), so P is streamed once.
-//   attn_dv_kernel  one workgroup per (32 keys, KV head); sums P^T dCtx over
-//                   the heads of the group and the query blocks that can
-//                   see those keys.
-//   attn_delta_kernel  delta = rowsum(P o dA) formed from P directly, for
-//                   callers that do not pass ctx.
-// One query row (decode) goes to the kernels in decode.hip.
+// Sequence path (s_q > 1), float32 (v_mfma_f32_16x16x4_f32):
+//   attn_dq_f32_kernel  workgroup = 16*QW query rows x HW heads of one KV
+//       group (HW*QW = 4 waves).  Each wave keeps its dCtx rows in
+//       registers and walks 32-key tiles of K and V staged in LDS (the next
+//       tile is fetched into registers while the current one is used).
+//       The scores are formed transposed, dA^T = V dCtx^T, so that a lane
+//       holds one query and four consecutive keys: P is read with one
+//       16-byte load per lane straight into the accumulator layout, and the
+//       resulting dS^T registers are already the A operand of dQ = dS K.
+//       delta comes from <dCtx, ctx> (ctx = P V), so P is streamed once.
+//       Query tiles are issued latest-first: under a causal mask they are
+//       the longest.
+//   attn_dv_f32_kernel  workgroup = 64 keys of one KV group and one chunk of
+//       query rows; each wave owns 16 keys x all head dims and sums
+//       P^T dCtx over the heads of the group; dCtx rows are staged in LDS.
+//       Chunks give the launch enough workgroups; their partial sums are
+//       added in chunk order by attn_dv_reduce_kernel.
+// bfloat16 inputs use the kernels further down.  One query row (decode)
+// goes to the kernels in decode.hip.
 #include "common.h"
 #include "kernels.h"
 
 namespace lbp {
+
+__host__ __device__ static inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Four consecutive floats of one P row from column `col`, zero past `ncol`.
+// vec: the row start is 16-byte aligned (ncol % 4 == 0).
+__device__ __forceinline__ float4 prow4(const float* rowp, int64_t col, int64_t ncol, bool vec) {
+  float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (vec) {
+    if (col < ncol) r = *reinterpret_cast<const float4*>(rowp + col);
+  } else {
+    if (col < ncol) r.x = rowp[col];
+    if (col + 1 < ncol) r.y = rowp[col + 1];
+    if (col + 2 < ncol) r.z = rowp[col + 2];
+    if (col + 3 < ncol) r.w = rowp[col + 3];
+  }
+  return r;
+}
+
+__device__ __forceinline__ float f4at(const float4& v, int j) {
+  return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+constexpr int FQ_KT = 32;  // keys per tile, float32 dq kernel
+constexpr int DV_KT = 64;  // keys per workgroup, dv kernels
+
+template <int D, int HW>
+__global__ __launch_bounds__(256) void attn_dq_f32_kernel(
+    int64_t s_q, int64_t s_kv, int Hq, int grp, const float* __restrict__ dctx,
+    const float* __restrict__ P, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ ctx, const float* __restrict__ delta_ws, float* __restrict__ dq,
+    float scale, int causal) {
+  constexpr int KT = FQ_KT, DK = D / 4, ND = D / 16, QW = 4 / HW, LDK = D + 4;
+  constexpr int NE = KT * D / 4;           // float4 per staged tile
+  constexpr int SE = (NE + 255) / 256;     // per thread
+  __shared__ float Vs[KT][LDK];
+  __shared__ float Ks[KT][LDK];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int l16 = lane & 15, c = lane >> 4;
+  const int64_t qt = causal ? (int64_t)(gridDim.x - 1 - blockIdx.x) : (int64_t)blockIdx.x;
+  const int h = (int)blockIdx.y * HW + (w % HW), g = h / grp;
+  const int64_t ldq = (int64_t)Hq * D, ldk = (int64_t)(Hq / grp) * D;
+  const int64_t qw0 = qt * (16 * QW);
+  const int64_t q0 = qw0 + 16 * (w / HW);
+  const int64_t qrow = q0 + l16;
+  const bool qok = qrow < s_q;
+  const bool vec = (s_kv & 3) == 0;
+
+  // B operand of dA^T = V dCtx^T: lane (query qrow, group c) holds head dims
+  // DK*c .. DK*c + DK - 1 (MFMA step j of that group is d = DK*c + j).
+  float dc[DK];
+#pragma unroll
+  for (int i = 0; i < DK; i += 4) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (qok) v = *reinterpret_cast<const float4*>(dctx + qrow * ldq + h * D + DK * c + i);
+    dc[i] = v.x;
+    dc[i + 1] = v.y;
+    dc[i + 2] = v.z;
+    dc[i + 3] = v.w;
+  }
+  float dl = 0.f;
+  if (ctx != nullptr) {
+#pragma unroll
+    for (int i = 0; i < DK; i += 4) {
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (qok) x = *reinterpret_cast<const float4*>(ctx + qrow * ldq + h * D + DK * c + i);
+      dl += dc[i] * x.x + dc[i + 1] * x.y + dc[i + 2] * x.z + dc[i + 3] * x.w;
+    }
+    dl += __shfl_xor(dl, 16, 64);
+    dl += __shfl_xor(dl, 32, 64);
+  } else if (qok) {
+    dl = delta_ws[(int64_t)h * s_q + qrow];
+  }
+
+  floatx4 acc[ND];
+#pragma unroll
+  for (int f = 0; f < ND; ++f) acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t off = s_kv - s_q;
+  const int64_t qlast = min(s_q, qw0 + 16 * QW) - 1;
+  const int64_t kend = causal ? min(s_kv, off + qlast + 1) : s_kv;
+  const int ntile = (int)cdiv64(kend, KT);
+  const float* prow = P + ((int64_t)h * s_q + (qok ? qrow : 0)) * s_kv;
+
+  float4 sv[SE], sk[SE], pc[2], pn[2];
+  auto fetch = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < SE; ++i) {
+      const int e = t + 256 * i;
+      const int64_t key = k0 + e / (D / 4);
+      const int d = 4 * (e % (D / 4));
+      sv[i] = sk[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e < NE && key < s_kv) {
+        sv[i] = *reinterpret_cast<const float4*>(V + key * ldk + g * D + d);
+        sk[i] = *reinterpret_cast<const float4*>(K + key * ldk + g * D + d);
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      pn[nt] = qok ? prow4(prow, k0 + 16 * nt + 4 * c, s_kv, vec) : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  if (ntile > 0) fetch(0);
+  for (int it = 0; it < ntile; ++it) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < SE; ++i) {
+      const int e = t + 256 * i;
+      if (e < NE) {
+        const int kr = e / (D / 4), d = 4 * (e % (D / 4));
+        *reinterpret_cast<float4*>(&Vs[kr][d]) = sv[i];
+        *reinterpret_cast<float4*>(&Ks[kr][d]) = sk[i];
+      }
+    }
+    pc[0] = pn[0];
+    pc[1] = pn[1];
+    __syncthreads();
+    if (it + 1 < ntile) fetch((int64_t)(it + 1) * KT);
+
+    // dA^T for two 16-key sub-tiles: row = key 16 nt + 4c + v, col = query l16.
+    // Four partial accumulators per sub-tile keep eight MFMA chains in flight.
+    floatx4 da[2][4];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) da[nt][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s4 = 0; s4 < DK / 4; ++s4)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float4 v4 = *reinterpret_cast<const float4*>(&Vs[16 * nt + l16][DK * c + 4 * s4]);
+        da[nt][0] = mfma16x16x4(v4.x, dc[4 * s4 + 0], da[nt][0]);
+        da[nt][1] = mfma16x16x4(v4.y, dc[4 * s4 + 1], da[nt][1]);
+        da[nt][2] = mfma16x16x4(v4.z, dc[4 * s4 + 2], da[nt][2]);
+        da[nt][3] = mfma16x16x4(v4.w, dc[4 * s4 + 3], da[nt][3]);
+      }
+    // dS^T = P^T o (dA^T - delta); then dQ += dS K with k index = key
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float a = (da[nt][0][v] + da[nt][1][v]) + (da[nt][2][v] + da[nt][3][v]);
+        const float ds = f4at(pc[nt], v) * (a - dl);
+#pragma unroll
+        for (int f = 0; f < ND; ++f)
+          acc[f] = mfma16x16x4(ds, Ks[16 * nt + 4 * c + v][16 * f + l16], acc[f]);
+      }
+  }
+#pragma unroll
+  for (int f = 0; f < ND; ++f)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t row = q0 + 4 * c + v;
+      if (row < s_q) dq[row * ldq + h * D + 16 * f + l16] = scale * acc[f][v];
+    }
+}
+
+// dV for 64 keys of KV group blockIdx.y over query chunk (blockIdx.x % cmax)
+// of `qc` rows.  MFMA rows = keys (wave w: 16w .. 16w+15), cols = head dims,
+// k = query rows (step s, group c: row qb + 4s + c).  Output: dv itself when
+// cmax == 1, else partial sums part[chunk][key][kv_dim].
+template <int D>
+__global__ __launch_bounds__(256) void attn_dv_f32_kernel(int64_t s_q, int64_t s_kv, int Hq,
+                                                          int grp, int cmax, int64_t qc,
+                                                          const float* __restrict__ dctx,
+                                                          const float* __restrict__ P,
+                                                          float* __restrict__ out, int causal) {
+  constexpr int ND = D / 16, LDC = D == 16 ? 48 : D + 16;
+  constexpr int NE = 16 * D / 4;  // float4 per staged dCtx block
+  constexpr int SE = (NE + 255) / 256;
+  __shared__ float dCs[16][LDC];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int l16 = lane & 15, c = lane >> 4;
+  const int jt = (int)(blockIdx.x / cmax), ch = (int)(blockIdx.x % cmax);
+  const int g = blockIdx.y;
+  const int64_t ldq = (int64_t)Hq * D, ldk = (int64_t)(Hq / grp) * D;
+  const int64_t k0 = (int64_t)jt * DV_KT;
+  const int64_t off = s_kv - s_q;
+  int64_t qbeg = causal ? k0 - off : 0;
+  qbeg = qbeg < 0 ? 0 : qbeg / 16 * 16;
+  const int64_t qa = qbeg + ch * qc;
+  const int64_t qz = min(s_q, qa + qc);
+  const int64_t key = k0 + 16 * w + l16;
+  const bool kok = key < s_kv;
+  float* dst = out + (cmax > 1 ? (int64_t)ch * s_kv * ldk : 0);
+  if (qa >= qz) return;  // empty chunk (never chunk 0)
+
+  floatx4 acc[ND];
+#pragma unroll
+  for (int f = 0; f < ND; ++f) acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int64_t nqb = cdiv64(qz - qa, 16);
+  const int64_t nit = nqb * grp;
+  float4 st[SE];
+  float pa[4];
+  auto fetch = [&](int64_t it) {
+    const int h = g * grp + (int)(it / nqb);
+    const int64_t qb = qa + 16 * (it % nqb);
+#pragma unroll
+    for (int i = 0; i < SE; ++i) {
+      const int e = t + 256 * i;
+      const int64_t row = qb + e / (D / 4);
+      st[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e < NE && row < qz)
+        st[i] = *reinterpret_cast<const float4*>(dctx + row * ldq + h * D + 4 * (e % (D / 4)));
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int64_t row = qb + 4 * s + c;
+      pa[s] = (kok && row < qz) ? P[((int64_t)h * s_q + row) * s_kv + key] : 0.f;
+    }
+  };
+  fetch(0);
+  for (int64_t it = 0; it < nit; ++it) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < SE; ++i) {
+      const int e = t + 256 * i;
+      if (e < NE) *reinterpret_cast<float4*>(&dCs[e / (D / 4)][4 * (e % (D / 4))]) = st[i];
+    }
+    float a[4] = {pa[0], pa[1], pa[2], pa[3]};
+    __syncthreads();
+    if (it + 1 < nit) fetch(it + 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int f = 0; f < ND; ++f) acc[f] = mfma16x16x4(a[s], dCs[4 * s + c][16 * f + l16], acc[f]);
+  }
+#pragma unroll
+  for (int f = 0; f < ND; ++f)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t k = k0 + 16 * w + 4 * c + v;
+      if (k < s_kv) dst[k * ldk + g * D + 16 * f + l16] = acc[f][v];
+    }
+}
+
+// dv[key][:] = sum of the chunk partials that exist for the key's tile, in
+// chunk order (zero when no query row sees the key).
+__global__ __launch_bounds__(256) void attn_dv_reduce_kernel(int64_t s_q, int64_t s_kv,
+                                                             int64_t ldk, int cmax, int64_t qc,
+                                                             const float* __restrict__ part,
+                                                             float* __restrict__ dv, int causal) {
+  const int64_t n4 = s_kv * ldk / 4;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n4) return;
+  const int64_t key = 4 * e / ldk;
+  const int64_t k0 = key / DV_KT * DV_KT;
+  const int64_t off = s_kv - s_q;
+  int64_t qbeg = causal ? k0 - off : 0;
+  qbeg = qbeg < 0 ? 0 : qbeg / 16 * 16;
+  const int64_t nch = qbeg < s_q ? cdiv64(s_q - qbeg, qc) : 0;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t ch = 0; ch < nch && ch < cmax; ++ch) {
+    const float4 v = reinterpret_cast<const float4*>(part + ch * s_kv * ldk)[e];
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  reinterpret_cast<float4*>(dv)[e] = s;
+}
+
+// ---------------------------------------------------------------- bfloat16
+// (kept from the first version until the bf16 MFMA kernels replace them)
+
 
 constexpr int AQ = 64;  // query rows per dq workgroup (16 per wave)
 constexpr int AK = 32;  // keys per dq inner block
@@ -227,11 +495,106 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(int64_t s_q, int64_t s_
   if (lane == 0) delta[(int64_t)h * s_q + i] = s;
 }
 
+// Query chunking of the dv kernels: about DV_WG_TARGET workgroups
+// (key tiles x KV groups x chunks), chunks a multiple of 16 rows.
+constexpr int DV_WG_TARGET = 512;
+struct DvPlan {
+  int cmax;
+  int64_t qc;
+};
+static DvPlan dv_plan(int64_t s_q, int64_t s_kv, int64_t Hkv) {
+  DvPlan p;
+  const int64_t tiles = cdiv64(s_kv, DV_KT) * Hkv;
+  int64_t want = cdiv64(DV_WG_TARGET, tiles < 1 ? 1 : tiles);
+  const int64_t maxc = cdiv64(s_q < 1 ? 1 : s_q, 16);
+  want = want < 1 ? 1 : (want > maxc ? maxc : want);
+  p.qc = cdiv64(cdiv64(s_q < 1 ? 1 : s_q, want), 16) * 16;
+  p.cmax = (int)cdiv64(s_q < 1 ? 1 : s_q, p.qc);
+  return p;
+}
+
+// Workspace of the sequence path, 256-byte aligned pieces:
+//   delta [Hq, s_q] f32 (callers without ctx) | dv chunk partials f32
+struct AttnWs {
+  size_t delta, part, end;
+};
+static size_t al256(size_t b) { return (b + 255) / 256 * 256; }
+static AttnWs attn_ws(int64_t s_q, int64_t s_kv, int64_t Hq, int64_t Hkv, int64_t D) {
+  AttnWs w;
+  const DvPlan dp = dv_plan(s_q, s_kv, Hkv);
+  w.delta = 0;
+  w.part = al256((size_t)Hq * s_q * 4);
+  const size_t pb = dp.cmax > 1 ? (size_t)dp.cmax * s_kv * Hkv * D * 4 : 0;
+  w.end = w.part + al256(pb);
+  return w;
+}
+
 size_t attn_ws_bytes(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_kv_heads,
                      int64_t head_dim) {
-  (void)n_kv_heads;
-  if (s_q == 1) return dec_attn_ws_bytes(s_kv, n_heads, head_dim);
-  return (size_t)n_heads * s_q * sizeof(float);
+  const size_t seq = attn_ws(s_q, s_kv, n_heads, n_kv_heads, head_dim).end;
+  if (s_q == 1) {
+    const size_t d = dec_attn_ws_bytes(s_kv, n_heads, head_dim);
+    return d > seq ? d : seq;
+  }
+  return seq;
+}
+
+// unmasked (query, key) pairs per head: the work the method must do
+static double attn_pairs(int64_t s_q, int64_t s_kv, int causal) {
+  return causal ? (double)s_q * (s_kv - s_q) + 0.5 * (double)s_q * (s_q + 1)
+                : (double)s_q * s_kv;
+}
+
+template <int D, int HW>
+static void launch_dq_f32(int64_t s_q, int64_t s_kv, int Hq, int grp, const float* dctx,
+                          const float* P, const float* K, const float* V, const float* ctx,
+                          const float* delta, float* dq, float scale, int causal, hipStream_t s) {
+  constexpr int QW = 4 / HW;
+  const dim3 grid((unsigned)cdiv64(s_q, 16 * QW), (unsigned)(Hq / HW));
+  attn_dq_f32_kernel<D, HW><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta,
+                                                 dq, scale, causal);
+}
+
+template <int D>
+static hipError_t attn_launch_f32(int64_t s_q, int64_t s_kv, int Hq, int Hkv, const float* dctx,
+                                  const float* P, const float* K, const float* V,
+                                  const float* ctx, float* dq, float* dv, float scale, int causal,
+                                  void* ws, hipStream_t s) {
+  const int grp = Hq / Hkv;
+  const AttnWs wl = attn_ws(s_q, s_kv, Hq, Hkv, D);
+  float* delta = (float*)((char*)ws + wl.delta);
+  const double pairs = attn_pairs(s_q, s_kv, causal);
+  const double pbytes = pairs * Hq * 4, qbytes = (double)s_q * Hq * D * 4;
+  const double kvbytes = (double)s_kv * Hkv * D * 4;
+  hipError_t e;
+  if (ctx == nullptr) {
+    attn_delta_kernel<float, D><<<dim3((unsigned)cdiv64(s_q, 4), (unsigned)Hq), 256, 0, s>>>(
+        s_q, s_kv, Hq, grp, dctx, P, V, delta, causal);
+    mark("attn_delta", pbytes + qbytes + kvbytes + (double)Hq * s_q * 4, 2.0 * D * pairs * Hq, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int hw = grp % 4 == 0 ? 4 : (grp % 2 == 0 ? 2 : 1);
+  if (hw == 4)
+    launch_dq_f32<D, 4>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta, dq, scale, causal, s);
+  else if (hw == 2)
+    launch_dq_f32<D, 2>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta, dq, scale, causal, s);
+  else
+    launch_dq_f32<D, 1>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta, dq, scale, causal, s);
+  mark("attn_dq_f32", pbytes + qbytes * (ctx ? 3 : 2) + 2 * kvbytes, 4.0 * D * pairs * Hq, s);
+  if ((e = hipGetLastError()) != hipSuccess || dv == nullptr) return e;
+  const DvPlan dp = dv_plan(s_q, s_kv, Hkv);
+  float* part = dp.cmax > 1 ? (float*)((char*)ws + wl.part) : dv;
+  const dim3 grid((unsigned)(cdiv64(s_kv, DV_KT) * dp.cmax), (unsigned)Hkv);
+  attn_dv_f32_kernel<D><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dp.cmax, dp.qc, dctx, P, part,
+                                             causal);
+  mark("attn_dv_f32", pbytes + qbytes + kvbytes * (dp.cmax > 1 ? dp.cmax : 1),
+       2.0 * D * pairs * Hq, s);
+  if ((e = hipGetLastError()) != hipSuccess || dp.cmax == 1) return e;
+  const int64_t n4 = s_kv * Hkv * D / 4;
+  attn_dv_reduce_kernel<<<dim3((unsigned)cdiv64(n4, 256)), 256, 0, s>>>(
+      s_q, s_kv, (int64_t)Hkv * D, dp.cmax, dp.qc, part, dv, causal);
+  mark("attn_dv_reduce", kvbytes * (dp.cmax + 1), 0, s);
+  return hipGetLastError();
 }
 
 template <typename T, int D>
@@ -241,9 +604,7 @@ static hipError_t attn_launch(int64_t s_q, int64_t s_kv, int Hq, int Hkv, const 
   const int grp = Hq / Hkv;
   const double es = sizeof(T);
   dim3 block(256);
-  // unmasked (query, key) pairs per head: the work the method must do
-  const double pairs = causal ? (double)s_q * (s_kv - s_q) + 0.5 * (double)s_q * (s_q + 1)
-                              : (double)s_q * s_kv;
+  const double pairs = attn_pairs(s_q, s_kv, causal);
   const double pbytes = pairs * Hq * es, qbytes = (double)s_q * Hq * D;
   const double kvbytes = (double)s_kv * Hkv * D;
   dim3 gq((unsigned)((s_q + AQ - 1) / AQ), (unsigned)Hq);
@@ -276,11 +637,16 @@ template <typename T>
 static hipError_t attn_dispatch_d(int64_t s_q, int64_t s_kv, int Hq, int Hkv, int D,
                                   const float* dctx, const void* P, const void* K, const void* V,
                                   const void* ctx, float* dq, float* dv, float scale, int causal,
-                                  float* ws, hipStream_t s) {
-#define LBP_ATTN_D(DD)                                                                        \
-  case DD:                                                                                    \
-    return attn_launch<T, DD>(s_q, s_kv, Hq, Hkv, dctx, (const T*)P, (const T*)K, (const T*)V, \
-                              (const T*)ctx, dq, dv, scale, causal, ws, s);
+                                  void* ws, hipStream_t s) {
+#define LBP_ATTN_D(DD)                                                                         \
+  case DD:                                                                                     \
+    if constexpr (sizeof(T) == 4)                                                              \
+      return attn_launch_f32<DD>(s_q, s_kv, Hq, Hkv, dctx, (const float*)P, (const float*)K,   \
+                                 (const float*)V, (const float*)ctx, dq, dv, scale, causal, ws, \
+                                 s);                                                           \
+    else                                                                                       \
+      return attn_launch<T, DD>(s_q, s_kv, Hq, Hkv, dctx, (const T*)P, (const T*)K,            \
+                                (const T*)V, (const T*)ctx, dq, dv, scale, causal, (float*)ws, s);
   switch (D) {
     LBP_ATTN_D(16)
     LBP_ATTN_D(32)
@@ -319,9 +685,9 @@ hipError_t launch_attn_bwd(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n
   }
   if (dt == F32)
     return attn_dispatch_d<float>(s_q, s_kv, (int)n_heads, (int)n_kv_heads, (int)head_dim, dctx,
-                                  P, K, V, ctx, dq, dv, scale, causal, (float*)ws, s);
+                                  P, K, V, ctx, dq, dv, scale, causal, ws, s);
   return attn_dispatch_d<bf16>(s_q, s_kv, (int)n_heads, (int)n_kv_heads, (int)head_dim, dctx, P,
-                               K, V, ctx, dq, dv, scale, causal, (float*)ws, s);
+                               K, V, ctx, dq, dv, scale, causal, ws, s);
 }
 
 }  // namespace lbp

@@ -71,6 +71,14 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return s;
 }
 
+// Workgroups are handed to the 8 XCDs round-robin by linear id.  Renumber
+// them so that XCD x runs one contiguous block of the T work items: items
+// that share operands (consecutive ids) then share that XCD's L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t L, int64_t T) {
+  const int64_t x = L & 7, j = L >> 3, q = T >> 3, r = T & 7;
+  return x * q + (x < r ? x : r) + j;
+}
+
 __device__ __forceinline__ floatx4 mfma16x16x4(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }

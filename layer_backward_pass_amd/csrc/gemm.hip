@@ -14,13 +14,15 @@ constexpr int GBM = 128, GBN = 128;
 
 // Output tile of the 16x16 MFMA accumulators: lane l holds rows 4*(l/16)+v
 // (v = 0..3) of column l%16.
+template <int FM, int FN>
 __device__ __forceinline__ void store_tile(float* C, int64_t ldc, int64_t M, int64_t N,
-                                           int64_t row0, int64_t col0, const floatx4 (&acc)[4][4]) {
+                                           int64_t row0, int64_t col0,
+                                           const floatx4 (&acc)[FM][FN]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int fi = 0; fi < 4; ++fi)
+  for (int fi = 0; fi < FM; ++fi)
 #pragma unroll
-    for (int fj = 0; fj < 4; ++fj) {
+    for (int fj = 0; fj < FN; ++fj) {
       const int64_t c = col0 + fj * 16 + (lane & 15);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -31,82 +33,136 @@ __device__ __forceinline__ void store_tile(float* C, int64_t ldc, int64_t M, int
 }
 
 // ---------------------------------------------------------------------------
-// fp32 GEMM.  4 waves in a 2x2 grid, each wave 64x64 = 4x4 MFMA tiles.
-// LDS holds the A tile k-major (As[k][m]) and the B tile as stored
-// (Bs[k][n]); row stride 144 floats puts lane groups 16 banks apart.
-constexpr int F_BK = 16, F_LD = GBM + 16;
+// fp32 GEMM: workgroup of 8 waves (512 threads), tile 128 x 256, BK = 32; the
+// waves form a 2 x 4 grid of 64 x 64 wave tiles (4 x 4 MFMA accumulators).
+// Both LDS tiles are k-contiguous, As[m][k] and Bs[n][k], row stride 36
+// floats: one 16-byte read gives a lane four consecutive k, which feed four
+// MFMA steps (k slot c of step j is 16 kb + 4c + j for A and B alike).  A is
+// read from HBM as 16-byte row segments; B, stored [k][n], is read as 4-byte
+// columns that are coalesced across the lanes (n), so each thread gathers
+// four k of one n and writes them with one 16-byte LDS store.  The LDS tiles
+// are double-buffered: the next k-tile's global loads are in flight while
+// the current one is used, one barrier per k-tile.  A wide workgroup tile
+// keeps the HBM/L2 bytes per MFMA low; with one workgroup per CU the MFMA
+// pipe then stays about three quarters busy.
+constexpr int F_BK = 32, F_LD = F_BK + 4, F_BM = 128, F_BN = 256, F_NT = 512;
 
-template <typename TA>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(int64_t M, int64_t N, int64_t K,
-                                                       const TA* __restrict__ A, int64_t lda,
-                                                       const float* __restrict__ B1,
-                                                       const float* __restrict__ B2, int64_t K1,
-                                                       int64_t ldb, float* __restrict__ C,
-                                                       int64_t ldc, int64_t kps,
-                                                       int64_t split_stride) {
-  __shared__ float As[F_BK][F_LD];
-  __shared__ float Bs[F_BK][F_LD];
+__device__ __forceinline__ float f4at(const float4& v, int j) {
+  return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+__global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, int64_t K,
+                                                        const float* __restrict__ A, int64_t lda,
+                                                        const float* __restrict__ B1,
+                                                        const float* __restrict__ B2, int64_t K1,
+                                                        int64_t ldb, float* __restrict__ C,
+                                                        int64_t ldc, int64_t kps,
+                                                        int64_t split_stride) {
+  constexpr int NA = F_BM * F_BK / 4 / F_NT;   // A float4 per thread (2)
+  constexpr int NBQ = F_BK * F_BN / 4 / F_NT;  // B k-quads per thread (4)
+  constexpr int BQS = F_NT / F_BN;             // k-quad stride between them (2)
+  __shared__ __attribute__((aligned(16))) float As[2][F_BM][F_LD];
+  __shared__ __attribute__((aligned(16))) float Bs[2][F_BN][F_LD];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int64_t bm = (int64_t)blockIdx.y * GBM, bn = (int64_t)blockIdx.x * GBN;
-  const int64_t kbeg = (int64_t)blockIdx.z * kps;
+  const int l16 = lane & 15, c = lane >> 4;
+  // 1-D grid: item u -> (split z, column panel n, row tile m), m fastest,
+  // so the row tiles that read one weight panel run together on one XCD.
+  const int64_t nm = (M + F_BM - 1) / F_BM, nn = (N + F_BN - 1) / F_BN;
+  const int64_t u = xcd_remap(blockIdx.x, (int64_t)gridDim.x);
+  const int64_t z = u / (nm * nn), rem = u - z * nm * nn;
+  const int64_t bm = (rem % nm) * F_BM, bn = (rem / nm) * F_BN;
+  const int64_t kbeg = z * kps;
   const int64_t kend = min(K, kbeg + kps);
-  C += (int64_t)blockIdx.z * split_stride;
-  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  C += z * split_stride;
+  const int wm = (w & 1) * 64, wn = (w >> 1) * 64;
 
-  // global->register staging: A 2 x float4 (rows t/4 and t/4+64, k (t%4)*4),
-  // B 2 x float4 (k rows t/32 and t/32+8, n (t%32)*4)
-  float4 ra[2], rb[2];
-  auto load = [&](int64_t k0) {
+  // A: rows (t/8) + 64 i, k quad t%8.  B: column t % 256, k quads t/256 + 2i.
+  const int am = t >> 3, ak = 4 * (t & 7), bc = t % F_BN, bq0 = t / F_BN;
+  const bool full_mn = bm + F_BM <= M && bn + F_BN <= N;
+  const float* arow[NA];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int64_t m = bm + (t >> 2) + 64 * r;
-      const int64_t k = k0 + (t & 3) * 4;
-      ra[r] = (m < M && k < kend) ? Act<TA>::ld4(A, m * lda + k) : make_float4(0, 0, 0, 0);
-      const int64_t kb = k0 + (t >> 5) + 8 * r;
-      const int64_t n = bn + (t & 31) * 4;
-      if (kb < kend && n < N) {
-        const float* bp = kb < K1 ? B1 + kb * ldb : B2 + (kb - K1) * ldb;
-        rb[r] = *reinterpret_cast<const float4*>(bp + n);
-      } else {
-        rb[r] = make_float4(0, 0, 0, 0);
+  for (int i = 0; i < NA; ++i) arow[i] = A + (bm + am + 64 * i) * lda + ak;
+  int64_t boff[NBQ];  // offset of this thread's quad i inside a k-tile of B
+#pragma unroll
+  for (int i = 0; i < NBQ; ++i) boff[i] = (int64_t)(4 * (bq0 + BQS * i)) * ldb + bn + bc;
+  float4 ra[NA], rb[NBQ];
+  auto load = [&](int64_t k0) {
+    const bool one_src = k0 + F_BK <= K1 || k0 >= K1;
+    if (full_mn && k0 + F_BK <= kend && one_src) {
+      const float* base = k0 < K1 ? B1 + k0 * ldb : B2 + (k0 - K1) * ldb;
+#pragma unroll
+      for (int i = 0; i < NA; ++i) ra[i] = *reinterpret_cast<const float4*>(arow[i] + k0);
+#pragma unroll
+      for (int i = 0; i < NBQ; ++i) {
+        const float* bp = base + boff[i];
+        rb[i] = make_float4(bp[0], bp[ldb], bp[2 * ldb], bp[3 * ldb]);
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int64_t m = bm + am + 64 * i;
+      ra[i] = (m < M && k0 + ak < kend) ? *reinterpret_cast<const float4*>(arow[i] + k0)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const int64_t n = bn + bc;
+#pragma unroll
+    for (int i = 0; i < NBQ; ++i) {
+      const int64_t kq = k0 + 4 * (bq0 + BQS * i);
+      rb[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (kq < kend && n < N) {  // kend and K1 are multiples of 4: a quad is whole
+        const float* bp = (kq < K1 ? B1 + kq * ldb : B2 + (kq - K1) * ldb) + n;
+        rb[i] = make_float4(bp[0], bp[ldb], bp[2 * ldb], bp[3 * ldb]);
       }
     }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      *reinterpret_cast<float4*>(&As[buf][am + 64 * i][ak]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < NBQ; ++i)
+      *reinterpret_cast<float4*>(&Bs[buf][bc][4 * (bq0 + BQS * i)]) = rb[i];
   };
   floatx4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  if (kbeg < kend) load(kbeg);
-  for (int64_t k0 = kbeg; k0 < kend; k0 += F_BK) {
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int m = (t >> 2) + 64 * r, k = (t & 3) * 4;
-      As[k + 0][m] = ra[r].x;
-      As[k + 1][m] = ra[r].y;
-      As[k + 2][m] = ra[r].z;
-      As[k + 3][m] = ra[r].w;
-      *reinterpret_cast<float4*>(&Bs[(t >> 5) + 8 * r][(t & 31) * 4]) = rb[r];
-    }
-    __syncthreads();
-    if (k0 + F_BK < kend) load(k0 + F_BK);
-#pragma unroll
-    for (int kk = 0; kk < F_BK; kk += 4) {
-      float a[4], b[4];
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        a[f] = As[kk + (lane >> 4)][wm + f * 16 + (lane & 15)];
-        b[f] = Bs[kk + (lane >> 4)][wn + f * 16 + (lane & 15)];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x4(a[i], b[j], acc[i][j]);
-    }
+  int buf = 0;
+  if (kbeg < kend) {
+    load(kbeg);
+    stash(0);
   }
-  store_tile(C, ldc, M, N, bm + wm, bn + wn, acc);
+  __syncthreads();
+  for (int64_t k0 = kbeg; k0 < kend; k0 += F_BK) {
+    const bool more = k0 + F_BK < kend;
+    // operands of both 16-k halves first, then the next tile's global loads
+    float4 a[2][4], b[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[kb][i] = *reinterpret_cast<const float4*>(&As[buf][wm + 16 * i + l16][16 * kb + 4 * c]);
+        b[kb][i] = *reinterpret_cast<const float4*>(&Bs[buf][wn + 16 * i + l16][16 * kb + 4 * c]);
+      }
+    if (more) load(k0 + F_BK);
+    // one MFMA per accumulator per k step: 16 independent chains
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = mfma16x16x4(f4at(a[kb][i], q), f4at(b[kb][j], q), acc[i][j]);
+    if (more) stash(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+  store_tile<4, 4>(C, ldc, M, N, bm + wm, bn + wn, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -207,7 +263,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(int64_t M, int64_t N, in
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32bf16(a[i], b[j], acc[i][j]);
   }
-  store_tile(C, ldc, M, N, bm + wm, bn + wn, acc);
+  store_tile<4, 4>(C, ldc, M, N, bm + wm, bn + wn, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -236,12 +292,42 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(int64_t M, int64_t N
 
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Split-K count from a small cost model: the CUs take the workgroups in
+// rounds (one fp32 workgroup or two bf16 workgroups per CU at a time); a
+// round lasts one tile's k-range at the rate measured for the kernel; split-K
+// adds the HBM round trip of its partial sums.
+struct GemmPlan {
+  int bm, bn, nsp;
+  int64_t kps;
+};
+static GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int b_dt) {
+  const bool f32 = b_dt == F32;
+  const int bm = f32 ? F_BM : GBM, bn = f32 ? F_BN : GBN, bk = f32 ? F_BK : 32;
+  const int slots = f32 ? 256 : 512;
+  // ns per k index for one tile: 2 bm bn flops at the sustained MFMA rate
+  const double ns_per_k = f32 ? 2.0 * bm * bn / (256.0 * 0.74 * 2.4)
+                              : 2.0 * bm * bn / (2048.0 * 0.5 * 2.4);
+  const int64_t tiles = cdiv(M, bm) * cdiv(N, bn);
+  GemmPlan best{bm, bn, 1, K};
+  double best_t = 1e30;
+  for (int s = 1; s <= 16; ++s) {
+    const int64_t kps = cdiv(cdiv(K, s), 64) * 64;
+    const int nsp = (int)cdiv(K, kps);
+    if (nsp != s && s > 1) continue;
+    if (s > 1 && kps < 4 * bk) break;
+    const int64_t rounds = cdiv(tiles * nsp, slots);
+    double tt = (double)rounds * kps * ns_per_k * 1e-3;               // us
+    if (nsp > 1) tt += (2.0 * nsp + 1) * M * N * 4 / 6.0e6;            // us at 6 TB/s
+    if (tt < best_t * 0.98) {
+      best_t = tt;
+      best = GemmPlan{bm, bn, nsp, kps};
+    }
+  }
+  return best;
+}
+
 int gemm_splits(int64_t M, int64_t N, int64_t K, int b_dt) {
-  const int64_t tiles = cdiv(M, GBM) * cdiv(N, GBN);
-  int s = 1;
-  while (tiles * s < 256 && K / (2 * s) >= 256 && s < 16) s *= 2;
-  (void)b_dt;
-  return s;
+  return gemm_plan(M, N, K, b_dt).nsp;
 }
 
 size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K, int b_dt) {
@@ -253,9 +339,9 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
                        const void* B1, const void* B2, int64_t K1, int b_dt, int64_t ldb,
                        float* C, int64_t ldc, float* partials, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
-  const int splits = gemm_splits(M, N, K, b_dt);
-  const int64_t kps = cdiv(cdiv(K, splits), 64) * 64;
-  const int nsp = (int)cdiv(K, kps);
+  const GemmPlan pl = gemm_plan(M, N, K, b_dt);
+  const int64_t kps = pl.kps;
+  const int nsp = pl.nsp;
   float* out = nsp > 1 ? partials : C;
   const int64_t ldo = nsp > 1 ? N : ldc;
   const int64_t sstride = nsp > 1 ? M * N : 0;
@@ -263,11 +349,12 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
     B2 = B1;
     K1 = K;
   }
-  dim3 grid((unsigned)cdiv(N, GBN), (unsigned)cdiv(M, GBM), (unsigned)nsp), block(256);
+  dim3 grid((unsigned)cdiv(N, pl.bn), (unsigned)cdiv(M, pl.bm), (unsigned)nsp), block(256);
   if (b_dt == F32) {
-    gemm_f32_kernel<float><<<grid, block, 0, s>>>(M, N, K, (const float*)A, lda,
-                                                  (const float*)B1, (const float*)B2, K1, ldb,
-                                                  out, ldo, kps, sstride);
+    const dim3 grid1((unsigned)(cdiv(N, pl.bn) * cdiv(M, pl.bm) * nsp));
+    gemm_f32_kernel<<<grid1, dim3(F_NT), 0, s>>>(M, N, K, (const float*)A, lda, (const float*)B1,
+                                                (const float*)B2, K1, ldb, out, ldo, kps,
+                                                sstride);
   } else if (a_dt == F32) {
     gemm_bf16_kernel<float><<<grid, block, 0, s>>>(M, N, K, (const float*)A, lda,
                                                    (const uint16_t*)B1, (const uint16_t*)B2, K1,

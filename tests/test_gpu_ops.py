@@ -105,6 +105,10 @@ def _attn_inputs(seed, s_q, s_kv, Hq, Hkv, D, causal, dt):
     (1, 1000, 32, 4, 32, 1, 1, F32),
     (96, 96, 8, 2, 128, 1, 1, BF16),
     (1, 300, 8, 4, 64, 0, 0, BF16),
+    (200, 333, 6, 2, 32, 1, 1, F32),      # group of 3, key count not a multiple of 4
+    (64, 64, 16, 2, 16, 0, 0, F32),       # group of 8, no mask, no ctx
+    (257, 257, 4, 4, 128, 1, 1, F32),     # group of 1, one row past a tile
+    (33, 1030, 8, 2, 64, 1, 1, F32),      # short query block at the end of a long cache
 ])
 def test_attention(s_q, s_kv, Hq, Hkv, D, causal, use_ctx, dt):
     print("attn", s_q, s_kv, Hq, Hkv, D, causal, use_ctx, dt, flush=True)

@@ -347,9 +347,8 @@ int lorabwd_rope_backward(int64_t rows, int64_t n_heads, int64_t head_dim, const
 
 size_t lorabwd_attn_workspace_size(int64_t s_q, int64_t s_kv, int64_t n_heads,
                                    int64_t n_kv_heads, int64_t head_dim, int dtype) {
-  (void)dtype;
-  if (s_q < 0 || s_kv < 0 || n_heads < 1) return 0;
-  return up(attn_ws_bytes(s_q, s_kv, n_heads, n_kv_heads, head_dim));
+  if (s_q < 0 || s_kv < 0 || n_heads < 1 || n_kv_heads < 1) return 0;
+  return up(attn_ws_bytes(s_q, s_kv, n_heads, n_kv_heads, head_dim, dtype));
 }
 
 int lorabwd_attn_backward(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_kv_heads,
@@ -460,7 +459,7 @@ LayerPlan layer_plan(void* ws, const lorabwd_layer_desc* d, int64_t rq, int64_t 
   } else {
     const size_t f = ffn_plan(nullptr, S, H, I, d->dtype).bytes;
     const size_t o = S == 1 ? dgemv_part_bytes(qd, H) : gemm_partial_bytes(S, qd, H, d->dtype);
-    const size_t a = up(attn_ws_bytes(S, L, d->n_heads, d->n_kv_heads, d->head_dim));
+    const size_t a = up(attn_ws_bytes(S, L, d->n_heads, d->n_kv_heads, d->head_dim, d->dtype));
     for (size_t v : {f, o, a})
       if (v > sc) sc = v;
   }

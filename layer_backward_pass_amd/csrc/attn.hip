@@ -267,7 +267,8 @@ __global__ __launch_bounds__(256) void attn_dv_f32_kernel(int64_t s_q, int64_t s
 __global__ __launch_bounds__(256) void attn_dv_reduce_kernel(int64_t s_q, int64_t s_kv,
                                                              int64_t ldk, int cmax, int64_t qc,
                                                              const float* __restrict__ part,
-                                                             float* __restrict__ dv, int causal) {
+                                                             float* __restrict__ dv, int causal,
+                                                             int qgran) {
   const int64_t n4 = s_kv * ldk / 4;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= n4) return;
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(256) void attn_dv_reduce_kernel(int64_t s_q, int64_
   const int64_t k0 = key / DV_KT * DV_KT;
   const int64_t off = s_kv - s_q;
   int64_t qbeg = causal ? k0 - off : 0;
-  qbeg = qbeg < 0 ? 0 : qbeg / 16 * 16;
+  qbeg = qbeg < 0 ? 0 : qbeg / qgran * qgran;
   const int64_t nch = qbeg < s_q ? cdiv64(s_q - qbeg, qc) : 0;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int64_t ch = 0; ch < nch && ch < cmax; ++ch) {
@@ -289,7 +290,406 @@ __global__ __launch_bounds__(256) void attn_dv_reduce_kernel(int64_t s_q, int64_
 }
 
 // ---------------------------------------------------------------- bfloat16
-// (kept from the first version until the bf16 MFMA kernels replace them)
+// bf16 inputs (P, K, V, ctx) run on v_mfma_f32_16x16x32_bf16; dCtx and dS are
+// rounded to bf16 as MFMA operands, accumulation and softmax algebra stay
+// fp32.  Operand lane layout: lane l holds row (or column) l%16 and the eight
+// k indices 8(l/16) .. 8(l/16)+7; result lane l, register v holds row
+// 4(l/16)+v, column l%16.
+//
+// transpose_bf16_kernel  dst[col][row] (bf16, rows padded with zeros to LR)
+//     from src[row][col] (fp32 or bf16).  Gives K as Kt[kv head][d][key] and
+//     dCtx as dCt[head][d][query], so the operands whose MFMA k index runs
+//     over keys or queries are 16-byte reads.
+// attn_dq_bf16_kernel  workgroup = HW heads of one KV group x QW wave groups;
+//     a wave owns two 16-query blocks, i and n-1-i, so every wave does about
+//     the same causal work.  64-key tiles of V and Kt are staged in LDS
+//     (double-buffered, next tile fetched during the current one).  Inside a
+//     tile the key of MFMA row m in sub-tile nt is 16(m/4) + 4 nt + m%4: a
+//     lane's four sub-tiles then hold 16 consecutive keys of its query, so P
+//     is read as 32 contiguous bytes, and the dS values for keys 16c + 8s ..
+//     +7 are the A operand of dQ = dS K with Kt read as one 16-byte row.
+// attn_dv_bf16_kernel  workgroup = 64 keys of one KV group x one query chunk;
+//     waves 2 x 2 over (32 keys, D/2 dims).  Per 64-query step, P^T is
+//     transposed into LDS and dCt copied; chunk partials as in fp32.
+constexpr int TR_R = 64, TR_C = 32;
+
+template <typename TS>
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(int64_t rows, int64_t LR,
+                                                             int64_t ld,
+                                                             const TS* __restrict__ src,
+                                                             uint16_t* __restrict__ dst) {
+  __shared__ uint16_t tile[TR_C][TR_R + 2];
+  const int t = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * TR_R, c0 = (int64_t)blockIdx.y * TR_C;
+  const int col = t & 31;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = (t >> 5) + 8 * i;
+    const int64_t r = r0 + row;
+    float v = 0.f;
+    if (r < rows) v = Act<TS>::ld(src, r * ld + c0 + col);
+    tile[col][row] = f2bf(v);
+  }
+  __syncthreads();
+  const int rc = t & 7, cc = t >> 3;
+  ushortx8 o;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = tile[cc][8 * rc + j];
+  *reinterpret_cast<ushortx8*>(dst + (c0 + cc) * LR + r0 + 8 * rc) = o;
+}
+
+__device__ __forceinline__ ushortx8 pack8(const float (&x)[8]) {
+  ushortx8 o;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = f2bf(x[j]);
+  return o;
+}
+
+constexpr int HQ_KT = 64;  // keys per tile, bf16 dq kernel
+
+template <int D, int HW>
+__global__ __launch_bounds__(256) void attn_dq_bf16_kernel(
+    int64_t s_q, int64_t s_kv, int Hq, int grp, int64_t LK, int npairs,
+    const float* __restrict__ dctx, const uint16_t* __restrict__ P,
+    const uint16_t* __restrict__ Kt, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ ctx, const float* __restrict__ delta_ws, float* __restrict__ dq,
+    float scale, int causal) {
+  constexpr int KT = HQ_KT, NK = D / 32, ND = D / 16, QW = 4 / HW;
+  constexpr int VLD = D + 8, KLD = KT + 8;
+  constexpr int NCH = KT * D / 8;            // 16-byte chunks per staged matrix
+  constexpr int SE = (NCH + 255) / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KT][VLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][D][KLD];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int l16 = lane & 15, c = lane >> 4;
+  const int h = (int)blockIdx.y * HW + (w % HW), g = h / grp;
+  const int64_t ldq = (int64_t)Hq * D, ldk = (int64_t)(Hq / grp) * D;
+  const int nsub = (int)cdiv64(s_q, 16);
+  const int64_t off = s_kv - s_q;
+  // key range of a 16-query block: causal end after its last row
+  auto kend_of = [&](int sb) -> int64_t {
+    if (!causal) return s_kv;
+    const int64_t last = min(s_q, (int64_t)16 * sb + 16) - 1;
+    return min(s_kv, off + last + 1);
+  };
+  // this wave's two blocks (the second is absent for the middle of an odd count)
+  const int pair = (int)blockIdx.x * QW + w / HW;
+  int sub[2];
+  bool has[2];
+  sub[0] = pair;
+  sub[1] = nsub - 1 - pair;
+  has[0] = pair < npairs;
+  has[1] = pair < npairs && sub[1] != sub[0];
+  int64_t kend[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) kend[s] = has[s] ? kend_of(sub[s]) : 0;
+  // the workgroup walks the longest key range among its waves
+  int64_t kend_wg = 0;
+  for (int j = 0; j < QW; ++j) {
+    const int pj = (int)blockIdx.x * QW + j;
+    if (pj < npairs) {
+      kend_wg = max(kend_wg, kend_of(pj));
+      if (nsub - 1 - pj != pj) kend_wg = max(kend_wg, kend_of(nsub - 1 - pj));
+    }
+  }
+  const int ntile = (int)cdiv64(kend_wg, KT);
+
+  // B operand of dA^T = V dCtx^T: dCtx[q][32 ks + 8c .. +7] as bf16; delta
+  ushortx8 dcb[2][NK];
+  float dl[2] = {0.f, 0.f};
+  int64_t qrow[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    qrow[s] = (int64_t)16 * sub[s] + l16;
+    const bool ok = has[s] && qrow[s] < s_q;
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (ok) {
+        const float* p = dctx + qrow[s] * ldq + h * D + 32 * ks + 8 * c;
+        const float4 u0 = *reinterpret_cast<const float4*>(p);
+        const float4 u1 = *reinterpret_cast<const float4*>(p + 4);
+        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+        x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+        if (ctx != nullptr) {
+          const float4 y0 = Act<bf16>::ld4((const bf16*)ctx, qrow[s] * ldq + h * D + 32 * ks + 8 * c);
+          const float4 y1 = Act<bf16>::ld4((const bf16*)ctx, qrow[s] * ldq + h * D + 32 * ks + 8 * c + 4);
+          part += x[0] * y0.x + x[1] * y0.y + x[2] * y0.z + x[3] * y0.w + x[4] * y1.x +
+                  x[5] * y1.y + x[6] * y1.z + x[7] * y1.w;
+        }
+      }
+      dcb[s][ks] = pack8(x);
+    }
+    if (ctx != nullptr) {
+      part += __shfl_xor(part, 16, 64);
+      part += __shfl_xor(part, 32, 64);
+      dl[s] = part;
+    } else if (ok) {
+      dl[s] = delta_ws[(int64_t)h * s_q + qrow[s]];
+    }
+  }
+
+  floatx4 acc[2][ND];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int f = 0; f < ND; ++f) acc[s][f] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const bool pvec = (s_kv & 7) == 0;
+  uint4 sv[SE], sk[SE];
+  ushortx8 pn[2][2];  // next tile's P: [block][half], keys 16c .. 16c+15
+  auto fetch = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < SE; ++i) {
+      const int e = t + 256 * i;
+      sv[i] = sk[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (e < NCH) {
+        const int kk = e / (D / 8), d8 = e % (D / 8);
+        if (k0 + kk < s_kv)
+          sv[i] = *reinterpret_cast<const uint4*>(V + (k0 + kk) * ldk + g * D + 8 * d8);
+        const int d = e / (KT / 8), k8 = e % (KT / 8);
+        sk[i] = *reinterpret_cast<const uint4*>(Kt + ((int64_t)g * D + d) * LK + k0 + 8 * k8);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bool ok = has[s] && qrow[s] < s_q && k0 < kend[s];
+      const uint16_t* pr = P + ((int64_t)h * s_q + (ok ? qrow[s] : 0)) * s_kv;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int64_t kc = k0 + 16 * c + 8 * hf;
+        ushortx8 v;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = 0;
+        if (ok) {
+          if (pvec) {
+            if (kc < s_kv) v = *reinterpret_cast<const ushortx8*>(pr + kc);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (kc + j < s_kv) v[j] = pr[kc + j];
+          }
+        }
+        pn[s][hf] = v;
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < SE; ++i) {
+      const int e = t + 256 * i;
+      if (e < NCH) {
+        const int kk = e / (D / 8), d8 = e % (D / 8);
+        const int row = 16 * ((kk >> 2) & 3) + 4 * (kk >> 4) + (kk & 3);
+        *reinterpret_cast<uint4*>(&Vs[buf][row][8 * d8]) = sv[i];
+        const int d = e / (KT / 8), k8 = e % (KT / 8);
+        *reinterpret_cast<uint4*>(&Ks[buf][d][8 * k8]) = sk[i];
+      }
+    }
+  };
+
+  int buf = 0;
+  if (ntile > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntile; ++it) {
+    const int64_t k0 = (int64_t)it * KT;
+    const bool more = it + 1 < ntile;
+    ushortx8 pc[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      pc[s][0] = pn[s][0];
+      pc[s][1] = pn[s][1];
+    }
+    if (more) fetch(k0 + KT);
+    const bool on0 = k0 < kend[0], on1 = k0 < kend[1];
+    // dA^T: sub-tile nt, row m -> key 16(m/4) + 4nt + m%4, column = query
+    floatx4 da[2][4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) da[s][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) {
+        const ushortx8 a = *reinterpret_cast<const ushortx8*>(&Vs[buf][16 * nt + l16][32 * ks + 8 * c]);
+        if (on0) da[0][nt] = mfma16x16x32bf16(a, dcb[0][ks], da[0][nt]);
+        if (on1) da[1][nt] = mfma16x16x32bf16(a, dcb[1][ks], da[1][nt]);
+      }
+    // dS (fp32 algebra), packed to bf16 in the A layout of dQ = dS K
+    ushortx8 dsa[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int nt = 2 * st + j / 4, v = j % 4;
+          const float p = bf2f(pc[s][st][4 * (nt & 1) + v]);
+          x[j] = p * (da[s][nt][v] - dl[s]);
+        }
+        dsa[s][st] = pack8(x);
+      }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int f = 0; f < ND; ++f) {
+        const ushortx8 b = *reinterpret_cast<const ushortx8*>(&Ks[buf][16 * f + l16][16 * c + 8 * st]);
+        if (on0) acc[0][f] = mfma16x16x32bf16(dsa[0][st], b, acc[0][f]);
+        if (on1) acc[1][f] = mfma16x16x32bf16(dsa[1][st], b, acc[1][f]);
+      }
+    if (more) stash(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    if (!has[s]) continue;
+#pragma unroll
+    for (int f = 0; f < ND; ++f)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t row = (int64_t)16 * sub[s] + 4 * c + v;
+        if (row < s_q) dq[row * ldq + h * D + 16 * f + l16] = scale * acc[s][f][v];
+      }
+  }
+}
+
+constexpr int HV_QT = 64;  // queries per step, bf16 dv kernel
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_dv_bf16_kernel(int64_t s_q, int64_t s_kv, int Hq,
+                                                           int grp, int cmax, int64_t qc,
+                                                           int64_t LQ,
+                                                           const uint16_t* __restrict__ P,
+                                                           const uint16_t* __restrict__ dCt,
+                                                           float* __restrict__ out, int causal) {
+  constexpr int QT = HV_QT, LDT = QT + 8, ND2 = D / 32;
+  constexpr int NP = DV_KT * QT / 8 / 256;  // P chunks of 8 keys per thread (2)
+  constexpr int NC = D * QT / 8;            // dCt chunks of 8 queries
+  constexpr int SC = (NC + 255) / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t Pt[2][DV_KT][LDT];
+  __shared__ __attribute__((aligned(16))) uint16_t Ct[2][D][LDT];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int l16 = lane & 15, c = lane >> 4;
+  const int jt = (int)(blockIdx.x / cmax), ch = (int)(blockIdx.x % cmax);
+  const int g = blockIdx.y;
+  const int64_t ldk = (int64_t)(Hq / grp) * D;
+  const int64_t k0 = (int64_t)jt * DV_KT;
+  const int64_t off = s_kv - s_q;
+  int64_t qbeg = causal ? k0 - off : 0;
+  qbeg = qbeg < 0 ? 0 : qbeg / QT * QT;
+  const int64_t qa = qbeg + ch * qc;
+  const int64_t qz = min(s_q, qa + qc);
+  float* dst = out + (cmax > 1 ? (int64_t)ch * s_kv * ldk : 0);
+  if (qa >= qz) return;  // empty chunk (never chunk 0)
+  const int kh = w & 1, dh = w >> 1;
+  const bool pvec = (s_kv & 7) == 0;
+
+  floatx4 acc[2][ND2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < ND2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int64_t nqb = cdiv64(qz - qa, QT);
+  const int64_t nit = nqb * grp;
+  ushortx8 rp[NP];
+  uint4 rc[SC];
+  auto fetch = [&](int64_t it) {
+    const int h = g * grp + (int)(it / nqb);
+    const int64_t qb = qa + QT * (it % nqb);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int e = t + 256 * i;
+      const int r = e >> 3, k8 = e & 7;
+      const int64_t q = qb + r, kc = k0 + 8 * k8;
+      ushortx8 v;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0;
+      if (q < qz) {
+        const uint16_t* pr = P + ((int64_t)h * s_q + q) * s_kv;
+        if (pvec) {
+          if (kc < s_kv) v = *reinterpret_cast<const ushortx8*>(pr + kc);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (kc + j < s_kv) v[j] = pr[kc + j];
+        }
+      }
+      rp[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < SC; ++i) {
+      const int e = t + 256 * i;
+      rc[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (e < NC) {
+        const int d = e / (QT / 8), q8 = e % (QT / 8);
+        // rows past qz belong to the next chunk (or are the zero padding)
+        if (qb + 8 * q8 < qz)
+          rc[i] = *reinterpret_cast<const uint4*>(dCt + ((int64_t)h * D + d) * LQ + qb + 8 * q8);
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int e = t + 256 * i;
+      const int r = e >> 3, k8 = e & 7;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) Pt[buf][8 * k8 + j][r] = rp[i][j];
+    }
+#pragma unroll
+    for (int i = 0; i < SC; ++i) {
+      const int e = t + 256 * i;
+      if (e < NC) {
+        const int d = e / (QT / 8), q8 = e % (QT / 8);
+        *reinterpret_cast<uint4*>(&Ct[buf][d][8 * q8]) = rc[i];
+      }
+    }
+  };
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  int buf = 0;
+  for (int64_t it = 0; it < nit; ++it) {
+    const bool more = it + 1 < nit;
+    if (more) fetch(it + 1);
+#pragma unroll
+    for (int ks = 0; ks < QT / 32; ++ks) {
+      ushortx8 a[2], b[ND2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+        a[mi] = *reinterpret_cast<const ushortx8*>(&Pt[buf][32 * kh + 16 * mi + l16][32 * ks + 8 * c]);
+#pragma unroll
+      for (int nj = 0; nj < ND2; ++nj)
+        b[nj] = *reinterpret_cast<const ushortx8*>(&Ct[buf][(D / 2) * dh + 16 * nj + l16][32 * ks + 8 * c]);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < ND2; ++nj) acc[mi][nj] = mfma16x16x32bf16(a[mi], b[nj], acc[mi][nj]);
+    }
+    if (more) stash(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < ND2; ++nj)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t k = k0 + 32 * kh + 16 * mi + 4 * c + v;
+        if (k < s_kv) dst[k * ldk + g * D + (D / 2) * dh + 16 * nj + l16] = acc[mi][nj][v];
+      }
+}
+
+// ---------------------------------------------------------------- bfloat16, D = 16
+// (head dim 16: one query tile per workgroup on the fp32 MFMA)
 
 
 constexpr int AQ = 64;  // query rows per dq workgroup (16 per wave)
@@ -513,25 +913,47 @@ static DvPlan dv_plan(int64_t s_q, int64_t s_kv, int64_t Hkv) {
   return p;
 }
 
+// Query chunking of the bf16 dv kernel: chunks a multiple of its 64-query step.
+static DvPlan dv_plan_bf16(int64_t s_q, int64_t s_kv, int64_t Hkv) {
+  DvPlan p;
+  const int64_t tiles = cdiv64(s_kv, DV_KT) * Hkv;
+  int64_t want = cdiv64(DV_WG_TARGET, tiles < 1 ? 1 : tiles);
+  const int64_t sq = s_q < 1 ? 1 : s_q;
+  const int64_t maxc = cdiv64(sq, HV_QT);
+  want = want < 1 ? 1 : (want > maxc ? maxc : want);
+  p.qc = cdiv64(cdiv64(sq, want), HV_QT) * HV_QT;
+  p.cmax = (int)cdiv64(sq, p.qc);
+  return p;
+}
+
+static bool bf16_mfma_path(int dt, int64_t D) { return dt == BF16 && D >= 32; }
+
 // Workspace of the sequence path, 256-byte aligned pieces:
-//   delta [Hq, s_q] f32 (callers without ctx) | dv chunk partials f32
+//   delta [Hq, s_q] f32 (callers without ctx) | dv chunk partials f32 |
+//   bf16 MFMA path: Kt [Hkv, D, LK] bf16 | dCt [Hq, D, LQ] bf16
 struct AttnWs {
-  size_t delta, part, end;
+  size_t delta, part, kt, dct, end;
+  int64_t LK, LQ;
 };
 static size_t al256(size_t b) { return (b + 255) / 256 * 256; }
-static AttnWs attn_ws(int64_t s_q, int64_t s_kv, int64_t Hq, int64_t Hkv, int64_t D) {
+static AttnWs attn_ws(int64_t s_q, int64_t s_kv, int64_t Hq, int64_t Hkv, int64_t D, int dt) {
   AttnWs w;
-  const DvPlan dp = dv_plan(s_q, s_kv, Hkv);
+  const bool hb = bf16_mfma_path(dt, D);
+  const DvPlan dp = hb ? dv_plan_bf16(s_q, s_kv, Hkv) : dv_plan(s_q, s_kv, Hkv);
+  w.LK = cdiv64(s_kv, 64) * 64;
+  w.LQ = cdiv64(s_q, 64) * 64;
   w.delta = 0;
   w.part = al256((size_t)Hq * s_q * 4);
   const size_t pb = dp.cmax > 1 ? (size_t)dp.cmax * s_kv * Hkv * D * 4 : 0;
-  w.end = w.part + al256(pb);
+  w.kt = w.part + al256(pb);
+  w.dct = w.kt + (hb ? al256((size_t)Hkv * D * w.LK * 2) : 0);
+  w.end = w.dct + (hb ? al256((size_t)Hq * D * w.LQ * 2) : 0);
   return w;
 }
 
 size_t attn_ws_bytes(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_kv_heads,
-                     int64_t head_dim) {
-  const size_t seq = attn_ws(s_q, s_kv, n_heads, n_kv_heads, head_dim).end;
+                     int64_t head_dim, int dt) {
+  const size_t seq = attn_ws(s_q, s_kv, n_heads, n_kv_heads, head_dim, dt).end;
   if (s_q == 1) {
     const size_t d = dec_attn_ws_bytes(s_kv, n_heads, head_dim);
     return d > seq ? d : seq;
@@ -561,7 +983,7 @@ static hipError_t attn_launch_f32(int64_t s_q, int64_t s_kv, int Hq, int Hkv, co
                                   const float* ctx, float* dq, float* dv, float scale, int causal,
                                   void* ws, hipStream_t s) {
   const int grp = Hq / Hkv;
-  const AttnWs wl = attn_ws(s_q, s_kv, Hq, Hkv, D);
+  const AttnWs wl = attn_ws(s_q, s_kv, Hq, Hkv, D, F32);
   float* delta = (float*)((char*)ws + wl.delta);
   const double pairs = attn_pairs(s_q, s_kv, causal);
   const double pbytes = pairs * Hq * 4, qbytes = (double)s_q * Hq * D * 4;
@@ -592,8 +1014,76 @@ static hipError_t attn_launch_f32(int64_t s_q, int64_t s_kv, int Hq, int Hkv, co
   if ((e = hipGetLastError()) != hipSuccess || dp.cmax == 1) return e;
   const int64_t n4 = s_kv * Hkv * D / 4;
   attn_dv_reduce_kernel<<<dim3((unsigned)cdiv64(n4, 256)), 256, 0, s>>>(
-      s_q, s_kv, (int64_t)Hkv * D, dp.cmax, dp.qc, part, dv, causal);
+      s_q, s_kv, (int64_t)Hkv * D, dp.cmax, dp.qc, part, dv, causal, 16);
   mark("attn_dv_reduce", kvbytes * (dp.cmax + 1), 0, s);
+  return hipGetLastError();
+}
+
+template <int D, int HW>
+static void launch_dq_bf16(int64_t s_q, int64_t s_kv, int Hq, int grp, int64_t LK,
+                           const float* dctx, const uint16_t* P, const uint16_t* Kt,
+                           const uint16_t* V, const uint16_t* ctx, const float* delta, float* dq,
+                           float scale, int causal, hipStream_t s) {
+  constexpr int QW = 4 / HW;
+  const int nsub = (int)cdiv64(s_q, 16);
+  const int npairs = (nsub + 1) / 2;
+  const dim3 grid((unsigned)cdiv64(npairs, QW), (unsigned)(Hq / HW));
+  attn_dq_bf16_kernel<D, HW><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, LK, npairs, dctx, P, Kt,
+                                                  V, ctx, delta, dq, scale, causal);
+}
+
+template <int D>
+static hipError_t attn_launch_bf16(int64_t s_q, int64_t s_kv, int Hq, int Hkv, const float* dctx,
+                                   const uint16_t* P, const uint16_t* K, const uint16_t* V,
+                                   const uint16_t* ctx, float* dq, float* dv, float scale,
+                                   int causal, void* ws, hipStream_t s) {
+  const int grp = Hq / Hkv;
+  const AttnWs wl = attn_ws(s_q, s_kv, Hq, Hkv, D, BF16);
+  char* wb = (char*)ws;
+  float* delta = (float*)(wb + wl.delta);
+  uint16_t* Kt = (uint16_t*)(wb + wl.kt);
+  uint16_t* dCt = (uint16_t*)(wb + wl.dct);
+  const double pairs = attn_pairs(s_q, s_kv, causal);
+  const double pbytes = pairs * Hq * 2, qbytes = (double)s_q * Hq * D;
+  const double kvbytes = (double)s_kv * Hkv * D;
+  hipError_t e;
+  transpose_bf16_kernel<bf16><<<dim3((unsigned)(wl.LK / TR_R), (unsigned)(Hkv * D / TR_C)), 256,
+                                0, s>>>(s_kv, wl.LK, (int64_t)Hkv * D, (const bf16*)K, Kt);
+  mark("transpose_bf16", kvbytes * 2 + (double)Hkv * D * wl.LK * 2, 0, s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ctx == nullptr) {
+    attn_delta_kernel<bf16, D><<<dim3((unsigned)cdiv64(s_q, 4), (unsigned)Hq), 256, 0, s>>>(
+        s_q, s_kv, Hq, grp, dctx, (const bf16*)P, (const bf16*)V, delta, causal);
+    mark("attn_delta", pbytes + qbytes * 4 + kvbytes * 2 + (double)Hq * s_q * 4,
+         2.0 * D * pairs * Hq, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int hw = grp % 4 == 0 ? 4 : (grp % 2 == 0 ? 2 : 1);
+  if (hw == 4)
+    launch_dq_bf16<D, 4>(s_q, s_kv, Hq, grp, wl.LK, dctx, P, Kt, V, ctx, delta, dq, scale, causal, s);
+  else if (hw == 2)
+    launch_dq_bf16<D, 2>(s_q, s_kv, Hq, grp, wl.LK, dctx, P, Kt, V, ctx, delta, dq, scale, causal, s);
+  else
+    launch_dq_bf16<D, 1>(s_q, s_kv, Hq, grp, wl.LK, dctx, P, Kt, V, ctx, delta, dq, scale, causal, s);
+  mark("attn_dq_bf16", pbytes + qbytes * (4 + 4 + (ctx ? 2 : 0)) + 2 * kvbytes * 2,
+       4.0 * D * pairs * Hq, s);
+  if ((e = hipGetLastError()) != hipSuccess || dv == nullptr) return e;
+  transpose_bf16_kernel<float><<<dim3((unsigned)(wl.LQ / TR_R), (unsigned)(Hq * D / TR_C)), 256,
+                                 0, s>>>(s_q, wl.LQ, (int64_t)Hq * D, dctx, dCt);
+  mark("transpose_bf16", qbytes * 4 + (double)Hq * D * wl.LQ * 2, 0, s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const DvPlan dp = dv_plan_bf16(s_q, s_kv, Hkv);
+  float* part = dp.cmax > 1 ? (float*)(wb + wl.part) : dv;
+  const dim3 grid((unsigned)(cdiv64(s_kv, DV_KT) * dp.cmax), (unsigned)Hkv);
+  attn_dv_bf16_kernel<D><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dp.cmax, dp.qc, wl.LQ, P, dCt,
+                                              part, causal);
+  mark("attn_dv_bf16", pbytes + qbytes * 2 + kvbytes * 4 * (dp.cmax > 1 ? dp.cmax : 1),
+       2.0 * D * pairs * Hq, s);
+  if ((e = hipGetLastError()) != hipSuccess || dp.cmax == 1) return e;
+  const int64_t n4 = s_kv * Hkv * D / 4;
+  attn_dv_reduce_kernel<<<dim3((unsigned)cdiv64(n4, 256)), 256, 0, s>>>(
+      s_q, s_kv, (int64_t)Hkv * D, dp.cmax, dp.qc, part, dv, causal, HV_QT);
+  mark("attn_dv_reduce", kvbytes * 4 * (dp.cmax + 1), 0, s);
   return hipGetLastError();
 }
 
@@ -644,6 +1134,10 @@ static hipError_t attn_dispatch_d(int64_t s_q, int64_t s_kv, int Hq, int Hkv, in
       return attn_launch_f32<DD>(s_q, s_kv, Hq, Hkv, dctx, (const float*)P, (const float*)K,   \
                                  (const float*)V, (const float*)ctx, dq, dv, scale, causal, ws, \
                                  s);                                                           \
+    else if constexpr (DD >= 32)                                                               \
+      return attn_launch_bf16<DD>(s_q, s_kv, Hq, Hkv, dctx, (const uint16_t*)P,                \
+                                  (const uint16_t*)K, (const uint16_t*)V, (const uint16_t*)ctx, \
+                                  dq, dv, scale, causal, ws, s);                               \
     else                                                                                       \
       return attn_launch<T, DD>(s_q, s_kv, Hq, Hkv, dctx, (const T*)P, (const T*)K,            \
                                 (const T*)V, (const T*)ctx, dq, dv, scale, causal, (float*)ws, s);

@@ -116,7 +116,7 @@ hipError_t launch_dec_attn(int dt, int head_dim, const DecAttnArgs& a, hipStream
 
 // ---- attention (attn.hip)
 size_t attn_ws_bytes(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_kv_heads,
-                     int64_t head_dim);
+                     int64_t head_dim, int dt);
 hipError_t launch_attn_bwd(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_kv_heads,
                            int64_t head_dim, const float* dctx, const void* P, const void* K,
                            const void* V, const void* ctx, int dt, float* dq, float* dv,

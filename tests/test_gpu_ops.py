@@ -109,6 +109,12 @@ def _attn_inputs(seed, s_q, s_kv, Hq, Hkv, D, causal, dt):
     (64, 64, 16, 2, 16, 0, 0, F32),       # group of 8, no mask, no ctx
     (257, 257, 4, 4, 128, 1, 1, F32),     # group of 1, one row past a tile
     (33, 1030, 8, 2, 64, 1, 1, F32),      # short query block at the end of a long cache
+    (200, 200, 8, 2, 64, 1, 1, BF16),
+    (130, 333, 6, 2, 32, 1, 0, BF16),     # bf16: group of 3, no ctx, keys not a multiple of 8
+    (257, 257, 4, 4, 128, 0, 1, BF16),    # bf16: no mask, group of 1, odd block count
+    (64, 64, 16, 2, 16, 1, 1, BF16),      # bf16: head dim 16
+    (33, 1030, 8, 2, 128, 1, 1, BF16),    # bf16: short query block, long cache
+    (640, 640, 8, 2, 128, 1, 1, BF16),    # bf16: several dv chunks
 ])
 def test_attention(s_q, s_kv, Hq, Hkv, D, causal, use_ctx, dt):
     print("attn", s_q, s_kv, Hq, Hkv, D, causal, use_ctx, dt, flush=True)

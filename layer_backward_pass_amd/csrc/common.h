@@ -83,6 +83,29 @@ __device__ __forceinline__ floatx4 mfma16x16x4(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// gfx950 LDS transpose read (16-bit elements).  Within each group of 16
+// lanes, result lane i, element j is the 16-bit value at offset i%4 from the
+// address given by lane 4j + i/4 of the group.  With the 16 lanes pointing
+// at four rows k .. k+3 of a row-major tile (lane i': row k + i'/4, columns
+// n0 + 4(i'%4) .. +3), lane i receives column n0 + i of rows k .. k+3.
+__device__ __forceinline__ ushortx4 lds_read_tr16(const uint16_t* p) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  const s4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s4*)(p));
+  return __builtin_bit_cast(ushortx4, r);
+}
+
+// MFMA bf16 operand (eight consecutive k of column n0 + l%16, k from row
+// k0 + 8(l/16)) out of a row-major [k][n] LDS tile with row stride ld.
+__device__ __forceinline__ ushortx8 lds_colk8(const uint16_t* tile, int ld, int k0, int n0,
+                                              int lane) {
+  const int l16 = lane & 15, c = lane >> 4;
+  const uint16_t* p = tile + (k0 + 8 * c + (l16 >> 2)) * ld + n0 + 4 * (l16 & 3);
+  const ushortx4 lo = lds_read_tr16(p);
+  const ushortx4 hi = lds_read_tr16(p + 4 * ld);
+  return ushortx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 __device__ __forceinline__ floatx4 mfma16x16x32bf16(ushortx8 a, ushortx8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

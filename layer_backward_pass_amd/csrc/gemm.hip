@@ -166,102 +166,130 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
 }
 
 // ---------------------------------------------------------------------------
-// bf16 GEMM.  Same wave layout; BK = 32.  A tile stored As[m][k] (bf16, k
-// contiguous: one 16-byte read per MFMA operand); the B tile is transposed
-// on its way into LDS (Bs[n][k]) by pairing consecutive k rows into 32-bit
-// words.  Row stride 40 bf16 (80 bytes) keeps 16-byte alignment.
-constexpr int H_BK = 32, H_LD = H_BK + 8;
+// bf16 GEMM: 512 threads, tile 128 x 256, BK = 64, waves 2 x 4 of 64 x 64
+// (v_mfma_f32_16x16x32_bf16).  A (bf16, or fp32 rounded to bf16 on the way
+// in) sits in LDS k-contiguous, As[m][k], and is read with one 16-byte load
+// per operand.  B keeps its memory layout in LDS, Bs[k][n], filled with
+// plain 16-byte copies; the LDS transpose read turns four k-rows of a column
+// into one lane's operand half.  Double-buffered, one barrier per k-tile.
+constexpr int H_BM = 128, H_BN = 256, H_BK = 64, H_NT = 512;
+constexpr int H_LDA = H_BK + 8, H_LDB = H_BN + 16;
 
 template <typename TA>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(int64_t M, int64_t N, int64_t K,
-                                                        const TA* __restrict__ A, int64_t lda,
-                                                        const uint16_t* __restrict__ B1,
-                                                        const uint16_t* __restrict__ B2,
-                                                        int64_t K1, int64_t ldb,
-                                                        float* __restrict__ C, int64_t ldc,
-                                                        int64_t kps, int64_t split_stride) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[GBM][H_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[GBN][H_LD];
+__global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, int64_t K,
+                                                         const TA* __restrict__ A, int64_t lda,
+                                                         const uint16_t* __restrict__ B1,
+                                                         const uint16_t* __restrict__ B2,
+                                                         int64_t K1, int64_t ldb,
+                                                         float* __restrict__ C, int64_t ldc,
+                                                         int64_t kps, int64_t split_stride) {
+  constexpr int NA = H_BM * H_BK / 8 / H_NT;  // A chunks of 8 per thread (2)
+  constexpr int NB = H_BK * H_BN / 8 / H_NT;  // B chunks of 8 per thread (4)
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][H_BM][H_LDA];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][H_BK][H_LDB];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int64_t bm = (int64_t)blockIdx.y * GBM, bn = (int64_t)blockIdx.x * GBN;
-  const int64_t kbeg = (int64_t)blockIdx.z * kps;
+  const int l16 = lane & 15, c = lane >> 4;
+  const int64_t nm = (M + H_BM - 1) / H_BM, nn = (N + H_BN - 1) / H_BN;
+  const int64_t u = xcd_remap(blockIdx.x, (int64_t)gridDim.x);
+  const int64_t z = u / (nm * nn), rem = u - z * nm * nn;
+  const int64_t bm = (rem % nm) * H_BM, bn = (rem / nm) * H_BN;
+  const int64_t kbeg = z * kps;
   const int64_t kend = min(K, kbeg + kps);
-  C += (int64_t)blockIdx.z * split_stride;
-  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  C += z * split_stride;
+  const int wm = (w & 1) * 64, wn = (w >> 1) * 64;
+  const bool full_mn = bm + H_BM <= M && bn + H_BN <= N;
 
-  // A: rows t/4 and t/4+64, 8 consecutive k at (t%4)*8 -> one uint4 of bf16
-  // B: k rows 2*(t/16), 2*(t/16)+1, 8 consecutive n at (t%16)*8
-  uint4 ra[2];
-  uint4 rb0, rb1;
+  uint4 ra[NA], rb[NB];
+  auto lda8 = [&](int64_t m, int64_t k) -> uint4 {
+    if constexpr (sizeof(TA) == 4) {
+      const float* p = (const float*)A + m * lda + k;
+      const float4 x = *reinterpret_cast<const float4*>(p);
+      const float4 y = *reinterpret_cast<const float4*>(p + 4);
+      return make_uint4((uint32_t)f2bf(x.x) | ((uint32_t)f2bf(x.y) << 16),
+                        (uint32_t)f2bf(x.z) | ((uint32_t)f2bf(x.w) << 16),
+                        (uint32_t)f2bf(y.x) | ((uint32_t)f2bf(y.y) << 16),
+                        (uint32_t)f2bf(y.z) | ((uint32_t)f2bf(y.w) << 16));
+    } else {
+      return *reinterpret_cast<const uint4*>((const uint16_t*)A + m * lda + k);
+    }
+  };
   auto load = [&](int64_t k0) {
+    const bool one_src = k0 + H_BK <= K1 || k0 >= K1;
+    if (full_mn && k0 + H_BK <= kend && one_src) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int64_t m = bm + (t >> 2) + 64 * r;
-      const int64_t k = k0 + (t & 3) * 8;
-      if (m < M && k < kend) {
-        if constexpr (sizeof(TA) == 4) {
-          const float4 x = *reinterpret_cast<const float4*>((const float*)A + m * lda + k);
-          const float4 y = *reinterpret_cast<const float4*>((const float*)A + m * lda + k + 4);
-          ra[r].x = (uint32_t)f2bf(x.x) | ((uint32_t)f2bf(x.y) << 16);
-          ra[r].y = (uint32_t)f2bf(x.z) | ((uint32_t)f2bf(x.w) << 16);
-          ra[r].z = (uint32_t)f2bf(y.x) | ((uint32_t)f2bf(y.y) << 16);
-          ra[r].w = (uint32_t)f2bf(y.z) | ((uint32_t)f2bf(y.w) << 16);
-        } else {
-          ra[r] = *reinterpret_cast<const uint4*>((const uint16_t*)A + m * lda + k);
-        }
-      } else {
-        ra[r] = make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < NA; ++i) {
+        const int e = t + H_NT * i;
+        ra[i] = lda8(bm + (e >> 3), k0 + 8 * (e & 7));
+      }
+      const uint16_t* base = k0 < K1 ? B1 + k0 * ldb : B2 + (k0 - K1) * ldb;
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int e = t + H_NT * i;
+        rb[i] = *reinterpret_cast<const uint4*>(base + (e >> 5) * ldb + bn + 8 * (e & 31));
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int e = t + H_NT * i;
+      const int64_t m = bm + (e >> 3), k = k0 + 8 * (e & 7);
+      ra[i] = (m < M && k < kend) ? lda8(m, k) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int e = t + H_NT * i;
+      const int64_t k = k0 + (e >> 5), n = bn + 8 * (e & 31);
+      rb[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (k < kend && n < N) {  // N % 8 == 0: a chunk is whole
+        const uint16_t* bp = k < K1 ? B1 + k * ldb : B2 + (k - K1) * ldb;
+        rb[i] = *reinterpret_cast<const uint4*>(bp + n);
       }
     }
-    const int64_t kb = k0 + 2 * (t >> 4);
-    const int64_t n = bn + (t & 15) * 8;
-    auto brow = [&](int64_t k) -> uint4 {
-      if (k < kend && n < N) {
-        const uint16_t* bp = k < K1 ? B1 + k * ldb : B2 + (k - K1) * ldb;
-        return *reinterpret_cast<const uint4*>(bp + n);
-      }
-      return make_uint4(0, 0, 0, 0);
-    };
-    rb0 = brow(kb);
-    rb1 = brow(kb + 1);
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int e = t + H_NT * i;
+      *reinterpret_cast<uint4*>(&As[buf][e >> 3][8 * (e & 7)]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int e = t + H_NT * i;
+      *reinterpret_cast<uint4*>(&Bs[buf][e >> 5][8 * (e & 31)]) = rb[i];
+    }
   };
   floatx4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  if (kbeg < kend) load(kbeg);
+  int buf = 0;
+  if (kbeg < kend) {
+    load(kbeg);
+    stash(0);
+  }
+  __syncthreads();
   for (int64_t k0 = kbeg; k0 < kend; k0 += H_BK) {
-    __syncthreads();
+    const bool more = k0 + H_BK < kend;
+    ushortx8 a[2][4], b[2][4];
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-      *reinterpret_cast<uint4*>(&As[(t >> 2) + 64 * r][(t & 3) * 8]) = ra[r];
-    {
-      const int kp = 2 * (t >> 4);
-      const int n0 = (t & 15) * 8;
-      const uint32_t a[4] = {rb0.x, rb0.y, rb0.z, rb0.w};
-      const uint32_t b[4] = {rb1.x, rb1.y, rb1.z, rb1.w};
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = (a[i] & 0xffffu) | (b[i] << 16);
-        const uint32_t hi = (a[i] >> 16) | (b[i] & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(&Bs[n0 + 2 * i][kp]) = lo;
-        *reinterpret_cast<uint32_t*>(&Bs[n0 + 2 * i + 1][kp]) = hi;
+        a[ks][i] = *reinterpret_cast<const ushortx8*>(&As[buf][wm + 16 * i + l16][32 * ks + 8 * c]);
+        b[ks][i] = lds_colk8(&Bs[buf][0][0], H_LDB, 32 * ks, wn + 16 * i, lane);
       }
-    }
+    if (more) load(k0 + H_BK);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32bf16(a[ks][i], b[ks][j], acc[i][j]);
+    if (more) stash(buf ^ 1);
     __syncthreads();
-    if (k0 + H_BK < kend) load(k0 + H_BK);
-    ushortx8 a[4], b[4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      a[f] = *reinterpret_cast<const ushortx8*>(&As[wm + f * 16 + (lane & 15)][8 * (lane >> 4)]);
-      b[f] = *reinterpret_cast<const ushortx8*>(&Bs[wn + f * 16 + (lane & 15)][8 * (lane >> 4)]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32bf16(a[i], b[j], acc[i][j]);
+    buf ^= 1;
   }
   store_tile<4, 4>(C, ldc, M, N, bm + wm, bn + wn, acc);
 }
@@ -302,11 +330,11 @@ struct GemmPlan {
 };
 static GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int b_dt) {
   const bool f32 = b_dt == F32;
-  const int bm = f32 ? F_BM : GBM, bn = f32 ? F_BN : GBN, bk = f32 ? F_BK : 32;
-  const int slots = f32 ? 256 : 512;
+  const int bm = f32 ? F_BM : H_BM, bn = f32 ? F_BN : H_BN, bk = f32 ? F_BK : H_BK;
+  const int slots = 256;  // one workgroup per CU (LDS)
   // ns per k index for one tile: 2 bm bn flops at the sustained MFMA rate
   const double ns_per_k = f32 ? 2.0 * bm * bn / (256.0 * 0.74 * 2.4)
-                              : 2.0 * bm * bn / (2048.0 * 0.5 * 2.4);
+                              : 2.0 * bm * bn / (4069.0 * 0.5 * 2.4);
   const int64_t tiles = cdiv(M, bm) * cdiv(N, bn);
   GemmPlan best{bm, bn, 1, K};
   double best_t = 1e30;
@@ -349,20 +377,22 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
     B2 = B1;
     K1 = K;
   }
-  dim3 grid((unsigned)cdiv(N, pl.bn), (unsigned)cdiv(M, pl.bm), (unsigned)nsp), block(256);
+  const dim3 block(256);
   if (b_dt == F32) {
     const dim3 grid1((unsigned)(cdiv(N, pl.bn) * cdiv(M, pl.bm) * nsp));
     gemm_f32_kernel<<<grid1, dim3(F_NT), 0, s>>>(M, N, K, (const float*)A, lda, (const float*)B1,
                                                 (const float*)B2, K1, ldb, out, ldo, kps,
                                                 sstride);
-  } else if (a_dt == F32) {
-    gemm_bf16_kernel<float><<<grid, block, 0, s>>>(M, N, K, (const float*)A, lda,
-                                                   (const uint16_t*)B1, (const uint16_t*)B2, K1,
-                                                   ldb, out, ldo, kps, sstride);
   } else {
-    gemm_bf16_kernel<uint16_t><<<grid, block, 0, s>>>(M, N, K, (const uint16_t*)A, lda,
-                                                      (const uint16_t*)B1, (const uint16_t*)B2,
-                                                      K1, ldb, out, ldo, kps, sstride);
+    const dim3 grid1((unsigned)(cdiv(N, pl.bn) * cdiv(M, pl.bm) * nsp));
+    if (a_dt == F32)
+      gemm_bf16_kernel<float><<<grid1, dim3(H_NT), 0, s>>>(M, N, K, (const float*)A, lda,
+                                                         (const uint16_t*)B1, (const uint16_t*)B2,
+                                                         K1, ldb, out, ldo, kps, sstride);
+    else
+      gemm_bf16_kernel<uint16_t><<<grid1, dim3(H_NT), 0, s>>>(
+          M, N, K, (const uint16_t*)A, lda, (const uint16_t*)B1, (const uint16_t*)B2, K1, ldb, out,
+          ldo, kps, sstride);
   }
   hipError_t e = hipGetLastError();
   mark(b_dt == F32 ? "gemm_f32_mfma" : "gemm_bf16_mfma",

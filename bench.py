@@ -57,6 +57,13 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline sample budget")
+    ap.add_argument("--pmc-pass", metavar="RECORDS_JSON",
+                    help="short eager run for a rocprofv3 --pmc pass: writes the step's kernel "
+                         "records to RECORDS_JSON, runs 3 eager steps and a 256 MiB plain copy "
+                         "(the counter calibration), prints nothing else")
+    ap.add_argument("--traffic-summary", nargs=3, metavar=("RECORDS_JSON", "FETCH_CSV", "WRITE_CSV"),
+                    help="turn the two counter passes (FETCH_SIZE, WRITE_SIZE) into "
+                         "profiles/traffic.json and print the table; no GPU needed")
     return ap.parse_args()
 
 
@@ -217,22 +224,125 @@ def roofline(cfg, kernels):
               "unit": "GB/s", "frac": round(achieved / PEAK["hbm_GBps"], 4)}
     rl.update({"kernel": name, "avg_us": round(avg_s * 1e6, 2), "launches_per_step": g["launches"],
                "event_gap_us": round(kernels[0]["event_gap_ms"] * 1e3, 2),
-               "alg_bytes": nbytes, "alg_flops": flops, "traffic": traffic_for(cfg, name)})
+               "alg_bytes": nbytes, "alg_flops": flops, "traffic": traffic_for(cfg, name, nbytes)})
     return rl
 
 
-def traffic_for(cfg, kernel):
-    """Measured HBM bytes per launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources; else None."""
+def traffic_for(cfg, kernel, alg_bytes):
+    """Measured HBM bytes per launch of `kernel` at this shape (identified by
+    its algorithmic bytes) from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
-    ent = data.get(cfg.name, {}).get(kernel)
+    ent = data.get(cfg.name)
     if not ent or ent.get("source_digest") != source_digest():
         return None
-    return ent.get("bytes_per_launch")
+    for k in ent.get("kernels", []):
+        if k["name"] == kernel and abs(k["alg_bytes"] - alg_bytes) <= 1e-6 * max(alg_bytes, 1.0):
+            return k["traffic_bytes"]
+    return None
+
+
+CAL_BYTES = 256 << 20  # the calibration copy reads and writes this many bytes
+
+
+def pmc_pass(lbp, hip, cfg, torch, path):
+    """Records of one step (kernel order, algorithmic bytes), then three eager
+    steps and the calibration copy, for rocprofv3 --pmc."""
+    copies = build_copies(cfg, 1, torch)
+    cp = copies[0]
+    cap = 128
+    ev = hip.events(cap)
+    recs = (lbp.KernelRecord * cap)()
+    cp["d_hidden"].copy_(cp["d_out"])
+    d = list(reversed(cp["layers"]))[0]
+    n = layer_call(lbp, cfg, d, cp["d_hidden"], gnorm=cp["gnorm"],
+                   timing=(ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)), recs))
+    torch.cuda.synchronize()
+    rows = [{"index": i, "name": recs[i].name.decode(), "alg_bytes": recs[i].alg_bytes,
+             "alg_flops": recs[i].alg_flops} for i in range(min(n, cap))]
+    for _ in range(3):
+        run_step(lbp, cfg, cp)
+    torch.cuda.synchronize()
+    src = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    with open(path, "w") as f:
+        json.dump({"workload": cfg.name, "layers": cfg.n_layers, "kernels_per_layer": len(rows),
+                   "records": rows, "calibration_bytes": CAL_BYTES}, f)
+
+
+def traffic_summary(records_json, fetch_csv, write_csv):
+    """HBM bytes per launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    each scaled by the factor that maps the same counter to the known bytes
+    of the calibration copy."""
+    import csv
+    with open(records_json) as f:
+        rec = json.load(f)
+
+    def read(path, counter):
+        lbp_rows, copy_rows = [], []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                v = float(r["Counter_Value"]) * 1024.0
+                if "lbp::" in name:
+                    lbp_rows.append((int(r["Dispatch_Id"]), name.split("(")[0], v))
+                elif "copy" in name.lower() and v > 0.5 * rec["calibration_bytes"]:
+                    copy_rows.append(v)
+        lbp_rows.sort()
+        return lbp_rows, copy_rows
+
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows, cal = read(path, counter)
+        if not cal:
+            raise SystemExit("no calibration copy found in %s" % path)
+        factor = rec["calibration_bytes"] / (sum(cal) / len(cal))
+        per = rec["kernels_per_layer"]
+        # the first layer call is the recorded one; then 3 eager steps
+        vals = {}
+        for j, (_, name, v) in enumerate(rows):
+            vals.setdefault(j % per, []).append((name, v * factor))
+        out[counter] = (factor, vals)
+    kernels = []
+    for r in rec["records"]:
+        f = out["FETCH_SIZE"][1].get(r["index"], [])
+        w = out["WRITE_SIZE"][1].get(r["index"], [])
+        if not f or not w:
+            continue
+        fb = sum(v for _, v in f) / len(f)
+        wb = sum(v for _, v in w) / len(w)
+        kernels.append({"index": r["index"], "name": r["name"], "symbol": f[0][0],
+                        "alg_bytes": r["alg_bytes"], "fetch_bytes": round(fb),
+                        "write_bytes": round(wb), "traffic_bytes": round(fb + wb),
+                        "traffic_over_alg": round((fb + wb) / r["alg_bytes"], 3) if r["alg_bytes"] else None})
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = {}
+    if os.path.exists(path):
+        with open(path) as fh:
+            data = json.load(fh)
+    data[rec["workload"]] = {
+        "source_digest": source_digest(),
+        "fetch_factor": round(out["FETCH_SIZE"][0], 4), "write_factor": round(out["WRITE_SIZE"][0], 4),
+        "calibration": "torch copy of %d MiB (reads and writes that many bytes)" % (rec["calibration_bytes"] >> 20),
+        "kernels": kernels}
+    with open(path, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+    print("| # | kernel | alg MB | FETCH MB | WRITE MB | traffic / alg |")
+    print("|---|---|---|---|---|---|")
+    for k in kernels:
+        print("| %d | %s | %.2f | %.2f | %.2f | %s |" % (k["index"], k["name"], k["alg_bytes"] / 1e6,
+                                                   k["fetch_bytes"] / 1e6, k["write_bytes"] / 1e6,
+                                                   k["traffic_over_alg"]))
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -279,6 +389,9 @@ def cpu_baseline(cfg, budget_s):
 # ------------------------------------------------------------------ main
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return 0
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU; --gpus %d is not supported (the multi-GPU "
               "path is design-only)" % args.gpus, file=sys.stderr)
@@ -291,6 +404,9 @@ def main():
         return 1
     lbp.load_library()
     cfg = synth.get_config(args.workload)
+    if args.pmc_pass:
+        pmc_pass(lbp, Hip(), cfg, torch, args.pmc_pass)
+        return 0
     steps = args.steps or DEFAULT_STEPS[cfg.name]
     warmup = args.warmup if args.warmup is not None else max(3, steps // 10)
     hip = Hip()

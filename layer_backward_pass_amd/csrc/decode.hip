@@ -655,6 +655,121 @@ __global__ __launch_bounds__(256) void dec_attn1c_kernel(DecAttnArgs a) {
   }
 }
 
+// One query row with ctx given, on the fp32 MFMA (16x16x4): workgroup =
+// one wave = 16 keys of one KV head (many small workgroups spread the
+// cache reads over the CUs), the group's heads padded to the 16 MFMA
+// columns (grp <= 16).
+//   dA^T [key x head] = V dCtx^T       k = head dim (lane group c owns
+//                                       dims DK c .. DK c + DK - 1)
+//   dS^T = P^T o (dA^T - delta)         delta_h = <dCtx_h, ctx_h>
+//   dq share [head x dim] = dS K        k = key (slot c of step v: key 4c + v)
+//   dV [key x dim] = P^T dCtx           k = head (4 heads per MFMA)
+// Every wave stores its dq share (chunk = workgroup) straight from the
+// accumulators; dec_attn_dqc adds the chunks in order.  (Staging the
+// shares through LDS was miscompiled by the ROCm 7.2 compiler: two of the
+// merged ds_write2_b32 stores of the 128-wide case got wrong offsets.)
+constexpr int DM_KB = 16;  // keys per workgroup (one wave)
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void dec_attn_mfma_kernel(DecAttnArgs a) {
+  constexpr int DK = D / 4, ND = D / 16;
+  const int lane = threadIdx.x;
+  const int l16 = lane & 15, c = lane >> 4;
+  const int g = blockIdx.y, grp = a.grp;
+  const int64_t ldk = (int64_t)(a.Hq / grp) * D;
+  const int64_t kb = (int64_t)blockIdx.x * DM_KB;
+  const bool hok = l16 < grp;
+  const int64_t hrow = (int64_t)(g * grp + (hok ? l16 : 0)) * D;
+  const int64_t kr = kb + l16;
+  const bool kok = kr < a.s_kv;
+  const bool dvh = c < grp;  // first block of four heads for dV
+  // ---- every independent global load first (one memory round trip)
+  float4 xv[DK / 4], yv[DK / 4], vv[DK / 4];
+#pragma unroll
+  for (int i = 0; i < DK / 4; ++i) {
+    xv[i] = yv[i] = vv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (hok) {
+      xv[i] = *reinterpret_cast<const float4*>(a.dctx + hrow + DK * c + 4 * i);
+      yv[i] = Act<T>::ld4((const T*)a.ctx, hrow + DK * c + 4 * i);
+    }
+    if (kok) vv[i] = Act<T>::ld4((const T*)a.V, kr * ldk + g * D + DK * c + 4 * i);
+  }
+  float pd[4], kv[4][ND], pa = 0.f, bd[ND];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int64_t key = kb + 4 * c + v;
+    const bool ok = key < a.s_kv;
+    pd[v] = (hok && ok) ? Act<T>::ld((const T*)a.P, (int64_t)(g * grp + l16) * a.s_kv + key) : 0.f;
+#pragma unroll
+    for (int f = 0; f < ND; ++f)
+      kv[v][f] = ok ? Act<T>::ld((const T*)a.K, key * ldk + g * D + 16 * f + l16) : 0.f;
+  }
+  if (a.dv != nullptr) {
+    pa = (dvh && kok) ? Act<T>::ld((const T*)a.P, (int64_t)(g * grp + c) * a.s_kv + kr) : 0.f;
+#pragma unroll
+    for (int f = 0; f < ND; ++f)
+      bd[f] = dvh ? a.dctx[(int64_t)(g * grp + c) * D + 16 * f + l16] : 0.f;
+  }
+  // ---- delta_h = <dCtx_h, ctx_h> (head l16; the four lane groups add up)
+  float dl = 0.f;
+#pragma unroll
+  for (int i = 0; i < DK / 4; ++i)
+    dl += xv[i].x * yv[i].x + xv[i].y * yv[i].y + xv[i].z * yv[i].z + xv[i].w * yv[i].w;
+  dl += __shfl_xor(dl, 16, 64);
+  dl += __shfl_xor(dl, 32, 64);
+  // ---- dA^T: rows = keys kb + l16, four chains for the MFMA pipe
+  floatx4 da[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) da[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < DK / 4; ++i) {
+    da[0] = mfma16x16x4(vv[i].x, xv[i].x, da[0]);
+    da[1] = mfma16x16x4(vv[i].y, xv[i].y, da[1]);
+    da[2] = mfma16x16x4(vv[i].z, xv[i].z, da[2]);
+    da[3] = mfma16x16x4(vv[i].w, xv[i].w, da[3]);
+  }
+  // ---- dS^T: lane (head l16, c) holds keys kb + 4c + v
+  float ds[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) ds[v] = pd[v] * (((da[0][v] + da[1][v]) + (da[2][v] + da[3][v])) - dl);
+  // ---- dq share: rows = heads, k = keys, columns = head dims
+  floatx4 aq[ND];
+#pragma unroll
+  for (int f = 0; f < ND; ++f) aq[f] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+#pragma unroll
+    for (int f = 0; f < ND; ++f) aq[f] = mfma16x16x4(ds[v], kv[v][f], aq[f]);
+  const int64_t nch = gridDim.x, chunk = blockIdx.x;
+#pragma unroll
+  for (int f = 0; f < ND; ++f)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int hh = 4 * c + v;
+      if (hh < grp) a.dq_part[((int64_t)(g * grp + hh) * nch + chunk) * D + 16 * f + l16] = aq[f][v];
+    }
+  // ---- dV: rows = keys, k = heads (slot c of block j: head 4j + c), cols = dims
+  if (a.dv != nullptr) {
+#pragma unroll
+    for (int f = 0; f < ND; ++f) {
+      floatx4 av = mfma16x16x4(pa, bd[f], floatx4{0.f, 0.f, 0.f, 0.f});
+      for (int j = 1; 4 * j < grp; ++j) {
+        const int hh = 4 * j + c;
+        const bool ok = hh < grp;
+        const float p2 =
+            (ok && kok) ? Act<T>::ld((const T*)a.P, (int64_t)(g * grp + hh) * a.s_kv + kr) : 0.f;
+        const float b2 = ok ? a.dctx[(int64_t)(g * grp + hh) * D + 16 * f + l16] : 0.f;
+        av = mfma16x16x4(p2, b2, av);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t key = kb + 4 * c + v;
+        if (key < a.s_kv) a.dv[key * ldk + g * D + 16 * f + l16] = av[v];
+      }
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(D) void dec_attn_dqc_kernel(DecAttnArgs a, int nchunks) {
   __shared__ float o[D];
@@ -703,6 +818,18 @@ static hipError_t dec_attn_launch(const DecAttnArgs& a, hipStream_t s) {
   const double es = sizeof(T);
   const int nch = (int)cdiv(a.s_kv, DA_KC);
   hipError_t e;
+  if (a.ctx != nullptr && a.grp <= 16) {
+    const int nb = (int)cdiv(a.s_kv, DM_KB);
+    dec_attn_mfma_kernel<T, D><<<dim3((unsigned)nb, (unsigned)Hkv), dim3(64), 0, s>>>(a);
+    mark("dec_attn_mfma",
+         2.0 * a.s_kv * Hkv * D * es + (double)a.Hq * a.s_kv * es + (double)a.Hq * D * (4 + es) +
+             (a.dv ? (double)a.s_kv * Hkv * D * 4 : 0.0) + (double)a.Hq * nb * D * 4,
+         6.0 * D * a.Hq * a.s_kv, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    dec_attn_dqc_kernel<D><<<dim3((unsigned)a.Hq), dim3(D), 0, s>>>(a, nb);
+    mark("dec_attn_dqc", (double)a.Hq * nb * D * 4 + (double)a.Hq * D * 4, 0, s);
+    return hipGetLastError();
+  }
   if (a.ctx != nullptr && a.grp <= 64 && dec_attn1c_smem(a.grp, D) <= 64 * 1024) {
     dec_attn1c_kernel<T, D><<<dim3((unsigned)nch, (unsigned)Hkv), dim3(256),
                               dec_attn1c_smem(a.grp, D), s>>>(a);
@@ -735,8 +862,9 @@ bool dec_attn_fits(int64_t s_kv, int64_t n_heads, int64_t n_kv_heads, int64_t he
 }
 
 size_t dec_attn_ws_bytes(int64_t s_kv, int64_t n_heads, int64_t head_dim) {
-  // dA [Hq, s_kv] for the two-pass path, or the dq shares [Hq, blocks, D]
-  const size_t a = (size_t)n_heads * s_kv, b = (size_t)n_heads * cdiv(s_kv, DA_KC) * head_dim;
+  // dA [Hq, s_kv] for the two-pass path, or the dq shares [Hq, chunks, D]
+  // (one per 16 keys for the MFMA kernel, one per DA_KC keys for the LDS one)
+  const size_t a = (size_t)n_heads * s_kv, b = (size_t)n_heads * cdiv(s_kv, 16) * head_dim;
   return (a > b ? a : b) * sizeof(float);
 }
 

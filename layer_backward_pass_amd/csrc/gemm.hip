@@ -185,6 +185,13 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
                                                          int64_t kps, int64_t split_stride) {
   constexpr int NA = H_BM * H_BK / 8 / H_NT;  // A chunks of 8 per thread (2)
   constexpr int NB = H_BK * H_BN / 8 / H_NT;  // B chunks of 8 per thread (4)
+  constexpr int AW = (int)sizeof(TA) / 2;     // 16-byte words per A chunk (fp32: 2)
+  // One k-tile of global data in registers; A stays in its HBM format until
+  // it is written to LDS, so no load has to complete before it is needed.
+  struct Stage {
+    uint4 a[NA][AW];
+    uint4 b[NB];
+  };
   __shared__ __attribute__((aligned(16))) uint16_t As[2][H_BM][H_LDA];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][H_BK][H_LDB];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -199,63 +206,54 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
   const int wm = (w & 1) * 64, wn = (w >> 1) * 64;
   const bool full_mn = bm + H_BM <= M && bn + H_BN <= N;
 
-  uint4 ra[NA], rb[NB];
-  auto lda8 = [&](int64_t m, int64_t k) -> uint4 {
-    if constexpr (sizeof(TA) == 4) {
-      const float* p = (const float*)A + m * lda + k;
-      const float4 x = *reinterpret_cast<const float4*>(p);
-      const float4 y = *reinterpret_cast<const float4*>(p + 4);
-      return make_uint4((uint32_t)f2bf(x.x) | ((uint32_t)f2bf(x.y) << 16),
-                        (uint32_t)f2bf(x.z) | ((uint32_t)f2bf(x.w) << 16),
-                        (uint32_t)f2bf(y.x) | ((uint32_t)f2bf(y.y) << 16),
-                        (uint32_t)f2bf(y.z) | ((uint32_t)f2bf(y.w) << 16));
-    } else {
-      return *reinterpret_cast<const uint4*>((const uint16_t*)A + m * lda + k);
-    }
-  };
-  auto load = [&](int64_t k0) {
+  auto load = [&](Stage& r, int64_t k0) {
     const bool one_src = k0 + H_BK <= K1 || k0 >= K1;
-    if (full_mn && k0 + H_BK <= kend && one_src) {
-#pragma unroll
-      for (int i = 0; i < NA; ++i) {
-        const int e = t + H_NT * i;
-        ra[i] = lda8(bm + (e >> 3), k0 + 8 * (e & 7));
-      }
-      const uint16_t* base = k0 < K1 ? B1 + k0 * ldb : B2 + (k0 - K1) * ldb;
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int e = t + H_NT * i;
-        rb[i] = *reinterpret_cast<const uint4*>(base + (e >> 5) * ldb + bn + 8 * (e & 31));
-      }
-      return;
-    }
+    const bool fast = full_mn && k0 + H_BK <= kend && one_src;
+    const uint16_t* base = k0 < K1 ? B1 + k0 * ldb : B2 + (k0 - K1) * ldb;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int e = t + H_NT * i;
       const int64_t m = bm + (e >> 3), k = k0 + 8 * (e & 7);
-      ra[i] = (m < M && k < kend) ? lda8(m, k) : make_uint4(0u, 0u, 0u, 0u);
+      const bool ok = fast || (m < M && k < kend);
+      const uint4* p = reinterpret_cast<const uint4*>(A + m * lda + k);
+#pragma unroll
+      for (int j = 0; j < AW; ++j) r.a[i][j] = ok ? p[j] : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int e = t + H_NT * i;
-      const int64_t k = k0 + (e >> 5), n = bn + 8 * (e & 31);
-      rb[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (k < kend && n < N) {  // N % 8 == 0: a chunk is whole
-        const uint16_t* bp = k < K1 ? B1 + k * ldb : B2 + (k - K1) * ldb;
-        rb[i] = *reinterpret_cast<const uint4*>(bp + n);
+      const int64_t kk = e >> 5, n = bn + 8 * (e & 31);
+      if (fast) {
+        r.b[i] = *reinterpret_cast<const uint4*>(base + kk * ldb + n);
+      } else {
+        const int64_t k = k0 + kk;  // N % 8 == 0: a chunk is whole
+        r.b[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (k < kend && n < N)
+          r.b[i] = *reinterpret_cast<const uint4*>((k < K1 ? B1 + k * ldb : B2 + (k - K1) * ldb) + n);
       }
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](const Stage& r, int buf) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int e = t + H_NT * i;
-      *reinterpret_cast<uint4*>(&As[buf][e >> 3][8 * (e & 7)]) = ra[i];
+      uint4 v;
+      if constexpr (AW == 2) {
+        const float4 x = __builtin_bit_cast(float4, r.a[i][0]);
+        const float4 y = __builtin_bit_cast(float4, r.a[i][1]);
+        v = make_uint4((uint32_t)f2bf(x.x) | ((uint32_t)f2bf(x.y) << 16),
+                       (uint32_t)f2bf(x.z) | ((uint32_t)f2bf(x.w) << 16),
+                       (uint32_t)f2bf(y.x) | ((uint32_t)f2bf(y.y) << 16),
+                       (uint32_t)f2bf(y.z) | ((uint32_t)f2bf(y.w) << 16));
+      } else {
+        v = r.a[i][0];
+      }
+      *reinterpret_cast<uint4*>(&As[buf][e >> 3][8 * (e & 7)]) = v;
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int e = t + H_NT * i;
-      *reinterpret_cast<uint4*>(&Bs[buf][e >> 5][8 * (e & 31)]) = rb[i];
+      *reinterpret_cast<uint4*>(&Bs[buf][e >> 5][8 * (e & 31)]) = r.b[i];
     }
   };
   floatx4 acc[4][4];
@@ -263,31 +261,37 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      ushortx8 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = *reinterpret_cast<const ushortx8*>(&As[buf][wm + 16 * i + l16][32 * ks + 8 * c]);
+        b[i] = lds_colk8(&Bs[buf][0][0], H_LDB, 32 * ks, wn + 16 * i, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32bf16(a[i], b[j], acc[i][j]);
+    }
+  };
 
+  // Two k-tiles in flight: the LDS buffer in use and one register stage.
+  // The stage is refilled right after it has been copied to LDS, and it is
+  // copied only after the MFMAs of the current tile have been issued.
+  Stage st;
   int buf = 0;
   if (kbeg < kend) {
-    load(kbeg);
-    stash(0);
+    load(st, kbeg);
+    stash(st, 0);
   }
   __syncthreads();
   for (int64_t k0 = kbeg; k0 < kend; k0 += H_BK) {
     const bool more = k0 + H_BK < kend;
-    ushortx8 a[2][4], b[2][4];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[ks][i] = *reinterpret_cast<const ushortx8*>(&As[buf][wm + 16 * i + l16][32 * ks + 8 * c]);
-        b[ks][i] = lds_colk8(&Bs[buf][0][0], H_LDB, 32 * ks, wn + 16 * i, lane);
-      }
-    if (more) load(k0 + H_BK);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32bf16(a[ks][i], b[ks][j], acc[i][j]);
-    if (more) stash(buf ^ 1);
+    if (more) load(st, k0 + H_BK);
+    compute(buf);
+    if (more) stash(st, buf ^ 1);
     __syncthreads();
     buf ^= 1;
   }

@@ -309,8 +309,10 @@ __global__ __launch_bounds__(256) void attn_dv_reduce_kernel(int64_t s_q, int64_
 //     is read as 32 contiguous bytes, and the dS values for keys 16c + 8s ..
 //     +7 are the A operand of dQ = dS K with Kt read as one 16-byte row.
 // attn_dv_bf16_kernel  workgroup = 64 keys of one KV group x one query chunk;
-//     waves 2 x 2 over (32 keys, D/2 dims).  Per 64-query step, P^T is
-//     transposed into LDS and dCt copied; chunk partials as in fp32.
+//     waves 2 x 2 over (32 keys, D/2 dims).  Per 64-query step the P block
+//     is copied to LDS as stored ([query][key]) and read as P^T through the
+//     LDS transpose read; dCt rows are copied; two steps of global loads
+//     are in flight.  Chunk partials as in fp32.
 constexpr int TR_R = 64, TR_C = 32;
 
 template <typename TS>
@@ -348,7 +350,7 @@ __device__ __forceinline__ ushortx8 pack8(const float (&x)[8]) {
 constexpr int HQ_KT = 64;  // keys per tile, bf16 dq kernel
 
 template <int D, int HW>
-__global__ __launch_bounds__(256) void attn_dq_bf16_kernel(
+__global__ __launch_bounds__(256, 2) void attn_dq_bf16_kernel(
     int64_t s_q, int64_t s_kv, int Hq, int grp, int64_t LK, int npairs,
     const float* __restrict__ dctx, const uint16_t* __restrict__ P,
     const uint16_t* __restrict__ Kt, const uint16_t* __restrict__ V,
@@ -438,20 +440,8 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(
 
   const bool pvec = (s_kv & 7) == 0;
   uint4 sv[SE], sk[SE];
-  ushortx8 pn[2][2];  // next tile's P: [block][half], keys 16c .. 16c+15
-  auto fetch = [&](int64_t k0) {
-#pragma unroll
-    for (int i = 0; i < SE; ++i) {
-      const int e = t + 256 * i;
-      sv[i] = sk[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (e < NCH) {
-        const int kk = e / (D / 8), d8 = e % (D / 8);
-        if (k0 + kk < s_kv)
-          sv[i] = *reinterpret_cast<const uint4*>(V + (k0 + kk) * ldk + g * D + 8 * d8);
-        const int d = e / (KT / 8), k8 = e % (KT / 8);
-        sk[i] = *reinterpret_cast<const uint4*>(Kt + ((int64_t)g * D + d) * LK + k0 + 8 * k8);
-      }
-    }
+  // P of the current tile: [block][half], keys 16c .. 16c+15
+  auto fetch_p = [&](int64_t k0, ushortx8 (&pc)[2][2]) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const bool ok = has[s] && qrow[s] < s_q && k0 < kend[s];
@@ -471,10 +461,24 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(
               if (kc + j < s_kv) v[j] = pr[kc + j];
           }
         }
-        pn[s][hf] = v;
+        pc[s][hf] = v;
       }
     }
   };
+  auto fetch = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < SE; ++i) {
+      const int e = t + 256 * i;
+      sv[i] = sk[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (e < NCH) {
+        const int kk = e / (D / 8), d8 = e % (D / 8);
+        if (k0 + kk < s_kv)
+          sv[i] = *reinterpret_cast<const uint4*>(V + (k0 + kk) * ldk + g * D + 8 * d8);
+        const int d = e / (KT / 8), k8 = e % (KT / 8);
+        sk[i] = *reinterpret_cast<const uint4*>(Kt + ((int64_t)g * D + d) * LK + k0 + 8 * k8);
+      }
+    }
+};
   auto stash = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < SE; ++i) {
@@ -499,11 +503,7 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(
     const int64_t k0 = (int64_t)it * KT;
     const bool more = it + 1 < ntile;
     ushortx8 pc[2][2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      pc[s][0] = pn[s][0];
-      pc[s][1] = pn[s][1];
-    }
+    fetch_p(k0, pc);
     if (more) fetch(k0 + KT);
     const bool on0 = k0 < kend[0], on1 = k0 < kend[1];
     // dA^T: sub-tile nt, row m -> key 16(m/4) + 4nt + m%4, column = query
@@ -573,7 +573,7 @@ __global__ __launch_bounds__(256) void attn_dv_bf16_kernel(int64_t s_q, int64_t 
   constexpr int NP = DV_KT * QT / 8 / 256;  // P chunks of 8 keys per thread (2)
   constexpr int NC = D * QT / 8;            // dCt chunks of 8 queries
   constexpr int SC = (NC + 255) / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t Pt[2][DV_KT][LDT];
+  __shared__ __attribute__((aligned(16))) uint16_t Pn[2][QT][DV_KT + 8];  // [query][key]
   __shared__ __attribute__((aligned(16))) uint16_t Ct[2][D][LDT];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int l16 = lane & 15, c = lane >> 4;
@@ -598,16 +598,19 @@ __global__ __launch_bounds__(256) void attn_dv_bf16_kernel(int64_t s_q, int64_t 
     for (int j = 0; j < ND2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   const int64_t nqb = cdiv64(qz - qa, QT);
   const int64_t nit = nqb * grp;
-  ushortx8 rp[NP];
-  uint4 rc[SC];
-  auto fetch = [&](int64_t it) {
+  // one 64-query step of global data; two of them are in flight
+  struct Stage {
+    ushortx8 p[NP];
+    uint4 c[SC];
+  };
+  auto fetch = [&](Stage& r, int64_t it) {
     const int h = g * grp + (int)(it / nqb);
     const int64_t qb = qa + QT * (it % nqb);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int e = t + 256 * i;
-      const int r = e >> 3, k8 = e & 7;
-      const int64_t q = qb + r, kc = k0 + 8 * k8;
+      const int rr = e >> 3, k8 = e & 7;
+      const int64_t q = qb + rr, kc = k0 + 8 * k8;
       ushortx8 v;
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = 0;
@@ -621,50 +624,43 @@ __global__ __launch_bounds__(256) void attn_dv_bf16_kernel(int64_t s_q, int64_t 
             if (kc + j < s_kv) v[j] = pr[kc + j];
         }
       }
-      rp[i] = v;
+      r.p[i] = v;
     }
 #pragma unroll
     for (int i = 0; i < SC; ++i) {
       const int e = t + 256 * i;
-      rc[i] = make_uint4(0u, 0u, 0u, 0u);
+      r.c[i] = make_uint4(0u, 0u, 0u, 0u);
       if (e < NC) {
         const int d = e / (QT / 8), q8 = e % (QT / 8);
         // rows past qz belong to the next chunk (or are the zero padding)
         if (qb + 8 * q8 < qz)
-          rc[i] = *reinterpret_cast<const uint4*>(dCt + ((int64_t)h * D + d) * LQ + qb + 8 * q8);
+          r.c[i] = *reinterpret_cast<const uint4*>(dCt + ((int64_t)h * D + d) * LQ + qb + 8 * q8);
       }
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](const Stage& r, int buf) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int e = t + 256 * i;
-      const int r = e >> 3, k8 = e & 7;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) Pt[buf][8 * k8 + j][r] = rp[i][j];
+      *reinterpret_cast<ushortx8*>(&Pn[buf][e >> 3][8 * (e & 7)]) = r.p[i];
     }
 #pragma unroll
     for (int i = 0; i < SC; ++i) {
       const int e = t + 256 * i;
       if (e < NC) {
         const int d = e / (QT / 8), q8 = e % (QT / 8);
-        *reinterpret_cast<uint4*>(&Ct[buf][d][8 * q8]) = rc[i];
+        *reinterpret_cast<uint4*>(&Ct[buf][d][8 * q8]) = r.c[i];
       }
     }
   };
-  fetch(0);
-  stash(0);
-  __syncthreads();
-  int buf = 0;
-  for (int64_t it = 0; it < nit; ++it) {
-    const bool more = it + 1 < nit;
-    if (more) fetch(it + 1);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < QT / 32; ++ks) {
       ushortx8 a[2], b[ND2];
+      // P^T operand: eight consecutive queries of key column 32 kh + 16 mi + l%16
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
-        a[mi] = *reinterpret_cast<const ushortx8*>(&Pt[buf][32 * kh + 16 * mi + l16][32 * ks + 8 * c]);
+        a[mi] = lds_colk8(&Pn[buf][0][0], DV_KT + 8, 32 * ks, 32 * kh + 16 * mi, lane);
 #pragma unroll
       for (int nj = 0; nj < ND2; ++nj)
         b[nj] = *reinterpret_cast<const ushortx8*>(&Ct[buf][(D / 2) * dh + 16 * nj + l16][32 * ks + 8 * c]);
@@ -673,9 +669,24 @@ __global__ __launch_bounds__(256) void attn_dv_bf16_kernel(int64_t s_q, int64_t 
 #pragma unroll
         for (int nj = 0; nj < ND2; ++nj) acc[mi][nj] = mfma16x16x32bf16(a[mi], b[nj], acc[mi][nj]);
     }
-    if (more) stash(buf ^ 1);
+  };
+  // step it in LDS buffer it % 2; stages s0, s1 hold the next two steps
+  Stage s0, s1;
+  fetch(s0, 0);
+  stash(s0, 0);
+  if (nit > 1) fetch(s0, 1);
+  if (nit > 2) fetch(s1, 2);
+  __syncthreads();
+  for (int64_t it = 0; it < nit; it += 2) {
+    compute(0);
+    if (it + 1 < nit) stash(s0, 1);
     __syncthreads();
-    buf ^= 1;
+    if (it + 3 < nit) fetch(s0, it + 3);
+    if (it + 1 >= nit) break;
+    compute(1);
+    if (it + 2 < nit) stash(s1, 0);
+    __syncthreads();
+    if (it + 4 < nit) fetch(s1, it + 4);
   }
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)

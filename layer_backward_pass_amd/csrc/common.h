@@ -97,10 +97,15 @@ __device__ __forceinline__ ushortx4 lds_read_tr16(const uint16_t* p) {
 
 // MFMA bf16 operand (eight consecutive k of column n0 + l%16, k from row
 // k0 + 8(l/16)) out of a row-major [k][n] LDS tile with row stride ld.
+// SWZ: the tile stores row k, column n at column n ^ (64 ((k / 8) % 2))
+// (rows >= 128 wide, k0 % 16 == 0), so that the four lane groups, whose
+// rows are 8 apart, do not read the same banks.
+template <bool SWZ = false>
 __device__ __forceinline__ ushortx8 lds_colk8(const uint16_t* tile, int ld, int k0, int n0,
                                               int lane) {
   const int l16 = lane & 15, c = lane >> 4;
-  const uint16_t* p = tile + (k0 + 8 * c + (l16 >> 2)) * ld + n0 + 4 * (l16 & 3);
+  const int nc = SWZ ? (n0 ^ (64 * (c & 1))) : n0;
+  const uint16_t* p = tile + (k0 + 8 * c + (l16 >> 2)) * ld + nc + 4 * (l16 & 3);
   const ushortx4 lo = lds_read_tr16(p);
   const ushortx4 hi = lds_read_tr16(p + 4 * ld);
   return ushortx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};

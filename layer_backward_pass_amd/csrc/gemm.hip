@@ -253,7 +253,8 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int e = t + H_NT * i;
-      *reinterpret_cast<uint4*>(&Bs[buf][e >> 5][8 * (e & 31)]) = r.b[i];
+      const int row = e >> 5;  // column chunk swizzled as lds_colk8<true> reads it
+      *reinterpret_cast<uint4*>(&Bs[buf][row][(8 * (e & 31)) ^ (64 * ((row >> 3) & 1))]) = r.b[i];
     }
   };
   floatx4 acc[4][4];
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         a[i] = *reinterpret_cast<const ushortx8*>(&As[buf][wm + 16 * i + l16][32 * ks + 8 * c]);
-        b[i] = lds_colk8(&Bs[buf][0][0], H_LDB, 32 * ks, wn + 16 * i, lane);
+        b[i] = lds_colk8<true>(&Bs[buf][0][0], H_LDB, 32 * ks, wn + 16 * i, lane);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)

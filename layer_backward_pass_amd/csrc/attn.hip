@@ -15,8 +15,8 @@
 //       16-byte load per lane straight into the accumulator layout, and the
 //       resulting dS^T registers are already the A operand of dQ = dS K.
 //       delta comes from <dCtx, ctx> (ctx = P V), so P is streamed once.
-//       Query tiles are issued latest-first: under a causal mask they are
-//       the longest.
+//       Under a causal mask the grid is ordered so that long and short
+//       query tiles pair up on a CU.
 //   attn_dv_f32_kernel  workgroup = 64 keys of one KV group and one chunk of
 //       query rows; each wave owns 16 keys x all head dims and sums
 //       P^T dCtx over the heads of the group; dCtx rows are staged in LDS.
@@ -66,8 +66,28 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
   __shared__ float Ks[KT][LDK];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int l16 = lane & 15, c = lane >> 4;
-  const int64_t qt = causal ? (int64_t)(gridDim.x - 1 - blockIdx.x) : (int64_t)blockIdx.x;
-  const int h = (int)blockIdx.y * HW + (w % HW), g = h / grp;
+  // 1-D grid over (query tile, head block).  Under the causal mask the first
+  // half of the grid takes the query tiles from the end (longest first) and
+  // the second half the complementary ones from the start, so the two
+  // workgroups that share a CU add up to about the same work.
+  const int nhb = Hq / HW;
+  const int64_t nqt = cdiv64(s_q, 16 * QW);
+  const int64_t L = blockIdx.x;
+  int64_t qt, hb;
+  if (causal) {
+    const int64_t H = (int64_t)nhb * ((nqt + 1) / 2);
+    if (L < H) {
+      qt = nqt - 1 - L / nhb;
+      hb = L % nhb;
+    } else {
+      qt = (L - H) / nhb;
+      hb = (L - H) % nhb;
+    }
+  } else {
+    qt = L / nhb;
+    hb = L % nhb;
+  }
+  const int h = (int)hb * HW + (w % HW), g = h / grp;
   const int64_t ldq = (int64_t)Hq * D, ldk = (int64_t)(Hq / grp) * D;
   const int64_t qw0 = qt * (16 * QW);
   const int64_t q0 = qw0 + 16 * (w / HW);
@@ -185,18 +205,22 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
 
 // dV for 64 keys of KV group blockIdx.y over query chunk (blockIdx.x % cmax)
 // of `qc` rows.  MFMA rows = keys (wave w: 16w .. 16w+15), cols = head dims,
-// k = query rows (step s, group c: row qb + 4s + c).  Output: dv itself when
-// cmax == 1, else partial sums part[chunk][key][kv_dim].
+// k = query rows (step s, group c: row qb + 4s + c).  32 query rows of one
+// head per step: their dCtx rows go to a double-buffered LDS tile, the P
+// values straight into registers; one step of loads is in flight.  Output:
+// dv itself when cmax == 1, else partial sums part[chunk][key][kv_dim].
+constexpr int FV_QT = 32;  // query rows per step, fp32 dv kernel
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_dv_f32_kernel(int64_t s_q, int64_t s_kv, int Hq,
                                                           int grp, int cmax, int64_t qc,
                                                           const float* __restrict__ dctx,
                                                           const float* __restrict__ P,
                                                           float* __restrict__ out, int causal) {
-  constexpr int ND = D / 16, LDC = D == 16 ? 48 : D + 16;
-  constexpr int NE = 16 * D / 4;  // float4 per staged dCtx block
+  constexpr int ND = D / 16, LDC = D == 16 ? 48 : D + 16, QT = FV_QT;
+  constexpr int NE = QT * D / 4;  // float4 per staged dCtx block
   constexpr int SE = (NE + 255) / 256;
-  __shared__ float dCs[16][LDC];
+  __shared__ float dCs[2][QT][LDC];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int l16 = lane & 15, c = lane >> 4;
   const int jt = (int)(blockIdx.x / cmax), ch = (int)(blockIdx.x % cmax);
@@ -216,42 +240,53 @@ __global__ __launch_bounds__(256) void attn_dv_f32_kernel(int64_t s_q, int64_t s
   floatx4 acc[ND];
 #pragma unroll
   for (int f = 0; f < ND; ++f) acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const int64_t nqb = cdiv64(qz - qa, 16);
+  const int64_t nqb = cdiv64(qz - qa, QT);
   const int64_t nit = nqb * grp;
-  float4 st[SE];
-  float pa[4];
-  auto fetch = [&](int64_t it) {
+  struct Stage {
+    float4 d[SE];
+    float p[QT / 4];
+  };
+  auto fetch = [&](Stage& r, int64_t it) {
     const int h = g * grp + (int)(it / nqb);
-    const int64_t qb = qa + 16 * (it % nqb);
+    const int64_t qb = qa + QT * (it % nqb);
 #pragma unroll
     for (int i = 0; i < SE; ++i) {
       const int e = t + 256 * i;
       const int64_t row = qb + e / (D / 4);
-      st[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      r.d[i] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (e < NE && row < qz)
-        st[i] = *reinterpret_cast<const float4*>(dctx + row * ldq + h * D + 4 * (e % (D / 4)));
+        r.d[i] = *reinterpret_cast<const float4*>(dctx + row * ldq + h * D + 4 * (e % (D / 4)));
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < QT / 4; ++s) {
       const int64_t row = qb + 4 * s + c;
-      pa[s] = (kok && row < qz) ? P[((int64_t)h * s_q + row) * s_kv + key] : 0.f;
+      r.p[s] = (kok && row < qz) ? P[((int64_t)h * s_q + row) * s_kv + key] : 0.f;
     }
   };
-  fetch(0);
-  for (int64_t it = 0; it < nit; ++it) {
-    __syncthreads();
+  auto stash = [&](const Stage& r, int buf) {
 #pragma unroll
     for (int i = 0; i < SE; ++i) {
       const int e = t + 256 * i;
-      if (e < NE) *reinterpret_cast<float4*>(&dCs[e / (D / 4)][4 * (e % (D / 4))]) = st[i];
+      if (e < NE) *reinterpret_cast<float4*>(&dCs[buf][e / (D / 4)][4 * (e % (D / 4))]) = r.d[i];
     }
-    float a[4] = {pa[0], pa[1], pa[2], pa[3]};
+  };
+  Stage cur, nxt;
+  fetch(cur, 0);
+  stash(cur, 0);
+  __syncthreads();
+  int buf = 0;
+  for (int64_t it = 0; it < nit; ++it) {
+    const bool more = it + 1 < nit;
+    if (more) fetch(nxt, it + 1);
+#pragma unroll
+    for (int s = 0; s < QT / 4; ++s)
+#pragma unroll
+      for (int f = 0; f < ND; ++f)
+        acc[f] = mfma16x16x4(cur.p[s], dCs[buf][4 * s + c][16 * f + l16], acc[f]);
+    if (more) stash(nxt, buf ^ 1);
     __syncthreads();
-    if (it + 1 < nit) fetch(it + 1);
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int f = 0; f < ND; ++f) acc[f] = mfma16x16x4(a[s], dCs[4 * s + c][16 * f + l16], acc[f]);
+    buf ^= 1;
+    cur = nxt;
   }
 #pragma unroll
   for (int f = 0; f < ND; ++f)
@@ -983,7 +1018,7 @@ static void launch_dq_f32(int64_t s_q, int64_t s_kv, int Hq, int grp, const floa
                           const float* P, const float* K, const float* V, const float* ctx,
                           const float* delta, float* dq, float scale, int causal, hipStream_t s) {
   constexpr int QW = 4 / HW;
-  const dim3 grid((unsigned)cdiv64(s_q, 16 * QW), (unsigned)(Hq / HW));
+  const dim3 grid((unsigned)(cdiv64(s_q, 16 * QW) * (Hq / HW)));
   attn_dq_f32_kernel<D, HW><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta,
                                                  dq, scale, causal);
 }

@@ -79,7 +79,7 @@ struct Carver {
 struct FfnPlan {
   float *dhid, *dn2, *partials;          // rows > 1
   void* dgu;
-  float *part1, *part2, *x2, *scal1, *scal2;  // rows == 1
+  float *part1, *part2, *scal1, *scal2;  // rows == 1
   size_t bytes;
 };
 
@@ -90,10 +90,9 @@ FfnPlan ffn_plan(void* ws, int64_t rows, int64_t dim, int64_t ffn, int dt) {
   FfnPlan p{};
   if (rows == 1) {
     p.part1 = c.take<float>(dgemv_part_bytes(ffn, dim));
-    p.part2 = c.take<float>(dgemv_part_bytes(dim, 2 * ffn));
-    p.x2 = c.take<float>((size_t)2 * ffn * 4);
+    p.part2 = c.take<float>(dgemv_part_bytes(dim, 2 * ffn, PRO_ACT));
     p.scal1 = c.take<float>((size_t)2 * dgemv_nscal(ffn, dim) * 4);
-    p.scal2 = c.take<float>((size_t)2 * dgemv_nscal(dim, 2 * ffn) * 4);
+    p.scal2 = c.take<float>((size_t)2 * dgemv_nscal(dim, 2 * ffn, PRO_ACT) * 4);
   } else {
     p.dhid = c.take<float>((size_t)rows * ffn * 4);
     p.dgu = c.take<void>((size_t)rows * 2 * ffn * esize(dt));
@@ -155,44 +154,42 @@ hipError_t ffn_run(int64_t rows, int64_t dim, int64_t ffn, int act, const float*
       g.scal = p.scal1;
     }
     if ((e = launch_dgemv(dt, dt, g, s)) != hipSuccess) return e;
-    // 2-3. dHid, sub-norm backward, activation backward -> [dGate | dUp]
-    RedArgs r{};
-    r.N = ffn;
-    r.splits = (int)dgemv_splits(ffn, dim);
-    r.part = p.part1;
-    r.y = p.x2;
-    if (hidden_pre) {
-      r.scal = p.scal1;
-      r.nscal = dgemv_nscal(ffn, dim);
-      r.nx = hidden_pre;
-      r.ngam = gamma_sub;
-      r.eps = eps;
-    }
-    r.gate = gate;
-    r.up = up_;
-    r.act = act;
-    if ((e = launch_dgemv_red(RED_ACT, dt, r, s)) != hipSuccess) return e;
-    // 4. part2 = [dGate | dUp] [W_gate; W_up] (+ the FFN norm's row-sum shares)
+    // 2-4. part2 = [dGate | dUp] [W_gate; W_up] (+ the FFN norm's row-sum
+    // shares); the prologue forms each workgroup's slice of [dGate | dUp]
+    // from part1: dHid, sub-norm backward, activation backward
     g = GemvArgs{};
     g.N = dim;
     g.K = 2 * ffn;
     g.K1 = ffn;
     g.W1 = w_gate;
     g.W2 = w_up;
-    g.x = p.x2;
     g.part = p.part2;
     g.ng = gamma_ffn;
     g.nx = resid1;
     g.scal = p.scal2;
+    g.pro = PRO_ACT;
+    g.p.part = p.part1;
+    g.p.splits = (int)dgemv_splits(ffn, dim);
+    g.p.pn = ffn;
+    if (hidden_pre) {
+      g.p.scal = p.scal1;
+      g.p.nscal = dgemv_nscal(ffn, dim);
+      g.p.nx = hidden_pre;
+      g.p.ngam = gamma_sub;
+      g.p.eps = eps;
+    }
+    g.p.gate = gate;
+    g.p.up = up_;
+    g.p.act = act;
     if ((e = launch_dgemv(dt, dt, g, s)) != hipSuccess) return e;
     // 5. d_resid += rmsnorm_bwd(resid1, gamma_ffn, dN2)
-    r = RedArgs{};
+    RedArgs r{};
     r.N = dim;
-    r.splits = (int)dgemv_splits(dim, 2 * ffn);
+    r.splits = (int)dgemv_splits(dim, 2 * ffn, PRO_ACT);
     r.part = p.part2;
     r.y = d_resid;
     r.scal = p.scal2;
-    r.nscal = dgemv_nscal(dim, 2 * ffn);
+    r.nscal = dgemv_nscal(dim, 2 * ffn, PRO_ACT);
     r.nx = resid1;
     r.ngam = gamma_ffn;
     r.eps = eps;
@@ -446,15 +443,15 @@ LayerPlan layer_plan(void* ws, const lorabwd_layer_desc* d, int64_t rq, int64_t 
   const size_t lv = rv > 0 ? up(lora_ws_bytes(S, H, kvd, rv)) : 0;
   size_t sc = lq > lv ? lq : lv;
   if (use_decode_chain(d)) {
-    p.part2 = c.take<float>(dgemv_part_bytes(H, 2 * I));
-    p.x2 = c.take<float>((size_t)2 * I * 4);
+    p.part2 = c.take<float>(dgemv_part_bytes(H, 2 * I, PRO_ACT));
+    p.x2 = c.take<float>((size_t)(2 * I > H ? 2 * I : H) * 4);
     p.scal1 = c.take<float>((size_t)2 * dgemv_nscal(I, H) * 4);
-    p.scal2 = c.take<float>((size_t)2 * dgemv_nscal(H, 2 * I) * 4);
-    p.scal3 = c.take<float>((size_t)2 * dgemv_nscal(qd, H) * 4);
+    p.scal2 = c.take<float>((size_t)2 * dgemv_nscal(H, 2 * I, PRO_ACT) * 4);
+    p.scal3 = c.take<float>((size_t)2 * dgemv_nscal(qd, H, PRO_RESID) * 4);
     p.dA = c.take<float>(dec_attn_ws_bytes(L, d->n_heads, d->head_dim));
     // part1 and part3 share the scratch region (part1 is dead once the
     // second stream has reduced it), and so do the adapters afterwards
-    for (size_t v : {dgemv_part_bytes(I, H), dgemv_part_bytes(qd, H)})
+    for (size_t v : {dgemv_part_bytes(I, H), dgemv_part_bytes(qd, H, PRO_RESID)})
       if (v > sc) sc = v;
   } else {
     const size_t f = ffn_plan(nullptr, S, H, I, d->dtype).bytes;
@@ -492,74 +489,76 @@ hipError_t decode_chain(const lorabwd_layer_desc* d, const lorabwd_layer_weights
     g.scal = p.scal1;
   }
   if ((e = launch_dgemv(dt, dt, g, s)) != hipSuccess) return e;
-  // dHid -> sub-norm backward -> activation backward -> x2 = [dGate | dUp]
-  RedArgs r{};
-  r.N = I;
-  r.splits = (int)dgemv_splits(I, H);
-  r.part = part13;
-  r.y = p.x2;
-  if (sub) {
-    r.scal = p.scal1;
-    r.nscal = dgemv_nscal(I, H);
-    r.nx = a->hidden_pre;
-    r.ngam = w->gamma_fsub;
-    r.eps = d->eps;
-  }
-  r.gate = a->gate;
-  r.up = a->up;
-  r.act = d->act;
-  if ((e = launch_dgemv_red(RED_ACT, dt, r, s)) != hipSuccess) return e;
-  // part2 = x2 [W_gate; W_up], with the FFN norm's row-sum shares
+  // part2 = [dGate | dUp] [W_gate; W_up], with the FFN norm's row-sum
+  // shares; the prologue forms each workgroup's slice of [dGate | dUp] from
+  // part1 (dHid, sub-norm backward, activation backward)
   g = GemvArgs{};
   g.N = H;
   g.K = 2 * I;
   g.K1 = I;
   g.W1 = w->w_gate;
   g.W2 = w->w_up;
-  g.x = p.x2;
   g.part = p.part2;
   g.ng = w->gamma_ffn;
   g.nx = a->resid1;
   g.scal = p.scal2;
+  g.pro = PRO_ACT;
+  g.p.part = part13;
+  g.p.splits = (int)dgemv_splits(I, H);
+  g.p.pn = I;
+  if (sub) {
+    g.p.scal = p.scal1;
+    g.p.nscal = dgemv_nscal(I, H);
+    g.p.nx = a->hidden_pre;
+    g.p.ngam = w->gamma_fsub;
+    g.p.eps = d->eps;
+  }
+  g.p.gate = a->gate;
+  g.p.up = a->up;
+  g.p.act = d->act;
   if ((e = launch_dgemv(dt, dt, g, s)) != hipSuccess) return e;
-  // d_hidden = d_out + rmsnorm_bwd(resid1, gamma_ffn, dN2)   (dH1, in place)
-  r = RedArgs{};
-  r.N = H;
-  r.splits = (int)dgemv_splits(H, 2 * I);
-  r.part = p.part2;
-  r.y = d_hidden;
-  r.scal = p.scal2;
-  r.nscal = dgemv_nscal(H, 2 * I);
-  r.nx = a->resid1;
-  r.ngam = w->gamma_ffn;
-  r.eps = d->eps;
-  if ((e = launch_dgemv_red(RED_ACCUM, dt, r, s)) != hipSuccess) return e;
-  // part3 = dH1 W_o, with the attention sub-norm's row-sum shares
+  // part3 = dH1 W_o, with the attention sub-norm's row-sum shares; the
+  // prologue forms dH1 = d_out + rmsnorm_bwd(resid1, gamma_ffn, dN2) for its
+  // rows from part2 (column block 0 also keeps it in x2)
   g = GemvArgs{};
   g.N = qd;
   g.K = H;
   g.W1 = w->w_o;
-  g.x = d_hidden;
   g.part = part13;
   if (sub) {
     g.ng = w->gamma_asub;
     g.nx = a->ctx;
     g.scal = p.scal3;
   }
+  g.pro = PRO_RESID;
+  g.p.part = p.part2;
+  g.p.splits = (int)dgemv_splits(H, 2 * I, PRO_ACT);
+  g.p.pn = H;
+  g.p.scal = p.scal2;
+  g.p.nscal = dgemv_nscal(H, 2 * I, PRO_ACT);
+  g.p.nx = a->resid1;
+  g.p.ngam = w->gamma_ffn;
+  g.p.eps = d->eps;
+  g.p.resid = d_hidden;
+  g.p.xout = p.x2;
   if ((e = launch_dgemv(dt, dt, g, s)) != hipSuccess) return e;
-  // dCtx (sub-norm backward applied)
-  r = RedArgs{};
+  // dCtx (sub-norm backward applied); the same launch moves dH1 into the
+  // caller's d_hidden, whose old contents W_o's prologue has consumed
+  RedArgs r{};
   r.N = qd;
-  r.splits = (int)dgemv_splits(qd, H);
+  r.splits = (int)dgemv_splits(qd, H, PRO_RESID);
   r.part = part13;
   r.y = p.dctx;
   if (sub) {
     r.scal = p.scal3;
-    r.nscal = dgemv_nscal(qd, H);
+    r.nscal = dgemv_nscal(qd, H, PRO_RESID);
     r.nx = a->ctx;
     r.ngam = w->gamma_asub;
     r.eps = d->eps;
   }
+  r.copy_src = p.x2;
+  r.copy_dst = d_hidden;
+  r.copy_n = H;
   if ((e = launch_dgemv_red(RED_STORE, dt, r, s)) != hipSuccess) return e;
   // attention backward, inverse RoPE at the token's position
   DecAttnArgs at{};

@@ -44,6 +44,54 @@ template <> struct Act<bf16> {
   }
 };
 
+// Buffer loads (MUBUF, offsets in bytes from a resource base).  A load whose
+// per-lane offset is at or past the resource's size reads 0 and touches no
+// memory, so a bound becomes an offset instead of a branch: a branch around
+// a load makes the compiler wait for every load still in flight where the
+// two paths join, which empties a register prefetch pipeline.  Only the
+// per-lane (VGPR) offset carries bounds here; resources stay below 1 GiB so
+// a valid offset plus BUF_OOB never wraps into range.
+typedef __amdgpu_buffer_rsrc_t brsrc_t;
+constexpr uint32_t BUF_OOB = 0x80000000u;
+constexpr uint32_t BUF_MAX_BYTES = 0x40000000u;
+__device__ __forceinline__ brsrc_t make_brsrc(const void* base, uint32_t bytes) {
+  // word 3 = 0x00020000: 32-bit raw data format for the gfx9 family
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ float4 bload_f4(brsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                     __uint_as_float(v[3]));
+}
+__device__ __forceinline__ uint2 bload_u2(brsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ float2 bload_f2(brsrc_t r, uint32_t off) {
+  const uint2 v = bload_u2(r, off);
+  return make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
+}
+__device__ __forceinline__ float4 bf4_to_f4(uint2 u) {
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+// 4 consecutive elements (float or bf16) at element index i as float; the
+// raw type is kept until use so that the load is not waited on early
+template <typename T> struct BufVec;
+template <> struct BufVec<float> {
+  typedef float4 raw;
+  static __device__ __forceinline__ raw load(brsrc_t r, uint32_t off) { return bload_f4(r, off); }
+  static __device__ __forceinline__ float4 cvt(raw v) { return v; }
+  static __device__ __forceinline__ raw zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+};
+template <> struct BufVec<bf16> {
+  typedef uint2 raw;
+  static __device__ __forceinline__ raw load(brsrc_t r, uint32_t off) { return bload_u2(r, off); }
+  static __device__ __forceinline__ float4 cvt(raw v) { return bf4_to_f4(v); }
+  static __device__ __forceinline__ raw zero() { return make_uint2(0u, 0u); }
+};
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

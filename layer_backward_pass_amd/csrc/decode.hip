@@ -3,21 +3,25 @@
 // the three weight streams (W_down, [W_gate; W_up], W_o) and everything
 // elementwise rides along with them:
 //
-//   dgemv<PLAIN>  part1 = d_out W_down over row chunks; every workgroup also
-//                 emits its share of <dHid*gamma_fsub, hidden_pre> (the
-//                 FFN sub-norm's row sum is linear in dHid) and, for the
-//                 first chunk, of sum hidden_pre^2
-//   dgemv<ACT>    prologue: dHid for its rows from part1, sub-norm backward,
-//                 ReLU^2 / SwiGLU backward; part2 = [dGate|dUp][W_gate;W_up]
-//                 plus the FFN-norm shares over resid1
-//   dgemv<RESID>  prologue: dN2 for its rows from part2, dH1 = d_out +
-//                 rmsnorm_bwd(resid1, gamma_ffn, dN2); part3 = dH1 W_o plus
-//                 the attention sub-norm shares over ctx
-//   dgemv_red     dCtx = sum of part3, attention sub-norm backward applied;
-//                 dH1 copied to the caller's d_hidden
-//   dec_attn1     dA = dCtx V^T and dV = P^T dCtx per block of keys
-//   dec_attn2     per head: delta, dS = P (dA - delta), dq = scale dS K and
-//                 the inverse RoPE rotation at the token's position
+//   dgemv<PRO_COPY>   part1 = d_out W_down over row chunks; every workgroup
+//                     also emits its share of <dHid*gamma_fsub, hidden_pre>
+//                     (the FFN sub-norm's row sum is linear in dHid) and, for
+//                     the first chunk, of sum hidden_pre^2
+//   dgemv<PRO_ACT>    prologue: dHid for its rows from part1, sub-norm
+//                     backward, ReLU^2 / SwiGLU backward; part2 =
+//                     [dGate|dUp][W_gate;W_up] plus the FFN-norm shares over
+//                     resid1
+//   dgemv<PRO_RESID>  prologue: dN2 for its rows from part2, dH1 = d_out +
+//                     rmsnorm_bwd(resid1, gamma_ffn, dN2); part3 = dH1 W_o
+//                     plus the attention sub-norm shares over ctx
+//   dgemv_red         dCtx = sum of part3, attention sub-norm backward
+//                     applied; dH1 copied to the caller's d_hidden
+//   dec_attn_mfma     per 16 keys of a KV head (one wave): dA = dCtx V^T,
+//                     dS = P (dA - delta) with delta = dCtx . ctx (the row
+//                     sum of P dA, as the output is P V), dV = P^T dCtx on
+//                     the fp32 MFMA, and this block's share of dq = scale dS K
+//   dec_attn_dqc      per head: the dq shares summed in order, then the
+//                     inverse RoPE rotation at the token's position
 //
 // Hesper "FFN Backward GPU Kernels" (the five steps of "Backward
 // (reverse)", "ReLU²×Mul Backward") and "Attention Backward GPU Kernels"
@@ -25,9 +29,11 @@
 // "Softmax Backward", "Attention Score Backward", "RoPE Backward").
 //
 // GEMV layout: a workgroup owns 256 adjacent output columns (one float4 per
-// lane) and a chunk of rows; its four waves split the rows, keep 8 rows of
-// 16-byte loads in flight each, and add their results in a fixed order.
-// Every reduction has a fixed order, so results are bitwise reproducible.
+// lane) and a chunk of rows; its four waves split the rows and keep two
+// stages of 8 rows of 16-byte loads in flight each, and add their results in
+// a fixed order.  Loads are buffer loads whose bounds are offsets (out of
+// range reads 0), so no branch interrupts the prefetch pipeline.  Every
+// reduction has a fixed order, so results are bitwise reproducible.
 #include "common.h"
 #include "kernels.h"
 
@@ -76,52 +82,235 @@ __device__ __forceinline__ void norm_consts_block(const float* sc, int64_t n, in
   c = dot / (nf * r2);
 }
 
-template <typename TW, typename TA>
+// x[kb .. kb+R) for the PRO_ACT / PRO_RESID prologues (see GemvPro).  The
+// producer's N is a multiple of 4 and so is R, so a thread takes 4 adjacent
+// rows (one float4 per partial vector): row quad q = t % nq, and the
+// S = 256 / nq threads of a quad split the producer's partials between them
+// (8 loads in flight each, so one round covers 8 S partials).  issue() puts
+// every load of the prologue in flight -- before the workgroup's first weight
+// rows, so they do not queue behind them -- and finish() adds the partials
+// (fixed order: per thread, then the S threads of a quad through LDS),
+// applies the norm and elementwise step, and writes x to LDS.
+template <typename TA, int PRO>
+struct GemvPrologue {
+  float4 v[8];
+  float2 sv[8];
+  typename BufVec<TA>::raw ex, e1, e2;
+  float4 eg, r1;
+  int nq, S, q, sub;
+  int64_t rr, j;
+  bool act, fin, norm;
+
+  __device__ __forceinline__ void issue(const GemvPro& p, int64_t kb, int R) {
+    const int t = threadIdx.x;
+    nq = R >> 2;
+    S = 256 / nq;
+    q = t % nq;
+    sub = t / nq;
+    act = sub < S;
+    fin = sub == 0;
+    rr = kb + 4 * q;
+    j = (PRO == PRO_ACT && rr >= p.pn) ? rr - p.pn : rr;
+    norm = p.scal != nullptr;
+    const brsrc_t rp = make_brsrc(p.part, (uint32_t)(p.splits * p.pn * 4));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sp = sub + u * S;
+      const uint32_t off = (act && sp < p.splits) ? (uint32_t)((sp * p.pn + j) * 4) : BUF_OOB;
+      v[u] = bload_f4(rp, off);
+    }
+    // absent inputs get an empty resource (every load reads 0)
+    const brsrc_t rs = make_brsrc(norm ? (const void*)p.scal : p.part, norm ? (uint32_t)(p.nscal * 8) : 0u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = t + 256 * u;
+      sv[u] = bload_f2(rs, i < p.nscal ? (uint32_t)(i * 8) : BUF_OOB);
+    }
+    const uint32_t ae = sizeof(TA);
+    const brsrc_t rx = make_brsrc(norm ? p.nx : (const void*)p.part, norm ? (uint32_t)(p.pn * ae) : 0u);
+    const brsrc_t rg = make_brsrc(norm ? (const void*)p.ngam : (const void*)p.part, norm ? (uint32_t)(p.pn * 4) : 0u);
+    ex = BufVec<TA>::load(rx, (uint32_t)(j * ae));
+    eg = bload_f4(rg, (uint32_t)(j * 4));
+    if (PRO == PRO_ACT) {
+      e1 = BufVec<TA>::load(make_brsrc(p.gate, (uint32_t)(p.pn * ae)), (uint32_t)(j * ae));
+      e2 = BufVec<TA>::load(make_brsrc(p.up, (uint32_t)(p.pn * ae)), (uint32_t)(j * ae));
+    } else {
+      r1 = bload_f4(make_brsrc(p.resid, (uint32_t)(p.pn * 4)), (uint32_t)(j * 4));
+    }
+  }
+
+  __device__ __forceinline__ void finish(const GemvPro& p, float* xs, float* red, float4* lred) {
+    const int t = threadIdx.x;
+    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      y.x += v[u].x;
+      y.y += v[u].y;
+      y.z += v[u].z;
+      y.w += v[u].w;
+    }
+    for (int s0 = sub + 8 * S; s0 < p.splits; s0 += 8 * S) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int sp = s0 + u * S;
+        v[u] = (act && sp < p.splits) ? *reinterpret_cast<const float4*>(p.part + (int64_t)sp * p.pn + j)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        y.x += v[u].x;
+        y.y += v[u].y;
+        y.z += v[u].z;
+        y.w += v[u].w;
+      }
+    }
+    if (act) lred[t] = y;
+    float inv_r = 1.f, cc = 0.f;
+    if (norm) {
+      float dot = 0.f, ss = 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        dot += sv[u].x;
+        ss += sv[u].y;
+      }
+      for (int64_t i0 = t + 2048; i0 < p.nscal; i0 += 2048) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t i = i0 + 256 * u;
+          sv[u] = i < p.nscal ? *reinterpret_cast<const float2*>(p.scal + 2 * i) : make_float2(0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          dot += sv[u].x;
+          ss += sv[u].y;
+        }
+      }
+      dot = block_sum<4>(dot, red);  // its barriers also publish lred
+      ss = block_sum<4>(ss, red);
+      const float nf = (float)p.pn;
+      const float r2 = ss / nf + p.eps;
+      inv_r = 1.0f / sqrtf(r2);
+      cc = dot / (nf * r2);
+    } else {
+      __syncthreads();
+    }
+    if (!fin) return;
+    y = lred[q];
+    for (int k = 1; k < S; ++k) {
+      const float4 o = lred[k * nq + q];
+      y.x += o.x;
+      y.y += o.y;
+      y.z += o.z;
+      y.w += o.w;
+    }
+    float z[4] = {y.x, y.y, y.z, y.w};
+    if (norm) {
+      const float4 xv = BufVec<TA>::cvt(ex);
+      const float xa[4] = {xv.x, xv.y, xv.z, xv.w}, ga[4] = {eg.x, eg.y, eg.z, eg.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) z[k] = (z[k] * ga[k] - xa[k] * cc) * inv_r;
+    }
+    float x[4];
+    if (PRO == PRO_ACT) {
+      const float4 gv = BufVec<TA>::cvt(e1), uv = BufVec<TA>::cvt(e2);
+      const float ga[4] = {gv.x, gv.y, gv.z, gv.w}, ua[4] = {uv.x, uv.y, uv.z, uv.w};
+      const bool is_gate = rr < p.pn;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float dg, du;
+        if (p.act == SWIGLU) act_bwd1<SWIGLU>(ga[k], ua[k], z[k], dg, du);
+        else act_bwd1<RELU2>(ga[k], ua[k], z[k], dg, du);
+        x[k] = is_gate ? dg : du;
+      }
+    } else {
+      x[0] = r1.x + z[0];
+      x[1] = r1.y + z[1];
+      x[2] = r1.z + z[2];
+      x[3] = r1.w + z[3];
+      if (blockIdx.x == 0) *reinterpret_cast<float4*>(p.xout + j) = make_float4(x[0], x[1], x[2], x[3]);
+    }
+    *reinterpret_cast<float4*>(xs + 4 * q) = make_float4(x[0], x[1], x[2], x[3]);
+  }
+};
+
+template <typename TW, typename TA, int PRO>
 __global__ __launch_bounds__(256) void dgemv_kernel(GemvArgs a) {
   extern __shared__ float xs[];  // [kc] the input vector of this chunk
   __shared__ float4 red4[3][64];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  __shared__ float nred[4];
+  __shared__ float4 lred[PRO == PRO_COPY ? 1 : 256];
+  typedef BufVec<TW> WB;
+  typedef typename WB::raw WV;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t kb = (int64_t)blockIdx.y * a.kc;
   const int64_t ke = min(a.K, kb + a.kc);
   const int R = (int)(ke - kb);
   const int64_t n = (int64_t)blockIdx.x * DG_COLS + lane * 4;
-  const int64_t per = (R + 3) / 4;
-  const int64_t r0 = kb + w * per, r1 = min(ke, r0 + per);
+  // rows [i0, i1) of the chunk belong to this wave (uniform across it)
+  const int per = (R + 3) / 4;
+  const int i0 = min(R, w * per), i1 = min(R, i0 + per);
   const bool nok = n < a.N;
-  // two named register buffers (indices known at compile time): the next
-  // 8 rows are in flight while the current 8 are multiplied
-  float4 wa[DG_U], wb[DG_U];
-  auto fetch = [&](float4 (&wv)[DG_U], int64_t r) {
+  // the chunk's rows as two buffer ranges: rows of W1 (global row < K1) and
+  // rows of W2; lanes past N and rows past the wave's share read 0
+  const uint32_t rowb = (uint32_t)(a.N * sizeof(TW));
+  const int n1 = kb < a.K1 ? (int)(min(ke, a.K1) - kb) : 0;
+  const int64_t kb2 = kb + n1 - a.K1;  // first row of the W2 part, within W2
+  const brsrc_t rs1 = make_brsrc(n1 > 0 ? (const char*)a.W1 + kb * rowb : (const char*)a.W1, n1 * rowb);
+  const brsrc_t rs2 = make_brsrc(n1 < R ? (const char*)a.W2 + kb2 * rowb : (const char*)a.W2,
+                                 (uint32_t)(R - n1) * rowb);
+  const uint32_t coff = nok ? (uint32_t)(n * sizeof(TW)) : BUF_OOB;
+  // two named register stages (indices known at compile time): the next 8
+  // rows are in flight while the current 8 are multiplied
+  WV wa[DG_U], wb[DG_U];
+  auto fetch = [&](WV (&wv)[DG_U], int i) {
 #pragma unroll
     for (int u = 0; u < DG_U; ++u) {
-      const int64_t rr = r + u;
-      if (nok && rr < r1) {
-        const TW* wp = rr < a.K1 ? (const TW*)a.W1 + rr * a.N : (const TW*)a.W2 + (rr - a.K1) * a.N;
-        wv[u] = Act<TW>::ld4(wp, n);
-      } else {
-        wv[u] = make_float4(0, 0, 0, 0);
-      }
+      const int ii = i + u;
+      const bool in1 = ii < n1;
+      const uint32_t roff = ii < i1 ? (uint32_t)(in1 ? ii : ii - n1) * rowb : BUF_OOB;
+      wv[u] = WB::load(in1 ? rs1 : rs2, coff + roff);
     }
   };
-  auto consume = [&](const float4 (&wv)[DG_U], int64_t r, float4& acc) {
+  auto consume = [&](const WV (&wv)[DG_U], int i, float4& acc) {
 #pragma unroll
     for (int u = 0; u < DG_U; ++u) {
-      const float xv = (r + u < r1) ? xs[r + u - kb] : 0.f;
-      fma4(acc, xv, wv[u]);
+      const int ii = i + u;
+      float xv = xs[ii < R ? ii : R - 1];
+      xv = ii < i1 ? xv : 0.f;
+      fma4(acc, xv, WB::cvt(wv[u]));
     }
   };
-  // the first rows are in flight before the input vector arrives
-  fetch(wa, r0);
-  for (int r = t; r < R; r += 256) xs[r] = a.x[kb + r];
+  // the input vector's loads (or the prologue's) go out first, then two
+  // stages of weight rows; the scheduling fences keep that order, since a
+  // wait for a load also waits for every load issued before it
+  GemvPrologue<TA, PRO> pro;
+  float xr = 0.f;
+  if (PRO == PRO_COPY) {
+    // R <= 256 (kc <= 256): one element per thread
+    xr = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        make_brsrc(a.x + kb, (uint32_t)R * 4), t < R ? (int)(t * 4) : (int)BUF_OOB, 0, 0));
+  } else {
+    pro.issue(a.p, kb, R);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  fetch(wa, i0);
+  fetch(wb, i0 + DG_U);
+  __builtin_amdgcn_sched_barrier(0);
+  if (PRO == PRO_COPY) {
+    if (t < R) xs[t] = xr;
+  } else {
+    pro.finish(a.p, xs, nred, lred);
+  }
   __syncthreads();
+  // every step refills both stages unconditionally (rows past the wave's
+  // share read 0 and meet a 0 input), so no branch splits the pipeline
   float4 acc = make_float4(0, 0, 0, 0);
-  for (int64_t r = r0; r < r1; r += 2 * DG_U) {
-    if (r + DG_U < r1) fetch(wb, r + DG_U);
-    consume(wa, r, acc);
-    if (r + DG_U < r1) {
-      if (r + 2 * DG_U < r1) fetch(wa, r + 2 * DG_U);
-      consume(wb, r + DG_U, acc);
-    }
+  for (int i = i0; i < i1; i += 2 * DG_U) {
+    consume(wa, i, acc);
+    fetch(wa, i + 2 * DG_U);
+    consume(wb, i + DG_U, acc);
+    fetch(wb, i + 3 * DG_U);
   }
   if (w > 0) red4[w - 1][lane] = acc;
   __syncthreads();
@@ -166,35 +355,45 @@ __global__ __launch_bounds__(256) void dgemv_red_kernel(RedArgs a) {
   const int64_t n = (int64_t)blockIdx.x * DR_COLS + c * 4;
   const bool nok = n < a.N;
   const bool norm = a.scal != nullptr;
-  // ---- every global load first: partial sums, norm shares, elementwise inputs
+  // ---- every global load first (buffer loads, bounds as offsets): partial
+  // sums, norm shares, elementwise inputs, the element this thread copies
+  const uint32_t es = sizeof(TA);
+  const uint32_t rowb = (uint32_t)(a.N * 4);
+  const brsrc_t rp = make_brsrc(a.part, (uint32_t)a.splits * rowb);
+  const uint32_t coff = nok ? (uint32_t)(n * 4) : BUF_OOB;
   float4 v[8];
-  float2 sv[8];
-  float4 xin = make_float4(0, 0, 0, 0), gin = xin, gt = xin, upv = xin, prev = xin;
-  const int first_tile = a.splits < 128 ? a.splits : 128;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int i = g + 16 * u;
-    v[u] = (nok && i < first_tile) ? *reinterpret_cast<const float4*>(a.part + (int64_t)i * a.N + n)
-                                   : make_float4(0, 0, 0, 0);
+    v[u] = bload_f4(rp, i < a.splits ? coff + (uint32_t)i * rowb : BUF_OOB);
   }
-  if (norm) {
+  float2 sv[8];
+  const brsrc_t rsc = make_brsrc(norm ? (const void*)a.scal : (const void*)a.part,
+                                 norm ? (uint32_t)(a.nscal * 8) : 0u);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t i = t + 256 * u;
-      sv[u] = i < a.nscal ? *reinterpret_cast<const float2*>(a.scal + 2 * i) : make_float2(0.f, 0.f);
-    }
+  for (int u = 0; u < 8; ++u) {
+    const int64_t i = t + 256 * u;
+    sv[u] = bload_f2(rsc, i < a.nscal ? (uint32_t)(i * 8) : BUF_OOB);
   }
-  if (t < 16 && nok) {
-    if (norm) {
-      xin = Act<TA>::ld4((const TA*)a.nx, n);
-      gin = *reinterpret_cast<const float4*>(a.ngam + n);
-    }
-    if (MODE == RED_ACT) {
-      gt = Act<TA>::ld4((const TA*)a.gate, n);
-      upv = Act<TA>::ld4((const TA*)a.up, n);
-    }
-    if (MODE == RED_ACCUM) prev = *reinterpret_cast<const float4*>(a.y + n);
+  const bool ew = t < 16 && nok;
+  const uint32_t eo = ew ? (uint32_t)(n * es) : BUF_OOB, eo4 = ew ? (uint32_t)(n * 4) : BUF_OOB;
+  const typename BufVec<TA>::raw xin = BufVec<TA>::load(
+      make_brsrc(norm ? a.nx : (const void*)a.part, norm ? (uint32_t)(a.N * es) : 0u), eo);
+  const float4 gin = bload_f4(
+      make_brsrc(norm ? (const void*)a.ngam : (const void*)a.part, norm ? rowb : 0u), eo4);
+  typename BufVec<TA>::raw gt = BufVec<TA>::zero(), upv = gt;
+  if (MODE == RED_ACT) {
+    gt = BufVec<TA>::load(make_brsrc(a.gate, (uint32_t)(a.N * es)), eo);
+    upv = BufVec<TA>::load(make_brsrc(a.up, (uint32_t)(a.N * es)), eo);
   }
+  float4 prev = make_float4(0, 0, 0, 0);
+  if (MODE == RED_ACCUM) prev = bload_f4(make_brsrc(a.y, rowb), eo4);
+  const int64_t ci = (int64_t)blockIdx.x * 256 + t;
+  float cv = 0.f;
+  if (a.copy_n > 0)
+    cv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        make_brsrc(a.copy_src, (uint32_t)(a.copy_n * 4)), ci < a.copy_n ? (int)(ci * 4) : (int)BUF_OOB,
+        0, 0));
   // ---- partial sums over row chunks (first tile in flight above)
   float4 s = make_float4(0, 0, 0, 0);
 #pragma unroll
@@ -208,8 +407,7 @@ __global__ __launch_bounds__(256) void dgemv_red_kernel(RedArgs a) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int i = i0 + 16 * u;
-      v[u] = (nok && i < a.splits) ? *reinterpret_cast<const float4*>(a.part + (int64_t)i * a.N + n)
-                                   : make_float4(0, 0, 0, 0);
+      v[u] = bload_f4(rp, i < a.splits ? coff + (uint32_t)i * rowb : BUF_OOB);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -232,7 +430,7 @@ __global__ __launch_bounds__(256) void dgemv_red_kernel(RedArgs a) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int64_t i = i0 + 256 * u;
-        sv[u] = i < a.nscal ? *reinterpret_cast<const float2*>(a.scal + 2 * i) : make_float2(0.f, 0.f);
+        sv[u] = bload_f2(rsc, i < a.nscal ? (uint32_t)(i * 8) : BUF_OOB);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -259,13 +457,15 @@ __global__ __launch_bounds__(256) void dgemv_red_kernel(RedArgs a) {
     }
     float o[4] = {y.x, y.y, y.z, y.w};
     if (norm) {
-      const float xv[4] = {xin.x, xin.y, xin.z, xin.w}, gv[4] = {gin.x, gin.y, gin.z, gin.w};
+      const float4 xf = BufVec<TA>::cvt(xin);
+      const float xv[4] = {xf.x, xf.y, xf.z, xf.w}, gv[4] = {gin.x, gin.y, gin.z, gin.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = (o[q] * gv[q] - xv[q] * cc) * inv_r;
     }
     if (MODE == RED_ACT) {
       // o = dHid: gated activation backward -> y[n] = dGate, y[N + n] = dUp
-      const float gv[4] = {gt.x, gt.y, gt.z, gt.w}, uv[4] = {upv.x, upv.y, upv.z, upv.w};
+      const float4 gf = BufVec<TA>::cvt(gt), uf = BufVec<TA>::cvt(upv);
+      const float gv[4] = {gf.x, gf.y, gf.z, gf.w}, uv[4] = {uf.x, uf.y, uf.z, uf.w};
       float dg[4], du[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -284,13 +484,22 @@ __global__ __launch_bounds__(256) void dgemv_red_kernel(RedArgs a) {
       *reinterpret_cast<float4*>(a.y + n) = make_float4(o[0], o[1], o[2], o[3]);
     }
   }
+  if (ci < a.copy_n) a.copy_dst[ci] = cv;
+  for (int64_t i = ci + (int64_t)gridDim.x * 256; i < a.copy_n; i += (int64_t)gridDim.x * 256)
+    a.copy_dst[i] = a.copy_src[i];
 }
 
-// Rows per workgroup: ~1000-1500 workgroups so the tail where some CUs run
-// out of work is short; every wave streams a multiple of 8 rows.
-int64_t dgemv_kc(int64_t N, int64_t K) {
+// Rows per chunk (a multiple of 32, 64..256), from a target workgroup count
+// measured on the decode layer's three weight streams: a plain GEMV takes
+// about 512 workgroups (two per CU, every wave streaming 40 or more rows, so
+// the per-workgroup start -- input vector, final cross-wave sum -- is paid
+// rarely); one whose prologue reduces the producer's partials takes about 768,
+// three per CU and all resident at once (the prologue's latency is exposed
+// once per generation of workgroups on a CU); the residual prologue, whose
+// GEMV is short, keeps small chunks (~400 workgroups for a 2560 x 2560 W_o).
+int64_t dgemv_kc(int64_t N, int64_t K, int pro) {
   const int64_t cb = cdiv(N, DG_COLS);
-  int64_t splits = cdiv(1536, cb);
+  int64_t splits = cdiv(pro == PRO_ACT ? 768 : pro == PRO_RESID ? 1536 : 512, cb);
   if (splits < 1) splits = 1;
   int64_t kc = cdiv(cdiv(K, splits), 32) * 32;
   if (kc < 64) kc = 64;
@@ -298,35 +507,67 @@ int64_t dgemv_kc(int64_t N, int64_t K) {
   return kc;
 }
 
-int64_t dgemv_splits(int64_t N, int64_t K) { return cdiv(K, dgemv_kc(N, K)); }
+int64_t dgemv_splits(int64_t N, int64_t K, int pro) { return cdiv(K, dgemv_kc(N, K, pro)); }
 
-size_t dgemv_part_bytes(int64_t N, int64_t K) {
-  return (size_t)dgemv_splits(N, K) * N * sizeof(float);
+size_t dgemv_part_bytes(int64_t N, int64_t K, int pro) {
+  return (size_t)dgemv_splits(N, K, pro) * N * sizeof(float);
 }
 
-int64_t dgemv_nscal(int64_t N, int64_t K) { return dgemv_splits(N, K) * cdiv(N, DG_COLS); }
+int64_t dgemv_nscal(int64_t N, int64_t K, int pro) {
+  return dgemv_splits(N, K, pro) * cdiv(N, DG_COLS);
+}
 
 hipError_t launch_dgemv(int w_dt, int a_dt, GemvArgs a, hipStream_t s) {
-  a.kc = dgemv_kc(a.N, a.K);
+  a.kc = dgemv_kc(a.N, a.K, a.pro);
+  // the prologues take rows in quads of a float4 partial (at most 64 quads
+  // per chunk, kc <= 256, so every quad has at least 4 threads)
+  if (a.pro != PRO_COPY && (a.p.pn % 4 != 0 || a.K % 4 != 0 || a.kc > 256 ||
+                            a.K != (a.pro == PRO_ACT ? 2 * a.p.pn : a.p.pn) ||
+                            (double)a.p.splits * a.p.pn * 4 >= BUF_MAX_BYTES ||
+                            (double)a.p.nscal * 8 >= BUF_MAX_BYTES))
+    return hipErrorInvalidValue;
+  // buffer ranges: one chunk of weight rows
+  if ((double)a.kc * a.N * (w_dt == F32 ? 4 : 2) >= BUF_MAX_BYTES) return hipErrorInvalidValue;
   if (a.W2 == nullptr) {
     a.W2 = a.W1;
     a.K1 = a.K;
   }
   dim3 grid((unsigned)cdiv(a.N, DG_COLS), (unsigned)cdiv(a.K, a.kc)), block(256);
   const size_t sm = (size_t)a.kc * sizeof(float);
+#define LBP_DGEMV(TW, TA)                                                            \
+  do {                                                                               \
+    if (a.pro == PRO_ACT) dgemv_kernel<TW, TA, PRO_ACT><<<grid, block, sm, s>>>(a);     \
+    else if (a.pro == PRO_RESID) dgemv_kernel<TW, TA, PRO_RESID><<<grid, block, sm, s>>>(a); \
+    else dgemv_kernel<TW, TA, PRO_COPY><<<grid, block, sm, s>>>(a);                    \
+  } while (0)
   if (w_dt == F32) {
-    if (a_dt == F32) dgemv_kernel<float, float><<<grid, block, sm, s>>>(a);
-    else dgemv_kernel<float, bf16><<<grid, block, sm, s>>>(a);
+    if (a_dt == F32) LBP_DGEMV(float, float);
+    else LBP_DGEMV(float, bf16);
   } else {
-    if (a_dt == F32) dgemv_kernel<bf16, float><<<grid, block, sm, s>>>(a);
-    else dgemv_kernel<bf16, bf16><<<grid, block, sm, s>>>(a);
+    if (a_dt == F32) LBP_DGEMV(bf16, float);
+    else LBP_DGEMV(bf16, bf16);
   }
+#undef LBP_DGEMV
   const double es = w_dt == F32 ? 4 : 2;
-  mark("dgemv", (double)a.K * a.N * es + a.K * 4.0 + a.N * 4.0, 2.0 * a.K * a.N, s);
+  // algorithmic bytes: the weights, the input vector and the result vector;
+  // a prologue reads, in place of the input vector, the reduced producer
+  // output and the elementwise inputs that form it (split partials are
+  // implementation traffic and not counted)
+  double xin = a.K * 4.0;
+  if (a.pro != PRO_COPY) {
+    const double ae = a_dt == F32 ? 4 : 2;
+    xin = a.p.pn * 4.0;
+    if (a.p.scal) xin += a.p.pn * (ae + 4);
+    xin += a.pro == PRO_ACT ? a.p.pn * 2 * ae : a.p.pn * 8.0;
+  }
+  mark("dgemv", (double)a.K * a.N * es + xin + a.N * 4.0, 2.0 * a.K * a.N, s);
   return hipGetLastError();
 }
 
 hipError_t launch_dgemv_red(int mode, int a_dt, RedArgs a, hipStream_t s) {
+  if ((double)a.splits * a.N * 4 >= BUF_MAX_BYTES || (double)a.nscal * 8 >= BUF_MAX_BYTES ||
+      (double)a.copy_n * 4 >= BUF_MAX_BYTES)
+    return hipErrorInvalidValue;
   dim3 grid((unsigned)cdiv(a.N, DR_COLS)), block(256);
 #define LBP_RED(TA)                                                        \
   do {                                                                     \
@@ -342,6 +583,7 @@ hipError_t launch_dgemv_red(int mode, int a_dt, RedArgs a, hipStream_t s) {
   if (a.scal) bytes += (double)a.N * (es + 4);
   if (mode == RED_ACT) bytes += (double)a.N * (2 * es + 4);
   if (mode == RED_ACCUM) bytes += (double)a.N * 4;
+  bytes += (double)a.copy_n * 8;
   mark(mode == RED_ACT ? "dgemv_red_act" : mode == RED_ACCUM ? "dgemv_red_resid" : "dgemv_red",
        bytes, 0, s);
   return hipGetLastError();

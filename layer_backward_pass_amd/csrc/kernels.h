@@ -49,15 +49,41 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
 // share of the row sums of the RMSNorm that consumes y = sum of parts:
 // scal[2*wg] = <y_part*ng, nx> over its columns and scal[2*wg+1] = sum nx^2
 // over them (first row chunk only), wg = chunk * column_blocks + block.
+// Prologue of a GEMV whose input x is the output of the previous one: every
+// workgroup sums the producer's row-chunk partials for its own rows, takes
+// the RMSNorm constants from the producer's shares, and applies the
+// elementwise step on the way into LDS.
+//   PRO_ACT    x = [dGate | dUp] of dHid = norm(sum of parts) (the norm only
+//              when scal is set); x has 2 pn rows
+//   PRO_RESID  x = resid + rmsnorm_bwd(nx, ngam, sum of parts); workgroups of
+//              column block 0 also store x to xout
+enum GemvProMode { PRO_COPY = 0, PRO_ACT = 1, PRO_RESID = 2 };
+struct GemvPro {
+  const float* part;
+  int splits;
+  int64_t pn;
+  const float* scal;
+  int64_t nscal;
+  const void* nx;
+  const float* ngam;
+  float eps;
+  const void* gate;
+  const void* up;
+  int act;
+  const float* resid;
+  float* xout;
+};
 struct GemvArgs {
   int64_t N, K, K1, kc;
   const void* W1;
   const void* W2;
-  const float* x;
+  const float* x;  // PRO_COPY input
   float* part;
   float* scal;
   const void* nx;
   const float* ng;
+  int pro;  // GemvProMode
+  GemvPro p;
 };
 
 // y = sum over `splits` chunks of part, then:
@@ -80,12 +106,18 @@ struct RedArgs {
   const void* gate;
   const void* up;
   int act;
+  // optional plain copy done by the same launch: copy_dst[i] = copy_src[i]
+  const float* copy_src;
+  float* copy_dst;
+  int64_t copy_n;
 };
 
-int64_t dgemv_kc(int64_t N, int64_t K);
-int64_t dgemv_splits(int64_t N, int64_t K);
-size_t dgemv_part_bytes(int64_t N, int64_t K);
-int64_t dgemv_nscal(int64_t N, int64_t K);
+// rows per chunk, chunk count, partial bytes and norm-share count of the
+// GEMV over K rows and N columns launched with prologue mode `pro`
+int64_t dgemv_kc(int64_t N, int64_t K, int pro = PRO_COPY);
+int64_t dgemv_splits(int64_t N, int64_t K, int pro = PRO_COPY);
+size_t dgemv_part_bytes(int64_t N, int64_t K, int pro = PRO_COPY);
+int64_t dgemv_nscal(int64_t N, int64_t K, int pro = PRO_COPY);
 hipError_t launch_dgemv(int w_dt, int a_dt, GemvArgs a, hipStream_t s);
 hipError_t launch_dgemv_red(int mode, int a_dt, RedArgs a, hipStream_t s);
 

@@ -152,6 +152,8 @@ def test_attention_without_dv_and_empty_queries():
     (1, 64, 96, "relu2", True, F32),        # decode GEMV path
     (133, 192, 320, "swiglu", False, F32),  # ragged tiles
     (1, 2560, 6912, "relu2", True, F32),    # decode layer shape
+    (1, 128, 344, "swiglu", False, BF16),   # decode GEMV path, bf16, ragged chunk
+    (1, 512, 1032, "swiglu", True, F32),
     (70, 256, 512, "relu2", True, BF16),
     (300, 128, 256, "swiglu", False, BF16),
 ])

@@ -382,9 +382,29 @@ __device__ __forceinline__ ushortx8 pack8(const float (&x)[8]) {
   return o;
 }
 
+// Eight consecutive bf16 keys kc .. kc+7 of a P row at element offset
+// `row` of resource r; keys at or past s_kv, and the whole chunk when !ok,
+// read 0.  With PVEC (s_kv a multiple of 8) it is one 16-byte load.
+template <bool PVEC>
+__device__ __forceinline__ ushortx8 load_p8(brsrc_t r, bool ok, int64_t row, int64_t kc,
+                                            int64_t s_kv) {
+  if (PVEC) {
+    const uint32_t off = (ok && kc < s_kv) ? (uint32_t)((row + kc) * 2) : BUF_OOB;
+    return __builtin_bit_cast(ushortx8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+  } else {
+    ushortx8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t off = (ok && kc + j < s_kv) ? (uint32_t)((row + kc + j) * 2) : BUF_OOB;
+      v[j] = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    }
+    return v;
+  }
+}
+
 constexpr int HQ_KT = 64;  // keys per tile, bf16 dq kernel
 
-template <int D, int HW>
+template <int D, int HW, bool PVEC>
 __global__ __launch_bounds__(256, 2) void attn_dq_bf16_kernel(
     int64_t s_q, int64_t s_kv, int Hq, int grp, int64_t LK, int npairs,
     const float* __restrict__ dctx, const uint16_t* __restrict__ P,
@@ -397,7 +417,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_bf16_kernel(
   constexpr int SE = (NCH + 255) / 256;
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KT][VLD];
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][D][KLD];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform, so are h and the blocks
   const int l16 = lane & 15, c = lane >> 4;
   const int h = (int)blockIdx.y * HW + (w % HW), g = h / grp;
   const int64_t ldq = (int64_t)Hq * D, ldk = (int64_t)(Hq / grp) * D;
@@ -473,47 +494,38 @@ __global__ __launch_bounds__(256, 2) void attn_dq_bf16_kernel(
 #pragma unroll
     for (int f = 0; f < ND; ++f) acc[s][f] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const bool pvec = (s_kv & 7) == 0;
+  // buffer resources: the 16 P rows of each of the wave's query blocks, and
+  // the V and Kt tiles of the kv group (bounds become offsets, see common.h)
+  brsrc_t prs[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+    prs[s] = make_brsrc(P + ((int64_t)h * s_q + (has[s] ? 16 * (int64_t)sub[s] : 0)) * s_kv,
+                        (uint32_t)(16 * s_kv * 2));
   uint4 sv[SE], sk[SE];
-  // P of the current tile: [block][half], keys 16c .. 16c+15
+  // P of one tile: [block][half], keys 16c .. 16c+15 (0 past the block's keys)
   auto fetch_p = [&](int64_t k0, ushortx8 (&pc)[2][2]) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const bool ok = has[s] && qrow[s] < s_q && k0 < kend[s];
-      const uint16_t* pr = P + ((int64_t)h * s_q + (ok ? qrow[s] : 0)) * s_kv;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int64_t kc = k0 + 16 * c + 8 * hf;
-        ushortx8 v;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = 0;
-        if (ok) {
-          if (pvec) {
-            if (kc < s_kv) v = *reinterpret_cast<const ushortx8*>(pr + kc);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              if (kc + j < s_kv) v[j] = pr[kc + j];
-          }
-        }
-        pc[s][hf] = v;
-      }
+      for (int hf = 0; hf < 2; ++hf)
+        pc[s][hf] = load_p8<PVEC>(prs[s], ok, (int64_t)l16 * s_kv, k0 + 16 * c + 8 * hf, s_kv);
     }
   };
-  auto fetch = [&](int64_t k0) {
+  // V and Kt of the tile at k0 (all 0 when !valid)
+  auto fetch = [&](int64_t k0, bool valid) {
+    const brsrc_t vr = make_brsrc(V + k0 * ldk + g * D, (uint32_t)(KT * ldk * 2));
+    const brsrc_t kr = make_brsrc(Kt + (int64_t)g * D * LK + k0, (uint32_t)(((D - 1) * LK + KT) * 2));
 #pragma unroll
     for (int i = 0; i < SE; ++i) {
       const int e = t + 256 * i;
-      sv[i] = sk[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (e < NCH) {
-        const int kk = e / (D / 8), d8 = e % (D / 8);
-        if (k0 + kk < s_kv)
-          sv[i] = *reinterpret_cast<const uint4*>(V + (k0 + kk) * ldk + g * D + 8 * d8);
-        const int d = e / (KT / 8), k8 = e % (KT / 8);
-        sk[i] = *reinterpret_cast<const uint4*>(Kt + ((int64_t)g * D + d) * LK + k0 + 8 * k8);
-      }
+      const bool eok = valid && e < NCH;
+      const int kk = e / (D / 8), d8 = e % (D / 8);
+      sv[i] = bload_u4(vr, (eok && k0 + kk < s_kv) ? (uint32_t)((kk * ldk + 8 * d8) * 2) : BUF_OOB);
+      const int d = e / (KT / 8), k8 = e % (KT / 8);
+      sk[i] = bload_u4(kr, eok ? (uint32_t)((d * LK + 8 * k8) * 2) : BUF_OOB);
     }
-};
+  };
   auto stash = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < SE; ++i) {
@@ -528,57 +540,75 @@ __global__ __launch_bounds__(256, 2) void attn_dq_bf16_kernel(
     }
   };
 
+  // Pipeline: the next tile's V/Kt loads go out at the top of a step, and
+  // the next tile's P as soon as this tile's dS is formed (into the same
+  // registers), so both fly during the dQ products, the barrier and the next
+  // step's dA products.  Loads are unconditional (past the end they read 0),
+  // so no branch makes the compiler drain them.
   int buf = 0;
-  if (ntile > 0) {
-    fetch(0);
-    stash(0);
-  }
+  ushortx8 pc[2][2];
+  fetch(0, ntile > 0);
+  stash(0);
+  fetch_p(0, pc);
   __syncthreads();
   for (int it = 0; it < ntile; ++it) {
     const int64_t k0 = (int64_t)it * KT;
-    const bool more = it + 1 < ntile;
-    ushortx8 pc[2][2];
-    fetch_p(k0, pc);
-    if (more) fetch(k0 + KT);
-    const bool on0 = k0 < kend[0], on1 = k0 < kend[1];
+    fetch(k0 + KT, it + 1 < ntile);
+    // Block 0 (the shorter key range) is active only on the first tiles, so
+    // a wave-uniform branch per phase picks a body with or without its
+    // products; block 1's run unconditionally (past its range, or when the
+    // wave has no second block, its P and dCtx operands are 0 and so are
+    // its contributions).
+    const bool on0 = k0 < kend[0];
     // dA^T: sub-tile nt, row m -> key 16(m/4) + 4nt + m%4, column = query
     floatx4 da[2][4];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) da[s][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int ks = 0; ks < NK; ++ks) {
-        const ushortx8 a = *reinterpret_cast<const ushortx8*>(&Vs[buf][16 * nt + l16][32 * ks + 8 * c]);
-        if (on0) da[0][nt] = mfma16x16x32bf16(a, dcb[0][ks], da[0][nt]);
-        if (on1) da[1][nt] = mfma16x16x32bf16(a, dcb[1][ks], da[1][nt]);
-      }
-    // dS (fp32 algebra), packed to bf16 in the A layout of dQ = dS K
     ushortx8 dsa[2][2];
+    auto tile_ds = [&](auto both) {
+      constexpr bool B = decltype(both)::value;
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int nt = 2 * st + j / 4, v = j % 4;
-          const float p = bf2f(pc[s][st][4 * (nt & 1) + v]);
-          x[j] = p * (da[s][nt][v] - dl[s]);
+        for (int ks = 0; ks < NK; ++ks) {
+          const ushortx8 a = *reinterpret_cast<const ushortx8*>(&Vs[buf][16 * nt + l16][32 * ks + 8 * c]);
+          if (B) da[0][nt] = mfma16x16x32bf16(a, dcb[0][ks], da[0][nt]);
+          da[1][nt] = mfma16x16x32bf16(a, dcb[1][ks], da[1][nt]);
         }
-        dsa[s][st] = pack8(x);
-      }
+      // dS (fp32 algebra), packed to bf16 in the A layout of dQ = dS K
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int s = B ? 0 : 1; s < 2; ++s)
 #pragma unroll
-      for (int f = 0; f < ND; ++f) {
-        const ushortx8 b = *reinterpret_cast<const ushortx8*>(&Ks[buf][16 * f + l16][16 * c + 8 * st]);
-        if (on0) acc[0][f] = mfma16x16x32bf16(dsa[0][st], b, acc[0][f]);
-        if (on1) acc[1][f] = mfma16x16x32bf16(dsa[1][st], b, acc[1][f]);
-      }
-    if (more) stash(buf ^ 1);
+        for (int st = 0; st < 2; ++st) {
+          float x[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int nt = 2 * st + j / 4, v = j % 4;
+            const float p = bf2f(pc[s][st][4 * (nt & 1) + v]);
+            x[j] = p * (da[s][nt][v] - dl[s]);
+          }
+          dsa[s][st] = pack8(x);
+        }
+    };
+    auto tile_dq = [&](auto both) {
+      constexpr bool B = decltype(both)::value;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int f = 0; f < ND; ++f) {
+          const ushortx8 b = *reinterpret_cast<const ushortx8*>(&Ks[buf][16 * f + l16][16 * c + 8 * st]);
+          if (B) acc[0][f] = mfma16x16x32bf16(dsa[0][st], b, acc[0][f]);
+          acc[1][f] = mfma16x16x32bf16(dsa[1][st], b, acc[1][f]);
+        }
+    };
+    if (on0) tile_ds(std::integral_constant<bool, true>{});
+    else tile_ds(std::integral_constant<bool, false>{});
+    fetch_p(k0 + KT, pc);
+    if (on0) tile_dq(std::integral_constant<bool, true>{});
+    else tile_dq(std::integral_constant<bool, false>{});
+    stash(buf ^ 1);
     __syncthreads();
     buf ^= 1;
   }
@@ -597,7 +627,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_bf16_kernel(
 
 constexpr int HV_QT = 64;  // queries per step, bf16 dv kernel
 
-template <int D>
+template <int D, bool PVEC>
 __global__ __launch_bounds__(256) void attn_dv_bf16_kernel(int64_t s_q, int64_t s_kv, int Hq,
                                                            int grp, int cmax, int64_t qc,
                                                            int64_t LQ,
@@ -624,7 +654,6 @@ __global__ __launch_bounds__(256) void attn_dv_bf16_kernel(int64_t s_q, int64_t 
   float* dst = out + (cmax > 1 ? (int64_t)ch * s_kv * ldk : 0);
   if (qa >= qz) return;  // empty chunk (never chunk 0)
   const int kh = w & 1, dh = w >> 1;
-  const bool pvec = (s_kv & 7) == 0;
 
   floatx4 acc[2][ND2];
 #pragma unroll
@@ -638,39 +667,29 @@ __global__ __launch_bounds__(256) void attn_dv_bf16_kernel(int64_t s_q, int64_t 
     ushortx8 p[NP];
     uint4 c[SC];
   };
+  // one step's loads (all 0 for a step past the last, so the pipeline runs
+  // without branches)
   auto fetch = [&](Stage& r, int64_t it) {
-    const int h = g * grp + (int)(it / nqb);
-    const int64_t qb = qa + QT * (it % nqb);
+    const bool valid = it < nit;
+    const int64_t itc = valid ? it : 0;
+    const int h = g * grp + (int)(itc / nqb);
+    const int64_t qb = qa + QT * (itc % nqb);
+    const brsrc_t pr = make_brsrc(P + ((int64_t)h * s_q + qb) * s_kv, (uint32_t)(QT * s_kv * 2));
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int e = t + 256 * i;
       const int rr = e >> 3, k8 = e & 7;
-      const int64_t q = qb + rr, kc = k0 + 8 * k8;
-      ushortx8 v;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = 0;
-      if (q < qz) {
-        const uint16_t* pr = P + ((int64_t)h * s_q + q) * s_kv;
-        if (pvec) {
-          if (kc < s_kv) v = *reinterpret_cast<const ushortx8*>(pr + kc);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (kc + j < s_kv) v[j] = pr[kc + j];
-        }
-      }
-      r.p[i] = v;
+      r.p[i] = load_p8<PVEC>(pr, valid && qb + rr < qz, (int64_t)rr * s_kv, k0 + 8 * k8, s_kv);
     }
+    const brsrc_t cr = make_brsrc(dCt + (int64_t)h * D * LQ + qb, (uint32_t)(((D - 1) * LQ + QT) * 2));
 #pragma unroll
     for (int i = 0; i < SC; ++i) {
       const int e = t + 256 * i;
-      r.c[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (e < NC) {
-        const int d = e / (QT / 8), q8 = e % (QT / 8);
-        // rows past qz belong to the next chunk (or are the zero padding)
-        if (qb + 8 * q8 < qz)
-          r.c[i] = *reinterpret_cast<const uint4*>(dCt + ((int64_t)h * D + d) * LQ + qb + 8 * q8);
-      }
+      const int d = e / (QT / 8), q8 = e % (QT / 8);
+      // rows past qz belong to the next chunk (or are the zero padding);
+      // their P rows read 0
+      const bool ok = valid && e < NC && qb + 8 * q8 < qz;
+      r.c[i] = bload_u4(cr, ok ? (uint32_t)((d * LQ + 8 * q8) * 2) : BUF_OOB);
     }
   };
   auto stash = [&](const Stage& r, int buf) {
@@ -706,22 +725,22 @@ __global__ __launch_bounds__(256) void attn_dv_bf16_kernel(int64_t s_q, int64_t 
     }
   };
   // step it in LDS buffer it % 2; stages s0, s1 hold the next two steps
+  // (an odd step count ends with a step of zeros in buffer 1)
   Stage s0, s1;
   fetch(s0, 0);
   stash(s0, 0);
-  if (nit > 1) fetch(s0, 1);
-  if (nit > 2) fetch(s1, 2);
+  fetch(s0, 1);
+  fetch(s1, 2);
   __syncthreads();
   for (int64_t it = 0; it < nit; it += 2) {
     compute(0);
-    if (it + 1 < nit) stash(s0, 1);
+    stash(s0, 1);
     __syncthreads();
-    if (it + 3 < nit) fetch(s0, it + 3);
-    if (it + 1 >= nit) break;
+    fetch(s0, it + 3);
     compute(1);
-    if (it + 2 < nit) stash(s1, 0);
+    stash(s1, 0);
     __syncthreads();
-    if (it + 4 < nit) fetch(s1, it + 4);
+    fetch(s1, it + 4);
   }
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
@@ -1074,8 +1093,12 @@ static void launch_dq_bf16(int64_t s_q, int64_t s_kv, int Hq, int grp, int64_t L
   const int nsub = (int)cdiv64(s_q, 16);
   const int npairs = (nsub + 1) / 2;
   const dim3 grid((unsigned)cdiv64(npairs, QW), (unsigned)(Hq / HW));
-  attn_dq_bf16_kernel<D, HW><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, LK, npairs, dctx, P, Kt,
-                                                  V, ctx, delta, dq, scale, causal);
+  if (s_kv % 8 == 0)
+    attn_dq_bf16_kernel<D, HW, true><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, LK, npairs, dctx, P,
+                                                          Kt, V, ctx, delta, dq, scale, causal);
+  else
+    attn_dq_bf16_kernel<D, HW, false><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, LK, npairs, dctx, P,
+                                                           Kt, V, ctx, delta, dq, scale, causal);
 }
 
 template <int D>
@@ -1121,8 +1144,12 @@ static hipError_t attn_launch_bf16(int64_t s_q, int64_t s_kv, int Hq, int Hkv, c
   const DvPlan dp = dv_plan_bf16(s_q, s_kv, Hkv);
   float* part = dp.cmax > 1 ? (float*)(wb + wl.part) : dv;
   const dim3 grid((unsigned)(cdiv64(s_kv, DV_KT) * dp.cmax), (unsigned)Hkv);
-  attn_dv_bf16_kernel<D><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dp.cmax, dp.qc, wl.LQ, P, dCt,
-                                              part, causal);
+  if (s_kv % 8 == 0)
+    attn_dv_bf16_kernel<D, true><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dp.cmax, dp.qc, wl.LQ, P,
+                                                      dCt, part, causal);
+  else
+    attn_dv_bf16_kernel<D, false><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dp.cmax, dp.qc, wl.LQ, P,
+                                                       dCt, part, causal);
   mark("attn_dv_bf16", pbytes + qbytes * 2 + kvbytes * 4 * (dp.cmax > 1 ? dp.cmax : 1),
        2.0 * D * pairs * Hq, s);
   if ((e = hipGetLastError()) != hipSuccess || dp.cmax == 1) return e;

@@ -72,6 +72,10 @@ __device__ __forceinline__ float2 bload_f2(brsrc_t r, uint32_t off) {
   const uint2 v = bload_u2(r, off);
   return make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
 }
+__device__ __forceinline__ uint4 bload_u4(brsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 __device__ __forceinline__ float4 bf4_to_f4(uint2 u) {
   return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                      __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));

@@ -175,7 +175,7 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
 constexpr int H_BM = 128, H_BN = 256, H_BK = 64, H_NT = 512;
 constexpr int H_LDA = H_BK + 8, H_LDB = H_BN + 16;
 
-template <typename TA>
+template <typename TA, bool SPLITB>
 __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, int64_t K,
                                                          const TA* __restrict__ A, int64_t lda,
                                                          const uint16_t* __restrict__ B1,
@@ -204,32 +204,55 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
   const int64_t kend = min(K, kbeg + kps);
   C += z * split_stride;
   const int wm = (w & 1) * 64, wn = (w >> 1) * 64;
-  const bool full_mn = bm + H_BM <= M && bn + H_BN <= N;
 
+  // Loads are buffer loads whose bounds are offsets (out of range reads 0):
+  // no branch splits the prefetch pipeline, and a k-tile past the end is all
+  // zeros.  A: the tile's rows as one range.  B: the rows of one k-tile,
+  // from W1 (rows < K1) or W2; with SPLITB (K1 not a multiple of the tile)
+  // every chunk reads both sources, each masked to its own rows.
+  const uint32_t aes = sizeof(TA);
+  const int64_t mrows = min((int64_t)H_BM, M - bm);
+  const brsrc_t ra = make_brsrc(A + bm * lda, (uint32_t)(((mrows - 1) * lda + K) * aes));
+  auto brows = [&](const uint16_t* Bs_, int64_t r0, int64_t nrows) -> brsrc_t {
+    return make_brsrc(Bs_ + r0 * ldb + bn, nrows > 0 ? (uint32_t)(nrows * ldb * 2) : 0u);
+  };
   auto load = [&](Stage& r, int64_t k0) {
-    const bool one_src = k0 + H_BK <= K1 || k0 >= K1;
-    const bool fast = full_mn && k0 + H_BK <= kend && one_src;
-    const uint16_t* base = k0 < K1 ? B1 + k0 * ldb : B2 + (k0 - K1) * ldb;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int e = t + H_NT * i;
-      const int64_t m = bm + (e >> 3), k = k0 + 8 * (e & 7);
-      const bool ok = fast || (m < M && k < kend);
-      const uint4* p = reinterpret_cast<const uint4*>(A + m * lda + k);
+      const int m = e >> 3;
+      const int64_t k = k0 + 8 * (e & 7);
+      const uint32_t off = (m < mrows && k < kend) ? (uint32_t)((m * lda + k) * aes) : BUF_OOB;
 #pragma unroll
-      for (int j = 0; j < AW; ++j) r.a[i][j] = ok ? p[j] : make_uint4(0u, 0u, 0u, 0u);
+      for (int j = 0; j < AW; ++j) r.a[i][j] = bload_u4(ra, off + 16 * j);
     }
+    if (!SPLITB) {
+      // the whole tile lies in one source (K1 is a multiple of the tile)
+      const bool s1 = k0 < K1;
+      const int64_t r0 = s1 ? k0 : k0 - K1;
+      const int64_t nrows = min(kend, s1 ? K1 : K) - k0;
+      const brsrc_t rb = brows(s1 ? B1 : B2, r0, nrows);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int e = t + H_NT * i;
-      const int64_t kk = e >> 5, n = bn + 8 * (e & 31);
-      if (fast) {
-        r.b[i] = *reinterpret_cast<const uint4*>(base + kk * ldb + n);
-      } else {
-        const int64_t k = k0 + kk;  // N % 8 == 0: a chunk is whole
-        r.b[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (k < kend && n < N)
-          r.b[i] = *reinterpret_cast<const uint4*>((k < K1 ? B1 + k * ldb : B2 + (k - K1) * ldb) + n);
+      for (int i = 0; i < NB; ++i) {
+        const int e = t + H_NT * i;
+        const int kk = e >> 5, n = 8 * (e & 31);  // N % 8 == 0: a chunk is whole
+        const uint32_t off = (kk < nrows && bn + n < N) ? (uint32_t)((kk * ldb + n) * 2) : BUF_OOB;
+        r.b[i] = bload_u4(rb, off);
+      }
+    } else {
+      const int64_t n1 = min(kend, K1) - k0;   // rows of this tile in W1
+      const int64_t r2 = k0 > K1 ? k0 - K1 : 0, lo2 = K1 > k0 ? K1 - k0 : 0;
+      const brsrc_t rb1 = brows(B1, k0 < K1 ? k0 : 0, n1);
+      const brsrc_t rb2 = brows(B2, r2, min(kend, K) - k0 - lo2);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int e = t + H_NT * i;
+        const int kk = e >> 5, n = 8 * (e & 31);
+        const bool nok = bn + n < N && k0 + kk < kend;
+        const uint32_t o1 = (nok && kk < n1) ? (uint32_t)((kk * ldb + n) * 2) : BUF_OOB;
+        const uint32_t o2 = (nok && kk >= lo2) ? (uint32_t)(((kk - lo2) * ldb + n) * 2) : BUF_OOB;
+        const uint4 v1 = bload_u4(rb1, o1), v2 = bload_u4(rb2, o2);
+        r.b[i] = make_uint4(v1.x | v2.x, v1.y | v2.y, v1.z | v2.z, v1.w | v2.w);
       }
     }
   };
@@ -278,23 +301,25 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
     }
   };
 
-  // Two k-tiles in flight: the LDS buffer in use and one register stage.
-  // The stage is refilled right after it has been copied to LDS, and it is
-  // copied only after the MFMAs of the current tile have been issued.
-  Stage st;
-  int buf = 0;
-  if (kbeg < kend) {
-    load(st, kbeg);
-    stash(st, 0);
-  }
+  // Three k-tiles in flight: the LDS buffer in use and two register stages,
+  // so a tile's loads have two compute phases to arrive.  Each stage is
+  // copied to LDS after the MFMAs of the current tile were issued and
+  // refilled right after.  An odd tile count ends with a tile of zeros.
+  Stage s0, s1;
+  load(s0, kbeg);
+  stash(s0, 0);
+  load(s0, kbeg + H_BK);
+  load(s1, kbeg + 2 * H_BK);
   __syncthreads();
-  for (int64_t k0 = kbeg; k0 < kend; k0 += H_BK) {
-    const bool more = k0 + H_BK < kend;
-    if (more) load(st, k0 + H_BK);
-    compute(buf);
-    if (more) stash(st, buf ^ 1);
+  for (int64_t k0 = kbeg; k0 < kend; k0 += 2 * H_BK) {
+    compute(0);
+    stash(s0, 1);
     __syncthreads();
-    buf ^= 1;
+    load(s0, k0 + 3 * H_BK);
+    compute(1);
+    stash(s1, 0);
+    __syncthreads();
+    load(s1, k0 + 4 * H_BK);
   }
   store_tile<4, 4>(C, ldc, M, N, bm + wm, bn + wn, acc);
 }
@@ -389,15 +414,23 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
                                                 (const float*)B2, K1, ldb, out, ldo, kps,
                                                 sstride);
   } else {
+    // buffer ranges: one tile's rows of A, one k-tile of B
+    if (((double)(H_BM - 1) * lda + K) * 4 >= BUF_MAX_BYTES || (double)H_BK * ldb * 2 >= BUF_MAX_BYTES)
+      return hipErrorInvalidValue;
     const dim3 grid1((unsigned)(cdiv(N, pl.bn) * cdiv(M, pl.bm) * nsp));
-    if (a_dt == F32)
-      gemm_bf16_kernel<float><<<grid1, dim3(H_NT), 0, s>>>(M, N, K, (const float*)A, lda,
-                                                         (const uint16_t*)B1, (const uint16_t*)B2,
-                                                         K1, ldb, out, ldo, kps, sstride);
-    else
-      gemm_bf16_kernel<uint16_t><<<grid1, dim3(H_NT), 0, s>>>(
-          M, N, K, (const uint16_t*)A, lda, (const uint16_t*)B1, (const uint16_t*)B2, K1, ldb, out,
-          ldo, kps, sstride);
+    const bool splitb = K1 % H_BK != 0;
+#define LBP_GEMM_BF16(TA, SB)                                                                 \
+  gemm_bf16_kernel<TA, SB><<<grid1, dim3(H_NT), 0, s>>>(M, N, K, (const TA*)A, lda,           \
+                                                       (const uint16_t*)B1, (const uint16_t*)B2, \
+                                                       K1, ldb, out, ldo, kps, sstride)
+    if (a_dt == F32) {
+      if (splitb) LBP_GEMM_BF16(float, true);
+      else LBP_GEMM_BF16(float, false);
+    } else {
+      if (splitb) LBP_GEMM_BF16(uint16_t, true);
+      else LBP_GEMM_BF16(uint16_t, false);
+    }
+#undef LBP_GEMM_BF16
   }
   hipError_t e = hipGetLastError();
   mark(b_dt == F32 ? "gemm_f32_mfma" : "gemm_bf16_mfma",

@@ -61,10 +61,10 @@ __device__ __forceinline__ float ld_h(const void* h, int hdt, int64_t e) {
 // g:  rows = 16 tokens, k = features; lane loads dy[i0+l%16][o0+16c+4(l/16)+j]
 // dB: rows = 16 features (tile j: o0 + 4m + j), k = tokens; lane loads
 //     dy[i0+4q+l/16][o0+4(l%16)+j].
-template <int RB, bool VEC>
+template <int RB, bool VEC, typename TH>
 __global__ __launch_bounds__(256) void lora_dy_kernel(int64_t rows, int64_t out_dim, int rank,
                                                       int64_t rs, const float* __restrict__ dy,
-                                                      const void* __restrict__ h, int hdt,
+                                                      const TH* __restrict__ h,
                                                       const float* __restrict__ Bm,
                                                       float* __restrict__ gpart,
                                                       float* __restrict__ dbpart) {
@@ -93,21 +93,47 @@ __global__ __launch_bounds__(256) void lora_dy_kernel(int64_t rows, int64_t out_
 #pragma unroll
     for (int b = 0; b < RB; ++b) accb[j][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t i0 = i_beg; i0 < i_end; i0 += 16) {
+  // The slice's rows of dy and h as buffer ranges (bounds are offsets; rows
+  // past the slice read 0), and two 16-row steps in flight: the next step's
+  // loads are issued before the current one is multiplied.
+  const int64_t nrow = i_end - i_beg;
+  const brsrc_t rdy = make_brsrc(dy + i_beg * out_dim, nrow > 0 ? (uint32_t)(nrow * out_dim * 4) : 0u);
+  const brsrc_t rh = make_brsrc(h + i_beg * rank, nrow > 0 ? (uint32_t)(nrow * rank * sizeof(TH)) : 0u);
+  struct Step {
     float4 ga[4], da[4];
     float hv[4][RB];
+  };
+  auto ld4 = [&](int64_t row, int64_t c) -> float4 {
+    const bool rok = row < i_end;
+    const int64_t e = (row - i_beg) * out_dim + c;
+    if (VEC) return bload_f4(rdy, (rok && c < out_dim) ? (uint32_t)(e * 4) : BUF_OOB);
+    float v[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) ga[c] = ld4f<VEC>(dy, i0 + l16, rows, o0 + 16 * c + 4 * l4, out_dim);
+    for (int j = 0; j < 4; ++j)
+      v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rdy, (rok && c + j < out_dim) ? (int)((e + j) * 4) : (int)BUF_OOB, 0, 0));
+    return make_float4(v[0], v[1], v[2], v[3]);
+  };
+  auto fetch = [&](Step& S, int64_t i0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) S.ga[c] = ld4(i0 + l16, o0 + 16 * c + 4 * l4);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int64_t i = i0 + 4 * q + l4;
-      da[q] = ld4f<VEC>(dy, i, rows, o0 + 4 * l16, out_dim);
+      S.da[q] = ld4(i, o0 + 4 * l16);
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
         const int r = 16 * b + l16;
-        hv[q][b] = (i < rows && r < rank) ? ld_h(h, hdt, i * rank + r) : 0.f;
+        const uint32_t off = (i < i_end && r < rank) ? (uint32_t)(((i - i_beg) * rank + r) * sizeof(TH))
+                                                     : BUF_OOB;
+        if (sizeof(TH) == 4)
+          S.hv[q][b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rh, (int)off, 0, 0));
+        else
+          S.hv[q][b] = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rh, (int)off, 0, 0));
       }
     }
+  };
+  auto step = [&](const Step& S, int64_t i0) {
     floatx4 accg[RB];
 #pragma unroll
     for (int b = 0; b < RB; ++b) accg[b] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -116,13 +142,13 @@ __global__ __launch_bounds__(256) void lora_dy_kernel(int64_t rows, int64_t out_
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int b = 0; b < RB; ++b) accg[b] = mfma16x16x4(f4get(ga[c], j), bv[c][j][b], accg[b]);
+        for (int b = 0; b < RB; ++b) accg[b] = mfma16x16x4(f4get(S.ga[c], j), bv[c][j][b], accg[b]);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int b = 0; b < RB; ++b) accb[j][b] = mfma16x16x4(f4get(da[q], j), hv[q][b], accb[j][b]);
+        for (int b = 0; b < RB; ++b) accb[j][b] = mfma16x16x4(f4get(S.da[q], j), S.hv[q][b], accb[j][b]);
     // sum the four waves' g tiles in a fixed order
 #pragma unroll
     for (int b = 0; b < RB; ++b)
@@ -131,11 +157,21 @@ __global__ __launch_bounds__(256) void lora_dy_kernel(int64_t rows, int64_t out_
     __syncthreads();
     for (int e = t; e < 16 * RP; e += 256) {
       const int row = e / RP, col = e % RP;
-      if (i0 + row < rows)
+      if (i0 + row < i_end)
         gpart[((int64_t)blockIdx.x * rows + i0 + row) * RP + col] =
             ((gs[0][row][col] + gs[1][row][col]) + gs[2][row][col]) + gs[3][row][col];
     }
     __syncthreads();
+  };
+  // (an odd step count ends with a step of zeros, whose rows are not stored)
+  Step s0, s1;
+  fetch(s0, i_beg);
+  fetch(s1, i_beg + 16);
+  for (int64_t i0 = i_beg; i0 < i_end; i0 += 32) {
+    step(s0, i0);
+    fetch(s0, i0 + 32);
+    step(s1, i0 + 16);
+    fetch(s1, i0 + 48);
   }
   // dB tile j, register v: feature o0 + 4(4 l4 + v) + j, rank 16b + l16
   float* dp = dbpart + (int64_t)blockIdx.y * out_dim * rank;
@@ -151,17 +187,11 @@ __global__ __launch_bounds__(256) void lora_dy_kernel(int64_t rows, int64_t out_
       }
 }
 
-// Four consecutive activations of x as float (in_dim % 8 == 0, c % 4 == 0).
-template <typename T>
-__device__ __forceinline__ float4 ld4x(const T* x, int64_t row, int64_t rows, int64_t c,
-                                       int64_t ncol) {
-  if (row >= rows || c >= ncol) return make_float4(0.f, 0.f, 0.f, 0.f);
-  return Act<T>::ld4(x, row * ncol + c);
-}
-
 // One pass over x [rows, in]: dapart[by][r][k] = sum_{i in slice} g[i,r] x[i,k].
 // Result rows = rank (16 per block b), cols = features (tile j: k0 + 4n + j),
-// k = tokens.  g is [rows, 16 RB], already scaled and zero-padded.
+// k = tokens.  g is [rows, 16 RB], already scaled and zero-padded.  Two
+// 16-row steps in flight, loads through buffer ranges (in_dim % 8 == 0, so
+// a 4-feature chunk is whole).
 template <int RB, typename T>
 __global__ __launch_bounds__(256) void lora_da_kernel(int64_t rows, int64_t in_dim, int rank,
                                                       int64_t rs, const float* __restrict__ g,
@@ -173,27 +203,49 @@ __global__ __launch_bounds__(256) void lora_da_kernel(int64_t rows, int64_t in_d
   const int64_t k0 = (int64_t)blockIdx.x * LG_COLS + w * LW_COLS;
   const int64_t i_beg = (int64_t)blockIdx.y * rs;
   const int64_t i_end = min(rows, i_beg + rs);
+  const int64_t nrow = i_end - i_beg;
+  const brsrc_t rx = make_brsrc(x + i_beg * in_dim, nrow > 0 ? (uint32_t)(nrow * in_dim * sizeof(T)) : 0u);
+  const brsrc_t rg = make_brsrc(g + i_beg * RP, nrow > 0 ? (uint32_t)(nrow * RP * 4) : 0u);
   floatx4 acc[4][RB];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int b = 0; b < RB; ++b) acc[j][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t i0 = i_beg; i0 < i_end; i0 += 16) {
-    float4 xa[4];
+  struct Step {
+    typename BufVec<T>::raw xa[4];
     float gv[4][RB];
+  };
+  auto fetch = [&](Step& S, int64_t i0) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int64_t i = i0 + 4 * q + l4;
-      xa[q] = ld4x<T>(x, i, rows, k0 + 4 * l16, in_dim);
+      const int64_t c = k0 + 4 * l16;
+      const bool ok = i < i_end;
+      S.xa[q] = BufVec<T>::load(rx, (ok && c < in_dim) ? (uint32_t)(((i - i_beg) * in_dim + c) * sizeof(T)) : BUF_OOB);
 #pragma unroll
-      for (int b = 0; b < RB; ++b) gv[q][b] = i < rows ? g[i * RP + 16 * b + l16] : 0.f;
+      for (int b = 0; b < RB; ++b)
+        S.gv[q][b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rg, ok ? (int)(((i - i_beg) * RP + 16 * b + l16) * 4) : (int)BUF_OOB, 0, 0));
     }
+  };
+  auto step = [&](const Step& S) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 4; ++q) {
+      const float4 xf = BufVec<T>::cvt(S.xa[q]);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int b = 0; b < RB; ++b) acc[j][b] = mfma16x16x4(gv[q][b], f4get(xa[q], j), acc[j][b]);
+        for (int b = 0; b < RB; ++b) acc[j][b] = mfma16x16x4(S.gv[q][b], f4get(xf, j), acc[j][b]);
+    }
+  };
+  Step s0, s1;
+  fetch(s0, i_beg);
+  fetch(s1, i_beg + 16);
+  for (int64_t i0 = i_beg; i0 < i_end; i0 += 32) {
+    step(s0);
+    fetch(s0, i0 + 32);
+    step(s1);
+    fetch(s1, i0 + 48);
   }
   // tile j, register v: rank 16b + 4 l4 + v, feature k0 + 4 l16 + j
   float* dp = dapart + (int64_t)blockIdx.y * rank * in_dim;
@@ -219,6 +271,21 @@ __device__ __forceinline__ void adamw1(float& p, float gr, float& m, float& v, f
 
 // Elements [0, nb): dB = s sum_slices dbpart, then AdamW on B (lr_b).
 // Elements [nb, nb + ng): g = s sum_groups gpart (ng = rows * 16 RB).
+// sum_{c < n} p[c * stride] in index order, 16 loads in flight at a time
+__device__ __forceinline__ float sum_strided(const float* __restrict__ p, int n, int64_t stride) {
+  float d = 0.f;
+  int c = 0;
+  for (; c + 16 <= n; c += 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = p[(int64_t)(c + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) d += v[u];
+  }
+  for (; c < n; ++c) d += p[(int64_t)c * stride];
+  return d;
+}
+
 __global__ __launch_bounds__(256) void lora_b_update_kernel(int64_t nb, int slices,
                                                             const float* __restrict__ dbpart,
                                                             int64_t ng, int groups,
@@ -228,8 +295,7 @@ __global__ __launch_bounds__(256) void lora_b_update_kernel(int64_t nb, int slic
                                                             float* grad_b, AdamHP hp) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e < nb) {
-    float d = 0.f;
-    for (int c = 0; c < slices; ++c) d += dbpart[(int64_t)c * nb + e];
+    float d = sum_strided(dbpart + e, slices, nb);
     d *= s;
     if (grad_b) grad_b[e] = d;
     float p = B[e], mm = m[e], vv = v[e];
@@ -239,9 +305,7 @@ __global__ __launch_bounds__(256) void lora_b_update_kernel(int64_t nb, int slic
     v[e] = vv;
   } else if (e < nb + ng) {
     const int64_t f = e - nb;
-    float d = 0.f;
-    for (int c = 0; c < groups; ++c) d += gpart[(int64_t)c * ng + f];
-    g[f] = s * d;
+    g[f] = s * sum_strided(gpart + f, groups, ng);
   }
 }
 
@@ -256,8 +320,7 @@ __global__ __launch_bounds__(256) void lora_a_update_kernel(int64_t n, int slice
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   float sq = 0.f;
   if (e < n) {
-    float d = 0.f;
-    for (int c = 0; c < slices; ++c) d += dapart[(int64_t)c * n + e];
+    const float d = sum_strided(dapart + e, slices, n);
     if (grad_a) grad_a[e] = d;
     sq = d * d;
     float p = A[e], mm = m[e], vv = v[e];
@@ -325,12 +388,17 @@ void launch_dy(int64_t rows, int64_t out_dim, int rank, const Slicing& sl, const
                const void* h, int hdt, const float* B, float* gpart, float* dbpart,
                hipStream_t s) {
   const dim3 grid((unsigned)sl.groups, (unsigned)sl.slices);
-  if (out_dim % 4 == 0)
-    lora_dy_kernel<RB, true><<<grid, 256, 0, s>>>(rows, out_dim, rank, sl.rs, dy, h, hdt, B,
-                                                  gpart, dbpart);
-  else
-    lora_dy_kernel<RB, false><<<grid, 256, 0, s>>>(rows, out_dim, rank, sl.rs, dy, h, hdt, B,
-                                                   gpart, dbpart);
+#define LBP_DY(VEC, TH)                                                                    \
+  lora_dy_kernel<RB, VEC, TH><<<grid, 256, 0, s>>>(rows, out_dim, rank, sl.rs, dy,         \
+                                                   (const TH*)h, B, gpart, dbpart)
+  if (out_dim % 4 == 0) {
+    if (hdt == F32) LBP_DY(true, float);
+    else LBP_DY(true, uint16_t);
+  } else {
+    if (hdt == F32) LBP_DY(false, float);
+    else LBP_DY(false, uint16_t);
+  }
+#undef LBP_DY
 }
 
 template <int RB>

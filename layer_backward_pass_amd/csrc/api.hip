@@ -97,8 +97,8 @@ FfnPlan ffn_plan(void* ws, int64_t rows, int64_t dim, int64_t ffn, int dt) {
     p.dhid = c.take<float>((size_t)rows * ffn * 4);
     p.dgu = c.take<void>((size_t)rows * 2 * ffn * esize(dt));
     p.dn2 = c.take<float>((size_t)rows * dim * 4);
-    const size_t a = gemm_partial_bytes(rows, ffn, dim, dt);
-    const size_t b = gemm_partial_bytes(rows, dim, 2 * ffn, dt);
+    const size_t a = gemm_partial_bytes(rows, ffn, dim, F32, dt);
+    const size_t b = gemm_partial_bytes(rows, dim, 2 * ffn, dt, dt);
     p.partials = c.take<float>(a > b ? a : b);
   }
   p.bytes = c.used;
@@ -455,7 +455,7 @@ LayerPlan layer_plan(void* ws, const lorabwd_layer_desc* d, int64_t rq, int64_t 
       if (v > sc) sc = v;
   } else {
     const size_t f = ffn_plan(nullptr, S, H, I, d->dtype).bytes;
-    const size_t o = S == 1 ? dgemv_part_bytes(qd, H) : gemm_partial_bytes(S, qd, H, d->dtype);
+    const size_t o = S == 1 ? dgemv_part_bytes(qd, H) : gemm_partial_bytes(S, qd, H, F32, d->dtype);
     const size_t a = up(attn_ws_bytes(S, L, d->n_heads, d->n_kv_heads, d->head_dim, d->dtype));
     for (size_t v : {f, o, a})
       if (v > sc) sc = v;

@@ -388,9 +388,33 @@ int gemm_splits(int64_t M, int64_t N, int64_t K, int b_dt) {
   return gemm_plan(M, N, K, b_dt).nsp;
 }
 
-size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K, int b_dt) {
+// Scratch of launch_gemm: the split-K partials, then (bf16 weights with an
+// fp32 A) A rounded to bf16, [M][K] -- the MFMA kernel then reads 2 bytes per
+// A element instead of 4 and keeps no conversion in its k-loop.
+static size_t gemm_part_only(int64_t M, int64_t N, int64_t K, int b_dt) {
   const int s = gemm_splits(M, N, K, b_dt);
-  return s > 1 ? (size_t)s * M * N * sizeof(float) : 0;
+  return s > 1 ? ((size_t)s * M * N * sizeof(float) + 255) / 256 * 256 : 0;
+}
+size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K, int a_dt, int b_dt) {
+  size_t b = gemm_part_only(M, N, K, b_dt);
+  if (a_dt == F32 && b_dt != F32) b += ((size_t)M * K * 2 + 255) / 256 * 256;
+  return b;
+}
+
+// A (fp32, row stride lda) -> bf16 [M][K], round to nearest even (K % 8 == 0)
+__global__ __launch_bounds__(256) void cvt_a_bf16_kernel(int64_t M, int64_t K, const float* __restrict__ A,
+                                                         int64_t lda, uint16_t* __restrict__ out) {
+  const int64_t q = K / 8, total = M * q;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t m = i / q, k = (i - m * q) * 8;
+    const float4 x = *reinterpret_cast<const float4*>(A + m * lda + k);
+    const float4 y = *reinterpret_cast<const float4*>(A + m * lda + k + 4);
+    *reinterpret_cast<uint4*>(out + m * K + k) =
+        make_uint4((uint32_t)f2bf(x.x) | ((uint32_t)f2bf(x.y) << 16),
+                   (uint32_t)f2bf(x.z) | ((uint32_t)f2bf(x.w) << 16),
+                   (uint32_t)f2bf(y.x) | ((uint32_t)f2bf(y.y) << 16),
+                   (uint32_t)f2bf(y.z) | ((uint32_t)f2bf(y.w) << 16));
+  }
 }
 
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt, int64_t lda,
@@ -414,6 +438,18 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
                                                 (const float*)B2, K1, ldb, out, ldo, kps,
                                                 sstride);
   } else {
+    if (a_dt == F32) {
+      // A to bf16 once, into the scratch after the partials
+      uint16_t* a16 = (uint16_t*)((char*)partials + gemm_part_only(M, N, K, b_dt));
+      int64_t blocks = cdiv(M * (K / 8), 256);
+      if (blocks > 8192) blocks = 8192;
+      cvt_a_bf16_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(M, K, (const float*)A, lda, a16);
+      mark("cvt_a_bf16", (double)M * K * 6, 0, s);
+      if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+      A = a16;
+      a_dt = BF16;
+      lda = K;
+    }
     // buffer ranges: one tile's rows of A, one k-tile of B
     if (((double)(H_BM - 1) * lda + K) * 4 >= BUF_MAX_BYTES || (double)H_BK * ldb * 2 >= BUF_MAX_BYTES)
       return hipErrorInvalidValue;

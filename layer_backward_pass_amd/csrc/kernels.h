@@ -34,11 +34,12 @@ hipError_t launch_to_bf16(int64_t n, const float* src, void* dst, hipStream_t s)
 // ---- products (gemm.hip)
 // C[M,N] = A[M,K] B[K,N]; B rows k < K1 come from B1 (row k), rows k >= K1
 // from B2 (row k - K1).  A is float or bf16 (a_dt), B is float or bf16
-// (b_dt).  bf16 B runs on bf16 matrix cores (A rounded to bf16).
-// split-K writes partial sums to `partials` ([splits, M, N]) and reduces
-// them in order; partial_bytes must cover gemm_partial_bytes().
+// (b_dt).  bf16 B runs on bf16 matrix cores (A rounded to bf16; an fp32 A
+// is first rounded into `partials` after the split-K area).  split-K writes
+// partial sums to `partials` ([splits, M, N]) and reduces them in order;
+// `partials` must hold gemm_partial_bytes(M, N, K, a_dt, b_dt) bytes.
 int gemm_splits(int64_t M, int64_t N, int64_t K, int b_dt);
-size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K, int b_dt);
+size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K, int a_dt, int b_dt);
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt, int64_t lda,
                        const void* B1, const void* B2, int64_t K1, int b_dt, int64_t ldb,
                        float* C, int64_t ldc, float* partials, hipStream_t s);

@@ -63,7 +63,8 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
   constexpr int BQS = F_NT / F_BN;             // k-quad stride between them (2)
   __shared__ __attribute__((aligned(16))) float As[2][F_BM][F_LD];
   __shared__ __attribute__((aligned(16))) float Bs[2][F_BN][F_LD];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
   const int l16 = lane & 15, c = lane >> 4;
   // 1-D grid: item u -> (split z, column panel n, row tile m), m fastest,
   // so the row tiles that read one weight panel run together on one XCD.
@@ -76,69 +77,54 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
   C += z * split_stride;
   const int wm = (w & 1) * 64, wn = (w >> 1) * 64;
 
-  // A: rows (t/8) + 64 i, k quad t%8.  B: column t % 256, k quads t/256 + 2i.
-  const int am = t >> 3, ak = 4 * (t & 7), bc = t % F_BN, bq0 = t / F_BN;
-  const bool full_mn = bm + F_BM <= M && bn + F_BN <= N;
-  const float* arow[NA];
-#pragma unroll
-  for (int i = 0; i < NA; ++i) arow[i] = A + (bm + am + 64 * i) * lda + ak;
-  int64_t boff[NBQ];  // offset of this thread's quad i inside a k-tile of B
-#pragma unroll
-  for (int i = 0; i < NBQ; ++i) boff[i] = (int64_t)(4 * (bq0 + BQS * i)) * ldb + bn + bc;
-  float4 ra[NA], rb[NBQ];
-  auto load = [&](int64_t k0) {
-    const bool one_src = k0 + F_BK <= K1 || k0 >= K1;
-    if (full_mn && k0 + F_BK <= kend && one_src) {
-      const float* base = k0 < K1 ? B1 + k0 * ldb : B2 + (k0 - K1) * ldb;
-#pragma unroll
-      for (int i = 0; i < NA; ++i) ra[i] = *reinterpret_cast<const float4*>(arow[i] + k0);
-#pragma unroll
-      for (int i = 0; i < NBQ; ++i) {
-        const float* bp = base + boff[i];
-        rb[i] = make_float4(bp[0], bp[ldb], bp[2 * ldb], bp[3 * ldb]);
-      }
-      return;
-    }
+  // A: rows (t/8) + 64 i, k quad t%8.  B: column t % 256, k quads t/256 + 2i
+  // (the quad index is uniform across a wave, so its source matrix is picked
+  // with a scalar select).  Loads are buffer loads whose bounds are offsets:
+  // out of range reads 0, a k-tile past the end is all zeros, and no branch
+  // splits the prefetch pipeline.
+  const int am = t >> 3, ak = 4 * (t & 7), bc = t % F_BN, bq0 = w / (F_BN / 64);
+  const int64_t mrows = min((int64_t)F_BM, M - bm);
+  const brsrc_t ra = make_brsrc(A + bm * lda, (uint32_t)(((mrows - 1) * lda + K) * 4));
+  const uint32_t bcoff = bn + bc < N ? (uint32_t)(bc * 4) : BUF_OOB;
+  struct Stage {
+    float4 a[NA], b[NBQ];
+  };
+  auto load = [&](Stage& r, int64_t k0) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      const int64_t m = bm + am + 64 * i;
-      ra[i] = (m < M && k0 + ak < kend) ? *reinterpret_cast<const float4*>(arow[i] + k0)
-                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int m = am + 64 * i;
+      const int64_t k = k0 + ak;
+      r.a[i] = bload_f4(ra, (m < mrows && k < kend) ? (uint32_t)((m * lda + k) * 4) : BUF_OOB);
     }
-    const int64_t n = bn + bc;
 #pragma unroll
     for (int i = 0; i < NBQ; ++i) {
-      const int64_t kq = k0 + 4 * (bq0 + BQS * i);
-      rb[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (kq < kend && n < N) {  // kend and K1 are multiples of 4: a quad is whole
-        const float* bp = (kq < K1 ? B1 + kq * ldb : B2 + (kq - K1) * ldb) + n;
-        rb[i] = make_float4(bp[0], bp[ldb], bp[2 * ldb], bp[3 * ldb]);
-      }
+      const int64_t kq = k0 + 4 * (bq0 + BQS * i);  // kend and K1 are multiples of 4
+      const bool s1 = kq < K1;
+      const brsrc_t rb = make_brsrc((s1 ? B1 + kq * ldb : B2 + (kq - K1) * ldb) + bn,
+                                    kq < kend ? (uint32_t)(4 * ldb * 4) : 0u);
+      float v[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        v[jj] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rb, (int)(bcoff + (uint32_t)(jj * ldb * 4)), 0, 0));
+      r.b[i] = make_float4(v[0], v[1], v[2], v[3]);
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](const Stage& r, int buf) {
 #pragma unroll
     for (int i = 0; i < NA; ++i)
-      *reinterpret_cast<float4*>(&As[buf][am + 64 * i][ak]) = ra[i];
+      *reinterpret_cast<float4*>(&As[buf][am + 64 * i][ak]) = r.a[i];
 #pragma unroll
     for (int i = 0; i < NBQ; ++i)
-      *reinterpret_cast<float4*>(&Bs[buf][bc][4 * (bq0 + BQS * i)]) = rb[i];
+      *reinterpret_cast<float4*>(&Bs[buf][bc][4 * (bq0 + BQS * i)]) = r.b[i];
   };
   floatx4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  int buf = 0;
-  if (kbeg < kend) {
-    load(kbeg);
-    stash(0);
-  }
-  __syncthreads();
-  for (int64_t k0 = kbeg; k0 < kend; k0 += F_BK) {
-    const bool more = k0 + F_BK < kend;
-    // operands of both 16-k halves first, then the next tile's global loads
+  auto compute = [&](int buf) {
+    // operands of both 16-k halves first
     float4 a[2][4], b[2][4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -147,7 +133,6 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
         a[kb][i] = *reinterpret_cast<const float4*>(&As[buf][wm + 16 * i + l16][16 * kb + 4 * c]);
         b[kb][i] = *reinterpret_cast<const float4*>(&Bs[buf][wn + 16 * i + l16][16 * kb + 4 * c]);
       }
-    if (more) load(k0 + F_BK);
     // one MFMA per accumulator per k step: 16 independent chains
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -156,11 +141,27 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = mfma16x16x4(f4at(a[kb][i], q), f4at(b[kb][j], q), acc[i][j]);
-    if (more) stash(buf ^ 1);
+          for (int jj = 0; jj < 4; ++jj)
+            acc[i][jj] = mfma16x16x4(f4at(a[kb][i], q), f4at(b[kb][jj], q), acc[i][jj]);
+  };
+
+  // Three k-tiles in flight: the LDS buffer in use and two register stages
+  // (an odd tile count ends with a tile of zeros).
+  Stage s0, s1;
+  load(s0, kbeg);
+  stash(s0, 0);
+  load(s0, kbeg + F_BK);
+  load(s1, kbeg + 2 * F_BK);
+  __syncthreads();
+  for (int64_t k0 = kbeg; k0 < kend; k0 += 2 * F_BK) {
+    compute(0);
+    stash(s0, 1);
     __syncthreads();
-    buf ^= 1;
+    load(s0, k0 + 3 * F_BK);
+    compute(1);
+    stash(s1, 0);
+    __syncthreads();
+    load(s1, k0 + 4 * F_BK);
   }
   store_tile<4, 4>(C, ldc, M, N, bm + wm, bn + wn, acc);
 }

@@ -53,7 +53,7 @@ __device__ __forceinline__ float f4at(const float4& v, int j) {
 constexpr int FQ_KT = 32;  // keys per tile, float32 dq kernel
 constexpr int DV_KT = 64;  // keys per workgroup, dv kernels
 
-template <int D, int HW>
+template <int D, int HW, bool PVEC>
 __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
     int64_t s_q, int64_t s_kv, int Hq, int grp, const float* __restrict__ dctx,
     const float* __restrict__ P, const float* __restrict__ K, const float* __restrict__ V,
@@ -62,9 +62,10 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
   constexpr int KT = FQ_KT, DK = D / 4, ND = D / 16, QW = 4 / HW, LDK = D + 4;
   constexpr int NE = KT * D / 4;           // float4 per staged tile
   constexpr int SE = (NE + 255) / 256;     // per thread
-  __shared__ float Vs[KT][LDK];
-  __shared__ float Ks[KT][LDK];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  __shared__ float Vs[2][KT][LDK];
+  __shared__ float Ks[2][KT][LDK];
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: h, q0 are too
   const int l16 = lane & 15, c = lane >> 4;
   // 1-D grid over (query tile, head block).  Under the causal mask the first
   // half of the grid takes the query tiles from the end (longest first) and
@@ -93,7 +94,6 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
   const int64_t q0 = qw0 + 16 * (w / HW);
   const int64_t qrow = q0 + l16;
   const bool qok = qrow < s_q;
-  const bool vec = (s_kv & 3) == 0;
 
   // B operand of dA^T = V dCtx^T: lane (query qrow, group c) holds head dims
   // DK*c .. DK*c + DK - 1 (MFMA step j of that group is d = DK*c + j).
@@ -129,42 +129,62 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
   const int64_t qlast = min(s_q, qw0 + 16 * QW) - 1;
   const int64_t kend = causal ? min(s_kv, off + qlast + 1) : s_kv;
   const int ntile = (int)cdiv64(kend, KT);
-  const float* prow = P + ((int64_t)h * s_q + (qok ? qrow : 0)) * s_kv;
-
-  float4 sv[SE], sk[SE], pc[2], pn[2];
-  auto fetch = [&](int64_t k0) {
+  // Buffer ranges (bounds are offsets, out of range reads 0): the wave's 16
+  // P rows, and one key tile of V and K.  Pipeline: the next tile's V/K
+  // loads go out at the top of a step and its P as soon as this tile's dS is
+  // formed (into the same registers), so both fly during the dQ products,
+  // the barrier and the next dA products; one barrier per tile.
+  const brsrc_t prs = make_brsrc(P + ((int64_t)h * s_q + q0) * s_kv, (uint32_t)(16 * s_kv * 4));
+  float4 sv[SE], sk[SE], pc[2];
+  auto fetch = [&](int64_t k0, bool valid) {
+    const brsrc_t vr = make_brsrc(V + k0 * ldk + g * D, (uint32_t)(KT * ldk * 4));
+    const brsrc_t kr = make_brsrc(K + k0 * ldk + g * D, (uint32_t)(KT * ldk * 4));
 #pragma unroll
     for (int i = 0; i < SE; ++i) {
       const int e = t + 256 * i;
-      const int64_t key = k0 + e / (D / 4);
-      const int d = 4 * (e % (D / 4));
-      sv[i] = sk[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e < NE && key < s_kv) {
-        sv[i] = *reinterpret_cast<const float4*>(V + key * ldk + g * D + d);
-        sk[i] = *reinterpret_cast<const float4*>(K + key * ldk + g * D + d);
+      const int kk = e / (D / 4), d = 4 * (e % (D / 4));
+      const uint32_t off = (valid && e < NE && k0 + kk < s_kv) ? (uint32_t)((kk * ldk + d) * 4) : BUF_OOB;
+      sv[i] = bload_f4(vr, off);
+      sk[i] = bload_f4(kr, off);
+    }
+  };
+  auto fetch_p = [&](int64_t k0) {
+    const bool ok = qok && k0 < kend;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int64_t col = k0 + 16 * nt + 4 * c;
+      const int64_t e = (int64_t)l16 * s_kv + col;
+      if (PVEC) {
+        pc[nt] = bload_f4(prs, (ok && col < s_kv) ? (uint32_t)(e * 4) : BUF_OOB);
+      } else {
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              prs, (ok && col + j < s_kv) ? (int)((e + j) * 4) : (int)BUF_OOB, 0, 0));
+        pc[nt] = make_float4(v[0], v[1], v[2], v[3]);
       }
     }
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-      pn[nt] = qok ? prow4(prow, k0 + 16 * nt + 4 * c, s_kv, vec) : make_float4(0.f, 0.f, 0.f, 0.f);
   };
-  if (ntile > 0) fetch(0);
-  for (int it = 0; it < ntile; ++it) {
-    __syncthreads();
+  auto stash = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < SE; ++i) {
       const int e = t + 256 * i;
       if (e < NE) {
         const int kr = e / (D / 4), d = 4 * (e % (D / 4));
-        *reinterpret_cast<float4*>(&Vs[kr][d]) = sv[i];
-        *reinterpret_cast<float4*>(&Ks[kr][d]) = sk[i];
+        *reinterpret_cast<float4*>(&Vs[buf][kr][d]) = sv[i];
+        *reinterpret_cast<float4*>(&Ks[buf][kr][d]) = sk[i];
       }
     }
-    pc[0] = pn[0];
-    pc[1] = pn[1];
-    __syncthreads();
-    if (it + 1 < ntile) fetch((int64_t)(it + 1) * KT);
-
+  };
+  fetch(0, ntile > 0);
+  stash(0);
+  fetch_p(0);
+  __syncthreads();
+  int buf = 0;
+  for (int it = 0; it < ntile; ++it) {
+    const int64_t k0 = (int64_t)it * KT;
+    fetch(k0 + KT, it + 1 < ntile);
     // dA^T for two 16-key sub-tiles: row = key 16 nt + 4c + v, col = query l16.
     // Four partial accumulators per sub-tile keep eight MFMA chains in flight.
     floatx4 da[2][4];
@@ -176,23 +196,33 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
     for (int s4 = 0; s4 < DK / 4; ++s4)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const float4 v4 = *reinterpret_cast<const float4*>(&Vs[16 * nt + l16][DK * c + 4 * s4]);
+        const float4 v4 = *reinterpret_cast<const float4*>(&Vs[buf][16 * nt + l16][DK * c + 4 * s4]);
         da[nt][0] = mfma16x16x4(v4.x, dc[4 * s4 + 0], da[nt][0]);
         da[nt][1] = mfma16x16x4(v4.y, dc[4 * s4 + 1], da[nt][1]);
         da[nt][2] = mfma16x16x4(v4.z, dc[4 * s4 + 2], da[nt][2]);
         da[nt][3] = mfma16x16x4(v4.w, dc[4 * s4 + 3], da[nt][3]);
       }
-    // dS^T = P^T o (dA^T - delta); then dQ += dS K with k index = key
+    // dS^T = P^T o (dA^T - delta)
+    float ds[2][4];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const float a = (da[nt][0][v] + da[nt][1][v]) + (da[nt][2][v] + da[nt][3][v]);
-        const float ds = f4at(pc[nt], v) * (a - dl);
+        ds[nt][v] = f4at(pc[nt], v) * (a - dl);
+      }
+    fetch_p(k0 + KT);
+    // dQ += dS K with k index = key
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int f = 0; f < ND; ++f)
-          acc[f] = mfma16x16x4(ds, Ks[16 * nt + 4 * c + v][16 * f + l16], acc[f]);
-      }
+          acc[f] = mfma16x16x4(ds[nt][v], Ks[buf][16 * nt + 4 * c + v][16 * f + l16], acc[f]);
+    stash(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
   }
 #pragma unroll
   for (int f = 0; f < ND; ++f)
@@ -1038,8 +1068,12 @@ static void launch_dq_f32(int64_t s_q, int64_t s_kv, int Hq, int grp, const floa
                           const float* delta, float* dq, float scale, int causal, hipStream_t s) {
   constexpr int QW = 4 / HW;
   const dim3 grid((unsigned)(cdiv64(s_q, 16 * QW) * (Hq / HW)));
-  attn_dq_f32_kernel<D, HW><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta,
-                                                 dq, scale, causal);
+  if (s_kv % 4 == 0)
+    attn_dq_f32_kernel<D, HW, true><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx,
+                                                         delta, dq, scale, causal);
+  else
+    attn_dq_f32_kernel<D, HW, false><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx,
+                                                          delta, dq, scale, causal);
 }
 
 template <int D>

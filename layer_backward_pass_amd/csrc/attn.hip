@@ -406,10 +406,9 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(int64_t rows, int64
 }
 
 __device__ __forceinline__ ushortx8 pack8(const float (&x)[8]) {
-  ushortx8 o;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) o[j] = f2bf(x[j]);
-  return o;
+  const uint4 u = make_uint4(pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3]), pk_bf16(x[4], x[5]),
+                             pk_bf16(x[6], x[7]));
+  return __builtin_bit_cast(ushortx8, u);
 }
 
 // Eight consecutive bf16 keys kc .. kc+7 of a P row at element offset

@@ -19,12 +19,17 @@ struct bf16 {
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// float32 -> bfloat16, round to nearest even; NaN stays NaN.
+// float32 -> bfloat16 by the hardware conversion (v_cvt_pk_bf16_f32): round
+// to nearest even; NaN stays NaN.
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// two floats rounded to bf16 and packed (a in the low half), one instruction
+typedef float lbp_float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 lbp_bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  const lbp_float2v f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, lbp_bf16x2v));
 }
 
 // Scalar and vector loads of an activation element (float or bf16) as float.

@@ -265,10 +265,10 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
       if constexpr (AW == 2) {
         const float4 x = __builtin_bit_cast(float4, r.a[i][0]);
         const float4 y = __builtin_bit_cast(float4, r.a[i][1]);
-        v = make_uint4((uint32_t)f2bf(x.x) | ((uint32_t)f2bf(x.y) << 16),
-                       (uint32_t)f2bf(x.z) | ((uint32_t)f2bf(x.w) << 16),
-                       (uint32_t)f2bf(y.x) | ((uint32_t)f2bf(y.y) << 16),
-                       (uint32_t)f2bf(y.z) | ((uint32_t)f2bf(y.w) << 16));
+        v = make_uint4(pk_bf16(x.x, x.y),
+                       pk_bf16(x.z, x.w),
+                       pk_bf16(y.x, y.y),
+                       pk_bf16(y.z, y.w));
       } else {
         v = r.a[i][0];
       }
@@ -411,10 +411,10 @@ __global__ __launch_bounds__(256) void cvt_a_bf16_kernel(int64_t M, int64_t K, c
     const float4 x = *reinterpret_cast<const float4*>(A + m * lda + k);
     const float4 y = *reinterpret_cast<const float4*>(A + m * lda + k + 4);
     *reinterpret_cast<uint4*>(out + m * K + k) =
-        make_uint4((uint32_t)f2bf(x.x) | ((uint32_t)f2bf(x.y) << 16),
-                   (uint32_t)f2bf(x.z) | ((uint32_t)f2bf(x.w) << 16),
-                   (uint32_t)f2bf(y.x) | ((uint32_t)f2bf(y.y) << 16),
-                   (uint32_t)f2bf(y.z) | ((uint32_t)f2bf(y.w) << 16));
+        make_uint4(pk_bf16(x.x, x.y),
+                   pk_bf16(x.z, x.w),
+                   pk_bf16(y.x, y.y),
+                   pk_bf16(y.z, y.w));
   }
 }
 

@@ -153,10 +153,10 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(int64_t rows, int64_t ffn,
     if (OUT_BF16) {
       uint16_t* o = (uint16_t*)dgu;
       uint2 a, b;
-      a.x = (uint32_t)f2bf(dg.x) | ((uint32_t)f2bf(dg.y) << 16);
-      a.y = (uint32_t)f2bf(dg.z) | ((uint32_t)f2bf(dg.w) << 16);
-      b.x = (uint32_t)f2bf(du.x) | ((uint32_t)f2bf(du.y) << 16);
-      b.y = (uint32_t)f2bf(du.z) | ((uint32_t)f2bf(du.w) << 16);
+      a.x = pk_bf16(dg.x, dg.y);
+      a.y = pk_bf16(dg.z, dg.w);
+      b.x = pk_bf16(du.x, du.y);
+      b.y = pk_bf16(du.z, du.w);
       *reinterpret_cast<uint2*>(o + og) = a;
       *reinterpret_cast<uint2*>(o + ou) = b;
     } else {
@@ -203,10 +203,10 @@ __global__ __launch_bounds__(256) void to_bf16_kernel(int64_t n, const float* __
     const float4 a = *reinterpret_cast<const float4*>(src + i);
     const float4 b = *reinterpret_cast<const float4*>(src + i + 4);
     uint4 o;
-    o.x = (uint32_t)f2bf(a.x) | ((uint32_t)f2bf(a.y) << 16);
-    o.y = (uint32_t)f2bf(a.z) | ((uint32_t)f2bf(a.w) << 16);
-    o.z = (uint32_t)f2bf(b.x) | ((uint32_t)f2bf(b.y) << 16);
-    o.w = (uint32_t)f2bf(b.z) | ((uint32_t)f2bf(b.w) << 16);
+    o.x = pk_bf16(a.x, a.y);
+    o.y = pk_bf16(a.z, a.w);
+    o.z = pk_bf16(b.x, b.y);
+    o.w = pk_bf16(b.z, b.w);
     *reinterpret_cast<uint4*>(dst + i) = o;
   }
 }

@@ -272,25 +272,34 @@ __global__ __launch_bounds__(256) void attn_dv_f32_kernel(int64_t s_q, int64_t s
   for (int f = 0; f < ND; ++f) acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
   const int64_t nqb = cdiv64(qz - qa, QT);
   const int64_t nit = nqb * grp;
+  // One step = 32 query rows of one head: its dCtx rows go to LDS, the P
+  // values of this lane's key straight into registers.  Two register stages
+  // used in turn; every load is a branch-free buffer load (a step past the
+  // end reads zeros), so the pipeline never drains on a branch.
   struct Stage {
     float4 d[SE];
     float p[QT / 4];
   };
   auto fetch = [&](Stage& r, int64_t it) {
-    const int h = g * grp + (int)(it / nqb);
-    const int64_t qb = qa + QT * (it % nqb);
+    const bool valid = it < nit;
+    const int64_t itc = valid ? it : 0;
+    const int h = g * grp + (int)(itc / nqb);
+    const int64_t qb = qa + QT * (itc % nqb);
+    const brsrc_t rd = make_brsrc(dctx + qb * ldq + h * D, (uint32_t)(QT * ldq * 4));
 #pragma unroll
     for (int i = 0; i < SE; ++i) {
       const int e = t + 256 * i;
-      const int64_t row = qb + e / (D / 4);
-      r.d[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e < NE && row < qz)
-        r.d[i] = *reinterpret_cast<const float4*>(dctx + row * ldq + h * D + 4 * (e % (D / 4)));
+      const int rr = e / (D / 4);
+      const bool ok = valid && e < NE && qb + rr < qz;
+      r.d[i] = bload_f4(rd, ok ? (uint32_t)((rr * ldq + 4 * (e % (D / 4))) * 4) : BUF_OOB);
     }
+    const brsrc_t rp = make_brsrc(P + ((int64_t)h * s_q + qb) * s_kv + k0, (uint32_t)(QT * s_kv * 4));
 #pragma unroll
-    for (int s = 0; s < QT / 4; ++s) {
-      const int64_t row = qb + 4 * s + c;
-      r.p[s] = (kok && row < qz) ? P[((int64_t)h * s_q + row) * s_kv + key] : 0.f;
+    for (int s2 = 0; s2 < QT / 4; ++s2) {
+      const int rr = 4 * s2 + c;
+      const bool ok = valid && kok && qb + rr < qz;
+      r.p[s2] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rp, ok ? (int)((rr * s_kv + 16 * w + l16) * 4) : (int)BUF_OOB, 0, 0));
     }
   };
   auto stash = [&](const Stage& r, int buf) {
@@ -300,23 +309,27 @@ __global__ __launch_bounds__(256) void attn_dv_f32_kernel(int64_t s_q, int64_t s
       if (e < NE) *reinterpret_cast<float4*>(&dCs[buf][e / (D / 4)][4 * (e % (D / 4))]) = r.d[i];
     }
   };
-  Stage cur, nxt;
-  fetch(cur, 0);
-  stash(cur, 0);
-  __syncthreads();
-  int buf = 0;
-  for (int64_t it = 0; it < nit; ++it) {
-    const bool more = it + 1 < nit;
-    if (more) fetch(nxt, it + 1);
+  auto compute = [&](const Stage& r, int buf) {
 #pragma unroll
-    for (int s = 0; s < QT / 4; ++s)
+    for (int s2 = 0; s2 < QT / 4; ++s2)
 #pragma unroll
       for (int f = 0; f < ND; ++f)
-        acc[f] = mfma16x16x4(cur.p[s], dCs[buf][4 * s + c][16 * f + l16], acc[f]);
-    if (more) stash(nxt, buf ^ 1);
+        acc[f] = mfma16x16x4(r.p[s2], dCs[buf][4 * s2 + c][16 * f + l16], acc[f]);
+  };
+  Stage s0, s1;
+  fetch(s0, 0);
+  stash(s0, 0);
+  fetch(s1, 1);
+  __syncthreads();
+  for (int64_t it = 0; it < nit; it += 2) {
+    compute(s0, 0);
+    stash(s1, 1);
     __syncthreads();
-    buf ^= 1;
-    cur = nxt;
+    fetch(s0, it + 2);
+    compute(s1, 1);
+    stash(s0, 0);
+    __syncthreads();
+    fetch(s1, it + 3);
   }
 #pragma unroll
   for (int f = 0; f < ND; ++f)

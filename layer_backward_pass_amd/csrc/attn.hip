@@ -356,13 +356,25 @@ __global__ __launch_bounds__(256) void attn_dv_reduce_kernel(int64_t s_q, int64_
   int64_t qbeg = causal ? k0 - off : 0;
   qbeg = qbeg < 0 ? 0 : qbeg / qgran * qgran;
   const int64_t nch = qbeg < s_q ? cdiv64(s_q - qbeg, qc) : 0;
+  // up to 8 chunk partials in flight, added in chunk order (an index past
+  // the last chunk re-reads chunk 0 and its term is dropped)
+  const int n = (int)(nch < cmax ? nch : cmax);
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int64_t ch = 0; ch < nch && ch < cmax; ++ch) {
-    const float4 v = reinterpret_cast<const float4*>(part + ch * s_kv * ldk)[e];
-    s.x += v.x;
-    s.y += v.y;
-    s.z += v.z;
-    s.w += v.w;
+  for (int c0 = 0; c0 < n; c0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int ch = c0 + u < n ? c0 + u : 0;
+      v[u] = reinterpret_cast<const float4*>(part + (int64_t)ch * s_kv * ldk)[e];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool take = c0 + u < n;
+      s.x += take ? v[u].x : 0.f;
+      s.y += take ? v[u].y : 0.f;
+      s.z += take ? v[u].z : 0.f;
+      s.w += take ? v[u].w : 0.f;
+    }
   }
   reinterpret_cast<float4*>(dv)[e] = s;
 }

@@ -337,13 +337,25 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(int64_t M, int64_t N
        t += (int64_t)gridDim.x * blockDim.x) {
     const int64_t m = t / q, n = (t - m * q) * 4;
     const float* p = P + m * N + n;
-    float4 s = *reinterpret_cast<const float4*>(p);
-    for (int i = 1; i < splits; ++i) {
-      const float4 v = *reinterpret_cast<const float4*>(p + i * stride);
-      s.x += v.x;
-      s.y += v.y;
-      s.z += v.z;
-      s.w += v.w;
+    // the partials of up to 8 splits in flight at a time, added in split order
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i0 = 0; i0 < splits; i0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        // a split index past the end re-reads the last split (a valid
+        // address, no branch) and its term is dropped below
+        const int i = i0 + u < splits ? i0 + u : splits - 1;
+        v[u] = *reinterpret_cast<const float4*>(p + i * stride);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool take = i0 + u < splits;
+        s.x += take ? v[u].x : 0.f;
+        s.y += take ? v[u].y : 0.f;
+        s.z += take ? v[u].z : 0.f;
+        s.w += take ? v[u].w : 0.f;
+      }
     }
     *reinterpret_cast<float4*>(C + m * ldc + n) = s;
   }

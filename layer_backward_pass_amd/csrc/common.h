@@ -57,6 +57,10 @@ template <> struct Act<bf16> {
 // per-lane (VGPR) offset carries bounds here; resources stay below 1 GiB so
 // a valid offset plus BUF_OOB never wraps into range.
 typedef __amdgpu_buffer_rsrc_t brsrc_t;
+// cache policy of a load that streams data read once (the nt bit): weight
+// rows of a GEMV are not worth keeping in L2 (decode [W_gate;W_up]:
+// 25.5 -> 23.6 us)
+constexpr int BUF_NT = 2;
 constexpr uint32_t BUF_OOB = 0x80000000u;
 constexpr uint32_t BUF_MAX_BYTES = 0x40000000u;
 __device__ __forceinline__ brsrc_t make_brsrc(const void* base, uint32_t bytes) {
@@ -64,13 +68,15 @@ __device__ __forceinline__ brsrc_t make_brsrc(const void* base, uint32_t bytes) 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
+template <int AUX = 0>
 __device__ __forceinline__ float4 bload_f4(brsrc_t r, uint32_t off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
   return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
                      __uint_as_float(v[3]));
 }
+template <int AUX = 0>
 __device__ __forceinline__ uint2 bload_u2(brsrc_t r, uint32_t off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, AUX);
   return make_uint2(v[0], v[1]);
 }
 __device__ __forceinline__ float2 bload_f2(brsrc_t r, uint32_t off) {
@@ -91,12 +97,14 @@ template <typename T> struct BufVec;
 template <> struct BufVec<float> {
   typedef float4 raw;
   static __device__ __forceinline__ raw load(brsrc_t r, uint32_t off) { return bload_f4(r, off); }
+  static __device__ __forceinline__ raw load_stream(brsrc_t r, uint32_t off) { return bload_f4<BUF_NT>(r, off); }
   static __device__ __forceinline__ float4 cvt(raw v) { return v; }
   static __device__ __forceinline__ raw zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
 };
 template <> struct BufVec<bf16> {
   typedef uint2 raw;
   static __device__ __forceinline__ raw load(brsrc_t r, uint32_t off) { return bload_u2(r, off); }
+  static __device__ __forceinline__ raw load_stream(brsrc_t r, uint32_t off) { return bload_u2<BUF_NT>(r, off); }
   static __device__ __forceinline__ float4 cvt(raw v) { return bf4_to_f4(v); }
   static __device__ __forceinline__ raw zero() { return make_uint2(0u, 0u); }
 };

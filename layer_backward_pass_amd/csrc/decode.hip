@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256) void dgemv_kernel(GemvArgs a) {
       const int ii = i + u;
       const bool in1 = ii < n1;
       const uint32_t roff = ii < i1 ? (uint32_t)(in1 ? ii : ii - n1) * rowb : BUF_OOB;
-      wv[u] = WB::load(in1 ? rs1 : rs2, coff + roff);
+      wv[u] = WB::load_stream(in1 ? rs1 : rs2, coff + roff);
     }
   };
   auto consume = [&](const WV (&wv)[DG_U], int i, float4& acc) {

@@ -53,12 +53,12 @@ __device__ __forceinline__ float f4at(const float4& v, int j) {
 constexpr int FQ_KT = 32;  // keys per tile, float32 dq kernel
 constexpr int DV_KT = 64;  // keys per workgroup, dv kernels
 
-template <int D, int HW, bool PVEC>
+template <int D, int HW, bool PVEC, bool KSPLIT>
 __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
     int64_t s_q, int64_t s_kv, int Hq, int grp, const float* __restrict__ dctx,
     const float* __restrict__ P, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ ctx, const float* __restrict__ delta_ws, float* __restrict__ dq,
-    float scale, int causal) {
+    float* __restrict__ dq2, float scale, int causal) {
   constexpr int KT = FQ_KT, DK = D / 4, ND = D / 16, QW = 4 / HW, LDK = D + 4;
   constexpr int NE = KT * D / 4;           // float4 per staged tile
   constexpr int SE = (NE + 255) / 256;     // per thread
@@ -67,15 +67,24 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: h, q0 are too
   const int l16 = lane & 15, c = lane >> 4;
-  // 1-D grid over (query tile, head block).  Under the causal mask the first
-  // half of the grid takes the query tiles from the end (longest first) and
-  // the second half the complementary ones from the start, so the two
-  // workgroups that share a CU add up to about the same work.
+  // 1-D grid over (query tile, head block).  Causal, without KSPLIT: the
+  // first half of the grid takes the query tiles from the end (longest
+  // first) and the second half the complementary ones, so the two
+  // workgroups that share a CU add up to about the same work.  KSPLIT (causal
+  // only): item L = (pair, head block, half); the workgroup takes query tiles
+  // p and nqt-1-p of the pair but only half of each one's key tiles, so every
+  // workgroup has the same work; half 0 writes dq, half 1 the partial dq2
+  // (the caller adds the two).
   const int nhb = Hq / HW;
   const int64_t nqt = cdiv64(s_q, 16 * QW);
   const int64_t L = blockIdx.x;
   int64_t qt, hb;
-  if (causal) {
+  int half = 0;
+  if (KSPLIT) {
+    half = (int)(L & 1);
+    hb = (L >> 1) % nhb;
+    qt = (L >> 1) / nhb;  // the pair index; the second tile is nqt-1-qt
+  } else if (causal) {
     const int64_t H = (int64_t)nhb * ((nqt + 1) / 2);
     if (L < H) {
       qt = nqt - 1 - L / nhb;
@@ -90,147 +99,162 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
   }
   const int h = (int)hb * HW + (w % HW), g = h / grp;
   const int64_t ldq = (int64_t)Hq * D, ldk = (int64_t)(Hq / grp) * D;
-  const int64_t qw0 = qt * (16 * QW);
-  const int64_t q0 = qw0 + 16 * (w / HW);
-  const int64_t qrow = q0 + l16;
-  const bool qok = qrow < s_q;
-
-  // B operand of dA^T = V dCtx^T: lane (query qrow, group c) holds head dims
-  // DK*c .. DK*c + DK - 1 (MFMA step j of that group is d = DK*c + j).
-  float dc[DK];
-#pragma unroll
-  for (int i = 0; i < DK; i += 4) {
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (qok) v = *reinterpret_cast<const float4*>(dctx + qrow * ldq + h * D + DK * c + i);
-    dc[i] = v.x;
-    dc[i + 1] = v.y;
-    dc[i + 2] = v.z;
-    dc[i + 3] = v.w;
-  }
-  float dl = 0.f;
-  if (ctx != nullptr) {
-#pragma unroll
+  auto segment = [&](int64_t qtile, int hpart, float* __restrict__ out) {
+  const int64_t qw0 = qtile * (16 * QW);
+    const int64_t q0 = qw0 + 16 * (w / HW);
+    const int64_t qrow = q0 + l16;
+    const bool qok = qrow < s_q;
+  
+    // B operand of dA^T = V dCtx^T: lane (query qrow, group c) holds head dims
+    // DK*c .. DK*c + DK - 1 (MFMA step j of that group is d = DK*c + j).
+    float dc[DK];
+  #pragma unroll
     for (int i = 0; i < DK; i += 4) {
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (qok) x = *reinterpret_cast<const float4*>(ctx + qrow * ldq + h * D + DK * c + i);
-      dl += dc[i] * x.x + dc[i + 1] * x.y + dc[i + 2] * x.z + dc[i + 3] * x.w;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (qok) v = *reinterpret_cast<const float4*>(dctx + qrow * ldq + h * D + DK * c + i);
+      dc[i] = v.x;
+      dc[i + 1] = v.y;
+      dc[i + 2] = v.z;
+      dc[i + 3] = v.w;
     }
-    dl += __shfl_xor(dl, 16, 64);
-    dl += __shfl_xor(dl, 32, 64);
-  } else if (qok) {
-    dl = delta_ws[(int64_t)h * s_q + qrow];
-  }
-
-  floatx4 acc[ND];
-#pragma unroll
-  for (int f = 0; f < ND; ++f) acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  const int64_t off = s_kv - s_q;
-  const int64_t qlast = min(s_q, qw0 + 16 * QW) - 1;
-  const int64_t kend = causal ? min(s_kv, off + qlast + 1) : s_kv;
-  const int ntile = (int)cdiv64(kend, KT);
-  // Buffer ranges (bounds are offsets, out of range reads 0): the wave's 16
-  // P rows, and one key tile of V and K.  Pipeline: the next tile's V/K
-  // loads go out at the top of a step and its P as soon as this tile's dS is
-  // formed (into the same registers), so both fly during the dQ products,
-  // the barrier and the next dA products; one barrier per tile.
-  const brsrc_t prs = make_brsrc(P + ((int64_t)h * s_q + q0) * s_kv, (uint32_t)(16 * s_kv * 4));
-  float4 sv[SE], sk[SE], pc[2];
-  auto fetch = [&](int64_t k0, bool valid) {
-    const brsrc_t vr = make_brsrc(V + k0 * ldk + g * D, (uint32_t)(KT * ldk * 4));
-    const brsrc_t kr = make_brsrc(K + k0 * ldk + g * D, (uint32_t)(KT * ldk * 4));
-#pragma unroll
-    for (int i = 0; i < SE; ++i) {
-      const int e = t + 256 * i;
-      const int kk = e / (D / 4), d = 4 * (e % (D / 4));
-      const uint32_t off = (valid && e < NE && k0 + kk < s_kv) ? (uint32_t)((kk * ldk + d) * 4) : BUF_OOB;
-      sv[i] = bload_f4(vr, off);
-      sk[i] = bload_f4(kr, off);
-    }
-  };
-  auto fetch_p = [&](int64_t k0) {
-    const bool ok = qok && k0 < kend;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int64_t col = k0 + 16 * nt + 4 * c;
-      const int64_t e = (int64_t)l16 * s_kv + col;
-      if (PVEC) {
-        pc[nt] = bload_f4(prs, (ok && col < s_kv) ? (uint32_t)(e * 4) : BUF_OOB);
-      } else {
-        float v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-              prs, (ok && col + j < s_kv) ? (int)((e + j) * 4) : (int)BUF_OOB, 0, 0));
-        pc[nt] = make_float4(v[0], v[1], v[2], v[3]);
+    float dl = 0.f;
+    if (ctx != nullptr) {
+  #pragma unroll
+      for (int i = 0; i < DK; i += 4) {
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (qok) x = *reinterpret_cast<const float4*>(ctx + qrow * ldq + h * D + DK * c + i);
+        dl += dc[i] * x.x + dc[i + 1] * x.y + dc[i + 2] * x.z + dc[i + 3] * x.w;
       }
+      dl += __shfl_xor(dl, 16, 64);
+      dl += __shfl_xor(dl, 32, 64);
+    } else if (qok) {
+      dl = delta_ws[(int64_t)h * s_q + qrow];
     }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < SE; ++i) {
-      const int e = t + 256 * i;
-      if (e < NE) {
-        const int kr = e / (D / 4), d = 4 * (e % (D / 4));
-        *reinterpret_cast<float4*>(&Vs[buf][kr][d]) = sv[i];
-        *reinterpret_cast<float4*>(&Ks[buf][kr][d]) = sk[i];
+  
+    floatx4 acc[ND];
+  #pragma unroll
+    for (int f = 0; f < ND; ++f) acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
+  
+    const int64_t off = s_kv - s_q;
+    const int64_t qlast = min(s_q, qw0 + 16 * QW) - 1;
+    const int64_t kend = causal ? min(s_kv, off + qlast + 1) : s_kv;
+    const int ntile_all = (int)cdiv64(kend, KT);
+    const int mid = (ntile_all + 1) / 2;
+    const int kt0 = !KSPLIT ? 0 : (hpart == 0 ? 0 : mid);
+    const int ntile = !KSPLIT ? ntile_all : (hpart == 0 ? mid : ntile_all);
+    // Buffer ranges (bounds are offsets, out of range reads 0): the wave's 16
+    // P rows, and one key tile of V and K.  Pipeline: the next tile's V/K
+    // loads go out at the top of a step and its P as soon as this tile's dS is
+    // formed (into the same registers), so both fly during the dQ products,
+    // the barrier and the next dA products; one barrier per tile.
+    const brsrc_t prs = make_brsrc(P + ((int64_t)h * s_q + q0) * s_kv, (uint32_t)(16 * s_kv * 4));
+    float4 sv[SE], sk[SE], pc[2];
+    auto fetch = [&](int64_t k0, bool valid) {
+      const brsrc_t vr = make_brsrc(V + k0 * ldk + g * D, (uint32_t)(KT * ldk * 4));
+      const brsrc_t kr = make_brsrc(K + k0 * ldk + g * D, (uint32_t)(KT * ldk * 4));
+  #pragma unroll
+      for (int i = 0; i < SE; ++i) {
+        const int e = t + 256 * i;
+        const int kk = e / (D / 4), d = 4 * (e % (D / 4));
+        const uint32_t off = (valid && e < NE && k0 + kk < s_kv) ? (uint32_t)((kk * ldk + d) * 4) : BUF_OOB;
+        sv[i] = bload_f4(vr, off);
+        sk[i] = bload_f4(kr, off);
       }
-    }
-  };
-  fetch(0, ntile > 0);
-  stash(0);
-  fetch_p(0);
-  __syncthreads();
-  int buf = 0;
-  for (int it = 0; it < ntile; ++it) {
-    const int64_t k0 = (int64_t)it * KT;
-    fetch(k0 + KT, it + 1 < ntile);
-    // dA^T for two 16-key sub-tiles: row = key 16 nt + 4c + v, col = query l16.
-    // Four partial accumulators per sub-tile keep eight MFMA chains in flight.
-    floatx4 da[2][4];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) da[nt][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s4 = 0; s4 < DK / 4; ++s4)
-#pragma unroll
+    };
+    auto fetch_p = [&](int64_t k0) {
+      const bool ok = qok && k0 < kend;
+  #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const float4 v4 = *reinterpret_cast<const float4*>(&Vs[buf][16 * nt + l16][DK * c + 4 * s4]);
-        da[nt][0] = mfma16x16x4(v4.x, dc[4 * s4 + 0], da[nt][0]);
-        da[nt][1] = mfma16x16x4(v4.y, dc[4 * s4 + 1], da[nt][1]);
-        da[nt][2] = mfma16x16x4(v4.z, dc[4 * s4 + 2], da[nt][2]);
-        da[nt][3] = mfma16x16x4(v4.w, dc[4 * s4 + 3], da[nt][3]);
+        const int64_t col = k0 + 16 * nt + 4 * c;
+        const int64_t e = (int64_t)l16 * s_kv + col;
+        if (PVEC) {
+          pc[nt] = bload_f4(prs, (ok && col < s_kv) ? (uint32_t)(e * 4) : BUF_OOB);
+        } else {
+          float v[4];
+  #pragma unroll
+          for (int j = 0; j < 4; ++j)
+            v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                prs, (ok && col + j < s_kv) ? (int)((e + j) * 4) : (int)BUF_OOB, 0, 0));
+          pc[nt] = make_float4(v[0], v[1], v[2], v[3]);
+        }
       }
-    // dS^T = P^T o (dA^T - delta)
-    float ds[2][4];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float a = (da[nt][0][v] + da[nt][1][v]) + (da[nt][2][v] + da[nt][3][v]);
-        ds[nt][v] = f4at(pc[nt], v) * (a - dl);
+    };
+    auto stash = [&](int buf) {
+  #pragma unroll
+      for (int i = 0; i < SE; ++i) {
+        const int e = t + 256 * i;
+        if (e < NE) {
+          const int kr = e / (D / 4), d = 4 * (e % (D / 4));
+          *reinterpret_cast<float4*>(&Vs[buf][kr][d]) = sv[i];
+          *reinterpret_cast<float4*>(&Ks[buf][kr][d]) = sk[i];
+        }
       }
-    fetch_p(k0 + KT);
-    // dQ += dS K with k index = key
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int f = 0; f < ND; ++f)
-          acc[f] = mfma16x16x4(ds[nt][v], Ks[buf][16 * nt + 4 * c + v][16 * f + l16], acc[f]);
-    stash(buf ^ 1);
+    };
+    fetch((int64_t)kt0 * KT, ntile > kt0);
+    stash(0);
+    fetch_p((int64_t)kt0 * KT);
     __syncthreads();
-    buf ^= 1;
-  }
-#pragma unroll
-  for (int f = 0; f < ND; ++f)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t row = q0 + 4 * c + v;
-      if (row < s_q) dq[row * ldq + h * D + 16 * f + l16] = scale * acc[f][v];
+    int buf = 0;
+    for (int it = kt0; it < ntile; ++it) {
+      const int64_t k0 = (int64_t)it * KT;
+      fetch(k0 + KT, it + 1 < ntile);
+      // dA^T for two 16-key sub-tiles: row = key 16 nt + 4c + v, col = query l16.
+      // Four partial accumulators per sub-tile keep eight MFMA chains in flight.
+      floatx4 da[2][4];
+  #pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) da[nt][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int s4 = 0; s4 < DK / 4; ++s4)
+  #pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const float4 v4 = *reinterpret_cast<const float4*>(&Vs[buf][16 * nt + l16][DK * c + 4 * s4]);
+          da[nt][0] = mfma16x16x4(v4.x, dc[4 * s4 + 0], da[nt][0]);
+          da[nt][1] = mfma16x16x4(v4.y, dc[4 * s4 + 1], da[nt][1]);
+          da[nt][2] = mfma16x16x4(v4.z, dc[4 * s4 + 2], da[nt][2]);
+          da[nt][3] = mfma16x16x4(v4.w, dc[4 * s4 + 3], da[nt][3]);
+        }
+      // dS^T = P^T o (dA^T - delta)
+      float ds[2][4];
+  #pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+  #pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float a = (da[nt][0][v] + da[nt][1][v]) + (da[nt][2][v] + da[nt][3][v]);
+          ds[nt][v] = f4at(pc[nt], v) * (a - dl);
+        }
+      fetch_p(k0 + KT);
+      // dQ += dS K with k index = key
+  #pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+  #pragma unroll
+        for (int v = 0; v < 4; ++v)
+  #pragma unroll
+          for (int f = 0; f < ND; ++f)
+            acc[f] = mfma16x16x4(ds[nt][v], Ks[buf][16 * nt + 4 * c + v][16 * f + l16], acc[f]);
+      stash(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
     }
+  #pragma unroll
+    for (int f = 0; f < ND; ++f)
+  #pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t row = q0 + 4 * c + v;
+        if (row < s_q) out[row * ldq + h * D + 16 * f + l16] = scale * acc[f][v];
+      }
+  };
+  if (KSPLIT) {
+    float* out = half == 0 ? dq : dq2;
+    segment(qt, half, out);
+    if (nqt - 1 - qt != qt) {
+      __syncthreads();
+      segment(nqt - 1 - qt, half, out);
+    }
+  } else {
+    segment(qt, 0, dq);
+  }
 }
 
 // dV for 64 keys of KV group blockIdx.y over query chunk (blockIdx.x % cmax)
@@ -1051,7 +1075,7 @@ static bool bf16_mfma_path(int dt, int64_t D) { return dt == BF16 && D >= 32; }
 //   delta [Hq, s_q] f32 (callers without ctx) | dv chunk partials f32 |
 //   bf16 MFMA path: Kt [Hkv, D, LK] bf16 | dCt [Hq, D, LQ] bf16
 struct AttnWs {
-  size_t delta, part, kt, dct, end;
+  size_t delta, part, kt, dct, dq2, end;
   int64_t LK, LQ;
 };
 static size_t al256(size_t b) { return (b + 255) / 256 * 256; }
@@ -1066,7 +1090,9 @@ static AttnWs attn_ws(int64_t s_q, int64_t s_kv, int64_t Hq, int64_t Hkv, int64_
   const size_t pb = dp.cmax > 1 ? (size_t)dp.cmax * s_kv * Hkv * D * 4 : 0;
   w.kt = w.part + al256(pb);
   w.dct = w.kt + (hb ? al256((size_t)Hkv * D * w.LK * 2) : 0);
-  w.end = w.dct + (hb ? al256((size_t)Hq * D * w.LQ * 2) : 0);
+  w.dq2 = w.dct + (hb ? al256((size_t)Hq * D * w.LQ * 2) : 0);
+  // fp32 path: the second key half's dq partial (causal key split)
+  w.end = w.dq2 + (hb ? 0 : al256((size_t)s_q * Hq * D * 4));
   return w;
 }
 
@@ -1089,15 +1115,36 @@ static double attn_pairs(int64_t s_q, int64_t s_kv, int causal) {
 template <int D, int HW>
 static void launch_dq_f32(int64_t s_q, int64_t s_kv, int Hq, int grp, const float* dctx,
                           const float* P, const float* K, const float* V, const float* ctx,
-                          const float* delta, float* dq, float scale, int causal, hipStream_t s) {
+                          const float* delta, float* dq, float* dq2, bool ksplit, float scale,
+                          int causal, hipStream_t s) {
   constexpr int QW = 4 / HW;
-  const dim3 grid((unsigned)(cdiv64(s_q, 16 * QW) * (Hq / HW)));
-  if (s_kv % 4 == 0)
-    attn_dq_f32_kernel<D, HW, true><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx,
-                                                         delta, dq, scale, causal);
-  else
-    attn_dq_f32_kernel<D, HW, false><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx,
-                                                          delta, dq, scale, causal);
+  const int64_t nqt = cdiv64(s_q, 16 * QW);
+  const dim3 grid((unsigned)((ksplit ? 2 * ((nqt + 1) / 2) : nqt) * (Hq / HW)));
+#define LBP_DQ32(PV, KS)                                                                       \
+  attn_dq_f32_kernel<D, HW, PV, KS><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, \
+                                                         delta, dq, dq2, scale, causal)
+  if (s_kv % 4 == 0) {
+    if (ksplit) LBP_DQ32(true, true);
+    else LBP_DQ32(true, false);
+  } else {
+    if (ksplit) LBP_DQ32(false, true);
+    else LBP_DQ32(false, false);
+  }
+#undef LBP_DQ32
+}
+
+// dst += src, float4 per thread (n4 float4)
+__global__ __launch_bounds__(256) void add_inplace_kernel(int64_t n4, float* __restrict__ dst,
+                                                          const float* __restrict__ src) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    float4 a = reinterpret_cast<float4*>(dst)[i];
+    const float4 b = reinterpret_cast<const float4*>(src)[i];
+    a.x += b.x;
+    a.y += b.y;
+    a.z += b.z;
+    a.w += b.w;
+    reinterpret_cast<float4*>(dst)[i] = a;
+  }
 }
 
 template <int D>
@@ -1119,14 +1166,27 @@ static hipError_t attn_launch_f32(int64_t s_q, int64_t s_kv, int Hq, int Hkv, co
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int hw = grp % 4 == 0 ? 4 : (grp % 2 == 0 ? 2 : 1);
+  // causal: split each query tile pair's key range in two halves (equal
+  // work per workgroup); the second half's partial is added afterwards
+  const bool ksplit = causal && cdiv64(s_q, 16 * (4 / hw)) >= 2;
+  float* dq2 = (float*)((char*)ws + wl.dq2);
   if (hw == 4)
-    launch_dq_f32<D, 4>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta, dq, scale, causal, s);
+    launch_dq_f32<D, 4>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta, dq, dq2, ksplit, scale, causal, s);
   else if (hw == 2)
-    launch_dq_f32<D, 2>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta, dq, scale, causal, s);
+    launch_dq_f32<D, 2>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta, dq, dq2, ksplit, scale, causal, s);
   else
-    launch_dq_f32<D, 1>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta, dq, scale, causal, s);
+    launch_dq_f32<D, 1>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta, dq, dq2, ksplit, scale, causal, s);
   mark("attn_dq_f32", pbytes + qbytes * (ctx ? 3 : 2) + 2 * kvbytes, 4.0 * D * pairs * Hq, s);
-  if ((e = hipGetLastError()) != hipSuccess || dv == nullptr) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ksplit) {
+    const int64_t n4 = s_q * Hq * D / 4;
+    int64_t blocks = cdiv64(n4, 256);
+    if (blocks > 4096) blocks = 4096;
+    add_inplace_kernel<<<dim3((unsigned)blocks), 256, 0, s>>>(n4, dq, dq2);
+    mark("attn_dq_add", qbytes * 3, 0, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (dv == nullptr) return hipSuccess;
   const DvPlan dp = dv_plan(s_q, s_kv, Hkv);
   float* part = dp.cmax > 1 ? (float*)((char*)ws + wl.part) : dv;
   const dim3 grid((unsigned)(cdiv64(s_kv, DV_KT) * dp.cmax), (unsigned)Hkv);

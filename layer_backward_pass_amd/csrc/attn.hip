@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
     // B operand of dA^T = V dCtx^T: lane (query qrow, group c) holds head dims
     // DK*c .. DK*c + DK - 1 (MFMA step j of that group is d = DK*c + j).
     float dc[DK];
-  #pragma unroll
+#pragma unroll
     for (int i = 0; i < DK; i += 4) {
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (qok) v = *reinterpret_cast<const float4*>(dctx + qrow * ldq + h * D + DK * c + i);
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
     }
     float dl = 0.f;
     if (ctx != nullptr) {
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < DK; i += 4) {
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
         if (qok) x = *reinterpret_cast<const float4*>(ctx + qrow * ldq + h * D + DK * c + i);
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
     }
   
     floatx4 acc[ND];
-  #pragma unroll
+#pragma unroll
     for (int f = 0; f < ND; ++f) acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
   
     const int64_t off = s_kv - s_q;
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
     auto fetch = [&](int64_t k0, bool valid) {
       const brsrc_t vr = make_brsrc(V + k0 * ldk + g * D, (uint32_t)(KT * ldk * 4));
       const brsrc_t kr = make_brsrc(K + k0 * ldk + g * D, (uint32_t)(KT * ldk * 4));
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < SE; ++i) {
         const int e = t + 256 * i;
         const int kk = e / (D / 4), d = 4 * (e % (D / 4));
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
     };
     auto fetch_p = [&](int64_t k0) {
       const bool ok = qok && k0 < kend;
-  #pragma unroll
+#pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int64_t col = k0 + 16 * nt + 4 * c;
         const int64_t e = (int64_t)l16 * s_kv + col;
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
           pc[nt] = bload_f4(prs, (ok && col < s_kv) ? (uint32_t)(e * 4) : BUF_OOB);
         } else {
           float v[4];
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 4; ++j)
             v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
                 prs, (ok && col + j < s_kv) ? (int)((e + j) * 4) : (int)BUF_OOB, 0, 0));
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
       }
     };
     auto stash = [&](int buf) {
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < SE; ++i) {
         const int e = t + 256 * i;
         if (e < NE) {
@@ -201,13 +201,13 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
       // dA^T for two 16-key sub-tiles: row = key 16 nt + 4c + v, col = query l16.
       // Four partial accumulators per sub-tile keep eight MFMA chains in flight.
       floatx4 da[2][4];
-  #pragma unroll
+#pragma unroll
       for (int nt = 0; nt < 2; ++nt)
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < 4; ++j) da[nt][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
+#pragma unroll
       for (int s4 = 0; s4 < DK / 4; ++s4)
-  #pragma unroll
+#pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           const float4 v4 = *reinterpret_cast<const float4*>(&Vs[buf][16 * nt + l16][DK * c + 4 * s4]);
           da[nt][0] = mfma16x16x4(v4.x, dc[4 * s4 + 0], da[nt][0]);
@@ -217,33 +217,39 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
         }
       // dS^T = P^T o (dA^T - delta)
       float ds[2][4];
-  #pragma unroll
+#pragma unroll
       for (int nt = 0; nt < 2; ++nt)
-  #pragma unroll
+#pragma unroll
         for (int v = 0; v < 4; ++v) {
           const float a = (da[nt][0][v] + da[nt][1][v]) + (da[nt][2][v] + da[nt][3][v]);
           ds[nt][v] = f4at(pc[nt], v) * (a - dl);
         }
       fetch_p(k0 + KT);
-      // dQ += dS K with k index = key
-  #pragma unroll
+      // dQ += dS K with k index = key.  Column n of MFMA tile f is head dim
+      // ND n + f, so a lane's K values for its ND tiles are contiguous
+      // (vector LDS reads) and its dq values contiguous on store.
+#pragma unroll
       for (int nt = 0; nt < 2; ++nt)
-  #pragma unroll
-        for (int v = 0; v < 4; ++v)
-  #pragma unroll
-          for (int f = 0; f < ND; ++f)
-            acc[f] = mfma16x16x4(ds[nt][v], Ks[buf][16 * nt + 4 * c + v][16 * f + l16], acc[f]);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float kv[ND];
+#pragma unroll
+          for (int f = 0; f < ND; ++f) kv[f] = Ks[buf][16 * nt + 4 * c + v][ND * l16 + f];
+#pragma unroll
+          for (int f = 0; f < ND; ++f) acc[f] = mfma16x16x4(ds[nt][v], kv[f], acc[f]);
+        }
       stash(buf ^ 1);
       __syncthreads();
       buf ^= 1;
     }
-  #pragma unroll
-    for (int f = 0; f < ND; ++f)
-  #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t row = q0 + 4 * c + v;
-        if (row < s_q) out[row * ldq + h * D + 16 * f + l16] = scale * acc[f][v];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t row = q0 + 4 * c + v;
+      if (row < s_q) {
+#pragma unroll
+        for (int f = 0; f < ND; ++f) out[row * ldq + h * D + ND * l16 + f] = scale * acc[f][v];
       }
+    }
   };
   if (KSPLIT) {
     float* out = half == 0 ? dq : dq2;

@@ -195,19 +195,26 @@ hipError_t ffn_run(int64_t rows, int64_t dim, int64_t ffn, int act, const float*
     r.eps = eps;
     return launch_dgemv_red(RED_ACCUM, dt, r, s);
   }
-  // 1. dHid = d_out W_down
+  // 1. dHid = d_out W_down (split-K partials are added by the next kernel)
+  int n1 = 1;
   e = launch_gemm(rows, ffn, dim, d_out, F32, dim, w_down, nullptr, dim, dt, ffn, p.dhid, ffn,
-                  p.partials, s);
+                  p.partials, s, &n1);
   if (e != hipSuccess) return e;
+  const float* dh = n1 > 1 ? p.partials : p.dhid;
+  const int64_t dhs = n1 > 1 ? rows * ffn : 0;
   // 2. sub-norm backward
   if (hidden_pre) {
-    e = launch_rmsnorm_bwd(rows, ffn, hidden_pre, dt, gamma_sub, p.dhid, p.dhid, eps, 0, s);
+    e = launch_rmsnorm_bwd(rows, ffn, hidden_pre, dt, gamma_sub, dh, p.dhid, eps, 0, s, n1, dhs);
     if (e != hipSuccess) return e;
+    dh = p.dhid;
+    n1 = 1;
   }
   // 3. gated activation backward -> [dGate | dUp]
-  e = launch_act_bwd(rows, ffn, act, gate, up_, dt, p.dhid, p.dgu, dt, s);
+  e = launch_act_bwd(rows, ffn, act, gate, up_, dt, dh, p.dgu, dt, s, n1, dhs);
   if (e != hipSuccess) return e;
-  // 4. dN2 = [dGate | dUp] [W_gate; W_up]
+  // 4. dN2 = [dGate | dUp] [W_gate; W_up] (the partials of W_down are dead);
+  // reduced by the product itself: the norm below reads dN2 twice, which
+  // costs more than one reduction pass when it comes as several partials
   e = launch_gemm(rows, dim, 2 * ffn, p.dgu, dt, 2 * ffn, w_gate, w_up, ffn, dt, dim, p.dn2, dim,
                   p.partials, s);
   if (e != hipSuccess) return e;

@@ -432,7 +432,8 @@ __global__ __launch_bounds__(256) void cvt_a_bf16_kernel(int64_t M, int64_t K, c
 
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt, int64_t lda,
                        const void* B1, const void* B2, int64_t K1, int b_dt, int64_t ldb,
-                       float* C, int64_t ldc, float* partials, hipStream_t s) {
+                       float* C, int64_t ldc, float* partials, hipStream_t s, int* deferred) {
+  if (deferred) *deferred = 1;
   if (M == 0 || N == 0) return hipSuccess;
   const GemmPlan pl = gemm_plan(M, N, K, b_dt);
   const int64_t kps = pl.kps;
@@ -487,6 +488,10 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
            (double)M * N * 4,
        2.0 * M * N * K, s);
   if (e != hipSuccess || nsp == 1) return e;
+  if (deferred) {
+    *deferred = nsp;
+    return hipSuccess;
+  }
   int64_t blocks = cdiv(M * (N / 4), 256);
   if (blocks > 4096) blocks = 4096;
   splitk_reduce_kernel<<<dim3((unsigned)blocks), block, 0, s>>>(M, N, nsp, partials, C, ldc);

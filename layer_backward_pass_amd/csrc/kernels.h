@@ -18,14 +18,18 @@ void mark(const char* name, double alg_bytes, double alg_flops, hipStream_t s);
 enum ActKind { SWIGLU = 0, RELU2 = 1 };
 
 // ---- row-wise kernels (rowwise.hip)
+// dy may be `nparts` split-K partial sums [nparts][rows][n] (stride pstride),
+// added in order; dx may alias dy when nparts == 1.
 hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, const float* gamma,
                               const float* dy, float* dx, float eps, int accumulate,
-                              hipStream_t s);
+                              hipStream_t s, int nparts = 1, int64_t pstride = 0);
 hipError_t launch_rope_bwd(int64_t rows, int64_t n_heads, int64_t head_dim, const float* dy,
                            float* dx, int64_t pos0, float base, hipStream_t s);
-// dgu[r, 0:I] = dGate, dgu[r, I:2I] = dUp; out_dt selects float or bf16 output.
+// dgu[r, 0:I] = dGate, dgu[r, I:2I] = dUp; out_dt selects float or bf16 output;
+// dhid may be `nparts` split-K partial sums (stride pstride), added in order.
 hipError_t launch_act_bwd(int64_t rows, int64_t ffn, int act, const void* gate, const void* up,
-                          int in_dt, const float* dhid, void* dgu, int out_dt, hipStream_t s);
+                          int in_dt, const float* dhid, void* dgu, int out_dt, hipStream_t s,
+                          int nparts = 1, int64_t pstride = 0);
 // p[0:n] = 0 (a kernel, not a memset, so the call can sit in a captured graph)
 hipError_t launch_fill_zero(int64_t n, float* p, hipStream_t s);
 // dst = bf16(src), n elements (n % 8 == 0)
@@ -40,9 +44,13 @@ hipError_t launch_to_bf16(int64_t n, const float* src, void* dst, hipStream_t s)
 // `partials` must hold gemm_partial_bytes(M, N, K, a_dt, b_dt) bytes.
 int gemm_splits(int64_t M, int64_t N, int64_t K, int b_dt);
 size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K, int a_dt, int b_dt);
+// With `deferred` non-null, a split-K product leaves its partial sums in
+// `partials` ([splits][M][N], dense) for the consumer to add, and
+// *deferred = splits (1: the result is in C).
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt, int64_t lda,
                        const void* B1, const void* B2, int64_t K1, int b_dt, int64_t ldb,
-                       float* C, int64_t ldc, float* partials, hipStream_t s);
+                       float* C, int64_t ldc, float* partials, hipStream_t s,
+                       int* deferred = nullptr);
 
 // ---- single-token (decode) kernels (decode.hip)
 // part[chunk, N] = x[K] W[K, N] over row chunks of kc rows (W rows k < K1

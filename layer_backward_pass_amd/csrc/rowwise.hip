@@ -13,12 +13,35 @@ namespace lbp {
 //   dx = (1/r) (dy*gamma - x <dy*gamma, x> / (n r^2)),  r = sqrt(mean(x^2)+eps)
 // Pass 1 reduces sum(x^2) and <dy*gamma, x> over the row; pass 2 writes dx
 // (or adds to it).  Each thread re-reads only the elements it read in pass
-// 1, so dx may alias dy.
+// 1, so dx may alias dy.  dy may arrive as `nparts` split-K partial sums
+// (stride pstride), added here in split order.
+__device__ __forceinline__ float4 sum_parts4(const float* p, int nparts, int64_t pstride) {
+  if (nparts == 1) return *reinterpret_cast<const float4*>(p);
+  // up to 8 partials in flight (an index past the last re-reads part 0 and
+  // its term is dropped), added in order
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i0 = 0; i0 < nparts; i0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = *reinterpret_cast<const float4*>(p + (i0 + u < nparts ? i0 + u : 0) * pstride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool take = i0 + u < nparts;
+      s.x += take ? v[u].x : 0.f;
+      s.y += take ? v[u].y : 0.f;
+      s.z += take ? v[u].z : 0.f;
+      s.w += take ? v[u].w : 0.f;
+    }
+  }
+  return s;
+}
+
 template <typename T, int ACC>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int64_t n, const T* __restrict__ x,
                                                           const float* __restrict__ gamma,
                                                           const float* dy, float* dx,
-                                                          float eps) {
+                                                          float eps, int nparts, int64_t pstride) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const T* xr = x + row * n;
@@ -28,7 +51,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int64_t n, const T* __
   for (int64_t i = (int64_t)threadIdx.x * 4; i < n; i += 1024) {
     float4 xv = Act<T>::ld4(xr, i);
     float4 gv = *reinterpret_cast<const float4*>(gamma + i);
-    float4 dv = *reinterpret_cast<const float4*>(dyr + i);
+    float4 dv = sum_parts4(dyr + i, nparts, pstride);
     ss += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
     dot += dv.x * gv.x * xv.x + dv.y * gv.y * xv.y + dv.z * gv.z * xv.z + dv.w * gv.w * xv.w;
   }
@@ -41,7 +64,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int64_t n, const T* __
   for (int64_t i = (int64_t)threadIdx.x * 4; i < n; i += 1024) {
     float4 xv = Act<T>::ld4(xr, i);
     float4 gv = *reinterpret_cast<const float4*>(gamma + i);
-    float4 dv = *reinterpret_cast<const float4*>(dyr + i);
+    float4 dv = sum_parts4(dyr + i, nparts, pstride);
     float4 o;
     o.x = (dv.x * gv.x - xv.x * c) * inv_r;
     o.y = (dv.y * gv.y - xv.y * c) * inv_r;
@@ -61,21 +84,22 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int64_t n, const T* __
 
 hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, const float* gamma,
                               const float* dy, float* dx, float eps, int accumulate,
-                              hipStream_t s) {
+                              hipStream_t s, int nparts, int64_t pstride) {
   if (rows == 0) return hipSuccess;
   dim3 grid((unsigned)rows), block(256);
   if (xdt == F32) {
     if (accumulate)
-      rmsnorm_bwd_kernel<float, 1><<<grid, block, 0, s>>>(n, (const float*)x, gamma, dy, dx, eps);
+      rmsnorm_bwd_kernel<float, 1><<<grid, block, 0, s>>>(n, (const float*)x, gamma, dy, dx, eps, nparts, pstride);
     else
-      rmsnorm_bwd_kernel<float, 0><<<grid, block, 0, s>>>(n, (const float*)x, gamma, dy, dx, eps);
+      rmsnorm_bwd_kernel<float, 0><<<grid, block, 0, s>>>(n, (const float*)x, gamma, dy, dx, eps, nparts, pstride);
   } else {
     if (accumulate)
-      rmsnorm_bwd_kernel<bf16, 1><<<grid, block, 0, s>>>(n, (const bf16*)x, gamma, dy, dx, eps);
+      rmsnorm_bwd_kernel<bf16, 1><<<grid, block, 0, s>>>(n, (const bf16*)x, gamma, dy, dx, eps, nparts, pstride);
     else
-      rmsnorm_bwd_kernel<bf16, 0><<<grid, block, 0, s>>>(n, (const bf16*)x, gamma, dy, dx, eps);
+      rmsnorm_bwd_kernel<bf16, 0><<<grid, block, 0, s>>>(n, (const bf16*)x, gamma, dy, dx, eps, nparts, pstride);
   }
-  mark("rmsnorm_bwd", (double)rows * n * ((xdt == F32 ? 4 : 2) + 8 + (accumulate ? 4 : 0)) + n * 4.0,
+  mark("rmsnorm_bwd",
+       (double)rows * n * ((xdt == F32 ? 4 : 2) + 4 * nparts + 4 + (accumulate ? 4 : 0)) + n * 4.0,
        (double)rows * n * 8, s);
   return hipGetLastError();
 }
@@ -133,7 +157,8 @@ template <typename T, int ACT, int OUT_BF16>
 __global__ __launch_bounds__(256) void act_bwd_kernel(int64_t rows, int64_t ffn,
                                                       const T* __restrict__ gate,
                                                       const T* __restrict__ up,
-                                                      const float* __restrict__ dhid, void* dgu) {
+                                                      const float* __restrict__ dhid, void* dgu,
+                                                      int nparts, int64_t pstride) {
   const int64_t q = ffn / 4;
   const int64_t total = rows * q;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
@@ -143,7 +168,7 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(int64_t rows, int64_t ffn,
     const int64_t i = r * ffn + c;
     const float4 g = Act<T>::ld4(gate, i);
     const float4 u = Act<T>::ld4(up, i);
-    const float4 dh = *reinterpret_cast<const float4*>(dhid + i);
+    const float4 dh = sum_parts4(dhid + i, nparts, pstride);
     float4 dg, du;
     act_bwd1<ACT>(g.x, u.x, dh.x, dg.x, du.x);
     act_bwd1<ACT>(g.y, u.y, dh.y, dg.y, du.y);
@@ -169,29 +194,31 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(int64_t rows, int64_t ffn,
 
 template <typename T, int ACT>
 static void act_launch(int64_t rows, int64_t ffn, const void* gate, const void* up,
-                       const float* dhid, void* dgu, int out_dt, hipStream_t s) {
+                       const float* dhid, void* dgu, int out_dt, hipStream_t s, int nparts,
+                       int64_t pstride) {
   const int64_t total = rows * (ffn / 4);
   int64_t blocks = (total + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (out_dt == BF16)
     act_bwd_kernel<T, ACT, 1><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
-        rows, ffn, (const T*)gate, (const T*)up, dhid, dgu);
+        rows, ffn, (const T*)gate, (const T*)up, dhid, dgu, nparts, pstride);
   else
     act_bwd_kernel<T, ACT, 0><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
-        rows, ffn, (const T*)gate, (const T*)up, dhid, dgu);
+        rows, ffn, (const T*)gate, (const T*)up, dhid, dgu, nparts, pstride);
 }
 
 hipError_t launch_act_bwd(int64_t rows, int64_t ffn, int act, const void* gate, const void* up,
-                          int in_dt, const float* dhid, void* dgu, int out_dt, hipStream_t s) {
+                          int in_dt, const float* dhid, void* dgu, int out_dt, hipStream_t s,
+                          int nparts, int64_t pstride) {
   if (rows == 0) return hipSuccess;
   if (in_dt == F32) {
-    if (act == SWIGLU) act_launch<float, SWIGLU>(rows, ffn, gate, up, dhid, dgu, out_dt, s);
-    else act_launch<float, RELU2>(rows, ffn, gate, up, dhid, dgu, out_dt, s);
+    if (act == SWIGLU) act_launch<float, SWIGLU>(rows, ffn, gate, up, dhid, dgu, out_dt, s, nparts, pstride);
+    else act_launch<float, RELU2>(rows, ffn, gate, up, dhid, dgu, out_dt, s, nparts, pstride);
   } else {
-    if (act == SWIGLU) act_launch<bf16, SWIGLU>(rows, ffn, gate, up, dhid, dgu, out_dt, s);
-    else act_launch<bf16, RELU2>(rows, ffn, gate, up, dhid, dgu, out_dt, s);
+    if (act == SWIGLU) act_launch<bf16, SWIGLU>(rows, ffn, gate, up, dhid, dgu, out_dt, s, nparts, pstride);
+    else act_launch<bf16, RELU2>(rows, ffn, gate, up, dhid, dgu, out_dt, s, nparts, pstride);
   }
-  mark("act_bwd", (double)rows * ffn * (2 * (in_dt == F32 ? 4 : 2) + 4 + 2 * (out_dt == F32 ? 4 : 2)),
+  mark("act_bwd", (double)rows * ffn * (2 * (in_dt == F32 ? 4 : 2) + 4 * nparts + 2 * (out_dt == F32 ? 4 : 2)),
        (double)rows * ffn * 12, s);
   return hipGetLastError();
 }

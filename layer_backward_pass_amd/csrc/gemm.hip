@@ -168,17 +168,17 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
 
 // ---------------------------------------------------------------------------
 // bf16 GEMM: 512 threads, tile 128 x 256, BK = 64, waves 2 x 4 of 64 x 64
-// (v_mfma_f32_16x16x32_bf16).  A (bf16, or fp32 rounded to bf16 on the way
-// in) sits in LDS k-contiguous, As[m][k], and is read with one 16-byte load
-// per operand.  B keeps its memory layout in LDS, Bs[k][n], filled with
+// (v_mfma_f32_16x16x32_bf16).  A (bf16; launch_gemm rounds an fp32 A first)
+// sits in LDS k-contiguous, As[m][k], and is read with one 16-byte load per
+// operand.  B keeps its memory layout in LDS, Bs[k][n], filled with
 // plain 16-byte copies; the LDS transpose read turns four k-rows of a column
 // into one lane's operand half.  Double-buffered, one barrier per k-tile.
 constexpr int H_BM = 128, H_BN = 256, H_BK = 64, H_NT = 512;
 constexpr int H_LDA = H_BK + 8, H_LDB = H_BN + 16;
 
-template <typename TA, bool SPLITB>
+template <bool SPLITB>
 __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, int64_t K,
-                                                         const TA* __restrict__ A, int64_t lda,
+                                                         const uint16_t* __restrict__ A, int64_t lda,
                                                          const uint16_t* __restrict__ B1,
                                                          const uint16_t* __restrict__ B2,
                                                          int64_t K1, int64_t ldb,
@@ -186,11 +186,9 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
                                                          int64_t kps, int64_t split_stride) {
   constexpr int NA = H_BM * H_BK / 8 / H_NT;  // A chunks of 8 per thread (2)
   constexpr int NB = H_BK * H_BN / 8 / H_NT;  // B chunks of 8 per thread (4)
-  constexpr int AW = (int)sizeof(TA) / 2;     // 16-byte words per A chunk (fp32: 2)
-  // One k-tile of global data in registers; A stays in its HBM format until
-  // it is written to LDS, so no load has to complete before it is needed.
+  // One k-tile of global data in registers
   struct Stage {
-    uint4 a[NA][AW];
+    uint4 a[NA];
     uint4 b[NB];
   };
   __shared__ __attribute__((aligned(16))) uint16_t As[2][H_BM][H_LDA];
@@ -211,9 +209,8 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
   // zeros.  A: the tile's rows as one range.  B: the rows of one k-tile,
   // from W1 (rows < K1) or W2; with SPLITB (K1 not a multiple of the tile)
   // every chunk reads both sources, each masked to its own rows.
-  const uint32_t aes = sizeof(TA);
   const int64_t mrows = min((int64_t)H_BM, M - bm);
-  const brsrc_t ra = make_brsrc(A + bm * lda, (uint32_t)(((mrows - 1) * lda + K) * aes));
+  const brsrc_t ra = make_brsrc(A + bm * lda, (uint32_t)(((mrows - 1) * lda + K) * 2));
   auto brows = [&](const uint16_t* Bs_, int64_t r0, int64_t nrows) -> brsrc_t {
     return make_brsrc(Bs_ + r0 * ldb + bn, nrows > 0 ? (uint32_t)(nrows * ldb * 2) : 0u);
   };
@@ -223,9 +220,7 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
       const int e = t + H_NT * i;
       const int m = e >> 3;
       const int64_t k = k0 + 8 * (e & 7);
-      const uint32_t off = (m < mrows && k < kend) ? (uint32_t)((m * lda + k) * aes) : BUF_OOB;
-#pragma unroll
-      for (int j = 0; j < AW; ++j) r.a[i][j] = bload_u4(ra, off + 16 * j);
+      r.a[i] = bload_u4(ra, (m < mrows && k < kend) ? (uint32_t)((m * lda + k) * 2) : BUF_OOB);
     }
     if (!SPLITB) {
       // the whole tile lies in one source (K1 is a multiple of the tile)
@@ -261,18 +256,7 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int e = t + H_NT * i;
-      uint4 v;
-      if constexpr (AW == 2) {
-        const float4 x = __builtin_bit_cast(float4, r.a[i][0]);
-        const float4 y = __builtin_bit_cast(float4, r.a[i][1]);
-        v = make_uint4(pk_bf16(x.x, x.y),
-                       pk_bf16(x.z, x.w),
-                       pk_bf16(y.x, y.y),
-                       pk_bf16(y.z, y.w));
-      } else {
-        v = r.a[i][0];
-      }
-      *reinterpret_cast<uint4*>(&As[buf][e >> 3][8 * (e & 7)]) = v;
+      *reinterpret_cast<uint4*>(&As[buf][e >> 3][8 * (e & 7)]) = r.a[i];
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
@@ -469,17 +453,12 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
       return hipErrorInvalidValue;
     const dim3 grid1((unsigned)(cdiv(N, pl.bn) * cdiv(M, pl.bm) * nsp));
     const bool splitb = K1 % H_BK != 0;
-#define LBP_GEMM_BF16(TA, SB)                                                                 \
-  gemm_bf16_kernel<TA, SB><<<grid1, dim3(H_NT), 0, s>>>(M, N, K, (const TA*)A, lda,           \
-                                                       (const uint16_t*)B1, (const uint16_t*)B2, \
-                                                       K1, ldb, out, ldo, kps, sstride)
-    if (a_dt == F32) {
-      if (splitb) LBP_GEMM_BF16(float, true);
-      else LBP_GEMM_BF16(float, false);
-    } else {
-      if (splitb) LBP_GEMM_BF16(uint16_t, true);
-      else LBP_GEMM_BF16(uint16_t, false);
-    }
+#define LBP_GEMM_BF16(SB)                                                                   \
+  gemm_bf16_kernel<SB><<<grid1, dim3(H_NT), 0, s>>>(M, N, K, (const uint16_t*)A, lda,         \
+                                                   (const uint16_t*)B1, (const uint16_t*)B2,  \
+                                                   K1, ldb, out, ldo, kps, sstride)
+    if (splitb) LBP_GEMM_BF16(true);
+    else LBP_GEMM_BF16(false);
 #undef LBP_GEMM_BF16
   }
   hipError_t e = hipGetLastError();

@@ -32,8 +32,6 @@ hipError_t launch_act_bwd(int64_t rows, int64_t ffn, int act, const void* gate, 
                           int nparts = 1, int64_t pstride = 0);
 // p[0:n] = 0 (a kernel, not a memset, so the call can sit in a captured graph)
 hipError_t launch_fill_zero(int64_t n, float* p, hipStream_t s);
-// dst = bf16(src), n elements (n % 8 == 0)
-hipError_t launch_to_bf16(int64_t n, const float* src, void* dst, hipStream_t s);
 
 // ---- products (gemm.hip)
 // C[M,N] = A[M,K] B[K,N]; B rows k < K1 come from B1 (row k), rows k >= K1

@@ -223,21 +223,6 @@ hipError_t launch_act_bwd(int64_t rows, int64_t ffn, int act, const void* gate, 
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void to_bf16_kernel(int64_t n, const float* __restrict__ src,
-                                                      uint16_t* __restrict__ dst) {
-  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8; i < n;
-       i += (int64_t)gridDim.x * blockDim.x * 8) {
-    const float4 a = *reinterpret_cast<const float4*>(src + i);
-    const float4 b = *reinterpret_cast<const float4*>(src + i + 4);
-    uint4 o;
-    o.x = pk_bf16(a.x, a.y);
-    o.y = pk_bf16(a.z, a.w);
-    o.z = pk_bf16(b.x, b.y);
-    o.w = pk_bf16(b.z, b.w);
-    *reinterpret_cast<uint4*>(dst + i) = o;
-  }
-}
-
 __global__ __launch_bounds__(256) void fill_zero_kernel(int64_t n, float* __restrict__ p) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -250,15 +235,6 @@ hipError_t launch_fill_zero(int64_t n, float* p, hipStream_t s) {
   if (blocks > 4096) blocks = 4096;
   fill_zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(n, p);
   mark("fill_zero", (double)n * 4, 0, s);
-  return hipGetLastError();
-}
-
-hipError_t launch_to_bf16(int64_t n, const float* src, void* dst, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  int64_t blocks = (n / 8 + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  to_bf16_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(n, src, (uint16_t*)dst);
-  mark("to_bf16", (double)n * 6, 0, s);
   return hipGetLastError();
 }
 

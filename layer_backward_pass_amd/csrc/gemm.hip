@@ -47,6 +47,51 @@ __device__ __forceinline__ void store_tile(float* C, int64_t ldc, int64_t M, int
 // pipe then stays about three quarters busy.
 constexpr int F_BK = 32, F_LD = F_BK + 4, F_BM = 128, F_BN = 256, F_NT = 512;
 
+// Work item of a product launch.  Tiles are numbered m-fastest over the
+// nm x nn grid.  Items u < nfull are whole tiles written to C; the other
+// tiles are split in k-chunks of kps, item nfull + j -> chunk z = j / ntail
+// of tile nfull + j % ntail (chunk-major, so neighbouring items still share
+// weight panels), written to partial slot z ([z][M][N], dense).  nfull = 0
+// is plain split-K; nfull = all tiles is no split.
+struct GemmWork {
+  int64_t bm, bn, kbeg, kend, ldo;
+  float* out;
+};
+template <int BM, int BN>
+__device__ __forceinline__ GemmWork gemm_work(int64_t M, int64_t N, int64_t K, int64_t kps,
+                                              int64_t nfull, float* C, int64_t ldc, float* P) {
+  const int64_t nm = (M + BM - 1) / BM, nn = (N + BN - 1) / BN, T = nm * nn;
+  // Workgroups start in launch order, so the whole tiles (the long items)
+  // take the first launch slots; each part is spread over the XCDs on its own.
+  const int64_t b = blockIdx.x, G = gridDim.x;
+  const int64_t u = b < nfull ? xcd_remap(b, nfull) : nfull + xcd_remap(b - nfull, G - nfull);
+  int64_t tile, z;
+  if (u < nfull) {
+    tile = u;
+    z = -1;
+  } else {
+    const int64_t j = u - nfull, nt = T - nfull;
+    z = j / nt;
+    tile = nfull + (j - z * nt);
+  }
+  GemmWork w;
+  w.bm = (tile % nm) * BM;
+  w.bn = (tile / nm) * BN;
+  if (z < 0) {
+    w.kbeg = 0;
+    w.kend = K;
+    w.out = C;
+    w.ldo = ldc;
+  } else {
+    w.kbeg = z * kps;
+    w.kend = min(K, w.kbeg + kps);
+    w.out = P + z * M * N;
+    w.ldo = N;
+  }
+  return w;
+}
+
+
 __device__ __forceinline__ float f4at(const float4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
@@ -56,8 +101,8 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
                                                         const float* __restrict__ B1,
                                                         const float* __restrict__ B2, int64_t K1,
                                                         int64_t ldb, float* __restrict__ C,
-                                                        int64_t ldc, int64_t kps,
-                                                        int64_t split_stride) {
+                                                        int64_t ldc, float* __restrict__ P,
+                                                        int64_t kps, int64_t nfull) {
   constexpr int NA = F_BM * F_BK / 4 / F_NT;   // A float4 per thread (2)
   constexpr int NBQ = F_BK * F_BN / 4 / F_NT;  // B k-quads per thread (4)
   constexpr int BQS = F_NT / F_BN;             // k-quad stride between them (2)
@@ -66,15 +111,10 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
   const int l16 = lane & 15, c = lane >> 4;
-  // 1-D grid: item u -> (split z, column panel n, row tile m), m fastest,
-  // so the row tiles that read one weight panel run together on one XCD.
-  const int64_t nm = (M + F_BM - 1) / F_BM, nn = (N + F_BN - 1) / F_BN;
-  const int64_t u = xcd_remap(blockIdx.x, (int64_t)gridDim.x);
-  const int64_t z = u / (nm * nn), rem = u - z * nm * nn;
-  const int64_t bm = (rem % nm) * F_BM, bn = (rem / nm) * F_BN;
-  const int64_t kbeg = z * kps;
-  const int64_t kend = min(K, kbeg + kps);
-  C += z * split_stride;
+  // 1-D grid of work items (gemm_work), m fastest, so the row tiles that
+  // read one weight panel run together on one XCD.
+  const GemmWork wk = gemm_work<F_BM, F_BN>(M, N, K, kps, nfull, C, ldc, P);
+  const int64_t bm = wk.bm, bn = wk.bn, kbeg = wk.kbeg, kend = wk.kend;
   const int wm = (w & 1) * 64, wn = (w >> 1) * 64;
 
   // A: rows (t/8) + 64 i, k quad t%8.  B: column t % 256, k quads t/256 + 2i
@@ -163,7 +203,7 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
     __syncthreads();
     load(s1, k0 + 4 * F_BK);
   }
-  store_tile<4, 4>(C, ldc, M, N, bm + wm, bn + wn, acc);
+  store_tile<4, 4>(wk.out, wk.ldo, M, N, bm + wm, bn + wn, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -183,7 +223,8 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
                                                          const uint16_t* __restrict__ B2,
                                                          int64_t K1, int64_t ldb,
                                                          float* __restrict__ C, int64_t ldc,
-                                                         int64_t kps, int64_t split_stride) {
+                                                         float* __restrict__ P, int64_t kps,
+                                                         int64_t nfull) {
   constexpr int NA = H_BM * H_BK / 8 / H_NT;  // A chunks of 8 per thread (2)
   constexpr int NB = H_BK * H_BN / 8 / H_NT;  // B chunks of 8 per thread (4)
   // One k-tile of global data in registers
@@ -195,13 +236,8 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][H_BK][H_LDB];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int l16 = lane & 15, c = lane >> 4;
-  const int64_t nm = (M + H_BM - 1) / H_BM, nn = (N + H_BN - 1) / H_BN;
-  const int64_t u = xcd_remap(blockIdx.x, (int64_t)gridDim.x);
-  const int64_t z = u / (nm * nn), rem = u - z * nm * nn;
-  const int64_t bm = (rem % nm) * H_BM, bn = (rem / nm) * H_BN;
-  const int64_t kbeg = z * kps;
-  const int64_t kend = min(K, kbeg + kps);
-  C += z * split_stride;
+  const GemmWork wk = gemm_work<H_BM, H_BN>(M, N, K, kps, nfull, C, ldc, P);
+  const int64_t bm = wk.bm, bn = wk.bn, kbeg = wk.kbeg, kend = wk.kend;
   const int wm = (w & 1) * 64, wn = (w >> 1) * 64;
 
   // Loads are buffer loads whose bounds are offsets (out of range reads 0):
@@ -306,20 +342,24 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
     __syncthreads();
     load(s1, k0 + 4 * H_BK);
   }
-  store_tile<4, 4>(C, ldc, M, N, bm + wm, bn + wn, acc);
+  store_tile<4, 4>(wk.out, wk.ldo, M, N, bm + wm, bn + wn, acc);
 }
 
 // ---------------------------------------------------------------------------
-// Fixed-order reduction of split-K partials: C[m, n] = sum_s P[s, m, n].
+// Fixed-order reduction of split-K partials: C[m, n] = sum_s P[s, m, n],
+// over the split tiles only -- columns n >= n0, except the rows m < mskip of
+// the first column panel [n0, n0 + bn), which were whole tiles.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(int64_t M, int64_t N, int splits,
                                                             const float* __restrict__ P,
-                                                            float* __restrict__ C, int64_t ldc) {
-  const int64_t q = N / 4;
+                                                            float* __restrict__ C, int64_t ldc,
+                                                            int64_t n0, int64_t bn, int64_t mskip) {
+  const int64_t q = (N - n0) / 4;
   const int64_t total = M * q;
   const int64_t stride = M * N;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
        t += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t m = t / q, n = (t - m * q) * 4;
+    const int64_t m = t / q, n = n0 + (t - m * q) * 4;
+    if (m < mskip && n < n0 + bn) continue;
     const float* p = P + m * N + n;
     // the partials of up to 8 splits in flight at a time, added in split order
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -347,35 +387,40 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(int64_t M, int64_t N
 
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Split-K count from a small cost model: the CUs take the workgroups in
-// rounds (one fp32 workgroup or two bf16 workgroups per CU at a time); a
-// round lasts one tile's k-range at the rate measured for the kernel; split-K
-// adds the HBM round trip of its partial sums.
+// Work split from a small cost model.  The CUs take the workgroups in
+// rounds of 256 (one per CU: LDS); a whole tile lasts its k-range at the rate
+// measured for the kernel.  The first nfull tiles (whole rounds) run whole;
+// the rest are split in nsp k-chunks so the ragged last round is short, at
+// the cost of an HBM round trip of their partial sums.  nfull = 0 is plain
+// split-K.
 struct GemmPlan {
   int bm, bn, nsp;
-  int64_t kps;
+  int64_t kps, nfull;
 };
 static GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int b_dt) {
   const bool f32 = b_dt == F32;
   const int bm = f32 ? F_BM : H_BM, bn = f32 ? F_BN : H_BN, bk = f32 ? F_BK : H_BK;
-  const int slots = 256;  // one workgroup per CU (LDS)
+  const int64_t slots = 256;
   // ns per k index for one tile: 2 bm bn flops at the sustained MFMA rate
   const double ns_per_k = f32 ? 2.0 * bm * bn / (256.0 * 0.74 * 2.4)
                               : 2.0 * bm * bn / (4069.0 * 0.5 * 2.4);
   const int64_t tiles = cdiv(M, bm) * cdiv(N, bn);
-  GemmPlan best{bm, bn, 1, K};
-  double best_t = 1e30;
-  for (int s = 1; s <= 16; ++s) {
-    const int64_t kps = cdiv(cdiv(K, s), 64) * 64;
-    const int nsp = (int)cdiv(K, kps);
-    if (nsp != s && s > 1) continue;
-    if (s > 1 && kps < 4 * bk) break;
-    const int64_t rounds = cdiv(tiles * nsp, slots);
-    double tt = (double)rounds * kps * ns_per_k * 1e-3;               // us
-    if (nsp > 1) tt += (2.0 * nsp + 1) * M * N * 4 / 6.0e6;            // us at 6 TB/s
-    if (tt < best_t * 0.98) {
-      best_t = tt;
-      best = GemmPlan{bm, bn, nsp, kps};
+  const double tile_bytes = (double)std::min((int64_t)bm, M) * std::min((int64_t)bn, N) * 4;
+  GemmPlan best{bm, bn, 1, K, tiles};
+  double best_t = (double)cdiv(tiles, slots) * K * ns_per_k * 1e-3;  // us
+  for (int64_t r = 0; r * slots < tiles; ++r) {
+    const int64_t nfull = r * slots, tail = tiles - nfull;
+    for (int s = 2; s <= 16; ++s) {
+      const int64_t kps = cdiv(cdiv(K, s), 64) * 64;
+      const int nsp = (int)cdiv(K, kps);
+      if (nsp != s) continue;
+      if (kps < 4 * bk) break;
+      double tt = ((double)r * K + (double)cdiv(tail * nsp, slots) * kps) * ns_per_k * 1e-3;
+      tt += (2.0 * nsp + 1) * tail * tile_bytes / 6.0e6;  // us at 6 TB/s
+      if (tt < best_t * 0.98) {
+        best_t = tt;
+        best = GemmPlan{bm, bn, nsp, kps, nfull};
+      }
     }
   }
   return best;
@@ -420,21 +465,19 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
   if (deferred) *deferred = 1;
   if (M == 0 || N == 0) return hipSuccess;
   const GemmPlan pl = gemm_plan(M, N, K, b_dt);
-  const int64_t kps = pl.kps;
+  const int64_t kps = pl.kps, nfull = pl.nfull;
   const int nsp = pl.nsp;
-  float* out = nsp > 1 ? partials : C;
-  const int64_t ldo = nsp > 1 ? N : ldc;
-  const int64_t sstride = nsp > 1 ? M * N : 0;
+  const int64_t tiles = cdiv(N, pl.bn) * cdiv(M, pl.bm);
+  const dim3 grid1((unsigned)(nfull + (tiles - nfull) * nsp));
   if (B2 == nullptr) {
     B2 = B1;
     K1 = K;
   }
   const dim3 block(256);
   if (b_dt == F32) {
-    const dim3 grid1((unsigned)(cdiv(N, pl.bn) * cdiv(M, pl.bm) * nsp));
     gemm_f32_kernel<<<grid1, dim3(F_NT), 0, s>>>(M, N, K, (const float*)A, lda, (const float*)B1,
-                                                (const float*)B2, K1, ldb, out, ldo, kps,
-                                                sstride);
+                                                (const float*)B2, K1, ldb, C, ldc, partials, kps,
+                                                nfull);
   } else {
     if (a_dt == F32) {
       // A to bf16 once, into the scratch after the partials
@@ -451,12 +494,11 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
     // buffer ranges: one tile's rows of A, one k-tile of B
     if (((double)(H_BM - 1) * lda + K) * 4 >= BUF_MAX_BYTES || (double)H_BK * ldb * 2 >= BUF_MAX_BYTES)
       return hipErrorInvalidValue;
-    const dim3 grid1((unsigned)(cdiv(N, pl.bn) * cdiv(M, pl.bm) * nsp));
     const bool splitb = K1 % H_BK != 0;
 #define LBP_GEMM_BF16(SB)                                                                   \
   gemm_bf16_kernel<SB><<<grid1, dim3(H_NT), 0, s>>>(M, N, K, (const uint16_t*)A, lda,         \
                                                    (const uint16_t*)B1, (const uint16_t*)B2,  \
-                                                   K1, ldb, out, ldo, kps, sstride)
+                                                   K1, ldb, C, ldc, partials, kps, nfull)
     if (splitb) LBP_GEMM_BF16(true);
     else LBP_GEMM_BF16(false);
 #undef LBP_GEMM_BF16
@@ -467,13 +509,17 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
            (double)M * N * 4,
        2.0 * M * N * K, s);
   if (e != hipSuccess || nsp == 1) return e;
-  if (deferred) {
+  if (deferred && nfull == 0) {
+    // plain split-K: the caller adds the partials itself
     *deferred = nsp;
     return hipSuccess;
   }
-  int64_t blocks = cdiv(M * (N / 4), 256);
+  const int64_t nm = cdiv(M, pl.bm);
+  const int64_t n0 = (nfull / nm) * pl.bn, mskip = (nfull % nm) * pl.bm;
+  int64_t blocks = cdiv(M * ((N - n0) / 4), 256);
   if (blocks > 4096) blocks = 4096;
-  splitk_reduce_kernel<<<dim3((unsigned)blocks), block, 0, s>>>(M, N, nsp, partials, C, ldc);
+  splitk_reduce_kernel<<<dim3((unsigned)blocks), block, 0, s>>>(M, N, nsp, partials, C, ldc, n0,
+                                                               pl.bn, mskip);
   mark("splitk_reduce", 0, 0, s);
   return hipGetLastError();
 }

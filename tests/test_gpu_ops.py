@@ -156,6 +156,10 @@ def test_attention_without_dv_and_empty_queries():
     (1, 512, 1032, "swiglu", True, F32),
     (70, 256, 512, "relu2", True, BF16),
     (300, 128, 256, "swiglu", False, BF16),
+    # 7 x 37 product tiles: 256 run whole, the last 3 (rows 512.. of the last
+    # column panel) split in k and added after
+    (833, 256, 9400, "swiglu", False, F32),
+    (833, 512, 9400, "relu2", True, BF16),
 ])
 def test_ffn(rows, dim, ffn, act, sub, dt):
     print("ffn", rows, dim, ffn, act, sub, dt, flush=True)

@@ -212,7 +212,10 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
 // sits in LDS k-contiguous, As[m][k], and is read with one 16-byte load per
 // operand.  B keeps its memory layout in LDS, Bs[k][n], filled with
 // plain 16-byte copies; the LDS transpose read turns four k-rows of a column
-// into one lane's operand half.  Double-buffered, one barrier per k-tile.
+// into one lane's operand half.  Double-buffered, one barrier per k-tile;
+// the operands of each half k-tile are read into registers during the
+// previous half's MFMAs (seq 2048 bf16 W_down 128.6 -> 122.6 us, gate/up
+// 236 -> 223 us).
 constexpr int H_BM = 128, H_BN = 256, H_BK = 64, H_NT = 512;
 constexpr int H_LDA = H_BK + 8, H_LDB = H_BN + 16;
 
@@ -306,41 +309,57 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int buf) {
+  // the MFMA operands of one half k-tile (k = 32 ks .. 32 ks + 31), read
+  // from LDS into registers
+  struct Half {
+    ushortx8 a[4], b[4];
+  };
+  auto read_half = [&](Half& o, int buf, int ks) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      ushortx8 a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = *reinterpret_cast<const ushortx8*>(&As[buf][wm + 16 * i + l16][32 * ks + 8 * c]);
-        b[i] = lds_colk8<true>(&Bs[buf][0][0], H_LDB, 32 * ks, wn + 16 * i, lane);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32bf16(a[i], b[j], acc[i][j]);
+    for (int i = 0; i < 4; ++i) {
+      o.a[i] = *reinterpret_cast<const ushortx8*>(&As[buf][wm + 16 * i + l16][32 * ks + 8 * c]);
+      o.b[i] = lds_colk8<true>(&Bs[buf][0][0], H_LDB, 32 * ks, wn + 16 * i, lane);
     }
   };
+  auto mma_half = [&](const Half& o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32bf16(o.a[i], o.b[j], acc[i][j]);
+  };
 
-  // Three k-tiles in flight: the LDS buffer in use and two register stages,
-  // so a tile's loads have two compute phases to arrive.  Each stage is
-  // copied to LDS after the MFMAs of the current tile were issued and
-  // refilled right after.  An odd tile count ends with a tile of zeros.
-  Stage s0, s1;
-  load(s0, kbeg);
-  stash(s0, 0);
-  load(s0, kbeg + H_BK);
-  load(s1, kbeg + 2 * H_BK);
+  // Pipeline in half k-tiles: the MFMAs of one half run from registers while
+  // the operands of the next half are read from LDS, so the LDS reads never
+  // wait for a barrier with the MFMA pipe idle.  Tile k sits in LDS buffer
+  // X, tile k+1 in Y.  Phase A: read (k, second half) from X, MFMAs of (k,
+  // first half); barrier (every read of X is complete).  Phase B: read
+  // (k+1, first half) from Y, MFMAs of (k, second half), tile k+2 copied
+  // from the register stage into X, tile k+3's global loads issued.  Loads
+  // past the end read 0.
+  Stage st;
+  Half h0, h1;
+  load(st, kbeg);
+  stash(st, 0);
+  load(st, kbeg + H_BK);
   __syncthreads();
-  for (int64_t k0 = kbeg; k0 < kend; k0 += 2 * H_BK) {
-    compute(0);
-    stash(s0, 1);
+  stash(st, 1);
+  load(st, kbeg + 2 * H_BK);
+  read_half(h0, 0, 0);
+  __syncthreads();
+  int buf = 0;
+  for (int64_t k0 = kbeg; k0 < kend; k0 += H_BK) {
+    read_half(h1, buf, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_half(h0);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    load(s0, k0 + 3 * H_BK);
-    compute(1);
-    stash(s1, 0);
-    __syncthreads();
-    load(s1, k0 + 4 * H_BK);
+    read_half(h0, buf ^ 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_half(h1);
+    __builtin_amdgcn_sched_barrier(0);
+    stash(st, buf);
+    load(st, k0 + 3 * H_BK);
+    buf ^= 1;
   }
   store_tile<4, 4>(wk.out, wk.ldo, M, N, bm + wm, bn + wn, acc);
 }

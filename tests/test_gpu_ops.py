@@ -237,6 +237,17 @@ def test_lora_adamw(rows, H, out, rank, step, dt):
     ("tiny", {"dtype": "bf16"}),
     ("decode", {"hidden": 128, "ffn": 256, "n_heads": 4, "n_kv_heads": 2, "head_dim": 32,
                 "kv_len": 70, "pos0": 69}),
+    # 19 key chunks, ragged
+    ("decode", {"hidden": 256, "ffn": 512, "n_heads": 8, "n_kv_heads": 2, "head_dim": 64,
+                "kv_len": 300, "pos0": 299}),
+    # six heads per KV head (dV takes a second block of heads), W_o's second
+    # column block ragged
+    ("decode", {"hidden": 192, "ffn": 384, "n_heads": 12, "n_kv_heads": 2, "head_dim": 32,
+                "kv_len": 40, "pos0": 39}),
+    ("decode", {"hidden": 256, "ffn": 512, "n_heads": 8, "n_kv_heads": 2, "head_dim": 128,
+                "kv_len": 130, "pos0": 129, "dtype": "bf16"}),
+    ("decode", {"hidden": 256, "ffn": 512, "n_heads": 8, "n_kv_heads": 4, "head_dim": 64,
+                "kv_len": 97, "pos0": 96, "sub_norms": 0, "act": "swiglu"}),
     ("seq512", {"seq": 80, "kv_len": 80, "hidden": 256, "ffn": 512, "n_heads": 4,
                 "n_kv_heads": 1, "head_dim": 64, "rank": 8, "alpha": 16.0}),
 ])

@@ -371,21 +371,25 @@ __global__ __launch_bounds__(256) void attn_dv_f32_kernel(int64_t s_q, int64_t s
 }
 
 // dv[key][:] = sum of the chunk partials that exist for the key's tile, in
-// chunk order (zero when no query row sees the key).
+// chunk order (zero when no query row sees the key).  The tile's work starts
+// at query qbeg (a multiple of qgran); with hsteps = 0 a chunk is qc
+// queries, else qc steps of (head, qgran-query block) over hsteps heads.
 __global__ __launch_bounds__(256) void attn_dv_reduce_kernel(int64_t s_q, int64_t s_kv,
                                                              int64_t ldk, int cmax, int64_t qc,
                                                              const float* __restrict__ part,
                                                              float* __restrict__ dv, int causal,
-                                                             int qgran) {
+                                                             int qgran, int kt, int hsteps) {
   const int64_t n4 = s_kv * ldk / 4;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= n4) return;
   const int64_t key = 4 * e / ldk;
-  const int64_t k0 = key / DV_KT * DV_KT;
+  const int64_t k0 = key / kt * kt;
   const int64_t off = s_kv - s_q;
   int64_t qbeg = causal ? k0 - off : 0;
   qbeg = qbeg < 0 ? 0 : qbeg / qgran * qgran;
-  const int64_t nch = qbeg < s_q ? cdiv64(s_q - qbeg, qc) : 0;
+  const int64_t nch = qbeg >= s_q ? 0
+                      : hsteps > 0 ? cdiv64(hsteps * cdiv64(s_q - qbeg, qgran), qc)
+                                   : cdiv64(s_q - qbeg, qc);
   // up to 8 chunk partials in flight, added in chunk order (an index past
   // the last chunk re-reads chunk 0 and its term is dropped)
   const int n = (int)(nch < cmax ? nch : cmax);
@@ -428,11 +432,14 @@ __global__ __launch_bounds__(256) void attn_dv_reduce_kernel(int64_t s_q, int64_
 //     lane's four sub-tiles then hold 16 consecutive keys of its query, so P
 //     is read as 32 contiguous bytes, and the dS values for keys 16c + 8s ..
 //     +7 are the A operand of dQ = dS K with Kt read as one 16-byte row.
-// attn_dv_bf16_kernel  workgroup = 64 keys of one KV group x one query chunk;
-//     waves 2 x 2 over (32 keys, D/2 dims).  Per 64-query step the P block
-//     is copied to LDS as stored ([query][key]) and read as P^T through the
-//     LDS transpose read; dCt rows are copied; two steps of global loads
-//     are in flight.  Chunk partials as in fp32.
+// attn_dv_bf16_kernel  workgroup = 128 keys of one KV group x one chunk of
+//     the tile's steps (head, 64-query block); waves 2 x 2 over (64 keys, D/2
+//     dims), two workgroups per CU.  Per step the P block is copied to LDS as
+//     stored ([query][key]) and read as P^T through the LDS transpose read;
+//     dCt rows are copied.  The operands of each 32-query half are read during
+//     the previous half's MFMAs.  Chunks hold equal step counts, sized so all
+//     of them run in one round (the causal mask gives early key tiles more
+//     steps); chunk partials as in fp32.
 constexpr int TR_R = 64, TR_C = 32;
 
 template <typename TS>
@@ -709,44 +716,86 @@ __global__ __launch_bounds__(256, 2) void attn_dq_bf16_kernel(
   }
 }
 
-constexpr int HV_QT = 64;  // queries per step, bf16 dv kernel
+constexpr int HV_QT = 64;   // queries per step, bf16 dv kernel
+constexpr int HV_KT = 128;  // keys per workgroup, bf16 dv kernel
+
+// Steps (head, 64-query block) of key tile j: the causal mask starts its
+// query range at the first row that sees the tile's first key.
+__host__ __device__ __forceinline__ int64_t dv_tile_qbeg(int64_t j, int64_t s_q, int64_t s_kv,
+                                                         int causal) {
+  int64_t qbeg = causal ? j * HV_KT - (s_kv - s_q) : 0;
+  return qbeg < 0 ? 0 : qbeg / HV_QT * HV_QT;
+}
+__host__ __device__ __forceinline__ int64_t dv_tile_steps(int64_t j, int64_t s_q, int64_t s_kv,
+                                                          int64_t grp, int causal) {
+  const int64_t qbeg = dv_tile_qbeg(j, s_q, s_kv, causal);
+  return qbeg >= s_q ? 0 : grp * ((s_q - qbeg + HV_QT - 1) / HV_QT);
+}
 
 template <int D, bool PVEC>
-__global__ __launch_bounds__(256) void attn_dv_bf16_kernel(int64_t s_q, int64_t s_kv, int Hq,
-                                                           int grp, int cmax, int64_t qc,
-                                                           int64_t LQ,
+__global__ __launch_bounds__(256, 2) void attn_dv_bf16_kernel(int64_t s_q, int64_t s_kv, int Hq,
+                                                           int grp, int cmax, int64_t cs,
+                                                           int64_t nfull, int64_t LQ,
                                                            const uint16_t* __restrict__ P,
                                                            const uint16_t* __restrict__ dCt,
                                                            float* __restrict__ out, int causal) {
-  constexpr int QT = HV_QT, LDT = QT + 8, ND2 = D / 32;
-  constexpr int NP = DV_KT * QT / 8 / 256;  // P chunks of 8 keys per thread (2)
-  constexpr int NC = D * QT / 8;            // dCt chunks of 8 queries
+  constexpr int QT = HV_QT, KT = HV_KT, LDP = KT + 16, LDT = QT + 8, NJ = D / 32;
+  constexpr int NP = KT * QT / 8 / 256;  // P chunks of 8 keys per thread (4)
+  constexpr int NC = D * QT / 8;         // dCt chunks of 8 queries
   constexpr int SC = (NC + 255) / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t Pn[2][QT][DV_KT + 8];  // [query][key]
+  __shared__ __attribute__((aligned(16))) uint16_t Pn[2][QT][LDP];  // [query][key], swizzled
   __shared__ __attribute__((aligned(16))) uint16_t Ct[2][D][LDT];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l16 = lane & 15, c = lane >> 4;
-  const int jt = (int)(blockIdx.x / cmax), ch = (int)(blockIdx.x % cmax);
-  const int g = blockIdx.y;
-  const int64_t ldk = (int64_t)(Hq / grp) * D;
-  const int64_t k0 = (int64_t)jt * DV_KT;
-  const int64_t off = s_kv - s_q;
-  int64_t qbeg = causal ? k0 - off : 0;
-  qbeg = qbeg < 0 ? 0 : qbeg / QT * QT;
-  const int64_t qa = qbeg + ch * qc;
-  const int64_t qz = min(s_q, qa + qc);
-  float* dst = out + (cmax > 1 ? (int64_t)ch * s_kv * ldk : 0);
-  if (qa >= qz) return;  // empty chunk (never chunk 0)
+  // Work item: a chunk of cs steps of key tile jt for KV group g.  Items
+  // are numbered full chunks first (every tile's, in tile order), then the
+  // tiles' shorter last chunks; the group varies fastest.  Workgroups go to
+  // the XCDs round-robin in launch order, so each XCD gets an even share of
+  // the long items.
+  const int Hkv = Hq / grp;
+  const int64_t nt = cdiv64(s_kv, KT);
+  int64_t L = blockIdx.x;
+  const int g = (int)(L % Hkv);
+  int64_t r = L / Hkv;
+  int64_t jt = 0, ch = 0;
+  if (r < nfull) {
+    for (; jt < nt; ++jt) {
+      const int64_t nf = dv_tile_steps(jt, s_q, s_kv, grp, causal) / cs;
+      if (r < nf) break;
+      r -= nf;
+    }
+    ch = r;
+  } else {
+    r -= nfull;
+    for (; jt < nt; ++jt) {
+      const int64_t ts = dv_tile_steps(jt, s_q, s_kv, grp, causal);
+      if (ts % cs != 0) {
+        if (r == 0) break;
+        --r;
+      }
+    }
+    if (jt < nt) ch = dv_tile_steps(jt, s_q, s_kv, grp, causal) / cs;
+  }
+  if (jt >= nt) return;  // no such item (the launch never makes one)
+  const int64_t ldk = (int64_t)Hkv * D;
+  const int64_t k0 = jt * KT;
+  const int64_t qbeg = dv_tile_qbeg(jt, s_q, s_kv, causal);
+  // the tile's steps (head, 64-query block), head-major; chunk ch takes
+  // steps [ch cs, ch cs + cs)
+  const int64_t nqb = cdiv64(s_q - qbeg, QT);
+  const int64_t st0 = ch * cs, st1 = min(nqb * grp, st0 + cs);
+  float* dst = out + (cmax > 1 ? ch * s_kv * ldk : 0);
+  if (st0 >= st1) return;
   const int kh = w & 1, dh = w >> 1;
 
-  floatx4 acc[2][ND2];
+  floatx4 acc[4][NJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < ND2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const int64_t nqb = cdiv64(qz - qa, QT);
-  const int64_t nit = nqb * grp;
-  // one 64-query step of global data; two of them are in flight
+    for (int j = 0; j < NJ; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int64_t nit = st1 - st0;
+  // one 64-query step of global data
   struct Stage {
     ushortx8 p[NP];
     uint4 c[SC];
@@ -755,24 +804,23 @@ __global__ __launch_bounds__(256) void attn_dv_bf16_kernel(int64_t s_q, int64_t 
   // without branches)
   auto fetch = [&](Stage& r, int64_t it) {
     const bool valid = it < nit;
-    const int64_t itc = valid ? it : 0;
-    const int h = g * grp + (int)(itc / nqb);
-    const int64_t qb = qa + QT * (itc % nqb);
+    const int64_t stp = st0 + (valid ? it : 0);
+    const int h = g * grp + (int)(stp / nqb);
+    const int64_t qb = qbeg + QT * (stp % nqb);
     const brsrc_t pr = make_brsrc(P + ((int64_t)h * s_q + qb) * s_kv, (uint32_t)(QT * s_kv * 2));
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int e = t + 256 * i;
-      const int rr = e >> 3, k8 = e & 7;
-      r.p[i] = load_p8<PVEC>(pr, valid && qb + rr < qz, (int64_t)rr * s_kv, k0 + 8 * k8, s_kv);
+      const int rr = e >> 4, k8 = e & 15;
+      r.p[i] = load_p8<PVEC>(pr, valid && qb + rr < s_q, (int64_t)rr * s_kv, k0 + 8 * k8, s_kv);
     }
     const brsrc_t cr = make_brsrc(dCt + (int64_t)h * D * LQ + qb, (uint32_t)(((D - 1) * LQ + QT) * 2));
 #pragma unroll
     for (int i = 0; i < SC; ++i) {
       const int e = t + 256 * i;
       const int d = e / (QT / 8), q8 = e % (QT / 8);
-      // rows past qz belong to the next chunk (or are the zero padding);
-      // their P rows read 0
-      const bool ok = valid && e < NC && qb + 8 * q8 < qz;
+      // rows past s_q are the zero padding; their P rows read 0
+      const bool ok = valid && e < NC && qb + 8 * q8 < s_q;
       r.c[i] = bload_u4(cr, ok ? (uint32_t)((d * LQ + 8 * q8) * 2) : BUF_OOB);
     }
   };
@@ -780,7 +828,8 @@ __global__ __launch_bounds__(256) void attn_dv_bf16_kernel(int64_t s_q, int64_t 
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int e = t + 256 * i;
-      *reinterpret_cast<ushortx8*>(&Pn[buf][e >> 3][8 * (e & 7)]) = r.p[i];
+      const int rr = e >> 4;  // key chunk swizzled as lds_colk8<true> reads it
+      *reinterpret_cast<ushortx8*>(&Pn[buf][rr][(8 * (e & 15)) ^ (64 * ((rr >> 3) & 1))]) = r.p[i];
     }
 #pragma unroll
     for (int i = 0; i < SC; ++i) {
@@ -791,48 +840,61 @@ __global__ __launch_bounds__(256) void attn_dv_bf16_kernel(int64_t s_q, int64_t 
       }
     }
   };
-  auto compute = [&](int buf) {
-#pragma unroll
-    for (int ks = 0; ks < QT / 32; ++ks) {
-      ushortx8 a[2], b[ND2];
-      // P^T operand: eight consecutive queries of key column 32 kh + 16 mi + l%16
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        a[mi] = lds_colk8(&Pn[buf][0][0], DV_KT + 8, 32 * ks, 32 * kh + 16 * mi, lane);
-#pragma unroll
-      for (int nj = 0; nj < ND2; ++nj)
-        b[nj] = *reinterpret_cast<const ushortx8*>(&Ct[buf][(D / 2) * dh + 16 * nj + l16][32 * ks + 8 * c]);
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < ND2; ++nj) acc[mi][nj] = mfma16x16x32bf16(a[mi], b[nj], acc[mi][nj]);
-    }
+  // MFMA operands of one half step (queries 32 ks .. 32 ks + 31)
+  struct Half {
+    ushortx8 a[4], b[NJ];
   };
-  // step it in LDS buffer it % 2; stages s0, s1 hold the next two steps
-  // (an odd step count ends with a step of zeros in buffer 1)
-  Stage s0, s1;
-  fetch(s0, 0);
-  stash(s0, 0);
-  fetch(s0, 1);
-  fetch(s1, 2);
+  auto read_half = [&](Half& o, int buf, int ks) {
+    // P^T operand: eight consecutive queries of key column 64 kh + 16 mi + l%16
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+      o.a[mi] = lds_colk8<true>(&Pn[buf][0][0], LDP, 32 * ks, 64 * kh + 16 * mi, lane);
+#pragma unroll
+    for (int nj = 0; nj < NJ; ++nj)
+      o.b[nj] = *reinterpret_cast<const ushortx8*>(&Ct[buf][(D / 2) * dh + 16 * nj + l16][32 * ks + 8 * c]);
+  };
+  auto mma = [&](const Half& o) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < NJ; ++nj) acc[mi][nj] = mfma16x16x32bf16(o.a[mi], o.b[nj], acc[mi][nj]);
+  };
+  // Step it sits in LDS buffer it % 2; register stages sa, sb hold the next
+  // two steps to be copied in.  Within a step the operands of each half are
+  // read during the previous half's MFMAs; one barrier per step (every read
+  // of a buffer is complete before it is refilled).  An odd step count ends
+  // with a step of zeros.
+  Stage sa;
+  Half h0, h1;
+  fetch(sa, 0);
+  stash(sa, 0);
+  fetch(sa, 1);
+  stash(sa, 1);
+  fetch(sa, 2);
   __syncthreads();
-  for (int64_t it = 0; it < nit; it += 2) {
-    compute(0);
-    stash(s0, 1);
+  read_half(h0, 0, 0);
+  int buf = 0;
+  for (int64_t it = 0; it < nit; ++it) {
+    read_half(h1, buf, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(h0);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    fetch(s0, it + 3);
-    compute(1);
-    stash(s1, 0);
-    __syncthreads();
-    fetch(s1, it + 4);
+    read_half(h0, buf ^ 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(h1);
+    __builtin_amdgcn_sched_barrier(0);
+    stash(sa, buf);
+    fetch(sa, it + 3);
+    buf ^= 1;
   }
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int nj = 0; nj < ND2; ++nj)
+    for (int nj = 0; nj < NJ; ++nj)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int64_t k = k0 + 32 * kh + 16 * mi + 4 * c + v;
+        const int64_t k = k0 + 64 * kh + 16 * mi + 4 * c + v;
         if (k < s_kv) dst[k * ldk + g * D + (D / 2) * dh + 16 * nj + l16] = acc[mi][nj][v];
       }
 }
@@ -1050,9 +1112,10 @@ constexpr int DV_WG_TARGET = 512;
 struct DvPlan {
   int cmax;
   int64_t qc;
+  int64_t nfull, items;  // bf16 kernel: full chunks per KV group, work items
 };
 static DvPlan dv_plan(int64_t s_q, int64_t s_kv, int64_t Hkv) {
-  DvPlan p;
+  DvPlan p{};
   const int64_t tiles = cdiv64(s_kv, DV_KT) * Hkv;
   int64_t want = cdiv64(DV_WG_TARGET, tiles < 1 ? 1 : tiles);
   const int64_t maxc = cdiv64(s_q < 1 ? 1 : s_q, 16);
@@ -1062,17 +1125,32 @@ static DvPlan dv_plan(int64_t s_q, int64_t s_kv, int64_t Hkv) {
   return p;
 }
 
-// Query chunking of the bf16 dv kernel: chunks a multiple of its 64-query step.
-static DvPlan dv_plan_bf16(int64_t s_q, int64_t s_kv, int64_t Hkv) {
-  DvPlan p;
-  const int64_t tiles = cdiv64(s_kv, DV_KT) * Hkv;
-  int64_t want = cdiv64(DV_WG_TARGET, tiles < 1 ? 1 : tiles);
-  const int64_t sq = s_q < 1 ? 1 : s_q;
-  const int64_t maxc = cdiv64(sq, HV_QT);
-  want = want < 1 ? 1 : (want > maxc ? maxc : want);
-  p.qc = cdiv64(cdiv64(sq, want), HV_QT) * HV_QT;
-  p.cmax = (int)cdiv64(sq, p.qc);
-  return p;
+// Work chunking of the bf16 dv kernel.  Key tile j has T_j steps (head,
+// 64-query block), fewer for later tiles under the causal mask; a chunk is
+// qc steps, the smallest count with which every chunk fits in one round of
+// HV_WG_TARGET workgroups, so no chunk is much longer than the others.
+constexpr int HV_WG_TARGET = 512;
+static DvPlan dv_plan_bf16(int64_t s_q, int64_t s_kv, int64_t Hkv, int64_t grp, int causal) {
+  const int64_t sq = s_q < 1 ? 1 : s_q, nt = cdiv64(s_kv, HV_KT);
+  auto steps = [&](int64_t j) { return dv_tile_steps(j, sq, s_kv, grp, causal); };
+  const int64_t tmax = steps(0) > 0 ? steps(0) : 1;
+  DvPlan p{};
+  for (int64_t cs = 4;; ++cs) {
+    int64_t n = 0;
+    for (int64_t j = 0; j < nt; ++j) n += cdiv64(steps(j), cs);
+    if (n * Hkv <= HV_WG_TARGET || cs >= tmax) {
+      p.qc = cs < tmax ? cs : tmax;
+      p.cmax = (int)cdiv64(tmax, p.qc);
+      p.nfull = 0;
+      int64_t np = 0;
+      for (int64_t j = 0; j < nt; ++j) {
+        p.nfull += steps(j) / p.qc;
+        np += steps(j) % p.qc != 0;
+      }
+      p.items = (p.nfull + np) * Hkv;
+      return p;
+    }
+  }
 }
 
 static bool bf16_mfma_path(int dt, int64_t D) { return dt == BF16 && D >= 32; }
@@ -1088,7 +1166,13 @@ static size_t al256(size_t b) { return (b + 255) / 256 * 256; }
 static AttnWs attn_ws(int64_t s_q, int64_t s_kv, int64_t Hq, int64_t Hkv, int64_t D, int dt) {
   AttnWs w;
   const bool hb = bf16_mfma_path(dt, D);
-  const DvPlan dp = hb ? dv_plan_bf16(s_q, s_kv, Hkv) : dv_plan(s_q, s_kv, Hkv);
+  // sized for the larger chunk count of the causal and the full mask
+  DvPlan dp = dv_plan(s_q, s_kv, Hkv);
+  if (hb) {
+    const DvPlan c1 = dv_plan_bf16(s_q, s_kv, Hkv, Hq / Hkv, 1);
+    const DvPlan c0 = dv_plan_bf16(s_q, s_kv, Hkv, Hq / Hkv, 0);
+    dp = c1.cmax > c0.cmax ? c1 : c0;
+  }
   w.LK = cdiv64(s_kv, 64) * 64;
   w.LQ = cdiv64(s_q, 64) * 64;
   w.delta = 0;
@@ -1203,7 +1287,7 @@ static hipError_t attn_launch_f32(int64_t s_q, int64_t s_kv, int Hq, int Hkv, co
   if ((e = hipGetLastError()) != hipSuccess || dp.cmax == 1) return e;
   const int64_t n4 = s_kv * Hkv * D / 4;
   attn_dv_reduce_kernel<<<dim3((unsigned)cdiv64(n4, 256)), 256, 0, s>>>(
-      s_q, s_kv, (int64_t)Hkv * D, dp.cmax, dp.qc, part, dv, causal, 16);
+      s_q, s_kv, (int64_t)Hkv * D, dp.cmax, dp.qc, part, dv, causal, 16, DV_KT, 0);
   mark("attn_dv_reduce", kvbytes * (dp.cmax + 1), 0, s);
   return hipGetLastError();
 }
@@ -1265,21 +1349,21 @@ static hipError_t attn_launch_bf16(int64_t s_q, int64_t s_kv, int Hq, int Hkv, c
                                  0, s>>>(s_q, wl.LQ, (int64_t)Hq * D, dctx, dCt);
   mark("transpose_bf16", qbytes * 4 + (double)Hq * D * wl.LQ * 2, 0, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const DvPlan dp = dv_plan_bf16(s_q, s_kv, Hkv);
+  const DvPlan dp = dv_plan_bf16(s_q, s_kv, Hkv, grp, causal);
   float* part = dp.cmax > 1 ? (float*)(wb + wl.part) : dv;
-  const dim3 grid((unsigned)(cdiv64(s_kv, DV_KT) * dp.cmax), (unsigned)Hkv);
+  const dim3 grid((unsigned)dp.items);
   if (s_kv % 8 == 0)
-    attn_dv_bf16_kernel<D, true><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dp.cmax, dp.qc, wl.LQ, P,
-                                                      dCt, part, causal);
+    attn_dv_bf16_kernel<D, true><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dp.cmax, dp.qc, dp.nfull,
+                                                      wl.LQ, P, dCt, part, causal);
   else
-    attn_dv_bf16_kernel<D, false><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dp.cmax, dp.qc, wl.LQ, P,
-                                                       dCt, part, causal);
+    attn_dv_bf16_kernel<D, false><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dp.cmax, dp.qc,
+                                                       dp.nfull, wl.LQ, P, dCt, part, causal);
   mark("attn_dv_bf16", pbytes + qbytes * 2 + kvbytes * 4 * (dp.cmax > 1 ? dp.cmax : 1),
        2.0 * D * pairs * Hq, s);
   if ((e = hipGetLastError()) != hipSuccess || dp.cmax == 1) return e;
   const int64_t n4 = s_kv * Hkv * D / 4;
   attn_dv_reduce_kernel<<<dim3((unsigned)cdiv64(n4, 256)), 256, 0, s>>>(
-      s_q, s_kv, (int64_t)Hkv * D, dp.cmax, dp.qc, part, dv, causal, HV_QT);
+      s_q, s_kv, (int64_t)Hkv * D, dp.cmax, dp.qc, part, dv, causal, HV_QT, HV_KT, grp);
   mark("attn_dv_reduce", kvbytes * 4 * (dp.cmax + 1), 0, s);
   return hipGetLastError();
 }

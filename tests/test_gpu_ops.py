@@ -115,6 +115,8 @@ def _attn_inputs(seed, s_q, s_kv, Hq, Hkv, D, causal, dt):
     (64, 64, 16, 2, 16, 1, 1, BF16),      # bf16: head dim 16
     (33, 1030, 8, 2, 128, 1, 1, BF16),    # bf16: short query block, long cache
     (640, 640, 8, 2, 128, 1, 1, BF16),    # bf16: several dv chunks
+    (700, 900, 8, 2, 64, 1, 1, BF16),     # bf16: dv chunks over (head, block) steps, ragged
+    (520, 520, 12, 4, 128, 0, 1, BF16),   # bf16: no mask, group of 3, ragged last block
 ])
 def test_attention(s_q, s_kv, Hq, Hkv, D, causal, use_ctx, dt):
     print("attn", s_q, s_kv, Hq, Hkv, D, causal, use_ctx, dt, flush=True)

@@ -67,23 +67,24 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: h, q0 are too
   const int l16 = lane & 15, c = lane >> 4;
-  // 1-D grid over (query tile, head block).  Causal, without KSPLIT: the
-  // first half of the grid takes the query tiles from the end (longest
-  // first) and the second half the complementary ones, so the two
-  // workgroups that share a CU add up to about the same work.  KSPLIT (causal
-  // only): item L = (pair, head block, half); the workgroup takes query tiles
-  // p and nqt-1-p of the pair but only half of each one's key tiles, so every
-  // workgroup has the same work; half 0 writes dq, half 1 the partial dq2
-  // (the caller adds the two).
+  // 1-D grid over (query tile, head block), head block fastest: workgroups
+  // go to the XCDs round-robin, so with eight head blocks each XCD works on
+  // one KV group.  Causal, without KSPLIT: the first half of the grid takes
+  // the query tiles from the end (longest first) and the second half the
+  // complementary ones, so the two workgroups that share a CU add up to
+  // about the same work.  KSPLIT (causal only): item L = (pair, half, head
+  // block); the workgroup takes query tiles p and nqt-1-p of the pair but
+  // only half of each one's key tiles, so every workgroup has the same work;
+  // half 0 writes dq, half 1 the partial dq2 (the caller adds the two).
   const int nhb = Hq / HW;
   const int64_t nqt = cdiv64(s_q, 16 * QW);
   const int64_t L = blockIdx.x;
   int64_t qt, hb;
   int half = 0;
   if (KSPLIT) {
-    half = (int)(L & 1);
-    hb = (L >> 1) % nhb;
-    qt = (L >> 1) / nhb;  // the pair index; the second tile is nqt-1-qt
+    hb = L % nhb;
+    half = (int)((L / nhb) & 1);
+    qt = L / (2 * nhb);  // the pair index; the second tile is nqt-1-qt
   } else if (causal) {
     const int64_t H = (int64_t)nhb * ((nqt + 1) / 2);
     if (L < H) {
@@ -511,7 +512,12 @@ __global__ __launch_bounds__(256, 2) void attn_dq_bf16_kernel(
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform, so are h and the blocks
   const int l16 = lane & 15, c = lane >> 4;
-  const int h = (int)blockIdx.y * HW + (w % HW), g = h / grp;
+  // 1-D grid, head group fastest: workgroups go to the XCDs round-robin, so
+  // with eight head groups each XCD works on one KV group (its K and V stay
+  // in that XCD's L2)
+  const int nhg = Hq / HW;
+  const int by = (int)(blockIdx.x % nhg), bx = (int)(blockIdx.x / nhg);
+  const int h = by * HW + (w % HW), g = h / grp;
   const int64_t ldq = (int64_t)Hq * D, ldk = (int64_t)(Hq / grp) * D;
   const int nsub = (int)cdiv64(s_q, 16);
   const int64_t off = s_kv - s_q;
@@ -522,7 +528,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_bf16_kernel(
     return min(s_kv, off + last + 1);
   };
   // this wave's two blocks (the second is absent for the middle of an odd count)
-  const int pair = (int)blockIdx.x * QW + w / HW;
+  const int pair = bx * QW + w / HW;
   int sub[2];
   bool has[2];
   sub[0] = pair;
@@ -535,7 +541,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_bf16_kernel(
   // the workgroup walks the longest key range among its waves
   int64_t kend_wg = 0;
   for (int j = 0; j < QW; ++j) {
-    const int pj = (int)blockIdx.x * QW + j;
+    const int pj = bx * QW + j;
     if (pj < npairs) {
       kend_wg = max(kend_wg, kend_of(pj));
       if (nsub - 1 - pj != pj) kend_wg = max(kend_wg, kend_of(nsub - 1 - pj));
@@ -1300,7 +1306,7 @@ static void launch_dq_bf16(int64_t s_q, int64_t s_kv, int Hq, int grp, int64_t L
   constexpr int QW = 4 / HW;
   const int nsub = (int)cdiv64(s_q, 16);
   const int npairs = (nsub + 1) / 2;
-  const dim3 grid((unsigned)cdiv64(npairs, QW), (unsigned)(Hq / HW));
+  const dim3 grid((unsigned)(cdiv64(npairs, QW) * (Hq / HW)));
   if (s_kv % 8 == 0)
     attn_dq_bf16_kernel<D, HW, true><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, LK, npairs, dctx, P,
                                                           Kt, V, ctx, delta, dq, scale, causal);

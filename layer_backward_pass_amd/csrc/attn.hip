@@ -264,17 +264,70 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
   }
 }
 
-// dV for 64 keys of KV group blockIdx.y over query chunk (blockIdx.x % cmax)
-// of `qc` rows.  MFMA rows = keys (wave w: 16w .. 16w+15), cols = head dims,
+// Work of the dv kernels.  A workgroup owns a tile of kt keys of one KV
+// group; the tile's query range starts at the first row that sees its first
+// key (causal), rounded down to qround, and is walked in steps of (head,
+// qblk-row block), head-major.  A work item is a chunk of cs consecutive
+// steps of one tile.  Items are numbered full chunks first (every tile's, in
+// tile order), then the tiles' shorter last chunks, the KV group varying
+// fastest: workgroups go to the XCDs round-robin in launch order, so with
+// eight KV groups each XCD works on one group and gets the same share of
+// long items.
+struct DvGeo {
+  int kt, qround, qblk;
+};
+__host__ __device__ __forceinline__ int64_t dv_tile_qbeg(int64_t j, int64_t s_q, int64_t s_kv,
+                                                         int causal, DvGeo q) {
+  int64_t qbeg = causal ? j * q.kt - (s_kv - s_q) : 0;
+  return qbeg < 0 ? 0 : qbeg / q.qround * q.qround;
+}
+__host__ __device__ __forceinline__ int64_t dv_tile_steps(int64_t j, int64_t s_q, int64_t s_kv,
+                                                          int64_t grp, int causal, DvGeo q) {
+  const int64_t qbeg = dv_tile_qbeg(j, s_q, s_kv, causal, q);
+  return qbeg >= s_q ? 0 : grp * ((s_q - qbeg + q.qblk - 1) / q.qblk);
+}
+// Item L -> (KV group g, tile jt, chunk ch); false when L names no item.
+__device__ __forceinline__ bool dv_item(int64_t L, int Hkv, int64_t s_q, int64_t s_kv, int grp,
+                                        int causal, DvGeo q, int64_t cs, int64_t nfull, int& g,
+                                        int64_t& jt, int64_t& ch) {
+  const int64_t nt = (s_kv + q.kt - 1) / q.kt;
+  g = (int)(L % Hkv);
+  int64_t r = L / Hkv;
+  jt = 0;
+  ch = 0;
+  if (r < nfull) {
+    for (; jt < nt; ++jt) {
+      const int64_t nf = dv_tile_steps(jt, s_q, s_kv, grp, causal, q) / cs;
+      if (r < nf) break;
+      r -= nf;
+    }
+    ch = r;
+  } else {
+    r -= nfull;
+    for (; jt < nt; ++jt) {
+      if (dv_tile_steps(jt, s_q, s_kv, grp, causal, q) % cs != 0) {
+        if (r == 0) break;
+        --r;
+      }
+    }
+    if (jt < nt) ch = dv_tile_steps(jt, s_q, s_kv, grp, causal, q) / cs;
+  }
+  return jt < nt;
+}
+
+// dV for 64 keys of one KV group over one work item (chunk of steps, see
+// dv_item).  MFMA rows = keys (wave w: 16w .. 16w+15), cols = head dims,
 // k = query rows (step s, group c: row qb + 4s + c).  32 query rows of one
 // head per step: their dCtx rows go to a double-buffered LDS tile, the P
 // values straight into registers; one step of loads is in flight.  Output:
 // dv itself when cmax == 1, else partial sums part[chunk][key][kv_dim].
 constexpr int FV_QT = 32;  // query rows per step, fp32 dv kernel
+constexpr DvGeo FV_GEO{DV_KT, 16, FV_QT};
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_dv_f32_kernel(int64_t s_q, int64_t s_kv, int Hq,
-                                                          int grp, int cmax, int64_t qc,
+                                                          int grp, int cmax, int64_t cs,
+                                                          int64_t nfull,
                                                           const float* __restrict__ dctx,
                                                           const float* __restrict__ P,
                                                           float* __restrict__ out, int causal) {
@@ -284,25 +337,23 @@ __global__ __launch_bounds__(256) void attn_dv_f32_kernel(int64_t s_q, int64_t s
   __shared__ float dCs[2][QT][LDC];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int l16 = lane & 15, c = lane >> 4;
-  const int jt = (int)(blockIdx.x / cmax), ch = (int)(blockIdx.x % cmax);
-  const int g = blockIdx.y;
+  int g;
+  int64_t jt, ch;
+  if (!dv_item(blockIdx.x, Hq / grp, s_q, s_kv, grp, causal, FV_GEO, cs, nfull, g, jt, ch)) return;
   const int64_t ldq = (int64_t)Hq * D, ldk = (int64_t)(Hq / grp) * D;
-  const int64_t k0 = (int64_t)jt * DV_KT;
-  const int64_t off = s_kv - s_q;
-  int64_t qbeg = causal ? k0 - off : 0;
-  qbeg = qbeg < 0 ? 0 : qbeg / 16 * 16;
-  const int64_t qa = qbeg + ch * qc;
-  const int64_t qz = min(s_q, qa + qc);
+  const int64_t k0 = jt * DV_KT;
+  const int64_t qbeg = dv_tile_qbeg(jt, s_q, s_kv, causal, FV_GEO);
+  const int64_t nqb = cdiv64(s_q - qbeg, QT);
+  const int64_t st0 = ch * cs, st1 = min(nqb * grp, st0 + cs);
   const int64_t key = k0 + 16 * w + l16;
   const bool kok = key < s_kv;
-  float* dst = out + (cmax > 1 ? (int64_t)ch * s_kv * ldk : 0);
-  if (qa >= qz) return;  // empty chunk (never chunk 0)
+  float* dst = out + (cmax > 1 ? ch * s_kv * ldk : 0);
+  if (st0 >= st1) return;
 
   floatx4 acc[ND];
 #pragma unroll
   for (int f = 0; f < ND; ++f) acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const int64_t nqb = cdiv64(qz - qa, QT);
-  const int64_t nit = nqb * grp;
+  const int64_t nit = st1 - st0;
   // One step = 32 query rows of one head: its dCtx rows go to LDS, the P
   // values of this lane's key straight into registers.  Two register stages
   // used in turn; every load is a branch-free buffer load (a step past the
@@ -313,22 +364,22 @@ __global__ __launch_bounds__(256) void attn_dv_f32_kernel(int64_t s_q, int64_t s
   };
   auto fetch = [&](Stage& r, int64_t it) {
     const bool valid = it < nit;
-    const int64_t itc = valid ? it : 0;
-    const int h = g * grp + (int)(itc / nqb);
-    const int64_t qb = qa + QT * (itc % nqb);
+    const int64_t stp = st0 + (valid ? it : 0);
+    const int h = g * grp + (int)(stp / nqb);
+    const int64_t qb = qbeg + QT * (stp % nqb);
     const brsrc_t rd = make_brsrc(dctx + qb * ldq + h * D, (uint32_t)(QT * ldq * 4));
 #pragma unroll
     for (int i = 0; i < SE; ++i) {
       const int e = t + 256 * i;
       const int rr = e / (D / 4);
-      const bool ok = valid && e < NE && qb + rr < qz;
+      const bool ok = valid && e < NE && qb + rr < s_q;
       r.d[i] = bload_f4(rd, ok ? (uint32_t)((rr * ldq + 4 * (e % (D / 4))) * 4) : BUF_OOB);
     }
     const brsrc_t rp = make_brsrc(P + ((int64_t)h * s_q + qb) * s_kv + k0, (uint32_t)(QT * s_kv * 4));
 #pragma unroll
     for (int s2 = 0; s2 < QT / 4; ++s2) {
       const int rr = 4 * s2 + c;
-      const bool ok = valid && kok && qb + rr < qz;
+      const bool ok = valid && kok && qb + rr < s_q;
       r.p[s2] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
           rp, ok ? (int)((rr * s_kv + 16 * w + l16) * 4) : (int)BUF_OOB, 0, 0));
     }
@@ -371,26 +422,19 @@ __global__ __launch_bounds__(256) void attn_dv_f32_kernel(int64_t s_q, int64_t s
     }
 }
 
-// dv[key][:] = sum of the chunk partials that exist for the key's tile, in
-// chunk order (zero when no query row sees the key).  The tile's work starts
-// at query qbeg (a multiple of qgran); with hsteps = 0 a chunk is qc
-// queries, else qc steps of (head, qgran-query block) over hsteps heads.
+// dv[key][:] = sum of the chunk partials that exist for the key's tile (a
+// chunk is cs steps, see dv_item), in chunk order (zero when no query row
+// sees the key).
 __global__ __launch_bounds__(256) void attn_dv_reduce_kernel(int64_t s_q, int64_t s_kv,
-                                                             int64_t ldk, int cmax, int64_t qc,
+                                                             int64_t ldk, int cmax, int64_t cs,
                                                              const float* __restrict__ part,
                                                              float* __restrict__ dv, int causal,
-                                                             int qgran, int kt, int hsteps) {
+                                                             int grp, DvGeo geo) {
   const int64_t n4 = s_kv * ldk / 4;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= n4) return;
   const int64_t key = 4 * e / ldk;
-  const int64_t k0 = key / kt * kt;
-  const int64_t off = s_kv - s_q;
-  int64_t qbeg = causal ? k0 - off : 0;
-  qbeg = qbeg < 0 ? 0 : qbeg / qgran * qgran;
-  const int64_t nch = qbeg >= s_q ? 0
-                      : hsteps > 0 ? cdiv64(hsteps * cdiv64(s_q - qbeg, qgran), qc)
-                                   : cdiv64(s_q - qbeg, qc);
+  const int64_t nch = cdiv64(dv_tile_steps(key / geo.kt, s_q, s_kv, grp, causal, geo), cs);
   // up to 8 chunk partials in flight, added in chunk order (an index past
   // the last chunk re-reads chunk 0 and its term is dropped)
   const int n = (int)(nch < cmax ? nch : cmax);
@@ -724,19 +768,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_bf16_kernel(
 
 constexpr int HV_QT = 64;   // queries per step, bf16 dv kernel
 constexpr int HV_KT = 128;  // keys per workgroup, bf16 dv kernel
-
-// Steps (head, 64-query block) of key tile j: the causal mask starts its
-// query range at the first row that sees the tile's first key.
-__host__ __device__ __forceinline__ int64_t dv_tile_qbeg(int64_t j, int64_t s_q, int64_t s_kv,
-                                                         int causal) {
-  int64_t qbeg = causal ? j * HV_KT - (s_kv - s_q) : 0;
-  return qbeg < 0 ? 0 : qbeg / HV_QT * HV_QT;
-}
-__host__ __device__ __forceinline__ int64_t dv_tile_steps(int64_t j, int64_t s_q, int64_t s_kv,
-                                                          int64_t grp, int causal) {
-  const int64_t qbeg = dv_tile_qbeg(j, s_q, s_kv, causal);
-  return qbeg >= s_q ? 0 : grp * ((s_q - qbeg + HV_QT - 1) / HV_QT);
-}
+constexpr DvGeo HV_GEO{HV_KT, HV_QT, HV_QT};
 
 template <int D, bool PVEC>
 __global__ __launch_bounds__(256, 2) void attn_dv_bf16_kernel(int64_t s_q, int64_t s_kv, int Hq,
@@ -754,39 +786,13 @@ __global__ __launch_bounds__(256, 2) void attn_dv_bf16_kernel(int64_t s_q, int64
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l16 = lane & 15, c = lane >> 4;
-  // Work item: a chunk of cs steps of key tile jt for KV group g.  Items
-  // are numbered full chunks first (every tile's, in tile order), then the
-  // tiles' shorter last chunks; the group varies fastest.  Workgroups go to
-  // the XCDs round-robin in launch order, so each XCD gets an even share of
-  // the long items.
   const int Hkv = Hq / grp;
-  const int64_t nt = cdiv64(s_kv, KT);
-  int64_t L = blockIdx.x;
-  const int g = (int)(L % Hkv);
-  int64_t r = L / Hkv;
-  int64_t jt = 0, ch = 0;
-  if (r < nfull) {
-    for (; jt < nt; ++jt) {
-      const int64_t nf = dv_tile_steps(jt, s_q, s_kv, grp, causal) / cs;
-      if (r < nf) break;
-      r -= nf;
-    }
-    ch = r;
-  } else {
-    r -= nfull;
-    for (; jt < nt; ++jt) {
-      const int64_t ts = dv_tile_steps(jt, s_q, s_kv, grp, causal);
-      if (ts % cs != 0) {
-        if (r == 0) break;
-        --r;
-      }
-    }
-    if (jt < nt) ch = dv_tile_steps(jt, s_q, s_kv, grp, causal) / cs;
-  }
-  if (jt >= nt) return;  // no such item (the launch never makes one)
+  int g;
+  int64_t jt, ch;
+  if (!dv_item(blockIdx.x, Hkv, s_q, s_kv, grp, causal, HV_GEO, cs, nfull, g, jt, ch)) return;
   const int64_t ldk = (int64_t)Hkv * D;
   const int64_t k0 = jt * KT;
-  const int64_t qbeg = dv_tile_qbeg(jt, s_q, s_kv, causal);
+  const int64_t qbeg = dv_tile_qbeg(jt, s_q, s_kv, causal, HV_GEO);
   // the tile's steps (head, 64-query block), head-major; chunk ch takes
   // steps [ch cs, ch cs + cs)
   const int64_t nqb = cdiv64(s_q - qbeg, QT);
@@ -1112,46 +1118,32 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(int64_t s_q, int64_t s_
   if (lane == 0) delta[(int64_t)h * s_q + i] = s;
 }
 
-// Query chunking of the dv kernels: about DV_WG_TARGET workgroups
-// (key tiles x KV groups x chunks), chunks a multiple of 16 rows.
-constexpr int DV_WG_TARGET = 512;
+// Work chunking of the dv kernels (see dv_item).  Key tile j has T_j steps,
+// fewer for later tiles under the causal mask; a chunk is cs steps, the
+// smallest count with which all chunks fit in `target` workgroups, so no
+// chunk is much longer than the others.
 struct DvPlan {
-  int cmax;
-  int64_t qc;
-  int64_t nfull, items;  // bf16 kernel: full chunks per KV group, work items
+  int cmax;              // chunks of the longest tile
+  int64_t cs;            // steps per chunk
+  int64_t nfull, items;  // full chunks per KV group, work items
 };
-static DvPlan dv_plan(int64_t s_q, int64_t s_kv, int64_t Hkv) {
-  DvPlan p{};
-  const int64_t tiles = cdiv64(s_kv, DV_KT) * Hkv;
-  int64_t want = cdiv64(DV_WG_TARGET, tiles < 1 ? 1 : tiles);
-  const int64_t maxc = cdiv64(s_q < 1 ? 1 : s_q, 16);
-  want = want < 1 ? 1 : (want > maxc ? maxc : want);
-  p.qc = cdiv64(cdiv64(s_q < 1 ? 1 : s_q, want), 16) * 16;
-  p.cmax = (int)cdiv64(s_q < 1 ? 1 : s_q, p.qc);
-  return p;
-}
-
-// Work chunking of the bf16 dv kernel.  Key tile j has T_j steps (head,
-// 64-query block), fewer for later tiles under the causal mask; a chunk is
-// qc steps, the smallest count with which every chunk fits in one round of
-// HV_WG_TARGET workgroups, so no chunk is much longer than the others.
-constexpr int HV_WG_TARGET = 512;
-static DvPlan dv_plan_bf16(int64_t s_q, int64_t s_kv, int64_t Hkv, int64_t grp, int causal) {
-  const int64_t sq = s_q < 1 ? 1 : s_q, nt = cdiv64(s_kv, HV_KT);
-  auto steps = [&](int64_t j) { return dv_tile_steps(j, sq, s_kv, grp, causal); };
+constexpr int FV_WG_TARGET = 768, HV_WG_TARGET = 512;
+static DvPlan dv_plan(int64_t s_q, int64_t s_kv, int64_t Hkv, int64_t grp, int causal, DvGeo q,
+                      int64_t target) {
+  const int64_t sq = s_q < 1 ? 1 : s_q, nt = cdiv64(s_kv, q.kt);
+  auto steps = [&](int64_t j) { return dv_tile_steps(j, sq, s_kv, grp, causal, q); };
   const int64_t tmax = steps(0) > 0 ? steps(0) : 1;
   DvPlan p{};
   for (int64_t cs = 4;; ++cs) {
     int64_t n = 0;
     for (int64_t j = 0; j < nt; ++j) n += cdiv64(steps(j), cs);
-    if (n * Hkv <= HV_WG_TARGET || cs >= tmax) {
-      p.qc = cs < tmax ? cs : tmax;
-      p.cmax = (int)cdiv64(tmax, p.qc);
-      p.nfull = 0;
+    if (n * Hkv <= target || cs >= tmax) {
+      p.cs = cs < tmax ? cs : tmax;
+      p.cmax = (int)cdiv64(tmax, p.cs);
       int64_t np = 0;
       for (int64_t j = 0; j < nt; ++j) {
-        p.nfull += steps(j) / p.qc;
-        np += steps(j) % p.qc != 0;
+        p.nfull += steps(j) / p.cs;
+        np += steps(j) % p.cs != 0;
       }
       p.items = (p.nfull + np) * Hkv;
       return p;
@@ -1173,12 +1165,11 @@ static AttnWs attn_ws(int64_t s_q, int64_t s_kv, int64_t Hq, int64_t Hkv, int64_
   AttnWs w;
   const bool hb = bf16_mfma_path(dt, D);
   // sized for the larger chunk count of the causal and the full mask
-  DvPlan dp = dv_plan(s_q, s_kv, Hkv);
-  if (hb) {
-    const DvPlan c1 = dv_plan_bf16(s_q, s_kv, Hkv, Hq / Hkv, 1);
-    const DvPlan c0 = dv_plan_bf16(s_q, s_kv, Hkv, Hq / Hkv, 0);
-    dp = c1.cmax > c0.cmax ? c1 : c0;
-  }
+  const DvGeo geo = hb ? HV_GEO : FV_GEO;
+  const int64_t tgt = hb ? HV_WG_TARGET : FV_WG_TARGET;
+  const DvPlan c1 = dv_plan(s_q, s_kv, Hkv, Hq / Hkv, 1, geo, tgt);
+  const DvPlan c0 = dv_plan(s_q, s_kv, Hkv, Hq / Hkv, 0, geo, tgt);
+  const DvPlan dp = c1.cmax > c0.cmax ? c1 : c0;
   w.LK = cdiv64(s_kv, 64) * 64;
   w.LQ = cdiv64(s_q, 64) * 64;
   w.delta = 0;
@@ -1283,17 +1274,16 @@ static hipError_t attn_launch_f32(int64_t s_q, int64_t s_kv, int Hq, int Hkv, co
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (dv == nullptr) return hipSuccess;
-  const DvPlan dp = dv_plan(s_q, s_kv, Hkv);
+  const DvPlan dp = dv_plan(s_q, s_kv, Hkv, grp, causal, FV_GEO, FV_WG_TARGET);
   float* part = dp.cmax > 1 ? (float*)((char*)ws + wl.part) : dv;
-  const dim3 grid((unsigned)(cdiv64(s_kv, DV_KT) * dp.cmax), (unsigned)Hkv);
-  attn_dv_f32_kernel<D><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dp.cmax, dp.qc, dctx, P, part,
-                                             causal);
+  attn_dv_f32_kernel<D><<<dim3((unsigned)dp.items), 256, 0, s>>>(
+      s_q, s_kv, Hq, grp, dp.cmax, dp.cs, dp.nfull, dctx, P, part, causal);
   mark("attn_dv_f32", pbytes + qbytes + kvbytes * (dp.cmax > 1 ? dp.cmax : 1),
        2.0 * D * pairs * Hq, s);
   if ((e = hipGetLastError()) != hipSuccess || dp.cmax == 1) return e;
   const int64_t n4 = s_kv * Hkv * D / 4;
   attn_dv_reduce_kernel<<<dim3((unsigned)cdiv64(n4, 256)), 256, 0, s>>>(
-      s_q, s_kv, (int64_t)Hkv * D, dp.cmax, dp.qc, part, dv, causal, 16, DV_KT, 0);
+      s_q, s_kv, (int64_t)Hkv * D, dp.cmax, dp.cs, part, dv, causal, grp, FV_GEO);
   mark("attn_dv_reduce", kvbytes * (dp.cmax + 1), 0, s);
   return hipGetLastError();
 }
@@ -1355,21 +1345,21 @@ static hipError_t attn_launch_bf16(int64_t s_q, int64_t s_kv, int Hq, int Hkv, c
                                  0, s>>>(s_q, wl.LQ, (int64_t)Hq * D, dctx, dCt);
   mark("transpose_bf16", qbytes * 4 + (double)Hq * D * wl.LQ * 2, 0, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const DvPlan dp = dv_plan_bf16(s_q, s_kv, Hkv, grp, causal);
+  const DvPlan dp = dv_plan(s_q, s_kv, Hkv, grp, causal, HV_GEO, HV_WG_TARGET);
   float* part = dp.cmax > 1 ? (float*)(wb + wl.part) : dv;
   const dim3 grid((unsigned)dp.items);
   if (s_kv % 8 == 0)
-    attn_dv_bf16_kernel<D, true><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dp.cmax, dp.qc, dp.nfull,
+    attn_dv_bf16_kernel<D, true><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dp.cmax, dp.cs, dp.nfull,
                                                       wl.LQ, P, dCt, part, causal);
   else
-    attn_dv_bf16_kernel<D, false><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dp.cmax, dp.qc,
+    attn_dv_bf16_kernel<D, false><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dp.cmax, dp.cs,
                                                        dp.nfull, wl.LQ, P, dCt, part, causal);
   mark("attn_dv_bf16", pbytes + qbytes * 2 + kvbytes * 4 * (dp.cmax > 1 ? dp.cmax : 1),
        2.0 * D * pairs * Hq, s);
   if ((e = hipGetLastError()) != hipSuccess || dp.cmax == 1) return e;
   const int64_t n4 = s_kv * Hkv * D / 4;
   attn_dv_reduce_kernel<<<dim3((unsigned)cdiv64(n4, 256)), 256, 0, s>>>(
-      s_q, s_kv, (int64_t)Hkv * D, dp.cmax, dp.qc, part, dv, causal, HV_QT, HV_KT, grp);
+      s_q, s_kv, (int64_t)Hkv * D, dp.cmax, dp.cs, part, dv, causal, grp, HV_GEO);
   mark("attn_dv_reduce", kvbytes * 4 * (dp.cmax + 1), 0, s);
   return hipGetLastError();
 }

@@ -4,11 +4,12 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one whole backward of the workload through the C-ABI library:
-the residual-stream gradient is reset from the upstream gradient (one small
-device copy) and lorabwd_layer_backward runs every step of the path (FFN
-backward, O-projection backward, attention backward, inverse RoPE, and, where
-the workload has adapters, LoRA gradients with AdamW) - for `stack36`, all
-36 layers in reverse order.  Inputs are resident in HBM before timing starts;
+lorabwd_layer_backward runs every step of the path (FFN backward,
+O-projection backward, attention backward, inverse RoPE, and, where the
+workload has adapters, LoRA gradients with AdamW) - for `stack36`, all 36
+layers in reverse order.  The top layer reads the upstream gradient (never
+written) and leaves dH1 in a separate buffer, which the layers below update
+in place, so replaying a step needs no reset copy.  Inputs are resident in HBM before timing starts;
 each input copy's step is captured once as a HIP graph and replayed.  Steps
 rotate over enough input copies that HBM-bound work cannot be served from
 the 256 MB Infinity Cache.
@@ -129,11 +130,13 @@ def build_copies(cfg, n_copies, torch):
 
 
 def run_step(lbp, cfg, cp):
-    """One step: reset the residual-stream gradient, then the layers in
-    reverse order (a single layer for one-layer workloads)."""
-    cp["d_hidden"].copy_(cp["d_out"])
-    for d in reversed(cp["layers"]):
-        layer_call(lbp, cfg, d, cp["d_hidden"], gnorm=cp["gnorm"])
+    """One step: the layers in reverse order (a single layer for one-layer
+    workloads).  The top layer reads the upstream gradient d_out, which is
+    never written, and leaves dH1 in d_hidden; the layers below update
+    d_hidden in place."""
+    for li, d in enumerate(reversed(cp["layers"])):
+        layer_call(lbp, cfg, d, cp["d_hidden"], gnorm=cp["gnorm"],
+                   d_out=cp["d_out"] if li == 0 else None)
 
 
 # ------------------------------------------------------------------ roofline
@@ -156,11 +159,11 @@ def kernel_profile(lbp, hip, cfg, copies, torch, reps):
     torch.cuda.synchronize()
     for r in range(reps):
         cp = copies[r % len(copies)]
-        cp["d_hidden"].copy_(cp["d_out"])
         for li, d in enumerate(reversed(cp["layers"])):
             torch.sum(filler, dim=(0,), out=sink)
             hip.record(ev[cap], stream)
             n = layer_call(lbp, cfg, d, cp["d_hidden"], gnorm=cp["gnorm"],
+                           d_out=cp["d_out"] if li == 0 else None,
                            timing=(ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)), recs))
             torch.cuda.synchronize()
             prev = ev[cap]
@@ -271,9 +274,8 @@ def pmc_pass(lbp, hip, cfg, torch, path):
     cap = 128
     ev = hip.events(cap)
     recs = (lbp.KernelRecord * cap)()
-    cp["d_hidden"].copy_(cp["d_out"])
     d = list(reversed(cp["layers"]))[0]
-    n = layer_call(lbp, cfg, d, cp["d_hidden"], gnorm=cp["gnorm"],
+    n = layer_call(lbp, cfg, d, cp["d_hidden"], gnorm=cp["gnorm"], d_out=cp["d_out"],
                    timing=(ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)), recs))
     torch.cuda.synchronize()
     rows = [{"index": i, "name": recs[i].name.decode(), "alg_bytes": recs[i].alg_bytes,

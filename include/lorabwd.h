@@ -248,7 +248,11 @@ typedef struct lorabwd_adamw {
 } lorabwd_adamw;
 
 size_t lorabwd_layer_workspace_size(const lorabwd_layer_desc* d);
-/* d_hidden  f32 [seq, hidden]  in: gradient of the layer output; out: dH1.
+/* d_out     f32 [seq, hidden] or NULL: gradient of the layer output.  Read
+ *           only; it must not overlap d_hidden.
+ * d_hidden  f32 [seq, hidden]  out: dH1, the gradient at the layer input's
+ *           residual stream.  With d_out NULL it is also the input (the
+ *           gradient of the layer output, overwritten in place).
  * q_state / v_state: NULL (or rank 0) = no adapter on that projection.
  * dq_pre_out f32 [seq, n_heads*head_dim] or NULL: the LoRA Q signal (dL/d q_pre).
  * dv_out     f32 [kv_len, n_kv_heads*head_dim] or NULL: dL/dV.
@@ -257,8 +261,9 @@ size_t lorabwd_layer_workspace_size(const lorabwd_layer_desc* d);
 int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w,
                            const lorabwd_layer_saved* a, lorabwd_lora_state* q_state,
                            lorabwd_lora_state* v_state, const lorabwd_adamw* hp,
-                           float* d_hidden, float* dq_pre_out, float* dv_out, float* gnorm_sq,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+                           const float* d_out, float* d_hidden, float* dq_pre_out,
+                           float* dv_out, float* gnorm_sq, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Measurement variant of lorabwd_layer_backward: the same work on the same
@@ -280,9 +285,9 @@ typedef struct lorabwd_kernel_record {
 int lorabwd_layer_backward_timed(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w,
                                  const lorabwd_layer_saved* a, lorabwd_lora_state* q_state,
                                  lorabwd_lora_state* v_state, const lorabwd_adamw* hp,
-                                 float* d_hidden, float* dq_pre_out, float* dv_out,
-                                 float* gnorm_sq, void* workspace, size_t workspace_bytes,
-                                 hipStream_t stream, hipEvent_t* events,
+                                 const float* d_out, float* d_hidden, float* dq_pre_out,
+                                 float* dv_out, float* gnorm_sq, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
                                  lorabwd_kernel_record* records, int capacity, int* n_kernels);
 
 #ifdef __cplusplus

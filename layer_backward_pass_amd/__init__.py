@@ -109,11 +109,12 @@ _SIGS = {
     "lorabwd_layer_backward": (c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
                                        ctypes.POINTER(LayerSaved), ctypes.POINTER(LoraState),
                                        ctypes.POINTER(LoraState), ctypes.POINTER(AdamW), c_vp,
-                                       c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+                                       c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "lorabwd_layer_backward_timed": (c_int, [
         ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), ctypes.POINTER(LayerSaved),
         ctypes.POINTER(LoraState), ctypes.POINTER(LoraState), ctypes.POINTER(AdamW), c_vp, c_vp,
-        c_vp, c_vp, c_vp, c_size, c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(KernelRecord), c_int,
+        c_vp, c_vp, c_vp, c_vp, c_size, c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(KernelRecord),
+        c_int,
         ctypes.POINTER(c_int)]),
 }
 
@@ -355,10 +356,11 @@ def make_desc(seq, kv_len, hidden, ffn, n_heads, n_kv_heads, head_dim, act=ACT_S
 
 def lorabwd_layer_backward(desc, weights, saved, d_hidden, q_state=None, v_state=None,
                            adamw=None, dq_pre_out=None, dv_out=None, gnorm_sq=None,
-                           stream=None, timing=None):
+                           stream=None, timing=None, d_out=None):
     """desc: LayerDesc; weights / saved: dicts of tensors keyed like the C
     structs; q_state / v_state: dicts with A, B, m_a, v_a, m_b, v_b (or None);
-    adamw: AdamW or None.  d_hidden is updated in place.
+    adamw: AdamW or None.  d_hidden receives dH1; it is also the input (the
+    gradient of the layer output, updated in place) unless d_out is given.
 
     timing: None, or (events, records) = (ctypes array of hipEvent_t,
     ctypes array of KernelRecord) to call lorabwd_layer_backward_timed; the
@@ -368,6 +370,8 @@ def lorabwd_layer_backward(desc, weights, saved, d_hidden, q_state=None, v_state
     S, L, H, I = d.seq, d.kv_len, d.hidden, d.ffn
     qd, kvd = d.n_heads * d.head_dim, d.n_kv_heads * d.head_dim
     _f32(d_hidden, "d_hidden", (S, H))
+    if d_out is not None:
+        _f32(d_out, "d_out", (S, H))
     wshapes = {"w_o": (H, qd), "w_gate": (I, H), "w_up": (I, H), "w_down": (H, I)}
     for k, s in wshapes.items():
         _need(weights[k], k, tdt, s)
@@ -409,7 +413,8 @@ def lorabwd_layer_backward(desc, weights, saved, d_hidden, q_state=None, v_state
             ctypes.byref(qs) if qs is not None else None,
             ctypes.byref(vs) if vs is not None else None,
             ctypes.byref(adamw) if adamw is not None else None,
-            _ptr(d_hidden), _ptr(dq_pre_out), _ptr(dv_out), _ptr(gnorm_sq), _ptr(ws), wsb,
+            _ptr(d_out), _ptr(d_hidden), _ptr(dq_pre_out), _ptr(dv_out), _ptr(gnorm_sq),
+            _ptr(ws), wsb,
             _stream(stream))
     if timing is None:
         _check("lorabwd_layer_backward", lib.lorabwd_layer_backward(*args))

@@ -136,7 +136,7 @@ hipError_t ffn_run(int64_t rows, int64_t dim, int64_t ffn, int act, const float*
                    const void* w_down, const void* w_gate, const void* w_up, const void* gate,
                    const void* up_, const void* hidden_pre, const float* gamma_sub,
                    const void* resid1, const float* gamma_ffn, float* d_resid, float eps, int dt,
-                   void* ws, hipStream_t s) {
+                   void* ws, hipStream_t s, const float* resid_in = nullptr) {
   if (rows == 0) return hipSuccess;
   FfnPlan p = ffn_plan(ws, rows, dim, ffn, dt);
   hipError_t e;
@@ -182,12 +182,13 @@ hipError_t ffn_run(int64_t rows, int64_t dim, int64_t ffn, int act, const float*
     g.p.up = up_;
     g.p.act = act;
     if ((e = launch_dgemv(dt, dt, g, s)) != hipSuccess) return e;
-    // 5. d_resid += rmsnorm_bwd(resid1, gamma_ffn, dN2)
+    // 5. d_resid = (resid_in or d_resid) + rmsnorm_bwd(resid1, gamma_ffn, dN2)
     RedArgs r{};
     r.N = dim;
     r.splits = (int)dgemv_splits(dim, 2 * ffn, PRO_ACT);
     r.part = p.part2;
     r.y = d_resid;
+    r.yin = resid_in;
     r.scal = p.scal2;
     r.nscal = dgemv_nscal(dim, 2 * ffn, PRO_ACT);
     r.nx = resid1;
@@ -218,8 +219,9 @@ hipError_t ffn_run(int64_t rows, int64_t dim, int64_t ffn, int act, const float*
   e = launch_gemm(rows, dim, 2 * ffn, p.dgu, dt, 2 * ffn, w_gate, w_up, ffn, dt, dim, p.dn2, dim,
                   p.partials, s);
   if (e != hipSuccess) return e;
-  // 5. d_resid += rmsnorm_bwd(resid1, gamma_ffn, dN2)
-  return launch_rmsnorm_bwd(rows, dim, resid1, dt, gamma_ffn, p.dn2, d_resid, eps, 1, s);
+  // 5. d_resid = (resid_in or d_resid) + rmsnorm_bwd(resid1, gamma_ffn, dN2)
+  return launch_rmsnorm_bwd(rows, dim, resid1, dt, gamma_ffn, p.dn2, d_resid, eps, 1, s, 1, 0,
+                            resid_in);
 }
 
 // ---------------------------------------------------------------- LoRA
@@ -475,8 +477,11 @@ LayerPlan layer_plan(void* ws, const lorabwd_layer_desc* d, int64_t rq, int64_t 
 // The single-token layer: three weight streams, each followed by a light
 // reduction that also applies the elementwise step after it (decode.hip).
 hipError_t decode_chain(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w,
-                        const lorabwd_layer_saved* a, const LayerPlan& p, float* d_hidden,
-                        float* dqp, float* dv, hipStream_t s) {
+                        const lorabwd_layer_saved* a, const LayerPlan& p, const float* d_in,
+                        float* d_hidden, float* dqp, float* dv, hipStream_t s) {
+  // d_in: the layer output's gradient; d_hidden receives dH1 (d_in == d_hidden
+  // in place: then dH1 waits in x2 until W_o's prologue has read d_in)
+  const bool inplace = d_in == d_hidden;
   const int64_t L = d->kv_len, H = d->hidden, I = d->ffn;
   const int64_t qd = d->n_heads * d->head_dim;
   const int dt = d->dtype;
@@ -488,7 +493,7 @@ hipError_t decode_chain(const lorabwd_layer_desc* d, const lorabwd_layer_weights
   g.N = I;
   g.K = H;
   g.W1 = w->w_down;
-  g.x = d_hidden;
+  g.x = d_in;
   g.part = part13;
   if (sub) {
     g.ng = w->gamma_fsub;
@@ -546,11 +551,11 @@ hipError_t decode_chain(const lorabwd_layer_desc* d, const lorabwd_layer_weights
   g.p.nx = a->resid1;
   g.p.ngam = w->gamma_ffn;
   g.p.eps = d->eps;
-  g.p.resid = d_hidden;
-  g.p.xout = p.x2;
+  g.p.resid = d_in;
+  g.p.xout = inplace ? p.x2 : d_hidden;
   if ((e = launch_dgemv(dt, dt, g, s)) != hipSuccess) return e;
-  // dCtx (sub-norm backward applied); the same launch moves dH1 into the
-  // caller's d_hidden, whose old contents W_o's prologue has consumed
+  // dCtx (sub-norm backward applied); in place, the same launch moves dH1
+  // into the caller's d_hidden, whose old contents W_o's prologue has consumed
   RedArgs r{};
   r.N = qd;
   r.splits = (int)dgemv_splits(qd, H, PRO_RESID);
@@ -563,9 +568,11 @@ hipError_t decode_chain(const lorabwd_layer_desc* d, const lorabwd_layer_weights
     r.ngam = w->gamma_asub;
     r.eps = d->eps;
   }
-  r.copy_src = p.x2;
-  r.copy_dst = d_hidden;
-  r.copy_n = H;
+  if (inplace) {
+    r.copy_src = p.x2;
+    r.copy_dst = d_hidden;
+    r.copy_n = H;
+  }
   if ((e = launch_dgemv_red(RED_STORE, dt, r, s)) != hipSuccess) return e;
   // attention backward, inverse RoPE at the token's position
   DecAttnArgs at{};
@@ -616,9 +623,9 @@ size_t lorabwd_layer_workspace_size(const lorabwd_layer_desc* d) {
 
 int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w,
                            const lorabwd_layer_saved* a, lorabwd_lora_state* qs,
-                           lorabwd_lora_state* vs, const lorabwd_adamw* hp, float* d_hidden,
-                           float* dq_pre_out, float* dv_out, float* gnorm_sq, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream) {
+                           lorabwd_lora_state* vs, const lorabwd_adamw* hp, const float* d_out,
+                           float* d_hidden, float* dq_pre_out, float* dv_out, float* gnorm_sq,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = desc_validate(d);
   if (st != LORABWD_OK) return st;
   LBP_CHECK(w && a, LORABWD_ERR_NULL);
@@ -639,7 +646,11 @@ int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weig
   if (sub) LBP_CHECK(w->gamma_fsub && w->gamma_asub && a->hidden_pre && a->ctx, LORABWD_ERR_NULL);
   if (S == 0) return LORABWD_OK;
   LBP_CHECK(d_hidden && w->w_o, LORABWD_ERR_NULL);
-  st = ffn_validate(S, H, I, d->act, d_hidden, w->w_down, w->w_gate, w->w_up, a->gate, a->up,
+  const float* din = d_out ? d_out : d_hidden;
+  LBP_CHECK(aligned16(din), LORABWD_ERR_ALIGN);
+  LBP_CHECK(din == d_hidden || !overlap(din, (size_t)S * H * 4, d_hidden, (size_t)S * H * 4),
+            LORABWD_ERR_ALIAS);
+  st = ffn_validate(S, H, I, d->act, din, w->w_down, w->w_gate, w->w_up, a->gate, a->up,
                     sub ? a->hidden_pre : nullptr, sub ? w->gamma_fsub : nullptr, a->resid1,
                     w->gamma_ffn, d_hidden, d->eps, dt);
   if (st != LORABWD_OK) return st;
@@ -679,12 +690,13 @@ int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weig
 
   // ---- all arguments valid: enqueue
   if (use_decode_chain(d)) {
-    LBP_HIP(decode_chain(d, w, a, plan, d_hidden, dqp, dv, stream));
+    LBP_HIP(decode_chain(d, w, a, plan, din, d_hidden, dqp, dv, stream));
   } else {
-    // FFN half, residual-stream gradient in place: d_hidden <- dH1
-    LBP_HIP(ffn_run(S, H, I, d->act, d_hidden, w->w_down, w->w_gate, w->w_up, a->gate, a->up,
+    // FFN half, residual-stream gradient: d_hidden <- dH1
+    LBP_HIP(ffn_run(S, H, I, d->act, din, w->w_down, w->w_gate, w->w_up, a->gate, a->up,
                     sub ? a->hidden_pre : nullptr, sub ? w->gamma_fsub : nullptr, a->resid1,
-                    w->gamma_ffn, d_hidden, d->eps, dt, plan.scratch, stream));
+                    w->gamma_ffn, d_hidden, d->eps, dt, plan.scratch, stream,
+                    din == d_hidden ? nullptr : din));
     // O-projection backward: dCtx = dH1 W_o
     if (S == 1) {
       GemvArgs g{};
@@ -733,16 +745,17 @@ int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weig
 int lorabwd_layer_backward_timed(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w,
                                  const lorabwd_layer_saved* a, lorabwd_lora_state* q_state,
                                  lorabwd_lora_state* v_state, const lorabwd_adamw* hp,
-                                 float* d_hidden, float* dq_pre_out, float* dv_out,
-                                 float* gnorm_sq, void* workspace, size_t workspace_bytes,
-                                 hipStream_t stream, hipEvent_t* events,
+                                 const float* d_out, float* d_hidden, float* dq_pre_out,
+                                 float* dv_out, float* gnorm_sq, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
                                  lorabwd_kernel_record* records, int capacity, int* n_kernels) {
   LBP_CHECK(capacity >= 0, LORABWD_ERR_ARG);
   LBP_CHECK(capacity == 0 || (events != nullptr && records != nullptr), LORABWD_ERR_NULL);
   Recorder rec{events, records, capacity, 0};
   tl_recorder = &rec;
-  const int st = lorabwd_layer_backward(d, w, a, q_state, v_state, hp, d_hidden, dq_pre_out,
-                                        dv_out, gnorm_sq, workspace, workspace_bytes, stream);
+  const int st = lorabwd_layer_backward(d, w, a, q_state, v_state, hp, d_out, d_hidden,
+                                        dq_pre_out, dv_out, gnorm_sq, workspace, workspace_bytes,
+                                        stream);
   tl_recorder = nullptr;
   if (n_kernels) *n_kernels = rec.count;
   return st;

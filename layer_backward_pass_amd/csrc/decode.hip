@@ -387,7 +387,7 @@ __global__ __launch_bounds__(256) void dgemv_red_kernel(RedArgs a) {
     upv = BufVec<TA>::load(make_brsrc(a.up, (uint32_t)(a.N * es)), eo);
   }
   float4 prev = make_float4(0, 0, 0, 0);
-  if (MODE == RED_ACCUM) prev = bload_f4(make_brsrc(a.y, rowb), eo4);
+  if (MODE == RED_ACCUM) prev = bload_f4(make_brsrc(a.yin ? a.yin : a.y, rowb), eo4);
   const int64_t ci = (int64_t)blockIdx.x * 256 + t;
   float cv = 0.f;
   if (a.copy_n > 0)

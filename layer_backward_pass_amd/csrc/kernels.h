@@ -19,10 +19,12 @@ enum ActKind { SWIGLU = 0, RELU2 = 1 };
 
 // ---- row-wise kernels (rowwise.hip)
 // dy may be `nparts` split-K partial sums [nparts][rows][n] (stride pstride),
-// added in order; dx may alias dy when nparts == 1.
+// added in order; dx may alias dy when nparts == 1.  accumulate: dx = rin +
+// result (rin NULL: dx += result).
 hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, const float* gamma,
                               const float* dy, float* dx, float eps, int accumulate,
-                              hipStream_t s, int nparts = 1, int64_t pstride = 0);
+                              hipStream_t s, int nparts = 1, int64_t pstride = 0,
+                              const float* rin = nullptr);
 hipError_t launch_rope_bwd(int64_t rows, int64_t n_heads, int64_t head_dim, const float* dy,
                            float* dx, int64_t pos0, float base, hipStream_t s);
 // dgu[r, 0:I] = dGate, dgu[r, I:2I] = dUp; out_dt selects float or bf16 output;
@@ -97,7 +99,7 @@ struct GemvArgs {
 //   scal set: z = rmsnorm_bwd(nx, ngam, y) with row sums from the nscal
 //             shares in scal; else z = y
 //   RED_STORE  y_out[n] = z
-//   RED_ACCUM  y_out[n] += z                      (residual skip)
+//   RED_ACCUM  y_out[n] = (yin ? yin : y_out)[n] + z   (residual skip)
 //   RED_ACT    y_out[n] = dGate(z), y_out[N + n] = dUp(z) from gate, up
 enum RedMode { RED_STORE = 0, RED_ACCUM = 1, RED_ACT = 2 };
 struct RedArgs {
@@ -105,6 +107,7 @@ struct RedArgs {
   int splits;
   const float* part;
   float* y;
+  const float* yin;  // RED_ACCUM: the residual term (NULL: y itself)
   const float* scal;
   int64_t nscal;
   const void* nx;

@@ -12,7 +12,7 @@ namespace lbp {
 // Backward GPU Kernels", section "RMSNorm Backward":
 //   dx = (1/r) (dy*gamma - x <dy*gamma, x> / (n r^2)),  r = sqrt(mean(x^2)+eps)
 // Pass 1 reduces sum(x^2) and <dy*gamma, x> over the row; pass 2 writes dx
-// (or adds to it).  Each thread re-reads only the elements it read in pass
+// (or adds it to dx, or to a separate residual input rin).  Each thread re-reads only the elements it read in pass
 // 1, so dx may alias dy.  dy may arrive as `nparts` split-K partial sums
 // (stride pstride), added here in split order.
 __device__ __forceinline__ float4 sum_parts4(const float* p, int nparts, int64_t pstride) {
@@ -41,7 +41,8 @@ template <typename T, int ACC>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int64_t n, const T* __restrict__ x,
                                                           const float* __restrict__ gamma,
                                                           const float* dy, float* dx,
-                                                          float eps, int nparts, int64_t pstride) {
+                                                          float eps, int nparts, int64_t pstride,
+                                                          const float* rin) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const T* xr = x + row * n;
@@ -72,7 +73,8 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int64_t n, const T* __
     o.w = (dv.w * gv.w - xv.w * c) * inv_r;
     float4* dp = reinterpret_cast<float4*>(dxr + i);
     if (ACC) {
-      float4 p = *dp;
+      // the residual term: dx itself, or the separate input rin
+      const float4 p = *reinterpret_cast<const float4*>((rin ? rin + row * n : dxr) + i);
       o.x += p.x;
       o.y += p.y;
       o.z += p.z;
@@ -84,19 +86,19 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int64_t n, const T* __
 
 hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, const float* gamma,
                               const float* dy, float* dx, float eps, int accumulate,
-                              hipStream_t s, int nparts, int64_t pstride) {
+                              hipStream_t s, int nparts, int64_t pstride, const float* rin) {
   if (rows == 0) return hipSuccess;
   dim3 grid((unsigned)rows), block(256);
   if (xdt == F32) {
     if (accumulate)
-      rmsnorm_bwd_kernel<float, 1><<<grid, block, 0, s>>>(n, (const float*)x, gamma, dy, dx, eps, nparts, pstride);
+      rmsnorm_bwd_kernel<float, 1><<<grid, block, 0, s>>>(n, (const float*)x, gamma, dy, dx, eps, nparts, pstride, rin);
     else
-      rmsnorm_bwd_kernel<float, 0><<<grid, block, 0, s>>>(n, (const float*)x, gamma, dy, dx, eps, nparts, pstride);
+      rmsnorm_bwd_kernel<float, 0><<<grid, block, 0, s>>>(n, (const float*)x, gamma, dy, dx, eps, nparts, pstride, rin);
   } else {
     if (accumulate)
-      rmsnorm_bwd_kernel<bf16, 1><<<grid, block, 0, s>>>(n, (const bf16*)x, gamma, dy, dx, eps, nparts, pstride);
+      rmsnorm_bwd_kernel<bf16, 1><<<grid, block, 0, s>>>(n, (const bf16*)x, gamma, dy, dx, eps, nparts, pstride, rin);
     else
-      rmsnorm_bwd_kernel<bf16, 0><<<grid, block, 0, s>>>(n, (const bf16*)x, gamma, dy, dx, eps, nparts, pstride);
+      rmsnorm_bwd_kernel<bf16, 0><<<grid, block, 0, s>>>(n, (const bf16*)x, gamma, dy, dx, eps, nparts, pstride, rin);
   }
   mark("rmsnorm_bwd",
        (double)rows * n * ((xdt == F32 ? 4 : 2) + 4 * nparts + 4 + (accumulate ? 4 : 0)) + n * 4.0,

@@ -147,14 +147,14 @@ class DeviceLayer:
         c = self.cfg
         return lbp.AdamW(c.lr, c.lr_b, c.beta1, c.beta2, c.adam_eps, c.weight_decay, c.step)
 
-    def run_gpu(self, d_hidden, dq_pre=None, dv=None, gnorm=None):
+    def run_gpu(self, d_hidden, dq_pre=None, dv=None, gnorm=None, d_out=None):
         import layer_backward_pass_amd as lbp
         return lbp.lorabwd_layer_backward(
             self.desc(), self.w, self.saved, d_hidden,
             q_state=self.lora["q"] if self.lora else None,
             v_state=self.lora["v"] if self.lora else None,
             adamw=self.adamw() if self.lora else None, dq_pre_out=dq_pre, dv_out=dv,
-            gnorm_sq=gnorm)
+            gnorm_sq=gnorm, d_out=d_out)
 
     def run_oracle(self, d_out):
         return OB.layer_bwd(f32_scalars(self.cfg), self.o_w, self.o_saved, d_out, self.o_lora)

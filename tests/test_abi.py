@@ -181,17 +181,20 @@ def test_layer_validation(lib):
     f = lib.lorabwd_layer_backward
     r = ctypes.byref
     dh = fake(50)
-    assert f(r(bad), r(w), r(a), None, None, None, dh, None, None, None, fake(60), ws, None) == ESHAPE
-    assert f(r(d), r(w), r(a), r(st), None, r(hp), dh, None, None, None, fake(60), ws, None) == ESTEP
+    assert f(r(bad), r(w), r(a), None, None, None, None, dh, None, None, None, fake(60), ws, None) == ESHAPE
+    assert f(r(d), r(w), r(a), r(st), None, r(hp), None, dh, None, None, None, fake(60), ws, None) == ESTEP
     hp.step = 1
-    assert f(r(d), r(w), r(a), r(st), None, None, dh, None, None, None, fake(60), ws, None) == ENULL
+    assert f(r(d), r(w), r(a), r(st), None, None, None, dh, None, None, None, fake(60), ws, None) == ENULL
     sub = lbp.make_desc(16, 16, 64, 256, 4, 2, 16, sub_norms=True)
-    assert f(r(sub), r(w), r(a), None, None, None, dh, None, None, None, fake(60), ws, None) == ENULL
-    assert f(r(d), r(w), r(a), r(st), None, r(hp), dh, None, None, None, fake(60), ws - 1, None) == EWS
-    assert f(r(d), r(w), r(a), r(st), None, r(hp), dh, fake(50) + 64, None, None, fake(60), ws,
+    assert f(r(sub), r(w), r(a), None, None, None, None, dh, None, None, None, fake(60), ws, None) == ENULL
+    assert f(r(d), r(w), r(a), r(st), None, r(hp), None, dh, None, None, None, fake(60), ws - 1, None) == EWS
+    assert f(r(d), r(w), r(a), r(st), None, r(hp), None, dh, fake(50) + 64, None, None, fake(60), ws,
+             None) == EALIAS
+    # a separate input must not overlap the output
+    assert f(r(d), r(w), r(a), None, None, None, fake(50) + 256, dh, None, None, None, fake(60), ws,
              None) == EALIAS
     d.kv_len = 8                                  # kv_len < seq
-    assert f(r(d), r(w), r(a), None, None, None, dh, None, None, None, fake(60), ws, None) == ESHAPE
+    assert f(r(d), r(w), r(a), None, None, None, None, dh, None, None, None, fake(60), ws, None) == ESHAPE
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -261,6 +261,39 @@ def test_layer_small(name, over):
     assert not bad, bad
 
 
+@pytest.mark.parametrize("name,over", [
+    ("decode", {"hidden": 256, "ffn": 512, "n_heads": 8, "n_kv_heads": 2, "head_dim": 64,
+                "kv_len": 300, "pos0": 299}),
+    ("tiny", {"seq": 45, "kv_len": 45}),
+    ("tiny", {"dtype": "bf16"}),
+])
+def test_layer_out_of_place(name, over):
+    """A separate d_out gives bitwise the in-place results and is not written."""
+    cfg = synth.get_config(name).with_(**over)
+    outs = []
+    for oop in (False, True):
+        dl = Hn.DeviceLayer(cfg, 0, DEV)
+        dq = torch.empty(cfg.seq, cfg.q_dim, device=DEV)
+        dv = torch.empty(cfg.kv_len, cfg.kv_dim, device=DEV)
+        g = torch.zeros(1, device=DEV)
+        if oop:
+            d_in = dl.d_out.clone()
+            d = torch.full_like(d_in, float("nan"))
+            dl.run_gpu(d, dq, dv, g, d_out=d_in)
+            torch.cuda.synchronize()
+            assert torch.equal(d_in, dl.d_out)
+        else:
+            d = dl.d_out.clone()
+            dl.run_gpu(d, dq, dv, g)
+        torch.cuda.synchronize()
+        o = [d.cpu(), dq.cpu(), dv.cpu(), g.cpu()]
+        if dl.lora:
+            o += [dl.lora[t][k].cpu() for t in ("q", "v") for k in ("A", "B")]
+        outs.append(o)
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
 def test_layer_deterministic():
     cfg = synth.get_config("tiny").with_(seq=70, kv_len=70)
     outs = []

@@ -252,6 +252,12 @@ def test_lora_adamw(rows, H, out, rank, step, dt):
                 "kv_len": 97, "pos0": 96, "sub_norms": 0, "act": "swiglu"}),
     ("seq512", {"seq": 80, "kv_len": 80, "hidden": 256, "ffn": 512, "n_heads": 4,
                 "n_kv_heads": 1, "head_dim": 64, "rank": 8, "alpha": 16.0}),
+    # bf16 sequence attention with the inverse RoPE in the dq kernel, late positions
+    ("seq512", {"seq": 96, "kv_len": 96, "hidden": 256, "ffn": 512, "n_heads": 8,
+                "n_kv_heads": 2, "head_dim": 64, "rank": 8, "alpha": 16.0, "dtype": "bf16",
+                "pos0": 1900}),
+    ("seq512", {"seq": 70, "kv_len": 70, "hidden": 256, "ffn": 512, "n_heads": 4,
+                "n_kv_heads": 2, "head_dim": 128, "rank": 4, "alpha": 8.0, "pos0": 3000}),
 ])
 def test_layer_small(name, over):
     cfg = synth.get_config(name).with_(**over)

@@ -554,6 +554,43 @@ hipError_t decode_chain(const lorabwd_layer_desc* d, const lorabwd_layer_weights
   g.p.resid = d_in;
   g.p.xout = inplace ? p.x2 : d_hidden;
   if ((e = launch_dgemv(dt, dt, g, s)) != hipSuccess) return e;
+  // attention backward, inverse RoPE at the token's position
+  DecAttnArgs at{};
+  at.s_kv = L;
+  at.Hq = (int)d->n_heads;
+  at.grp = (int)(d->n_heads / d->n_kv_heads);
+  at.dctx = p.dctx;
+  at.P = a->P;
+  at.K = a->K;
+  at.V = a->V;
+  at.ctx = a->ctx;
+  at.dA = p.dA;
+  at.dq_part = p.dA;
+  at.dv = dv;
+  at.dq = dqp;
+  at.scale = d->attn_scale;
+  at.rope = 1;
+  at.pos = d->pos0;
+  at.log2_base = log2((double)d->rope_base);
+  const int wo_splits = (int)dgemv_splits(qd, H, PRO_RESID);
+  if (a->ctx != nullptr && dec_attn_red_fits(d->n_heads, d->n_kv_heads, d->head_dim, wo_splits)) {
+    // the attention launch adds the W_o partials (and applies the sub-norm
+    // backward) itself; in place it also moves dH1 into d_hidden
+    at.part = part13;
+    at.splits = wo_splits;
+    if (sub) {
+      at.nsc = p.scal3;
+      at.nscal = dgemv_nscal(qd, H, PRO_RESID);
+      at.ngam = w->gamma_asub;
+      at.eps = d->eps;
+    }
+    if (inplace) {
+      at.copy_src = p.x2;
+      at.copy_dst = d_hidden;
+      at.copy_n = H;
+    }
+    return launch_dec_attn(dt, (int)d->head_dim, at, s);
+  }
   // dCtx (sub-norm backward applied); in place, the same launch moves dH1
   // into the caller's d_hidden, whose old contents W_o's prologue has consumed
   RedArgs r{};
@@ -574,24 +611,6 @@ hipError_t decode_chain(const lorabwd_layer_desc* d, const lorabwd_layer_weights
     r.copy_n = H;
   }
   if ((e = launch_dgemv_red(RED_STORE, dt, r, s)) != hipSuccess) return e;
-  // attention backward, inverse RoPE at the token's position
-  DecAttnArgs at{};
-  at.s_kv = L;
-  at.Hq = (int)d->n_heads;
-  at.grp = (int)(d->n_heads / d->n_kv_heads);
-  at.dctx = p.dctx;
-  at.P = a->P;
-  at.K = a->K;
-  at.V = a->V;
-  at.ctx = a->ctx;
-  at.dA = p.dA;
-  at.dq_part = p.dA;
-  at.dv = dv;
-  at.dq = dqp;
-  at.scale = d->attn_scale;
-  at.rope = 1;
-  at.pos = d->pos0;
-  at.log2_base = log2((double)d->rope_base);
   return launch_dec_attn(dt, (int)d->head_dim, at, s);
 }
 

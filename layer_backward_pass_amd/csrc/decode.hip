@@ -14,8 +14,11 @@
 //   dgemv<PRO_RESID>  prologue: dN2 for its rows from part2, dH1 = d_out +
 //                     rmsnorm_bwd(resid1, gamma_ffn, dN2); part3 = dH1 W_o
 //                     plus the attention sub-norm shares over ctx
-//   dgemv_red         dCtx = sum of part3, attention sub-norm backward
-//                     applied; dH1 copied to the caller's d_hidden
+//   dec_attn_red      dCtx of the KV group = sum of part3, attention sub-norm
+//                     backward applied (into LDS), then the dec_attn_mfma
+//                     work below; dH1 copied to the caller's d_hidden when
+//                     in place (dgemv_red + dec_attn_mfma where it does not
+//                     fit: grp D > 1024, or no ctx)
 //   dec_attn_mfma     per 16 keys of a KV head (one wave): dA = dCtx V^T,
 //                     dS = P (dA - delta) with delta = dCtx . ctx (the row
 //                     sum of P dA, as the output is P V), dV = P^T dCtx on
@@ -1012,6 +1015,254 @@ __global__ __launch_bounds__(64) void dec_attn_mfma_kernel(DecAttnArgs a) {
   }
 }
 
+// The W_o reduction and the attention in one launch: workgroup = 16 DR_NA
+// keys of one KV group.  All four waves first add the group's dCtx columns
+// from the W_o partials (fixed split order per thread, then the threads of a
+// column quad in order) and apply the attention sub-norm backward with the
+// row sums from the W_o launch's shares; the columns go to LDS.  Then the
+// first DR_NA waves do the dec_attn_mfma work of 16 keys each; their
+// key/value/P loads, which do not depend on dCtx, are issued right after the
+// partials' loads, so the two latencies overlap.  Replaces dgemv_red and a
+// launch boundary (decode step 65.1 -> 64.2 us); every workgroup re-reads
+// its group's partials, so small workgroups (many CUs) pay off.
+constexpr int DR_SPL = 20;  // partials in flight per thread (splits / (256 / quads))
+constexpr int DR_NA = 1;    // waves of a dec_attn_red workgroup that do attention (16 keys each; 1 measured fastest)
+
+// One element of type T at byte offset off (0 when out of range), kept raw
+// until it is converted, so that every load is issued before the first wait.
+template <typename T> struct Buf1;
+template <> struct Buf1<float> {
+  typedef uint32_t raw;
+  static __device__ __forceinline__ raw load(brsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+  }
+  static __device__ __forceinline__ float cvt(raw v) { return __uint_as_float(v); }
+};
+template <> struct Buf1<bf16> {
+  typedef uint16_t raw;
+  static __device__ __forceinline__ raw load(brsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+  }
+  static __device__ __forceinline__ float cvt(raw v) { return bf2f(v); }
+};
+
+bool dec_attn_red_fits(int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int splits) {
+  const int64_t nq = n_heads / n_kv_heads * head_dim / 4;  // column quads of a group
+  return n_heads / n_kv_heads <= 16 && nq <= 256 && 256 % nq == 0 &&
+         splits <= DR_SPL * (256 / nq);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void dec_attn_red_kernel(DecAttnArgs a) {
+  constexpr int DK = D / 4, ND = D / 16;
+  extern __shared__ float4 smem4[];
+  __shared__ float nred[4];
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int l16 = lane & 15, c = lane >> 4;
+  const int g = blockIdx.y, grp = a.grp;
+  const int GC = grp * D, nq = GC / 4, S = 256 / nq;
+  const int64_t qn = (int64_t)a.Hq * D;  // one query row, all heads
+  const int64_t ldk = (int64_t)(a.Hq / grp) * D;
+  float4* red4 = smem4;                         // [256]
+  float* dC = reinterpret_cast<float*>(smem4 + 256);  // [GC]
+  // ---- the group's dCtx partials first: thread (quad q, sub) takes splits
+  // sub, sub + S, ... (one round of DR_SPL loads)
+  const int q = t % nq, sub = t / nq;
+  const brsrc_t rp = make_brsrc(a.part + (int64_t)g * GC, (uint32_t)(((a.splits - 1) * qn + GC) * 4));
+  float4 pv[DR_SPL];
+#pragma unroll
+  for (int u = 0; u < DR_SPL; ++u) {
+    const int sp = sub + S * u;
+    pv[u] = bload_f4(rp, sp < a.splits ? (uint32_t)((sp * qn + 4 * q) * 4) : BUF_OOB);
+  }
+  const bool norm = a.nsc != nullptr;
+  const brsrc_t rn = make_brsrc(norm ? (const void*)a.nsc : (const void*)a.part,
+                                norm ? (uint32_t)(a.nscal * 8) : 0u);
+  float2 sv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t i = t + 256 * u;
+    sv[u] = bload_f2(rn, i < a.nscal ? (uint32_t)(i * 8) : BUF_OOB);
+  }
+  // (buffer loads throughout: a load under a branch would make the compiler
+  // wait for the partials at the join)
+  constexpr uint32_t ES = sizeof(T);
+  typedef typename BufVec<T>::raw R4;
+  typedef typename Buf1<T>::raw R1;
+  const bool nok = norm && t < nq;
+  const R4 nxr = BufVec<T>::load(make_brsrc(norm ? a.ctx : (const void*)a.part, norm ? (uint32_t)(qn * ES) : 0u),
+                                 nok ? (uint32_t)(((int64_t)g * GC + 4 * t) * ES) : BUF_OOB);
+  const float4 ng = bload_f4(make_brsrc(norm ? (const void*)a.ngam : (const void*)a.part, norm ? (uint32_t)(qn * 4) : 0u),
+                             nok ? (uint32_t)(((int64_t)g * GC + 4 * t) * 4) : BUF_OOB);
+  // ---- the workgroup's 16 keys (wave 0): every load that does not need dCtx
+  // (the other waves take out-of-range offsets: no memory is touched)
+  const bool w0 = w < DR_NA;
+  const int64_t kb = ((int64_t)blockIdx.x * DR_NA + w) * DM_KB;
+  const bool hok = w0 && l16 < grp;
+  const int64_t hrow = (int64_t)(g * grp + (hok ? l16 : 0)) * D;
+  const int64_t kr = kb + l16;
+  const bool kok = w0 && kr < a.s_kv;
+  const bool dvh = w0 && c < grp;
+  const brsrc_t rc = make_brsrc(a.ctx, (uint32_t)(qn * ES));
+  const brsrc_t rv = make_brsrc(a.V, (uint32_t)(a.s_kv * ldk * ES));
+  const brsrc_t rk = make_brsrc(a.K, (uint32_t)(a.s_kv * ldk * ES));
+  const brsrc_t rpp = make_brsrc(a.P, (uint32_t)(a.Hq * a.s_kv * ES));
+  R4 yr[DK / 4], vr[DK / 4];
+#pragma unroll
+  for (int i = 0; i < DK / 4; ++i) {
+    yr[i] = BufVec<T>::load(rc, hok ? (uint32_t)((hrow + DK * c + 4 * i) * ES) : BUF_OOB);
+    vr[i] = BufVec<T>::load(rv, kok ? (uint32_t)((kr * ldk + g * D + DK * c + 4 * i) * ES) : BUF_OOB);
+  }
+  R1 pdr[4], kvr[4][ND], par;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int64_t key = kb + 4 * c + v;
+    const bool ok = w0 && key < a.s_kv;
+    pdr[v] = Buf1<T>::load(rpp, (hok && ok) ? (uint32_t)(((int64_t)(g * grp + l16) * a.s_kv + key) * ES) : BUF_OOB);
+#pragma unroll
+    for (int f = 0; f < ND; ++f)
+      kvr[v][f] = Buf1<T>::load(rk, ok ? (uint32_t)((key * ldk + g * D + 16 * f + l16) * ES) : BUF_OOB);
+  }
+  par = Buf1<T>::load(rpp, (a.dv != nullptr && dvh && kok)
+                               ? (uint32_t)(((int64_t)(g * grp + c) * a.s_kv + kr) * ES)
+                               : BUF_OOB);
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- dCtx columns: partial sums, then the sub-norm backward
+  float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int u = 0; u < DR_SPL; ++u) {
+    y.x += pv[u].x;
+    y.y += pv[u].y;
+    y.z += pv[u].z;
+    y.w += pv[u].w;
+  }
+  red4[t] = y;
+  float inv_r = 1.f, cc = 0.f;
+  if (norm) {
+    float dot = 0.f, ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      dot += sv[u].x;
+      ss += sv[u].y;
+    }
+    for (int64_t i0 = t + 1024; i0 < a.nscal; i0 += 256) {
+      const float2 e = *reinterpret_cast<const float2*>(a.nsc + 2 * i0);
+      dot += e.x;
+      ss += e.y;
+    }
+    dot = block_sum<4>(dot, nred);  // its barriers also publish red4
+    ss = block_sum<4>(ss, nred);
+    const float nf = (float)qn;
+    const float r2 = ss / nf + a.eps;
+    inv_r = 1.0f / sqrtf(r2);
+    cc = dot / (nf * r2);
+  } else {
+    __syncthreads();
+  }
+  if (t < nq) {
+    float4 z = red4[t];
+    for (int j = 1; j < S; ++j) {
+      const float4 o = red4[j * nq + t];
+      z.x += o.x;
+      z.y += o.y;
+      z.z += o.z;
+      z.w += o.w;
+    }
+    if (norm) {
+      const float4 xf = BufVec<T>::cvt(nxr);
+      z.x = (z.x * ng.x - xf.x * cc) * inv_r;
+      z.y = (z.y * ng.y - xf.y * cc) * inv_r;
+      z.z = (z.z * ng.z - xf.z * cc) * inv_r;
+      z.w = (z.w * ng.w - xf.w * cc) * inv_r;
+    }
+    *reinterpret_cast<float4*>(dC + 4 * t) = z;
+  }
+  __syncthreads();
+  if (a.copy_n > 0) {
+    const int64_t nwg = (int64_t)gridDim.x * gridDim.y;
+    for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 256 + t; i < a.copy_n; i += nwg * 256)
+      a.copy_dst[i] = a.copy_src[i];
+  }
+  if (!w0) return;
+  // ---- the dec_attn_mfma work, dCtx from LDS
+  float4 xv[DK / 4], yv[DK / 4], vv[DK / 4];
+  float bd[ND], pd[4], kv[4][ND];
+#pragma unroll
+  for (int i = 0; i < DK / 4; ++i) {
+    yv[i] = BufVec<T>::cvt(yr[i]);
+    vv[i] = BufVec<T>::cvt(vr[i]);
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    pd[v] = Buf1<T>::cvt(pdr[v]);
+#pragma unroll
+    for (int f = 0; f < ND; ++f) kv[v][f] = Buf1<T>::cvt(kvr[v][f]);
+  }
+  const float pa = Buf1<T>::cvt(par);
+#pragma unroll
+  for (int i = 0; i < DK / 4; ++i)
+    xv[i] = hok ? *reinterpret_cast<const float4*>(dC + l16 * D + DK * c + 4 * i)
+                : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int f = 0; f < ND; ++f) bd[f] = dvh ? dC[c * D + 16 * f + l16] : 0.f;
+  float dl = 0.f;
+#pragma unroll
+  for (int i = 0; i < DK / 4; ++i)
+    dl += xv[i].x * yv[i].x + xv[i].y * yv[i].y + xv[i].z * yv[i].z + xv[i].w * yv[i].w;
+  dl += __shfl_xor(dl, 16, 64);
+  dl += __shfl_xor(dl, 32, 64);
+  floatx4 da[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) da[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < DK / 4; ++i) {
+    da[0] = mfma16x16x4(vv[i].x, xv[i].x, da[0]);
+    da[1] = mfma16x16x4(vv[i].y, xv[i].y, da[1]);
+    da[2] = mfma16x16x4(vv[i].z, xv[i].z, da[2]);
+    da[3] = mfma16x16x4(vv[i].w, xv[i].w, da[3]);
+  }
+  float ds[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) ds[v] = pd[v] * (((da[0][v] + da[1][v]) + (da[2][v] + da[3][v])) - dl);
+  floatx4 aq[ND];
+#pragma unroll
+  for (int f = 0; f < ND; ++f) aq[f] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+#pragma unroll
+    for (int f = 0; f < ND; ++f) aq[f] = mfma16x16x4(ds[v], kv[v][f], aq[f]);
+  const int64_t nch = (a.s_kv + DM_KB - 1) / DM_KB, chunk = (int64_t)blockIdx.x * DR_NA + w;
+  if (chunk < nch) {
+#pragma unroll
+    for (int f = 0; f < ND; ++f)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int hh = 4 * c + v;
+        if (hh < grp) a.dq_part[((int64_t)(g * grp + hh) * nch + chunk) * D + 16 * f + l16] = aq[f][v];
+      }
+  }
+  if (a.dv != nullptr) {
+#pragma unroll
+    for (int f = 0; f < ND; ++f) {
+      floatx4 av = mfma16x16x4(pa, bd[f], floatx4{0.f, 0.f, 0.f, 0.f});
+      for (int j = 1; 4 * j < grp; ++j) {
+        const int hh = 4 * j + c;
+        const bool ok = hh < grp;
+        const float p2 =
+            (ok && kok) ? Act<T>::ld((const T*)a.P, (int64_t)(g * grp + hh) * a.s_kv + kr) : 0.f;
+        const float b2 = ok ? dC[hh * D + 16 * f + l16] : 0.f;
+        av = mfma16x16x4(p2, b2, av);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t key = kb + 4 * c + v;
+        if (key < a.s_kv) a.dv[key * ldk + g * D + 16 * f + l16] = av[v];
+      }
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(D) void dec_attn_dqc_kernel(DecAttnArgs a, int nchunks) {
   __shared__ float o[D];
@@ -1060,6 +1311,24 @@ static hipError_t dec_attn_launch(const DecAttnArgs& a, hipStream_t s) {
   const double es = sizeof(T);
   const int nch = (int)cdiv(a.s_kv, DA_KC);
   hipError_t e;
+  if (a.part != nullptr) {
+    // the caller checked dec_attn_red_fits and passes ctx
+    if (a.ctx == nullptr || !dec_attn_red_fits(a.Hq, Hkv, D, a.splits) ||
+        (double)a.splits * a.Hq * D * 4 >= BUF_MAX_BYTES || (double)a.nscal * 8 >= BUF_MAX_BYTES)
+      return hipErrorInvalidValue;
+    const int nb = (int)cdiv(a.s_kv, DM_KB);
+    const size_t sm = 256 * sizeof(float4) + (size_t)a.grp * D * sizeof(float);
+    dec_attn_red_kernel<T, D><<<dim3((unsigned)cdiv(nb, DR_NA), (unsigned)Hkv), dim3(256), sm, s>>>(a);
+    mark("dec_attn_red",
+         2.0 * a.s_kv * Hkv * D * es + (double)a.Hq * a.s_kv * es + (double)a.Hq * D * (4 + es) +
+             (a.dv ? (double)a.s_kv * Hkv * D * 4 : 0.0) + (double)a.Hq * nb * D * 4 +
+             (double)a.copy_n * 8,
+         6.0 * D * a.Hq * a.s_kv, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    dec_attn_dqc_kernel<D><<<dim3((unsigned)a.Hq), dim3(D), 0, s>>>(a, nb);
+    mark("dec_attn_dqc", (double)a.Hq * nb * D * 4 + (double)a.Hq * D * 4, 0, s);
+    return hipGetLastError();
+  }
   if (a.ctx != nullptr && a.grp <= 16) {
     const int nb = (int)cdiv(a.s_kv, DM_KB);
     dec_attn_mfma_kernel<T, D><<<dim3((unsigned)nb, (unsigned)Hkv), dim3(64), 0, s>>>(a);

@@ -151,7 +151,23 @@ struct DecAttnArgs {
   int rope;
   int64_t pos;
   double log2_base;
+  // With part set (dec_attn_red_fits), dctx is not read: every workgroup
+  // forms its KV group's dCtx columns from `splits` partial sums
+  // part[splits][Hq D] and, with nsc set, applies the RMSNorm backward over
+  // the concatenated heads (x = ctx, weight ngam, length Hq D) with the row
+  // sums from the nscal share pairs nsc (<y ngam, x>, sum x^2).  copy_n
+  // floats copy_src -> copy_dst are moved on the side.
+  const float* part;
+  int splits;
+  const float* nsc;
+  int64_t nscal;
+  const float* ngam;
+  float eps;
+  const float* copy_src;
+  float* copy_dst;
+  int64_t copy_n;
 };
+bool dec_attn_red_fits(int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int splits);
 bool dec_attn_fits(int64_t s_kv, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim);
 size_t dec_attn_ws_bytes(int64_t s_kv, int64_t n_heads, int64_t head_dim);
 hipError_t launch_dec_attn(int dt, int head_dim, const DecAttnArgs& a, hipStream_t s);

@@ -429,6 +429,7 @@ struct LayerPlan {
   float *dctx, *dq, *dv;
   float *part2, *x2, *scal1, *scal2, *scal3, *dA;  // single-token chain only
   void* scratch;
+  size_t lora_v_off;  // the V adapter's LoRA workspace: scratch + lora_v_off
   size_t bytes;
 };
 
@@ -448,9 +449,11 @@ LayerPlan layer_plan(void* ws, const lorabwd_layer_desc* d, int64_t rq, int64_t 
   p.dctx = c.take<float>((size_t)S * qd * 4);
   p.dq = c.take<float>((size_t)S * qd * 4);
   p.dv = c.take<float>((size_t)L * kvd * 4);
+  // the two adapters run in the same launches, each in its own region
   const size_t lq = rq > 0 ? up(lora_ws_bytes(S, H, qd, rq)) : 0;
   const size_t lv = rv > 0 ? up(lora_ws_bytes(S, H, kvd, rv)) : 0;
-  size_t sc = lq > lv ? lq : lv;
+  size_t sc = lq + lv;
+  p.lora_v_off = lq;
   if (use_decode_chain(d)) {
     p.part2 = c.take<float>(dgemv_part_bytes(H, 2 * I, PRO_ACT));
     p.x2 = c.take<float>((size_t)(2 * I > H ? 2 * I : H) * 4);
@@ -742,21 +745,23 @@ int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weig
                             d->attn_scale, d->causal, plan.scratch, stream));
     LBP_HIP(launch_rope_bwd(S, Hq, D, plan.dq, dqp, d->pos0, d->rope_base, stream));
   }
-  if (lq) {
-    const AdamHP h = make_hp(lr_a, lr_b, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, step);
-    LBP_HIP(launch_lora_adamw(S, H, qd, qs->rank, dqp, a->attn_input, a->lora_q_h, dt, qs->A,
-                              qs->B, qs->m_a, qs->v_a, qs->m_b, qs->v_b, nullptr, nullptr,
-                              gnorm_sq, d->lora_alpha / (float)qs->rank, h, plan.scratch,
-                              stream));
-  }
-  if (lv) {
-    // the adapter sees the value rows of the current tokens: the last S of
+  if (lq || lv) {
+    // both adapters' gradient + AdamW passes in the same launches; the
+    // value adapter sees the value rows of the current tokens: the last S of
     // the kv_len rows (all of them when kv_len == seq)
     const AdamHP h = make_hp(lr_a, lr_b, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, step);
-    LBP_HIP(launch_lora_adamw(S, H, kvd, vs->rank, dv + (L - S) * kvd, a->attn_input,
-                              a->lora_v_h, dt, vs->A, vs->B, vs->m_a, vs->v_a, vs->m_b, vs->v_b,
-                              nullptr, nullptr, gnorm_sq, d->lora_alpha / (float)vs->rank, h,
-                              plan.scratch, stream));
+    LoraJob jobs[2];
+    int nj = 0;
+    if (lq)
+      jobs[nj++] = LoraJob{S, H, qd, qs->rank, dqp, a->attn_input, a->lora_q_h, dt, qs->A, qs->B,
+                           qs->m_a, qs->v_a, qs->m_b, qs->v_b, nullptr, nullptr,
+                           d->lora_alpha / (float)qs->rank, plan.scratch};
+    if (lv)
+      jobs[nj++] = LoraJob{S, H, kvd, vs->rank, dv + (L - S) * kvd, a->attn_input, a->lora_v_h, dt,
+                           vs->A, vs->B, vs->m_a, vs->v_a, vs->m_b, vs->v_b, nullptr, nullptr,
+                           d->lora_alpha / (float)vs->rank,
+                           (char*)plan.scratch + plan.lora_v_off};
+    LBP_HIP(launch_lora_adamw_jobs(jobs, nj, gnorm_sq, h, stream));
   }
   return LORABWD_OK;
 }

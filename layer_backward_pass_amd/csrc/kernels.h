@@ -185,6 +185,21 @@ size_t lora_ws_bytes(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank
 struct AdamHP {
   float lr_a, lr_b, beta1, beta2, eps, wd, bc1, bc2;
 };
+// One adapter's LoRA gradient + AdamW work (ws: its own lora_ws_bytes).
+struct LoraJob {
+  int64_t rows, in_dim, out_dim, rank;
+  const float* dy;
+  const void* x;
+  const void* h;
+  int dt;
+  float *A, *B, *m_a, *v_a, *m_b, *v_b, *grad_a, *grad_b;
+  float scaling;
+  void* ws;
+};
+// Up to two adapters, in the same launches where their shapes allow;
+// gnorm_sq += ||dA||^2 of each, in job order.
+hipError_t launch_lora_adamw_jobs(const LoraJob* jobs, int njobs, float* gnorm_sq,
+                                  const AdamHP& hp, hipStream_t s);
 hipError_t launch_lora_adamw(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank,
                              const float* dy, const void* x, const void* h, int dt, float* A,
                              float* B, float* m_a, float* v_a, float* m_b, float* v_b,

@@ -14,6 +14,12 @@
 // the per-slice partial sums are reduced in a fixed order by the update
 // kernels, so every result is deterministic.  Ranks are padded to a multiple
 // of 16 (the MFMA tile width) with zeros.
+//
+// A layer's two adapters (Q and V) run in the same launches: every kernel
+// takes a pair of argument sets and blockIdx.z picks the adapter; the grid
+// covers the larger of the two and the other's surplus workgroups return.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -24,6 +30,47 @@ constexpr int LG_COLS = 256;   // columns per workgroup
 constexpr int L_TARGET = 256;  // workgroups aimed for per pass
 
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Per-adapter arguments of each pass (gx, gy: that adapter's own grid).
+struct DyArgs {
+  int64_t rows, out_dim, rs;
+  int rank, gx, gy;
+  const float* dy;
+  const void* h;
+  const float* B;
+  float* gpart;
+  float* dbpart;
+};
+struct DaArgs {
+  int64_t rows, in_dim, rs;
+  int rank, gx, gy;
+  const float* g;
+  const void* x;
+  float* dapart;
+};
+struct BUpdArgs {
+  int64_t nb, ng;
+  int slices, groups, nblk;
+  const float* dbpart;
+  const float* gpart;
+  float* g;
+  float s, lr;
+  float *B, *m, *v, *grad_b;
+};
+struct AUpdArgs {
+  int64_t n;
+  int slices, nblk;
+  const float* dapart;
+  float *A, *m, *v, *grad_a;
+  float* sq_part;
+};
+template <typename A>
+struct Pair {
+  A a[2];
+  // the adapter of this workgroup (a select, not an indexed copy of the
+  // kernel arguments)
+  __device__ __forceinline__ const A& pick() const { return blockIdx.z == 0 ? a[0] : a[1]; }
+};
 
 // Four consecutive floats of row `row` starting at column `c`, zero outside
 // [0, rows) x [0, ncol).  VEC: ncol % 4 == 0 and c % 4 == 0, one 16-byte load.
@@ -62,12 +109,16 @@ __device__ __forceinline__ float ld_h(const void* h, int hdt, int64_t e) {
 // dB: rows = 16 features (tile j: o0 + 4m + j), k = tokens; lane loads
 //     dy[i0+4q+l/16][o0+4(l%16)+j].
 template <int RB, bool VEC, typename TH>
-__global__ __launch_bounds__(256) void lora_dy_kernel(int64_t rows, int64_t out_dim, int rank,
-                                                      int64_t rs, const float* __restrict__ dy,
-                                                      const TH* __restrict__ h,
-                                                      const float* __restrict__ Bm,
-                                                      float* __restrict__ gpart,
-                                                      float* __restrict__ dbpart) {
+__global__ __launch_bounds__(256) void lora_dy_kernel(Pair<DyArgs> pa) {
+  const DyArgs& A = pa.pick();
+  if ((int)blockIdx.x >= A.gx || (int)blockIdx.y >= A.gy) return;
+  const int64_t rows = A.rows, out_dim = A.out_dim, rs = A.rs;
+  const int rank = A.rank;
+  const float* __restrict__ dy = A.dy;
+  const TH* __restrict__ h = (const TH*)A.h;
+  const float* __restrict__ Bm = A.B;
+  float* __restrict__ gpart = A.gpart;
+  float* __restrict__ dbpart = A.dbpart;
   constexpr int RP = 16 * RB;
   __shared__ float gs[4][16][RP + 1];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -193,10 +244,14 @@ __global__ __launch_bounds__(256) void lora_dy_kernel(int64_t rows, int64_t out_
 // 16-row steps in flight, loads through buffer ranges (in_dim % 8 == 0, so
 // a 4-feature chunk is whole).
 template <int RB, typename T>
-__global__ __launch_bounds__(256) void lora_da_kernel(int64_t rows, int64_t in_dim, int rank,
-                                                      int64_t rs, const float* __restrict__ g,
-                                                      const T* __restrict__ x,
-                                                      float* __restrict__ dapart) {
+__global__ __launch_bounds__(256) void lora_da_kernel(Pair<DaArgs> pa) {
+  const DaArgs& A = pa.pick();
+  if ((int)blockIdx.x >= A.gx || (int)blockIdx.y >= A.gy) return;
+  const int64_t rows = A.rows, in_dim = A.in_dim, rs = A.rs;
+  const int rank = A.rank;
+  const float* __restrict__ g = A.g;
+  const T* __restrict__ x = (const T*)A.x;
+  float* __restrict__ dapart = A.dapart;
   constexpr int RP = 16 * RB;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int l16 = lane & 15, l4 = lane >> 4;
@@ -286,62 +341,58 @@ __device__ __forceinline__ float sum_strided(const float* __restrict__ p, int n,
   return d;
 }
 
-__global__ __launch_bounds__(256) void lora_b_update_kernel(int64_t nb, int slices,
-                                                            const float* __restrict__ dbpart,
-                                                            int64_t ng, int groups,
-                                                            const float* __restrict__ gpart,
-                                                            float* __restrict__ g, float s,
-                                                            float* B, float* m, float* v,
-                                                            float* grad_b, AdamHP hp) {
+__global__ __launch_bounds__(256) void lora_b_update_kernel(Pair<BUpdArgs> pa, AdamHP hp) {
+  const BUpdArgs& A = pa.pick();
+  if ((int)blockIdx.x >= A.nblk) return;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e < nb) {
-    float d = sum_strided(dbpart + e, slices, nb);
-    d *= s;
-    if (grad_b) grad_b[e] = d;
-    float p = B[e], mm = m[e], vv = v[e];
-    adamw1(p, d, mm, vv, hp.lr_b, hp);
-    B[e] = p;
-    m[e] = mm;
-    v[e] = vv;
-  } else if (e < nb + ng) {
-    const int64_t f = e - nb;
-    g[f] = s * sum_strided(gpart + f, groups, ng);
+  if (e < A.nb) {
+    float d = sum_strided(A.dbpart + e, A.slices, A.nb);
+    d *= A.s;
+    if (A.grad_b) A.grad_b[e] = d;
+    float p = A.B[e], mm = A.m[e], vv = A.v[e];
+    adamw1(p, d, mm, vv, A.lr, hp);
+    A.B[e] = p;
+    A.m[e] = mm;
+    A.v[e] = vv;
+  } else if (e < A.nb + A.ng) {
+    const int64_t f = e - A.nb;
+    A.g[f] = A.s * sum_strided(A.gpart + f, A.groups, A.ng);
   }
 }
 
 // dA = sum_slices dapart, AdamW on A (lr_a), per-workgroup sum of dA^2.
-__global__ __launch_bounds__(256) void lora_a_update_kernel(int64_t n, int slices,
-                                                            const float* __restrict__ dapart,
-                                                            float* A, float* m, float* v,
-                                                            float* grad_a,
-                                                            float* __restrict__ sq_part,
-                                                            AdamHP hp) {
+__global__ __launch_bounds__(256) void lora_a_update_kernel(Pair<AUpdArgs> pa, AdamHP hp) {
   __shared__ float red[4];
+  const AUpdArgs& A = pa.pick();
+  if ((int)blockIdx.x >= A.nblk) return;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   float sq = 0.f;
-  if (e < n) {
-    const float d = sum_strided(dapart + e, slices, n);
-    if (grad_a) grad_a[e] = d;
+  if (e < A.n) {
+    const float d = sum_strided(A.dapart + e, A.slices, A.n);
+    if (A.grad_a) A.grad_a[e] = d;
     sq = d * d;
-    float p = A[e], mm = m[e], vv = v[e];
+    float p = A.A[e], mm = A.m[e], vv = A.v[e];
     adamw1(p, d, mm, vv, hp.lr_a, hp);
-    A[e] = p;
-    m[e] = mm;
-    v[e] = vv;
+    A.A[e] = p;
+    A.m[e] = mm;
+    A.v[e] = vv;
   }
   sq = block_sum<4>(sq, red);
-  if (threadIdx.x == 0) sq_part[blockIdx.x] = sq;
+  if (threadIdx.x == 0) A.sq_part[blockIdx.x] = sq;
 }
 
-// gnorm_sq += sum of the per-workgroup partials, in index order.
-__global__ __launch_bounds__(64) void lora_gnorm_kernel(int nparts,
-                                                        const float* __restrict__ sq_part,
+// gnorm_sq += the per-workgroup partials of adapter 0, then of adapter 1
+// (n1 = 0: none), each summed in index order.
+__global__ __launch_bounds__(64) void lora_gnorm_kernel(int n0, const float* __restrict__ sq0,
+                                                        int n1, const float* __restrict__ sq1,
                                                         float* gnorm_sq) {
   const int lane = threadIdx.x;
-  float s = 0.f;
-  for (int i = lane; i < nparts; i += 64) s += sq_part[i];
-  s = wave_sum(s);
-  if (lane == 0) *gnorm_sq += s;
+  float s0 = 0.f, s1 = 0.f;
+  for (int i = lane; i < n0; i += 64) s0 += sq0[i];
+  for (int i = lane; i < n1; i += 64) s1 += sq1[i];
+  s0 = wave_sum(s0);
+  s1 = wave_sum(s1);
+  if (lane == 0) *gnorm_sq = (*gnorm_sq + s0) + s1;
 }
 
 namespace {
@@ -383,40 +434,124 @@ LoraWs lora_ws(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank) {
   return w;
 }
 
-template <int RB>
-void launch_dy(int64_t rows, int64_t out_dim, int rank, const Slicing& sl, const float* dy,
-               const void* h, int hdt, const float* B, float* gpart, float* dbpart,
-               hipStream_t s) {
-  const dim3 grid((unsigned)sl.groups, (unsigned)sl.slices);
-#define LBP_DY(VEC, TH)                                                                    \
-  lora_dy_kernel<RB, VEC, TH><<<grid, 256, 0, s>>>(rows, out_dim, rank, sl.rs, dy,         \
-                                                   (const TH*)h, B, gpart, dbpart)
-  if (out_dim % 4 == 0) {
-    if (hdt == F32) LBP_DY(true, float);
-    else LBP_DY(true, uint16_t);
-  } else {
-    if (hdt == F32) LBP_DY(false, float);
-    else LBP_DY(false, uint16_t);
-  }
-#undef LBP_DY
-}
-
-template <int RB>
-void launch_da(int64_t rows, int64_t in_dim, int rank, const Slicing& sl, const float* g,
-               const void* x, int dt, float* dapart, hipStream_t s) {
-  const dim3 grid((unsigned)sl.groups, (unsigned)sl.slices);
-  if (dt == F32)
-    lora_da_kernel<RB, float><<<grid, 256, 0, s>>>(rows, in_dim, rank, sl.rs, g,
-                                                   (const float*)x, dapart);
-  else
-    lora_da_kernel<RB, bf16><<<grid, 256, 0, s>>>(rows, in_dim, rank, sl.rs, g,
-                                                  (const bf16*)x, dapart);
-}
-
 }  // namespace
 
 size_t lora_ws_bytes(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank) {
   return (size_t)lora_ws(rows, in_dim, out_dim, rank).end * sizeof(float);
+}
+
+// One launch group: one adapter, or two whose passes share template
+// arguments (rank blocks, dtype, vector path), run in the same launches.
+template <int RB, bool VEC, typename TH>
+static hipError_t lora_group(const LoraJob* const* jobs, int nz, float* gnorm_sq,
+                             const AdamHP& hp, hipStream_t s) {
+  Pair<DyArgs> dy{};
+  Pair<BUpdArgs> bu{};
+  Pair<DaArgs> da{};
+  Pair<AUpdArgs> au{};
+  int gx = 0, gy = 0, bx = 0, ax = 0, dx = 0, dyy = 0;
+  double by_dy = 0, fl_dy = 0, by_b = 0, fl_b = 0, by_da = 0, fl_da = 0, by_a = 0, fl_a = 0;
+  const int64_t rows = jobs[0]->rows;
+  for (int z = 0; z < 2; ++z) {
+    const LoraJob& j = *jobs[z < nz ? z : 0];
+    const LoraWs o = lora_ws(j.rows, j.in_dim, j.out_dim, j.rank);
+    float* const base = (float*)j.ws;
+    const Slicing sy = slicing(j.rows, j.out_dim), sa = slicing(j.rows, j.in_dim);
+    const int64_t rp = 16 * RB;
+    dy.a[z] = DyArgs{j.rows, j.out_dim, sy.rs, (int)j.rank, (int)sy.groups, (int)sy.slices,
+                     j.dy, j.h, j.B, base + o.gpart, base + o.part};
+    const int64_t nb = j.out_dim * j.rank, ng = j.rows > 0 ? j.rows * rp : 0;
+    bu.a[z] = BUpdArgs{nb, ng, (int)sy.slices, (int)sy.groups, (int)cdiv(nb + ng, 256),
+                       base + o.part, base + o.gpart, base + o.g, j.scaling, hp.lr_b,
+                       j.B, j.m_b, j.v_b, j.grad_b};
+    da.a[z] = DaArgs{j.rows, j.in_dim, sa.rs, (int)j.rank, (int)sa.groups, (int)sa.slices,
+                     base + o.g, j.x, base + o.part};
+    au.a[z] = AUpdArgs{j.rank * j.in_dim, (int)sa.slices, (int)cdiv(j.rank * j.in_dim, 256),
+                       base + o.part, j.A, j.m_a, j.v_a, j.grad_a, base + o.sq};
+    if (z >= nz) continue;
+    gx = max(gx, (int)sy.groups);
+    gy = max(gy, (int)sy.slices);
+    bx = max(bx, bu.a[z].nblk);
+    dx = max(dx, (int)sa.groups);
+    dyy = max(dyy, (int)sa.slices);
+    ax = max(ax, au.a[z].nblk);
+    const double esz = j.dt == F32 ? 4.0 : 2.0;
+    by_dy += (double)j.rows * j.out_dim * 4 + (double)j.rows * j.rank * esz + (double)nb * 4;
+    fl_dy += 4.0 * j.rows * j.out_dim * j.rank;
+    by_b += (double)nb * 4 * (6 + (j.grad_b ? 1 : 0)) + (double)ng * 4;
+    fl_b += 12.0 * nb;
+    by_da += (double)j.rows * j.in_dim * esz + (double)j.rows * j.rank * 4;
+    fl_da += 2.0 * j.rows * j.in_dim * j.rank;
+    by_a += (double)j.rank * j.in_dim * 4 * (6 + (j.grad_a ? 1 : 0));
+    fl_a += 14.0 * j.rank * j.in_dim;
+  }
+  hipError_t e;
+  if (rows > 0) {
+    lora_dy_kernel<RB, VEC, TH><<<dim3((unsigned)gx, (unsigned)gy, (unsigned)nz), 256, 0, s>>>(dy);
+    mark("lora_dy", by_dy, fl_dy, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // with no token rows the gradients are zero: no slices, no groups
+  lora_b_update_kernel<<<dim3((unsigned)bx, 1, (unsigned)nz), 256, 0, s>>>(bu, hp);
+  mark("lora_adamw_b", by_b, fl_b, s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (rows > 0) {
+    lora_da_kernel<RB, typename std::conditional<sizeof(TH) == 4, float, bf16>::type>
+        <<<dim3((unsigned)dx, (unsigned)dyy, (unsigned)nz), 256, 0, s>>>(da);
+    mark("lora_da", by_da, fl_da, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  lora_a_update_kernel<<<dim3((unsigned)ax, 1, (unsigned)nz), 256, 0, s>>>(au, hp);
+  mark("lora_adamw_a", by_a, fl_a, s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (gnorm_sq != nullptr) {
+    lora_gnorm_kernel<<<dim3(1), dim3(64), 0, s>>>(au.a[0].nblk, au.a[0].sq_part,
+                                                  nz > 1 ? au.a[1].nblk : 0, au.a[1].sq_part,
+                                                  gnorm_sq);
+    mark("lora_gnorm", 4.0 * (ax * nz) + 8, (double)(ax * nz), s);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+static hipError_t lora_dispatch(const LoraJob* const* jobs, int nz, float* gnorm_sq,
+                                const AdamHP& hp, hipStream_t s) {
+  const LoraJob& j = *jobs[0];
+  const int rb = (int)cdiv(j.rank, 16);
+  const bool vec = j.out_dim % 4 == 0;
+#define LBP_LG(RBV)                                                                    \
+  case RBV:                                                                            \
+    if (vec) {                                                                         \
+      if (j.dt == F32) return lora_group<RBV, true, float>(jobs, nz, gnorm_sq, hp, s);  \
+      return lora_group<RBV, true, uint16_t>(jobs, nz, gnorm_sq, hp, s);               \
+    }                                                                                  \
+    if (j.dt == F32) return lora_group<RBV, false, float>(jobs, nz, gnorm_sq, hp, s);   \
+    return lora_group<RBV, false, uint16_t>(jobs, nz, gnorm_sq, hp, s);
+  switch (rb) {
+    LBP_LG(1)
+    LBP_LG(2)
+    LBP_LG(3)
+    default:
+      LBP_LG(4)
+  }
+#undef LBP_LG
+}
+
+hipError_t launch_lora_adamw_jobs(const LoraJob* jobs, int njobs, float* gnorm_sq,
+                                  const AdamHP& hp, hipStream_t s) {
+  if (njobs <= 0) return hipSuccess;
+  const LoraJob* p[2] = {&jobs[0], njobs > 1 ? &jobs[1] : &jobs[0]};
+  if (njobs == 2) {
+    const LoraJob &a = jobs[0], &b = jobs[1];
+    const bool same = cdiv(a.rank, 16) == cdiv(b.rank, 16) && a.dt == b.dt &&
+                      (a.out_dim % 4 == 0) == (b.out_dim % 4 == 0) && a.rows == b.rows;
+    if (same) return lora_dispatch(p, 2, gnorm_sq, hp, s);
+    hipError_t e = lora_dispatch(p, 1, gnorm_sq, hp, s);
+    if (e != hipSuccess) return e;
+    p[0] = &jobs[1];
+    return lora_dispatch(p, 1, gnorm_sq, hp, s);
+  }
+  return lora_dispatch(p, 1, gnorm_sq, hp, s);
 }
 
 hipError_t launch_lora_adamw(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank,
@@ -424,56 +559,9 @@ hipError_t launch_lora_adamw(int64_t rows, int64_t in_dim, int64_t out_dim, int6
                              float* B, float* m_a, float* v_a, float* m_b, float* v_b,
                              float* grad_a, float* grad_b, float* gnorm_sq, float scaling,
                              const AdamHP& hp, void* ws, hipStream_t s) {
-  const LoraWs o = lora_ws(rows, in_dim, out_dim, rank);
-  float* const base = (float*)ws;
-  struct {
-    float *g, *gpart, *part, *sq;
-  } w = {base + o.g, base + o.gpart, base + o.part, base + o.sq};
-  const Slicing sy = slicing(rows, out_dim), sa = slicing(rows, in_dim);
-  const int r = (int)rank, rb = (int)cdiv(rank, 16);
-  const int64_t rp = 16 * rb;
-  const double esz = dt == F32 ? 4.0 : 2.0;
-  hipError_t e;
-  if (rows > 0) {
-    switch (rb) {
-      case 1: launch_dy<1>(rows, out_dim, r, sy, dy, h, dt, B, w.gpart, w.part, s); break;
-      case 2: launch_dy<2>(rows, out_dim, r, sy, dy, h, dt, B, w.gpart, w.part, s); break;
-      case 3: launch_dy<3>(rows, out_dim, r, sy, dy, h, dt, B, w.gpart, w.part, s); break;
-      default: launch_dy<4>(rows, out_dim, r, sy, dy, h, dt, B, w.gpart, w.part, s); break;
-    }
-    mark("lora_dy", (double)rows * out_dim * 4 + (double)rows * rank * esz + (double)out_dim * rank * 4,
-         4.0 * rows * out_dim * rank, s);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  // with no token rows the gradients are zero: no slices, no groups
-  const int64_t nb = out_dim * rank, ng = rows > 0 ? rows * rp : 0;
-  lora_b_update_kernel<<<dim3((unsigned)cdiv(nb + ng, 256)), 256, 0, s>>>(
-      nb, (int)sy.slices, w.part, ng, (int)sy.groups, w.gpart, w.g, scaling, B, m_b, v_b, grad_b,
-      hp);
-  mark("lora_adamw_b", (double)nb * 4 * (6 + (grad_b ? 1 : 0)) + (double)ng * 4, 12.0 * nb, s);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (rows > 0) {
-    switch (rb) {
-      case 1: launch_da<1>(rows, in_dim, r, sa, w.g, x, dt, w.part, s); break;
-      case 2: launch_da<2>(rows, in_dim, r, sa, w.g, x, dt, w.part, s); break;
-      case 3: launch_da<3>(rows, in_dim, r, sa, w.g, x, dt, w.part, s); break;
-      default: launch_da<4>(rows, in_dim, r, sa, w.g, x, dt, w.part, s); break;
-    }
-    mark("lora_da", (double)rows * in_dim * esz + (double)rows * rank * 4,
-         2.0 * rows * in_dim * rank, s);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  const int nsq = (int)cdiv(rank * in_dim, 256);
-  lora_a_update_kernel<<<dim3((unsigned)nsq), 256, 0, s>>>(rank * in_dim, (int)sa.slices, w.part,
-                                                            A, m_a, v_a, grad_a, w.sq, hp);
-  mark("lora_adamw_a", (double)rank * in_dim * 4 * (6 + (grad_a ? 1 : 0)), 14.0 * rank * in_dim, s);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (gnorm_sq != nullptr) {
-    lora_gnorm_kernel<<<dim3(1), dim3(64), 0, s>>>(nsq, w.sq, gnorm_sq);
-    mark("lora_gnorm", 4.0 * nsq + 8, (double)nsq, s);
-    e = hipGetLastError();
-  }
-  return e;
+  const LoraJob j{rows, in_dim, out_dim, rank, dy, x, h, dt, A, B, m_a, v_a, m_b, v_b,
+                  grad_a, grad_b, scaling, ws};
+  return launch_lora_adamw_jobs(&j, 1, gnorm_sq, hp, s);
 }
 
 }  // namespace lbp

@@ -214,14 +214,14 @@ hipError_t ffn_run(int64_t rows, int64_t dim, int64_t ffn, int act, const float*
   e = launch_act_bwd(rows, ffn, act, gate, up_, dt, dh, p.dgu, dt, s, n1, dhs);
   if (e != hipSuccess) return e;
   // 4. dN2 = [dGate | dUp] [W_gate; W_up] (the partials of W_down are dead);
-  // reduced by the product itself: the norm below reads dN2 twice, which
-  // costs more than one reduction pass when it comes as several partials
+  // split-K partials are left for the norm below, which reads its row once
+  int n2 = 1;
   e = launch_gemm(rows, dim, 2 * ffn, p.dgu, dt, 2 * ffn, w_gate, w_up, ffn, dt, dim, p.dn2, dim,
-                  p.partials, s);
+                  p.partials, s, &n2);
   if (e != hipSuccess) return e;
   // 5. d_resid = (resid_in or d_resid) + rmsnorm_bwd(resid1, gamma_ffn, dN2)
-  return launch_rmsnorm_bwd(rows, dim, resid1, dt, gamma_ffn, p.dn2, d_resid, eps, 1, s, 1, 0,
-                            resid_in);
+  return launch_rmsnorm_bwd(rows, dim, resid1, dt, gamma_ffn, n2 > 1 ? p.partials : p.dn2, d_resid,
+                            eps, 1, s, n2, n2 > 1 ? rows * dim : 0, resid_in);
 }
 
 // ---------------------------------------------------------------- LoRA

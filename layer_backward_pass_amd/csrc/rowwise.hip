@@ -7,6 +7,8 @@
 
 namespace lbp {
 
+static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 // ---------------------------------------------------------------------------
 // RMSNorm backward, one 256-thread workgroup per row.  Hesper "Attention
 // Backward GPU Kernels", section "RMSNorm Backward":
@@ -84,12 +86,116 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int64_t n, const T* __
   }
 }
 
+// The same with the row held in registers (n <= 1024 Q): x, gamma and dy
+// (the sum of its nparts partials, in split order, PB partials in flight)
+// are read once, so split-K partials cost one pass instead of two.
+template <typename T, int ACC, int Q>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_reg_kernel(int64_t n, const T* __restrict__ x,
+                                                              const float* __restrict__ gamma,
+                                                              const float* dy, float* dx,
+                                                              float eps, int nparts,
+                                                              int64_t pstride, const float* rin) {
+  constexpr int PB = Q <= 4 ? 4 : 2;
+  __shared__ float red[4];
+  const int t = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int64_t n4 = n / 4;
+  const uint32_t ES = sizeof(T);
+  const brsrc_t rx = make_brsrc(x + row * n, (uint32_t)(n * ES));
+  const brsrc_t rgm = make_brsrc(gamma, (uint32_t)(n * 4));
+  const brsrc_t rdy = make_brsrc(dy + row * n, (uint32_t)(((nparts - 1) * pstride + n) * 4));
+  typename BufVec<T>::raw xr[Q];
+  float4 gm[Q], y[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int64_t i4 = t + 256 * q;
+    const bool ok = i4 < n4;
+    xr[q] = BufVec<T>::load(rx, ok ? (uint32_t)(i4 * 4 * ES) : BUF_OOB);
+    gm[q] = bload_f4(rgm, ok ? (uint32_t)(i4 * 16) : BUF_OOB);
+    y[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int p0 = 0; p0 < nparts; p0 += PB) {
+    float4 v[PB][Q];
+#pragma unroll
+    for (int u = 0; u < PB; ++u)
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int64_t i4 = t + 256 * q;
+        const int p = p0 + u;
+        v[u][q] = bload_f4(rdy, (p < nparts && i4 < n4) ? (uint32_t)((p * pstride + 4 * i4) * 4) : BUF_OOB);
+      }
+#pragma unroll
+    for (int u = 0; u < PB; ++u)
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        y[q].x += v[u][q].x;
+        y[q].y += v[u][q].y;
+        y[q].z += v[u][q].z;
+        y[q].w += v[u][q].w;
+      }
+  }
+  float4 xv[Q];
+  float ss = 0.f, dot = 0.f;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    xv[q] = BufVec<T>::cvt(xr[q]);
+    ss += xv[q].x * xv[q].x + xv[q].y * xv[q].y + xv[q].z * xv[q].z + xv[q].w * xv[q].w;
+    dot += y[q].x * gm[q].x * xv[q].x + y[q].y * gm[q].y * xv[q].y + y[q].z * gm[q].z * xv[q].z +
+           y[q].w * gm[q].w * xv[q].w;
+  }
+  ss = block_sum<4>(ss, red);
+  dot = block_sum<4>(dot, red);
+  const float nf = (float)n;
+  const float r2 = ss / nf + eps;
+  const float inv_r = 1.0f / sqrtf(r2);
+  const float c = dot / (nf * r2);
+  float* dxr = dx + row * n;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int64_t i4 = t + 256 * q;
+    if (i4 >= n4) continue;
+    float4 o;
+    o.x = (y[q].x * gm[q].x - xv[q].x * c) * inv_r;
+    o.y = (y[q].y * gm[q].y - xv[q].y * c) * inv_r;
+    o.z = (y[q].z * gm[q].z - xv[q].z * c) * inv_r;
+    o.w = (y[q].w * gm[q].w - xv[q].w * c) * inv_r;
+    float4* dp = reinterpret_cast<float4*>(dxr + 4 * i4);
+    if (ACC) {
+      const float4 pr = *reinterpret_cast<const float4*>((rin ? rin + row * n : dxr) + 4 * i4);
+      o.x += pr.x;
+      o.y += pr.y;
+      o.z += pr.z;
+      o.w += pr.w;
+    }
+    *dp = o;
+  }
+}
+
 hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, const float* gamma,
                               const float* dy, float* dx, float eps, int accumulate,
                               hipStream_t s, int nparts, int64_t pstride, const float* rin) {
   if (rows == 0) return hipSuccess;
   dim3 grid((unsigned)rows), block(256);
-  if (xdt == F32) {
+  const int64_t Q = cdiv(n / 4, 256);
+  if (Q <= 8 && ((double)(nparts - 1) * pstride + n) * 4 < BUF_MAX_BYTES) {
+#define LBP_RN(T, QV)                                                                           \
+  case QV:                                                                                      \
+    if (accumulate)                                                                             \
+      rmsnorm_bwd_reg_kernel<T, 1, QV><<<grid, block, 0, s>>>(n, (const T*)x, gamma, dy, dx,    \
+                                                             eps, nparts, pstride, rin);        \
+    else                                                                                        \
+      rmsnorm_bwd_reg_kernel<T, 0, QV><<<grid, block, 0, s>>>(n, (const T*)x, gamma, dy, dx,    \
+                                                             eps, nparts, pstride, rin);        \
+    break;
+    if (xdt == F32) {
+      switch (Q) { LBP_RN(float, 1) LBP_RN(float, 2) LBP_RN(float, 3) LBP_RN(float, 4)
+                   LBP_RN(float, 5) LBP_RN(float, 6) LBP_RN(float, 7) default: LBP_RN(float, 8) }
+    } else {
+      switch (Q) { LBP_RN(bf16, 1) LBP_RN(bf16, 2) LBP_RN(bf16, 3) LBP_RN(bf16, 4)
+                   LBP_RN(bf16, 5) LBP_RN(bf16, 6) LBP_RN(bf16, 7) default: LBP_RN(bf16, 8) }
+    }
+#undef LBP_RN
+  } else if (xdt == F32) {
     if (accumulate)
       rmsnorm_bwd_kernel<float, 1><<<grid, block, 0, s>>>(n, (const float*)x, gamma, dy, dx, eps, nparts, pstride, rin);
     else

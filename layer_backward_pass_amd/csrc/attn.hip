@@ -1238,7 +1238,7 @@ template <int D>
 static hipError_t attn_launch_f32(int64_t s_q, int64_t s_kv, int Hq, int Hkv, const float* dctx,
                                   const float* P, const float* K, const float* V,
                                   const float* ctx, float* dq, float* dv, float scale, int causal,
-                                  void* ws, hipStream_t s) {
+                                  void* ws, hipStream_t s, const float** dq_second) {
   const int grp = Hq / Hkv;
   const AttnWs wl = attn_ws(s_q, s_kv, Hq, Hkv, D, F32);
   float* delta = (float*)((char*)ws + wl.delta);
@@ -1265,7 +1265,9 @@ static hipError_t attn_launch_f32(int64_t s_q, int64_t s_kv, int Hq, int Hkv, co
     launch_dq_f32<D, 1>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta, dq, dq2, ksplit, scale, causal, s);
   mark("attn_dq_f32", pbytes + qbytes * (ctx ? 3 : 2) + 2 * kvbytes, 4.0 * D * pairs * Hq, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ksplit) {
+  if (ksplit && dq_second != nullptr) {
+    *dq_second = dq2;  // the caller adds it (the inverse RoPE pass does)
+  } else if (ksplit) {
     const int64_t n4 = s_q * Hq * D / 4;
     int64_t blocks = cdiv64(n4, 256);
     if (blocks > 4096) blocks = 4096;
@@ -1404,13 +1406,13 @@ template <typename T>
 static hipError_t attn_dispatch_d(int64_t s_q, int64_t s_kv, int Hq, int Hkv, int D,
                                   const float* dctx, const void* P, const void* K, const void* V,
                                   const void* ctx, float* dq, float* dv, float scale, int causal,
-                                  void* ws, hipStream_t s) {
+                                  void* ws, hipStream_t s, const float** dq_second) {
 #define LBP_ATTN_D(DD)                                                                         \
   case DD:                                                                                     \
     if constexpr (sizeof(T) == 4)                                                              \
       return attn_launch_f32<DD>(s_q, s_kv, Hq, Hkv, dctx, (const float*)P, (const float*)K,   \
                                  (const float*)V, (const float*)ctx, dq, dv, scale, causal, ws, \
-                                 s);                                                           \
+                                 s, dq_second);                                                \
     else if constexpr (DD >= 32)                                                               \
       return attn_launch_bf16<DD>(s_q, s_kv, Hq, Hkv, dctx, (const uint16_t*)P,                \
                                   (const uint16_t*)K, (const uint16_t*)V, (const uint16_t*)ctx, \
@@ -1432,7 +1434,9 @@ static hipError_t attn_dispatch_d(int64_t s_q, int64_t s_kv, int Hq, int Hkv, in
 hipError_t launch_attn_bwd(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_kv_heads,
                            int64_t head_dim, const float* dctx, const void* P, const void* K,
                            const void* V, const void* ctx, int dt, float* dq, float* dv,
-                           float scale, int causal, void* ws, hipStream_t s) {
+                           float scale, int causal, void* ws, hipStream_t s,
+                           const float** dq_second) {
+  if (dq_second != nullptr) *dq_second = nullptr;
   if (s_q == 0) {
     if (dv != nullptr) return launch_fill_zero(s_kv * n_kv_heads * head_dim, dv, s);
     return hipSuccess;
@@ -1456,9 +1460,9 @@ hipError_t launch_attn_bwd(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n
   }
   if (dt == F32)
     return attn_dispatch_d<float>(s_q, s_kv, (int)n_heads, (int)n_kv_heads, (int)head_dim, dctx,
-                                  P, K, V, ctx, dq, dv, scale, causal, ws, s);
+                                  P, K, V, ctx, dq, dv, scale, causal, ws, s, dq_second);
   return attn_dispatch_d<bf16>(s_q, s_kv, (int)n_heads, (int)n_kv_heads, (int)head_dim, dctx, P,
-                               K, V, ctx, dq, dv, scale, causal, ws, s);
+                               K, V, ctx, dq, dv, scale, causal, ws, s, dq_second);
 }
 
 }  // namespace lbp

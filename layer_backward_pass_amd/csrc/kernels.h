@@ -25,8 +25,10 @@ hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, c
                               const float* dy, float* dx, float eps, int accumulate,
                               hipStream_t s, int nparts = 1, int64_t pstride = 0,
                               const float* rin = nullptr);
+// dy2 (may be NULL): a second term added to dy before the rotation
 hipError_t launch_rope_bwd(int64_t rows, int64_t n_heads, int64_t head_dim, const float* dy,
-                           float* dx, int64_t pos0, float base, hipStream_t s);
+                           float* dx, int64_t pos0, float base, hipStream_t s,
+                           const float* dy2 = nullptr);
 // dgu[r, 0:I] = dGate, dgu[r, I:2I] = dUp; out_dt selects float or bf16 output;
 // dhid may be `nparts` split-K partial sums (stride pstride), added in order.
 hipError_t launch_act_bwd(int64_t rows, int64_t ffn, int act, const void* gate, const void* up,
@@ -178,7 +180,8 @@ size_t attn_ws_bytes(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_kv_he
 hipError_t launch_attn_bwd(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_kv_heads,
                            int64_t head_dim, const float* dctx, const void* P, const void* K,
                            const void* V, const void* ctx, int dt, float* dq, float* dv,
-                           float scale, int causal, void* ws, hipStream_t s);
+                           float scale, int causal, void* ws, hipStream_t s,
+                           const float** dq_second = nullptr);
 
 // ---- LoRA + AdamW (lora.hip)
 size_t lora_ws_bytes(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank);

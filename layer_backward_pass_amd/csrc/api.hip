@@ -196,10 +196,13 @@ hipError_t ffn_run(int64_t rows, int64_t dim, int64_t ffn, int act, const float*
     r.eps = eps;
     return launch_dgemv_red(RED_ACCUM, dt, r, s);
   }
-  // 1. dHid = d_out W_down (split-K partials are added by the next kernel)
+  // 1. dHid = d_out W_down (split-K partials are added by the next kernel);
+  // without a sub-norm the product's store may apply step 3 itself
   int n1 = 1;
+  const ActEpi ae{gate, up_, p.dgu, act, dt, dt};
+  bool act_done = false;
   e = launch_gemm(rows, ffn, dim, d_out, F32, dim, w_down, nullptr, dim, dt, ffn, p.dhid, ffn,
-                  p.partials, s, &n1);
+                  p.partials, s, &n1, hidden_pre ? nullptr : &ae, &act_done);
   if (e != hipSuccess) return e;
   const float* dh = n1 > 1 ? p.partials : p.dhid;
   const int64_t dhs = n1 > 1 ? rows * ffn : 0;
@@ -211,8 +214,10 @@ hipError_t ffn_run(int64_t rows, int64_t dim, int64_t ffn, int act, const float*
     n1 = 1;
   }
   // 3. gated activation backward -> [dGate | dUp]
-  e = launch_act_bwd(rows, ffn, act, gate, up_, dt, dh, p.dgu, dt, s, n1, dhs);
-  if (e != hipSuccess) return e;
+  if (!act_done) {
+    e = launch_act_bwd(rows, ffn, act, gate, up_, dt, dh, p.dgu, dt, s, n1, dhs);
+    if (e != hipSuccess) return e;
+  }
   // 4. dN2 = [dGate | dUp] [W_gate; W_up] (the partials of W_down are dead);
   // split-K partials are left for the norm below, which reads its row once
   int n2 = 1;

@@ -1,16 +1,18 @@
 // Transposed products of the backward pass, dX = dY W with W [out, in]
 // row-major: C[M,N] = A[M,K] B[K,N], A = gradient rows, B = weight.
-//   * fp32 weights: v_mfma_f32_16x16x4_f32, 128x128x16 workgroup tiles
-//   * bf16 weights: v_mfma_f32_16x16x32_bf16, 128x128x32 tiles, the
-//     gradient operand rounded to bf16 when staged in LDS
+//   * fp32 weights: v_mfma_f32_16x16x4_f32, 128x256 workgroup tiles, BK 32
+//   * bf16 weights: v_mfma_f32_16x16x32_bf16, 128x256 tiles, BK 64; an fp32
+//     gradient operand is rounded to bf16 first (cvt_a_bf16_kernel)
 // Split-K partial sums go to caller scratch and are reduced in a fixed
-// order (no float atomics), so results are bitwise reproducible.
+// order (no float atomics), so results are bitwise reproducible.  The W_down
+// product can apply the gated-activation backward to its output as it is
+// stored (ActEpi), so dHid never goes to memory.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace lbp {
-
-constexpr int GBM = 128, GBN = 128;
 
 // Output tile of the 16x16 MFMA accumulators: lane l holds rows 4*(l/16)+v
 // (v = 0..3) of column l%16.
@@ -32,6 +34,104 @@ __device__ __forceinline__ void store_tile(float* C, int64_t ldc, int64_t M, int
     }
 }
 
+// A whole 128 x 256 tile of dHid (C[r][c] = dHid of feature c) through the
+// gated-activation backward: [dGate | dUp] go to e.out[r][c], e.out[r][N + c]
+// (TO: float or bf16), from gate / up [M][N] (TG).  The accumulators pass
+// through LDS (`stage`: 64 x EPI_LD floats, free once the k-loop is done) in
+// two halves of 64 rows, so that each thread then takes eight consecutive
+// features of a row with 16-byte loads and stores; a half's gate/up loads
+// are in flight while its accumulators are written.  N % 8 == 0.
+constexpr int EPI_LD = 260;
+template <typename TG, typename TO, int ACT>
+__device__ __forceinline__ void act_tile_epilogue(const ActEpi& e, int64_t M, int64_t N,
+                                                  int64_t bm, int64_t bn, int wm, int wn,
+                                                  const floatx4 (&acc)[4][4], float* stage) {
+  constexpr int GV = sizeof(TG) == 2 ? 1 : 2;  // 16-byte chunks per eight features
+  const int t = threadIdx.x, lane = t & 63;
+  const int64_t mrows = min((int64_t)128, M - bm);
+  const uint32_t bytes = (uint32_t)(mrows * N * sizeof(TG));
+  const brsrc_t rg = make_brsrc((const TG*)e.gate + bm * N, bytes);
+  const brsrc_t ru = make_brsrc((const TG*)e.up + bm * N, bytes);
+  const int cl = 8 * (t & 31), rl = t >> 5;  // eight features of row rl (+16 p)
+  const int64_t gc = bn + cl;
+  __syncthreads();  // every wave is past its last LDS read of the k-loop
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint4 g[4][GV], u[4][GV];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = 64 * h + 16 * p + rl;
+      const bool ok = r < mrows && gc < N;
+#pragma unroll
+      for (int q = 0; q < GV; ++q) {
+        const uint32_t off = ok ? (uint32_t)((r * N + gc) * sizeof(TG) + 16 * q) : BUF_OOB;
+        g[p][q] = bload_u4(rg, off);
+        u[p][q] = bload_u4(ru, off);
+      }
+    }
+    if (wm == 64 * h) {
+#pragma unroll
+      for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+        for (int fj = 0; fj < 4; ++fj)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            stage[(fi * 16 + 4 * (lane >> 4) + v) * EPI_LD + wn + fj * 16 + (lane & 15)] =
+                acc[fi][fj][v];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = 64 * h + 16 * p + rl;
+      const float4 d0 = *reinterpret_cast<const float4*>(&stage[(16 * p + rl) * EPI_LD + cl]);
+      const float4 d1 = *reinterpret_cast<const float4*>(&stage[(16 * p + rl) * EPI_LD + cl + 4]);
+      const float dh[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+      float gv[8], uv[8];
+      if constexpr (GV == 1) {
+        const uint32_t gw[4] = {g[p][0].x, g[p][0].y, g[p][0].z, g[p][0].w};
+        const uint32_t uw[4] = {u[p][0].x, u[p][0].y, u[p][0].z, u[p][0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          gv[2 * i] = __uint_as_float(gw[i] << 16);
+          gv[2 * i + 1] = __uint_as_float(gw[i] & 0xffff0000u);
+          uv[2 * i] = __uint_as_float(uw[i] << 16);
+          uv[2 * i + 1] = __uint_as_float(uw[i] & 0xffff0000u);
+        }
+      } else {
+        const uint32_t gw[8] = {g[p][0].x, g[p][0].y, g[p][0].z, g[p][0].w,
+                                g[p][1].x, g[p][1].y, g[p][1].z, g[p][1].w};
+        const uint32_t uw[8] = {u[p][0].x, u[p][0].y, u[p][0].z, u[p][0].w,
+                                u[p][1].x, u[p][1].y, u[p][1].z, u[p][1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          gv[i] = __uint_as_float(gw[i]);
+          uv[i] = __uint_as_float(uw[i]);
+        }
+      }
+      float dg[8], du[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) act_bwd1<ACT>(gv[i], uv[i], dh[i], dg[i], du[i]);
+      if (r < mrows && gc < N) {
+        TO* o = (TO*)e.out + (bm + r) * 2 * N + gc;
+        if constexpr (sizeof(TO) == 2) {
+          *reinterpret_cast<uint4*>(o) = make_uint4(pk_bf16(dg[0], dg[1]), pk_bf16(dg[2], dg[3]),
+                                                    pk_bf16(dg[4], dg[5]), pk_bf16(dg[6], dg[7]));
+          *reinterpret_cast<uint4*>(o + N) =
+              make_uint4(pk_bf16(du[0], du[1]), pk_bf16(du[2], du[3]), pk_bf16(du[4], du[5]),
+                         pk_bf16(du[6], du[7]));
+        } else {
+          float* of = (float*)o;
+          *reinterpret_cast<float4*>(of) = make_float4(dg[0], dg[1], dg[2], dg[3]);
+          *reinterpret_cast<float4*>(of + 4) = make_float4(dg[4], dg[5], dg[6], dg[7]);
+          *reinterpret_cast<float4*>(of + N) = make_float4(du[0], du[1], du[2], du[3]);
+          *reinterpret_cast<float4*>(of + N + 4) = make_float4(du[4], du[5], du[6], du[7]);
+        }
+      }
+    }
+    if (h == 0) __syncthreads();  // the second half overwrites the stage
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 GEMM: workgroup of 8 waves (512 threads), tile 128 x 256, BK = 32; the
 // waves form a 2 x 4 grid of 64 x 64 wave tiles (4 x 4 MFMA accumulators).
@@ -46,6 +146,7 @@ __device__ __forceinline__ void store_tile(float* C, int64_t ldc, int64_t M, int
 // keeps the HBM/L2 bytes per MFMA low; with one workgroup per CU the MFMA
 // pipe then stays about three quarters busy.
 constexpr int F_BK = 32, F_LD = F_BK + 4, F_BM = 128, F_BN = 256, F_NT = 512;
+static_assert(2 * F_BN * F_LD >= 64 * EPI_LD, "activation stage fits in Bs");
 
 // Work item of a product launch.  Tiles are numbered m-fastest over the
 // nm x nn grid.  Items u < nfull are whole tiles written to C; the other
@@ -56,6 +157,7 @@ constexpr int F_BK = 32, F_LD = F_BK + 4, F_BM = 128, F_BN = 256, F_NT = 512;
 struct GemmWork {
   int64_t bm, bn, kbeg, kend, ldo;
   float* out;
+  bool whole;
 };
 template <int BM, int BN>
 __device__ __forceinline__ GemmWork gemm_work(int64_t M, int64_t N, int64_t K, int64_t kps,
@@ -77,6 +179,7 @@ __device__ __forceinline__ GemmWork gemm_work(int64_t M, int64_t N, int64_t K, i
   GemmWork w;
   w.bm = (tile % nm) * BM;
   w.bn = (tile / nm) * BN;
+  w.whole = z < 0;
   if (z < 0) {
     w.kbeg = 0;
     w.kend = K;
@@ -96,13 +199,34 @@ __device__ __forceinline__ float f4at(const float4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
+// The store of a product's 128 x 256 tile: through the activation backward
+// for a whole tile of an ACT-epilogue launch, else plain (C, or a partial
+// slot).  EPI: 0 plain, else 1 + act + 2 (gate/up bf16) + 4 (out bf16).
+template <int EPI>
+__device__ __forceinline__ void store_out(const ActEpi& e, const GemmWork& wk, int64_t M,
+                                          int64_t N, int wm, int wn, const floatx4 (&acc)[4][4],
+                                          float* stage) {
+  if constexpr (EPI != 0) {
+    if (wk.whole) {
+      constexpr int ACT = (EPI - 1) & 1;
+      constexpr bool GB = ((EPI - 1) & 2) != 0, OB = ((EPI - 1) & 4) != 0;
+      typedef typename std::conditional<GB, bf16, float>::type TG;
+      typedef typename std::conditional<OB, bf16, float>::type TO;
+      act_tile_epilogue<TG, TO, ACT>(e, M, N, wk.bm, wk.bn, wm, wn, acc, stage);
+      return;
+    }
+  }
+  store_tile<4, 4>(wk.out, wk.ldo, M, N, wk.bm + wm, wk.bn + wn, acc);
+}
+
+template <int EPI>
 __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, int64_t K,
                                                         const float* __restrict__ A, int64_t lda,
                                                         const float* __restrict__ B1,
                                                         const float* __restrict__ B2, int64_t K1,
                                                         int64_t ldb, float* __restrict__ C,
                                                         int64_t ldc, float* __restrict__ P,
-                                                        int64_t kps, int64_t nfull) {
+                                                        int64_t kps, int64_t nfull, ActEpi epi) {
   constexpr int NA = F_BM * F_BK / 4 / F_NT;   // A float4 per thread (2)
   constexpr int NBQ = F_BK * F_BN / 4 / F_NT;  // B k-quads per thread (4)
   constexpr int BQS = F_NT / F_BN;             // k-quad stride between them (2)
@@ -203,7 +327,7 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
     __syncthreads();
     load(s1, k0 + 4 * F_BK);
   }
-  store_tile<4, 4>(wk.out, wk.ldo, M, N, bm + wm, bn + wn, acc);
+  store_out<EPI>(epi, wk, M, N, wm, wn, acc, &Bs[0][0][0]);
 }
 
 // ---------------------------------------------------------------------------
@@ -218,8 +342,9 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
 // 236 -> 223 us).
 constexpr int H_BM = 128, H_BN = 256, H_BK = 64, H_NT = 512;
 constexpr int H_LDA = H_BK + 8, H_LDB = H_BN + 16;
+static_assert(2 * H_BK * H_LDB * 2 >= 64 * EPI_LD * 4, "activation stage fits in Bs");
 
-template <bool SPLITB>
+template <bool SPLITB, int EPI>
 __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, int64_t K,
                                                          const uint16_t* __restrict__ A, int64_t lda,
                                                          const uint16_t* __restrict__ B1,
@@ -227,7 +352,7 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
                                                          int64_t K1, int64_t ldb,
                                                          float* __restrict__ C, int64_t ldc,
                                                          float* __restrict__ P, int64_t kps,
-                                                         int64_t nfull) {
+                                                         int64_t nfull, ActEpi epi) {
   constexpr int NA = H_BM * H_BK / 8 / H_NT;  // A chunks of 8 per thread (2)
   constexpr int NB = H_BK * H_BN / 8 / H_NT;  // B chunks of 8 per thread (4)
   // One k-tile of global data in registers
@@ -361,17 +486,19 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
     load(st, k0 + 3 * H_BK);
     buf ^= 1;
   }
-  store_tile<4, 4>(wk.out, wk.ldo, M, N, bm + wm, bn + wn, acc);
+  store_out<EPI>(epi, wk, M, N, wm, wn, acc, reinterpret_cast<float*>(&Bs[0][0][0]));
 }
 
 // ---------------------------------------------------------------------------
 // Fixed-order reduction of split-K partials: C[m, n] = sum_s P[s, m, n],
 // over the split tiles only -- columns n >= n0, except the rows m < mskip of
 // the first column panel [n0, n0 + bn), which were whole tiles.
+template <int EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(int64_t M, int64_t N, int splits,
                                                             const float* __restrict__ P,
                                                             float* __restrict__ C, int64_t ldc,
-                                                            int64_t n0, int64_t bn, int64_t mskip) {
+                                                            int64_t n0, int64_t bn, int64_t mskip,
+                                                            ActEpi epi) {
   const int64_t q = (N - n0) / 4;
   const int64_t total = M * q;
   const int64_t stride = M * N;
@@ -400,7 +527,30 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(int64_t M, int64_t N
         s.w += take ? v[u].w : 0.f;
       }
     }
-    *reinterpret_cast<float4*>(C + m * ldc + n) = s;
+    if constexpr (EPI != 0) {
+      // through the activation backward (see store_tile_act)
+      constexpr int ACT = (EPI - 1) & 1;
+      constexpr bool GB = ((EPI - 1) & 2) != 0, OB = ((EPI - 1) & 4) != 0;
+      typedef typename std::conditional<GB, bf16, float>::type TG;
+      const float4 g = Act<TG>::ld4((const TG*)epi.gate, m * N + n);
+      const float4 u = Act<TG>::ld4((const TG*)epi.up, m * N + n);
+      float4 dg, du;
+      act_bwd1<ACT>(g.x, u.x, s.x, dg.x, du.x);
+      act_bwd1<ACT>(g.y, u.y, s.y, dg.y, du.y);
+      act_bwd1<ACT>(g.z, u.z, s.z, dg.z, du.z);
+      act_bwd1<ACT>(g.w, u.w, s.w, dg.w, du.w);
+      if constexpr (OB) {
+        uint16_t* o = (uint16_t*)epi.out + m * 2 * N + n;
+        *reinterpret_cast<uint2*>(o) = make_uint2(pk_bf16(dg.x, dg.y), pk_bf16(dg.z, dg.w));
+        *reinterpret_cast<uint2*>(o + N) = make_uint2(pk_bf16(du.x, du.y), pk_bf16(du.z, du.w));
+      } else {
+        float* o = (float*)epi.out + m * 2 * N + n;
+        *reinterpret_cast<float4*>(o) = dg;
+        *reinterpret_cast<float4*>(o + N) = du;
+      }
+    } else {
+      *reinterpret_cast<float4*>(C + m * ldc + n) = s;
+    }
   }
 }
 
@@ -480,12 +630,24 @@ __global__ __launch_bounds__(256) void cvt_a_bf16_kernel(int64_t M, int64_t K, c
 
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt, int64_t lda,
                        const void* B1, const void* B2, int64_t K1, int b_dt, int64_t ldb,
-                       float* C, int64_t ldc, float* partials, hipStream_t s, int* deferred) {
+                       float* C, int64_t ldc, float* partials, hipStream_t s, int* deferred,
+                       const ActEpi* act, bool* act_done) {
   if (deferred) *deferred = 1;
+  if (act_done) *act_done = false;
   if (M == 0 || N == 0) return hipSuccess;
   const GemmPlan pl = gemm_plan(M, N, K, b_dt);
   const int64_t kps = pl.kps, nfull = pl.nfull;
   const int nsp = pl.nsp;
+  // the activation epilogue: whole tiles apply it as they store, a split
+  // tail is reduced through it; a plain split-K product leaves its partials
+  // (the caller's activation pass adds them) -- and gate/up/out take the
+  // weights' dtype
+  const bool use_act = act != nullptr && (nsp == 1 || nfull > 0) &&
+                       act->gdt == b_dt && act->odt == b_dt && ldc == N && N % 8 == 0 &&
+                       128.0 * N * 4 < BUF_MAX_BYTES;
+  const int epi = use_act ? 1 + act->act + (b_dt == BF16 ? 6 : 0) : 0;
+  const ActEpi ea = use_act ? *act : ActEpi{};
+  if (act_done) *act_done = use_act;
   const int64_t tiles = cdiv(N, pl.bn) * cdiv(M, pl.bm);
   const dim3 grid1((unsigned)(nfull + (tiles - nfull) * nsp));
   if (B2 == nullptr) {
@@ -494,9 +656,14 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
   }
   const dim3 block(256);
   if (b_dt == F32) {
-    gemm_f32_kernel<<<grid1, dim3(F_NT), 0, s>>>(M, N, K, (const float*)A, lda, (const float*)B1,
-                                                (const float*)B2, K1, ldb, C, ldc, partials, kps,
-                                                nfull);
+#define LBP_GEMM_F32(E)                                                                        \
+  gemm_f32_kernel<E><<<grid1, dim3(F_NT), 0, s>>>(M, N, K, (const float*)A, lda, (const float*)B1, \
+                                                  (const float*)B2, K1, ldb, C, ldc, partials, kps, \
+                                                  nfull, ea)
+    if (epi == 1) LBP_GEMM_F32(1);
+    else if (epi == 2) LBP_GEMM_F32(2);
+    else LBP_GEMM_F32(0);
+#undef LBP_GEMM_F32
   } else {
     if (a_dt == F32) {
       // A to bf16 once, into the scratch after the partials
@@ -514,12 +681,20 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
     if (((double)(H_BM - 1) * lda + K) * 4 >= BUF_MAX_BYTES || (double)H_BK * ldb * 2 >= BUF_MAX_BYTES)
       return hipErrorInvalidValue;
     const bool splitb = K1 % H_BK != 0;
-#define LBP_GEMM_BF16(SB)                                                                   \
-  gemm_bf16_kernel<SB><<<grid1, dim3(H_NT), 0, s>>>(M, N, K, (const uint16_t*)A, lda,         \
-                                                   (const uint16_t*)B1, (const uint16_t*)B2,  \
-                                                   K1, ldb, C, ldc, partials, kps, nfull)
-    if (splitb) LBP_GEMM_BF16(true);
-    else LBP_GEMM_BF16(false);
+#define LBP_GEMM_BF16(SB, E)                                                                \
+  gemm_bf16_kernel<SB, E><<<grid1, dim3(H_NT), 0, s>>>(M, N, K, (const uint16_t*)A, lda,      \
+                                                      (const uint16_t*)B1, (const uint16_t*)B2, \
+                                                      K1, ldb, C, ldc, partials, kps, nfull, ea)
+    if (epi == 7) {
+      if (splitb) LBP_GEMM_BF16(true, 7);
+      else LBP_GEMM_BF16(false, 7);
+    } else if (epi == 8) {
+      if (splitb) LBP_GEMM_BF16(true, 8);
+      else LBP_GEMM_BF16(false, 8);
+    } else {
+      if (splitb) LBP_GEMM_BF16(true, 0);
+      else LBP_GEMM_BF16(false, 0);
+    }
 #undef LBP_GEMM_BF16
   }
   hipError_t e = hipGetLastError();
@@ -537,8 +712,17 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
   const int64_t n0 = (nfull / nm) * pl.bn, mskip = (nfull % nm) * pl.bm;
   int64_t blocks = cdiv(M * ((N - n0) / 4), 256);
   if (blocks > 4096) blocks = 4096;
-  splitk_reduce_kernel<<<dim3((unsigned)blocks), block, 0, s>>>(M, N, nsp, partials, C, ldc, n0,
-                                                               pl.bn, mskip);
+#define LBP_RED(E)                                                                          \
+  splitk_reduce_kernel<E><<<dim3((unsigned)blocks), block, 0, s>>>(M, N, nsp, partials, C, ldc, \
+                                                                  n0, pl.bn, mskip, ea)
+  switch (epi) {
+    case 1: LBP_RED(1); break;
+    case 2: LBP_RED(2); break;
+    case 7: LBP_RED(7); break;
+    case 8: LBP_RED(8); break;
+    default: LBP_RED(0);
+  }
+#undef LBP_RED
   mark("splitk_reduce", 0, 0, s);
   return hipGetLastError();
 }

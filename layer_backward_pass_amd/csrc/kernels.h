@@ -49,10 +49,23 @@ size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K, int a_dt, int b_dt);
 // With `deferred` non-null, a split-K product leaves its partial sums in
 // `partials` ([splits][M][N], dense) for the consumer to add, and
 // *deferred = splits (1: the result is in C).
+// With `act` set, the product is dHid of a gated activation: where the plan
+// allows (whole tiles, or a split tail that is reduced here) the store goes
+// through the activation backward, out[r][0:N] = dGate, out[r][N:2N] = dUp
+// from gate / up [M][N] (gdt, odt: F32 or BF16), C is not written and
+// *act_done = true; otherwise C (or the deferred partials) as above.
+struct ActEpi {
+  const void* gate;
+  const void* up;
+  void* out;
+  int act;  // ActKind
+  int gdt, odt;
+};
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt, int64_t lda,
                        const void* B1, const void* B2, int64_t K1, int b_dt, int64_t ldb,
                        float* C, int64_t ldc, float* partials, hipStream_t s,
-                       int* deferred = nullptr);
+                       int* deferred = nullptr, const ActEpi* act = nullptr,
+                       bool* act_done = nullptr);
 
 // ---- single-token (decode) kernels (decode.hip)
 // part[chunk, N] = x[K] W[K, N] over row chunks of kc rows (W rows k < K1

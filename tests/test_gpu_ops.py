@@ -162,6 +162,11 @@ def test_attention_without_dv_and_empty_queries():
     # column panel) split in k and added after
     (833, 256, 9400, "swiglu", False, F32),
     (833, 512, 9400, "relu2", True, BF16),
+    # without a sub-norm the dHid product applies the activation backward
+    # in its store: bf16 whole tiles + a split tail reduced through it, and
+    # fp32 whole tiles with ragged rows and columns
+    (833, 512, 9400, "relu2", False, BF16),
+    (700, 128, 520, "relu2", False, F32),
 ])
 def test_ffn(rows, dim, ffn, act, sub, dt):
     print("ffn", rows, dim, ffn, act, sub, dt, flush=True)

@@ -16,8 +16,10 @@
 // of 16 (the MFMA tile width) with zeros.
 //
 // A layer's two adapters (Q and V) run in the same launches: every kernel
-// takes a pair of argument sets and blockIdx.z picks the adapter; the grid
-// covers the larger of the two and the other's surplus workgroups return.
+// takes a pair of argument sets: the two passes over the data walk one flat
+// list of both adapters' workgroups, the update kernels take blockIdx.z as
+// the adapter (the grid covers the larger of the two and the other's
+// surplus workgroups return).
 #include <type_traits>
 
 #include "common.h"
@@ -70,6 +72,19 @@ struct Pair {
   // the adapter of this workgroup (a select, not an indexed copy of the
   // kernel arguments)
   __device__ __forceinline__ const A& pick() const { return blockIdx.z == 0 ? a[0] : a[1]; }
+  // Flat 1-D grid of the two adapters' (column group, row slice) items:
+  // adapter 0's gx x gy first, then adapter 1's, column group fastest, so
+  // consecutive workgroups (which the hardware deals out to the XCDs in
+  // turn) spread each adapter over every XCD.
+  __device__ __forceinline__ const A& item(int& bx, int& by) const {
+    const int64_t L = blockIdx.x, n0 = (int64_t)a[0].gx * a[0].gy;
+    const bool second = L >= n0;
+    const A& r = second ? a[1] : a[0];
+    const int64_t loc = second ? L - n0 : L;
+    bx = (int)(loc % r.gx);
+    by = (int)(loc / r.gx);
+    return r;
+  }
 };
 
 // Four consecutive floats of row `row` starting at column `c`, zero outside
@@ -110,8 +125,8 @@ __device__ __forceinline__ float ld_h(const void* h, int hdt, int64_t e) {
 //     dy[i0+4q+l/16][o0+4(l%16)+j].
 template <int RB, bool VEC, typename TH>
 __global__ __launch_bounds__(256) void lora_dy_kernel(Pair<DyArgs> pa) {
-  const DyArgs& A = pa.pick();
-  if ((int)blockIdx.x >= A.gx || (int)blockIdx.y >= A.gy) return;
+  int bx, by;
+  const DyArgs& A = pa.item(bx, by);
   const int64_t rows = A.rows, out_dim = A.out_dim, rs = A.rs;
   const int rank = A.rank;
   const float* __restrict__ dy = A.dy;
@@ -123,8 +138,8 @@ __global__ __launch_bounds__(256) void lora_dy_kernel(Pair<DyArgs> pa) {
   __shared__ float gs[4][16][RP + 1];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int l16 = lane & 15, l4 = lane >> 4;
-  const int64_t o0 = (int64_t)blockIdx.x * LG_COLS + w * LW_COLS;
-  const int64_t i_beg = (int64_t)blockIdx.y * rs;
+  const int64_t o0 = (int64_t)bx * LG_COLS + w * LW_COLS;
+  const int64_t i_beg = (int64_t)by * rs;
   const int64_t i_end = min(rows, i_beg + rs);
 
   float bv[4][4][RB];  // B operand of g: B[o0+16c+4 l4+j][16b+l16]
@@ -209,7 +224,7 @@ __global__ __launch_bounds__(256) void lora_dy_kernel(Pair<DyArgs> pa) {
     for (int e = t; e < 16 * RP; e += 256) {
       const int row = e / RP, col = e % RP;
       if (i0 + row < i_end)
-        gpart[((int64_t)blockIdx.x * rows + i0 + row) * RP + col] =
+        gpart[((int64_t)bx * rows + i0 + row) * RP + col] =
             ((gs[0][row][col] + gs[1][row][col]) + gs[2][row][col]) + gs[3][row][col];
     }
     __syncthreads();
@@ -225,7 +240,7 @@ __global__ __launch_bounds__(256) void lora_dy_kernel(Pair<DyArgs> pa) {
     fetch(s1, i0 + 48);
   }
   // dB tile j, register v: feature o0 + 4(4 l4 + v) + j, rank 16b + l16
-  float* dp = dbpart + (int64_t)blockIdx.y * out_dim * rank;
+  float* dp = dbpart + (int64_t)by * out_dim * rank;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -245,8 +260,8 @@ __global__ __launch_bounds__(256) void lora_dy_kernel(Pair<DyArgs> pa) {
 // a 4-feature chunk is whole).
 template <int RB, typename T>
 __global__ __launch_bounds__(256) void lora_da_kernel(Pair<DaArgs> pa) {
-  const DaArgs& A = pa.pick();
-  if ((int)blockIdx.x >= A.gx || (int)blockIdx.y >= A.gy) return;
+  int bx, by;
+  const DaArgs& A = pa.item(bx, by);
   const int64_t rows = A.rows, in_dim = A.in_dim, rs = A.rs;
   const int rank = A.rank;
   const float* __restrict__ g = A.g;
@@ -255,8 +270,8 @@ __global__ __launch_bounds__(256) void lora_da_kernel(Pair<DaArgs> pa) {
   constexpr int RP = 16 * RB;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int l16 = lane & 15, l4 = lane >> 4;
-  const int64_t k0 = (int64_t)blockIdx.x * LG_COLS + w * LW_COLS;
-  const int64_t i_beg = (int64_t)blockIdx.y * rs;
+  const int64_t k0 = (int64_t)bx * LG_COLS + w * LW_COLS;
+  const int64_t i_beg = (int64_t)by * rs;
   const int64_t i_end = min(rows, i_beg + rs);
   const int64_t nrow = i_end - i_beg;
   const brsrc_t rx = make_brsrc(x + i_beg * in_dim, nrow > 0 ? (uint32_t)(nrow * in_dim * sizeof(T)) : 0u);
@@ -303,7 +318,7 @@ __global__ __launch_bounds__(256) void lora_da_kernel(Pair<DaArgs> pa) {
     fetch(s1, i0 + 48);
   }
   // tile j, register v: rank 16b + 4 l4 + v, feature k0 + 4 l16 + j
-  float* dp = dapart + (int64_t)blockIdx.y * rank * in_dim;
+  float* dp = dapart + (int64_t)by * rank * in_dim;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -449,7 +464,8 @@ static hipError_t lora_group(const LoraJob* const* jobs, int nz, float* gnorm_sq
   Pair<BUpdArgs> bu{};
   Pair<DaArgs> da{};
   Pair<AUpdArgs> au{};
-  int gx = 0, gy = 0, bx = 0, ax = 0, dx = 0, dyy = 0;
+  int64_t ny = 0, nd = 0;  // items of the dy and dA passes
+  int bx = 0, ax = 0;
   double by_dy = 0, fl_dy = 0, by_b = 0, fl_b = 0, by_da = 0, fl_da = 0, by_a = 0, fl_a = 0;
   const int64_t rows = jobs[0]->rows;
   for (int z = 0; z < 2; ++z) {
@@ -469,11 +485,9 @@ static hipError_t lora_group(const LoraJob* const* jobs, int nz, float* gnorm_sq
     au.a[z] = AUpdArgs{j.rank * j.in_dim, (int)sa.slices, (int)cdiv(j.rank * j.in_dim, 256),
                        base + o.part, j.A, j.m_a, j.v_a, j.grad_a, base + o.sq};
     if (z >= nz) continue;
-    gx = max(gx, (int)sy.groups);
-    gy = max(gy, (int)sy.slices);
+    ny += sy.groups * sy.slices;
+    nd += sa.groups * sa.slices;
     bx = max(bx, bu.a[z].nblk);
-    dx = max(dx, (int)sa.groups);
-    dyy = max(dyy, (int)sa.slices);
     ax = max(ax, au.a[z].nblk);
     const double esz = j.dt == F32 ? 4.0 : 2.0;
     by_dy += (double)j.rows * j.out_dim * 4 + (double)j.rows * j.rank * esz + (double)nb * 4;
@@ -487,7 +501,7 @@ static hipError_t lora_group(const LoraJob* const* jobs, int nz, float* gnorm_sq
   }
   hipError_t e;
   if (rows > 0) {
-    lora_dy_kernel<RB, VEC, TH><<<dim3((unsigned)gx, (unsigned)gy, (unsigned)nz), 256, 0, s>>>(dy);
+    lora_dy_kernel<RB, VEC, TH><<<dim3((unsigned)ny), 256, 0, s>>>(dy);
     mark("lora_dy", by_dy, fl_dy, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -497,7 +511,7 @@ static hipError_t lora_group(const LoraJob* const* jobs, int nz, float* gnorm_sq
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (rows > 0) {
     lora_da_kernel<RB, typename std::conditional<sizeof(TH) == 4, float, bf16>::type>
-        <<<dim3((unsigned)dx, (unsigned)dyy, (unsigned)nz), 256, 0, s>>>(da);
+        <<<dim3((unsigned)nd), 256, 0, s>>>(da);
     mark("lora_da", by_da, fl_da, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

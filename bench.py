@@ -9,10 +9,12 @@ O-projection backward, attention backward, inverse RoPE, and, where the
 workload has adapters, LoRA gradients with AdamW) - for `stack36`, all 36
 layers in reverse order.  The top layer reads the upstream gradient (never
 written) and leaves dH1 in a separate buffer, which the layers below update
-in place, so replaying a step needs no reset copy.  Inputs are resident in HBM before timing starts;
-each input copy's step is captured once as a HIP graph and replayed.  Steps
-rotate over enough input copies that HBM-bound work cannot be served from
-the 256 MB Infinity Cache.
+in place, so replaying a step needs no reset copy.  Inputs are resident in HBM before timing starts.
+Steps rotate over enough input copies that HBM-bound work cannot be served
+from the 256 MB Infinity Cache; one HIP graph holds the steps of all copies
+in rotation order (as a model's backward holds its layers), so a graph
+launch is paid once per round of copies, and a graph per copy covers a
+step count that is not a whole number of rounds.
 
 Workloads (default: decode):
   decode       one token, 512-slot K/V cache, hidden 2560, ffn 6912, 20/5 heads
@@ -432,29 +434,40 @@ def main():
     for cp in copies:
         run_step(lbp, cfg, cp)
     torch.cuda.synchronize()
-    graphs = []
+    graphs, round_graph = [], None
     if not args.no_graph:
         for cp in copies:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 run_step(lbp, cfg, cp)
             graphs.append(g)
+        if len(copies) > 1:
+            round_graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(round_graph):
+                for cp in copies:
+                    run_step(lbp, cfg, cp)
         torch.cuda.synchronize()
 
-    def step(i):
-        if graphs:
-            graphs[i % len(graphs)].replay()
-        else:
-            run_step(lbp, cfg, copies[i % len(copies)])
+    def run(first, count):
+        """Steps first .. first+count-1 (step i on copy i mod copies)."""
+        i, end = first, first + count
+        while i < end:
+            if round_graph is not None and i % len(copies) == 0 and end - i >= len(copies):
+                round_graph.replay()
+                i += len(copies)
+            elif graphs:
+                graphs[i % len(graphs)].replay()
+                i += 1
+            else:
+                run_step(lbp, cfg, copies[i % len(copies)])
+                i += 1
 
-    for i in range(warmup):
-        step(i)
+    run(0, warmup)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream().cuda_stream
     ev = hip.events(2)
     hip.record(ev[0], stream)
-    for i in range(steps):
-        step(i)
+    run(warmup, steps)
     hip.record(ev[1], stream)
     torch.cuda.synchronize()
     ms = hip.elapsed_ms(ev[0], ev[1])
@@ -486,6 +499,7 @@ def main():
                    "kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "act": cfg.act,
                    "sub_norms": cfg.sub_norms, "lora_rank": cfg.rank, "layers": cfg.n_layers,
                    "input_copies": len(copies), "hip_graph": bool(graphs),
+                   "steps_per_graph_launch": len(copies) if round_graph is not None else 1,
                    "kernels_per_step": len(kernels) * (cfg.n_layers if cfg.n_layers > 1 else 1)},
         "roofline": rl,
         "cpu_baseline": cpu,

@@ -305,6 +305,57 @@ def test_layer_out_of_place(name, over):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("name,over", [
+    ("decode", {}),                                   # the benchmark's workload
+    ("tiny", {"seq": 70, "kv_len": 70}),              # LoRA state advances each call
+    ("tiny", {"dtype": "bf16", "seq": 96, "kv_len": 96}),
+])
+def test_layer_graph_replay(name, over):
+    """The layer captured once in a HIP graph and replayed (as the benchmark
+    times it) matches eager calls bitwise, replay after replay, with eager
+    work and synchronisation between the replays."""
+    cfg = synth.get_config(name).with_(**over)
+    sides = []
+    for _ in range(2):
+        dl = Hn.DeviceLayer(cfg, 0, DEV)
+        bufs = {"d_in": dl.d_out.clone(), "d": torch.empty_like(dl.d_out),
+                "dq": torch.empty(cfg.seq, cfg.q_dim, device=DEV),
+                "dv": torch.empty(cfg.kv_len, cfg.kv_dim, device=DEV),
+                "g": torch.zeros(1, device=DEV)}
+        sides.append((dl, bufs))
+
+    def call(side):
+        dl, b = side
+        dl.run_gpu(b["d"], b["dq"], b["dv"], b["g"], d_out=b["d_in"])
+
+    # one eager call each first (sizes the workspace before the capture)
+    for side in sides:
+        call(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(sides[1])
+    torch.cuda.synchronize()
+
+    def state(side):
+        dl, b = side
+        o = [b[k].cpu() for k in ("d", "dq", "dv", "g")]
+        if dl.lora:
+            o += [dl.lora[t][k].cpu() for t in ("q", "v") for k in ("A", "B", "m_a", "v_b")]
+        return o
+
+    for rep in range(3):
+        for side in sides:
+            side[1]["g"].zero_()
+            side[1]["d"].fill_(float("nan"))
+        torch.cuda.synchronize()
+        call(sides[0])
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(state(sides[0]), state(sides[1])):
+            assert torch.equal(a, b), rep
+
+
 def test_layer_deterministic():
     cfg = synth.get_config("tiny").with_(seq=70, kv_len=70)
     outs = []

@@ -698,9 +698,12 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
 #undef LBP_GEMM_BF16
   }
   hipError_t e = hipGetLastError();
+  // with the activation epilogue the product's output is [dGate | dUp] from
+  // gate and up (weights' dtype) instead of C
+  const double es = b_dt == F32 ? 4 : 2;
   mark(b_dt == F32 ? "gemm_f32_mfma" : "gemm_bf16_mfma",
-       (double)M * K * (a_dt == F32 ? 4 : 2) + (double)K * N * (b_dt == F32 ? 4 : 2) +
-           (double)M * N * 4,
+       (double)M * K * (a_dt == F32 ? 4 : 2) + (double)K * N * es +
+           (use_act ? (double)M * N * 4 * es : (double)M * N * 4),
        2.0 * M * N * K, s);
   if (e != hipSuccess || nsp == 1) return e;
   if (deferred && nfull == 0) {

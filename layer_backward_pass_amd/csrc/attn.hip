@@ -467,8 +467,9 @@ __global__ __launch_bounds__(256) void attn_dv_reduce_kernel(int64_t s_q, int64_
 //
 // transpose_bf16_kernel  dst[col][row] (bf16, rows padded with zeros to LR)
 //     from src[row][col] (fp32 or bf16).  Gives K as Kt[kv head][d][key] and
-//     dCtx as dCt[head][d][query], so the operands whose MFMA k index runs
-//     over keys or queries are 16-byte reads.
+//     dCtx as dCt[head][d][query] (both in one launch, ahead of dQ), so the
+//     operands whose MFMA k index runs over keys or queries are 16-byte
+//     reads.
 // attn_dq_bf16_kernel  workgroup = HW heads of one KV group x QW wave groups;
 //     a wave owns two 16-query blocks, i and n-1-i, so every wave does about
 //     the same causal work.  64-key tiles of V and Kt are staged in LDS
@@ -487,21 +488,37 @@ __global__ __launch_bounds__(256) void attn_dv_reduce_kernel(int64_t s_q, int64_
 //     steps); chunk partials as in fp32.
 constexpr int TR_R = 64, TR_C = 32;
 
-template <typename TS>
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(int64_t rows, int64_t LR,
-                                                             int64_t ld,
-                                                             const TS* __restrict__ src,
-                                                             uint16_t* __restrict__ dst) {
+// One transposition of the launch below: src [rows][cols] (row stride ld)
+// into dst [cols][LR] in tiles of TR_R rows x TR_C columns, gx x gy tiles.
+struct TrJob {
+  int64_t rows, LR, ld;
+  const void* src;
+  uint16_t* dst;
+  int gx, gy;
+};
+
+// Kᵀ (bf16 source) and dCtxᵀ (fp32 source) in one launch: the first
+// a.gx * a.gy workgroups take job a, the rest job b.
+template <typename TA, typename TB>
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(TrJob a, TrJob b) {
   __shared__ uint16_t tile[TR_C][TR_R + 2];
+  const int64_t na = (int64_t)a.gx * a.gy;
+  const bool second = (int64_t)blockIdx.x >= na;
+  const int64_t loc = second ? (int64_t)blockIdx.x - na : (int64_t)blockIdx.x;
+  const TrJob& jb = second ? b : a;
+  const int64_t rows = jb.rows, LR = jb.LR, ld = jb.ld;
+  uint16_t* __restrict__ dst = jb.dst;
   const int t = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.x * TR_R, c0 = (int64_t)blockIdx.y * TR_C;
+  const int64_t r0 = (loc % jb.gx) * TR_R, c0 = (loc / jb.gx) * TR_C;
   const int col = t & 31;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = (t >> 5) + 8 * i;
     const int64_t r = r0 + row;
     float v = 0.f;
-    if (r < rows) v = Act<TS>::ld(src, r * ld + c0 + col);
+    if (r < rows)
+      v = second ? Act<TB>::ld((const TB*)jb.src, r * ld + c0 + col)
+                 : Act<TA>::ld((const TA*)jb.src, r * ld + c0 + col);
     tile[col][row] = f2bf(v);
   }
   __syncthreads();
@@ -1322,9 +1339,16 @@ static hipError_t attn_launch_bf16(int64_t s_q, int64_t s_kv, int Hq, int Hkv, c
   const double pbytes = pairs * Hq * 2, qbytes = (double)s_q * Hq * D;
   const double kvbytes = (double)s_kv * Hkv * D;
   hipError_t e;
-  transpose_bf16_kernel<bf16><<<dim3((unsigned)(wl.LK / TR_R), (unsigned)(Hkv * D / TR_C)), 256,
-                                0, s>>>(s_kv, wl.LK, (int64_t)Hkv * D, (const bf16*)K, Kt);
-  mark("transpose_bf16", kvbytes * 2 + (double)Hkv * D * wl.LK * 2, 0, s);
+  // Kᵀ for dQ and, when dV is wanted, dCtxᵀ for it, in one launch
+  const TrJob jk{s_kv, wl.LK, (int64_t)Hkv * D, K, Kt, (int)(wl.LK / TR_R), (int)(Hkv * D / TR_C)};
+  const TrJob jd{s_q, wl.LQ, (int64_t)Hq * D, dctx, dCt, (int)(wl.LQ / TR_R),
+                 dv != nullptr ? (int)(Hq * D / TR_C) : 0};
+  const int64_t ntr = (int64_t)jk.gx * jk.gy + (int64_t)jd.gx * jd.gy;
+  transpose_bf16_kernel<bf16, float><<<dim3((unsigned)ntr), 256, 0, s>>>(jk, jd);
+  mark("transpose_bf16",
+       kvbytes * 2 + (double)Hkv * D * wl.LK * 2 +
+           (dv != nullptr ? qbytes * 4 + (double)Hq * D * wl.LQ * 2 : 0.0),
+       0, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ctx == nullptr) {
     attn_delta_kernel<bf16, D><<<dim3((unsigned)cdiv64(s_q, 4), (unsigned)Hq), 256, 0, s>>>(
@@ -1343,10 +1367,6 @@ static hipError_t attn_launch_bf16(int64_t s_q, int64_t s_kv, int Hq, int Hkv, c
   mark("attn_dq_bf16", pbytes + qbytes * (4 + 4 + (ctx ? 2 : 0)) + 2 * kvbytes * 2,
        4.0 * D * pairs * Hq, s);
   if ((e = hipGetLastError()) != hipSuccess || dv == nullptr) return e;
-  transpose_bf16_kernel<float><<<dim3((unsigned)(wl.LQ / TR_R), (unsigned)(Hq * D / TR_C)), 256,
-                                 0, s>>>(s_q, wl.LQ, (int64_t)Hq * D, dctx, dCt);
-  mark("transpose_bf16", qbytes * 4 + (double)Hq * D * wl.LQ * 2, 0, s);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   const DvPlan dp = dv_plan(s_q, s_kv, Hkv, grp, causal, HV_GEO, HV_WG_TARGET);
   float* part = dp.cmax > 1 ? (float*)(wb + wl.part) : dv;
   const dim3 grid((unsigned)dp.items);

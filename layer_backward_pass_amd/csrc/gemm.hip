@@ -339,7 +339,8 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
 // into one lane's operand half.  Double-buffered, one barrier per k-tile;
 // the operands of each half k-tile are read into registers during the
 // previous half's MFMAs (seq 2048 bf16 W_down 128.6 -> 122.6 us, gate/up
-// 236 -> 223 us).
+// 236 -> 223 us), and two register stages keep the global loads of the
+// next two k-tiles in flight (gate/up 219.5 -> 212.3 us).
 constexpr int H_BM = 128, H_BN = 256, H_BK = 64, H_NT = 512;
 constexpr int H_LDA = H_BK + 8, H_LDB = H_BN + 16;
 static_assert(2 * H_BK * H_LDB * 2 >= 64 * EPI_LD * 4, "activation stage fits in Bs");
@@ -461,18 +462,8 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
   // (k+1, first half) from Y, MFMAs of (k, second half), tile k+2 copied
   // from the register stage into X, tile k+3's global loads issued.  Loads
   // past the end read 0.
-  Stage st;
   Half h0, h1;
-  load(st, kbeg);
-  stash(st, 0);
-  load(st, kbeg + H_BK);
-  __syncthreads();
-  stash(st, 1);
-  load(st, kbeg + 2 * H_BK);
-  read_half(h0, 0, 0);
-  __syncthreads();
-  int buf = 0;
-  for (int64_t k0 = kbeg; k0 < kend; k0 += H_BK) {
+  auto step = [&](int buf, Stage& sx, int64_t knext) {
     read_half(h1, buf, 1);
     __builtin_amdgcn_sched_barrier(0);
     mma_half(h0);
@@ -482,9 +473,42 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
     __builtin_amdgcn_sched_barrier(0);
     mma_half(h1);
     __builtin_amdgcn_sched_barrier(0);
-    stash(st, buf);
-    load(st, k0 + 3 * H_BK);
-    buf ^= 1;
+    stash(sx, buf);
+    load(sx, knext);
+  };
+  if constexpr (!SPLITB) {
+    // two register stages used in turn: tiles k+2 and k+3 are in flight
+    // while tile k is multiplied (an odd tile count ends with a tile of
+    // zeros); the two-source loads of SPLITB leave no registers for it
+    Stage s0, s1;
+    load(s0, kbeg);
+    stash(s0, 0);
+    load(s0, kbeg + H_BK);
+    load(s1, kbeg + 2 * H_BK);
+    __syncthreads();
+    stash(s0, 1);
+    load(s0, kbeg + 3 * H_BK);
+    read_half(h0, 0, 0);
+    __syncthreads();
+    for (int64_t k0 = kbeg; k0 < kend; k0 += 2 * H_BK) {
+      step(0, s1, k0 + 4 * H_BK);
+      step(1, s0, k0 + 5 * H_BK);
+    }
+  } else {
+    Stage st;
+    load(st, kbeg);
+    stash(st, 0);
+    load(st, kbeg + H_BK);
+    __syncthreads();
+    stash(st, 1);
+    load(st, kbeg + 2 * H_BK);
+    read_half(h0, 0, 0);
+    __syncthreads();
+    int buf = 0;
+    for (int64_t k0 = kbeg; k0 < kend; k0 += H_BK) {
+      step(buf, st, k0 + 3 * H_BK);
+      buf ^= 1;
+    }
   }
   store_out<EPI>(epi, wk, M, N, wm, wn, acc, reinterpret_cast<float*>(&Bs[0][0][0]));
 }

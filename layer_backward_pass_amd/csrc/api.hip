@@ -746,11 +746,15 @@ int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weig
     if (sub)
       LBP_HIP(launch_rmsnorm_bwd(S, qd, a->ctx, dt, w->gamma_asub, plan.dctx, plan.dctx, d->eps, 0,
                                  stream));
-    // a split dq's second key half is added by the inverse RoPE pass
+    // the inverse RoPE (which also adds a split dq's second key half) runs in
+    // the attention's last launch where it can, else on its own
     const float* dq2 = nullptr;
+    const RopeArgs rope{dqp, d->pos0, d->rope_base};
+    bool rope_done = false;
     LBP_HIP(launch_attn_bwd(S, L, Hq, Hkv, D, plan.dctx, a->P, a->K, a->V, a->ctx, dt, plan.dq, dv,
-                            d->attn_scale, d->causal, plan.scratch, stream, &dq2));
-    LBP_HIP(launch_rope_bwd(S, Hq, D, plan.dq, dqp, d->pos0, d->rope_base, stream, dq2));
+                            d->attn_scale, d->causal, plan.scratch, stream, &dq2, &rope, &rope_done));
+    if (!rope_done)
+      LBP_HIP(launch_rope_bwd(S, Hq, D, plan.dq, dqp, d->pos0, d->rope_base, stream, dq2));
   }
   if (lq || lv) {
     // both adapters' gradient + AdamW passes in the same launches; the

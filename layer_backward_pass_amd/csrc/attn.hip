@@ -425,13 +425,11 @@ __global__ __launch_bounds__(256) void attn_dv_f32_kernel(int64_t s_q, int64_t s
 // dv[key][:] = sum of the chunk partials that exist for the key's tile (a
 // chunk is cs steps, see dv_item), in chunk order (zero when no query row
 // sees the key).
-__global__ __launch_bounds__(256) void attn_dv_reduce_kernel(int64_t s_q, int64_t s_kv,
-                                                             int64_t ldk, int cmax, int64_t cs,
-                                                             const float* __restrict__ part,
-                                                             float* __restrict__ dv, int causal,
-                                                             int grp, DvGeo geo) {
+__device__ __forceinline__ void dv_reduce_at(int64_t e, int64_t s_q, int64_t s_kv, int64_t ldk,
+                                             int cmax, int64_t cs, const float* __restrict__ part,
+                                             float* __restrict__ dv, int causal, int grp,
+                                             DvGeo geo) {
   const int64_t n4 = s_kv * ldk / 4;
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= n4) return;
   const int64_t key = 4 * e / ldk;
   const int64_t nch = cdiv64(dv_tile_steps(key / geo.kt, s_q, s_kv, grp, causal, geo), cs);
@@ -456,6 +454,63 @@ __global__ __launch_bounds__(256) void attn_dv_reduce_kernel(int64_t s_q, int64_
     }
   }
   reinterpret_cast<float4*>(dv)[e] = s;
+}
+
+__global__ __launch_bounds__(256) void attn_dv_reduce_kernel(int64_t s_q, int64_t s_kv,
+                                                             int64_t ldk, int cmax, int64_t cs,
+                                                             const float* __restrict__ part,
+                                                             float* __restrict__ dv, int causal,
+                                                             int grp, DvGeo geo) {
+  dv_reduce_at((int64_t)blockIdx.x * 256 + threadIdx.x, s_q, s_kv, ldk, cmax, cs, part, dv,
+               causal, grp, geo);
+}
+
+// The same reduction in its first nred workgroups, and the inverse RoPE of
+// dq (+ dq2) one row per workgroup after them: one launch instead of two.
+struct RopeRows {
+  const float* dy;
+  const float* dy2;
+  float* dx;
+  int64_t n_heads;
+  int head_dim, threads;
+  int64_t pos0;
+  double log2_base;
+};
+__global__ __launch_bounds__(256) void attn_dv_reduce_rope_kernel(
+    int64_t s_q, int64_t s_kv, int64_t ldk, int cmax, int64_t cs, const float* __restrict__ part,
+    float* __restrict__ dv, int causal, int grp, DvGeo geo, int64_t nred, RopeRows r) {
+  if ((int64_t)blockIdx.x < nred) {
+    dv_reduce_at((int64_t)blockIdx.x * 256 + threadIdx.x, s_q, s_kv, ldk, cmax, cs, part, dv,
+                 causal, grp, geo);
+    return;
+  }
+  if ((int)threadIdx.x >= r.threads) return;
+  rope_bwd_row((int64_t)blockIdx.x - nred, threadIdx.x, r.threads, r.n_heads, r.head_dim, r.dy,
+               r.dy2, r.dx, r.pos0, r.log2_base);
+}
+
+// The last launch of a dV with chunk partials: the reduction, with the
+// inverse RoPE of dq (rows s_q) when rope is set.
+static hipError_t launch_dv_reduce(int64_t s_q, int64_t s_kv, int Hq, int Hkv, int D, int cmax,
+                                   int64_t cs, const float* part, float* dv, int causal, DvGeo geo,
+                                   const float* dq, const float* dq2, const RopeArgs* rope,
+                                   bool* rope_done, hipStream_t s) {
+  const int64_t ldk = (int64_t)Hkv * D, n4 = s_kv * ldk / 4, nred = cdiv64(n4, 256);
+  const double kvbytes = (double)s_kv * ldk * 4;
+  if (rope == nullptr || rope_done == nullptr) {
+    attn_dv_reduce_kernel<<<dim3((unsigned)nred), 256, 0, s>>>(s_q, s_kv, ldk, cmax, cs, part, dv,
+                                                               causal, Hq / Hkv, geo);
+    mark("attn_dv_reduce", kvbytes * (cmax + 1), 0, s);
+    return hipGetLastError();
+  }
+  const RopeRows r{dq, dq2, rope->dx, Hq, D, rope_threads(Hq, D), rope->pos0,
+                   log2((double)rope->base)};
+  attn_dv_reduce_rope_kernel<<<dim3((unsigned)(nred + s_q)), 256, 0, s>>>(
+      s_q, s_kv, ldk, cmax, cs, part, dv, causal, Hq / Hkv, geo, nred, r);
+  const double qe = (double)s_q * Hq * D;
+  mark("attn_dv_reduce_rope", kvbytes * (cmax + 1) + qe * (dq2 ? 12 : 8), qe * 3, s);
+  *rope_done = true;
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- bfloat16
@@ -1255,7 +1310,8 @@ template <int D>
 static hipError_t attn_launch_f32(int64_t s_q, int64_t s_kv, int Hq, int Hkv, const float* dctx,
                                   const float* P, const float* K, const float* V,
                                   const float* ctx, float* dq, float* dv, float scale, int causal,
-                                  void* ws, hipStream_t s, const float** dq_second) {
+                                  void* ws, hipStream_t s, const float** dq_second,
+                                  const RopeArgs* rope, bool* rope_done) {
   const int grp = Hq / Hkv;
   const AttnWs wl = attn_ws(s_q, s_kv, Hq, Hkv, D, F32);
   float* delta = (float*)((char*)ws + wl.delta);
@@ -1300,11 +1356,8 @@ static hipError_t attn_launch_f32(int64_t s_q, int64_t s_kv, int Hq, int Hkv, co
   mark("attn_dv_f32", pbytes + qbytes + kvbytes * (dp.cmax > 1 ? dp.cmax : 1),
        2.0 * D * pairs * Hq, s);
   if ((e = hipGetLastError()) != hipSuccess || dp.cmax == 1) return e;
-  const int64_t n4 = s_kv * Hkv * D / 4;
-  attn_dv_reduce_kernel<<<dim3((unsigned)cdiv64(n4, 256)), 256, 0, s>>>(
-      s_q, s_kv, (int64_t)Hkv * D, dp.cmax, dp.cs, part, dv, causal, grp, FV_GEO);
-  mark("attn_dv_reduce", kvbytes * (dp.cmax + 1), 0, s);
-  return hipGetLastError();
+  return launch_dv_reduce(s_q, s_kv, Hq, Hkv, D, dp.cmax, dp.cs, part, dv, causal, FV_GEO, dq,
+                          ksplit && dq_second != nullptr ? dq2 : nullptr, rope, rope_done, s);
 }
 
 template <int D, int HW>
@@ -1328,7 +1381,8 @@ template <int D>
 static hipError_t attn_launch_bf16(int64_t s_q, int64_t s_kv, int Hq, int Hkv, const float* dctx,
                                    const uint16_t* P, const uint16_t* K, const uint16_t* V,
                                    const uint16_t* ctx, float* dq, float* dv, float scale,
-                                   int causal, void* ws, hipStream_t s) {
+                                   int causal, void* ws, hipStream_t s, const RopeArgs* rope,
+                                   bool* rope_done) {
   const int grp = Hq / Hkv;
   const AttnWs wl = attn_ws(s_q, s_kv, Hq, Hkv, D, BF16);
   char* wb = (char*)ws;
@@ -1379,11 +1433,8 @@ static hipError_t attn_launch_bf16(int64_t s_q, int64_t s_kv, int Hq, int Hkv, c
   mark("attn_dv_bf16", pbytes + qbytes * 2 + kvbytes * 4 * (dp.cmax > 1 ? dp.cmax : 1),
        2.0 * D * pairs * Hq, s);
   if ((e = hipGetLastError()) != hipSuccess || dp.cmax == 1) return e;
-  const int64_t n4 = s_kv * Hkv * D / 4;
-  attn_dv_reduce_kernel<<<dim3((unsigned)cdiv64(n4, 256)), 256, 0, s>>>(
-      s_q, s_kv, (int64_t)Hkv * D, dp.cmax, dp.cs, part, dv, causal, grp, HV_GEO);
-  mark("attn_dv_reduce", kvbytes * 4 * (dp.cmax + 1), 0, s);
-  return hipGetLastError();
+  return launch_dv_reduce(s_q, s_kv, Hq, Hkv, D, dp.cmax, dp.cs, part, dv, causal, HV_GEO, dq,
+                          nullptr, rope, rope_done, s);
 }
 
 template <typename T, int D>
@@ -1426,17 +1477,18 @@ template <typename T>
 static hipError_t attn_dispatch_d(int64_t s_q, int64_t s_kv, int Hq, int Hkv, int D,
                                   const float* dctx, const void* P, const void* K, const void* V,
                                   const void* ctx, float* dq, float* dv, float scale, int causal,
-                                  void* ws, hipStream_t s, const float** dq_second) {
+                                  void* ws, hipStream_t s, const float** dq_second,
+                                  const RopeArgs* rope, bool* rope_done) {
 #define LBP_ATTN_D(DD)                                                                         \
   case DD:                                                                                     \
     if constexpr (sizeof(T) == 4)                                                              \
       return attn_launch_f32<DD>(s_q, s_kv, Hq, Hkv, dctx, (const float*)P, (const float*)K,   \
                                  (const float*)V, (const float*)ctx, dq, dv, scale, causal, ws, \
-                                 s, dq_second);                                                \
+                                 s, dq_second, rope, rope_done);                               \
     else if constexpr (DD >= 32)                                                               \
       return attn_launch_bf16<DD>(s_q, s_kv, Hq, Hkv, dctx, (const uint16_t*)P,                \
                                   (const uint16_t*)K, (const uint16_t*)V, (const uint16_t*)ctx, \
-                                  dq, dv, scale, causal, ws, s);                               \
+                                  dq, dv, scale, causal, ws, s, rope, rope_done);              \
     else                                                                                       \
       return attn_launch<T, DD>(s_q, s_kv, Hq, Hkv, dctx, (const T*)P, (const T*)K,            \
                                 (const T*)V, (const T*)ctx, dq, dv, scale, causal, (float*)ws, s);
@@ -1455,8 +1507,9 @@ hipError_t launch_attn_bwd(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n
                            int64_t head_dim, const float* dctx, const void* P, const void* K,
                            const void* V, const void* ctx, int dt, float* dq, float* dv,
                            float scale, int causal, void* ws, hipStream_t s,
-                           const float** dq_second) {
+                           const float** dq_second, const RopeArgs* rope, bool* rope_done) {
   if (dq_second != nullptr) *dq_second = nullptr;
+  if (rope_done != nullptr) *rope_done = false;
   if (s_q == 0) {
     if (dv != nullptr) return launch_fill_zero(s_kv * n_kv_heads * head_dim, dv, s);
     return hipSuccess;
@@ -1480,9 +1533,11 @@ hipError_t launch_attn_bwd(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n
   }
   if (dt == F32)
     return attn_dispatch_d<float>(s_q, s_kv, (int)n_heads, (int)n_kv_heads, (int)head_dim, dctx,
-                                  P, K, V, ctx, dq, dv, scale, causal, ws, s, dq_second);
+                                  P, K, V, ctx, dq, dv, scale, causal, ws, s, dq_second, rope,
+                                  rope_done);
   return attn_dispatch_d<bf16>(s_q, s_kv, (int)n_heads, (int)n_kv_heads, (int)head_dim, dctx, P,
-                               K, V, ctx, dq, dv, scale, causal, ws, s, dq_second);
+                               K, V, ctx, dq, dv, scale, causal, ws, s, dq_second, rope,
+                               rope_done);
 }
 
 }  // namespace lbp

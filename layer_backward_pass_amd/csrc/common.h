@@ -181,6 +181,38 @@ __device__ __forceinline__ floatx4 mfma16x16x32bf16(ushortx8 a, ushortx8 b, floa
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Inverse NeoX RoPE of one row, all heads.  Hesper "Attention Backward GPU
+// Kernels", section "RoPE Backward (inverse rotation)", of dy (+ dy2: the two
+// key halves of a split attention dq, added here).  Thread tid < nthr is
+// (d, hg) = (tid % half, tid / half): it forms theta_d = pos * base^(-2d/D)
+// and its cosine and sine in float64 once, then rotates the (d, d + half)
+// pair of every head hg, hg + HG, ...  The angle of a late position needs
+// float64: at pos ~2e3 one float32 ulp of theta is ~1e-4 rad.
+__device__ __forceinline__ void rope_bwd_row(int64_t row, int tid, int nthr, int64_t n_heads,
+                                             int head_dim, const float* dy, const float* dy2,
+                                             float* dx, int64_t pos0, double log2_base) {
+  const int half = head_dim >> 1;
+  const int d = tid % half;
+  const int hg = tid / half;
+  const int HG = nthr / half;
+  const double pos = (double)(pos0 + row);
+  const double inv_freq = exp2(-(2.0 * d / head_dim) * log2_base);
+  double sn, cs;
+  sincos(pos * inv_freq, &sn, &cs);
+  const float c = (float)cs, s = (float)sn;
+  const int64_t base = row * n_heads * head_dim;
+  for (int64_t h = hg; h < n_heads; h += HG) {
+    const int64_t i = base + h * head_dim + d;
+    float lo = dy[i], hi = dy[i + half];
+    if (dy2 != nullptr) {
+      lo += dy2[i];
+      hi += dy2[i + half];
+    }
+    dx[i] = lo * c + hi * s;
+    dx[i + half] = -lo * s + hi * c;
+  }
+}
+
 // Gated activation backward of one element.
 //   SwiGLU (entrenar wgpu_backward.rs, "SiLU backward"): s = sigmoid(g),
 //     dGate = dH up s (1 + g (1 - s)),  dUp = dH g s

@@ -29,6 +29,20 @@ hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, c
 hipError_t launch_rope_bwd(int64_t rows, int64_t n_heads, int64_t head_dim, const float* dy,
                            float* dx, int64_t pos0, float base, hipStream_t s,
                            const float* dy2 = nullptr);
+// threads of a row of the inverse RoPE: (pair, head group), at most 256
+inline int rope_threads(int64_t n_heads, int64_t head_dim) {
+  const int half = (int)head_dim / 2;
+  int threads = 256 / half * half;
+  if ((int64_t)(threads / half) > n_heads) threads = (int)n_heads * half;
+  return threads;
+}
+// The inverse RoPE of the attention's dq rows into dx (positions pos0 ...),
+// for launch_attn_bwd to run inside its last launch.
+struct RopeArgs {
+  float* dx;
+  int64_t pos0;
+  float base;
+};
 // dgu[r, 0:I] = dGate, dgu[r, I:2I] = dUp; out_dt selects float or bf16 output;
 // dhid may be `nparts` split-K partial sums (stride pstride), added in order.
 hipError_t launch_act_bwd(int64_t rows, int64_t ffn, int act, const void* gate, const void* up,
@@ -188,13 +202,17 @@ size_t dec_attn_ws_bytes(int64_t s_kv, int64_t n_heads, int64_t head_dim);
 hipError_t launch_dec_attn(int dt, int head_dim, const DecAttnArgs& a, hipStream_t s);
 
 // ---- attention (attn.hip)
+// With rope set, the inverse RoPE of dq (plus the split second half) may run
+// in the launch that adds the dV chunk partials; *rope_done says whether it
+// did (else the caller runs it, with *dq_second as dy2).
 size_t attn_ws_bytes(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_kv_heads,
                      int64_t head_dim, int dt);
 hipError_t launch_attn_bwd(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_kv_heads,
                            int64_t head_dim, const float* dctx, const void* P, const void* K,
                            const void* V, const void* ctx, int dt, float* dq, float* dv,
                            float scale, int causal, void* ws, hipStream_t s,
-                           const float** dq_second = nullptr);
+                           const float** dq_second = nullptr, const RopeArgs* rope = nullptr,
+                           bool* rope_done = nullptr);
 
 // ---- LoRA + AdamW (lora.hip)
 size_t lora_ws_bytes(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank);

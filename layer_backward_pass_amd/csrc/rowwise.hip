@@ -213,46 +213,19 @@ hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, c
 }
 
 // ---------------------------------------------------------------------------
-// Inverse NeoX RoPE.  Hesper "Attention Backward GPU Kernels", section "RoPE
-// Backward (inverse rotation)", of dy (+ dy2: the two key halves of a split
-// attention dq, added here).  One workgroup per row; thread (d, hg)
-// forms theta_d = pos * base^(-2d/D) and its cosine and sine in float64 once,
-// then rotates the (d, d+half) pair of every head hg, hg+HG, ...  The angle
-// of a late position needs float64: at pos ~2e3 one float32 ulp of theta is
-// ~1e-4 rad.
+// Inverse NeoX RoPE (rope_bwd_row in common.h): one workgroup per row.
 __global__ __launch_bounds__(256) void rope_bwd_kernel(int64_t n_heads, int head_dim,
                                                        const float* dy, const float* dy2,
                                                        float* dx, int64_t pos0,
                                                        double log2_base) {
-  const int half = head_dim >> 1;
-  const int d = threadIdx.x % half;
-  const int hg = threadIdx.x / half;
-  const int HG = blockDim.x / half;
-  const int64_t row = blockIdx.x;
-  const double pos = (double)(pos0 + row);
-  const double inv_freq = exp2(-(2.0 * d / head_dim) * log2_base);
-  double sn, cs;
-  sincos(pos * inv_freq, &sn, &cs);
-  const float c = (float)cs, s = (float)sn;
-  const int64_t base = row * n_heads * head_dim;
-  for (int64_t h = hg; h < n_heads; h += HG) {
-    const int64_t i = base + h * head_dim + d;
-    float lo = dy[i], hi = dy[i + half];
-    if (dy2 != nullptr) {
-      lo += dy2[i];
-      hi += dy2[i + half];
-    }
-    dx[i] = lo * c + hi * s;
-    dx[i + half] = -lo * s + hi * c;
-  }
+  rope_bwd_row(blockIdx.x, threadIdx.x, blockDim.x, n_heads, head_dim, dy, dy2, dx, pos0,
+               log2_base);
 }
 
 hipError_t launch_rope_bwd(int64_t rows, int64_t n_heads, int64_t head_dim, const float* dy,
                            float* dx, int64_t pos0, float base, hipStream_t s, const float* dy2) {
   if (rows == 0) return hipSuccess;
-  const int half = (int)head_dim / 2;
-  int threads = 256 / half * half;
-  if ((int64_t)(threads / half) > n_heads) threads = (int)n_heads * half;
+  const int threads = rope_threads(n_heads, head_dim);
   rope_bwd_kernel<<<dim3((unsigned)rows), dim3(threads), 0, s>>>(n_heads, (int)head_dim, dy, dy2,
                                                                    dx, pos0, log2((double)base));
   mark("rope_bwd", (double)rows * n_heads * head_dim * (dy2 ? 12 : 8),

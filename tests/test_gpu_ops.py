@@ -148,6 +148,22 @@ def test_attention_without_dv_and_empty_queries():
     assert torch.count_nonzero(dv).item() == 0
 
 
+@pytest.mark.parametrize("s_q,s_kv,Hq,Hkv,D,dt", [
+    (96, 96, 8, 2, 128, BF16),    # the bf16 MFMA kernels: only Kᵀ is transposed
+    (130, 200, 8, 2, 64, BF16),
+    (70, 70, 8, 2, 128, F32),     # fp32 MFMA kernels with the causal key split
+])
+def test_attention_dq_only(s_q, s_kv, Hq, Hkv, D, dt):
+    """dQ without dV on the MFMA paths (no dV launches, no dCtx transpose)."""
+    dctx, P, K, V, ctx = _attn_inputs(9, s_q, s_kv, Hq, Hkv, D, True, dt)
+    dq = torch.empty(s_q, Hq * D, device=DEV)
+    lbp().lorabwd_attn_backward(dctx, P, K, V, ctx, dq, None, Hq, Hkv, D)
+    torch.cuda.synchronize()
+    wq, _ = OB.attention_bwd(Hn.host(dctx), Hn.host(P), Hn.host(K), Hn.host(V), Hq, Hkv,
+                             D ** -0.5)
+    assert Hn.rel_err(Hn.host(dq), wq) <= tol(dt)
+
+
 # ------------------------------------------------------------------ FFN
 @pytest.mark.parametrize("rows,dim,ffn,act,sub,dt", [
     (16, 64, 256, "swiglu", False, F32),

@@ -136,7 +136,8 @@ hipError_t ffn_run(int64_t rows, int64_t dim, int64_t ffn, int act, const float*
                    const void* w_down, const void* w_gate, const void* w_up, const void* gate,
                    const void* up_, const void* hidden_pre, const float* gamma_sub,
                    const void* resid1, const float* gamma_ffn, float* d_resid, float eps, int dt,
-                   void* ws, hipStream_t s, const float* resid_in = nullptr) {
+                   void* ws, hipStream_t s, const float* resid_in = nullptr,
+                   uint16_t* d_resid16 = nullptr) {
   if (rows == 0) return hipSuccess;
   FfnPlan p = ffn_plan(ws, rows, dim, ffn, dt);
   hipError_t e;
@@ -224,9 +225,10 @@ hipError_t ffn_run(int64_t rows, int64_t dim, int64_t ffn, int act, const float*
   e = launch_gemm(rows, dim, 2 * ffn, p.dgu, dt, 2 * ffn, w_gate, w_up, ffn, dt, dim, p.dn2, dim,
                   p.partials, s, &n2);
   if (e != hipSuccess) return e;
-  // 5. d_resid = (resid_in or d_resid) + rmsnorm_bwd(resid1, gamma_ffn, dN2)
+  // 5. d_resid = (resid_in or d_resid) + rmsnorm_bwd(resid1, gamma_ffn, dN2),
+  // with a bf16 copy in d_resid16 when asked for
   return launch_rmsnorm_bwd(rows, dim, resid1, dt, gamma_ffn, n2 > 1 ? p.partials : p.dn2, d_resid,
-                            eps, 1, s, n2, n2 > 1 ? rows * dim : 0, resid_in);
+                            eps, 1, s, n2, n2 > 1 ? rows * dim : 0, resid_in, d_resid16);
 }
 
 // ---------------------------------------------------------------- LoRA
@@ -432,6 +434,7 @@ namespace {
 
 struct LayerPlan {
   float *dctx, *dq, *dv;
+  uint16_t* h16;  // bf16 copy of dH1: the W_o product's operand (bf16 sequence layers)
   float *part2, *x2, *scal1, *scal2, *scal3, *dA;  // single-token chain only
   void* scratch;
   size_t lora_v_off;  // the V adapter's LoRA workspace: scratch + lora_v_off
@@ -471,6 +474,7 @@ LayerPlan layer_plan(void* ws, const lorabwd_layer_desc* d, int64_t rq, int64_t 
     for (size_t v : {dgemv_part_bytes(I, H), dgemv_part_bytes(qd, H, PRO_RESID)})
       if (v > sc) sc = v;
   } else {
+    if (d->dtype == BF16 && S > 1) p.h16 = c.take<uint16_t>((size_t)S * H * 2);
     const size_t f = ffn_plan(nullptr, S, H, I, d->dtype).bytes;
     const size_t o = S == 1 ? dgemv_part_bytes(qd, H) : gemm_partial_bytes(S, qd, H, F32, d->dtype);
     const size_t a = up(attn_ws_bytes(S, L, d->n_heads, d->n_kv_heads, d->head_dim, d->dtype));
@@ -723,7 +727,7 @@ int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weig
     LBP_HIP(ffn_run(S, H, I, d->act, din, w->w_down, w->w_gate, w->w_up, a->gate, a->up,
                     sub ? a->hidden_pre : nullptr, sub ? w->gamma_fsub : nullptr, a->resid1,
                     w->gamma_ffn, d_hidden, d->eps, dt, plan.scratch, stream,
-                    din == d_hidden ? nullptr : din));
+                    din == d_hidden ? nullptr : din, plan.h16));
     // O-projection backward: dCtx = dH1 W_o
     if (S == 1) {
       GemvArgs g{};
@@ -740,7 +744,9 @@ int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weig
       r.y = plan.dctx;
       LBP_HIP(launch_dgemv_red(RED_STORE, dt, r, stream));
     } else {
-      LBP_HIP(launch_gemm(S, qd, H, d_hidden, F32, H, w->w_o, nullptr, H, dt, qd, plan.dctx, qd,
+      // bf16 weights take the bf16 copy the FFN norm wrote (no rounding pass)
+      LBP_HIP(launch_gemm(S, qd, H, plan.h16 ? (const void*)plan.h16 : (const void*)d_hidden,
+                          plan.h16 ? BF16 : F32, H, w->w_o, nullptr, H, dt, qd, plan.dctx, qd,
                           (float*)plan.scratch, stream));
     }
     if (sub)

@@ -20,11 +20,11 @@ enum ActKind { SWIGLU = 0, RELU2 = 1 };
 // ---- row-wise kernels (rowwise.hip)
 // dy may be `nparts` split-K partial sums [nparts][rows][n] (stride pstride),
 // added in order; dx may alias dy when nparts == 1.  accumulate: dx = rin +
-// result (rin NULL: dx += result).
+// result (rin NULL: dx += result).  dx16 (may be NULL): a bf16 copy of dx.
 hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, const float* gamma,
                               const float* dy, float* dx, float eps, int accumulate,
                               hipStream_t s, int nparts = 1, int64_t pstride = 0,
-                              const float* rin = nullptr);
+                              const float* rin = nullptr, uint16_t* dx16 = nullptr);
 // dy2 (may be NULL): a second term added to dy before the rotation
 hipError_t launch_rope_bwd(int64_t rows, int64_t n_heads, int64_t head_dim, const float* dy,
                            float* dx, int64_t pos0, float base, hipStream_t s,

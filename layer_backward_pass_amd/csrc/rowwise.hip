@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int64_t n, const T* __
                                                           const float* __restrict__ gamma,
                                                           const float* dy, float* dx,
                                                           float eps, int nparts, int64_t pstride,
-                                                          const float* rin) {
+                                                          const float* rin, uint16_t* dx16) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const T* xr = x + row * n;
@@ -83,6 +83,8 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int64_t n, const T* __
       o.w += p.w;
     }
     *dp = o;
+    if (dx16 != nullptr)
+      *reinterpret_cast<uint2*>(dx16 + row * n + i) = make_uint2(pk_bf16(o.x, o.y), pk_bf16(o.z, o.w));
   }
 }
 
@@ -94,7 +96,8 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_reg_kernel(int64_t n, const T
                                                               const float* __restrict__ gamma,
                                                               const float* dy, float* dx,
                                                               float eps, int nparts,
-                                                              int64_t pstride, const float* rin) {
+                                                              int64_t pstride, const float* rin,
+                                                              uint16_t* dx16) {
   constexpr int PB = Q <= 4 ? 4 : 2;
   __shared__ float red[4];
   const int t = threadIdx.x;
@@ -168,12 +171,16 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_reg_kernel(int64_t n, const T
       o.w += pr.w;
     }
     *dp = o;
+    if (dx16 != nullptr)
+      *reinterpret_cast<uint2*>(dx16 + row * n + 4 * i4) =
+          make_uint2(pk_bf16(o.x, o.y), pk_bf16(o.z, o.w));
   }
 }
 
 hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, const float* gamma,
                               const float* dy, float* dx, float eps, int accumulate,
-                              hipStream_t s, int nparts, int64_t pstride, const float* rin) {
+                              hipStream_t s, int nparts, int64_t pstride, const float* rin,
+                              uint16_t* dx16) {
   if (rows == 0) return hipSuccess;
   dim3 grid((unsigned)rows), block(256);
   const int64_t Q = cdiv(n / 4, 256);
@@ -182,10 +189,10 @@ hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, c
   case QV:                                                                                      \
     if (accumulate)                                                                             \
       rmsnorm_bwd_reg_kernel<T, 1, QV><<<grid, block, 0, s>>>(n, (const T*)x, gamma, dy, dx,    \
-                                                             eps, nparts, pstride, rin);        \
+                                                             eps, nparts, pstride, rin, dx16);        \
     else                                                                                        \
       rmsnorm_bwd_reg_kernel<T, 0, QV><<<grid, block, 0, s>>>(n, (const T*)x, gamma, dy, dx,    \
-                                                             eps, nparts, pstride, rin);        \
+                                                             eps, nparts, pstride, rin, dx16);        \
     break;
     if (xdt == F32) {
       switch (Q) { LBP_RN(float, 1) LBP_RN(float, 2) LBP_RN(float, 3) LBP_RN(float, 4)
@@ -197,14 +204,14 @@ hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, c
 #undef LBP_RN
   } else if (xdt == F32) {
     if (accumulate)
-      rmsnorm_bwd_kernel<float, 1><<<grid, block, 0, s>>>(n, (const float*)x, gamma, dy, dx, eps, nparts, pstride, rin);
+      rmsnorm_bwd_kernel<float, 1><<<grid, block, 0, s>>>(n, (const float*)x, gamma, dy, dx, eps, nparts, pstride, rin, dx16);
     else
-      rmsnorm_bwd_kernel<float, 0><<<grid, block, 0, s>>>(n, (const float*)x, gamma, dy, dx, eps, nparts, pstride, rin);
+      rmsnorm_bwd_kernel<float, 0><<<grid, block, 0, s>>>(n, (const float*)x, gamma, dy, dx, eps, nparts, pstride, rin, dx16);
   } else {
     if (accumulate)
-      rmsnorm_bwd_kernel<bf16, 1><<<grid, block, 0, s>>>(n, (const bf16*)x, gamma, dy, dx, eps, nparts, pstride, rin);
+      rmsnorm_bwd_kernel<bf16, 1><<<grid, block, 0, s>>>(n, (const bf16*)x, gamma, dy, dx, eps, nparts, pstride, rin, dx16);
     else
-      rmsnorm_bwd_kernel<bf16, 0><<<grid, block, 0, s>>>(n, (const bf16*)x, gamma, dy, dx, eps, nparts, pstride, rin);
+      rmsnorm_bwd_kernel<bf16, 0><<<grid, block, 0, s>>>(n, (const bf16*)x, gamma, dy, dx, eps, nparts, pstride, rin, dx16);
   }
   mark("rmsnorm_bwd",
        (double)rows * n * ((xdt == F32 ? 4 : 2) + 4 * nparts + 4 + (accumulate ? 4 : 0)) + n * 4.0,

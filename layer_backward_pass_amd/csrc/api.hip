@@ -729,6 +729,7 @@ int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weig
                     w->gamma_ffn, d_hidden, d->eps, dt, plan.scratch, stream,
                     din == d_hidden ? nullptr : din, plan.h16));
     // O-projection backward: dCtx = dH1 W_o
+    bool dct_ready = false;
     if (S == 1) {
       GemvArgs g{};
       g.N = qd;
@@ -744,10 +745,19 @@ int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weig
       r.y = plan.dctx;
       LBP_HIP(launch_dgemv_red(RED_STORE, dt, r, stream));
     } else {
-      // bf16 weights take the bf16 copy the FFN norm wrote (no rounding pass)
+      // bf16 weights take the bf16 copy the FFN norm wrote (no rounding
+      // pass); without the sub-norm (which changes dCtx afterwards) the
+      // product also writes dCtxᵀ for the attention's dV (whole row blocks
+      // of 64 queries, so the attention finds no padding to clear)
+      int64_t LQ = 0;
+      uint16_t* dct = !sub && S % 64 == 0
+                          ? attn_dct_buffer(plan.scratch, S, L, Hq, Hkv, D, dt, &LQ)
+                          : nullptr;
+      const TCopy tc{dct, LQ};
       LBP_HIP(launch_gemm(S, qd, H, plan.h16 ? (const void*)plan.h16 : (const void*)d_hidden,
                           plan.h16 ? BF16 : F32, H, w->w_o, nullptr, H, dt, qd, plan.dctx, qd,
-                          (float*)plan.scratch, stream));
+                          (float*)plan.scratch, stream, nullptr, nullptr, nullptr,
+                          dct ? &tc : nullptr, &dct_ready));
     }
     if (sub)
       LBP_HIP(launch_rmsnorm_bwd(S, qd, a->ctx, dt, w->gamma_asub, plan.dctx, plan.dctx, d->eps, 0,
@@ -758,7 +768,8 @@ int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weig
     const RopeArgs rope{dqp, d->pos0, d->rope_base};
     bool rope_done = false;
     LBP_HIP(launch_attn_bwd(S, L, Hq, Hkv, D, plan.dctx, a->P, a->K, a->V, a->ctx, dt, plan.dq, dv,
-                            d->attn_scale, d->causal, plan.scratch, stream, &dq2, &rope, &rope_done));
+                            d->attn_scale, d->causal, plan.scratch, stream, &dq2, &rope, &rope_done,
+                            dct_ready));
     if (!rope_done)
       LBP_HIP(launch_rope_bwd(S, Hq, D, plan.dq, dqp, d->pos0, d->rope_base, stream, dq2));
   }

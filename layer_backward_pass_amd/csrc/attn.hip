@@ -1382,7 +1382,7 @@ static hipError_t attn_launch_bf16(int64_t s_q, int64_t s_kv, int Hq, int Hkv, c
                                    const uint16_t* P, const uint16_t* K, const uint16_t* V,
                                    const uint16_t* ctx, float* dq, float* dv, float scale,
                                    int causal, void* ws, hipStream_t s, const RopeArgs* rope,
-                                   bool* rope_done) {
+                                   bool* rope_done, bool dct_ready) {
   const int grp = Hq / Hkv;
   const AttnWs wl = attn_ws(s_q, s_kv, Hq, Hkv, D, BF16);
   char* wb = (char*)ws;
@@ -1396,12 +1396,12 @@ static hipError_t attn_launch_bf16(int64_t s_q, int64_t s_kv, int Hq, int Hkv, c
   // Kᵀ for dQ and, when dV is wanted, dCtxᵀ for it, in one launch
   const TrJob jk{s_kv, wl.LK, (int64_t)Hkv * D, K, Kt, (int)(wl.LK / TR_R), (int)(Hkv * D / TR_C)};
   const TrJob jd{s_q, wl.LQ, (int64_t)Hq * D, dctx, dCt, (int)(wl.LQ / TR_R),
-                 dv != nullptr ? (int)(Hq * D / TR_C) : 0};
+                 dv != nullptr && !dct_ready ? (int)(Hq * D / TR_C) : 0};
   const int64_t ntr = (int64_t)jk.gx * jk.gy + (int64_t)jd.gx * jd.gy;
   transpose_bf16_kernel<bf16, float><<<dim3((unsigned)ntr), 256, 0, s>>>(jk, jd);
   mark("transpose_bf16",
        kvbytes * 2 + (double)Hkv * D * wl.LK * 2 +
-           (dv != nullptr ? qbytes * 4 + (double)Hq * D * wl.LQ * 2 : 0.0),
+           (jd.gy > 0 ? qbytes * 4 + (double)Hq * D * wl.LQ * 2 : 0.0),
        0, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ctx == nullptr) {
@@ -1478,7 +1478,7 @@ static hipError_t attn_dispatch_d(int64_t s_q, int64_t s_kv, int Hq, int Hkv, in
                                   const float* dctx, const void* P, const void* K, const void* V,
                                   const void* ctx, float* dq, float* dv, float scale, int causal,
                                   void* ws, hipStream_t s, const float** dq_second,
-                                  const RopeArgs* rope, bool* rope_done) {
+                                  const RopeArgs* rope, bool* rope_done, bool dct_ready) {
 #define LBP_ATTN_D(DD)                                                                         \
   case DD:                                                                                     \
     if constexpr (sizeof(T) == 4)                                                              \
@@ -1488,7 +1488,7 @@ static hipError_t attn_dispatch_d(int64_t s_q, int64_t s_kv, int Hq, int Hkv, in
     else if constexpr (DD >= 32)                                                               \
       return attn_launch_bf16<DD>(s_q, s_kv, Hq, Hkv, dctx, (const uint16_t*)P,                \
                                   (const uint16_t*)K, (const uint16_t*)V, (const uint16_t*)ctx, \
-                                  dq, dv, scale, causal, ws, s, rope, rope_done);              \
+                                  dq, dv, scale, causal, ws, s, rope, rope_done, dct_ready);   \
     else                                                                                       \
       return attn_launch<T, DD>(s_q, s_kv, Hq, Hkv, dctx, (const T*)P, (const T*)K,            \
                                 (const T*)V, (const T*)ctx, dq, dv, scale, causal, (float*)ws, s);
@@ -1507,7 +1507,8 @@ hipError_t launch_attn_bwd(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n
                            int64_t head_dim, const float* dctx, const void* P, const void* K,
                            const void* V, const void* ctx, int dt, float* dq, float* dv,
                            float scale, int causal, void* ws, hipStream_t s,
-                           const float** dq_second, const RopeArgs* rope, bool* rope_done) {
+                           const float** dq_second, const RopeArgs* rope, bool* rope_done,
+                           bool dct_ready) {
   if (dq_second != nullptr) *dq_second = nullptr;
   if (rope_done != nullptr) *rope_done = false;
   if (s_q == 0) {
@@ -1534,10 +1535,19 @@ hipError_t launch_attn_bwd(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n
   if (dt == F32)
     return attn_dispatch_d<float>(s_q, s_kv, (int)n_heads, (int)n_kv_heads, (int)head_dim, dctx,
                                   P, K, V, ctx, dq, dv, scale, causal, ws, s, dq_second, rope,
-                                  rope_done);
+                                  rope_done, false);
   return attn_dispatch_d<bf16>(s_q, s_kv, (int)n_heads, (int)n_kv_heads, (int)head_dim, dctx, P,
                                K, V, ctx, dq, dv, scale, causal, ws, s, dq_second, rope,
-                               rope_done);
+                               rope_done, dct_ready);
+}
+
+uint16_t* attn_dct_buffer(void* ws, int64_t s_q, int64_t s_kv, int64_t n_heads,
+                          int64_t n_kv_heads, int64_t head_dim, int dt, int64_t* LQ) {
+  // the bf16 MFMA launch is the one that takes dCtxᵀ (sequence rows)
+  if (s_q <= 1 || dt != BF16 || !bf16_mfma_path(dt, head_dim)) return nullptr;
+  const AttnWs wl = attn_ws(s_q, s_kv, n_heads, n_kv_heads, head_dim, dt);
+  *LQ = wl.LQ;
+  return (uint16_t*)((char*)ws + wl.dct);
 }
 
 }  // namespace lbp

@@ -199,14 +199,53 @@ __device__ __forceinline__ float f4at(const float4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
+// A whole 128 x 256 tile also stored as a bf16 copy transposed, T[c][r]
+// (row stride e.ldt) for its columns c and rows r.  The accumulators pass
+// through LDS as bf16 [256 columns][128 rows + 8] (the B staging area), so
+// each thread then writes 16-byte chunks of 8 rows of one column.  M % 8 == 0.
+constexpr int TC_LD = 136;
+__device__ __forceinline__ void tcopy_tile_epilogue(const ActEpi& e, int64_t M, int64_t N,
+                                                    int64_t bm, int64_t bn, int wm, int wn,
+                                                    const floatx4 (&acc)[4][4],
+                                                    uint16_t* stage) {
+  const int t = threadIdx.x, lane = t & 63;
+  uint16_t* T = (uint16_t*)e.out;
+  __syncthreads();  // every wave is past its last LDS read of the k-loop
+#pragma unroll
+  for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+    for (int fj = 0; fj < 4; ++fj)
+#pragma unroll
+      for (int v = 0; v < 4; v += 2) {
+        const int row = wm + fi * 16 + 4 * (lane >> 4) + v, col = wn + fj * 16 + (lane & 15);
+        *reinterpret_cast<uint32_t*>(&stage[col * TC_LD + row]) =
+            pk_bf16(acc[fi][fj][v], acc[fi][fj][v + 1]);
+      }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int ch = t + 512 * i, col = ch >> 4, r8 = 8 * (ch & 15);
+    const int64_t gc = bn + col, gr = bm + r8;
+    if (gc < N && gr < M)
+      *reinterpret_cast<uint4*>(T + gc * e.ldt + gr) =
+          *reinterpret_cast<const uint4*>(&stage[col * TC_LD + r8]);
+  }
+}
+
 // The store of a product's 128 x 256 tile: through the activation backward
 // for a whole tile of an ACT-epilogue launch, else plain (C, or a partial
-// slot).  EPI: 0 plain, else 1 + act + 2 (gate/up bf16) + 4 (out bf16).
+// slot), for EPI 16 plus the transposed bf16 copy.  EPI: 0 plain, 16
+// transposed copy, else 1 + act + 2 (gate/up bf16) + 4 (out bf16).
 template <int EPI>
 __device__ __forceinline__ void store_out(const ActEpi& e, const GemmWork& wk, int64_t M,
                                           int64_t N, int wm, int wn, const floatx4 (&acc)[4][4],
                                           float* stage) {
-  if constexpr (EPI != 0) {
+  if constexpr (EPI == 16) {
+    store_tile<4, 4>(wk.out, wk.ldo, M, N, wk.bm + wm, wk.bn + wn, acc);
+    if (wk.whole)
+      tcopy_tile_epilogue(e, M, N, wk.bm, wk.bn, wm, wn, acc, reinterpret_cast<uint16_t*>(stage));
+    return;
+  } else if constexpr (EPI != 0) {
     if (wk.whole) {
       constexpr int ACT = (EPI - 1) & 1;
       constexpr bool GB = ((EPI - 1) & 2) != 0, OB = ((EPI - 1) & 4) != 0;
@@ -344,6 +383,7 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
 constexpr int H_BM = 128, H_BN = 256, H_BK = 64, H_NT = 512;
 constexpr int H_LDA = H_BK + 8, H_LDB = H_BN + 16;
 static_assert(2 * H_BK * H_LDB * 2 >= 64 * EPI_LD * 4, "activation stage fits in Bs");
+static_assert(2 * H_BK * H_LDB >= H_BN * TC_LD, "transposed-copy stage fits in Bs");
 
 template <bool SPLITB, int EPI>
 __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, int64_t K,
@@ -655,9 +695,10 @@ __global__ __launch_bounds__(256) void cvt_a_bf16_kernel(int64_t M, int64_t K, c
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt, int64_t lda,
                        const void* B1, const void* B2, int64_t K1, int b_dt, int64_t ldb,
                        float* C, int64_t ldc, float* partials, hipStream_t s, int* deferred,
-                       const ActEpi* act, bool* act_done) {
+                       const ActEpi* act, bool* act_done, const TCopy* tc, bool* tc_done) {
   if (deferred) *deferred = 1;
   if (act_done) *act_done = false;
+  if (tc_done) *tc_done = false;
   if (M == 0 || N == 0) return hipSuccess;
   const GemmPlan pl = gemm_plan(M, N, K, b_dt);
   const int64_t kps = pl.kps, nfull = pl.nfull;
@@ -669,9 +710,17 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
   const bool use_act = act != nullptr && (nsp == 1 || nfull > 0) &&
                        act->gdt == b_dt && act->odt == b_dt && ldc == N && N % 8 == 0 &&
                        128.0 * N * 4 < BUF_MAX_BYTES;
-  const int epi = use_act ? 1 + act->act + (b_dt == BF16 ? 6 : 0) : 0;
-  const ActEpi ea = use_act ? *act : ActEpi{};
+  // the transposed bf16 copy: every tile whole, bf16 operands
+  const bool use_tc = !use_act && tc != nullptr && tc_done != nullptr && nsp == 1 &&
+                      b_dt == BF16 && a_dt == BF16 && M % 8 == 0 && tc->ld % 8 == 0;
+  const int epi = use_act ? 1 + act->act + (b_dt == BF16 ? 6 : 0) : (use_tc ? 16 : 0);
+  ActEpi ea = use_act ? *act : ActEpi{};
+  if (use_tc) {
+    ea.out = tc->dst;
+    ea.ldt = tc->ld;
+  }
   if (act_done) *act_done = use_act;
+  if (tc_done) *tc_done = use_tc;
   const int64_t tiles = cdiv(N, pl.bn) * cdiv(M, pl.bm);
   const dim3 grid1((unsigned)(nfull + (tiles - nfull) * nsp));
   if (B2 == nullptr) {
@@ -715,6 +764,9 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
     } else if (epi == 8) {
       if (splitb) LBP_GEMM_BF16(true, 8);
       else LBP_GEMM_BF16(false, 8);
+    } else if (epi == 16) {
+      if (splitb) LBP_GEMM_BF16(true, 16);
+      else LBP_GEMM_BF16(false, 16);
     } else {
       if (splitb) LBP_GEMM_BF16(true, 0);
       else LBP_GEMM_BF16(false, 0);
@@ -727,7 +779,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
   const double es = b_dt == F32 ? 4 : 2;
   mark(b_dt == F32 ? "gemm_f32_mfma" : "gemm_bf16_mfma",
        (double)M * K * (a_dt == F32 ? 4 : 2) + (double)K * N * es +
-           (use_act ? (double)M * N * 4 * es : (double)M * N * 4),
+           (use_act ? (double)M * N * 4 * es : (double)M * N * (use_tc ? 6 : 4)),
        2.0 * M * N * K, s);
   if (e != hipSuccess || nsp == 1) return e;
   if (deferred && nfull == 0) {

@@ -74,12 +74,20 @@ struct ActEpi {
   void* out;
   int act;  // ActKind
   int gdt, odt;
+  int64_t ldt;  // (transposed copy) row stride of out
+};
+// With `tc` set (bf16 weights and A, no split), C is also written as a bf16
+// copy transposed, tc->dst[n][m] with row stride tc->ld; *tc_done says so.
+struct TCopy {
+  uint16_t* dst;
+  int64_t ld;
 };
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt, int64_t lda,
                        const void* B1, const void* B2, int64_t K1, int b_dt, int64_t ldb,
                        float* C, int64_t ldc, float* partials, hipStream_t s,
                        int* deferred = nullptr, const ActEpi* act = nullptr,
-                       bool* act_done = nullptr);
+                       bool* act_done = nullptr, const TCopy* tc = nullptr,
+                       bool* tc_done = nullptr);
 
 // ---- single-token (decode) kernels (decode.hip)
 // part[chunk, N] = x[K] W[K, N] over row chunks of kc rows (W rows k < K1
@@ -212,7 +220,12 @@ hipError_t launch_attn_bwd(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n
                            const void* V, const void* ctx, int dt, float* dq, float* dv,
                            float scale, int causal, void* ws, hipStream_t s,
                            const float** dq_second = nullptr, const RopeArgs* rope = nullptr,
-                           bool* rope_done = nullptr);
+                           bool* rope_done = nullptr, bool dct_ready = false);
+// The bf16 attention's dCtxᵀ buffer inside its workspace (bf16 [Hq D][LQ],
+// LQ = s_q rounded up to 64), or NULL where the path takes none.  A caller
+// that fills it (dct_ready) spares the attention its transposition.
+uint16_t* attn_dct_buffer(void* ws, int64_t s_q, int64_t s_kv, int64_t n_heads,
+                          int64_t n_kv_heads, int64_t head_dim, int dt, int64_t* LQ);
 
 // ---- LoRA + AdamW (lora.hip)
 size_t lora_ws_bytes(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank);

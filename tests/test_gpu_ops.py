@@ -279,6 +279,9 @@ def test_lora_adamw(rows, H, out, rank, step, dt):
                 "pos0": 1900}),
     ("seq512", {"seq": 70, "kv_len": 70, "hidden": 256, "ffn": 512, "n_heads": 4,
                 "n_kv_heads": 2, "head_dim": 128, "rank": 4, "alpha": 8.0, "pos0": 3000}),
+    # bf16, whole 64-query blocks: the W_o product also writes dCtxᵀ for dV
+    ("seq512", {"seq": 128, "kv_len": 128, "hidden": 256, "ffn": 512, "n_heads": 8,
+                "n_kv_heads": 2, "head_dim": 128, "rank": 8, "alpha": 16.0, "dtype": "bf16"}),
 ])
 def test_layer_small(name, over):
     cfg = synth.get_config(name).with_(**over)

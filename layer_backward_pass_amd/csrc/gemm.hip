@@ -6,7 +6,8 @@
 // Split-K partial sums go to caller scratch and are reduced in a fixed
 // order (no float atomics), so results are bitwise reproducible.  The W_down
 // product can apply the gated-activation backward to its output as it is
-// stored (ActEpi), so dHid never goes to memory.
+// stored (ActEpi), so dHid never goes to memory; the W_o product can also
+// store its output transposed in bf16 (TCopy) for the attention's dV.
 #include <type_traits>
 
 #include "common.h"

@@ -47,7 +47,7 @@ PEAK = {  # MI355X published peaks (dense)
     "f32_TFLOPs": 157.3,
     "bf16_TFLOPs": 2516.6,
 }
-COPIES = {"decode": 6, "tiny": 1, "seq512": 2, "seq2048bf16": 2, "stack36": 1}
+COPIES = {"decode": 6, "tiny": 1, "seq512": 4, "seq2048bf16": 4, "stack36": 1}
 DEFAULT_STEPS = {"decode": 2000, "tiny": 2000, "seq512": 200, "seq2048bf16": 100, "stack36": 5}
 
 

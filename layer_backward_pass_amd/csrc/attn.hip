@@ -612,19 +612,26 @@ __device__ __forceinline__ ushortx8 load_p8(brsrc_t r, bool ok, int64_t row, int
 
 constexpr int HQ_KT = 64;  // keys per tile, bf16 dq kernel
 
+// LDS of the bf16 dQ and dV workgroups (16-bit elements)
+template <int D>
+constexpr int dq_bf16_lds() {
+  return 2 * HQ_KT * (D + 8) + 2 * D * (HQ_KT + 8);
+}
+
+// Workgroup blk of the bf16 dQ launch, on the LDS at smem (dq_bf16_lds).
 template <int D, int HW, bool PVEC>
-__global__ __launch_bounds__(256, 2) void attn_dq_bf16_kernel(
-    int64_t s_q, int64_t s_kv, int Hq, int grp, int64_t LK, int npairs,
+__device__ __forceinline__ void attn_dq_bf16_body(
+    int64_t blk, int64_t s_q, int64_t s_kv, int Hq, int grp, int64_t LK, int npairs,
     const float* __restrict__ dctx, const uint16_t* __restrict__ P,
     const uint16_t* __restrict__ Kt, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ ctx, const float* __restrict__ delta_ws, float* __restrict__ dq,
-    float scale, int causal) {
+    float scale, int causal, uint16_t* smem) {
   constexpr int KT = HQ_KT, NK = D / 32, ND = D / 16, QW = 4 / HW;
   constexpr int VLD = D + 8, KLD = KT + 8;
   constexpr int NCH = KT * D / 8;            // 16-byte chunks per staged matrix
   constexpr int SE = (NCH + 255) / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KT][VLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][D][KLD];
+  auto& Vs = *reinterpret_cast<uint16_t(*)[2][KT][VLD]>(smem);
+  auto& Ks = *reinterpret_cast<uint16_t(*)[2][D][KLD]>(smem + 2 * KT * VLD);
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform, so are h and the blocks
   const int l16 = lane & 15, c = lane >> 4;
@@ -632,7 +639,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_bf16_kernel(
   // with eight head groups each XCD works on one KV group (its K and V stay
   // in that XCD's L2)
   const int nhg = Hq / HW;
-  const int by = (int)(blockIdx.x % nhg), bx = (int)(blockIdx.x / nhg);
+  const int by = (int)(blk % nhg), bx = (int)(blk / nhg);
   const int h = by * HW + (w % HW), g = h / grp;
   const int64_t ldq = (int64_t)Hq * D, ldk = (int64_t)(Hq / grp) * D;
   const int nsub = (int)cdiv64(s_q, 16);
@@ -838,30 +845,48 @@ __global__ __launch_bounds__(256, 2) void attn_dq_bf16_kernel(
   }
 }
 
+template <int D, int HW, bool PVEC>
+__global__ __launch_bounds__(256, 2) void attn_dq_bf16_kernel(
+    int64_t s_q, int64_t s_kv, int Hq, int grp, int64_t LK, int npairs,
+    const float* __restrict__ dctx, const uint16_t* __restrict__ P,
+    const uint16_t* __restrict__ Kt, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ ctx, const float* __restrict__ delta_ws, float* __restrict__ dq,
+    float scale, int causal) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[dq_bf16_lds<D>()];
+  attn_dq_bf16_body<D, HW, PVEC>(blockIdx.x, s_q, s_kv, Hq, grp, LK, npairs, dctx, P, Kt, V, ctx,
+                                 delta_ws, dq, scale, causal, smem);
+}
+
 constexpr int HV_QT = 64;   // queries per step, bf16 dv kernel
 constexpr int HV_KT = 128;  // keys per workgroup, bf16 dv kernel
 constexpr DvGeo HV_GEO{HV_KT, HV_QT, HV_QT};
 
+template <int D>
+constexpr int dv_bf16_lds() {
+  return 2 * HV_QT * (HV_KT + 16) + 2 * D * (HV_QT + 8);
+}
+
+// Work item blk of the bf16 dV launch, on the LDS at smem (dv_bf16_lds).
 template <int D, bool PVEC>
-__global__ __launch_bounds__(256, 2) void attn_dv_bf16_kernel(int64_t s_q, int64_t s_kv, int Hq,
-                                                           int grp, int cmax, int64_t cs,
-                                                           int64_t nfull, int64_t LQ,
-                                                           const uint16_t* __restrict__ P,
-                                                           const uint16_t* __restrict__ dCt,
-                                                           float* __restrict__ out, int causal) {
+__device__ __forceinline__ void attn_dv_bf16_body(int64_t blk, int64_t s_q, int64_t s_kv, int Hq,
+                                                  int grp, int cmax, int64_t cs, int64_t nfull,
+                                                  int64_t LQ, const uint16_t* __restrict__ P,
+                                                  const uint16_t* __restrict__ dCt,
+                                                  float* __restrict__ out, int causal,
+                                                  uint16_t* smem) {
   constexpr int QT = HV_QT, KT = HV_KT, LDP = KT + 16, LDT = QT + 8, NJ = D / 32;
   constexpr int NP = KT * QT / 8 / 256;  // P chunks of 8 keys per thread (4)
   constexpr int NC = D * QT / 8;         // dCt chunks of 8 queries
   constexpr int SC = (NC + 255) / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t Pn[2][QT][LDP];  // [query][key], swizzled
-  __shared__ __attribute__((aligned(16))) uint16_t Ct[2][D][LDT];
+  auto& Pn = *reinterpret_cast<uint16_t(*)[2][QT][LDP]>(smem);  // [query][key], swizzled
+  auto& Ct = *reinterpret_cast<uint16_t(*)[2][D][LDT]>(smem + 2 * QT * LDP);
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l16 = lane & 15, c = lane >> 4;
   const int Hkv = Hq / grp;
   int g;
   int64_t jt, ch;
-  if (!dv_item(blockIdx.x, Hkv, s_q, s_kv, grp, causal, HV_GEO, cs, nfull, g, jt, ch)) return;
+  if (!dv_item(blk, Hkv, s_q, s_kv, grp, causal, HV_GEO, cs, nfull, g, jt, ch)) return;
   const int64_t ldk = (int64_t)Hkv * D;
   const int64_t k0 = jt * KT;
   const int64_t qbeg = dv_tile_qbeg(jt, s_q, s_kv, causal, HV_GEO);
@@ -981,6 +1006,39 @@ __global__ __launch_bounds__(256, 2) void attn_dv_bf16_kernel(int64_t s_q, int64
         const int64_t k = k0 + 64 * kh + 16 * mi + 4 * c + v;
         if (k < s_kv) dst[k * ldk + g * D + (D / 2) * dh + 16 * nj + l16] = acc[mi][nj][v];
       }
+}
+
+template <int D, bool PVEC>
+__global__ __launch_bounds__(256, 2) void attn_dv_bf16_kernel(int64_t s_q, int64_t s_kv, int Hq,
+                                                           int grp, int cmax, int64_t cs,
+                                                           int64_t nfull, int64_t LQ,
+                                                           const uint16_t* __restrict__ P,
+                                                           const uint16_t* __restrict__ dCt,
+                                                           float* __restrict__ out, int causal) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[dv_bf16_lds<D>()];
+  attn_dv_bf16_body<D, PVEC>(blockIdx.x, s_q, s_kv, Hq, grp, cmax, cs, nfull, LQ, P, dCt, out,
+                             causal, smem);
+}
+
+// dQ and dV in one launch: workgroups [0, ndq) are dQ's, the rest dV's work
+// items, so dV work fills the CUs as the dQ workgroups of unequal causal
+// length finish.
+template <int D, int HW, bool PVEC>
+__global__ __launch_bounds__(256, 2) void attn_dqdv_bf16_kernel(
+    int64_t s_q, int64_t s_kv, int Hq, int grp, int64_t LK, int npairs,
+    const float* __restrict__ dctx, const uint16_t* __restrict__ P,
+    const uint16_t* __restrict__ Kt, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ ctx, const float* __restrict__ delta_ws, float* __restrict__ dq,
+    float scale, int causal, int64_t ndq, int cmax, int64_t cs, int64_t nfull, int64_t LQ,
+    const uint16_t* __restrict__ dCt, float* __restrict__ dvout) {
+  constexpr int LDS = dq_bf16_lds<D>() > dv_bf16_lds<D>() ? dq_bf16_lds<D>() : dv_bf16_lds<D>();
+  __shared__ __attribute__((aligned(16))) uint16_t smem[LDS];
+  if ((int64_t)blockIdx.x < ndq)
+    attn_dq_bf16_body<D, HW, PVEC>(blockIdx.x, s_q, s_kv, Hq, grp, LK, npairs, dctx, P, Kt, V,
+                                   ctx, delta_ws, dq, scale, causal, smem);
+  else
+    attn_dv_bf16_body<D, PVEC>((int64_t)blockIdx.x - ndq, s_q, s_kv, Hq, grp, cmax, cs, nfull,
+                               LQ, P, dCt, dvout, causal, smem);
 }
 
 // ---------------------------------------------------------------- bfloat16, D = 16
@@ -1364,11 +1422,26 @@ template <int D, int HW>
 static void launch_dq_bf16(int64_t s_q, int64_t s_kv, int Hq, int grp, int64_t LK,
                            const float* dctx, const uint16_t* P, const uint16_t* Kt,
                            const uint16_t* V, const uint16_t* ctx, const float* delta, float* dq,
-                           float scale, int causal, hipStream_t s) {
+                           float scale, int causal, hipStream_t s, const DvPlan* dp = nullptr,
+                           int64_t LQ = 0, const uint16_t* dCt = nullptr, float* dvout = nullptr) {
   constexpr int QW = 4 / HW;
   const int nsub = (int)cdiv64(s_q, 16);
   const int npairs = (nsub + 1) / 2;
-  const dim3 grid((unsigned)(cdiv64(npairs, QW) * (Hq / HW)));
+  const int64_t ndq = cdiv64(npairs, QW) * (Hq / HW);
+  if (dp != nullptr) {
+    // dV's work items in the same launch, after dQ's workgroups
+    const dim3 g2((unsigned)(ndq + dp->items));
+    if (s_kv % 8 == 0)
+      attn_dqdv_bf16_kernel<D, HW, true><<<g2, 256, 0, s>>>(
+          s_q, s_kv, Hq, grp, LK, npairs, dctx, P, Kt, V, ctx, delta, dq, scale, causal, ndq,
+          dp->cmax, dp->cs, dp->nfull, LQ, dCt, dvout);
+    else
+      attn_dqdv_bf16_kernel<D, HW, false><<<g2, 256, 0, s>>>(
+          s_q, s_kv, Hq, grp, LK, npairs, dctx, P, Kt, V, ctx, delta, dq, scale, causal, ndq,
+          dp->cmax, dp->cs, dp->nfull, LQ, dCt, dvout);
+    return;
+  }
+  const dim3 grid((unsigned)ndq);
   if (s_kv % 8 == 0)
     attn_dq_bf16_kernel<D, HW, true><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, LK, npairs, dctx, P,
                                                           Kt, V, ctx, delta, dq, scale, causal);
@@ -1411,28 +1484,27 @@ static hipError_t attn_launch_bf16(int64_t s_q, int64_t s_kv, int Hq, int Hkv, c
          2.0 * D * pairs * Hq, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const int hw = grp % 4 == 0 ? 4 : (grp % 2 == 0 ? 2 : 1);
-  if (hw == 4)
-    launch_dq_bf16<D, 4>(s_q, s_kv, Hq, grp, wl.LK, dctx, P, Kt, V, ctx, delta, dq, scale, causal, s);
-  else if (hw == 2)
-    launch_dq_bf16<D, 2>(s_q, s_kv, Hq, grp, wl.LK, dctx, P, Kt, V, ctx, delta, dq, scale, causal, s);
-  else
-    launch_dq_bf16<D, 1>(s_q, s_kv, Hq, grp, wl.LK, dctx, P, Kt, V, ctx, delta, dq, scale, causal, s);
-  mark("attn_dq_bf16", pbytes + qbytes * (4 + 4 + (ctx ? 2 : 0)) + 2 * kvbytes * 2,
-       4.0 * D * pairs * Hq, s);
-  if ((e = hipGetLastError()) != hipSuccess || dv == nullptr) return e;
+  // dQ, and with dv wanted dV in the same launch
   const DvPlan dp = dv_plan(s_q, s_kv, Hkv, grp, causal, HV_GEO, HV_WG_TARGET);
   float* part = dp.cmax > 1 ? (float*)(wb + wl.part) : dv;
-  const dim3 grid((unsigned)dp.items);
-  if (s_kv % 8 == 0)
-    attn_dv_bf16_kernel<D, true><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dp.cmax, dp.cs, dp.nfull,
-                                                      wl.LQ, P, dCt, part, causal);
+  const DvPlan* dpp = dv != nullptr ? &dp : nullptr;
+  const int hw = grp % 4 == 0 ? 4 : (grp % 2 == 0 ? 2 : 1);
+  if (hw == 4)
+    launch_dq_bf16<D, 4>(s_q, s_kv, Hq, grp, wl.LK, dctx, P, Kt, V, ctx, delta, dq, scale, causal, s,
+                         dpp, wl.LQ, dCt, part);
+  else if (hw == 2)
+    launch_dq_bf16<D, 2>(s_q, s_kv, Hq, grp, wl.LK, dctx, P, Kt, V, ctx, delta, dq, scale, causal, s,
+                         dpp, wl.LQ, dCt, part);
   else
-    attn_dv_bf16_kernel<D, false><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dp.cmax, dp.cs,
-                                                       dp.nfull, wl.LQ, P, dCt, part, causal);
-  mark("attn_dv_bf16", pbytes + qbytes * 2 + kvbytes * 4 * (dp.cmax > 1 ? dp.cmax : 1),
-       2.0 * D * pairs * Hq, s);
-  if ((e = hipGetLastError()) != hipSuccess || dp.cmax == 1) return e;
+    launch_dq_bf16<D, 1>(s_q, s_kv, Hq, grp, wl.LK, dctx, P, Kt, V, ctx, delta, dq, scale, causal, s,
+                         dpp, wl.LQ, dCt, part);
+  const double dqb = pbytes + qbytes * (4 + 4 + (ctx ? 2 : 0)) + 2 * kvbytes * 2;
+  const double dvb = pbytes + qbytes * 2 + kvbytes * 4 * (dp.cmax > 1 ? dp.cmax : 1);
+  if (dv == nullptr)
+    mark("attn_dq_bf16", dqb, 4.0 * D * pairs * Hq, s);
+  else
+    mark("attn_dqdv_bf16", dqb + dvb, 6.0 * D * pairs * Hq, s);
+  if ((e = hipGetLastError()) != hipSuccess || dv == nullptr || dp.cmax == 1) return e;
   return launch_dv_reduce(s_q, s_kv, Hq, Hkv, D, dp.cmax, dp.cs, part, dv, causal, HV_GEO, dq,
                           nullptr, rope, rope_done, s);
 }

@@ -229,7 +229,7 @@ def layer_bwd(cfg, w, saved, d_out, lora=None):
       dCtx  = rmsnorm_bwd(ctx, gamma_asub, dCtx)   (only with sub-norms)
       dQ,dV = attention_bwd(dCtx, P, K, V)
       dQpre = rope_bwd(dQ), row i at position pos0 + i
-      for (Q: dQpre, lora_q_h), (V: dV, lora_v_h):
+      for (Q: dQpre, lora_q_h), (V: dV[-S:], lora_v_h):
           dA, dB = lora_grads(...); gnorm_sq += ||dA||^2 (A only)
           A <- adamw(A, dA, lr), B <- adamw(B, dB, lr_b)
 
@@ -237,7 +237,10 @@ def layer_bwd(cfg, w, saved, d_out, lora=None):
     pos0, scale, and for LoRA alpha, lr, lr_b, beta1, beta2, adam_eps,
     weight_decay, step.  w: weights and gammas; saved: attn_input, resid1,
     gate, up, hidden_pre (sub-norms), ctx, P, K, V, lora_q_h, lora_v_h.
-    lora: dict with A_q, B_q, A_v, B_v and their m_/v_ moments, or None."""
+    lora: dict with A_q, B_q, A_v, B_v and their m_/v_ moments, or None.
+    The value adapter acts on the values of the S current tokens, which are
+    the last S of the kv_len rows (all of them when kv_len == S); a cached
+    prefix's rows receive dV but no adapter gradient."""
     sub = bool(cfg.sub_norms)
     dh1 = ffn_bwd(d_out, w["W_down"], w["W_gate"], w["W_up"], saved["gate"],
                   saved["up"], saved["resid1"], w["gamma_ffn"], cfg.eps, cfg.act,
@@ -254,7 +257,8 @@ def layer_bwd(cfg, w, saved, d_out, lora=None):
     res = dict(d_hidden=dh1, dctx=dctx, dq=dq, dq_pre=dq_pre, dv=dv, gnorm_sq=0.0)
     if lora is not None:
         x_a = saved["attn_input"]
-        for tag, dy, h in (("q", dq_pre, saved["lora_q_h"]), ("v", dv, saved["lora_v_h"])):
+        for tag, dy, h in (("q", dq_pre, saved["lora_q_h"]),
+                           ("v", dv[dv.shape[0] - rows:], saved["lora_v_h"])):
             A, B = lora["A_" + tag], lora["B_" + tag]
             rank = A.shape[0]
             dA, dB = lora_grads(dy, h, x_a, B, cfg.alpha, rank)

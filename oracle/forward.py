@@ -27,7 +27,10 @@ saved):
 x_attn is x_res held fixed (the stop-gradient reading: the gradient passed to
 the layer below flows through the residual stream only).  In the decode layer
 the keys and values come from a cache whose last slot is the current token,
-and there are no adapters.
+and there are no adapters.  A chunk of S tokens after a cached prefix
+(K_prefix, V_prefix: the prefix's post-RoPE keys and its values, held fixed)
+attends to the prefix rows followed by its own; the adapters act on the
+chunk's own projections only.
 """
 import numpy as np
 
@@ -128,12 +131,16 @@ def layer_forward(cfg, w, x_res, x_attn=None, lora=None, q_pre=None, v_in=None):
         v = np.asarray(w["V_cache"], np.float64) if v_in is None else v_in
     else:
         k = rope(x_a @ w["W_k"].T, Hkv, D, pos, cfg.rope_base)
+        if "K_prefix" in w:
+            k = np.concatenate([np.asarray(w["K_prefix"], np.float64), k])
         if v_in is None:
             v = x_a @ w["W_v"].T
             if lora is not None:
                 h_v = x_a @ lora["A_v"].T
                 saved["lora_v_h"] = h_v
                 v = v + (cfg.alpha / lora["A_v"].shape[0]) * (h_v @ lora["B_v"].T)
+            if "V_prefix" in w:
+                v = np.concatenate([np.asarray(w["V_prefix"], np.float64), v])
         else:
             v = v_in
             if lora is not None:
@@ -158,7 +165,8 @@ def make_layer(cfg, draws):
     """Split seeded draws into (weights, saved activations, LoRA state) by
     running the forward once on the drawn layer input."""
     w = {k: v for k, v in draws.items()
-         if k.startswith("W_") or k.startswith("gamma_") or k in ("K_cache", "V_cache")}
+         if k.startswith("W_") or k.startswith("gamma_")
+         or k in ("K_cache", "V_cache", "K_prefix", "V_prefix")}
     lora = None
     if cfg.rank > 0:
         lora = {k: draws[k] for k in draws

@@ -19,7 +19,7 @@ TENSOR_IDS = {
     "x": 0, "d_out": 1, "W_q": 2, "W_k": 3, "W_v": 4, "W_o": 5, "W_gate": 6,
     "W_up": 7, "W_down": 8, "gamma_attn": 9, "gamma_ffn": 10, "gamma_fsub": 11,
     "gamma_asub": 12, "A_q": 13, "B_q": 14, "A_v": 15, "B_v": 16, "K_cache": 17,
-    "V_cache": 18, "m_state": 19, "v_state": 20,
+    "V_cache": 18, "m_state": 19, "v_state": 20, "K_prefix": 21, "V_prefix": 22,
     # timing-only draws (stand-ins for saved activations)
     "t_attn_input": 40, "t_resid1": 41, "t_gate": 42, "t_up": 43,
     "t_hidden_pre": 44, "t_ctx": 45, "t_P": 46, "t_K": 47, "t_V": 48,
@@ -78,11 +78,18 @@ def draw_layer(cfg, layer=0):
     if cfg.seq == cfg.kv_len:
         d["W_k"] = _weight(cfg, layer, "W_k", (kvd, H))
         d["W_v"] = _weight(cfg, layer, "W_v", (kvd, H))
-    else:
+    elif cfg.seq == 1 and r == 0:
         # decode: the cache (post-RoPE keys, values) is drawn directly; the
         # last slot is the current token
         d["K_cache"] = normal(cfg, layer, "K_cache", (cfg.kv_len, kvd))
         d["V_cache"] = normal(cfg, layer, "V_cache", (cfg.kv_len, kvd))
+    else:
+        # a chunk of tokens after a cached prefix: the prefix's post-RoPE keys
+        # and values are drawn directly, the chunk's come from its projections
+        d["W_k"] = _weight(cfg, layer, "W_k", (kvd, H))
+        d["W_v"] = _weight(cfg, layer, "W_v", (kvd, H))
+        d["K_prefix"] = normal(cfg, layer, "K_prefix", (cfg.kv_len - S, kvd))
+        d["V_prefix"] = normal(cfg, layer, "V_prefix", (cfg.kv_len - S, kvd))
     if r > 0:
         d["A_q"] = normal(cfg, layer, "A_q", (r, H), 0.02)
         d["B_q"] = normal(cfg, layer, "B_q", (qd, r), 0.02)

@@ -16,8 +16,9 @@ import synth
 from oracle import forward as F
 from oracle import fd
 
-SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                   "oracle", "backward.py")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "backward.py")
+FWD_SRC = os.path.join(ROOT, "oracle", "forward.py")
 
 MUTATIONS = [
     # (old, new) - each old string must occur in oracle/backward.py
@@ -46,12 +47,13 @@ MUTATIONS = [
      "dq_pre = rope_bwd(dq, cfg.n_heads, cfg.head_dim, np.arange(rows),"),           # positions
     ('res["gnorm_sq"] += float(np.sum(dA * dA))',
      'res["gnorm_sq"] += float(np.sum(dA * dA) + np.sum(dB * dB))'),                 # gnorm of B too
+    ("dv[dv.shape[0] - rows:]", "dv[:rows]"),                                        # prefix rows
 ]
 
 
-def _load_mutant(old, new):
-    src = open(SRC).read()
-    assert src.count(old) >= 1, old
+def _load_mutant(old, new, path=SRC):
+    src = open(path).read()
+    assert src.count(old) == 1, old
     mod = types.ModuleType("oracle_mutant")
     exec(compile(src.replace(old, new, 1), "oracle_mutant", "exec"), mod.__dict__)
     return mod
@@ -126,6 +128,18 @@ def _checks(B):
         return float(np.sum(dd["d_out"] * o))
     out.append(fd.rel_err(rd["dq_pre"], fd.grad(lambda z: Ld(q_pre=z), sd_["q_pre"])) < 1e-5)
     out.append(fd.rel_err(rd["d_hidden"], fd.grad(lambda z: Ld(x=z), dd["x"])) < 1e-5)
+    # a chunk after a cached prefix: the V adapter sees the chunk's dV rows
+    cp = cfg.with_(seq=5, kv_len=11, pos0=6)
+    dp = synth.draw_layer(cp)
+    wp, sp, lp = F.make_layer(cp, dp)
+    rp = B.layer_bwd(cp, wp, sp, dp["d_out"], lp)
+
+    def Lp(z):
+        l2 = dict(lp)
+        l2["B_v"] = z
+        o, _ = F.layer_forward(cp, wp, dp["x"], lora=l2)
+        return float(np.sum(dp["d_out"] * o))
+    out.append(fd.rel_err(rp["dB_v"], fd.grad(Lp, lp["B_v"], rel_step=1e-5)) < 1e-5)
     # multi-step AdamW v update against its definition through a second step
     p2, m2, v2 = B.adamw(np.array([1.0]), np.array([0.5]), np.array([0.1]), np.array([0.04]),
                          1e-3, 0.9, 0.999, 1e-8, 0.0, 2)
@@ -145,5 +159,52 @@ def test_mutation_is_caught(i):
     try:
         ok = all(_checks(B))
     except (ValueError, IndexError):  # a shape error also exposes the mistake
+        ok = False
+    assert not ok, "mutation not caught: %r -> %r" % (old, new)
+
+
+# Mutations of oracle/forward.py context() (the apply step that builds ctx for
+# the whole-stack parity inputs); each old string occurs once in that file.
+CONTEXT_MUTATIONS = [
+    ("        g = h // grp\n        ctx[:, h * D:(h + 1) * D] = P[h] @ V[:, g * D:(g + 1) * D]\n    return ctx",
+     "        g = h % n_kv_heads\n        ctx[:, h * D:(h + 1) * D] = P[h] @ V[:, g * D:(g + 1) * D]\n    return ctx"),
+    ("        ctx[:, h * D:(h + 1) * D] = P[h] @ V[:, g * D:(g + 1) * D]\n    return ctx",
+     "        ctx[:, h * D:(h + 1) * D] = P[h].T @ V[:, g * D:(g + 1) * D]\n    return ctx"),
+    ("    grp = n_heads // n_kv_heads\n    ctx = np.zeros((P.shape[1], n_heads * D))",
+     "    grp = n_kv_heads\n    ctx = np.zeros((P.shape[1], n_heads * D))"),
+]
+
+
+def _context_checks(Fm):
+    """The pins of test_oracle_pins.test_context_is_the_apply_step, run on
+    the module under test (square and GQA 6:2 cases)."""
+    ok = []
+    for s_q, s_kv, Hq, Hkv in ((5, 5, 4, 2), (4, 4, 6, 2)):
+        r = np.random.default_rng(5 + Hq)
+        D = 3
+        P = r.random((Hq, s_q, s_kv))
+        V = r.standard_normal((s_kv, Hkv * D))
+        ctx = Fm.context(P, V, Hq, Hkv)
+        loops = np.zeros((s_q, Hq * D))
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            for i in range(s_q):
+                for d in range(D):
+                    loops[i, h * D + d] = sum(P[h, i, j] * V[j, g * D + d] for j in range(s_kv))
+        ok.append(np.allclose(ctx, loops, rtol=1e-13, atol=1e-15))
+    return ok
+
+
+def test_unmutated_context_passes():
+    assert all(_context_checks(F))
+
+
+@pytest.mark.parametrize("i", range(len(CONTEXT_MUTATIONS)))
+def test_context_mutation_is_caught(i):
+    old, new = CONTEXT_MUTATIONS[i]
+    Fm = _load_mutant(old, new, FWD_SRC)
+    try:
+        ok = all(_context_checks(Fm))
+    except (ValueError, IndexError):
         ok = False
     assert not ok, "mutation not caught: %r -> %r" % (old, new)

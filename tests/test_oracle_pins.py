@@ -235,6 +235,43 @@ def test_attention_bwd_brute_force_loops():
     np.testing.assert_allclose(dv, dv2, rtol=1e-12, atol=1e-14)
 
 
+@pytest.mark.parametrize("s_q,s_kv,Hq,Hkv,causal", [
+    (5, 5, 4, 2, True), (5, 5, 4, 2, False), (4, 7, 6, 2, True), (3, 6, 6, 2, False)])
+def test_context_is_the_apply_step(s_q, s_kv, Hq, Hkv, causal):
+    # ctx_h = P_h V_g with g = h // (Hq/Hkv) ([ENT] backward_through_layers,
+    # kv_head = head / heads_per_kv), pinned three ways: scalar loops; the
+    # forward's own attention output on the same P; and the delta identity
+    # rowsum(P o (dCtx V^T)) = <dCtx, ctx> (the page form of delta against
+    # the ctx form) on a P that is NOT a softmax of anything (random rows)
+    D = 3
+    r = rng(31 + Hq + s_kv)
+    P = r.random((Hq, s_q, s_kv))
+    if causal:
+        P = np.where(F.causal_mask(s_q, s_kv)[None], P, 0.0)
+    V = r.standard_normal((s_kv, Hkv * D))
+    ctx = F.context(P, V, Hq, Hkv)
+    assert ctx.shape == (s_q, Hq * D)
+    loops = np.zeros_like(ctx)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        for i in range(s_q):
+            for d in range(D):
+                loops[i, h * D + d] = sum(P[h, i, j] * V[j, g * D + d] for j in range(s_kv))
+    np.testing.assert_allclose(ctx, loops, rtol=1e-13, atol=1e-15)
+    dctx = r.standard_normal(ctx.shape)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        dA = dctx[:, h * D:(h + 1) * D] @ V[:, g * D:(g + 1) * D].T
+        page = np.sum(P[h] * dA, axis=-1)
+        form = np.sum(dctx[:, h * D:(h + 1) * D] * ctx[:, h * D:(h + 1) * D], axis=-1)
+        assert np.max(np.abs(page - form)) < 1e-12
+    # the forward's attention (softmax of real scores) gives the same ctx
+    q = r.standard_normal((s_q, Hq * D))
+    k = r.standard_normal((s_kv, Hkv * D))
+    P2, ctx2 = F.attention(q, k, V, Hq, Hkv, D, 0.5, causal)
+    np.testing.assert_allclose(F.context(P2, V, Hq, Hkv), ctx2, rtol=1e-13, atol=1e-15)
+
+
 # ---------------------------------------------------------------- LoRA / AdamW
 def test_lora_grads_fd_and_loops():
     r = rng(14)
@@ -333,6 +370,22 @@ def test_layer_fd_tiny_swiglu_lora(tiny):
     assert fd.rel_err(res["dq_pre"], nq) < 1e-5
     nv = fd.grad(lambda z: L(lora=lora, v_in=z), saved["V"])
     assert fd.rel_err(res["dv"], nv) < 1e-5
+
+
+def test_layer_fd_chunk_after_cached_prefix(tiny):
+    # 5 tokens after a 6-row cached prefix (kv_len 11, positions 6..10): the
+    # value adapter acts on the chunk's own values only, so its gradients come
+    # from the last 5 rows of dV; finite differences of the forward decide
+    cfg = tiny.with_(seq=5, kv_len=11, pos0=6)
+    d, w, saved, lora, res, L = _layer_fd(cfg)
+    assert saved["K"].shape[0] == 11 and res["dv"].shape[0] == 11
+    assert fd.rel_err(res["d_hidden"], fd.grad(lambda z: L(x=z, lora=lora), d["x"])) < 1e-5
+    for k in ("A_q", "B_q", "A_v", "B_v"):
+        def Lk(z, k=k):
+            l2 = dict(lora)
+            l2[k] = z
+            return L(lora=l2)
+        assert fd.rel_err(res["d" + k], fd.grad(Lk, lora[k], rel_step=1e-5)) < 1e-5, k
 
 
 def test_layer_fd_decode_like_relu2_subnorms():

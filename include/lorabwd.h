@@ -23,9 +23,18 @@
  *  - Feature sizes (hidden, ffn, n_heads*head_dim, n_kv_heads*head_dim) must
  *    be multiples of 8; head_dim must be 16, 32, 64 or 128; row counts may be
  *    any value >= 0 (0 is a no-op that returns LORABWD_OK).
+ *  - Size limits: row counts (rows, seq, kv_len, s_q, s_kv) and feature sizes
+ *    at most 2^20, at most 4096 query heads.  Within these, a shape that one
+ *    of the kernels cannot take (a buffer range of 1 GiB or more, such as one
+ *    chunk of weight rows of a one-token product or a one-token K/V cache,
+ *    or the one-token attention's LDS) is refused with LORABWD_ERR_SHAPE by a
+ *    checking pass of the whole call that runs before anything is enqueued.
  *  - GQA: query head h reads KV head h / (n_heads / n_kv_heads).
- *  - Every call validates all arguments before touching the GPU: a negative
- *    status means nothing was enqueued and no output was written.  A zero
+ *  - Every call validates all arguments before touching the GPU: a status
+ *    other than LORABWD_OK and LORABWD_ERR_HIP means nothing was enqueued
+ *    and no output was written.  LORABWD_ERR_HIP (a launch the runtime
+ *    refused, e.g. no usable device) can leave the kernels before it
+ *    enqueued.  A zero
  *    status means the work is enqueued on `stream`; results are valid once
  *    the stream is synchronised.  No call allocates or frees device memory,
  *    synchronises the device, or keeps state between calls: scratch memory

@@ -18,6 +18,9 @@ struct Recorder {
   int count;
 };
 static thread_local Recorder* tl_recorder = nullptr;
+static thread_local bool tl_dry = false;
+
+bool dry_run() { return tl_dry; }
 
 void mark(const char* name, double alg_bytes, double alg_flops, hipStream_t s) {
   Recorder* r = tl_recorder;
@@ -41,8 +44,20 @@ inline size_t up(size_t b) { return (b + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline bool dtype_ok(int dt) { return dt == LORABWD_F32 || dt == LORABWD_BF16; }
 inline size_t esize(int dt) { return dt == LORABWD_BF16 ? 2 : 4; }
-inline bool feat_ok(int64_t n) { return n > 0 && n % 8 == 0; }
+// Size limits of every entry point (lorabwd.h): row counts and feature
+// sizes up to 2^20, at most 4096 heads.  Within them all grid dimensions fit;
+// the kernels' own limits (1 GiB buffer ranges, LDS) are checked by the
+// checking pass below.
+constexpr int64_t kMaxRows = int64_t(1) << 20;
+constexpr int64_t kMaxFeat = int64_t(1) << 20;
+constexpr int64_t kMaxHeads = 4096;
+inline bool rows_ok(int64_t r) { return r >= 0 && r <= kMaxRows; }
+inline bool feat_ok(int64_t n) { return n > 0 && n % 8 == 0 && n <= kMaxFeat; }
 inline bool head_dim_ok(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+inline bool heads_ok(int64_t hq, int64_t hkv, int64_t d) {
+  return hq >= 1 && hkv >= 1 && hq <= kMaxHeads && hq % hkv == 0 && head_dim_ok(d) &&
+         hq * d <= kMaxFeat;
+}
 inline bool finite(float x) { return isfinite(x); }
 
 // Byte ranges [a, a+na) and [b, b+nb) intersect.
@@ -73,6 +88,30 @@ struct Carver {
 #define LBP_HIP(expr)                                   \
   do {                                                  \
     if ((expr) != hipSuccess) return LORABWD_ERR_HIP;   \
+  } while (0)
+
+// Runs a composition of launchers as a checking pass (no HIP call is made,
+// see dry_run in kernels.h): LORABWD_OK, or LORABWD_ERR_SHAPE where some
+// kernel cannot take the shape.  Every entry point passes this before its
+// real pass, so a refused shape leaves nothing enqueued.
+template <typename Fn>
+int check_pass(Fn&& fn) {
+  tl_dry = true;
+  const hipError_t e = fn();
+  tl_dry = false;
+  return e == hipSuccess ? LORABWD_OK : LORABWD_ERR_SHAPE;
+}
+
+#define LBP_E(expr)                                \
+  do {                                             \
+    if ((e = (expr)) != hipSuccess) return e;      \
+  } while (0)
+
+#define LBP_RUN(expr)                                   \
+  do {                                                  \
+    const int st_ = check_pass([&] { return (expr); }); \
+    if (st_ != LORABWD_OK) return st_;                  \
+    LBP_HIP(expr);                                      \
   } while (0)
 
 // ---------------------------------------------------------------- FFN
@@ -111,7 +150,7 @@ int ffn_validate(int64_t rows, int64_t dim, int64_t ffn, int act, const float* d
                  const void* resid1, const float* gamma_ffn, float* d_resid, float eps, int dt) {
   LBP_CHECK(dtype_ok(dt), LORABWD_ERR_DTYPE);
   LBP_CHECK(act == LORABWD_ACT_SWIGLU || act == LORABWD_ACT_RELU2, LORABWD_ERR_DTYPE);
-  LBP_CHECK(rows >= 0 && feat_ok(dim) && feat_ok(ffn), LORABWD_ERR_SHAPE);
+  LBP_CHECK(rows_ok(rows) && feat_ok(dim) && feat_ok(ffn), LORABWD_ERR_SHAPE);
   LBP_CHECK(finite(eps) && eps >= 0.f, LORABWD_ERR_ARG);
   if (rows == 0) return LORABWD_OK;
   LBP_CHECK(d_out && w_down && w_gate && w_up && gate && up_ && resid1 && gamma_ffn && d_resid,
@@ -238,7 +277,8 @@ int lora_validate(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank, c
                   float alpha, float lr_a, float lr_b, float beta1, float beta2, float eps,
                   float wd, int step, int dt) {
   LBP_CHECK(dtype_ok(dt), LORABWD_ERR_DTYPE);
-  LBP_CHECK(rows >= 0 && feat_ok(in_dim) && out_dim > 0 && rank >= 1 && rank <= 64,
+  LBP_CHECK(rows_ok(rows) && feat_ok(in_dim) && out_dim > 0 && out_dim <= kMaxFeat && rank >= 1 &&
+                rank <= 64,
             LORABWD_ERR_SHAPE);
   LBP_CHECK(step >= 1, LORABWD_ERR_STEP);
   LBP_CHECK(finite(alpha) && finite(lr_a) && finite(lr_b) && finite(wd) && finite(eps) &&
@@ -283,8 +323,7 @@ int attn_validate(int64_t s_q, int64_t s_kv, int64_t Hq, int64_t Hkv, int64_t D,
                   const float* dctx, const void* P, const void* K, const void* V,
                   const void* ctx, float* dq, float* dv, float scale, int causal, int dt) {
   LBP_CHECK(dtype_ok(dt), LORABWD_ERR_DTYPE);
-  LBP_CHECK(s_q >= 0 && s_kv >= 0 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0 && head_dim_ok(D),
-            LORABWD_ERR_SHAPE);
+  LBP_CHECK(rows_ok(s_q) && rows_ok(s_kv) && heads_ok(Hq, Hkv, D), LORABWD_ERR_SHAPE);
   LBP_CHECK(causal == 0 || causal == 1, LORABWD_ERR_ARG);
   LBP_CHECK(!causal || s_q <= s_kv, LORABWD_ERR_SHAPE);
   LBP_CHECK(s_q == 0 || s_kv >= 1, LORABWD_ERR_SHAPE);
@@ -332,7 +371,7 @@ int lorabwd_rmsnorm_backward(int64_t rows, int64_t n, const void* x, const float
                              const float* dy, float* dx, float eps, int accumulate, int dtype,
                              hipStream_t stream) {
   LBP_CHECK(dtype_ok(dtype), LORABWD_ERR_DTYPE);
-  LBP_CHECK(rows >= 0 && feat_ok(n), LORABWD_ERR_SHAPE);
+  LBP_CHECK(rows_ok(rows) && feat_ok(n), LORABWD_ERR_SHAPE);
   LBP_CHECK(finite(eps) && eps >= 0.f && (accumulate == 0 || accumulate == 1), LORABWD_ERR_ARG);
   if (rows == 0) return LORABWD_OK;
   LBP_CHECK(x && gamma && dy && dx, LORABWD_ERR_NULL);
@@ -341,20 +380,21 @@ int lorabwd_rmsnorm_backward(int64_t rows, int64_t n, const void* x, const float
   LBP_CHECK(dx == dy || !overlap(dx, nb, dy, nb), LORABWD_ERR_ALIAS);
   LBP_CHECK(!overlap(dx, nb, x, (size_t)rows * n * esize(dtype)), LORABWD_ERR_ALIAS);
   LBP_CHECK(!overlap(dx, nb, gamma, (size_t)n * 4), LORABWD_ERR_ALIAS);
-  LBP_HIP(launch_rmsnorm_bwd(rows, n, x, dtype, gamma, dy, dx, eps, accumulate, stream));
+  LBP_RUN(launch_rmsnorm_bwd(rows, n, x, dtype, gamma, dy, dx, eps, accumulate, stream));
   return LORABWD_OK;
 }
 
 int lorabwd_rope_backward(int64_t rows, int64_t n_heads, int64_t head_dim, const float* dy,
                           float* dx, int64_t pos0, float base, hipStream_t stream) {
-  LBP_CHECK(rows >= 0 && n_heads >= 1 && head_dim_ok(head_dim) && pos0 >= 0, LORABWD_ERR_SHAPE);
+  LBP_CHECK(rows_ok(rows) && heads_ok(n_heads, 1, head_dim) && pos0 >= 0 && pos0 <= (int64_t(1) << 40),
+            LORABWD_ERR_SHAPE);
   LBP_CHECK(finite(base) && base > 0.f, LORABWD_ERR_ARG);
   if (rows == 0) return LORABWD_OK;
   LBP_CHECK(dy && dx, LORABWD_ERR_NULL);
   LBP_CHECK(aligned16(dy) && aligned16(dx), LORABWD_ERR_ALIGN);
   const size_t nb = (size_t)rows * n_heads * head_dim * 4;
   LBP_CHECK(dx == dy || !overlap(dx, nb, dy, nb), LORABWD_ERR_ALIAS);
-  LBP_HIP(launch_rope_bwd(rows, n_heads, head_dim, dy, dx, pos0, base, stream));
+  LBP_RUN(launch_rope_bwd(rows, n_heads, head_dim, dy, dx, pos0, base, stream));
   return LORABWD_OK;
 }
 
@@ -376,7 +416,7 @@ int lorabwd_attn_backward(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_
   const size_t need = lorabwd_attn_workspace_size(s_q, s_kv, n_heads, n_kv_heads, head_dim, dtype);
   LBP_CHECK(workspace_bytes >= need && (need == 0 || workspace != nullptr), LORABWD_ERR_WORKSPACE);
   LBP_CHECK(aligned16(workspace), LORABWD_ERR_ALIGN);
-  LBP_HIP(launch_attn_bwd(s_q, s_kv, n_heads, n_kv_heads, head_dim, dctx, P, K, V, ctx, dtype, dq,
+  LBP_RUN(launch_attn_bwd(s_q, s_kv, n_heads, n_kv_heads, head_dim, dctx, P, K, V, ctx, dtype, dq,
                           dv, scale, causal, workspace, stream));
   return LORABWD_OK;
 }
@@ -398,7 +438,7 @@ int lorabwd_ffn_backward(int64_t rows, int64_t dim, int64_t ffn_dim, int act, co
   const size_t need = lorabwd_ffn_workspace_size(rows, dim, ffn_dim, dtype);
   LBP_CHECK(workspace && workspace_bytes >= need, LORABWD_ERR_WORKSPACE);
   LBP_CHECK(aligned16(workspace), LORABWD_ERR_ALIGN);
-  LBP_HIP(ffn_run(rows, dim, ffn_dim, act, d_out, w_down, w_gate, w_up, gate, up_, hidden_pre,
+  LBP_RUN(ffn_run(rows, dim, ffn_dim, act, d_out, w_down, w_gate, w_up, gate, up_, hidden_pre,
                   gamma_sub, resid1, gamma_ffn, d_resid, eps, dtype, workspace, stream));
   return LORABWD_OK;
 }
@@ -423,7 +463,7 @@ int lorabwd_lora_grad_adamw(int64_t rows, int64_t in_dim, int64_t out_dim, int64
   LBP_CHECK(workspace && workspace_bytes >= need, LORABWD_ERR_WORKSPACE);
   LBP_CHECK(aligned16(workspace), LORABWD_ERR_ALIGN);
   const AdamHP hp = make_hp(lr_a, lr_b, beta1, beta2, eps, weight_decay, step);
-  LBP_HIP(launch_lora_adamw(rows, in_dim, out_dim, rank, dy, x, h, dtype, A, B, m_a, v_a, m_b,
+  LBP_RUN(launch_lora_adamw(rows, in_dim, out_dim, rank, dy, x, h, dtype, A, B, m_a, v_a, m_b,
                             v_b, grad_a, grad_b, gnorm_sq, alpha / (float)rank, hp, workspace,
                             stream));
   return LORABWD_OK;
@@ -626,13 +666,103 @@ hipError_t decode_chain(const lorabwd_layer_desc* d, const lorabwd_layer_weights
   return launch_dec_attn(dt, (int)d->head_dim, at, s);
 }
 
+// Everything one layer enqueues (arguments already validated).
+hipError_t layer_run(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w,
+                     const lorabwd_layer_saved* a, const lorabwd_lora_state* qs,
+                     const lorabwd_lora_state* vs, const lorabwd_adamw* hp, const LayerPlan& plan,
+                     const float* din, float* d_hidden, float* dqp, float* dv, float* gnorm_sq,
+                     hipStream_t stream) {
+  const int64_t S = d->seq, L = d->kv_len, H = d->hidden, I = d->ffn;
+  const int64_t Hq = d->n_heads, Hkv = d->n_kv_heads, D = d->head_dim;
+  const int64_t qd = Hq * D, kvd = Hkv * D;
+  const int dt = d->dtype;
+  const bool sub = d->sub_norms != 0;
+  const bool lq = has_lora(qs), lv = has_lora(vs);
+  const float lr_a = hp ? hp->lr_a : 0.f, lr_b = hp ? hp->lr_b : 0.f;
+  const int step = hp ? hp->step : 1;
+  hipError_t e;
+  if (use_decode_chain(d)) {
+    LBP_E(decode_chain(d, w, a, plan, din, d_hidden, dqp, dv, stream));
+  } else {
+    // FFN half, residual-stream gradient: d_hidden <- dH1
+    LBP_E(ffn_run(S, H, I, d->act, din, w->w_down, w->w_gate, w->w_up, a->gate, a->up,
+                    sub ? a->hidden_pre : nullptr, sub ? w->gamma_fsub : nullptr, a->resid1,
+                    w->gamma_ffn, d_hidden, d->eps, dt, plan.scratch, stream,
+                    din == d_hidden ? nullptr : din, plan.h16));
+    // O-projection backward: dCtx = dH1 W_o
+    bool dct_ready = false;
+    if (S == 1) {
+      GemvArgs g{};
+      g.N = qd;
+      g.K = H;
+      g.W1 = w->w_o;
+      g.x = d_hidden;
+      g.part = (float*)plan.scratch;
+      LBP_E(launch_dgemv(dt, dt, g, stream));
+      RedArgs r{};
+      r.N = qd;
+      r.splits = (int)dgemv_splits(qd, H);
+      r.part = (float*)plan.scratch;
+      r.y = plan.dctx;
+      LBP_E(launch_dgemv_red(RED_STORE, dt, r, stream));
+    } else {
+      // bf16 weights take the bf16 copy the FFN norm wrote (no rounding
+      // pass); without the sub-norm (which changes dCtx afterwards) the
+      // product also writes dCtxᵀ for the attention's dV (whole row blocks
+      // of 64 queries, so the attention finds no padding to clear)
+      int64_t LQ = 0;
+      uint16_t* dct = !sub && S % 64 == 0
+                          ? attn_dct_buffer(plan.scratch, S, L, Hq, Hkv, D, dt, &LQ)
+                          : nullptr;
+      const TCopy tc{dct, LQ};
+      LBP_E(launch_gemm(S, qd, H, plan.h16 ? (const void*)plan.h16 : (const void*)d_hidden,
+                          plan.h16 ? BF16 : F32, H, w->w_o, nullptr, H, dt, qd, plan.dctx, qd,
+                          (float*)plan.scratch, stream, nullptr, nullptr, nullptr,
+                          dct ? &tc : nullptr, &dct_ready));
+    }
+    if (sub)
+      LBP_E(launch_rmsnorm_bwd(S, qd, a->ctx, dt, w->gamma_asub, plan.dctx, plan.dctx, d->eps, 0,
+                                 stream));
+    // the inverse RoPE (which also adds a split dq's second key half) runs in
+    // the attention's last launch where it can, else on its own
+    const float* dq2 = nullptr;
+    const RopeArgs rope{dqp, d->pos0, d->rope_base};
+    bool rope_done = false;
+    LBP_E(launch_attn_bwd(S, L, Hq, Hkv, D, plan.dctx, a->P, a->K, a->V, a->ctx, dt, plan.dq, dv,
+                            d->attn_scale, d->causal, plan.scratch, stream, &dq2, &rope, &rope_done,
+                            dct_ready));
+    if (!rope_done)
+      LBP_E(launch_rope_bwd(S, Hq, D, plan.dq, dqp, d->pos0, d->rope_base, stream, dq2));
+  }
+  if (lq || lv) {
+    // both adapters' gradient + AdamW passes in the same launches; the
+    // value adapter sees the value rows of the current tokens: the last S of
+    // the kv_len rows (all of them when kv_len == seq)
+    const AdamHP h = make_hp(lr_a, lr_b, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, step);
+    LoraJob jobs[2];
+    int nj = 0;
+    if (lq)
+      jobs[nj++] = LoraJob{S, H, qd, qs->rank, dqp, a->attn_input, a->lora_q_h, dt, qs->A, qs->B,
+                           qs->m_a, qs->v_a, qs->m_b, qs->v_b, nullptr, nullptr,
+                           d->lora_alpha / (float)qs->rank, plan.scratch};
+    if (lv)
+      jobs[nj++] = LoraJob{S, H, kvd, vs->rank, dv + (L - S) * kvd, a->attn_input, a->lora_v_h, dt,
+                           vs->A, vs->B, vs->m_a, vs->v_a, vs->m_b, vs->v_b, nullptr, nullptr,
+                           d->lora_alpha / (float)vs->rank,
+                           (char*)plan.scratch + plan.lora_v_off};
+    LBP_E(launch_lora_adamw_jobs(jobs, nj, gnorm_sq, h, stream));
+  }
+  return hipSuccess;
+}
+
 int desc_validate(const lorabwd_layer_desc* d) {
   LBP_CHECK(d != nullptr, LORABWD_ERR_NULL);
   LBP_CHECK(dtype_ok(d->dtype), LORABWD_ERR_DTYPE);
   LBP_CHECK(d->act == LORABWD_ACT_SWIGLU || d->act == LORABWD_ACT_RELU2, LORABWD_ERR_DTYPE);
-  LBP_CHECK(d->seq >= 0 && d->kv_len >= d->seq && d->kv_len >= 1 && feat_ok(d->hidden) &&
-                feat_ok(d->ffn) && d->n_heads >= 1 && d->n_kv_heads >= 1 &&
-                d->n_heads % d->n_kv_heads == 0 && head_dim_ok(d->head_dim) && d->pos0 >= 0,
+  LBP_CHECK(rows_ok(d->seq) && rows_ok(d->kv_len) && d->kv_len >= d->seq && d->kv_len >= 1 &&
+                feat_ok(d->hidden) && feat_ok(d->ffn) &&
+                heads_ok(d->n_heads, d->n_kv_heads, d->head_dim) && d->pos0 >= 0 &&
+                d->pos0 <= (int64_t(1) << 40),
             LORABWD_ERR_SHAPE);
   LBP_CHECK((d->sub_norms == 0 || d->sub_norms == 1) && (d->causal == 0 || d->causal == 1),
             LORABWD_ERR_ARG);
@@ -719,78 +849,13 @@ int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weig
     if (st != LORABWD_OK) return st;
   }
 
-  // ---- all arguments valid: enqueue
-  if (use_decode_chain(d)) {
-    LBP_HIP(decode_chain(d, w, a, plan, din, d_hidden, dqp, dv, stream));
-  } else {
-    // FFN half, residual-stream gradient: d_hidden <- dH1
-    LBP_HIP(ffn_run(S, H, I, d->act, din, w->w_down, w->w_gate, w->w_up, a->gate, a->up,
-                    sub ? a->hidden_pre : nullptr, sub ? w->gamma_fsub : nullptr, a->resid1,
-                    w->gamma_ffn, d_hidden, d->eps, dt, plan.scratch, stream,
-                    din == d_hidden ? nullptr : din, plan.h16));
-    // O-projection backward: dCtx = dH1 W_o
-    bool dct_ready = false;
-    if (S == 1) {
-      GemvArgs g{};
-      g.N = qd;
-      g.K = H;
-      g.W1 = w->w_o;
-      g.x = d_hidden;
-      g.part = (float*)plan.scratch;
-      LBP_HIP(launch_dgemv(dt, dt, g, stream));
-      RedArgs r{};
-      r.N = qd;
-      r.splits = (int)dgemv_splits(qd, H);
-      r.part = (float*)plan.scratch;
-      r.y = plan.dctx;
-      LBP_HIP(launch_dgemv_red(RED_STORE, dt, r, stream));
-    } else {
-      // bf16 weights take the bf16 copy the FFN norm wrote (no rounding
-      // pass); without the sub-norm (which changes dCtx afterwards) the
-      // product also writes dCtxᵀ for the attention's dV (whole row blocks
-      // of 64 queries, so the attention finds no padding to clear)
-      int64_t LQ = 0;
-      uint16_t* dct = !sub && S % 64 == 0
-                          ? attn_dct_buffer(plan.scratch, S, L, Hq, Hkv, D, dt, &LQ)
-                          : nullptr;
-      const TCopy tc{dct, LQ};
-      LBP_HIP(launch_gemm(S, qd, H, plan.h16 ? (const void*)plan.h16 : (const void*)d_hidden,
-                          plan.h16 ? BF16 : F32, H, w->w_o, nullptr, H, dt, qd, plan.dctx, qd,
-                          (float*)plan.scratch, stream, nullptr, nullptr, nullptr,
-                          dct ? &tc : nullptr, &dct_ready));
-    }
-    if (sub)
-      LBP_HIP(launch_rmsnorm_bwd(S, qd, a->ctx, dt, w->gamma_asub, plan.dctx, plan.dctx, d->eps, 0,
-                                 stream));
-    // the inverse RoPE (which also adds a split dq's second key half) runs in
-    // the attention's last launch where it can, else on its own
-    const float* dq2 = nullptr;
-    const RopeArgs rope{dqp, d->pos0, d->rope_base};
-    bool rope_done = false;
-    LBP_HIP(launch_attn_bwd(S, L, Hq, Hkv, D, plan.dctx, a->P, a->K, a->V, a->ctx, dt, plan.dq, dv,
-                            d->attn_scale, d->causal, plan.scratch, stream, &dq2, &rope, &rope_done,
-                            dct_ready));
-    if (!rope_done)
-      LBP_HIP(launch_rope_bwd(S, Hq, D, plan.dq, dqp, d->pos0, d->rope_base, stream, dq2));
-  }
-  if (lq || lv) {
-    // both adapters' gradient + AdamW passes in the same launches; the
-    // value adapter sees the value rows of the current tokens: the last S of
-    // the kv_len rows (all of them when kv_len == seq)
-    const AdamHP h = make_hp(lr_a, lr_b, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, step);
-    LoraJob jobs[2];
-    int nj = 0;
-    if (lq)
-      jobs[nj++] = LoraJob{S, H, qd, qs->rank, dqp, a->attn_input, a->lora_q_h, dt, qs->A, qs->B,
-                           qs->m_a, qs->v_a, qs->m_b, qs->v_b, nullptr, nullptr,
-                           d->lora_alpha / (float)qs->rank, plan.scratch};
-    if (lv)
-      jobs[nj++] = LoraJob{S, H, kvd, vs->rank, dv + (L - S) * kvd, a->attn_input, a->lora_v_h, dt,
-                           vs->A, vs->B, vs->m_a, vs->v_a, vs->m_b, vs->v_b, nullptr, nullptr,
-                           d->lora_alpha / (float)vs->rank,
-                           (char*)plan.scratch + plan.lora_v_off};
-    LBP_HIP(launch_lora_adamw_jobs(jobs, nj, gnorm_sq, h, stream));
-  }
+  // ---- all arguments valid: a checking pass of the whole composition,
+  // then the real one
+  st = check_pass([&] {
+    return layer_run(d, w, a, qs, vs, hp, plan, din, d_hidden, dqp, dv, gnorm_sq, stream);
+  });
+  if (st != LORABWD_OK) return st;
+  LBP_HIP(layer_run(d, w, a, qs, vs, hp, plan, din, d_hidden, dqp, dv, gnorm_sq, stream));
   return LORABWD_OK;
 }
 

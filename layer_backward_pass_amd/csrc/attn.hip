@@ -1604,6 +1604,15 @@ hipError_t launch_attn_bwd(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n
     a.scale = scale;
     return launch_dec_attn(dt, (int)head_dim, a, s);
   }
+  // buffer ranges (a block of 64 query rows of P, dctx and ctx; 64 key rows
+  // of K and V; one head of the transposed bf16 copies) and grid rows (heads)
+  const double es = dt == F32 ? 4 : 2, lq = (double)n_heads * head_dim;
+  const double lk = (double)n_kv_heads * head_dim;
+  if (64.0 * s_kv * es >= BUF_MAX_BYTES || 64.0 * lq * 4 >= BUF_MAX_BYTES ||
+      64.0 * lk * 4 >= BUF_MAX_BYTES || (double)head_dim * (s_kv + 64) * 2 >= BUF_MAX_BYTES ||
+      (double)head_dim * (s_q + 64) * 2 >= BUF_MAX_BYTES || n_heads > 65535)
+    return hipErrorInvalidValue;
+  if (dry_run()) return hipSuccess;
   if (dt == F32)
     return attn_dispatch_d<float>(s_q, s_kv, (int)n_heads, (int)n_kv_heads, (int)head_dim, dctx,
                                   P, K, V, ctx, dq, dv, scale, causal, ws, s, dq_second, rope,

@@ -529,8 +529,10 @@ hipError_t launch_dgemv(int w_dt, int a_dt, GemvArgs a, hipStream_t s) {
                             (double)a.p.splits * a.p.pn * 4 >= BUF_MAX_BYTES ||
                             (double)a.p.nscal * 8 >= BUF_MAX_BYTES))
     return hipErrorInvalidValue;
-  // buffer ranges: one chunk of weight rows
-  if ((double)a.kc * a.N * (w_dt == F32 ? 4 : 2) >= BUF_MAX_BYTES) return hipErrorInvalidValue;
+  // buffer ranges: one chunk of weight rows, the input vector
+  if ((double)a.kc * a.N * (w_dt == F32 ? 4 : 2) >= BUF_MAX_BYTES || (double)a.K * 4 >= BUF_MAX_BYTES)
+    return hipErrorInvalidValue;
+  if (dry_run()) return hipSuccess;
   if (a.W2 == nullptr) {
     a.W2 = a.W1;
     a.K1 = a.K;
@@ -569,8 +571,9 @@ hipError_t launch_dgemv(int w_dt, int a_dt, GemvArgs a, hipStream_t s) {
 
 hipError_t launch_dgemv_red(int mode, int a_dt, RedArgs a, hipStream_t s) {
   if ((double)a.splits * a.N * 4 >= BUF_MAX_BYTES || (double)a.nscal * 8 >= BUF_MAX_BYTES ||
-      (double)a.copy_n * 4 >= BUF_MAX_BYTES)
+      (double)a.copy_n * 4 >= BUF_MAX_BYTES || (double)a.N * 4 >= BUF_MAX_BYTES)
     return hipErrorInvalidValue;
+  if (dry_run()) return hipSuccess;
   dim3 grid((unsigned)cdiv(a.N, DR_COLS)), block(256);
 #define LBP_RED(TA)                                                        \
   do {                                                                     \
@@ -1311,11 +1314,19 @@ static hipError_t dec_attn_launch(const DecAttnArgs& a, hipStream_t s) {
   const double es = sizeof(T);
   const int nch = (int)cdiv(a.s_kv, DA_KC);
   hipError_t e;
+  // buffer ranges: the whole cache (K, V), P and the query row; the
+  // two-pass path keeps a row of scores per head in LDS
+  if ((double)a.s_kv * Hkv * D * es >= BUF_MAX_BYTES || (double)a.Hq * a.s_kv * es >= BUF_MAX_BYTES ||
+      !dec_attn_fits(a.s_kv, a.Hq, Hkv, D))
+    return hipErrorInvalidValue;
   if (a.part != nullptr) {
     // the caller checked dec_attn_red_fits and passes ctx
     if (a.ctx == nullptr || !dec_attn_red_fits(a.Hq, Hkv, D, a.splits) ||
         (double)a.splits * a.Hq * D * 4 >= BUF_MAX_BYTES || (double)a.nscal * 8 >= BUF_MAX_BYTES)
       return hipErrorInvalidValue;
+  }
+  if (dry_run()) return hipSuccess;
+  if (a.part != nullptr) {
     const int nb = (int)cdiv(a.s_kv, DM_KB);
     const size_t sm = 256 * sizeof(float4) + (size_t)a.grp * D * sizeof(float);
     dec_attn_red_kernel<T, D><<<dim3((unsigned)cdiv(nb, DR_NA), (unsigned)Hkv), dim3(256), sm, s>>>(a);

@@ -722,6 +722,20 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
   }
   if (act_done) *act_done = use_act;
   if (tc_done) *tc_done = use_tc;
+  // buffer ranges: one tile's rows of A, one k-tile of B (an fp32 A of the
+  // bf16 path is first rounded into a dense [M][K] copy)
+  if (b_dt == F32) {
+    if (((double)(F_BM - 1) * lda + K) * 4 >= BUF_MAX_BYTES || 16.0 * ldb >= BUF_MAX_BYTES)
+      return hipErrorInvalidValue;
+  } else {
+    const double la = a_dt == F32 ? (double)K : (double)lda;
+    if (((double)(H_BM - 1) * la + K) * 4 >= BUF_MAX_BYTES || (double)H_BK * ldb * 2 >= BUF_MAX_BYTES)
+      return hipErrorInvalidValue;
+  }
+  if (dry_run()) {
+    if (deferred && nsp > 1 && nfull == 0) *deferred = nsp;
+    return hipSuccess;
+  }
   const int64_t tiles = cdiv(N, pl.bn) * cdiv(M, pl.bm);
   const dim3 grid1((unsigned)(nfull + (tiles - nfull) * nsp));
   if (B2 == nullptr) {
@@ -751,9 +765,6 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
       a_dt = BF16;
       lda = K;
     }
-    // buffer ranges: one tile's rows of A, one k-tile of B
-    if (((double)(H_BM - 1) * lda + K) * 4 >= BUF_MAX_BYTES || (double)H_BK * ldb * 2 >= BUF_MAX_BYTES)
-      return hipErrorInvalidValue;
     const bool splitb = K1 % H_BK != 0;
 #define LBP_GEMM_BF16(SB, E)                                                                \
   gemm_bf16_kernel<SB, E><<<grid1, dim3(H_NT), 0, s>>>(M, N, K, (const uint16_t*)A, lda,      \

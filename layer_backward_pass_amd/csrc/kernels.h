@@ -15,6 +15,15 @@ enum DType { F32 = 0, BF16 = 1 };
 // unless the calling thread is inside lorabwd_layer_backward_timed, which
 // then records a caller-owned event on the stream.
 void mark(const char* name, double alg_bytes, double alg_flops, hipStream_t s);
+
+// Checking pass: while the calling thread runs a composition inside a dry
+// run, every launcher only evaluates the shape limits of its kernels (buffer
+// ranges, LDS sizes) and returns hipSuccess, or hipErrorInvalidValue for a
+// shape its kernels cannot take, without any HIP call.  The C-ABI layer runs
+// each composition this way before the real pass, so a shape the kernels
+// reject is refused before anything is enqueued.  Outputs a launcher reports
+// to its caller (split counts, which epilogue ran) are set as in a real pass.
+bool dry_run();
 enum ActKind { SWIGLU = 0, RELU2 = 1 };
 
 // ---- row-wise kernels (rowwise.hip)

@@ -499,6 +499,16 @@ static hipError_t lora_group(const LoraJob* const* jobs, int nz, float* gnorm_sq
     by_a += (double)j.rank * j.in_dim * 4 * (6 + (j.grad_a ? 1 : 0));
     fl_a += 14.0 * j.rank * j.in_dim;
   }
+  // buffer ranges: one row slice of dy, h, x and g
+  for (int z = 0; z < nz; ++z) {
+    const LoraJob& j = *jobs[z];
+    const Slicing sy = slicing(j.rows, j.out_dim), sa = slicing(j.rows, j.in_dim);
+    const double esz = j.dt == F32 ? 4.0 : 2.0;
+    if ((double)sy.rs * j.out_dim * 4 >= BUF_MAX_BYTES || (double)sy.rs * j.rank * esz >= BUF_MAX_BYTES ||
+        (double)sa.rs * j.in_dim * esz >= BUF_MAX_BYTES || (double)sa.rs * 16 * RB * 4 >= BUF_MAX_BYTES)
+      return hipErrorInvalidValue;
+  }
+  if (dry_run()) return hipSuccess;
   hipError_t e;
   if (rows > 0) {
     lora_dy_kernel<RB, VEC, TH><<<dim3((unsigned)ny), 256, 0, s>>>(dy);

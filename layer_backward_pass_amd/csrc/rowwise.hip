@@ -182,6 +182,7 @@ hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, c
                               hipStream_t s, int nparts, int64_t pstride, const float* rin,
                               uint16_t* dx16) {
   if (rows == 0) return hipSuccess;
+  if (dry_run()) return hipSuccess;
   dim3 grid((unsigned)rows), block(256);
   const int64_t Q = cdiv(n / 4, 256);
   if (Q <= 8 && ((double)(nparts - 1) * pstride + n) * 4 < BUF_MAX_BYTES) {
@@ -232,6 +233,7 @@ __global__ __launch_bounds__(256) void rope_bwd_kernel(int64_t n_heads, int head
 hipError_t launch_rope_bwd(int64_t rows, int64_t n_heads, int64_t head_dim, const float* dy,
                            float* dx, int64_t pos0, float base, hipStream_t s, const float* dy2) {
   if (rows == 0) return hipSuccess;
+  if (dry_run()) return hipSuccess;
   const int threads = rope_threads(n_heads, head_dim);
   rope_bwd_kernel<<<dim3((unsigned)rows), dim3(threads), 0, s>>>(n_heads, (int)head_dim, dy, dy2,
                                                                    dx, pos0, log2((double)base));
@@ -306,6 +308,7 @@ hipError_t launch_act_bwd(int64_t rows, int64_t ffn, int act, const void* gate, 
                           int in_dt, const float* dhid, void* dgu, int out_dt, hipStream_t s,
                           int nparts, int64_t pstride) {
   if (rows == 0) return hipSuccess;
+  if (dry_run()) return hipSuccess;
   if (in_dt == F32) {
     if (act == SWIGLU) act_launch<float, SWIGLU>(rows, ffn, gate, up, dhid, dgu, out_dt, s, nparts, pstride);
     else act_launch<float, RELU2>(rows, ffn, gate, up, dhid, dgu, out_dt, s, nparts, pstride);
@@ -326,6 +329,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(int64_t n, float* __rest
 
 hipError_t launch_fill_zero(int64_t n, float* p, hipStream_t s) {
   if (n == 0) return hipSuccess;
+  if (dry_run()) return hipSuccess;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   fill_zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(n, p);

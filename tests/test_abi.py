@@ -197,6 +197,63 @@ def test_layer_validation(lib):
     assert f(r(d), r(w), r(a), None, None, None, None, dh, None, None, None, fake(60), ws, None) == ESHAPE
 
 
+def far(i):
+    # fake addresses 4 TiB apart, for the multi-gigabyte shapes below
+    return (1 << 46) + i * (1 << 42)
+
+
+def test_size_limits_and_kernel_limits_are_validated(lib):
+    # Row counts and feature sizes above 2^20, more than 4096 heads, and
+    # shapes within those caps that a kernel still cannot take (a 1 GiB buffer
+    # range, the single-token attention's LDS) are refused with ESHAPE by the
+    # validation and checking pass, before any HIP call: with no GPU here a
+    # call that got as far as a launch would report EHIP instead.
+    p = [far(i) for i in range(13)]
+    big = (1 << 20) + 8
+    f = lib.lorabwd_rmsnorm_backward
+    assert f(big, 64, p[0], p[1], p[2], p[3], 1e-6, 0, 0, None) == ESHAPE
+    assert f(4, big, p[0], p[1], p[2], p[3], 1e-6, 0, 0, None) == ESHAPE
+    assert lib.lorabwd_rope_backward(big, 4, 16, p[0], p[1], 0, 1e4, None) == ESHAPE
+    assert lib.lorabwd_rope_backward(4, 8192, 128, p[0], p[1], 0, 1e4, None) == ESHAPE
+
+    def attn(s_q, s_kv, hq, hkv, d):
+        ws = lib.lorabwd_attn_workspace_size(s_q, s_kv, hq, hkv, d, 0)
+        return lib.lorabwd_attn_backward(s_q, s_kv, hq, hkv, d, p[0], p[1], p[2], p[3], p[4],
+                                         p[5], p[6], 0.1, 1, 0, p[7], max(ws, 256), None)
+    assert attn(4, big, 4, 2, 64) == ESHAPE              # rows cap
+    assert attn(1, 4096, 8192, 1024, 16) == ESHAPE       # more than 4096 heads
+    assert attn(1, 4096, 1024, 1024, 128) == ESHAPE      # K/V cache range of 2 GiB
+
+    def ffn(rows, dim, ffn_dim):
+        ws = lib.lorabwd_ffn_workspace_size(rows, dim, ffn_dim, 0)
+        return lib.lorabwd_ffn_backward(rows, dim, ffn_dim, 0, p[0], p[1], p[2], p[3], p[4], p[5],
+                                        None, None, p[6], p[7], p[8], 1e-6, 0, p[9],
+                                        max(ws, 256), None)
+    assert ffn(4, big, 1024) == ESHAPE
+    assert ffn(1, 1 << 20, 1024) == ESHAPE               # one GEMV chunk of weight rows > 1 GiB
+    assert ffn(1, 1024, 1 << 20) == ESHAPE
+
+    def lora(rows, out_dim):
+        ws = lib.lorabwd_lora_workspace_size(rows, 64, out_dim, 4)
+        return lib.lorabwd_lora_grad_adamw(rows, 64, out_dim, 4, p[0], p[1], p[2], p[3], p[4],
+                                           p[5], p[6], p[7], p[8], None, None, None, 8.0, 1e-4,
+                                           1.6e-3, 0.9, 0.999, 1e-8, 0.01, 1, 0, p[9], ws, None)
+    assert lora(big, 64) == ESHAPE
+    assert lora(512, 1 << 20) == ESHAPE                  # a row slice of dy > 1 GiB
+
+    # a one-token layer whose cache range is beyond the kernels' limit
+    d = lbp.make_desc(1, 4096, 1024, 2048, 1024, 1024, 128, act=lbp.ACT_RELU2, pos0=4095)
+    ws = lib.lorabwd_layer_workspace_size(ctypes.byref(d))
+    w = lbp.LayerWeights(*[far(i) for i in range(4)], far(4), None, None)
+    a = lbp.LayerSaved(*[far(10 + i) for i in range(11)])
+    r = ctypes.byref
+    assert lib.lorabwd_layer_backward(r(d), r(w), r(a), None, None, None, None, far(40), None,
+                                      None, None, far(50), ws, None) == ESHAPE
+    d.seq, d.kv_len = big, big
+    assert lib.lorabwd_layer_backward(r(d), r(w), r(a), None, None, None, None, far(40), None,
+                                      None, None, far(50), ws, None) == ESHAPE
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(OSError):
         lbp.load_library(str(tmp_path / "missing.so"))

@@ -6,8 +6,13 @@ pointers and the current HIP stream to the library, and raises LorabwdError
 on a non-zero status.  No computation happens here, and there is no
 fallback: if the library cannot be loaded every call raises.
 
-Workspaces are torch uint8 tensors cached per (device, size class); the
-library itself never allocates.
+Workspaces are torch uint8 tensors cached per (device, stream); the library
+itself never allocates.  Calls on one stream share its workspace (they are
+ordered by the stream); calls on different streams never share one.  A
+workspace that grows is replaced, and the old buffer is kept alive (never
+freed), because a HIP graph captured earlier may still write to it; growing
+while a graph is being captured raises, since the new buffer would be
+allocated inside the capture: run each shape once eagerly before capturing.
 """
 import ctypes
 import os
@@ -197,25 +202,37 @@ def _opt(t, name, dtype=None, shape=None):
     return None if t is None else _need(t, name, dtype, shape)
 
 
-def _stream(stream):
+def _stream_obj(stream, device):
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    return torch.cuda.current_stream(device) if stream is None else stream
+
+
+def _stream(stream, device=None):
+    return _stream_obj(stream, device).cuda_stream
 
 
 _WS = {}
+_RETIRED = []  # superseded workspaces, kept alive for graphs captured with them
 
 
-def _workspace(nbytes, device):
-    """A cached uint8 device buffer of at least nbytes (grown on demand).
-    Calls that share a workspace must be ordered on one stream."""
+def _workspace(nbytes, device, stream=None):
+    """The uint8 device workspace of (device, stream), at least nbytes (grown
+    on demand; see the module docstring)."""
     torch = _torch()
-    key = str(device)
-    buf = _WS.get(key)
     if nbytes == 0:
         return None, 0
+    so = _stream_obj(stream, device)
+    key = (str(device), so.cuda_stream)
+    buf = _WS.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError(
+                "lorabwd: the workspace of this stream would grow to %d bytes during HIP graph "
+                "capture; run the call once eagerly before capturing" % nbytes)
+        if buf is not None:
+            _RETIRED.append(buf)
+        with torch.cuda.stream(so):
+            buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _WS[key] = buf
     return buf, buf.numel()
 
@@ -267,11 +284,11 @@ def lorabwd_attn_backward(dctx, P, K, V, ctx, dq, dv, n_heads, n_kv_heads, head_
         scale = head_dim ** -0.5
     lib = load_library()
     need = lib.lorabwd_attn_workspace_size(s_q, s_kv, n_heads, n_kv_heads, head_dim, dt)
-    ws, wsb = _workspace(need, dq.device)
+    ws, wsb = _workspace(need, dq.device, stream)
     _check("lorabwd_attn_backward", lib.lorabwd_attn_backward(
         s_q, s_kv, n_heads, n_kv_heads, head_dim, _ptr(dctx), _ptr(P), _ptr(K), _ptr(V),
         _ptr(ctx), _ptr(dq), _ptr(dv), scale, int(bool(causal)), dt, _ptr(ws), wsb,
-        _stream(stream)))
+        _stream(stream, dq.device)))
     return dq, dv
 
 
@@ -298,11 +315,11 @@ def lorabwd_ffn_backward(d_out, w_down, w_gate, w_up, gate, up, resid1, gamma_ff
     _f32(d_resid, "d_resid", (rows, dim))
     lib = load_library()
     need = lib.lorabwd_ffn_workspace_size(rows, dim, ffn, dt)
-    ws, wsb = _workspace(need, d_out.device)
+    ws, wsb = _workspace(need, d_out.device, stream)
     _check("lorabwd_ffn_backward", lib.lorabwd_ffn_backward(
         rows, dim, ffn, act, _ptr(d_out), _ptr(w_down), _ptr(w_gate), _ptr(w_up), _ptr(gate),
         _ptr(up), _ptr(hidden_pre), _ptr(gamma_sub), _ptr(resid1), _ptr(gamma_ffn),
-        _ptr(d_resid), eps, dt, _ptr(ws), wsb, _stream(stream)))
+        _ptr(d_resid), eps, dt, _ptr(ws), wsb, _stream(stream, d_out.device)))
     return d_resid
 
 
@@ -331,11 +348,11 @@ def lorabwd_lora_grad_adamw(dy, x, h, A, B, m_a, v_a, m_b, v_b, alpha, lr_a, lr_
         _f32(gnorm_sq, "gnorm_sq", (1,))
     lib = load_library()
     need = lib.lorabwd_lora_workspace_size(rows, in_dim, out_dim, rank)
-    ws, wsb = _workspace(need, dy.device)
+    ws, wsb = _workspace(need, dy.device, stream)
     _check("lorabwd_lora_grad_adamw", lib.lorabwd_lora_grad_adamw(
         rows, in_dim, out_dim, rank, _ptr(dy), _ptr(x), _ptr(h), _ptr(A), _ptr(B), _ptr(m_a),
         _ptr(v_a), _ptr(m_b), _ptr(v_b), _ptr(grad_a), _ptr(grad_b), _ptr(gnorm_sq), alpha, lr_a,
-        lr_b, beta1, beta2, eps, weight_decay, step, dt, _ptr(ws), wsb, _stream(stream)))
+        lr_b, beta1, beta2, eps, weight_decay, step, dt, _ptr(ws), wsb, _stream(stream, dy.device)))
 
 
 def lorabwd_layer_backward_timed(desc, weights, saved, d_hidden, events, records, **kw):
@@ -408,14 +425,14 @@ def lorabwd_layer_backward(desc, weights, saved, d_hidden, q_state=None, v_state
         _f32(gnorm_sq, "gnorm_sq", (1,))
     lib = load_library()
     need = lib.lorabwd_layer_workspace_size(ctypes.byref(d))
-    ws, wsb = _workspace(need, d_hidden.device)
+    ws, wsb = _workspace(need, d_hidden.device, stream)
     args = (ctypes.byref(d), ctypes.byref(w), ctypes.byref(a),
             ctypes.byref(qs) if qs is not None else None,
             ctypes.byref(vs) if vs is not None else None,
             ctypes.byref(adamw) if adamw is not None else None,
             _ptr(d_out), _ptr(d_hidden), _ptr(dq_pre_out), _ptr(dv_out), _ptr(gnorm_sq),
             _ptr(ws), wsb,
-            _stream(stream))
+            _stream(stream, d_hidden.device))
     if timing is None:
         _check("lorabwd_layer_backward", lib.lorabwd_layer_backward(*args))
         return d_hidden

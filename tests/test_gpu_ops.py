@@ -282,6 +282,17 @@ def test_lora_adamw(rows, H, out, rank, step, dt):
     # bf16, whole 64-query blocks: the W_o product also writes dCtxᵀ for dV
     ("seq512", {"seq": 128, "kv_len": 128, "hidden": 256, "ffn": 512, "n_heads": 8,
                 "n_kv_heads": 2, "head_dim": 128, "rank": 8, "alpha": 16.0, "dtype": "bf16"}),
+    # a chunk of tokens after a cached prefix (kv_len > seq) with both
+    # adapters: the value adapter takes the chunk's last rows of dV
+    ("seq512", {"seq": 40, "kv_len": 100, "pos0": 60, "hidden": 256, "ffn": 512, "n_heads": 4,
+                "n_kv_heads": 2, "head_dim": 64, "rank": 8, "alpha": 16.0}),
+    ("seq512", {"seq": 64, "kv_len": 200, "pos0": 136, "hidden": 256, "ffn": 512,
+                "n_heads": 8, "n_kv_heads": 2, "head_dim": 128, "rank": 8, "alpha": 16.0,
+                "dtype": "bf16"}),
+    # one token against a cache too long for the single-token attention
+    # kernels' LDS: the general composition with one query row
+    ("decode", {"hidden": 128, "ffn": 256, "n_heads": 4, "n_kv_heads": 2, "head_dim": 32,
+                "kv_len": 16400, "pos0": 16399}),
 ])
 def test_layer_small(name, over):
     cfg = synth.get_config(name).with_(**over)

@@ -16,7 +16,7 @@ in rotation order (as a model's backward holds its layers), so a graph
 launch is paid once per round of copies, and a graph per copy covers a
 step count that is not a whole number of rounds.
 
-Workloads (default: decode):
+Workloads (default: stack36):
   decode       one token, 512-slot K/V cache, hidden 2560, ffn 6912, 20/5 heads
                of 128, ReLU^2 x up with sub-norms, ternary fp32 weights
   seq512       512 tokens, hidden 2560, ffn 9728, 32/8 heads, SwiGLU, LoRA r16, fp32
@@ -26,9 +26,12 @@ Workloads (default: decode):
 
 Prints ONE JSON line.  `roofline` describes the kernel with the largest
 share of the step, timed with HIP events recorded on the library's stream
-right after each kernel (lorabwd_layer_backward_timed); its algorithmic
-bytes / flops come from the library.  `cpu_baseline` times the float64
-oracle on the host on a bounded sample of the same workload.
+right after each kernel (lorabwd_layer_backward_timed; the raw interval
+between consecutive events, so it includes one event record); its
+algorithmic bytes / flops come from the library.  `attn` sums the attention
+launches of a layer (dA, softmax backward, dQ, dV and their helper launches)
+against the three contractions on unmasked pairs.  `cpu_baseline` times the
+float64 oracle on the host on a bounded sample of the same workload.
 """
 import argparse
 import ctypes
@@ -48,7 +51,7 @@ PEAK = {  # MI355X published peaks (dense)
     "bf16_TFLOPs": 2516.6,
 }
 COPIES = {"decode": 6, "tiny": 1, "seq512": 4, "seq2048bf16": 4, "stack36": 1}
-DEFAULT_STEPS = {"decode": 2000, "tiny": 2000, "seq512": 200, "seq2048bf16": 100, "stack36": 5}
+DEFAULT_STEPS = {"decode": 2000, "tiny": 2000, "seq512": 200, "seq2048bf16": 100, "stack36": 10}
 
 
 def parse():
@@ -56,7 +59,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode", choices=sorted(COPIES))
+    ap.add_argument("--workload", default="stack36", choices=sorted(COPIES))
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline sample budget")
@@ -174,25 +177,15 @@ def kernel_profile(lbp, hip, cfg, copies, torch, reps):
                 prev = ev[i]
                 key = (i, recs[i].name.decode())
                 s = stats.setdefault(key, {"ms": 0.0, "n": 0, "bytes": recs[i].alg_bytes,
-                                           "flops": recs[i].alg_flops})
+                                           "flops": recs[i].alg_flops,
+                                           "impl": recs[i].impl_bytes})
                 s["ms"] += ms
                 s["n"] += 1
-    # cost of one event record between two kernels, measured the same way
-    # with no kernel in between; subtracted from every kernel's interval
-    gaps = []
-    for _ in range(20):
-        torch.sum(filler, dim=(0,), out=sink)
-        hip.record(ev[cap], stream)
-        hip.record(ev[0], stream)
-        hip.record(ev[1], stream)
-        torch.cuda.synchronize()
-        gaps.append(hip.elapsed_ms(ev[0], ev[1]))
-    gap = sorted(gaps)[len(gaps) // 2]
     del filler, sink
     out = []
     for (i, name), s in sorted(stats.items()):
-        out.append({"index": i, "name": name, "avg_ms": max(s["ms"] / s["n"] - gap, 1e-6),
-                    "alg_bytes": s["bytes"], "alg_flops": s["flops"], "event_gap_ms": gap})
+        out.append({"index": i, "name": name, "avg_ms": s["ms"] / s["n"], "alg_bytes": s["bytes"],
+                    "alg_flops": s["flops"], "impl_bytes": s["impl"]})
     return out
 
 
@@ -241,10 +234,42 @@ def roofline(cfg, kernels):
         achieved = nbytes / avg_s / 1e9
         rl = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_GBps"],
               "unit": "GB/s", "frac": round(achieved / PEAK["hbm_GBps"], 4)}
-    rl.update({"kernel": name, "avg_us": round(avg_s * 1e6, 2), "launches_per_step": g["launches"],
-               "event_gap_us": round(kernels[0]["event_gap_ms"] * 1e3, 2),
-               "alg_bytes": nbytes, "alg_flops": flops, "traffic": traffic_for(cfg, name, nbytes)})
+    rl.update({"kernel": name, "avg_us": round(avg_s * 1e6, 2),
+               "launches_per_layer": g["launches"], "alg_bytes": nbytes, "alg_flops": flops,
+               "traffic": traffic_for(cfg, name, nbytes)})
     return rl
+
+
+def attn_pairs(cfg):
+    """Unmasked (query, key) pairs per head (query i at key position
+    kv_len - seq + i when causal)."""
+    s_q, s_kv = cfg.seq, cfg.kv_len
+    if cfg.causal:
+        return s_q * (s_kv - s_q) + s_q * (s_q + 1) / 2.0
+    return float(s_q * s_kv)
+
+
+def attention_summary(cfg, kernels):
+    """The attention launches of one layer (names attn_*, transpose_*, dec_attn_*)
+    together: their summed event-timed duration against the three
+    contractions dA = dCtx V^T, dQ = dS K, dV = P^T dCtx on unmasked pairs
+    (2 flops per multiply-add), and against the single-pass bytes the
+    attention must move (P over unmasked pairs, dCtx, ctx, K, V, dq, dV)."""
+    names = ("attn", "transpose", "dec_attn")
+    ks = [k for k in kernels if k["name"].startswith(names)]
+    if not ks:
+        return None
+    us = sum(k["avg_ms"] for k in ks) * 1e3
+    flops = 3 * 2.0 * cfg.head_dim * attn_pairs(cfg) * cfg.n_heads
+    es = 2 if cfg.dtype == "bf16" else 4
+    qe, kve = cfg.seq * cfg.q_dim, cfg.kv_len * cfg.kv_dim
+    nbytes = (attn_pairs(cfg) * cfg.n_heads * es + qe * (4 + es + 4) + kve * (2 * es + 4))
+    peak = PEAK["bf16_TFLOPs"] if cfg.dtype == "bf16" else PEAK["f32_TFLOPs"]
+    tf = flops / (us * 1e-6) / 1e12
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"launches": [k["name"] for k in ks], "us": round(us, 2), "flops": flops,
+            "TFLOPs": round(tf, 2), "mfma_peak": peak, "mfma_frac": round(tf / peak, 4),
+            "alg_bytes": nbytes, "GBps": round(gbs, 1), "hbm_frac": round(gbs / PEAK["hbm_GBps"], 4)}
 
 
 def traffic_for(cfg, kernel, alg_bytes):
@@ -364,44 +389,65 @@ def traffic_summary(records_json, fetch_csv, write_csv):
 
 
 # ------------------------------------------------------------------ CPU baseline
+def blas_info():
+    """(vendor and version, threads) of NumPy's BLAS."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            b = max(blas, key=lambda i: i.get("num_threads", 1))
+            return "%s %s" % (b.get("internal_api", "?"), b.get("version", "?")), b.get("num_threads", 1)
+    except Exception:  # noqa: BLE001
+        pass
+    return "unknown", 1
+
+
 def cpu_baseline(cfg, budget_s):
-    """The float64 oracle's layer backward on the host, timed on a bounded
-    sample: whole layers of the same workload, repeated until the budget is
-    used (at least once); for the stack, one of its 36 layers."""
+    """The float64 oracle's backward on the host, timed on a bounded sample of
+    the same workload: whole steps (for the stack, all its layers in reverse
+    order, the gradient handed down from layer to layer), repeated until the
+    budget is used (at least once).  Input generation and the float64
+    conversion are outside the timer; the stack's layers take the inputs of
+    a few drawn layers in rotation (the oracle's cost does not depend on the
+    values)."""
     import numpy as np
     import synth
     from oracle import backward as OB
     one = cfg.with_(n_layers=1)
-    t = synth.draw_timing_layer(one, 0)
     f64 = lambda a: np.asarray(a, np.float64)  # noqa: E731
-    w = {k: f64(v) for k, v in t.items() if k.startswith("W_") or k.startswith("gamma_")}
-    saved = {k: f64(t[k]) for k in ("attn_input", "resid1", "gate", "up", "ctx", "P", "K", "V",
-                                    "hidden_pre", "lora_q_h", "lora_v_h") if k in t}
-    lora = None
-    if cfg.rank > 0:
-        lora = {k: f64(v) for k, v in t.items()
-                if k[:2] in ("A_", "B_") or k[:4] in ("m_A_", "m_B_", "v_A_", "v_B_")}
-    d_out = f64(t["d_out"])
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
+    distinct = min(cfg.n_layers, 4)
+    layers = []
+    for l in range(distinct):
+        t = synth.draw_timing_layer(one, l)
+        w = {k: f64(v) for k, v in t.items() if k.startswith("W_") or k.startswith("gamma_")}
+        saved = {k: f64(t[k]) for k in ("attn_input", "resid1", "gate", "up", "ctx", "P", "K",
+                                        "V", "hidden_pre", "lora_q_h", "lora_v_h") if k in t}
+        lora = None
+        if cfg.rank > 0:
+            lora = {k: f64(v) for k, v in t.items()
+                    if k[:2] in ("A_", "B_") or k[:4] in ("m_A_", "m_B_", "v_A_", "v_B_")}
+        layers.append((w, saved, lora))
+        if l == 0:
+            d_out = f64(t["d_out"])
+        del t
+    blas, threads = blas_info()
     runs, t0 = 0, time.perf_counter()
     while True:
-        OB.layer_bwd(one, w, saved, d_out, lora)
+        d = d_out
+        for l in range(cfg.n_layers - 1, -1, -1):
+            w, saved, lora = layers[l % distinct]
+            d = OB.layer_bwd(one, w, saved, d, lora)["d_hidden"]
         runs += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or (runs >= 1 and el * (runs + 1) / runs > 3 * budget_s):
+        if el >= budget_s or el * (runs + 1) / runs > 3 * budget_s:
             break
-    per_layer = el / runs
-    per_step = per_layer * cfg.n_layers
+    per_step = el / runs
+    what = ("%d whole step(s) of the %s workload, each all %d layers in reverse order "
+            "(inputs of %d drawn layers in rotation)" % (runs, cfg.name, cfg.n_layers, distinct)
+            if cfg.n_layers > 1 else "%d whole-layer backward(s) of the %s workload" % (runs, cfg.name))
     return {"value": round(cfg.seq / per_step, 3), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "%d whole-layer backward(s) of the %s workload (%s), %.1f s%s" % (
-                runs, cfg.name, "float64 NumPy", el,
-                "; stack = 36 x one layer" if cfg.n_layers > 1 else "")}
+            "kind": "oracle", "blas": blas,
+            "sample": "%s; float64 NumPy, %.1f s timed, input generation excluded" % (what, el)}
 
 
 # ------------------------------------------------------------------ main
@@ -478,6 +524,7 @@ def main():
     kernels = kernel_profile(lbp, hip, cfg, copies, torch,
                              reps=max(3, min(20, steps // 10)) if cfg.n_layers == 1 else 1)
     rl = roofline(cfg, kernels)
+    attn = attention_summary(cfg, kernels)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, args.cpu_seconds)
@@ -502,8 +549,11 @@ def main():
                    "steps_per_graph_launch": len(copies) if round_graph is not None else 1,
                    "kernels_per_step": len(kernels) * (cfg.n_layers if cfg.n_layers > 1 else 1)},
         "roofline": rl,
+        "attn": attn,
         "cpu_baseline": cpu,
-        "kernels": [{"name": k["name"], "avg_us": round(k["avg_ms"] * 1e3, 2)} for k in kernels],
+        "kernels": [{"name": k["name"], "avg_us": round(k["avg_ms"] * 1e3, 2),
+                     "alg_MB": round(k["alg_bytes"] / 1e6, 3), "impl_MB": round(k["impl_bytes"] / 1e6, 3),
+                     "GFLOP": round(k["alg_flops"] / 1e9, 3)} for k in kernels],
     }
     print(json.dumps(out))
     return 0

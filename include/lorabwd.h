@@ -278,10 +278,15 @@ int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weig
  * Measurement variant of lorabwd_layer_backward: the same work on the same
  * stream, and right after the i-th kernel it enqueues (i < capacity) it
  * records the caller-created HIP event events[i] on `stream` and fills
- * records[i] with the kernel's name and the algorithmic HBM bytes and
+ * records[i] with the kernel's name, the algorithmic HBM bytes and
  * floating-point operations that kernel's step of the method has to move /
- * perform at this shape (masked attention pairs, split-K partial sums and
- * other implementation traffic are not counted).  *n_kernels receives the
+ * perform at this shape, and an estimate of the bytes it moves on top.
+ * Algorithmic bytes are the method's single pass: every tensor at the step's
+ * boundary read or written once at its storage type, masked attention pairs
+ * excluded; a tensor that several launches of one step read (P in the dQ and
+ * the dV launches, the partial sums of a split product) is counted once, at
+ * one of them.  impl_bytes holds the rest: split-K and chunk partials,
+ * transposed or rounded copies, second reads.  *n_kernels receives the
  * number of kernels enqueued.  With an event recorded just before the call,
  * consecutive events bracket each kernel.
  * ---------------------------------------------------------------------- */
@@ -289,6 +294,7 @@ typedef struct lorabwd_kernel_record {
   const char* name;  /* static string */
   double alg_bytes;
   double alg_flops;
+  double impl_bytes;
 } lorabwd_kernel_record;
 
 int lorabwd_layer_backward_timed(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w,

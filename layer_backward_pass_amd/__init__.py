@@ -78,7 +78,7 @@ class LayerSaved(ctypes.Structure):
 
 class KernelRecord(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char_p), ("alg_bytes", ctypes.c_double),
-                ("alg_flops", ctypes.c_double)]
+                ("alg_flops", ctypes.c_double), ("impl_bytes", ctypes.c_double)]
 
 
 class LoraState(ctypes.Structure):

@@ -22,7 +22,8 @@ static thread_local bool tl_dry = false;
 
 bool dry_run() { return tl_dry; }
 
-void mark(const char* name, double alg_bytes, double alg_flops, hipStream_t s) {
+void mark(const char* name, double alg_bytes, double alg_flops, hipStream_t s,
+          double impl_bytes) {
   Recorder* r = tl_recorder;
   if (r == nullptr) return;
   if (r->count < r->capacity) {
@@ -30,6 +31,7 @@ void mark(const char* name, double alg_bytes, double alg_flops, hipStream_t s) {
     r->records[r->count].name = name;
     r->records[r->count].alg_bytes = alg_bytes;
     r->records[r->count].alg_flops = alg_flops;
+    r->records[r->count].impl_bytes = impl_bytes;
   }
   ++r->count;
 }
@@ -365,7 +367,7 @@ const char* lorabwd_status_string(int status) {
   }
 }
 
-int lorabwd_abi_version(void) { return 1; }
+int lorabwd_abi_version(void) { return 2; }
 
 int lorabwd_rmsnorm_backward(int64_t rows, int64_t n, const void* x, const float* gamma,
                              const float* dy, float* dx, float eps, int accumulate, int dtype,

@@ -500,7 +500,7 @@ static hipError_t launch_dv_reduce(int64_t s_q, int64_t s_kv, int Hq, int Hkv, i
   if (rope == nullptr || rope_done == nullptr) {
     attn_dv_reduce_kernel<<<dim3((unsigned)nred), 256, 0, s>>>(s_q, s_kv, ldk, cmax, cs, part, dv,
                                                                causal, Hq / Hkv, geo);
-    mark("attn_dv_reduce", kvbytes * (cmax + 1), 0, s);
+    mark("attn_dv_reduce", 0, 0, s, kvbytes * (cmax + 1));  // dV counted at the dV launch
     return hipGetLastError();
   }
   const RopeRows r{dq, dq2, rope->dx, Hq, D, rope_threads(Hq, D), rope->pos0,
@@ -508,7 +508,9 @@ static hipError_t launch_dv_reduce(int64_t s_q, int64_t s_kv, int Hq, int Hkv, i
   attn_dv_reduce_rope_kernel<<<dim3((unsigned)(nred + s_q)), 256, 0, s>>>(
       s_q, s_kv, ldk, cmax, cs, part, dv, causal, Hq / Hkv, geo, nred, r);
   const double qe = (double)s_q * Hq * D;
-  mark("attn_dv_reduce_rope", kvbytes * (cmax + 1) + qe * (dq2 ? 12 : 8), qe * 3, s);
+  // the inverse RoPE reads dq and writes dq_pre (a split dq's second half on
+  // top); dV was counted at the dV launch, its chunk partials are not
+  mark("attn_dv_reduce_rope", qe * 8, qe * 3, s, kvbytes * (cmax + 1) + (dq2 ? qe * 4 : 0.0));
   *rope_done = true;
   return hipGetLastError();
 }
@@ -1380,7 +1382,7 @@ static hipError_t attn_launch_f32(int64_t s_q, int64_t s_kv, int Hq, int Hkv, co
   if (ctx == nullptr) {
     attn_delta_kernel<float, D><<<dim3((unsigned)cdiv64(s_q, 4), (unsigned)Hq), 256, 0, s>>>(
         s_q, s_kv, Hq, grp, dctx, P, V, delta, causal);
-    mark("attn_delta", pbytes + qbytes + kvbytes + (double)Hq * s_q * 4, 2.0 * D * pairs * Hq, s);
+    mark("attn_delta", 0, 2.0 * D * pairs * Hq, s, pbytes + qbytes + kvbytes + (double)Hq * s_q * 4);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int hw = grp % 4 == 0 ? 4 : (grp % 2 == 0 ? 2 : 1);
@@ -1394,7 +1396,10 @@ static hipError_t attn_launch_f32(int64_t s_q, int64_t s_kv, int Hq, int Hkv, co
     launch_dq_f32<D, 2>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta, dq, dq2, ksplit, scale, causal, s);
   else
     launch_dq_f32<D, 1>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta, dq, dq2, ksplit, scale, causal, s);
-  mark("attn_dq_f32", pbytes + qbytes * (ctx ? 3 : 2) + 2 * kvbytes, 4.0 * D * pairs * Hq, s);
+  // the attention's single pass: P, dCtx, ctx, K and V read once, dq
+  // written (dV's write is counted at its launch)
+  mark("attn_dq_f32", pbytes + qbytes * (ctx ? 3 : 2) + 2 * kvbytes, 4.0 * D * pairs * Hq, s,
+       ksplit ? qbytes : 0.0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ksplit && dq_second != nullptr) {
     *dq_second = dq2;  // the caller adds it (the inverse RoPE pass does)
@@ -1403,7 +1408,7 @@ static hipError_t attn_launch_f32(int64_t s_q, int64_t s_kv, int Hq, int Hkv, co
     int64_t blocks = cdiv64(n4, 256);
     if (blocks > 4096) blocks = 4096;
     add_inplace_kernel<<<dim3((unsigned)blocks), 256, 0, s>>>(n4, dq, dq2);
-    mark("attn_dq_add", qbytes * 3, 0, s);
+    mark("attn_dq_add", 0, 0, s, qbytes * 3);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (dv == nullptr) return hipSuccess;
@@ -1411,8 +1416,8 @@ static hipError_t attn_launch_f32(int64_t s_q, int64_t s_kv, int Hq, int Hkv, co
   float* part = dp.cmax > 1 ? (float*)((char*)ws + wl.part) : dv;
   attn_dv_f32_kernel<D><<<dim3((unsigned)dp.items), 256, 0, s>>>(
       s_q, s_kv, Hq, grp, dp.cmax, dp.cs, dp.nfull, dctx, P, part, causal);
-  mark("attn_dv_f32", pbytes + qbytes + kvbytes * (dp.cmax > 1 ? dp.cmax : 1),
-       2.0 * D * pairs * Hq, s);
+  mark("attn_dv_f32", kvbytes, 2.0 * D * pairs * Hq, s,
+       pbytes + qbytes + (dp.cmax > 1 ? kvbytes * (dp.cmax - 1) : 0.0));
   if ((e = hipGetLastError()) != hipSuccess || dp.cmax == 1) return e;
   return launch_dv_reduce(s_q, s_kv, Hq, Hkv, D, dp.cmax, dp.cs, part, dv, causal, FV_GEO, dq,
                           ksplit && dq_second != nullptr ? dq2 : nullptr, rope, rope_done, s);
@@ -1472,16 +1477,15 @@ static hipError_t attn_launch_bf16(int64_t s_q, int64_t s_kv, int Hq, int Hkv, c
                  dv != nullptr && !dct_ready ? (int)(Hq * D / TR_C) : 0};
   const int64_t ntr = (int64_t)jk.gx * jk.gy + (int64_t)jd.gx * jd.gy;
   transpose_bf16_kernel<bf16, float><<<dim3((unsigned)ntr), 256, 0, s>>>(jk, jd);
-  mark("transpose_bf16",
+  mark("transpose_bf16", 0, 0, s,
        kvbytes * 2 + (double)Hkv * D * wl.LK * 2 +
-           (jd.gy > 0 ? qbytes * 4 + (double)Hq * D * wl.LQ * 2 : 0.0),
-       0, s);
+           (jd.gy > 0 ? qbytes * 4 + (double)Hq * D * wl.LQ * 2 : 0.0));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ctx == nullptr) {
     attn_delta_kernel<bf16, D><<<dim3((unsigned)cdiv64(s_q, 4), (unsigned)Hq), 256, 0, s>>>(
         s_q, s_kv, Hq, grp, dctx, (const bf16*)P, (const bf16*)V, delta, causal);
-    mark("attn_delta", pbytes + qbytes * 4 + kvbytes * 2 + (double)Hq * s_q * 4,
-         2.0 * D * pairs * Hq, s);
+    mark("attn_delta", 0, 2.0 * D * pairs * Hq, s,
+         pbytes + qbytes * 4 + kvbytes * 2 + (double)Hq * s_q * 4);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // dQ, and with dv wanted dV in the same launch
@@ -1498,12 +1502,16 @@ static hipError_t attn_launch_bf16(int64_t s_q, int64_t s_kv, int Hq, int Hkv, c
   else
     launch_dq_bf16<D, 1>(s_q, s_kv, Hq, grp, wl.LK, dctx, P, Kt, V, ctx, delta, dq, scale, causal, s,
                          dpp, wl.LQ, dCt, part);
-  const double dqb = pbytes + qbytes * (4 + 4 + (ctx ? 2 : 0)) + 2 * kvbytes * 2;
-  const double dvb = pbytes + qbytes * 2 + kvbytes * 4 * (dp.cmax > 1 ? dp.cmax : 1);
+  // the attention's single pass: P, dCtx (fp32), ctx, K and V read once,
+  // dq and dV written; the dV body's second read of P, the transposed
+  // copies it reads and its chunk partials are implementation traffic
+  const double alg = pbytes + qbytes * (4 + 4 + (ctx ? 2 : 0)) + 2 * kvbytes * 2 +
+                     (dv != nullptr ? kvbytes * 4 : 0.0);
   if (dv == nullptr)
-    mark("attn_dq_bf16", dqb, 4.0 * D * pairs * Hq, s);
+    mark("attn_dq_bf16", alg, 4.0 * D * pairs * Hq, s);
   else
-    mark("attn_dqdv_bf16", dqb + dvb, 6.0 * D * pairs * Hq, s);
+    mark("attn_dqdv_bf16", alg, 6.0 * D * pairs * Hq, s,
+         pbytes + qbytes * 2 + (dp.cmax > 1 ? kvbytes * 4 * (dp.cmax - 1) : 0.0));
   if ((e = hipGetLastError()) != hipSuccess || dv == nullptr || dp.cmax == 1) return e;
   return launch_dv_reduce(s_q, s_kv, Hq, Hkv, D, dp.cmax, dp.cs, part, dv, causal, HV_GEO, dq,
                           nullptr, rope, rope_done, s);
@@ -1523,25 +1531,25 @@ static hipError_t attn_launch(int64_t s_q, int64_t s_kv, int Hq, int Hkv, const 
   if (ctx != nullptr) {
     attn_dq_kernel<T, D, 1><<<gq, block, 0, s>>>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, nullptr,
                                                   dq, scale, causal);
-    mark("attn_dq_mfma", pbytes + qbytes * (8 + es) + 2 * kvbytes * es, 4.0 * D * pairs * Hq, s);
+    mark("attn_dq_mfma", pbytes + qbytes * (8 + es) + 2 * kvbytes * es, 4.0 * D * pairs * Hq, s);  // P, dCtx, ctx, K, V once; dq
   } else {
     attn_delta_kernel<T, D><<<dim3((unsigned)((s_q + 3) / 4), (unsigned)Hq), block, 0, s>>>(
         s_q, s_kv, Hq, grp, dctx, P, V, ws, causal);
-    mark("attn_delta", pbytes + qbytes * 4 + kvbytes * es + (double)Hq * s_q * 4,
-         2.0 * D * pairs * Hq, s);
+    mark("attn_delta", 0, 2.0 * D * pairs * Hq, s,
+         pbytes + qbytes * 4 + kvbytes * es + (double)Hq * s_q * 4);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     attn_dq_kernel<T, D, 0><<<gq, block, 0, s>>>(s_q, s_kv, Hq, grp, dctx, P, K, V, nullptr, ws,
                                                   dq, scale, causal);
-    mark("attn_dq_mfma", pbytes + qbytes * 8 + 2 * kvbytes * es + (double)Hq * s_q * 4,
-         4.0 * D * pairs * Hq, s);
+    mark("attn_dq_mfma", pbytes + qbytes * 8 + 2 * kvbytes * es, 4.0 * D * pairs * Hq, s,
+         (double)Hq * s_q * 4);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || dv == nullptr) return e;
   constexpr int KB = 16 * (D >= 32 ? 2 : 4);
   attn_dv_kernel<T, D><<<dim3((unsigned)((s_kv + KB - 1) / KB), (unsigned)Hkv), block, 0, s>>>(
       s_q, s_kv, Hq, grp, dctx, P, dv, causal);
-  mark("attn_dv_mfma", pbytes + qbytes * 4 + kvbytes * 4, 2.0 * D * pairs * Hq, s);
+  mark("attn_dv_mfma", kvbytes * 4, 2.0 * D * pairs * Hq, s, pbytes + qbytes * 4);
   return hipGetLastError();
 }
 

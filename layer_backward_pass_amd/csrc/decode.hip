@@ -565,7 +565,12 @@ hipError_t launch_dgemv(int w_dt, int a_dt, GemvArgs a, hipStream_t s) {
     if (a.p.scal) xin += a.p.pn * (ae + 4);
     xin += a.pro == PRO_ACT ? a.p.pn * 2 * ae : a.p.pn * 8.0;
   }
-  mark("dgemv", (double)a.K * a.N * es + xin + a.N * 4.0, 2.0 * a.K * a.N, s);
+  // implementation traffic: this launch's row-chunk partials beyond one
+  // result vector, and the producer partials every column block re-reads
+  const double nsp = (double)cdiv(a.K, a.kc);
+  const double reread = a.pro != PRO_COPY ? (double)cdiv(a.N, DG_COLS) * a.p.splits * a.p.pn * 4.0 - a.p.pn * 4.0 : 0.0;
+  mark("dgemv", (double)a.K * a.N * es + xin + a.N * 4.0, 2.0 * a.K * a.N, s,
+       (nsp - 1) * a.N * 4.0 + reread);
   return hipGetLastError();
 }
 
@@ -1332,12 +1337,11 @@ static hipError_t dec_attn_launch(const DecAttnArgs& a, hipStream_t s) {
     dec_attn_red_kernel<T, D><<<dim3((unsigned)cdiv(nb, DR_NA), (unsigned)Hkv), dim3(256), sm, s>>>(a);
     mark("dec_attn_red",
          2.0 * a.s_kv * Hkv * D * es + (double)a.Hq * a.s_kv * es + (double)a.Hq * D * (4 + es) +
-             (a.dv ? (double)a.s_kv * Hkv * D * 4 : 0.0) + (double)a.Hq * nb * D * 4 +
-             (double)a.copy_n * 8,
-         6.0 * D * a.Hq * a.s_kv, s);
+             (a.dv ? (double)a.s_kv * Hkv * D * 4 : 0.0) + (double)a.copy_n * 8,
+         6.0 * D * a.Hq * a.s_kv, s, (double)a.Hq * nb * D * 4);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     dec_attn_dqc_kernel<D><<<dim3((unsigned)a.Hq), dim3(D), 0, s>>>(a, nb);
-    mark("dec_attn_dqc", (double)a.Hq * nb * D * 4 + (double)a.Hq * D * 4, 0, s);
+    mark("dec_attn_dqc", (double)a.Hq * D * 4, 0, s, (double)a.Hq * nb * D * 4);
     return hipGetLastError();
   }
   if (a.ctx != nullptr && a.grp <= 16) {
@@ -1345,11 +1349,11 @@ static hipError_t dec_attn_launch(const DecAttnArgs& a, hipStream_t s) {
     dec_attn_mfma_kernel<T, D><<<dim3((unsigned)nb, (unsigned)Hkv), dim3(64), 0, s>>>(a);
     mark("dec_attn_mfma",
          2.0 * a.s_kv * Hkv * D * es + (double)a.Hq * a.s_kv * es + (double)a.Hq * D * (4 + es) +
-             (a.dv ? (double)a.s_kv * Hkv * D * 4 : 0.0) + (double)a.Hq * nb * D * 4,
-         6.0 * D * a.Hq * a.s_kv, s);
+             (a.dv ? (double)a.s_kv * Hkv * D * 4 : 0.0),
+         6.0 * D * a.Hq * a.s_kv, s, (double)a.Hq * nb * D * 4);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     dec_attn_dqc_kernel<D><<<dim3((unsigned)a.Hq), dim3(D), 0, s>>>(a, nb);
-    mark("dec_attn_dqc", (double)a.Hq * nb * D * 4 + (double)a.Hq * D * 4, 0, s);
+    mark("dec_attn_dqc", (double)a.Hq * D * 4, 0, s, (double)a.Hq * nb * D * 4);
     return hipGetLastError();
   }
   if (a.ctx != nullptr && a.grp <= 64 && dec_attn1c_smem(a.grp, D) <= 64 * 1024) {
@@ -1357,24 +1361,25 @@ static hipError_t dec_attn_launch(const DecAttnArgs& a, hipStream_t s) {
                               dec_attn1c_smem(a.grp, D), s>>>(a);
     mark("dec_attn1c",
          2.0 * a.s_kv * Hkv * D * es + (double)a.Hq * a.s_kv * es + (double)a.Hq * D * (4 + es) +
-             (a.dv ? (double)a.s_kv * Hkv * D * 4 : 0.0) + (double)a.Hq * nch * D * 4,
-         6.0 * D * a.Hq * a.s_kv, s);
+             (a.dv ? (double)a.s_kv * Hkv * D * 4 : 0.0),
+         6.0 * D * a.Hq * a.s_kv, s, (double)a.Hq * nch * D * 4);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     dec_attn_dqc_kernel<D><<<dim3((unsigned)a.Hq), dim3(D), 0, s>>>(a, nch);
-    mark("dec_attn_dqc", (double)a.Hq * nch * D * 4 + (double)a.Hq * D * 4, 0, s);
+    mark("dec_attn_dqc", (double)a.Hq * D * 4, 0, s, (double)a.Hq * nch * D * 4);
     return hipGetLastError();
   }
   dec_attn1_kernel<T, D><<<dim3((unsigned)nch, (unsigned)Hkv), dim3(256),
                            dec_attn1_smem(a.grp, D), s>>>(a);
+  // P, V, dCtx and K (second launch) once, dV and dq written; dA is an
+  // intermediate written here and read by the second launch
   mark("dec_attn1",
-       (double)a.s_kv * Hkv * D * es + (double)a.Hq * a.s_kv * (es + 4) + (double)a.Hq * D * 4 +
+       (double)a.s_kv * Hkv * D * es + (double)a.Hq * a.s_kv * es + (double)a.Hq * D * 4 +
            (a.dv ? (double)a.s_kv * Hkv * D * 4 : 0.0),
-       4.0 * D * a.Hq * a.s_kv, s);
+       4.0 * D * a.Hq * a.s_kv, s, (double)a.Hq * a.s_kv * 4);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   dec_attn2_kernel<T, D><<<dim3((unsigned)a.Hq), dim3(1024), dec_attn2_smem(a.s_kv, D), s>>>(a);
-  mark("dec_attn2",
-       (double)a.Hq * a.s_kv * (es + 4) + (double)a.s_kv * Hkv * D * es + (double)a.Hq * D * 4,
-       2.0 * D * a.Hq * a.s_kv, s);
+  mark("dec_attn2", (double)a.s_kv * Hkv * D * es + (double)a.Hq * D * 4, 2.0 * D * a.Hq * a.s_kv, s,
+       (double)a.Hq * a.s_kv * (es + 4));
   return hipGetLastError();
 }
 

@@ -697,6 +697,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
                        const void* B1, const void* B2, int64_t K1, int b_dt, int64_t ldb,
                        float* C, int64_t ldc, float* partials, hipStream_t s, int* deferred,
                        const ActEpi* act, bool* act_done, const TCopy* tc, bool* tc_done) {
+  const int a_dt0 = a_dt;  // the operand as the caller holds it
   if (deferred) *deferred = 1;
   if (act_done) *act_done = false;
   if (tc_done) *tc_done = false;
@@ -759,7 +760,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
       int64_t blocks = cdiv(M * (K / 8), 256);
       if (blocks > 8192) blocks = 8192;
       cvt_a_bf16_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(M, K, (const float*)A, lda, a16);
-      mark("cvt_a_bf16", (double)M * K * 6, 0, s);
+      mark("cvt_a_bf16", 0, 0, s, (double)M * K * 6);  // a rounded copy of A
       if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
       A = a16;
       a_dt = BF16;
@@ -789,10 +790,16 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
   // with the activation epilogue the product's output is [dGate | dUp] from
   // gate and up (weights' dtype) instead of C
   const double es = b_dt == F32 ? 4 : 2;
+  // A at the type the caller holds it (a rounded copy is implementation
+  // traffic), B once, the result once (with the activation epilogue: gate and
+  // up read, [dGate | dUp] written, in place of dHid); split-K partials and
+  // the transposed bf16 copy are implementation traffic
   mark(b_dt == F32 ? "gemm_f32_mfma" : "gemm_bf16_mfma",
-       (double)M * K * (a_dt == F32 ? 4 : 2) + (double)K * N * es +
-           (use_act ? (double)M * N * 4 * es : (double)M * N * (use_tc ? 6 : 4)),
-       2.0 * M * N * K, s);
+       (double)M * K * (a_dt0 == F32 ? 4 : 2) + (double)K * N * es +
+           (use_act ? (double)M * N * 4 * es : (double)M * N * 4),
+       2.0 * M * N * K, s,
+       (use_tc ? (double)M * N * 2 : 0.0) +
+           (nsp > 1 ? (double)(tiles - nfull) * pl.bm * pl.bn * 4 * nsp : 0.0));
   if (e != hipSuccess || nsp == 1) return e;
   if (deferred && nfull == 0) {
     // plain split-K: the caller adds the partials itself
@@ -814,7 +821,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
     default: LBP_RED(0);
   }
 #undef LBP_RED
-  mark("splitk_reduce", 0, 0, s);
+  mark("splitk_reduce", 0, 0, s, (double)(tiles - nfull) * pl.bm * pl.bn * 4 * (nsp + 1));
   return hipGetLastError();
 }
 

@@ -11,10 +11,16 @@ namespace lbp {
 enum DType { F32 = 0, BF16 = 1 };
 
 // Measurement hook: after each kernel launch a launcher calls mark() with the
-// kernel's name and its algorithmic HBM bytes and flops.  It does nothing
-// unless the calling thread is inside lorabwd_layer_backward_timed, which
-// then records a caller-owned event on the stream.
-void mark(const char* name, double alg_bytes, double alg_flops, hipStream_t s);
+// kernel's name, its algorithmic HBM bytes and flops (the method's single
+// pass: every tensor at the step's boundary read or written once at its
+// storage type, masked attention pairs excluded; a tensor read by several
+// launches of one step is counted at one of them), and the implementation
+// bytes it moves on top (split-K and chunk partials, transposed or rounded
+// copies, second reads).  It does nothing unless the calling thread is inside
+// lorabwd_layer_backward_timed, which then records a caller-owned event on
+// the stream.
+void mark(const char* name, double alg_bytes, double alg_flops, hipStream_t s,
+          double impl_bytes = 0.0);
 
 // Checking pass: while the calling thread runs a composition inside a dry
 // run, every launcher only evaluates the shape limits of its kernels (buffer

@@ -215,8 +215,8 @@ hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, c
       rmsnorm_bwd_kernel<bf16, 0><<<grid, block, 0, s>>>(n, (const bf16*)x, gamma, dy, dx, eps, nparts, pstride, rin, dx16);
   }
   mark("rmsnorm_bwd",
-       (double)rows * n * ((xdt == F32 ? 4 : 2) + 4 * nparts + 4 + (accumulate ? 4 : 0)) + n * 4.0,
-       (double)rows * n * 8, s);
+       (double)rows * n * ((xdt == F32 ? 4 : 2) + 4 + 4 + (accumulate ? 4 : 0)) + n * 4.0,
+       (double)rows * n * 8, s, (double)rows * n * (4.0 * (nparts - 1) + (dx16 ? 2 : 0)));
   return hipGetLastError();
 }
 
@@ -237,8 +237,8 @@ hipError_t launch_rope_bwd(int64_t rows, int64_t n_heads, int64_t head_dim, cons
   const int threads = rope_threads(n_heads, head_dim);
   rope_bwd_kernel<<<dim3((unsigned)rows), dim3(threads), 0, s>>>(n_heads, (int)head_dim, dy, dy2,
                                                                    dx, pos0, log2((double)base));
-  mark("rope_bwd", (double)rows * n_heads * head_dim * (dy2 ? 12 : 8),
-       (double)rows * n_heads * head_dim * 3, s);
+  mark("rope_bwd", (double)rows * n_heads * head_dim * 8, (double)rows * n_heads * head_dim * 3,
+       s, dy2 ? (double)rows * n_heads * head_dim * 4 : 0.0);
   return hipGetLastError();
 }
 
@@ -316,8 +316,8 @@ hipError_t launch_act_bwd(int64_t rows, int64_t ffn, int act, const void* gate, 
     if (act == SWIGLU) act_launch<bf16, SWIGLU>(rows, ffn, gate, up, dhid, dgu, out_dt, s, nparts, pstride);
     else act_launch<bf16, RELU2>(rows, ffn, gate, up, dhid, dgu, out_dt, s, nparts, pstride);
   }
-  mark("act_bwd", (double)rows * ffn * (2 * (in_dt == F32 ? 4 : 2) + 4 * nparts + 2 * (out_dt == F32 ? 4 : 2)),
-       (double)rows * ffn * 12, s);
+  mark("act_bwd", (double)rows * ffn * (2 * (in_dt == F32 ? 4 : 2) + 4 + 2 * (out_dt == F32 ? 4 : 2)),
+       (double)rows * ffn * 12, s, (double)rows * ffn * 4 * (nparts - 1));
   return hipGetLastError();
 }
 
@@ -333,7 +333,7 @@ hipError_t launch_fill_zero(int64_t n, float* p, hipStream_t s) {
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   fill_zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(n, p);
-  mark("fill_zero", (double)n * 4, 0, s);
+  mark("fill_zero", (double)n * 4, 0, s);  // dV of no queries: the output itself
   return hipGetLastError();
 }
 

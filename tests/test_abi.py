@@ -56,7 +56,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.lorabwd_abi_version() == 1
+    assert lib.lorabwd_abi_version() == 2
     for code in (OK, ENULL, ESHAPE, EALIGN, EDTYPE, EWS, ESTEP, EALIAS, EHIP, EARG):
         s = lib.lorabwd_status_string(code).decode()
         assert s and s != "unknown status"

@@ -10,9 +10,10 @@ Workspaces are torch uint8 tensors cached per (device, stream); the library
 itself never allocates.  Calls on one stream share its workspace (they are
 ordered by the stream); calls on different streams never share one.  A
 workspace that grows is replaced, and the old buffer is kept alive (never
-freed), because a HIP graph captured earlier may still write to it; growing
-while a graph is being captured raises, since the new buffer would be
-allocated inside the capture: run each shape once eagerly before capturing.
+freed), because a HIP graph captured earlier may still write to it.  Under
+graph capture the capture stream gets its own workspace, allocated from the
+graph's memory pool and likewise kept alive; graphs captured on one stream
+share it, so replaying two of them concurrently on different streams races.
 """
 import ctypes
 import os
@@ -225,10 +226,6 @@ def _workspace(nbytes, device, stream=None):
     key = (str(device), so.cuda_stream)
     buf = _WS.get(key)
     if buf is None or buf.numel() < nbytes:
-        if torch.cuda.is_current_stream_capturing():
-            raise RuntimeError(
-                "lorabwd: the workspace of this stream would grow to %d bytes during HIP graph "
-                "capture; run the call once eagerly before capturing" % nbytes)
         if buf is not None:
             _RETIRED.append(buf)
         with torch.cuda.stream(so):

@@ -305,6 +305,27 @@ int lorabwd_layer_backward_timed(const lorabwd_layer_desc* d, const lorabwd_laye
                                  size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
                                  lorabwd_kernel_record* records, int capacity, int* n_kernels);
 
+/* ------------------------------------------------------------------------
+ * Allocation-free variant of lorabwd_layer_backward, for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments
+ * and results as lorabwd_layer_backward, without workspace: the scratch is
+ * a static device array of LORABWD_NOALLOC_SCRATCH_BYTES that every GPU the
+ * library runs on holds until the process ends (found on the device that is
+ * current at the call, once per device).  The single-token layer needs about
+ * 3.6 MiB at hidden 2560 / ffn 6912 / 512 cached keys; a layer whose
+ * lorabwd_layer_workspace_size exceeds the limit returns
+ * LORABWD_ERR_WORKSPACE before anything is enqueued.  All calls on one GPU
+ * share that scratch: calls that overlap in time on one GPU (different
+ * streams, or graphs replayed concurrently) race and must not be issued.
+ * ---------------------------------------------------------------------- */
+#define LORABWD_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int lorabwd_layer_backward_noalloc(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w,
+                                   const lorabwd_layer_saved* a, lorabwd_lora_state* q_state,
+                                   lorabwd_lora_state* v_state, const lorabwd_adamw* hp,
+                                   const float* d_out, float* d_hidden, float* dq_pre_out,
+                                   float* dv_out, float* gnorm_sq, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

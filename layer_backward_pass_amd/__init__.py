@@ -25,7 +25,8 @@ __all__ = [
     "lorabwd_ffn_backward", "lorabwd_lora_grad_adamw", "lorabwd_layer_backward",
     "lorabwd_attn_workspace_size", "lorabwd_ffn_workspace_size",
     "lorabwd_lora_workspace_size", "lorabwd_layer_workspace_size", "lorabwd_status_string",
-    "lorabwd_layer_backward_timed", "KernelRecord", "make_desc",
+    "lorabwd_layer_backward_timed", "lorabwd_layer_backward_noalloc", "KernelRecord",
+    "make_desc", "NOALLOC_SCRATCH_BYTES",
     "F32", "BF16", "ACT_SWIGLU", "ACT_RELU2",
 ]
 
@@ -38,7 +39,9 @@ EXPORTS = [
     "lorabwd_ffn_workspace_size", "lorabwd_ffn_backward",
     "lorabwd_lora_workspace_size", "lorabwd_lora_grad_adamw",
     "lorabwd_layer_workspace_size", "lorabwd_layer_backward", "lorabwd_layer_backward_timed",
+    "lorabwd_layer_backward_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 16 << 20  # LORABWD_NOALLOC_SCRATCH_BYTES
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -116,6 +119,10 @@ _SIGS = {
                                        ctypes.POINTER(LayerSaved), ctypes.POINTER(LoraState),
                                        ctypes.POINTER(LoraState), ctypes.POINTER(AdamW), c_vp,
                                        c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "lorabwd_layer_backward_noalloc": (c_int, [
+        ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), ctypes.POINTER(LayerSaved),
+        ctypes.POINTER(LoraState), ctypes.POINTER(LoraState), ctypes.POINTER(AdamW), c_vp, c_vp,
+        c_vp, c_vp, c_vp, c_vp]),
     "lorabwd_layer_backward_timed": (c_int, [
         ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), ctypes.POINTER(LayerSaved),
         ctypes.POINTER(LoraState), ctypes.POINTER(LoraState), ctypes.POINTER(AdamW), c_vp, c_vp,
@@ -368,9 +375,15 @@ def make_desc(seq, kv_len, hidden, ffn, n_heads, n_kv_heads, head_dim, act=ACT_S
                      head_dim ** -0.5 if attn_scale is None else attn_scale, lora_alpha)
 
 
+def lorabwd_layer_backward_noalloc(desc, weights, saved, d_hidden, **kw):
+    """lorabwd_layer_backward on the library's static per-device scratch (no
+    workspace is allocated; see include/lorabwd.h for its size limit)."""
+    return lorabwd_layer_backward(desc, weights, saved, d_hidden, noalloc=True, **kw)
+
+
 def lorabwd_layer_backward(desc, weights, saved, d_hidden, q_state=None, v_state=None,
                            adamw=None, dq_pre_out=None, dv_out=None, gnorm_sq=None,
-                           stream=None, timing=None, d_out=None):
+                           stream=None, timing=None, d_out=None, noalloc=False):
     """desc: LayerDesc; weights / saved: dicts of tensors keyed like the C
     structs; q_state / v_state: dicts with A, B, m_a, v_a, m_b, v_b (or None);
     adamw: AdamW or None.  d_hidden receives dH1; it is also the input (the
@@ -378,7 +391,10 @@ def lorabwd_layer_backward(desc, weights, saved, d_hidden, q_state=None, v_state
 
     timing: None, or (events, records) = (ctypes array of hipEvent_t,
     ctypes array of KernelRecord) to call lorabwd_layer_backward_timed; the
-    number of kernels enqueued is then returned."""
+    number of kernels enqueued is then returned.  noalloc: call
+    lorabwd_layer_backward_noalloc instead (no timing)."""
+    if noalloc and timing is not None:
+        raise ValueError("noalloc calls are not timed")
     d = desc
     tdt = _torch().bfloat16 if d.dtype == BF16 else _torch().float32
     S, L, H, I = d.seq, d.kv_len, d.hidden, d.ffn
@@ -421,15 +437,18 @@ def lorabwd_layer_backward(desc, weights, saved, d_hidden, q_state=None, v_state
     if gnorm_sq is not None:
         _f32(gnorm_sq, "gnorm_sq", (1,))
     lib = load_library()
-    need = lib.lorabwd_layer_workspace_size(ctypes.byref(d))
-    ws, wsb = _workspace(need, d_hidden.device, stream)
-    args = (ctypes.byref(d), ctypes.byref(w), ctypes.byref(a),
+    head = (ctypes.byref(d), ctypes.byref(w), ctypes.byref(a),
             ctypes.byref(qs) if qs is not None else None,
             ctypes.byref(vs) if vs is not None else None,
             ctypes.byref(adamw) if adamw is not None else None,
-            _ptr(d_out), _ptr(d_hidden), _ptr(dq_pre_out), _ptr(dv_out), _ptr(gnorm_sq),
-            _ptr(ws), wsb,
-            _stream(stream, d_hidden.device))
+            _ptr(d_out), _ptr(d_hidden), _ptr(dq_pre_out), _ptr(dv_out), _ptr(gnorm_sq))
+    if noalloc:
+        _check("lorabwd_layer_backward_noalloc", lib.lorabwd_layer_backward_noalloc(
+            *head, _stream(stream, d_hidden.device)))
+        return d_hidden
+    need = lib.lorabwd_layer_workspace_size(ctypes.byref(d))
+    ws, wsb = _workspace(need, d_hidden.device, stream)
+    args = head + (_ptr(ws), wsb, _stream(stream, d_hidden.device))
     if timing is None:
         _check("lorabwd_layer_backward", lib.lorabwd_layer_backward(*args))
         return d_hidden

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/lorabwd.h"
 #include "kernels.h"
 
@@ -757,6 +759,33 @@ hipError_t layer_run(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w
   return hipSuccess;
 }
 
+
+// Scratch of lorabwd_layer_backward_noalloc: a file-scope device array, so
+// every GPU the library runs on holds its own copy until the process ends.
+// Host code never uses the array's name as an address (on the host it is
+// only a stand-in); it takes each device's address once from
+// hipGetSymbolAddress and passes that pointer to the kernels.
+constexpr size_t kNoAllocBytes = LORABWD_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address (looked up once per device), or NULL
+// if the runtime cannot give it.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 int desc_validate(const lorabwd_layer_desc* d) {
   LBP_CHECK(d != nullptr, LORABWD_ERR_NULL);
   LBP_CHECK(dtype_ok(d->dtype), LORABWD_ERR_DTYPE);
@@ -784,11 +813,14 @@ size_t lorabwd_layer_workspace_size(const lorabwd_layer_desc* d) {
   return layer_plan(nullptr, d, 64, 64).bytes;
 }
 
-int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w,
-                           const lorabwd_layer_saved* a, lorabwd_lora_state* qs,
-                           lorabwd_lora_state* vs, const lorabwd_adamw* hp, const float* d_out,
-                           float* d_hidden, float* dq_pre_out, float* dv_out, float* gnorm_sq,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// lorabwd_layer_backward and, with noalloc, its allocation-free variant
+// (the workspace is then this device's static scratch).
+static int layer_entry(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w,
+                       const lorabwd_layer_saved* a, lorabwd_lora_state* qs,
+                       lorabwd_lora_state* vs, const lorabwd_adamw* hp, const float* d_out,
+                       float* d_hidden, float* dq_pre_out, float* dv_out, float* gnorm_sq,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream,
+                       bool noalloc) {
   int st = desc_validate(d);
   if (st != LORABWD_OK) return st;
   LBP_CHECK(w && a, LORABWD_ERR_NULL);
@@ -821,6 +853,14 @@ int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weig
                 aligned16(dv_out) && aligned16(a->attn_input) && aligned16(a->lora_q_h) &&
                 aligned16(a->lora_v_h),
             LORABWD_ERR_ALIGN);
+  if (noalloc) {
+    // the layer's workspace must fit the static scratch (nothing reads a
+    // region of it before writing it: none has to start at zero)
+    LBP_CHECK(lorabwd_layer_workspace_size(d) <= kNoAllocBytes, LORABWD_ERR_WORKSPACE);
+    workspace = device_scratch();
+    LBP_CHECK(workspace != nullptr, LORABWD_ERR_HIP);
+    workspace_bytes = kNoAllocBytes;
+  }
   const LayerPlan plan = layer_plan(workspace, d, lq ? qs->rank : 0, lv ? vs->rank : 0);
   LBP_CHECK(workspace && workspace_bytes >= lorabwd_layer_workspace_size(d),
             LORABWD_ERR_WORKSPACE);
@@ -859,6 +899,24 @@ int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weig
   if (st != LORABWD_OK) return st;
   LBP_HIP(layer_run(d, w, a, qs, vs, hp, plan, din, d_hidden, dqp, dv, gnorm_sq, stream));
   return LORABWD_OK;
+}
+
+int lorabwd_layer_backward(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w,
+                           const lorabwd_layer_saved* a, lorabwd_lora_state* qs,
+                           lorabwd_lora_state* vs, const lorabwd_adamw* hp, const float* d_out,
+                           float* d_hidden, float* dq_pre_out, float* dv_out, float* gnorm_sq,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return layer_entry(d, w, a, qs, vs, hp, d_out, d_hidden, dq_pre_out, dv_out, gnorm_sq,
+                     workspace, workspace_bytes, stream, false);
+}
+
+int lorabwd_layer_backward_noalloc(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w,
+                                   const lorabwd_layer_saved* a, lorabwd_lora_state* q_state,
+                                   lorabwd_lora_state* v_state, const lorabwd_adamw* hp,
+                                   const float* d_out, float* d_hidden, float* dq_pre_out,
+                                   float* dv_out, float* gnorm_sq, hipStream_t stream) {
+  return layer_entry(d, w, a, q_state, v_state, hp, d_out, d_hidden, dq_pre_out, dv_out, gnorm_sq,
+                     nullptr, 0, stream, true);
 }
 
 int lorabwd_layer_backward_timed(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w,

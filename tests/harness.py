@@ -87,6 +87,17 @@ SAVED = ("attn_input", "resid1", "gate", "up", "hidden_pre", "ctx", "P", "K", "V
          "lora_q_h", "lora_v_h")
 
 
+def desc_of(c):
+    """The C-ABI layer descriptor of a workload config."""
+    import layer_backward_pass_amd as lbp
+    return lbp.make_desc(c.seq, c.kv_len, c.hidden, c.ffn, c.n_heads, c.n_kv_heads,
+                         c.head_dim, act=lbp.ACT_SWIGLU if c.act == "swiglu" else lbp.ACT_RELU2,
+                         sub_norms=c.sub_norms, causal=c.causal,
+                         dtype=lbp.BF16 if c.dtype == "bf16" else lbp.F32, pos0=c.pos0,
+                         eps=c.eps, rope_base=c.rope_base, attn_scale=c.scale,
+                         lora_alpha=c.alpha)
+
+
 class DeviceLayer:
     """One layer's weights, saved activations and LoRA state on the GPU, plus
     the float64 copies the oracle reads."""
@@ -133,14 +144,7 @@ class DeviceLayer:
                 self.o_lora["v_B_" + tag] = hc(st["v_b"])
 
     def desc(self):
-        import layer_backward_pass_amd as lbp
-        c = self.cfg
-        return lbp.make_desc(c.seq, c.kv_len, c.hidden, c.ffn, c.n_heads, c.n_kv_heads,
-                             c.head_dim, act=lbp.ACT_SWIGLU if c.act == "swiglu" else lbp.ACT_RELU2,
-                             sub_norms=c.sub_norms, causal=c.causal,
-                             dtype=lbp.BF16 if c.dtype == "bf16" else lbp.F32, pos0=c.pos0,
-                             eps=c.eps, rope_base=c.rope_base, attn_scale=c.scale,
-                             lora_alpha=c.alpha)
+        return desc_of(self.cfg)
 
     def adamw(self):
         import layer_backward_pass_amd as lbp

@@ -254,6 +254,24 @@ def test_size_limits_and_kernel_limits_are_validated(lib):
                                       None, None, far(50), ws, None) == ESHAPE
 
 
+def test_noalloc_validation(lib):
+    # the allocation-free layer: a layer whose workspace exceeds the static
+    # scratch is refused with EWS before any HIP call; invalid descriptors
+    # with their usual codes
+    assert lbp.NOALLOC_SCRATCH_BYTES == 16 << 20
+    big = lbp.make_desc(512, 512, 2560, 9728, 32, 8, 128, lora_alpha=32.0)
+    assert lib.lorabwd_layer_workspace_size(ctypes.byref(big)) > lbp.NOALLOC_SCRATCH_BYTES
+    w = lbp.LayerWeights(*[far(i) for i in range(4)], far(4), None, None)
+    a = lbp.LayerSaved(*[far(10 + i) for i in range(11)])
+    r = ctypes.byref
+    f = lib.lorabwd_layer_backward_noalloc
+    assert f(r(big), r(w), r(a), None, None, None, None, far(40), None, None, None, None) == EWS
+    bad = lbp.make_desc(16, 16, 64, 256, 4, 3, 16)
+    assert f(r(bad), r(w), r(a), None, None, None, None, far(40), None, None, None, None) == ESHAPE
+    d = lbp.make_desc(16, 16, 64, 256, 4, 2, 16)
+    assert f(r(d), r(w), r(a), None, None, None, None, None, None, None, None, None) == ENULL
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(OSError):
         lbp.load_library(str(tmp_path / "missing.so"))

@@ -44,6 +44,19 @@ def rmsnorm_bwd(x, gamma, dy, eps):
     return (g - x * dot / (n * r * r)) / r
 
 
+def head_rmsnorm_bwd(x, n_heads, gamma, dy, eps):
+    """QK-norm backward: the RMSNorm backward above applied to each head's
+    head_dim slice of a [rows, n_heads*head_dim] tensor (x the norm's input,
+    the projection output), with one scale vector gamma [head_dim] for every
+    head.  The trainer's saved Q and K are "after QK-norm + RoPE" ([ENT]
+    LayerActivations), so this step sits between the inverse RoPE and the
+    LoRA Q signal."""
+    x = np.asarray(x, np.float64)
+    rows = x.shape[0]
+    dx = rmsnorm_bwd(x.reshape(rows, n_heads, -1), gamma, np.asarray(dy, np.float64).reshape(rows, n_heads, -1), eps)
+    return dx.reshape(rows, -1)
+
+
 # --------------------------------------------------------------------------
 # RoPE backward (NeoX split-half)
 # --------------------------------------------------------------------------
@@ -229,6 +242,7 @@ def layer_bwd(cfg, w, saved, d_out, lora=None):
       dCtx  = rmsnorm_bwd(ctx, gamma_asub, dCtx)   (only with sub-norms)
       dQ,dV = attention_bwd(dCtx, P, K, V)
       dQpre = rope_bwd(dQ), row i at position pos0 + i
+      (qk_norm) dQpre = head_rmsnorm_bwd(q_raw, gamma_q, dQpre)
       for (Q: dQpre, lora_q_h), (V: dV[-S:], lora_v_h):
           dA, dB = lora_grads(...); gnorm_sq += ||dA||^2 (A only)
           A <- adamw(A, dA, lr), B <- adamw(B, dB, lr_b)
@@ -254,6 +268,8 @@ def layer_bwd(cfg, w, saved, d_out, lora=None):
     rows = dq.shape[0]
     dq_pre = rope_bwd(dq, cfg.n_heads, cfg.head_dim, cfg.pos0 + np.arange(rows),
                       cfg.rope_base)
+    if getattr(cfg, "qk_norm", False):
+        dq_pre = head_rmsnorm_bwd(saved["q_raw"], cfg.n_heads, w["gamma_q"], dq_pre, cfg.eps)
     res = dict(d_hidden=dh1, dctx=dctx, dq=dq, dq_pre=dq_pre, dv=dv, gnorm_sq=0.0)
     if lora is not None:
         x_a = saved["attn_input"]

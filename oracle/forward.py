@@ -13,6 +13,10 @@ saved):
   q_pre  = x_a W_q^T + s (x_a A_q^T) B_q^T        LoRA on the Q output, s = alpha/r
   k_pre  = x_a W_k^T
   v      = x_a W_v^T + s (x_a A_v^T) B_v^T        LoRA on the V output
+  (qk_norm) q_pre, k_pre = HeadNorm(q_pre; gamma_q), HeadNorm(k_pre; gamma_k):
+                   RMSNorm over each head's head_dim features, one scale
+                   vector of head_dim shared by the heads (the trainer saves Q
+                   and K "after QK-norm + RoPE")
   q, k   = RoPE(q_pre), RoPE(k_pre)               NeoX split-half, row i at pos0+i
   P_h    = softmax(scale q_h k_g^T + causal mask) scale = 1/sqrt(D)
   ctx    = P V                                    per head
@@ -56,6 +60,15 @@ def rope(x, n_heads, head_dim, positions, base):
     out[..., :half] = lo * c - hi * s
     out[..., half:] = lo * s + hi * c
     return out.reshape(rows, n_heads * head_dim)
+
+
+def head_rmsnorm(x, n_heads, gamma, eps):
+    """RMSNorm over each head's slice of a [rows, n_heads*head_dim] tensor,
+    with one scale vector gamma [head_dim] for every head."""
+    x = np.asarray(x, np.float64)
+    rows = x.shape[0]
+    y = rmsnorm(x.reshape(rows, n_heads, -1), gamma, eps)
+    return y.reshape(rows, -1)
 
 
 def act_fwd(act, gate, up):
@@ -125,12 +138,21 @@ def layer_forward(cfg, w, x_res, x_attn=None, lora=None, q_pre=None, v_in=None):
             q_pre = q_pre + (cfg.alpha / lora["A_q"].shape[0]) * (h_q @ lora["B_q"].T)
     elif lora is not None:
         saved["lora_q_h"] = x_a @ lora["A_q"].T
-    q = rope(q_pre, Hq, D, pos, cfg.rope_base)
+    qk_norm = getattr(cfg, "qk_norm", False)
+    if qk_norm:
+        saved["q_raw"] = q_pre
+        q = rope(head_rmsnorm(q_pre, Hq, w["gamma_q"], cfg.eps), Hq, D, pos, cfg.rope_base)
+    else:
+        q = rope(q_pre, Hq, D, pos, cfg.rope_base)
     if "K_cache" in w:
         k = np.asarray(w["K_cache"], np.float64)
         v = np.asarray(w["V_cache"], np.float64) if v_in is None else v_in
     else:
-        k = rope(x_a @ w["W_k"].T, Hkv, D, pos, cfg.rope_base)
+        k_pre = x_a @ w["W_k"].T
+        if qk_norm:
+            saved["k_raw"] = k_pre
+            k_pre = head_rmsnorm(k_pre, Hkv, w["gamma_k"], cfg.eps)
+        k = rope(k_pre, Hkv, D, pos, cfg.rope_base)
         if "K_prefix" in w:
             k = np.concatenate([np.asarray(w["K_prefix"], np.float64), k])
         if v_in is None:

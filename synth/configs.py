@@ -41,6 +41,7 @@ class LayerConfig:
     weight_decay: float = 0.01
     step: int = 1
     ternary: bool = False      # weights are 0.02 * {-1, 0, +1}
+    qk_norm: bool = False      # per-head RMSNorm of the Q and K projections before RoPE
 
     @property
     def q_dim(self):

@@ -10,7 +10,7 @@ Distributions (the workload recipe):
   * layer input x, upstream gradient d_out, decode K/V cache: N(0, 1)
   * base weights, LoRA A and B: N(0, 0.02); decode weights 0.02 * t with
     t uniform on {-1, 0, +1}
-  * RMSNorm scales gamma: 1 + 0.1 * N(0, 1)
+  * RMSNorm scales gamma (also the per-head QK-norm scales): 1 + 0.1 * N(0, 1)
   * AdamW moments m, v: zero (one step from a fresh optimizer)
 """
 import numpy as np
@@ -20,6 +20,7 @@ TENSOR_IDS = {
     "W_up": 7, "W_down": 8, "gamma_attn": 9, "gamma_ffn": 10, "gamma_fsub": 11,
     "gamma_asub": 12, "A_q": 13, "B_q": 14, "A_v": 15, "B_v": 16, "K_cache": 17,
     "V_cache": 18, "m_state": 19, "v_state": 20, "K_prefix": 21, "V_prefix": 22,
+    "gamma_q": 23, "gamma_k": 24,
     # timing-only draws (stand-ins for saved activations)
     "t_attn_input": 40, "t_resid1": 41, "t_gate": 42, "t_up": 43,
     "t_hidden_pre": 44, "t_ctx": 45, "t_P": 46, "t_K": 47, "t_V": 48,
@@ -75,6 +76,9 @@ def draw_layer(cfg, layer=0):
     if cfg.sub_norms:
         d["gamma_fsub"] = gamma(cfg, layer, "gamma_fsub", I)
         d["gamma_asub"] = gamma(cfg, layer, "gamma_asub", qd)
+    if cfg.qk_norm:
+        d["gamma_q"] = gamma(cfg, layer, "gamma_q", cfg.head_dim)
+        d["gamma_k"] = gamma(cfg, layer, "gamma_k", cfg.head_dim)
     if cfg.seq == cfg.kv_len:
         d["W_k"] = _weight(cfg, layer, "W_k", (kvd, H))
         d["W_v"] = _weight(cfg, layer, "W_v", (kvd, H))

@@ -48,6 +48,10 @@ MUTATIONS = [
     ('res["gnorm_sq"] += float(np.sum(dA * dA))',
      'res["gnorm_sq"] += float(np.sum(dA * dA) + np.sum(dB * dB))'),                 # gnorm of B too
     ("dv[dv.shape[0] - rows:]", "dv[:rows]"),                                        # prefix rows
+    ('dq_pre = head_rmsnorm_bwd(saved["q_raw"], cfg.n_heads, w["gamma_q"], dq_pre, cfg.eps)',
+     'dq_pre = head_rmsnorm_bwd(saved["q_raw"], cfg.n_heads, w["gamma_k"], dq_pre, cfg.eps)'),
+    ("dx = rmsnorm_bwd(x.reshape(rows, n_heads, -1), gamma,",
+     "dx = rmsnorm_bwd(x.reshape(rows, -1, n_heads).transpose(0, 2, 1), gamma,"),     # head layout
 ]
 
 
@@ -128,6 +132,16 @@ def _checks(B):
         return float(np.sum(dd["d_out"] * o))
     out.append(fd.rel_err(rd["dq_pre"], fd.grad(lambda z: Ld(q_pre=z), sd_["q_pre"])) < 1e-5)
     out.append(fd.rel_err(rd["d_hidden"], fd.grad(lambda z: Ld(x=z), dd["x"])) < 1e-5)
+    # QK-norm: FD of dQpre with respect to the Q projection output
+    cq = cfg.with_(qk_norm=True, pos0=5)
+    dq_ = synth.draw_layer(cq)
+    wq, sq, lq = F.make_layer(cq, dq_)
+    rq = B.layer_bwd(cq, wq, sq, dq_["d_out"], lq)
+
+    def Lq(z):
+        o, _ = F.layer_forward(cq, wq, dq_["x"], lora=lq, q_pre=z)
+        return float(np.sum(dq_["d_out"] * o))
+    out.append(fd.rel_err(rq["dq_pre"], fd.grad(Lq, sq["q_raw"])) < 1e-5)
     # a chunk after a cached prefix: the V adapter sees the chunk's dV rows
     cp = cfg.with_(seq=5, kv_len=11, pos0=6)
     dp = synth.draw_layer(cp)

@@ -388,6 +388,42 @@ def test_layer_fd_chunk_after_cached_prefix(tiny):
         assert fd.rel_err(res["d" + k], fd.grad(Lk, lora[k], rel_step=1e-5)) < 1e-5, k
 
 
+def test_layer_fd_qk_norm(tiny):
+    # QK-norm (per-head RMSNorm of the Q and K projections before RoPE, one
+    # head_dim scale vector): finite differences of the forward with respect
+    # to the Q projection output (before the norm) and the Q adapter, at late
+    # positions and with GQA 4:2
+    cfg = tiny.with_(qk_norm=True, pos0=37)
+    d, w, saved, lora, res, L = _layer_fd(cfg)
+    assert "q_raw" in saved and "k_raw" in saved
+    num = fd.grad(lambda z: L(q_pre=z, lora=lora), saved["q_raw"])
+    assert fd.rel_err(res["dq_pre"], num) < 1e-5
+    for k in ("A_q", "B_q"):
+        def Lk(z, k=k):
+            l2 = dict(lora)
+            l2[k] = z
+            return L(lora=l2)
+        assert fd.rel_err(res["d" + k], fd.grad(Lk, lora[k], rel_step=1e-5)) < 1e-5, k
+    # and it differs from the layer without the norm (the step is not a no-op)
+    res0 = B.layer_bwd(cfg.with_(qk_norm=False), w, saved, d["d_out"], lora)
+    assert fd.rel_err(res0["dq_pre"], res["dq_pre"]) > 1e-2
+
+
+def test_head_rmsnorm_bwd_per_head_loops():
+    # the per-head norm backward equals the row norm backward on each head's
+    # slice separately, with the shared scale vector
+    r = rng(41)
+    x = r.standard_normal((3, 4 * 6))
+    dy = r.standard_normal(x.shape)
+    g = 1 + 0.1 * r.standard_normal(6)
+    dx = B.head_rmsnorm_bwd(x, 4, g, dy, 1e-6)
+    for i in range(3):
+        for h in range(4):
+            sl = slice(6 * h, 6 * h + 6)
+            np.testing.assert_allclose(dx[i, sl], B.rmsnorm_bwd(x[i, sl], g, dy[i, sl], 1e-6),
+                                       rtol=1e-14, atol=1e-15)
+
+
 def test_layer_fd_decode_like_relu2_subnorms():
     # the decode layer at a tiny size: one token at the last of 12 cache slots,
     # ReLU^2 x up FFN, both sub-norms, ternary weights, no adapters

@@ -200,6 +200,14 @@ int lorabwd_lora_grad_adamw(int64_t rows, int64_t in_dim, int64_t out_dim, int64
  * lorabwd_attn_backward, lorabwd_rope_backward (positions pos0 + i), then
  * the LoRA Q and V updates of [ENT] backward_through_layers.
  *
+ * With qk_norm = 1 the Q projection output went through a per-head RMSNorm
+ * (one scale vector gamma_q of head_dim for every head) before RoPE, as the
+ * trainer's saved Q is "after QK-norm + RoPE" ([ENT] LayerActivations): the
+ * inverse RoPE is followed by that norm's backward on each head's slice,
+ * from the saved projection output q_raw, and the LoRA Q signal is the
+ * gradient of q_raw.  (On its own this step is lorabwd_rmsnorm_backward
+ * with rows = seq * n_heads and n = head_dim.)
+ *
  * The gradient handed to the layer below is the residual-stream gradient
  * dH1 (the attention branch input is not differentiated).
  * ---------------------------------------------------------------------- */
@@ -220,6 +228,8 @@ typedef struct lorabwd_layer_desc {
   float rope_base;
   float attn_scale;    /* usually 1/sqrt(head_dim) */
   float lora_alpha;    /* adapter scaling is lora_alpha / rank */
+  int32_t qk_norm;     /* 1: per-head RMSNorm of the Q projection before RoPE (gamma_q, q_raw) */
+  int32_t reserved;    /* must be 0 */
 } lorabwd_layer_desc;
 
 typedef struct lorabwd_layer_weights {
@@ -230,6 +240,7 @@ typedef struct lorabwd_layer_weights {
   const float* gamma_ffn;   /* [hidden] */
   const float* gamma_fsub;  /* [ffn]; sub_norms only */
   const float* gamma_asub;  /* [n_heads*head_dim]; sub_norms only */
+  const float* gamma_q;     /* [head_dim]; qk_norm only */
 } lorabwd_layer_weights;
 
 typedef struct lorabwd_layer_saved {   /* all act type */
@@ -244,6 +255,7 @@ typedef struct lorabwd_layer_saved {   /* all act type */
   const void* V;           /* [kv_len, n_kv_heads*head_dim] */
   const void* lora_q_h;    /* [seq, rank_q]   attn_input A_q^T */
   const void* lora_v_h;    /* [seq, rank_v]   attn_input A_v^T */
+  const void* q_raw;       /* [seq, n_heads*head_dim]  Q projection output before QK-norm; qk_norm only */
 } lorabwd_layer_saved;
 
 typedef struct lorabwd_lora_state {

@@ -66,18 +66,19 @@ class LayerDesc(ctypes.Structure):
                 ("n_heads", c_i64), ("n_kv_heads", c_i64), ("head_dim", c_i64), ("pos0", c_i64),
                 ("act", ctypes.c_int32), ("sub_norms", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32), ("eps", c_float),
-                ("rope_base", c_float), ("attn_scale", c_float), ("lora_alpha", c_float)]
+                ("rope_base", c_float), ("attn_scale", c_float), ("lora_alpha", c_float),
+                ("qk_norm", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
     _fields_ = [("w_o", c_vp), ("w_gate", c_vp), ("w_up", c_vp), ("w_down", c_vp),
-                ("gamma_ffn", c_vp), ("gamma_fsub", c_vp), ("gamma_asub", c_vp)]
+                ("gamma_ffn", c_vp), ("gamma_fsub", c_vp), ("gamma_asub", c_vp), ("gamma_q", c_vp)]
 
 
 class LayerSaved(ctypes.Structure):
     _fields_ = [("attn_input", c_vp), ("resid1", c_vp), ("gate", c_vp), ("up", c_vp),
                 ("hidden_pre", c_vp), ("ctx", c_vp), ("P", c_vp), ("K", c_vp), ("V", c_vp),
-                ("lora_q_h", c_vp), ("lora_v_h", c_vp)]
+                ("lora_q_h", c_vp), ("lora_v_h", c_vp), ("q_raw", c_vp)]
 
 
 class KernelRecord(ctypes.Structure):
@@ -369,10 +370,11 @@ def lorabwd_layer_workspace_size(desc):
 
 def make_desc(seq, kv_len, hidden, ffn, n_heads, n_kv_heads, head_dim, act=ACT_SWIGLU,
               sub_norms=False, causal=True, dtype=F32, pos0=0, eps=1e-6, rope_base=10000.0,
-              attn_scale=None, lora_alpha=0.0):
+              attn_scale=None, lora_alpha=0.0, qk_norm=False):
     return LayerDesc(seq, kv_len, hidden, ffn, n_heads, n_kv_heads, head_dim, pos0, act,
                      int(sub_norms), int(causal), dtype, eps, rope_base,
-                     head_dim ** -0.5 if attn_scale is None else attn_scale, lora_alpha)
+                     head_dim ** -0.5 if attn_scale is None else attn_scale, lora_alpha,
+                     int(qk_norm), 0)
 
 
 def lorabwd_layer_backward_noalloc(desc, weights, saved, d_hidden, **kw):
@@ -409,9 +411,11 @@ def lorabwd_layer_backward(desc, weights, saved, d_hidden, q_state=None, v_state
     if d.sub_norms:
         _f32(weights["gamma_fsub"], "gamma_fsub", (I,))
         _f32(weights["gamma_asub"], "gamma_asub", (qd,))
+    if d.qk_norm:
+        _f32(weights["gamma_q"], "gamma_q", (d.head_dim,))
     sshapes = {"attn_input": (S, H), "resid1": (S, H), "gate": (S, I), "up": (S, I),
                "hidden_pre": (S, I), "ctx": (S, qd), "P": (d.n_heads, S, L), "K": (L, kvd),
-               "V": (L, kvd)}
+               "V": (L, kvd), "q_raw": (S, qd)}
     for k, s in sshapes.items():
         if saved.get(k) is not None:
             _need(saved[k], k, tdt, s)

@@ -369,7 +369,7 @@ const char* lorabwd_status_string(int status) {
   }
 }
 
-int lorabwd_abi_version(void) { return 2; }
+int lorabwd_abi_version(void) { return 3; }
 
 int lorabwd_rmsnorm_backward(int64_t rows, int64_t n, const void* x, const float* gamma,
                              const float* dy, float* dx, float eps, int accumulate, int dtype,
@@ -685,8 +685,15 @@ hipError_t layer_run(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w
   const float lr_a = hp ? hp->lr_a : 0.f, lr_b = hp ? hp->lr_b : 0.f;
   const int step = hp ? hp->step : 1;
   hipError_t e;
+  // QK-norm: the per-head RMSNorm backward after the inverse RoPE
+  const RopeNormArgs qkn = d->qk_norm ? RopeNormArgs{a->q_raw, dt == BF16 ? 1 : 0, w->gamma_q, d->eps}
+                                      : RopeNormArgs{nullptr, 0, nullptr, 0.f};
   if (use_decode_chain(d)) {
     LBP_E(decode_chain(d, w, a, plan, din, d_hidden, dqp, dv, stream));
+    // the single-token attention applies the inverse RoPE as it stores dq;
+    // the norm backward runs on each head's row (rows = heads, n = head_dim)
+    if (d->qk_norm)
+      LBP_E(launch_rmsnorm_bwd(S * Hq, D, a->q_raw, dt, w->gamma_q, dqp, dqp, d->eps, 0, stream));
   } else {
     // FFN half, residual-stream gradient: d_hidden <- dH1
     LBP_E(ffn_run(S, H, I, d->act, din, w->w_down, w->w_gate, w->w_up, a->gate, a->up,
@@ -730,13 +737,13 @@ hipError_t layer_run(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w
     // the inverse RoPE (which also adds a split dq's second key half) runs in
     // the attention's last launch where it can, else on its own
     const float* dq2 = nullptr;
-    const RopeArgs rope{dqp, d->pos0, d->rope_base};
+    const RopeArgs rope{dqp, d->pos0, d->rope_base, qkn};
     bool rope_done = false;
     LBP_E(launch_attn_bwd(S, L, Hq, Hkv, D, plan.dctx, a->P, a->K, a->V, a->ctx, dt, plan.dq, dv,
                             d->attn_scale, d->causal, plan.scratch, stream, &dq2, &rope, &rope_done,
                             dct_ready));
     if (!rope_done)
-      LBP_E(launch_rope_bwd(S, Hq, D, plan.dq, dqp, d->pos0, d->rope_base, stream, dq2));
+      LBP_E(launch_rope_bwd(S, Hq, D, plan.dq, dqp, d->pos0, d->rope_base, stream, dq2, &qkn));
   }
   if (lq || lv) {
     // both adapters' gradient + AdamW passes in the same launches; the
@@ -795,7 +802,8 @@ int desc_validate(const lorabwd_layer_desc* d) {
                 heads_ok(d->n_heads, d->n_kv_heads, d->head_dim) && d->pos0 >= 0 &&
                 d->pos0 <= (int64_t(1) << 40),
             LORABWD_ERR_SHAPE);
-  LBP_CHECK((d->sub_norms == 0 || d->sub_norms == 1) && (d->causal == 0 || d->causal == 1),
+  LBP_CHECK((d->sub_norms == 0 || d->sub_norms == 1) && (d->causal == 0 || d->causal == 1) &&
+                (d->qk_norm == 0 || d->qk_norm == 1) && d->reserved == 0,
             LORABWD_ERR_ARG);
   LBP_CHECK(finite(d->eps) && d->eps >= 0.f && finite(d->rope_base) && d->rope_base > 0.f &&
                 finite(d->attn_scale) && finite(d->lora_alpha),
@@ -839,6 +847,7 @@ static int layer_entry(const lorabwd_layer_desc* d, const lorabwd_layer_weights*
   if (lq) LBP_CHECK(a->lora_q_h != nullptr, LORABWD_ERR_NULL);
   if (lv) LBP_CHECK(a->lora_v_h != nullptr, LORABWD_ERR_NULL);
   if (sub) LBP_CHECK(w->gamma_fsub && w->gamma_asub && a->hidden_pre && a->ctx, LORABWD_ERR_NULL);
+  if (d->qk_norm) LBP_CHECK(w->gamma_q && a->q_raw, LORABWD_ERR_NULL);
   if (S == 0) return LORABWD_OK;
   LBP_CHECK(d_hidden && w->w_o, LORABWD_ERR_NULL);
   const float* din = d_out ? d_out : d_hidden;
@@ -849,7 +858,8 @@ static int layer_entry(const lorabwd_layer_desc* d, const lorabwd_layer_weights*
                     sub ? a->hidden_pre : nullptr, sub ? w->gamma_fsub : nullptr, a->resid1,
                     w->gamma_ffn, d_hidden, d->eps, dt);
   if (st != LORABWD_OK) return st;
-  LBP_CHECK(aligned16(w->w_o) && aligned16(w->gamma_asub) && aligned16(dq_pre_out) &&
+  LBP_CHECK(aligned16(w->w_o) && aligned16(w->gamma_asub) && aligned16(w->gamma_q) &&
+                aligned16(a->q_raw) && aligned16(dq_pre_out) &&
                 aligned16(dv_out) && aligned16(a->attn_input) && aligned16(a->lora_q_h) &&
                 aligned16(a->lora_v_h),
             LORABWD_ERR_ALIGN);

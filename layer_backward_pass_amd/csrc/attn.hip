@@ -475,6 +475,7 @@ struct RopeRows {
   int head_dim, threads;
   int64_t pos0;
   double log2_base;
+  RopeNorm norm;
 };
 __global__ __launch_bounds__(256) void attn_dv_reduce_rope_kernel(
     int64_t s_q, int64_t s_kv, int64_t ldk, int cmax, int64_t cs, const float* __restrict__ part,
@@ -486,7 +487,7 @@ __global__ __launch_bounds__(256) void attn_dv_reduce_rope_kernel(
   }
   if ((int)threadIdx.x >= r.threads) return;
   rope_bwd_row((int64_t)blockIdx.x - nred, threadIdx.x, r.threads, r.n_heads, r.head_dim, r.dy,
-               r.dy2, r.dx, r.pos0, r.log2_base);
+               r.dy2, r.dx, r.pos0, r.log2_base, r.norm);
 }
 
 // The last launch of a dV with chunk partials: the reduction, with the
@@ -503,14 +504,18 @@ static hipError_t launch_dv_reduce(int64_t s_q, int64_t s_kv, int Hq, int Hkv, i
     mark("attn_dv_reduce", 0, 0, s, kvbytes * (cmax + 1));  // dV counted at the dV launch
     return hipGetLastError();
   }
+  const RopeNorm nm = rope->norm.x != nullptr
+                          ? RopeNorm{rope->norm.x, rope->norm.x_bf16, rope->norm.gamma, rope->norm.eps}
+                          : RopeNorm{nullptr, 0, nullptr, 0.f};
   const RopeRows r{dq, dq2, rope->dx, Hq, D, rope_threads(Hq, D), rope->pos0,
-                   log2((double)rope->base)};
+                   log2((double)rope->base), nm};
   attn_dv_reduce_rope_kernel<<<dim3((unsigned)(nred + s_q)), 256, 0, s>>>(
       s_q, s_kv, ldk, cmax, cs, part, dv, causal, Hq / Hkv, geo, nred, r);
   const double qe = (double)s_q * Hq * D;
   // the inverse RoPE reads dq and writes dq_pre (a split dq's second half on
   // top); dV was counted at the dV launch, its chunk partials are not
-  mark("attn_dv_reduce_rope", qe * 8, qe * 3, s, kvbytes * (cmax + 1) + (dq2 ? qe * 4 : 0.0));
+  mark("attn_dv_reduce_rope", qe * (8 + (nm.x ? (nm.x_bf16 ? 2 : 4) : 0)), qe * (nm.x ? 9 : 3), s,
+       kvbytes * (cmax + 1) + (dq2 ? qe * 4 : 0.0));
   *rope_done = true;
   return hipGetLastError();
 }

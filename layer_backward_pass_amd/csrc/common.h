@@ -188,9 +188,31 @@ __device__ __forceinline__ floatx4 mfma16x16x32bf16(ushortx8 a, ushortx8 b, floa
 // and its cosine and sine in float64 once, then rotates the (d, d + half)
 // pair of every head hg, hg + HG, ...  The angle of a late position needs
 // float64: at pos ~2e3 one float32 ulp of theta is ~1e-4 rad.
+//
+// With norm.x set (QK-norm: the rotated values are the gradient of a per-head
+// RMSNorm's output), each head's rotated slice g then goes through that
+// norm's backward, dx = (gamma g - x <gamma g, x> / (D r^2)) / r with
+// r = sqrt(mean(x^2) + eps) over the head's D features of the norm input x
+// (the saved projection output) and one scale vector gamma [D] for every
+// head.  A head's `half` threads are consecutive lanes of one wave (half
+// divides 64 and every thread of a head runs the same iterations), so its
+// two sums are a shuffle reduction within that lane group.
+struct RopeNorm {
+  const void* x;  // [rows, n_heads * head_dim] float or bf16; NULL: no norm
+  int x_bf16;
+  const float* gamma;  // [head_dim]
+  float eps;
+};
+
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int m = width >> 1; m > 0; m >>= 1) v += __shfl_xor(v, m, width);
+  return v;
+}
+
 __device__ __forceinline__ void rope_bwd_row(int64_t row, int tid, int nthr, int64_t n_heads,
                                              int head_dim, const float* dy, const float* dy2,
-                                             float* dx, int64_t pos0, double log2_base) {
+                                             float* dx, int64_t pos0, double log2_base,
+                                             const RopeNorm& nm = RopeNorm{nullptr, 0, nullptr, 0.f}) {
   const int half = head_dim >> 1;
   const int d = tid % half;
   const int hg = tid / half;
@@ -201,6 +223,8 @@ __device__ __forceinline__ void rope_bwd_row(int64_t row, int tid, int nthr, int
   sincos(pos * inv_freq, &sn, &cs);
   const float c = (float)cs, s = (float)sn;
   const int64_t base = row * n_heads * head_dim;
+  const bool norm = nm.x != nullptr;
+  const float g_lo = norm ? nm.gamma[d] : 0.f, g_hi = norm ? nm.gamma[d + half] : 0.f;
   for (int64_t h = hg; h < n_heads; h += HG) {
     const int64_t i = base + h * head_dim + d;
     float lo = dy[i], hi = dy[i + half];
@@ -208,8 +232,30 @@ __device__ __forceinline__ void rope_bwd_row(int64_t row, int tid, int nthr, int
       lo += dy2[i];
       hi += dy2[i + half];
     }
-    dx[i] = lo * c + hi * s;
-    dx[i + half] = -lo * s + hi * c;
+    float o_lo = lo * c + hi * s;
+    float o_hi = -lo * s + hi * c;
+    if (norm) {
+      float x_lo, x_hi;
+      if (nm.x_bf16) {
+        const uint16_t* xb = (const uint16_t*)nm.x;
+        x_lo = bf2f(xb[i]);
+        x_hi = bf2f(xb[i + half]);
+      } else {
+        const float* xf = (const float*)nm.x;
+        x_lo = xf[i];
+        x_hi = xf[i + half];
+      }
+      const float gl = g_lo * o_lo, gh = g_hi * o_hi;
+      const float sxx = group_sum(x_lo * x_lo + x_hi * x_hi, half);
+      const float sgx = group_sum(gl * x_lo + gh * x_hi, half);
+      const float r2 = sxx / (float)head_dim + nm.eps;
+      const float inv_r = 1.0f / sqrtf(r2);
+      const float k = sgx / ((float)head_dim * r2);
+      o_lo = (gl - x_lo * k) * inv_r;
+      o_hi = (gh - x_hi * k) * inv_r;
+    }
+    dx[i] = o_lo;
+    dx[i + half] = o_hi;
   }
 }
 

@@ -40,10 +40,20 @@ hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, c
                               const float* dy, float* dx, float eps, int accumulate,
                               hipStream_t s, int nparts = 1, int64_t pstride = 0,
                               const float* rin = nullptr, uint16_t* dx16 = nullptr);
-// dy2 (may be NULL): a second term added to dy before the rotation
+// The per-head RMSNorm backward that may follow the inverse RoPE (QK-norm):
+// x [rows, n_heads * head_dim] (float, or bf16 when x_bf16), gamma
+// [head_dim]; x NULL means no norm.
+struct RopeNormArgs {
+  const void* x;
+  int x_bf16;
+  const float* gamma;
+  float eps;
+};
+// dy2 (may be NULL): a second term added to dy before the rotation; norm
+// (may be NULL or have x NULL): the QK-norm backward after it
 hipError_t launch_rope_bwd(int64_t rows, int64_t n_heads, int64_t head_dim, const float* dy,
                            float* dx, int64_t pos0, float base, hipStream_t s,
-                           const float* dy2 = nullptr);
+                           const float* dy2 = nullptr, const RopeNormArgs* norm = nullptr);
 // threads of a row of the inverse RoPE: (pair, head group), at most 256
 inline int rope_threads(int64_t n_heads, int64_t head_dim) {
   const int half = (int)head_dim / 2;
@@ -57,6 +67,7 @@ struct RopeArgs {
   float* dx;
   int64_t pos0;
   float base;
+  RopeNormArgs norm;
 };
 // dgu[r, 0:I] = dGate, dgu[r, I:2I] = dUp; out_dt selects float or bf16 output;
 // dhid may be `nparts` split-K partial sums (stride pstride), added in order.

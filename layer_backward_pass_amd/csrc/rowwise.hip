@@ -225,20 +225,25 @@ hipError_t launch_rmsnorm_bwd(int64_t rows, int64_t n, const void* x, int xdt, c
 __global__ __launch_bounds__(256) void rope_bwd_kernel(int64_t n_heads, int head_dim,
                                                        const float* dy, const float* dy2,
                                                        float* dx, int64_t pos0,
-                                                       double log2_base) {
+                                                       double log2_base, RopeNorm nm) {
   rope_bwd_row(blockIdx.x, threadIdx.x, blockDim.x, n_heads, head_dim, dy, dy2, dx, pos0,
-               log2_base);
+               log2_base, nm);
 }
 
 hipError_t launch_rope_bwd(int64_t rows, int64_t n_heads, int64_t head_dim, const float* dy,
-                           float* dx, int64_t pos0, float base, hipStream_t s, const float* dy2) {
+                           float* dx, int64_t pos0, float base, hipStream_t s, const float* dy2,
+                           const RopeNormArgs* norm) {
   if (rows == 0) return hipSuccess;
   if (dry_run()) return hipSuccess;
   const int threads = rope_threads(n_heads, head_dim);
+  const RopeNorm nm = norm != nullptr && norm->x != nullptr
+                          ? RopeNorm{norm->x, norm->x_bf16, norm->gamma, norm->eps}
+                          : RopeNorm{nullptr, 0, nullptr, 0.f};
   rope_bwd_kernel<<<dim3((unsigned)rows), dim3(threads), 0, s>>>(n_heads, (int)head_dim, dy, dy2,
-                                                                   dx, pos0, log2((double)base));
-  mark("rope_bwd", (double)rows * n_heads * head_dim * 8, (double)rows * n_heads * head_dim * 3,
-       s, dy2 ? (double)rows * n_heads * head_dim * 4 : 0.0);
+                                                                   dx, pos0, log2((double)base), nm);
+  const double qe = (double)rows * n_heads * head_dim;
+  mark("rope_bwd", qe * (8 + (nm.x ? (nm.x_bf16 ? 2 : 4) : 0)), qe * (nm.x ? 9 : 3), s,
+       dy2 ? qe * 4 : 0.0);
   return hipGetLastError();
 }
 

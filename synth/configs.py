@@ -8,6 +8,8 @@ Five workloads, named by what they are:
               LoRA r16 on Q and V
   seq2048bf16 the seq512 layer at 2048 tokens with bf16 activations/weights
   stack36     36 seq512-shaped layers at 1024 tokens, fp32
+  seq512qk    the seq512 layer with QK-norm (per-head RMSNorm of Q and K before
+              RoPE, as Qwen3-style layers have)
 """
 from dataclasses import dataclass, replace
 
@@ -78,8 +80,9 @@ SEQ512 = LayerConfig("seq512", 2, seq=512, kv_len=512, hidden=2560, ffn=9728,
 SEQ2048BF16 = SEQ512.with_(name="seq2048bf16", index=3, seq=2048, kv_len=2048,
                            dtype="bf16")
 STACK36 = SEQ512.with_(name="stack36", index=4, seq=1024, kv_len=1024, n_layers=36)
+SEQ512QK = SEQ512.with_(name="seq512qk", index=5, qk_norm=True)
 
-CONFIGS = {c.name: c for c in (TINY, DECODE, SEQ512, SEQ2048BF16, STACK36)}
+CONFIGS = {c.name: c for c in (TINY, DECODE, SEQ512, SEQ2048BF16, STACK36, SEQ512QK)}
 
 
 def get_config(name):

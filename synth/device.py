@@ -48,6 +48,9 @@ def draw_timing_layer_device(cfg, layer=0, device="cuda:0"):
         "lora": None,
     }
     del P
+    if cfg.qk_norm:
+        d["weights"]["gamma_q"] = 1 + n((cfg.head_dim,), 0.1, f32)
+        d["saved"]["q_raw"] = n((S, qd))
     if cfg.sub_norms:
         d["weights"]["gamma_fsub"] = 1 + n((I,), 0.1, f32)
         d["weights"]["gamma_asub"] = 1 + n((qd,), 0.1, f32)

@@ -84,7 +84,7 @@ def f32_scalars(cfg):
 
 WEIGHTS = ("W_o", "W_gate", "W_up", "W_down")
 SAVED = ("attn_input", "resid1", "gate", "up", "hidden_pre", "ctx", "P", "K", "V",
-         "lora_q_h", "lora_v_h")
+         "lora_q_h", "lora_v_h", "q_raw")
 
 
 def desc_of(c):
@@ -95,7 +95,7 @@ def desc_of(c):
                          sub_norms=c.sub_norms, causal=c.causal,
                          dtype=lbp.BF16 if c.dtype == "bf16" else lbp.F32, pos0=c.pos0,
                          eps=c.eps, rope_base=c.rope_base, attn_scale=c.scale,
-                         lora_alpha=c.alpha)
+                         lora_alpha=c.alpha, qk_norm=c.qk_norm)
 
 
 class DeviceLayer:
@@ -110,7 +110,7 @@ class DeviceLayer:
         dt = tdtype(cfg)
         f32 = torch.float32
         self.w = {k.lower(): dev(w[k], dt, device) for k in WEIGHTS}
-        for k in ("gamma_ffn", "gamma_fsub", "gamma_asub"):
+        for k in ("gamma_ffn", "gamma_fsub", "gamma_asub", "gamma_q"):
             if k in w:
                 self.w[k] = dev(w[k], f32, device)
         self.saved = {k: dev(saved[k], dt, device) for k in SAVED if k in saved}

@@ -293,6 +293,17 @@ def test_lora_adamw(rows, H, out, rank, step, dt):
     # kernels' LDS: the general composition with one query row
     ("decode", {"hidden": 128, "ffn": 256, "n_heads": 4, "n_kv_heads": 2, "head_dim": 32,
                 "kv_len": 16400, "pos0": 16399}),
+    # QK-norm: the per-head norm backward after the inverse RoPE, fused into
+    # the standalone RoPE launch (tiny, bf16), into the launch that adds the
+    # dV chunk partials (fp32 sequence), and after the single-token attention
+    ("tiny", {"qk_norm": True, "pos0": 9}),
+    ("seq512", {"seq": 100, "kv_len": 100, "hidden": 256, "ffn": 512, "n_heads": 8,
+                "n_kv_heads": 2, "head_dim": 128, "rank": 8, "alpha": 16.0, "qk_norm": True}),
+    ("seq512", {"seq": 96, "kv_len": 96, "hidden": 256, "ffn": 512, "n_heads": 8,
+                "n_kv_heads": 2, "head_dim": 64, "rank": 8, "alpha": 16.0, "dtype": "bf16",
+                "qk_norm": True, "pos0": 700}),
+    ("decode", {"hidden": 256, "ffn": 512, "n_heads": 8, "n_kv_heads": 2, "head_dim": 64,
+                "kv_len": 130, "pos0": 129, "qk_norm": True}),
 ])
 def test_layer_small(name, over):
     cfg = synth.get_config(name).with_(**over)

@@ -135,15 +135,19 @@ def softmax_bwd(P, dA):
     return P * (dA - delta)
 
 
-def attention_bwd(dctx, P, K, V, n_heads, n_kv_heads, scale, return_parts=False):
+def attention_bwd(dctx, P, K, V, n_heads, n_kv_heads, scale, return_parts=False, Q=None):
     """Attention backward from saved softmax weights, per query head h with
     KV head g = h // (n_heads // n_kv_heads):
       apply backward  dA  = dCtx_h @ V_g^T        [ATTN] "Attention Apply Backward"
       softmax bwd     dS  = softmax_bwd(P_h, dA)  [ATTN] "Softmax Backward"
       score bwd (Q)   dQ_h = scale * dS @ K_g     [ATTN] "Attention Score Backward"
       value grad      dV_g += P_h^T @ dCtx_h      [ENT] attention backward, grad_v
-    dctx [s_q, Hq*D]; P [Hq, s_q, s_kv]; K, V [s_kv, Hkv*D] (K post-RoPE).
-    Returns dQ [s_q, Hq*D] (post-RoPE domain) and dV [s_kv, Hkv*D]."""
+      score bwd (K)   dK_g += scale * dS^T @ Q_h  (scores = scale Q K^T, the
+                      same product rule as dQ; only with Q given)
+    dctx [s_q, Hq*D]; P [Hq, s_q, s_kv]; K, V [s_kv, Hkv*D] (K post-RoPE);
+    Q [s_q, Hq*D] post-RoPE or None.
+    Returns dQ [s_q, Hq*D] (post-RoPE domain) and dV [s_kv, Hkv*D], and dK
+    [s_kv, Hkv*D] (post-RoPE domain) last when Q is given."""
     dctx = np.asarray(dctx, np.float64)
     P = np.asarray(P, np.float64)
     K = np.asarray(K, np.float64)
@@ -154,6 +158,7 @@ def attention_bwd(dctx, P, K, V, n_heads, n_kv_heads, scale, return_parts=False)
     grp = n_heads // n_kv_heads
     dQ = np.zeros((s_q, n_heads * D))
     dV = np.zeros((s_kv, n_kv_heads * D))
+    dK = None if Q is None else np.zeros((s_kv, n_kv_heads * D))
     parts = []
     for h in range(n_heads):
         g = h // grp
@@ -164,11 +169,14 @@ def attention_bwd(dctx, P, K, V, n_heads, n_kv_heads, scale, return_parts=False)
         dS = softmax_bwd(P[h], dA)
         dQ[:, h * D:(h + 1) * D] = scale * (dS @ Kg)
         dV[:, g * D:(g + 1) * D] += P[h].T @ dC
+        if dK is not None:
+            dK[:, g * D:(g + 1) * D] += scale * (dS.T @ np.asarray(Q, np.float64)[:, h * D:(h + 1) * D])
         if return_parts:
             parts.append((dA, dS))
+    out = (dQ, dV) if dK is None else (dQ, dV, dK)
     if return_parts:
-        return dQ, dV, parts
-    return dQ, dV
+        return out + (parts,)
+    return out
 
 
 # --------------------------------------------------------------------------
@@ -263,14 +271,18 @@ def layer_bwd(cfg, w, saved, d_out, lora=None):
     dctx = dh1 @ np.asarray(w["W_o"], np.float64)
     if sub:
         dctx = rmsnorm_bwd(saved["ctx"], w["gamma_asub"], dctx, cfg.eps)
-    dq, dv = attention_bwd(dctx, saved["P"], saved["K"], saved["V"],
-                           cfg.n_heads, cfg.n_kv_heads, cfg.scale)
+    input_grad = getattr(cfg, "input_grad", False)
+    r_att = attention_bwd(dctx, saved["P"], saved["K"], saved["V"], cfg.n_heads,
+                          cfg.n_kv_heads, cfg.scale, Q=saved["q"] if input_grad else None)
+    dq, dv = r_att[0], r_att[1]
     rows = dq.shape[0]
     dq_pre = rope_bwd(dq, cfg.n_heads, cfg.head_dim, cfg.pos0 + np.arange(rows),
                       cfg.rope_base)
     if getattr(cfg, "qk_norm", False):
         dq_pre = head_rmsnorm_bwd(saved["q_raw"], cfg.n_heads, w["gamma_q"], dq_pre, cfg.eps)
     res = dict(d_hidden=dh1, dctx=dctx, dq=dq, dq_pre=dq_pre, dv=dv, gnorm_sq=0.0)
+    if input_grad:
+        res.update(attn_input_bwd(cfg, w, saved, dh1, dq_pre, r_att[2], dv, lora))
     if lora is not None:
         x_a = saved["attn_input"]
         for tag, dy, h in (("q", dq_pre, saved["lora_q_h"]),
@@ -289,6 +301,42 @@ def layer_bwd(cfg, w, saved, d_out, lora=None):
                         "A_" + tag: nA, "m_A_" + tag: mA, "v_A_" + tag: vA,
                         "B_" + tag: nB, "m_B_" + tag: mB, "v_B_" + tag: vB})
     return res
+
+
+def attn_input_bwd(cfg, w, saved, dh1, dq_pre, dk, dv, lora=None):
+    """The attention branch's input gradient (no stop-gradient at the
+    attention input), added to the residual-stream gradient dH1:
+      dKpre = rope_bwd(dK), key row j at position pos0 - (kv_len - S) + j
+      (qk_norm) dKpre = head_rmsnorm_bwd(k_raw, gamma_k, dKpre)
+      dXa   = dQpre W_q + dKpre W_k + dV W_v       (the chunk's own S key and
+              value rows; a cached prefix's rows are held fixed)
+              + s (dQpre B_q) A_q + s (dV B_v) A_v  (adapters, before the update)
+      dX    = dH1 + rmsnorm_bwd(x, gamma_attn, dXa)
+    This is the gradient of the layer with respect to its input x through
+    both the residual stream and the attention branch.  [ATTN] "Gradient
+    Flow" stops at dQpre and [ENT] backward_through_layers passes only the
+    residual-stream gradient down; this step completes the chain rule
+    through the projections and the attention norm that both omit."""
+    if "K_cache" in w:
+        raise ValueError("the attention input gradient needs the K and V projections (a cache "
+                         "drawn whole has no dependence on the layer input)")
+    S = dh1.shape[0]
+    L = dk.shape[0]
+    Hkv, D = cfg.n_kv_heads, cfg.head_dim
+    kpos = cfg.pos0 - (L - S) + np.arange(L)
+    dk_pre = rope_bwd(dk, Hkv, D, kpos, cfg.rope_base)
+    dk_cur = dk_pre[L - S:]
+    if getattr(cfg, "qk_norm", False):
+        dk_cur = head_rmsnorm_bwd(saved["k_raw"], Hkv, w["gamma_k"], dk_cur, cfg.eps)
+    dv_cur = np.asarray(dv, np.float64)[L - S:]
+    dxa = (dq_pre @ np.asarray(w["W_q"], np.float64) + dk_cur @ np.asarray(w["W_k"], np.float64)
+           + dv_cur @ np.asarray(w["W_v"], np.float64))
+    if lora is not None:
+        for tag, dy in (("q", dq_pre), ("v", dv_cur)):
+            A, Bm = np.asarray(lora["A_" + tag], np.float64), np.asarray(lora["B_" + tag], np.float64)
+            dxa = dxa + (float(cfg.alpha) / A.shape[0]) * ((dy @ Bm) @ A)
+    dx = dh1 + rmsnorm_bwd(saved["x"], w["gamma_attn"], dxa, cfg.eps)
+    return dict(d_hidden=dx, dh1=dh1, dk=dk, dk_pre=dk_cur, dxa=dxa)
 
 
 def stack_bwd(cfg, layers, grad_hidden):

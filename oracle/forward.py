@@ -177,7 +177,7 @@ def layer_forward(cfg, w, x_res, x_attn=None, lora=None, q_pre=None, v_in=None):
     f = rmsnorm(hid, w["gamma_fsub"], cfg.eps) if cfg.sub_norms else hid
     out = h1 + f @ w["W_down"].T
     saved.update(q_pre=q_pre, q=q, K=k, V=v, P=P, ctx=ctx, resid1=h1,
-                 hidden_input=n2, gate=gate, up=up)
+                 hidden_input=n2, gate=gate, up=up, x=x_attn)
     if cfg.sub_norms:
         saved["hidden_pre"] = hid
     return out, saved

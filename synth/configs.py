@@ -44,6 +44,7 @@ class LayerConfig:
     step: int = 1
     ternary: bool = False      # weights are 0.02 * {-1, 0, +1}
     qk_norm: bool = False      # per-head RMSNorm of the Q and K projections before RoPE
+    input_grad: bool = False   # differentiate the attention branch input too (no stop-gradient)
 
     @property
     def q_dim(self):

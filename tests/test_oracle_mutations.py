@@ -52,6 +52,12 @@ MUTATIONS = [
      'dq_pre = head_rmsnorm_bwd(saved["q_raw"], cfg.n_heads, w["gamma_k"], dq_pre, cfg.eps)'),
     ("dx = rmsnorm_bwd(x.reshape(rows, n_heads, -1), gamma,",
      "dx = rmsnorm_bwd(x.reshape(rows, -1, n_heads).transpose(0, 2, 1), gamma,"),     # head layout
+    ("dK[:, g * D:(g + 1) * D] += scale * (dS.T @", "dK[:, g * D:(g + 1) * D] += (dS.T @"),  # scale
+    ("kpos = cfg.pos0 - (L - S) + np.arange(L)", "kpos = cfg.pos0 + np.arange(L)"),  # key positions
+    ("+ dv_cur @ np.asarray(w[\"W_v\"], np.float64))", ")"),                         # dropped dV term
+    ("dxa = dxa + (float(cfg.alpha) / A.shape[0]) * ((dy @ Bm) @ A)", "dxa = dxa"),  # adapters
+    ("dx = dh1 + rmsnorm_bwd(saved[\"x\"], w[\"gamma_attn\"], dxa, cfg.eps)",
+     "dx = dh1 + dxa"),                                                              # no norm bwd
 ]
 
 
@@ -132,6 +138,18 @@ def _checks(B):
         return float(np.sum(dd["d_out"] * o))
     out.append(fd.rel_err(rd["dq_pre"], fd.grad(lambda z: Ld(q_pre=z), sd_["q_pre"])) < 1e-5)
     out.append(fd.rel_err(rd["d_hidden"], fd.grad(lambda z: Ld(x=z), dd["x"])) < 1e-5)
+    # the input gradient without the stop-gradient: FD of the layer in x,
+    # plain and after a cached prefix with QK-norm
+    for over in ({}, {"seq": 5, "kv_len": 11, "pos0": 6, "qk_norm": True}):
+        ci = cfg.with_(input_grad=True, **over)
+        di = synth.draw_layer(ci)
+        wi, si, li = F.make_layer(ci, di)
+        ri = B.layer_bwd(ci, wi, si, di["d_out"], li)
+
+        def Li(z, ci=ci, wi=wi, li=li, di=di):
+            o, _ = F.layer_forward(ci, wi, z, lora=li)
+            return float(np.sum(di["d_out"] * o))
+        out.append(fd.rel_err(ri["d_hidden"], fd.grad(Li, di["x"])) < 1e-5)
     # QK-norm: FD of dQpre with respect to the Q projection output
     cq = cfg.with_(qk_norm=True, pos0=5)
     dq_ = synth.draw_layer(cq)

@@ -200,6 +200,10 @@ def test_attention_bwd_fd(s_q, s_kv, Hq, Hkv, D, causal):
     nv = fd.grad(lambda z: float(np.sum(dctx * F.attention(q, k, z, Hq, Hkv, D, sc, causal)[1])), v)
     assert fd.rel_err(dq, nq) < 1e-7
     assert fd.rel_err(dv, nv) < 1e-7
+    # dK from the same product rule, against finite differences in K
+    _, _, dk = B.attention_bwd(dctx, P, k, v, Hq, Hkv, sc, Q=q)
+    nk = fd.grad(lambda z: float(np.sum(dctx * F.attention(q, z, v, Hq, Hkv, D, sc, causal)[1])), k)
+    assert fd.rel_err(dk, nk) < 1e-7
 
 
 def test_attention_delta_identity_and_row_sums():
@@ -422,6 +426,29 @@ def test_head_rmsnorm_bwd_per_head_loops():
             sl = slice(6 * h, 6 * h + 6)
             np.testing.assert_allclose(dx[i, sl], B.rmsnorm_bwd(x[i, sl], g, dy[i, sl], 1e-6),
                                        rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("over", [
+    {},                                                   # GQA 4:2, SwiGLU, both adapters
+    {"qk_norm": True, "pos0": 23},                        # QK-norm on Q and K, late positions
+    {"seq": 5, "kv_len": 11, "pos0": 6},                  # a chunk after a cached prefix
+    {"n_kv_heads": 4, "causal": False, "rank": 0},        # MHA, no mask, no adapters
+])
+def test_layer_fd_input_gradient_without_stop_gradient(tiny, over):
+    # the exact gradient of the layer with respect to its input x, through
+    # the residual stream AND the attention branch (x feeds both): central
+    # differences of <dOut, out(x)> with x_attn = x
+    cfg = tiny.with_(input_grad=True, **over)
+    d = synth.draw_layer(cfg)
+    w, saved, lora = F.make_layer(cfg, d)
+    res = B.layer_bwd(cfg, w, saved, d["d_out"], lora)
+
+    def L(z):
+        out, _ = F.layer_forward(cfg, w, z, lora=lora)
+        return float(np.sum(d["d_out"] * out))
+    assert fd.rel_err(res["d_hidden"], fd.grad(L, d["x"])) < 1e-5
+    # the attention branch is not negligible: the stop-gradient answer differs
+    assert fd.rel_err(res["dh1"], res["d_hidden"]) > 1e-3
 
 
 def test_layer_fd_decode_like_relu2_subnorms():

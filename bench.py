@@ -23,6 +23,8 @@ Workloads (default: stack36):
   seq2048bf16  the seq512 layer at 2048 tokens with bf16 activations/weights
   stack36      36 seq512-shaped layers at 1024 tokens, fp32
   seq512qk     the seq512 layer with QK-norm before RoPE
+  seq512ig, seq2048bf16ig
+               those layers with the exact input gradient through attention
   tiny         hidden 64, 16 tokens (launch-bound; parity-size case)
 
 Prints ONE JSON line.  `roofline` describes the kernel with the largest
@@ -51,9 +53,10 @@ PEAK = {  # MI355X published peaks (dense)
     "f32_TFLOPs": 157.3,
     "bf16_TFLOPs": 2516.6,
 }
-COPIES = {"decode": 6, "tiny": 1, "seq512": 4, "seq2048bf16": 4, "stack36": 1, "seq512qk": 4}
+COPIES = {"decode": 6, "tiny": 1, "seq512": 4, "seq2048bf16": 4, "stack36": 1, "seq512qk": 4,
+          "seq512ig": 4, "seq2048bf16ig": 4}
 DEFAULT_STEPS = {"decode": 2000, "tiny": 2000, "seq512": 200, "seq2048bf16": 100, "stack36": 10,
-                 "seq512qk": 200}
+                 "seq512qk": 200, "seq512ig": 200, "seq2048bf16ig": 100}
 
 
 def parse():
@@ -115,7 +118,7 @@ def layer_call(lbp, cfg, d, d_hidden, **kw):
                          sub_norms=cfg.sub_norms, causal=cfg.causal,
                          dtype=lbp.BF16 if cfg.dtype == "bf16" else lbp.F32, pos0=cfg.pos0,
                          eps=cfg.eps, rope_base=cfg.rope_base, attn_scale=cfg.scale,
-                         lora_alpha=cfg.alpha, qk_norm=cfg.qk_norm)
+                         lora_alpha=cfg.alpha, qk_norm=cfg.qk_norm, input_grad=cfg.input_grad)
     lora = d["lora"]
     hp = lbp.AdamW(cfg.lr, cfg.lr_b, cfg.beta1, cfg.beta2, cfg.adam_eps, cfg.weight_decay,
                    cfg.step) if lora else None

@@ -208,8 +208,19 @@ int lorabwd_lora_grad_adamw(int64_t rows, int64_t in_dim, int64_t out_dim, int64
  * gradient of q_raw.  (On its own this step is lorabwd_rmsnorm_backward
  * with rows = seq * n_heads and n = head_dim.)
  *
- * The gradient handed to the layer below is the residual-stream gradient
- * dH1 (the attention branch input is not differentiated).
+ * With input_grad = 0 the gradient handed to the layer below is the
+ * residual-stream gradient dH1 (the attention branch input is held fixed,
+ * as [ATTN] "Gradient Flow" stops at dQpre and [ENT] passes only that
+ * gradient down).  With input_grad = 1 it is the exact gradient of the
+ * layer input x through both paths:
+ *   dK    = scale dS^T Q (post-RoPE queries q), inverse RoPE at the key
+ *           positions, (qk_norm) the per-head norm backward with gamma_k
+ *           from the saved K projection output k_raw
+ *   dXa   = dQpre W_q + dKpre W_k + dV W_v  over the chunk's own S rows
+ *           + s (dQpre B_q) A_q + s (dV B_v) A_v  (adapters before the update)
+ *   d_hidden = dH1 + rmsnorm_bwd(x, gamma_attn, dXa)
+ * (needs w_q, w_k, w_v, gamma_attn, x and q; not for bf16 with head_dim 16;
+ * one-token layers then run the general composition).
  * ---------------------------------------------------------------------- */
 typedef struct lorabwd_layer_desc {
   int64_t seq;         /* query rows S */
@@ -228,8 +239,8 @@ typedef struct lorabwd_layer_desc {
   float rope_base;
   float attn_scale;    /* usually 1/sqrt(head_dim) */
   float lora_alpha;    /* adapter scaling is lora_alpha / rank */
-  int32_t qk_norm;     /* 1: per-head RMSNorm of the Q projection before RoPE (gamma_q, q_raw) */
-  int32_t reserved;    /* must be 0 */
+  int32_t qk_norm;     /* 1: per-head RMSNorm of the Q (and K) projection before RoPE */
+  int32_t input_grad;  /* 1: differentiate the attention branch input too (see above) */
 } lorabwd_layer_desc;
 
 typedef struct lorabwd_layer_weights {
@@ -241,6 +252,11 @@ typedef struct lorabwd_layer_weights {
   const float* gamma_fsub;  /* [ffn]; sub_norms only */
   const float* gamma_asub;  /* [n_heads*head_dim]; sub_norms only */
   const float* gamma_q;     /* [head_dim]; qk_norm only */
+  const void* w_q;          /* act [n_heads*head_dim, hidden]; input_grad only */
+  const void* w_k;          /* act [n_kv_heads*head_dim, hidden]; input_grad only */
+  const void* w_v;          /* act [n_kv_heads*head_dim, hidden]; input_grad only */
+  const float* gamma_attn;  /* [hidden] the attention norm's scale; input_grad only */
+  const float* gamma_k;     /* [head_dim]; qk_norm with input_grad */
 } lorabwd_layer_weights;
 
 typedef struct lorabwd_layer_saved {   /* all act type */
@@ -256,6 +272,10 @@ typedef struct lorabwd_layer_saved {   /* all act type */
   const void* lora_q_h;    /* [seq, rank_q]   attn_input A_q^T */
   const void* lora_v_h;    /* [seq, rank_v]   attn_input A_v^T */
   const void* q_raw;       /* [seq, n_heads*head_dim]  Q projection output before QK-norm; qk_norm only */
+  const void* x;           /* [seq, hidden]   layer input (before the attention norm); input_grad only */
+  const void* q;           /* [seq, n_heads*head_dim]  Q after (QK-norm and) RoPE; input_grad only */
+  const void* k_raw;       /* [seq, n_kv_heads*head_dim]  the chunk's K projection output before
+                              QK-norm; qk_norm with input_grad */
 } lorabwd_layer_saved;
 
 typedef struct lorabwd_lora_state {

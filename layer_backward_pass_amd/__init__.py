@@ -67,18 +67,21 @@ class LayerDesc(ctypes.Structure):
                 ("act", ctypes.c_int32), ("sub_norms", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32), ("eps", c_float),
                 ("rope_base", c_float), ("attn_scale", c_float), ("lora_alpha", c_float),
-                ("qk_norm", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("qk_norm", ctypes.c_int32), ("input_grad", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
     _fields_ = [("w_o", c_vp), ("w_gate", c_vp), ("w_up", c_vp), ("w_down", c_vp),
-                ("gamma_ffn", c_vp), ("gamma_fsub", c_vp), ("gamma_asub", c_vp), ("gamma_q", c_vp)]
+                ("gamma_ffn", c_vp), ("gamma_fsub", c_vp), ("gamma_asub", c_vp), ("gamma_q", c_vp),
+                ("w_q", c_vp), ("w_k", c_vp), ("w_v", c_vp), ("gamma_attn", c_vp),
+                ("gamma_k", c_vp)]
 
 
 class LayerSaved(ctypes.Structure):
     _fields_ = [("attn_input", c_vp), ("resid1", c_vp), ("gate", c_vp), ("up", c_vp),
                 ("hidden_pre", c_vp), ("ctx", c_vp), ("P", c_vp), ("K", c_vp), ("V", c_vp),
-                ("lora_q_h", c_vp), ("lora_v_h", c_vp), ("q_raw", c_vp)]
+                ("lora_q_h", c_vp), ("lora_v_h", c_vp), ("q_raw", c_vp), ("x", c_vp), ("q", c_vp),
+                ("k_raw", c_vp)]
 
 
 class KernelRecord(ctypes.Structure):
@@ -370,11 +373,11 @@ def lorabwd_layer_workspace_size(desc):
 
 def make_desc(seq, kv_len, hidden, ffn, n_heads, n_kv_heads, head_dim, act=ACT_SWIGLU,
               sub_norms=False, causal=True, dtype=F32, pos0=0, eps=1e-6, rope_base=10000.0,
-              attn_scale=None, lora_alpha=0.0, qk_norm=False):
+              attn_scale=None, lora_alpha=0.0, qk_norm=False, input_grad=False):
     return LayerDesc(seq, kv_len, hidden, ffn, n_heads, n_kv_heads, head_dim, pos0, act,
                      int(sub_norms), int(causal), dtype, eps, rope_base,
                      head_dim ** -0.5 if attn_scale is None else attn_scale, lora_alpha,
-                     int(qk_norm), 0)
+                     int(qk_norm), int(input_grad))
 
 
 def lorabwd_layer_backward_noalloc(desc, weights, saved, d_hidden, **kw):
@@ -413,9 +416,15 @@ def lorabwd_layer_backward(desc, weights, saved, d_hidden, q_state=None, v_state
         _f32(weights["gamma_asub"], "gamma_asub", (qd,))
     if d.qk_norm:
         _f32(weights["gamma_q"], "gamma_q", (d.head_dim,))
+    if d.input_grad:
+        for k, s in (("w_q", (qd, H)), ("w_k", (kvd, H)), ("w_v", (kvd, H))):
+            _need(weights[k], k, tdt, s)
+        _f32(weights["gamma_attn"], "gamma_attn", (H,))
+        if d.qk_norm:
+            _f32(weights["gamma_k"], "gamma_k", (d.head_dim,))
     sshapes = {"attn_input": (S, H), "resid1": (S, H), "gate": (S, I), "up": (S, I),
                "hidden_pre": (S, I), "ctx": (S, qd), "P": (d.n_heads, S, L), "K": (L, kvd),
-               "V": (L, kvd), "q_raw": (S, qd)}
+               "V": (L, kvd), "q_raw": (S, qd), "x": (S, H), "q": (S, qd), "k_raw": (S, kvd)}
     for k, s in sshapes.items():
         if saved.get(k) is not None:
             _need(saved[k], k, tdt, s)

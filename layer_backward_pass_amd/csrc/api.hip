@@ -369,7 +369,7 @@ const char* lorabwd_status_string(int status) {
   }
 }
 
-int lorabwd_abi_version(void) { return 3; }
+int lorabwd_abi_version(void) { return 4; }
 
 int lorabwd_rmsnorm_backward(int64_t rows, int64_t n, const void* x, const float* gamma,
                              const float* dy, float* dx, float eps, int accumulate, int dtype,
@@ -478,6 +478,7 @@ namespace {
 
 struct LayerPlan {
   float *dctx, *dq, *dv;
+  float *dk, *dkp, *xa;  // input_grad: dK [kv_len, kvd], dKpre [seq, kvd], dXa parts [4, seq, hidden]
   uint16_t* h16;  // bf16 copy of dH1: the W_o product's operand (bf16 sequence layers)
   float *part2, *x2, *scal1, *scal2, *scal3, *dA;  // single-token chain only
   void* scratch;
@@ -490,7 +491,8 @@ bool has_lora(const lorabwd_lora_state* s) { return s != nullptr && s->rank > 0;
 // One token whose attention fits the decode kernels runs the fused GEMV
 // chain of decode.hip; everything else runs the general composition.
 bool use_decode_chain(const lorabwd_layer_desc* d) {
-  return d->seq == 1 && dec_attn_fits(d->kv_len, d->n_heads, d->n_kv_heads, d->head_dim);
+  return d->seq == 1 && !d->input_grad &&
+         dec_attn_fits(d->kv_len, d->n_heads, d->n_kv_heads, d->head_dim);
 }
 
 LayerPlan layer_plan(void* ws, const lorabwd_layer_desc* d, int64_t rq, int64_t rv) {
@@ -519,10 +521,19 @@ LayerPlan layer_plan(void* ws, const lorabwd_layer_desc* d, int64_t rq, int64_t 
       if (v > sc) sc = v;
   } else {
     if (d->dtype == BF16 && S > 1) p.h16 = c.take<uint16_t>((size_t)S * H * 2);
+    const bool ig = d->input_grad != 0;
+    if (ig) {
+      p.dk = c.take<float>((size_t)L * kvd * 4);
+      p.dkp = c.take<float>((size_t)S * kvd * 4);
+      p.xa = c.take<float>((size_t)4 * S * H * 4);
+    }
     const size_t f = ffn_plan(nullptr, S, H, I, d->dtype).bytes;
     const size_t o = S == 1 ? dgemv_part_bytes(qd, H) : gemm_partial_bytes(S, qd, H, F32, d->dtype);
-    const size_t a = up(attn_ws_bytes(S, L, d->n_heads, d->n_kv_heads, d->head_dim, d->dtype));
-    for (size_t v : {f, o, a})
+    const size_t a = up(attn_ws_bytes(S, L, d->n_heads, d->n_kv_heads, d->head_dim, d->dtype, ig));
+    // the transposed Q, K and V products of the input gradient
+    const size_t g1 = ig ? gemm_partial_bytes(S, H, qd, F32, d->dtype) : 0;
+    const size_t g2 = ig ? gemm_partial_bytes(S, H, kvd, F32, d->dtype) : 0;
+    for (size_t v : {f, o, a, g1, g2})
       if (v > sc) sc = v;
   }
   p.scratch = c.take<void>(sc);
@@ -739,11 +750,29 @@ hipError_t layer_run(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w
     const float* dq2 = nullptr;
     const RopeArgs rope{dqp, d->pos0, d->rope_base, qkn};
     bool rope_done = false;
+    const bool ig = d->input_grad != 0;
     LBP_E(launch_attn_bwd(S, L, Hq, Hkv, D, plan.dctx, a->P, a->K, a->V, a->ctx, dt, plan.dq, dv,
                             d->attn_scale, d->causal, plan.scratch, stream, &dq2, &rope, &rope_done,
-                            dct_ready));
+                            dct_ready, ig ? a->q : nullptr, ig ? plan.dk : nullptr));
     if (!rope_done)
       LBP_E(launch_rope_bwd(S, Hq, D, plan.dq, dqp, d->pos0, d->rope_base, stream, dq2, &qkn));
+    if (ig) {
+      // dKpre of the chunk's own key rows (positions pos0 ...): inverse RoPE,
+      // and with QK-norm the per-head norm backward from the saved k_raw
+      const RopeNormArgs kn = d->qk_norm
+                                  ? RopeNormArgs{a->k_raw, dt == BF16 ? 1 : 0, w->gamma_k, d->eps}
+                                  : RopeNormArgs{nullptr, 0, nullptr, 0.f};
+      LBP_E(launch_rope_bwd(S, Hkv, D, plan.dk + (L - S) * kvd, plan.dkp, d->pos0, d->rope_base,
+                            stream, nullptr, &kn));
+      // the transposed Q, K and V products, one part of dXa each
+      const int64_t SH = S * H;
+      LBP_E(launch_gemm(S, H, qd, dqp, F32, qd, w->w_q, nullptr, qd, dt, H, plan.xa, H,
+                        (float*)plan.scratch, stream));
+      LBP_E(launch_gemm(S, H, kvd, plan.dkp, F32, kvd, w->w_k, nullptr, kvd, dt, H, plan.xa + SH,
+                        H, (float*)plan.scratch, stream));
+      LBP_E(launch_gemm(S, H, kvd, dv + (L - S) * kvd, F32, kvd, w->w_v, nullptr, kvd, dt, H,
+                        plan.xa + 2 * SH, H, (float*)plan.scratch, stream));
+    }
   }
   if (lq || lv) {
     // both adapters' gradient + AdamW passes in the same launches; the
@@ -761,7 +790,14 @@ hipError_t layer_run(const lorabwd_layer_desc* d, const lorabwd_layer_weights* w
                            vs->A, vs->B, vs->m_a, vs->v_a, vs->m_b, vs->v_b, nullptr, nullptr,
                            d->lora_alpha / (float)vs->rank,
                            (char*)plan.scratch + plan.lora_v_off};
-    LBP_E(launch_lora_adamw_jobs(jobs, nj, gnorm_sq, h, stream));
+    // with input_grad the adapters' share of dXa goes to its fourth part
+    LBP_E(launch_lora_adamw_jobs(jobs, nj, gnorm_sq, h, stream,
+                                 d->input_grad ? plan.xa + 3 * S * H : nullptr));
+  }
+  if (d->input_grad) {
+    // d_hidden = dH1 + rmsnorm_bwd(x, gamma_attn, sum of the dXa parts)
+    LBP_E(launch_rmsnorm_bwd(S, H, a->x, dt, w->gamma_attn, plan.xa, d_hidden, d->eps, 1, stream,
+                             lq || lv ? 4 : 3, S * H));
   }
   return hipSuccess;
 }
@@ -803,8 +839,10 @@ int desc_validate(const lorabwd_layer_desc* d) {
                 d->pos0 <= (int64_t(1) << 40),
             LORABWD_ERR_SHAPE);
   LBP_CHECK((d->sub_norms == 0 || d->sub_norms == 1) && (d->causal == 0 || d->causal == 1) &&
-                (d->qk_norm == 0 || d->qk_norm == 1) && d->reserved == 0,
+                (d->qk_norm == 0 || d->qk_norm == 1) && (d->input_grad == 0 || d->input_grad == 1),
             LORABWD_ERR_ARG);
+  // the attention input gradient's dK is not built for bf16 with head_dim 16
+  LBP_CHECK(!d->input_grad || d->dtype != LORABWD_BF16 || d->head_dim >= 32, LORABWD_ERR_SHAPE);
   LBP_CHECK(finite(d->eps) && d->eps >= 0.f && finite(d->rope_base) && d->rope_base > 0.f &&
                 finite(d->attn_scale) && finite(d->lora_alpha),
             LORABWD_ERR_ARG);
@@ -848,6 +886,12 @@ static int layer_entry(const lorabwd_layer_desc* d, const lorabwd_layer_weights*
   if (lv) LBP_CHECK(a->lora_v_h != nullptr, LORABWD_ERR_NULL);
   if (sub) LBP_CHECK(w->gamma_fsub && w->gamma_asub && a->hidden_pre && a->ctx, LORABWD_ERR_NULL);
   if (d->qk_norm) LBP_CHECK(w->gamma_q && a->q_raw, LORABWD_ERR_NULL);
+  if (d->input_grad) {
+    LBP_CHECK(w->w_q && w->w_k && w->w_v && w->gamma_attn && a->x && a->q, LORABWD_ERR_NULL);
+    if (d->qk_norm) LBP_CHECK(w->gamma_k && a->k_raw, LORABWD_ERR_NULL);
+    const void* ps[] = {w->w_q, w->w_k, w->w_v, w->gamma_attn, w->gamma_k, a->x, a->q, a->k_raw};
+    for (const void* q : ps) LBP_CHECK(aligned16(q), LORABWD_ERR_ALIGN);
+  }
   if (S == 0) return LORABWD_OK;
   LBP_CHECK(d_hidden && w->w_o, LORABWD_ERR_NULL);
   const float* din = d_out ? d_out : d_hidden;

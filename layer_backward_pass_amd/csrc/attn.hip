@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
     int64_t s_q, int64_t s_kv, int Hq, int grp, const float* __restrict__ dctx,
     const float* __restrict__ P, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ ctx, const float* __restrict__ delta_ws, float* __restrict__ dq,
-    float* __restrict__ dq2, float scale, int causal) {
+    float* __restrict__ dq2, float scale, int causal, float* __restrict__ ds_out) {
   constexpr int KT = FQ_KT, DK = D / 4, ND = D / 16, QW = 4 / HW, LDK = D + 4;
   constexpr int NE = KT * D / 4;           // float4 per staged tile
   constexpr int SE = (NE + 255) / 256;     // per thread
@@ -226,6 +226,24 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(
           ds[nt][v] = f4at(pc[nt], v) * (a - dl);
         }
       fetch_p(k0 + KT);
+      // scale dS, stored as P is ([head][query][key]) for the dK pass; the
+      // tiles this workgroup computes cover every key a query sees
+      if (ds_out != nullptr && qok) {
+        float* dsr = ds_out + ((int64_t)h * s_q + qrow) * s_kv;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int64_t col = k0 + 16 * nt + 4 * c;
+          if (PVEC) {
+            if (col < s_kv)
+              *reinterpret_cast<float4*>(dsr + col) =
+                  make_float4(scale * ds[nt][0], scale * ds[nt][1], scale * ds[nt][2], scale * ds[nt][3]);
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (col + v < s_kv) dsr[col + v] = scale * ds[nt][v];
+          }
+        }
+      }
       // dQ += dS K with k index = key.  Column n of MFMA tile f is head dim
       // ND n + f, so a lane's K values for its ND tiles are contiguous
       // (vector LDS reads) and its dq values contiguous on store.
@@ -324,7 +342,10 @@ __device__ __forceinline__ bool dv_item(int64_t L, int Hkv, int64_t s_q, int64_t
 constexpr int FV_QT = 32;  // query rows per step, fp32 dv kernel
 constexpr DvGeo FV_GEO{DV_KT, 16, FV_QT};
 
-template <int D>
+// CMASK (causal only): read P only at keys the query sees (key <= s_kv - s_q
+// + query), 0 elsewhere; the dK pass runs this kernel on (scale dS, Q), whose
+// dS is written only where the dQ kernel computed it.
+template <int D, bool CMASK>
 __global__ __launch_bounds__(256) void attn_dv_f32_kernel(int64_t s_q, int64_t s_kv, int Hq,
                                                           int grp, int cmax, int64_t cs,
                                                           int64_t nfull,
@@ -379,7 +400,7 @@ __global__ __launch_bounds__(256) void attn_dv_f32_kernel(int64_t s_q, int64_t s
 #pragma unroll
     for (int s2 = 0; s2 < QT / 4; ++s2) {
       const int rr = 4 * s2 + c;
-      const bool ok = valid && kok && qb + rr < s_q;
+      const bool ok = valid && kok && qb + rr < s_q && (!CMASK || key <= s_kv - s_q + qb + rr);
       r.p[s2] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
           rp, ok ? (int)((rr * s_kv + 16 * w + l16) * 4) : (int)BUF_OOB, 0, 0));
     }
@@ -632,7 +653,7 @@ __device__ __forceinline__ void attn_dq_bf16_body(
     const float* __restrict__ dctx, const uint16_t* __restrict__ P,
     const uint16_t* __restrict__ Kt, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ ctx, const float* __restrict__ delta_ws, float* __restrict__ dq,
-    float scale, int causal, uint16_t* smem) {
+    float scale, int causal, uint16_t* smem, uint16_t* __restrict__ ds_out) {
   constexpr int KT = HQ_KT, NK = D / 32, ND = D / 16, QW = 4 / HW;
   constexpr int VLD = D + 8, KLD = KT + 8;
   constexpr int NCH = KT * D / 8;            // 16-byte chunks per staged matrix
@@ -817,6 +838,22 @@ __device__ __forceinline__ void attn_dq_bf16_body(
             x[j] = p * (da[s][nt][v] - dl[s]);
           }
           dsa[s][st] = pack8(x);
+          // scale dS as bf16, stored as P is ([head][query][key]) for the
+          // dK pass: keys k0 + 16c + 8st .. +7 of query qrow[s]
+          if (ds_out != nullptr && has[s] && qrow[s] < s_q && k0 < kend[s]) {
+            uint16_t* dsr = ds_out + ((int64_t)h * s_q + qrow[s]) * s_kv;
+            const int64_t kc = k0 + 16 * c + 8 * st;
+            float y[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) y[j] = scale * x[j];
+            if (PVEC) {
+              if (kc < s_kv) *reinterpret_cast<ushortx8*>(dsr + kc) = pack8(y);
+            } else {
+#pragma unroll
+              for (int j = 0; j < 8; ++j)
+                if (kc + j < s_kv) dsr[kc + j] = f2bf(y[j]);
+            }
+          }
         }
     };
     auto tile_dq = [&](auto both) {
@@ -858,10 +895,10 @@ __global__ __launch_bounds__(256, 2) void attn_dq_bf16_kernel(
     const float* __restrict__ dctx, const uint16_t* __restrict__ P,
     const uint16_t* __restrict__ Kt, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ ctx, const float* __restrict__ delta_ws, float* __restrict__ dq,
-    float scale, int causal) {
+    float scale, int causal, uint16_t* __restrict__ ds_out) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[dq_bf16_lds<D>()];
   attn_dq_bf16_body<D, HW, PVEC>(blockIdx.x, s_q, s_kv, Hq, grp, LK, npairs, dctx, P, Kt, V, ctx,
-                                 delta_ws, dq, scale, causal, smem);
+                                 delta_ws, dq, scale, causal, smem, ds_out);
 }
 
 constexpr int HV_QT = 64;   // queries per step, bf16 dv kernel
@@ -874,7 +911,9 @@ constexpr int dv_bf16_lds() {
 }
 
 // Work item blk of the bf16 dV launch, on the LDS at smem (dv_bf16_lds).
-template <int D, bool PVEC>
+// CMASK (causal only): P is read only at keys the query sees, 0 elsewhere
+// (the dK pass on scale dS, written only where the dQ kernel computed it).
+template <int D, bool PVEC, bool CMASK>
 __device__ __forceinline__ void attn_dv_bf16_body(int64_t blk, int64_t s_q, int64_t s_kv, int Hq,
                                                   int grp, int cmax, int64_t cs, int64_t nfull,
                                                   int64_t LQ, const uint16_t* __restrict__ P,
@@ -928,7 +967,13 @@ __device__ __forceinline__ void attn_dv_bf16_body(int64_t blk, int64_t s_q, int6
     for (int i = 0; i < NP; ++i) {
       const int e = t + 256 * i;
       const int rr = e >> 4, k8 = e & 15;
-      r.p[i] = load_p8<PVEC>(pr, valid && qb + rr < s_q, (int64_t)rr * s_kv, k0 + 8 * k8, s_kv);
+      const int64_t kc = k0 + 8 * k8, lim = s_kv - s_q + qb + rr;  // last key the row sees
+      r.p[i] = load_p8<PVEC>(pr, valid && qb + rr < s_q && (!CMASK || kc <= lim), (int64_t)rr * s_kv,
+                             kc, s_kv);
+      if (CMASK) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r.p[i][j] = kc + j <= lim ? r.p[i][j] : (unsigned short)0;
+      }
     }
     const brsrc_t cr = make_brsrc(dCt + (int64_t)h * D * LQ + qb, (uint32_t)(((D - 1) * LQ + QT) * 2));
 #pragma unroll
@@ -1015,7 +1060,7 @@ __device__ __forceinline__ void attn_dv_bf16_body(int64_t blk, int64_t s_q, int6
       }
 }
 
-template <int D, bool PVEC>
+template <int D, bool PVEC, bool CMASK>
 __global__ __launch_bounds__(256, 2) void attn_dv_bf16_kernel(int64_t s_q, int64_t s_kv, int Hq,
                                                            int grp, int cmax, int64_t cs,
                                                            int64_t nfull, int64_t LQ,
@@ -1023,8 +1068,8 @@ __global__ __launch_bounds__(256, 2) void attn_dv_bf16_kernel(int64_t s_q, int64
                                                            const uint16_t* __restrict__ dCt,
                                                            float* __restrict__ out, int causal) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[dv_bf16_lds<D>()];
-  attn_dv_bf16_body<D, PVEC>(blockIdx.x, s_q, s_kv, Hq, grp, cmax, cs, nfull, LQ, P, dCt, out,
-                             causal, smem);
+  attn_dv_bf16_body<D, PVEC, CMASK>(blockIdx.x, s_q, s_kv, Hq, grp, cmax, cs, nfull, LQ, P, dCt,
+                                    out, causal, smem);
 }
 
 // dQ and dV in one launch: workgroups [0, ndq) are dQ's, the rest dV's work
@@ -1037,15 +1082,15 @@ __global__ __launch_bounds__(256, 2) void attn_dqdv_bf16_kernel(
     const uint16_t* __restrict__ Kt, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ ctx, const float* __restrict__ delta_ws, float* __restrict__ dq,
     float scale, int causal, int64_t ndq, int cmax, int64_t cs, int64_t nfull, int64_t LQ,
-    const uint16_t* __restrict__ dCt, float* __restrict__ dvout) {
+    const uint16_t* __restrict__ dCt, float* __restrict__ dvout, uint16_t* __restrict__ ds_out) {
   constexpr int LDS = dq_bf16_lds<D>() > dv_bf16_lds<D>() ? dq_bf16_lds<D>() : dv_bf16_lds<D>();
   __shared__ __attribute__((aligned(16))) uint16_t smem[LDS];
   if ((int64_t)blockIdx.x < ndq)
     attn_dq_bf16_body<D, HW, PVEC>(blockIdx.x, s_q, s_kv, Hq, grp, LK, npairs, dctx, P, Kt, V,
-                                   ctx, delta_ws, dq, scale, causal, smem);
+                                   ctx, delta_ws, dq, scale, causal, smem, ds_out);
   else
-    attn_dv_bf16_body<D, PVEC>((int64_t)blockIdx.x - ndq, s_q, s_kv, Hq, grp, cmax, cs, nfull,
-                               LQ, P, dCt, dvout, causal, smem);
+    attn_dv_bf16_body<D, PVEC, false>((int64_t)blockIdx.x - ndq, s_q, s_kv, Hq, grp, cmax, cs,
+                                      nfull, LQ, P, dCt, dvout, causal, smem);
 }
 
 // ---------------------------------------------------------------- bfloat16, D = 16
@@ -1293,12 +1338,15 @@ static bool bf16_mfma_path(int dt, int64_t D) { return dt == BF16 && D >= 32; }
 // Workspace of the sequence path, 256-byte aligned pieces:
 //   delta [Hq, s_q] f32 (callers without ctx) | dv chunk partials f32 |
 //   bf16 MFMA path: Kt [Hkv, D, LK] bf16 | dCt [Hq, D, LQ] bf16
+//   with dK: scale dS [Hq, s_q, s_kv] (f32, or bf16 on the bf16 MFMA path) |
+//   bf16 MFMA path: Qt [Hq, D, LQ] bf16
 struct AttnWs {
-  size_t delta, part, kt, dct, dq2, end;
+  size_t delta, part, kt, dct, dq2, ds, qt, end;
   int64_t LK, LQ;
 };
 static size_t al256(size_t b) { return (b + 255) / 256 * 256; }
-static AttnWs attn_ws(int64_t s_q, int64_t s_kv, int64_t Hq, int64_t Hkv, int64_t D, int dt) {
+static AttnWs attn_ws(int64_t s_q, int64_t s_kv, int64_t Hq, int64_t Hkv, int64_t D, int dt,
+                      bool with_dk = false) {
   AttnWs w;
   const bool hb = bf16_mfma_path(dt, D);
   // sized for the larger chunk count of the causal and the full mask
@@ -1316,13 +1364,16 @@ static AttnWs attn_ws(int64_t s_q, int64_t s_kv, int64_t Hq, int64_t Hkv, int64_
   w.dct = w.kt + (hb ? al256((size_t)Hkv * D * w.LK * 2) : 0);
   w.dq2 = w.dct + (hb ? al256((size_t)Hq * D * w.LQ * 2) : 0);
   // fp32 path: the second key half's dq partial (causal key split)
-  w.end = w.dq2 + (hb ? 0 : al256((size_t)s_q * Hq * D * 4));
+  w.ds = w.dq2 + (hb ? 0 : al256((size_t)s_q * Hq * D * 4));
+  w.qt = w.ds + (with_dk ? al256((size_t)Hq * s_q * s_kv * (dt == BF16 ? 2 : 4)) : 0);
+  w.end = w.qt + (with_dk && hb ? al256((size_t)Hq * D * w.LQ * 2) : 0);
   return w;
 }
 
 size_t attn_ws_bytes(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_kv_heads,
-                     int64_t head_dim, int dt) {
-  const size_t seq = attn_ws(s_q, s_kv, n_heads, n_kv_heads, head_dim, dt).end;
+                     int64_t head_dim, int dt, bool with_dk) {
+  const size_t seq = attn_ws(s_q, s_kv, n_heads, n_kv_heads, head_dim, dt, with_dk).end;
+  if (with_dk) return seq;
   if (s_q == 1) {
     const size_t d = dec_attn_ws_bytes(s_kv, n_heads, head_dim);
     return d > seq ? d : seq;
@@ -1340,13 +1391,13 @@ template <int D, int HW>
 static void launch_dq_f32(int64_t s_q, int64_t s_kv, int Hq, int grp, const float* dctx,
                           const float* P, const float* K, const float* V, const float* ctx,
                           const float* delta, float* dq, float* dq2, bool ksplit, float scale,
-                          int causal, hipStream_t s) {
+                          int causal, hipStream_t s, float* ds) {
   constexpr int QW = 4 / HW;
   const int64_t nqt = cdiv64(s_q, 16 * QW);
   const dim3 grid((unsigned)((ksplit ? 2 * ((nqt + 1) / 2) : nqt) * (Hq / HW)));
 #define LBP_DQ32(PV, KS)                                                                       \
   attn_dq_f32_kernel<D, HW, PV, KS><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, \
-                                                         delta, dq, dq2, scale, causal)
+                                                         delta, dq, dq2, scale, causal, ds)
   if (s_kv % 4 == 0) {
     if (ksplit) LBP_DQ32(true, true);
     else LBP_DQ32(true, false);
@@ -1376,9 +1427,11 @@ static hipError_t attn_launch_f32(int64_t s_q, int64_t s_kv, int Hq, int Hkv, co
                                   const float* P, const float* K, const float* V,
                                   const float* ctx, float* dq, float* dv, float scale, int causal,
                                   void* ws, hipStream_t s, const float** dq_second,
-                                  const RopeArgs* rope, bool* rope_done) {
+                                  const RopeArgs* rope, bool* rope_done, const float* Q,
+                                  float* dk) {
   const int grp = Hq / Hkv;
-  const AttnWs wl = attn_ws(s_q, s_kv, Hq, Hkv, D, F32);
+  const AttnWs wl = attn_ws(s_q, s_kv, Hq, Hkv, D, F32, dk != nullptr);
+  float* ds = dk != nullptr ? (float*)((char*)ws + wl.ds) : nullptr;
   float* delta = (float*)((char*)ws + wl.delta);
   const double pairs = attn_pairs(s_q, s_kv, causal);
   const double pbytes = pairs * Hq * 4, qbytes = (double)s_q * Hq * D * 4;
@@ -1396,15 +1449,16 @@ static hipError_t attn_launch_f32(int64_t s_q, int64_t s_kv, int Hq, int Hkv, co
   const bool ksplit = causal && cdiv64(s_q, 16 * (4 / hw)) >= 2;
   float* dq2 = (float*)((char*)ws + wl.dq2);
   if (hw == 4)
-    launch_dq_f32<D, 4>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta, dq, dq2, ksplit, scale, causal, s);
+    launch_dq_f32<D, 4>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta, dq, dq2, ksplit, scale, causal, s, ds);
   else if (hw == 2)
-    launch_dq_f32<D, 2>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta, dq, dq2, ksplit, scale, causal, s);
+    launch_dq_f32<D, 2>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta, dq, dq2, ksplit, scale, causal, s, ds);
   else
-    launch_dq_f32<D, 1>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta, dq, dq2, ksplit, scale, causal, s);
+    launch_dq_f32<D, 1>(s_q, s_kv, Hq, grp, dctx, P, K, V, ctx, delta, dq, dq2, ksplit, scale, causal, s, ds);
   // the attention's single pass: P, dCtx, ctx, K and V read once, dq
-  // written (dV's write is counted at its launch)
+  // written (dV's write is counted at its launch; with dK, dS is written
+  // for its pass)
   mark("attn_dq_f32", pbytes + qbytes * (ctx ? 3 : 2) + 2 * kvbytes, 4.0 * D * pairs * Hq, s,
-       ksplit ? qbytes : 0.0);
+       (ksplit ? qbytes : 0.0) + (ds ? pbytes : 0.0));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ksplit && dq_second != nullptr) {
     *dq_second = dq2;  // the caller adds it (the inverse RoPE pass does)
@@ -1416,16 +1470,38 @@ static hipError_t attn_launch_f32(int64_t s_q, int64_t s_kv, int Hq, int Hkv, co
     mark("attn_dq_add", 0, 0, s, qbytes * 3);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (dv == nullptr) return hipSuccess;
   const DvPlan dp = dv_plan(s_q, s_kv, Hkv, grp, causal, FV_GEO, FV_WG_TARGET);
-  float* part = dp.cmax > 1 ? (float*)((char*)ws + wl.part) : dv;
-  attn_dv_f32_kernel<D><<<dim3((unsigned)dp.items), 256, 0, s>>>(
-      s_q, s_kv, Hq, grp, dp.cmax, dp.cs, dp.nfull, dctx, P, part, causal);
-  mark("attn_dv_f32", kvbytes, 2.0 * D * pairs * Hq, s,
-       pbytes + qbytes + (dp.cmax > 1 ? kvbytes * (dp.cmax - 1) : 0.0));
+  float* const partbuf = (float*)((char*)ws + wl.part);
+  if (dv != nullptr) {
+    float* part = dp.cmax > 1 ? partbuf : dv;
+    attn_dv_f32_kernel<D, false><<<dim3((unsigned)dp.items), 256, 0, s>>>(
+        s_q, s_kv, Hq, grp, dp.cmax, dp.cs, dp.nfull, dctx, P, part, causal);
+    mark("attn_dv_f32", kvbytes, 2.0 * D * pairs * Hq, s,
+         pbytes + qbytes + (dp.cmax > 1 ? kvbytes * (dp.cmax - 1) : 0.0));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (dp.cmax > 1 &&
+        (e = launch_dv_reduce(s_q, s_kv, Hq, Hkv, D, dp.cmax, dp.cs, part, dv, causal, FV_GEO, dq,
+                              ksplit && dq_second != nullptr ? dq2 : nullptr, rope, rope_done, s)) !=
+            hipSuccess)
+      return e;
+  }
+  if (dk == nullptr) return hipSuccess;
+  // dK = scale dS^T Q: the dV kernel on (scale dS, Q), reading dS only at the
+  // keys each query sees; chunk partials reduced as dV's are
+  float* kpart = dp.cmax > 1 ? partbuf : dk;
+  if (causal)
+    attn_dv_f32_kernel<D, true><<<dim3((unsigned)dp.items), 256, 0, s>>>(
+        s_q, s_kv, Hq, grp, dp.cmax, dp.cs, dp.nfull, Q, ds, kpart, causal);
+  else
+    attn_dv_f32_kernel<D, false><<<dim3((unsigned)dp.items), 256, 0, s>>>(
+        s_q, s_kv, Hq, grp, dp.cmax, dp.cs, dp.nfull, Q, ds, kpart, causal);
+  // dK written; Q once (dS is implementation traffic: the method never
+  // stores it)
+  mark("attn_dk_f32", kvbytes + qbytes, 2.0 * D * pairs * Hq, s,
+       pbytes + (dp.cmax > 1 ? kvbytes * (dp.cmax - 1) : 0.0));
   if ((e = hipGetLastError()) != hipSuccess || dp.cmax == 1) return e;
-  return launch_dv_reduce(s_q, s_kv, Hq, Hkv, D, dp.cmax, dp.cs, part, dv, causal, FV_GEO, dq,
-                          ksplit && dq_second != nullptr ? dq2 : nullptr, rope, rope_done, s);
+  return launch_dv_reduce(s_q, s_kv, Hq, Hkv, D, dp.cmax, dp.cs, kpart, dk, causal, FV_GEO, dq,
+                          nullptr, nullptr, nullptr, s);
 }
 
 template <int D, int HW>
@@ -1433,7 +1509,8 @@ static void launch_dq_bf16(int64_t s_q, int64_t s_kv, int Hq, int grp, int64_t L
                            const float* dctx, const uint16_t* P, const uint16_t* Kt,
                            const uint16_t* V, const uint16_t* ctx, const float* delta, float* dq,
                            float scale, int causal, hipStream_t s, const DvPlan* dp = nullptr,
-                           int64_t LQ = 0, const uint16_t* dCt = nullptr, float* dvout = nullptr) {
+                           int64_t LQ = 0, const uint16_t* dCt = nullptr, float* dvout = nullptr,
+                           uint16_t* ds = nullptr) {
   constexpr int QW = 4 / HW;
   const int nsub = (int)cdiv64(s_q, 16);
   const int npairs = (nsub + 1) / 2;
@@ -1444,20 +1521,20 @@ static void launch_dq_bf16(int64_t s_q, int64_t s_kv, int Hq, int grp, int64_t L
     if (s_kv % 8 == 0)
       attn_dqdv_bf16_kernel<D, HW, true><<<g2, 256, 0, s>>>(
           s_q, s_kv, Hq, grp, LK, npairs, dctx, P, Kt, V, ctx, delta, dq, scale, causal, ndq,
-          dp->cmax, dp->cs, dp->nfull, LQ, dCt, dvout);
+          dp->cmax, dp->cs, dp->nfull, LQ, dCt, dvout, ds);
     else
       attn_dqdv_bf16_kernel<D, HW, false><<<g2, 256, 0, s>>>(
           s_q, s_kv, Hq, grp, LK, npairs, dctx, P, Kt, V, ctx, delta, dq, scale, causal, ndq,
-          dp->cmax, dp->cs, dp->nfull, LQ, dCt, dvout);
+          dp->cmax, dp->cs, dp->nfull, LQ, dCt, dvout, ds);
     return;
   }
   const dim3 grid((unsigned)ndq);
   if (s_kv % 8 == 0)
     attn_dq_bf16_kernel<D, HW, true><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, LK, npairs, dctx, P,
-                                                          Kt, V, ctx, delta, dq, scale, causal);
+                                                          Kt, V, ctx, delta, dq, scale, causal, ds);
   else
     attn_dq_bf16_kernel<D, HW, false><<<grid, 256, 0, s>>>(s_q, s_kv, Hq, grp, LK, npairs, dctx, P,
-                                                           Kt, V, ctx, delta, dq, scale, causal);
+                                                           Kt, V, ctx, delta, dq, scale, causal, ds);
 }
 
 template <int D>
@@ -1465,10 +1542,11 @@ static hipError_t attn_launch_bf16(int64_t s_q, int64_t s_kv, int Hq, int Hkv, c
                                    const uint16_t* P, const uint16_t* K, const uint16_t* V,
                                    const uint16_t* ctx, float* dq, float* dv, float scale,
                                    int causal, void* ws, hipStream_t s, const RopeArgs* rope,
-                                   bool* rope_done, bool dct_ready) {
+                                   bool* rope_done, bool dct_ready, const uint16_t* Q, float* dk) {
   const int grp = Hq / Hkv;
-  const AttnWs wl = attn_ws(s_q, s_kv, Hq, Hkv, D, BF16);
+  const AttnWs wl = attn_ws(s_q, s_kv, Hq, Hkv, D, BF16, dk != nullptr);
   char* wb = (char*)ws;
+  uint16_t* ds = dk != nullptr ? (uint16_t*)(wb + wl.ds) : nullptr;
   float* delta = (float*)(wb + wl.delta);
   uint16_t* Kt = (uint16_t*)(wb + wl.kt);
   uint16_t* dCt = (uint16_t*)(wb + wl.dct);
@@ -1500,26 +1578,54 @@ static hipError_t attn_launch_bf16(int64_t s_q, int64_t s_kv, int Hq, int Hkv, c
   const int hw = grp % 4 == 0 ? 4 : (grp % 2 == 0 ? 2 : 1);
   if (hw == 4)
     launch_dq_bf16<D, 4>(s_q, s_kv, Hq, grp, wl.LK, dctx, P, Kt, V, ctx, delta, dq, scale, causal, s,
-                         dpp, wl.LQ, dCt, part);
+                         dpp, wl.LQ, dCt, part, ds);
   else if (hw == 2)
     launch_dq_bf16<D, 2>(s_q, s_kv, Hq, grp, wl.LK, dctx, P, Kt, V, ctx, delta, dq, scale, causal, s,
-                         dpp, wl.LQ, dCt, part);
+                         dpp, wl.LQ, dCt, part, ds);
   else
     launch_dq_bf16<D, 1>(s_q, s_kv, Hq, grp, wl.LK, dctx, P, Kt, V, ctx, delta, dq, scale, causal, s,
-                         dpp, wl.LQ, dCt, part);
+                         dpp, wl.LQ, dCt, part, ds);
   // the attention's single pass: P, dCtx (fp32), ctx, K and V read once,
   // dq and dV written; the dV body's second read of P, the transposed
   // copies it reads and its chunk partials are implementation traffic
   const double alg = pbytes + qbytes * (4 + 4 + (ctx ? 2 : 0)) + 2 * kvbytes * 2 +
                      (dv != nullptr ? kvbytes * 4 : 0.0);
   if (dv == nullptr)
-    mark("attn_dq_bf16", alg, 4.0 * D * pairs * Hq, s);
+    mark("attn_dq_bf16", alg, 4.0 * D * pairs * Hq, s, ds ? pbytes : 0.0);
   else
     mark("attn_dqdv_bf16", alg, 6.0 * D * pairs * Hq, s,
-         pbytes + qbytes * 2 + (dp.cmax > 1 ? kvbytes * 4 * (dp.cmax - 1) : 0.0));
-  if ((e = hipGetLastError()) != hipSuccess || dv == nullptr || dp.cmax == 1) return e;
-  return launch_dv_reduce(s_q, s_kv, Hq, Hkv, D, dp.cmax, dp.cs, part, dv, causal, HV_GEO, dq,
-                          nullptr, rope, rope_done, s);
+         pbytes * (ds ? 2 : 1) + qbytes * 2 + (dp.cmax > 1 ? kvbytes * 4 * (dp.cmax - 1) : 0.0));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (dv != nullptr && dp.cmax > 1 &&
+      (e = launch_dv_reduce(s_q, s_kv, Hq, Hkv, D, dp.cmax, dp.cs, part, dv, causal, HV_GEO, dq,
+                            nullptr, rope, rope_done, s)) != hipSuccess)
+    return e;
+  if (dk == nullptr) return hipSuccess;
+  // dK = scale dS^T Q: the dV body on (scale dS, Q^T), reading dS only at the
+  // keys each query sees; Q^T [Hq, D, LQ] bf16 (zero padded) first
+  uint16_t* Qt = (uint16_t*)(wb + wl.qt);
+  const TrJob jq{s_q, wl.LQ, (int64_t)Hq * D, Q, Qt, (int)(wl.LQ / TR_R), (int)(Hq * D / TR_C)};
+  const TrJob none{0, 0, 0, nullptr, nullptr, 0, 0};
+  transpose_bf16_kernel<bf16, bf16><<<dim3((unsigned)((int64_t)jq.gx * jq.gy)), 256, 0, s>>>(jq, none);
+  mark("transpose_bf16", 0, 0, s, qbytes * 2 + (double)Hq * D * wl.LQ * 2);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  float* kpart = dp.cmax > 1 ? (float*)(wb + wl.part) : dk;
+#define LBP_DK16(PV, CM)                                                                      \
+  attn_dv_bf16_kernel<D, PV, CM><<<dim3((unsigned)dp.items), 256, 0, s>>>(                     \
+      s_q, s_kv, Hq, grp, dp.cmax, dp.cs, dp.nfull, wl.LQ, ds, Qt, kpart, causal)
+  if (s_kv % 8 == 0) {
+    if (causal) LBP_DK16(true, true);
+    else LBP_DK16(true, false);
+  } else {
+    if (causal) LBP_DK16(false, true);
+    else LBP_DK16(false, false);
+  }
+#undef LBP_DK16
+  mark("attn_dk_bf16", kvbytes * 4 + qbytes * 2, 2.0 * D * pairs * Hq, s,
+       pbytes + (dp.cmax > 1 ? kvbytes * 4 * (dp.cmax - 1) : 0.0));
+  if ((e = hipGetLastError()) != hipSuccess || dp.cmax == 1) return e;
+  return launch_dv_reduce(s_q, s_kv, Hq, Hkv, D, dp.cmax, dp.cs, kpart, dk, causal, HV_GEO, dq,
+                          nullptr, nullptr, nullptr, s);
 }
 
 template <typename T, int D>
@@ -1563,17 +1669,21 @@ static hipError_t attn_dispatch_d(int64_t s_q, int64_t s_kv, int Hq, int Hkv, in
                                   const float* dctx, const void* P, const void* K, const void* V,
                                   const void* ctx, float* dq, float* dv, float scale, int causal,
                                   void* ws, hipStream_t s, const float** dq_second,
-                                  const RopeArgs* rope, bool* rope_done, bool dct_ready) {
+                                  const RopeArgs* rope, bool* rope_done, bool dct_ready,
+                                  const void* Q, float* dk) {
 #define LBP_ATTN_D(DD)                                                                         \
   case DD:                                                                                     \
     if constexpr (sizeof(T) == 4)                                                              \
       return attn_launch_f32<DD>(s_q, s_kv, Hq, Hkv, dctx, (const float*)P, (const float*)K,   \
                                  (const float*)V, (const float*)ctx, dq, dv, scale, causal, ws, \
-                                 s, dq_second, rope, rope_done);                               \
+                                 s, dq_second, rope, rope_done, (const float*)Q, dk);          \
     else if constexpr (DD >= 32)                                                               \
       return attn_launch_bf16<DD>(s_q, s_kv, Hq, Hkv, dctx, (const uint16_t*)P,                \
                                   (const uint16_t*)K, (const uint16_t*)V, (const uint16_t*)ctx, \
-                                  dq, dv, scale, causal, ws, s, rope, rope_done, dct_ready);   \
+                                  dq, dv, scale, causal, ws, s, rope, rope_done, dct_ready,    \
+                                  (const uint16_t*)Q, dk);                                     \
+    else if (dk != nullptr)                                                                    \
+      return hipErrorInvalidValue; /* dK is not built for bf16 with head_dim 16 */             \
     else                                                                                       \
       return attn_launch<T, DD>(s_q, s_kv, Hq, Hkv, dctx, (const T*)P, (const T*)K,            \
                                 (const T*)V, (const T*)ctx, dq, dv, scale, causal, (float*)ws, s);
@@ -1593,14 +1703,17 @@ hipError_t launch_attn_bwd(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n
                            const void* V, const void* ctx, int dt, float* dq, float* dv,
                            float scale, int causal, void* ws, hipStream_t s,
                            const float** dq_second, const RopeArgs* rope, bool* rope_done,
-                           bool dct_ready) {
+                           bool dct_ready, const void* Q, float* dk) {
   if (dq_second != nullptr) *dq_second = nullptr;
   if (rope_done != nullptr) *rope_done = false;
   if (s_q == 0) {
-    if (dv != nullptr) return launch_fill_zero(s_kv * n_kv_heads * head_dim, dv, s);
-    return hipSuccess;
+    hipError_t e = hipSuccess;
+    if (dv != nullptr) e = launch_fill_zero(s_kv * n_kv_heads * head_dim, dv, s);
+    if (e == hipSuccess && dk != nullptr) e = launch_fill_zero(s_kv * n_kv_heads * head_dim, dk, s);
+    return e;
   }
-  if (s_q == 1 && dec_attn_fits(s_kv, n_heads, n_kv_heads, head_dim)) {
+  if (dk != nullptr && (Q == nullptr || (dt == BF16 && head_dim < 32))) return hipErrorInvalidValue;
+  if (s_q == 1 && dk == nullptr && dec_attn_fits(s_kv, n_heads, n_kv_heads, head_dim)) {
     DecAttnArgs a{};
     a.s_kv = s_kv;
     a.Hq = (int)n_heads;
@@ -1629,10 +1742,10 @@ hipError_t launch_attn_bwd(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n
   if (dt == F32)
     return attn_dispatch_d<float>(s_q, s_kv, (int)n_heads, (int)n_kv_heads, (int)head_dim, dctx,
                                   P, K, V, ctx, dq, dv, scale, causal, ws, s, dq_second, rope,
-                                  rope_done, false);
+                                  rope_done, false, Q, dk);
   return attn_dispatch_d<bf16>(s_q, s_kv, (int)n_heads, (int)n_kv_heads, (int)head_dim, dctx, P,
                                K, V, ctx, dq, dv, scale, causal, ws, s, dq_second, rope,
-                               rope_done, dct_ready);
+                               rope_done, dct_ready, Q, dk);
 }
 
 uint16_t* attn_dct_buffer(void* ws, int64_t s_q, int64_t s_kv, int64_t n_heads,

@@ -239,14 +239,20 @@ hipError_t launch_dec_attn(int dt, int head_dim, const DecAttnArgs& a, hipStream
 // With rope set, the inverse RoPE of dq (plus the split second half) may run
 // in the launch that adds the dV chunk partials; *rope_done says whether it
 // did (else the caller runs it, with *dq_second as dy2).
+// With dk set, also dK = scale dS^T Q [s_kv, n_kv_heads*head_dim] (after
+// RoPE, like K) from the post-RoPE queries Q (act type): the dQ kernels store
+// scale dS and the dV kernels run a second pass on (scale dS, Q).  The
+// workspace must then be attn_ws_bytes(..., with_dk = true); not for bf16
+// with head_dim 16 (hipErrorInvalidValue).
 size_t attn_ws_bytes(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_kv_heads,
-                     int64_t head_dim, int dt);
+                     int64_t head_dim, int dt, bool with_dk = false);
 hipError_t launch_attn_bwd(int64_t s_q, int64_t s_kv, int64_t n_heads, int64_t n_kv_heads,
                            int64_t head_dim, const float* dctx, const void* P, const void* K,
                            const void* V, const void* ctx, int dt, float* dq, float* dv,
                            float scale, int causal, void* ws, hipStream_t s,
                            const float** dq_second = nullptr, const RopeArgs* rope = nullptr,
-                           bool* rope_done = nullptr, bool dct_ready = false);
+                           bool* rope_done = nullptr, bool dct_ready = false,
+                           const void* Q = nullptr, float* dk = nullptr);
 // The bf16 attention's dCtxᵀ buffer inside its workspace (bf16 [Hq D][LQ],
 // LQ = s_q rounded up to 64), or NULL where the path takes none.  A caller
 // that fills it (dct_ready) spares the attention its transposition.
@@ -270,9 +276,12 @@ struct LoraJob {
   void* ws;
 };
 // Up to two adapters, in the same launches where their shapes allow;
-// gnorm_sq += ||dA||^2 of each, in job order.
+// gnorm_sq += ||dA||^2 of each, in job order.  With dx set (jobs sharing
+// rows and in_dim), also dx [rows][in_dim] = sum over the adapters of
+// s (dy B) A with the B and A of before the update: their share of the
+// gradient at the adapters' input.
 hipError_t launch_lora_adamw_jobs(const LoraJob* jobs, int njobs, float* gnorm_sq,
-                                  const AdamHP& hp, hipStream_t s);
+                                  const AdamHP& hp, hipStream_t s, float* dx = nullptr);
 hipError_t launch_lora_adamw(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank,
                              const float* dy, const void* x, const void* h, int dt, float* A,
                              float* B, float* m_a, float* v_a, float* m_b, float* v_b,

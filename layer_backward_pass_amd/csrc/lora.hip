@@ -396,6 +396,53 @@ __global__ __launch_bounds__(256) void lora_a_update_kernel(Pair<AUpdArgs> pa, A
   if (threadIdx.x == 0) A.sq_part[blockIdx.x] = sq;
 }
 
+// The adapters' share of the gradient at their input x (the attention
+// input gradient): out[i][n] (+)= sum over adapters of sum_{r < rank}
+// g[i][r] A[r][n], with g = s dy B as the B update reduced it and A before
+// its update.  Workgroup = 256 columns x 16 rows; the rows' g values are
+// staged in LDS, each thread walks A's rank rows for its column.
+struct DxArgs {
+  const float* g;  // [rows][rp]
+  int64_t rp;
+  const float* A;  // [rank][n]
+  int rank;
+};
+__global__ __launch_bounds__(256) void lora_dx_kernel(int64_t rows, int64_t n, DxArgs a0, DxArgs a1,
+                                                      int nadp, float* __restrict__ out,
+                                                      int accumulate) {
+  __shared__ float gs[2][16][64];
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * 16;
+  for (int z = 0; z < 2; ++z) {
+    const DxArgs& a = z == 0 ? a0 : a1;
+    for (int e = threadIdx.x; e < 16 * 64; e += 256) {
+      const int i = e >> 6, r = e & 63;
+      gs[z][i][r] = (z < nadp && r0 + i < rows && r < a.rank) ? a.g[(r0 + i) * a.rp + r] : 0.f;
+    }
+  }
+  __syncthreads();
+  if (col >= n) return;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int z = 0; z < nadp; ++z) {
+    const DxArgs& a = z == 0 ? a0 : a1;
+    for (int r = 0; r < a.rank; ++r) {
+      const float av = a.A[(int64_t)r * n + col];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] += gs[z][i][r] * av;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t row = r0 + i;
+    if (row < rows) {
+      float* o = out + row * n + col;
+      *o = accumulate ? *o + acc[i] : acc[i];
+    }
+  }
+}
+
 // gnorm_sq += the per-workgroup partials of adapter 0, then of adapter 1
 // (n1 = 0: none), each summed in index order.
 __global__ __launch_bounds__(64) void lora_gnorm_kernel(int n0, const float* __restrict__ sq0,
@@ -459,7 +506,7 @@ size_t lora_ws_bytes(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank
 // arguments (rank blocks, dtype, vector path), run in the same launches.
 template <int RB, bool VEC, typename TH>
 static hipError_t lora_group(const LoraJob* const* jobs, int nz, float* gnorm_sq,
-                             const AdamHP& hp, hipStream_t s) {
+                             const AdamHP& hp, hipStream_t s, float* dx, int dx_acc) {
   Pair<DyArgs> dy{};
   Pair<BUpdArgs> bu{};
   Pair<DaArgs> da{};
@@ -519,6 +566,22 @@ static hipError_t lora_group(const LoraJob* const* jobs, int nz, float* gnorm_sq
   lora_b_update_kernel<<<dim3((unsigned)bx, 1, (unsigned)nz), 256, 0, s>>>(bu, hp);
   mark("lora_adamw_b", by_b, fl_b, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (dx != nullptr && rows > 0) {
+    // the adapters' input-gradient term, while A is still the pre-update A
+    DxArgs xa[2];
+    for (int z = 0; z < 2; ++z) {
+      const LoraJob& j = *jobs[z < nz ? z : 0];
+      const LoraWs o = lora_ws(j.rows, j.in_dim, j.out_dim, j.rank);
+      xa[z] = DxArgs{(const float*)j.ws + o.g, 16 * RB, j.A, (int)j.rank};
+    }
+    const int64_t n = jobs[0]->in_dim;
+    lora_dx_kernel<<<dim3((unsigned)cdiv(n, 256), (unsigned)cdiv(rows, 16)), 256, 0, s>>>(
+        rows, n, xa[0], xa[1], nz, dx, dx_acc);
+    double rk = 0;
+    for (int z = 0; z < nz; ++z) rk += (double)jobs[z]->rank;
+    mark("lora_dx", (double)rows * n * 4 * (dx_acc ? 2 : 1) + rk * (n + rows) * 4, 2.0 * rows * n * rk, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (rows > 0) {
     lora_da_kernel<RB, typename std::conditional<sizeof(TH) == 4, float, bf16>::type>
         <<<dim3((unsigned)nd), 256, 0, s>>>(da);
@@ -539,18 +602,18 @@ static hipError_t lora_group(const LoraJob* const* jobs, int nz, float* gnorm_sq
 }
 
 static hipError_t lora_dispatch(const LoraJob* const* jobs, int nz, float* gnorm_sq,
-                                const AdamHP& hp, hipStream_t s) {
+                                const AdamHP& hp, hipStream_t s, float* dx, int dx_acc) {
   const LoraJob& j = *jobs[0];
   const int rb = (int)cdiv(j.rank, 16);
   const bool vec = j.out_dim % 4 == 0;
 #define LBP_LG(RBV)                                                                    \
   case RBV:                                                                            \
     if (vec) {                                                                         \
-      if (j.dt == F32) return lora_group<RBV, true, float>(jobs, nz, gnorm_sq, hp, s);  \
-      return lora_group<RBV, true, uint16_t>(jobs, nz, gnorm_sq, hp, s);               \
+      if (j.dt == F32) return lora_group<RBV, true, float>(jobs, nz, gnorm_sq, hp, s, dx, dx_acc);  \
+      return lora_group<RBV, true, uint16_t>(jobs, nz, gnorm_sq, hp, s, dx, dx_acc);               \
     }                                                                                  \
-    if (j.dt == F32) return lora_group<RBV, false, float>(jobs, nz, gnorm_sq, hp, s);   \
-    return lora_group<RBV, false, uint16_t>(jobs, nz, gnorm_sq, hp, s);
+    if (j.dt == F32) return lora_group<RBV, false, float>(jobs, nz, gnorm_sq, hp, s, dx, dx_acc);   \
+    return lora_group<RBV, false, uint16_t>(jobs, nz, gnorm_sq, hp, s, dx, dx_acc);
   switch (rb) {
     LBP_LG(1)
     LBP_LG(2)
@@ -562,20 +625,20 @@ static hipError_t lora_dispatch(const LoraJob* const* jobs, int nz, float* gnorm
 }
 
 hipError_t launch_lora_adamw_jobs(const LoraJob* jobs, int njobs, float* gnorm_sq,
-                                  const AdamHP& hp, hipStream_t s) {
+                                  const AdamHP& hp, hipStream_t s, float* dx) {
   if (njobs <= 0) return hipSuccess;
   const LoraJob* p[2] = {&jobs[0], njobs > 1 ? &jobs[1] : &jobs[0]};
   if (njobs == 2) {
     const LoraJob &a = jobs[0], &b = jobs[1];
     const bool same = cdiv(a.rank, 16) == cdiv(b.rank, 16) && a.dt == b.dt &&
                       (a.out_dim % 4 == 0) == (b.out_dim % 4 == 0) && a.rows == b.rows;
-    if (same) return lora_dispatch(p, 2, gnorm_sq, hp, s);
-    hipError_t e = lora_dispatch(p, 1, gnorm_sq, hp, s);
+    if (same) return lora_dispatch(p, 2, gnorm_sq, hp, s, dx, 0);
+    hipError_t e = lora_dispatch(p, 1, gnorm_sq, hp, s, dx, 0);
     if (e != hipSuccess) return e;
     p[0] = &jobs[1];
-    return lora_dispatch(p, 1, gnorm_sq, hp, s);
+    return lora_dispatch(p, 1, gnorm_sq, hp, s, dx, 1);
   }
-  return lora_dispatch(p, 1, gnorm_sq, hp, s);
+  return lora_dispatch(p, 1, gnorm_sq, hp, s, dx, 0);
 }
 
 hipError_t launch_lora_adamw(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank,
@@ -585,7 +648,7 @@ hipError_t launch_lora_adamw(int64_t rows, int64_t in_dim, int64_t out_dim, int6
                              const AdamHP& hp, void* ws, hipStream_t s) {
   const LoraJob j{rows, in_dim, out_dim, rank, dy, x, h, dt, A, B, m_a, v_a, m_b, v_b,
                   grad_a, grad_b, scaling, ws};
-  return launch_lora_adamw_jobs(&j, 1, gnorm_sq, hp, s);
+  return launch_lora_adamw_jobs(&j, 1, gnorm_sq, hp, s, nullptr);
 }
 
 }  // namespace lbp

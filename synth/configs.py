@@ -10,6 +10,10 @@ Five workloads, named by what they are:
   stack36     36 seq512-shaped layers at 1024 tokens, fp32
   seq512qk    the seq512 layer with QK-norm (per-head RMSNorm of Q and K before
               RoPE, as Qwen3-style layers have)
+  seq512ig, seq2048bf16ig
+              the seq512 / seq2048bf16 layers with the exact input gradient
+              through the attention branch (dK, the transposed Q/K/V
+              products, the adapters' terms, the attention-norm backward)
 """
 from dataclasses import dataclass, replace
 
@@ -82,8 +86,11 @@ SEQ2048BF16 = SEQ512.with_(name="seq2048bf16", index=3, seq=2048, kv_len=2048,
                            dtype="bf16")
 STACK36 = SEQ512.with_(name="stack36", index=4, seq=1024, kv_len=1024, n_layers=36)
 SEQ512QK = SEQ512.with_(name="seq512qk", index=5, qk_norm=True)
+SEQ512IG = SEQ512.with_(name="seq512ig", index=6, input_grad=True)
+SEQ2048BF16IG = SEQ2048BF16.with_(name="seq2048bf16ig", index=7, input_grad=True)
 
-CONFIGS = {c.name: c for c in (TINY, DECODE, SEQ512, SEQ2048BF16, STACK36, SEQ512QK)}
+CONFIGS = {c.name: c for c in (TINY, DECODE, SEQ512, SEQ2048BF16, STACK36, SEQ512QK, SEQ512IG,
+                               SEQ2048BF16IG)}
 
 
 def get_config(name):

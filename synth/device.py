@@ -51,6 +51,13 @@ def draw_timing_layer_device(cfg, layer=0, device="cuda:0"):
     if cfg.qk_norm:
         d["weights"]["gamma_q"] = 1 + n((cfg.head_dim,), 0.1, f32)
         d["saved"]["q_raw"] = n((S, qd))
+    if cfg.input_grad:
+        d["weights"].update(w_q=w((qd, H)), w_k=w((kvd, H)), w_v=w((kvd, H)),
+                            gamma_attn=1 + n((H,), 0.1, f32))
+        d["saved"].update(x=n((S, H)), q=n((S, qd)))
+        if cfg.qk_norm:
+            d["weights"]["gamma_k"] = 1 + n((cfg.head_dim,), 0.1, f32)
+            d["saved"]["k_raw"] = n((S, kvd))
     if cfg.sub_norms:
         d["weights"]["gamma_fsub"] = 1 + n((I,), 0.1, f32)
         d["weights"]["gamma_asub"] = 1 + n((qd,), 0.1, f32)

@@ -85,6 +85,9 @@ def f32_scalars(cfg):
 WEIGHTS = ("W_o", "W_gate", "W_up", "W_down")
 SAVED = ("attn_input", "resid1", "gate", "up", "hidden_pre", "ctx", "P", "K", "V",
          "lora_q_h", "lora_v_h", "q_raw")
+# the attention input gradient's extra weights and saved tensors
+IG_WEIGHTS = ("W_q", "W_k", "W_v")
+IG_SAVED = ("x", "q", "k_raw")
 
 
 def desc_of(c):
@@ -95,7 +98,7 @@ def desc_of(c):
                          sub_norms=c.sub_norms, causal=c.causal,
                          dtype=lbp.BF16 if c.dtype == "bf16" else lbp.F32, pos0=c.pos0,
                          eps=c.eps, rope_base=c.rope_base, attn_scale=c.scale,
-                         lora_alpha=c.alpha, qk_norm=c.qk_norm)
+                         lora_alpha=c.alpha, qk_norm=c.qk_norm, input_grad=c.input_grad)
 
 
 class DeviceLayer:
@@ -109,11 +112,14 @@ class DeviceLayer:
         w, saved, lora = OF.make_layer(cfg, draws)
         dt = tdtype(cfg)
         f32 = torch.float32
-        self.w = {k.lower(): dev(w[k], dt, device) for k in WEIGHTS}
-        for k in ("gamma_ffn", "gamma_fsub", "gamma_asub", "gamma_q"):
+        ig = cfg.input_grad
+        self.w = {k.lower(): dev(w[k], dt, device) for k in WEIGHTS + (IG_WEIGHTS if ig else ())}
+        gammas = ("gamma_ffn", "gamma_fsub", "gamma_asub", "gamma_q")
+        for k in gammas + (("gamma_attn", "gamma_k") if ig else ()):
             if k in w:
                 self.w[k] = dev(w[k], f32, device)
-        self.saved = {k: dev(saved[k], dt, device) for k in SAVED if k in saved}
+        self.saved = {k: dev(saved[k], dt, device) for k in SAVED + (IG_SAVED if ig else ())
+                      if k in saved}
         self.d_out = dev(draws["d_out"], f32, device)
         self.lora = None
         if lora is not None:

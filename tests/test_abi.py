@@ -56,7 +56,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.lorabwd_abi_version() == 3
+    assert lib.lorabwd_abi_version() == 4
     for code in (OK, ENULL, ESHAPE, EALIGN, EDTYPE, EWS, ESTEP, EALIAS, EHIP, EARG):
         s = lib.lorabwd_status_string(code).decode()
         assert s and s != "unknown status"
@@ -195,7 +195,7 @@ def test_layer_validation(lib):
              None) == EALIAS
     qn = lbp.make_desc(16, 16, 64, 256, 4, 2, 16, qk_norm=True)  # QK-norm without gamma_q
     assert f(r(qn), r(w), r(a), None, None, None, None, dh, None, None, None, fake(60), ws, None) == ENULL
-    qn.qk_norm, qn.reserved = 0, 1
+    qn.qk_norm, qn.input_grad = 0, 2
     assert f(r(qn), r(w), r(a), None, None, None, None, dh, None, None, None, fake(60), ws, None) == EARG
     d.kv_len = 8                                  # kv_len < seq
     assert f(r(d), r(w), r(a), None, None, None, None, dh, None, None, None, fake(60), ws, None) == ESHAPE

@@ -28,7 +28,8 @@ def _log(msg):
     print(msg, flush=True)
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "seq512", "seq2048bf16", "seq512qk"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "seq512", "seq2048bf16", "seq512qk", "seq512ig",
+                                  "seq2048bf16ig"])
 def test_full_size_layer(name):
     cfg = synth.get_config(name)
     t0 = time.time()

@@ -304,6 +304,29 @@ def test_lora_adamw(rows, H, out, rank, step, dt):
                 "qk_norm": True, "pos0": 700}),
     ("decode", {"hidden": 256, "ffn": 512, "n_heads": 8, "n_kv_heads": 2, "head_dim": 64,
                 "kv_len": 130, "pos0": 129, "qk_norm": True}),
+    # the exact input gradient through the attention branch (dK = scale dS^T Q
+    # from the dQ kernels' stored dS, the transposed Q/K/V products, the
+    # adapters' terms and the attention-norm backward): fp32 with ragged
+    # tiles, with QK-norm, after a cached prefix, non-causal; bf16
+    ("tiny", {"input_grad": True}),
+    ("tiny", {"input_grad": True, "seq": 45, "kv_len": 45}),
+    ("seq512", {"seq": 100, "kv_len": 100, "hidden": 256, "ffn": 512, "n_heads": 8,
+                "n_kv_heads": 2, "head_dim": 128, "rank": 8, "alpha": 16.0, "input_grad": True,
+                "qk_norm": True, "pos0": 33}),
+    ("seq512", {"seq": 40, "kv_len": 100, "pos0": 60, "hidden": 256, "ffn": 512, "n_heads": 4,
+                "n_kv_heads": 2, "head_dim": 64, "rank": 8, "alpha": 16.0, "input_grad": True}),
+    ("seq512", {"seq": 70, "kv_len": 70, "hidden": 256, "ffn": 512, "n_heads": 4,
+                "n_kv_heads": 4, "head_dim": 32, "rank": 0, "causal": False, "input_grad": True}),
+    ("seq512", {"seq": 128, "kv_len": 128, "hidden": 256, "ffn": 512, "n_heads": 8,
+                "n_kv_heads": 2, "head_dim": 128, "rank": 8, "alpha": 16.0, "dtype": "bf16",
+                "input_grad": True}),
+    ("seq512", {"seq": 96, "kv_len": 96, "hidden": 256, "ffn": 512, "n_heads": 8,
+                "n_kv_heads": 2, "head_dim": 64, "rank": 8, "alpha": 16.0, "dtype": "bf16",
+                "input_grad": True, "qk_norm": True, "pos0": 300}),
+    # one token after a 39-row prefix: the general composition with one query
+    # row (a single key would make the softmax constant and dQ identically 0)
+    ("seq512", {"seq": 1, "kv_len": 40, "pos0": 39, "hidden": 256, "ffn": 512, "n_heads": 4,
+                "n_kv_heads": 2, "head_dim": 64, "rank": 4, "alpha": 8.0, "input_grad": True}),
 ])
 def test_layer_small(name, over):
     cfg = synth.get_config(name).with_(**over)

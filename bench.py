@@ -426,7 +426,8 @@ def cpu_baseline(cfg, budget_s):
         t = synth.draw_timing_layer(one, l)
         w = {k: f64(v) for k, v in t.items() if k.startswith("W_") or k.startswith("gamma_")}
         saved = {k: f64(t[k]) for k in ("attn_input", "resid1", "gate", "up", "ctx", "P", "K",
-                                        "V", "hidden_pre", "lora_q_h", "lora_v_h") if k in t}
+                                        "V", "hidden_pre", "lora_q_h", "lora_v_h", "q_raw", "x",
+                                        "q", "k_raw") if k in t}
         lora = None
         if cfg.rank > 0:
             lora = {k: f64(v) for k, v in t.items()

@@ -24,7 +24,7 @@ TENSOR_IDS = {
     # timing-only draws (stand-ins for saved activations)
     "t_attn_input": 40, "t_resid1": 41, "t_gate": 42, "t_up": 43,
     "t_hidden_pre": 44, "t_ctx": 45, "t_P": 46, "t_K": 47, "t_V": 48,
-    "t_lora_q_h": 49, "t_lora_v_h": 50,
+    "t_lora_q_h": 49, "t_lora_v_h": 50, "t_q_raw": 51, "t_x": 52, "t_q": 53, "t_k_raw": 54,
 }
 
 
@@ -155,6 +155,18 @@ def draw_timing_layer(cfg, layer=0):
         t["hidden_pre"] = n("t_hidden_pre", (S, I))
         t["gamma_fsub"] = (1 + n("gamma_fsub", (I,), 0.1)).astype(f)
         t["gamma_asub"] = (1 + n("gamma_asub", (qd,), 0.1)).astype(f)
+    if cfg.qk_norm:
+        t["q_raw"] = n("t_q_raw", (S, qd))
+        t["gamma_q"] = (1 + n("gamma_q", (cfg.head_dim,), 0.1)).astype(f)
+    if cfg.input_grad:
+        for k, shp in (("W_q", (qd, H)), ("W_k", (kvd, H)), ("W_v", (kvd, H))):
+            t[k] = n(k, shp, 0.02)
+        t["gamma_attn"] = (1 + n("gamma_attn", (H,), 0.1)).astype(f)
+        t["x"] = n("t_x", (S, H))
+        t["q"] = n("t_q", (S, qd))
+        if cfg.qk_norm:
+            t["k_raw"] = n("t_k_raw", (S, kvd))
+            t["gamma_k"] = (1 + n("gamma_k", (cfg.head_dim,), 0.1)).astype(f)
     if r > 0:
         t["lora_q_h"] = n("t_lora_q_h", (S, r), 0.1)
         t["lora_v_h"] = n("t_lora_v_h", (S, r), 0.1)

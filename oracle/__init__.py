@@ -18,6 +18,8 @@ Modules:
             it turns seeded draws into consistent saved activations and is the
             function the finite-difference pins differentiate
   fd        central finite differences
+  bitlinear the packed ternary (BitLinear) weight format of the decode layer:
+            packing, unpacking and the transposed product
 
 Every function is pinned by tests/test_oracle_*.py (finite differences,
 closed forms, invariants, special cases reducing to library routines).  The
@@ -25,4 +27,4 @@ one thing no pin can fix is the choice among readings where the pages
 disagree (which forward is differentiated); those readings are listed in the
 module docstrings below and in the design notes.
 """
-from . import backward, forward, fd  # noqa: F401
+from . import backward, bitlinear, forward, fd  # noqa: F401

@@ -240,3 +240,47 @@ def test_context_mutation_is_caught(i):
     except (ValueError, IndexError):
         ok = False
     assert not ok, "mutation not caught: %r -> %r" % (old, new)
+
+
+# Mutations of oracle/bitlinear.py (the packed ternary weight format).
+BL_SRC = os.path.join(ROOT, "oracle", "bitlinear.py")
+BITLINEAR_MUTATIONS = [
+    ("CODE = {0: 0b00, 1: 0b01, -1: 0b11}", "CODE = {0: 0b00, 1: 0b01, -1: 0b10}"),     # code of -1
+    ("out[r, c // 4] |= np.uint8(code << (2 * (c % 4)))",
+     "out[r, c // 4] |= np.uint8(code << (2 * (3 - c % 4)))"),                        # bit order
+    ("return float(scale) * (np.asarray(dy, np.float64) @ unpack_ternary(packed, cols))",
+     "return (np.asarray(dy, np.float64) @ unpack_ternary(packed, cols))"),            # scale dropped
+]
+
+
+def _bitlinear_checks(M):
+    g = {}
+    with open(os.path.join(ROOT, "tests", "golden", "ternary_pack_example.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                k, v = (s.strip() for s in line.split("=", 1))
+                g[k] = np.array([float(t) for t in v.split()])
+    w = np.stack([g["w_row0"], g["w_row1"]])
+    ok = [np.array_equal(M.pack_ternary(w).reshape(-1), g["packed"].astype(np.uint8))]
+    r = np.random.default_rng(9)
+    t = r.integers(-1, 2, size=(5, 16))
+    dy = r.standard_normal((2, 5))
+    ok.append(np.allclose(M.bitlinear_t(dy, M.pack_ternary(0.02 * t), 0.02, 16), dy @ (0.02 * t)))
+    return ok
+
+
+def test_unmutated_bitlinear_passes():
+    from oracle import bitlinear
+    assert all(_bitlinear_checks(bitlinear))
+
+
+@pytest.mark.parametrize("i", range(len(BITLINEAR_MUTATIONS)))
+def test_bitlinear_mutation_is_caught(i):
+    old, new = BITLINEAR_MUTATIONS[i]
+    M = _load_mutant(old, new, BL_SRC)
+    try:
+        ok = all(_bitlinear_checks(M))
+    except (ValueError, IndexError, KeyError):
+        ok = False
+    assert not ok, "mutation not caught: %r -> %r" % (old, new)

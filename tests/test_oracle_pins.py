@@ -346,6 +346,38 @@ def test_adamw_matches_torch_float64(step):
     np.testing.assert_allclose(ov, opt.state[tp]["exp_avg_sq"].numpy(), rtol=1e-13)
 
 
+# ---------------------------------------------------------------- packed ternary weights
+def test_ternary_pack_golden():
+    from oracle import bitlinear as BL
+    g = load_golden("ternary_pack_example.txt")
+    w = np.stack([g["w_row0"], g["w_row1"]])
+    packed = BL.pack_ternary(w)
+    assert packed.dtype == np.uint8 and packed.shape == (2, 2)
+    np.testing.assert_array_equal(packed.reshape(-1), g["packed"].astype(np.uint8))
+    np.testing.assert_array_equal(BL.unpack_ternary(packed, 8), np.sign(w))
+
+
+def test_ternary_pack_round_trip_and_product():
+    from oracle import bitlinear as BL
+    r = rng(51)
+    t = r.integers(-1, 2, size=(7, 24))
+    w = 0.02 * t
+    packed = BL.pack_ternary(w)
+    # every byte holds only the codes 00, 01, 11 in each 2-bit field
+    for j in range(4):
+        assert not np.any(((packed >> (2 * j)) & 3) == 2)
+    np.testing.assert_array_equal(BL.unpack_ternary(packed, 24), t)
+    dy = r.standard_normal((3, 7))
+    np.testing.assert_allclose(BL.bitlinear_t(dy, packed, 0.02, 24), dy @ w, rtol=1e-14, atol=1e-16)
+    # the bit position of one column: a single +1 at column 4c + j sets code 01 at bits 2j
+    for c in range(6):
+        for j in range(4):
+            e = np.zeros((1, 24))
+            e[0, 4 * c + j] = 1.0
+            p = BL.pack_ternary(e)
+            assert p[0, c] == 1 << (2 * j) and p.sum() == 1 << (2 * j)
+
+
 # ---------------------------------------------------------------- whole layer
 def _layer_fd(cfg, seed_layer=0):
     d = synth.draw_layer(cfg, seed_layer)

@@ -23,6 +23,7 @@ Workloads (default: stack36):
   seq2048bf16  the seq512 layer at 2048 tokens with bf16 activations/weights
   stack36      36 seq512-shaped layers at 1024 tokens, fp32
   seq512qk     the seq512 layer with QK-norm before RoPE
+  decode_packed  the decode layer on packed ternary weights (2 bits per value)
   seq512ig, seq2048bf16ig
                those layers with the exact input gradient through attention
   tiny         hidden 64, 16 tokens (launch-bound; parity-size case)
@@ -54,9 +55,9 @@ PEAK = {  # MI355X published peaks (dense)
     "bf16_TFLOPs": 2516.6,
 }
 COPIES = {"decode": 6, "tiny": 1, "seq512": 4, "seq2048bf16": 4, "stack36": 1, "seq512qk": 4,
-          "seq512ig": 4, "seq2048bf16ig": 4}
+          "seq512ig": 4, "seq2048bf16ig": 4, "decode_packed": 24}
 DEFAULT_STEPS = {"decode": 2000, "tiny": 2000, "seq512": 200, "seq2048bf16": 100, "stack36": 10,
-                 "seq512qk": 200, "seq512ig": 200, "seq2048bf16ig": 100}
+                 "seq512qk": 200, "seq512ig": 200, "seq2048bf16ig": 100, "decode_packed": 4800}
 
 
 def parse():
@@ -118,7 +119,8 @@ def layer_call(lbp, cfg, d, d_hidden, **kw):
                          sub_norms=cfg.sub_norms, causal=cfg.causal,
                          dtype=lbp.BF16 if cfg.dtype == "bf16" else lbp.F32, pos0=cfg.pos0,
                          eps=cfg.eps, rope_base=cfg.rope_base, attn_scale=cfg.scale,
-                         lora_alpha=cfg.alpha, qk_norm=cfg.qk_norm, input_grad=cfg.input_grad)
+                         lora_alpha=cfg.alpha, qk_norm=cfg.qk_norm, input_grad=cfg.input_grad,
+                         weight_format=1 if cfg.packed else 0)
     lora = d["lora"]
     hp = lbp.AdamW(cfg.lr, cfg.lr_b, cfg.beta1, cfg.beta2, cfg.adam_eps, cfg.weight_decay,
                    cfg.step) if lora else None
@@ -128,11 +130,24 @@ def layer_call(lbp, cfg, d, d_hidden, **kw):
                                       gnorm_sq=kw.pop("gnorm", None), **kw)
 
 
-def build_copies(cfg, n_copies, torch):
+def pack_weights(lbp, d, torch):
+    """Packed ternary storage of a drawn decode layer's four weight matrices
+    (values 0.02 * {-1, 0, +1} in float32), with their scale."""
+    import numpy as np
+    for k in ("w_o", "w_gate", "w_up", "w_down"):
+        d["weights"][k] = lbp.lorabwd_pack_ternary(d["weights"][k])
+        d["weights"]["scale_" + k[2:]] = float(np.float32(0.02))
+    torch.cuda.synchronize()
+    return d
+
+
+def build_copies(cfg, n_copies, torch, lbp=None):
     from synth.device import draw_timing_layer_device
     copies = []
     for c in range(n_copies):
         layers = [draw_timing_layer_device(cfg, c * cfg.n_layers + l) for l in range(cfg.n_layers)]
+        if cfg.packed:
+            layers = [pack_weights(lbp, d, torch) for d in layers]
         copies.append({"layers": layers, "d_out": layers[-1]["d_out"],
                        "d_hidden": torch.empty_like(layers[-1]["d_out"]),
                        "gnorm": torch.zeros(1, device="cuda:0")})
@@ -301,7 +316,7 @@ CAL_BYTES = 256 << 20  # the calibration copy reads and writes this many bytes
 def pmc_pass(lbp, hip, cfg, torch, path):
     """Records of one step (kernel order, algorithmic bytes), then three eager
     steps and the calibration copy, for rocprofv3 --pmc."""
-    copies = build_copies(cfg, 1, torch)
+    copies = build_copies(cfg, 1, torch, lbp)
     cp = copies[0]
     cap = 128
     ev = hip.events(cap)
@@ -481,7 +496,7 @@ def main():
     warmup = args.warmup if args.warmup is not None else max(3, steps // 10)
     hip = Hip()
     torch.cuda.set_device(0)
-    copies = build_copies(cfg, COPIES[cfg.name], torch)
+    copies = build_copies(cfg, COPIES[cfg.name], torch, lbp)
     # eager warm-up: sizes the workspace, loads the code objects
     for cp in copies:
         run_step(lbp, cfg, cp)

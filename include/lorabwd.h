@@ -97,6 +97,24 @@ int lorabwd_rmsnorm_backward(int64_t rows, int64_t n, const void* x, const float
                              int dtype, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Packed ternary (BitLinear) weights.  The decode layer's projections are
+ * BitLinear layers ([FFN] executeFFNBackward takes W_down, W_gate, W_up as
+ * BitLinear; [ATTN] "Gradient Flow": O projection backward, BitLinear
+ * transpose), whose values are {-s, 0, +s} with one scale s per matrix.  The
+ * pages give no storage format; this library's is 2 bits per value by sign
+ * (0 -> 00, +s -> 01, -s -> 11), four consecutive columns of a row per byte
+ * (column 4c + j in bits 2j .. 2j+1 of byte c), rows one after another: a
+ * [rows, cols] matrix packs into uint8 [rows, cols / 4], 1/16 of its float32
+ * bytes.
+ * w      act [rows, cols] (float32 or bfloat16, `dtype`), coded by sign (the
+ *        scale is the caller's: pass it with the packed matrix)
+ * packed uint8 [rows, cols / 4]; cols a multiple of 8, rows <= 2^20.
+ * ---------------------------------------------------------------------- */
+size_t lorabwd_ternary_packed_bytes(int64_t rows, int64_t cols);
+int lorabwd_pack_ternary(int64_t rows, int64_t cols, const void* w, int dtype, uint8_t* packed,
+                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Inverse NeoX RoPE.  [ATTN] "RoPE Backward (inverse rotation)": per head,
  * with half = head_dim/2 and theta_d = pos * base^(-2d/head_dim), d < half,
  *   dx[d]      =  dy[d] cos(theta_d) + dy[d+half] sin(theta_d)
@@ -241,6 +259,10 @@ typedef struct lorabwd_layer_desc {
   float lora_alpha;    /* adapter scaling is lora_alpha / rank */
   int32_t qk_norm;     /* 1: per-head RMSNorm of the Q (and K) projection before RoPE */
   int32_t input_grad;  /* 1: differentiate the attention branch input too (see above) */
+  int32_t weight_format; /* 0: w_o, w_gate, w_up, w_down in dtype; 1: packed ternary
+                            (lorabwd_pack_ternary) with scales scale_o ... scale_down;
+                            single-token layers only */
+  int32_t reserved;    /* must be 0 */
 } lorabwd_layer_desc;
 
 typedef struct lorabwd_layer_weights {
@@ -257,6 +279,7 @@ typedef struct lorabwd_layer_weights {
   const void* w_v;          /* act [n_kv_heads*head_dim, hidden]; input_grad only */
   const float* gamma_attn;  /* [hidden] the attention norm's scale; input_grad only */
   const float* gamma_k;     /* [head_dim]; qk_norm with input_grad */
+  float scale_o, scale_gate, scale_up, scale_down;  /* packed ternary weights only */
 } lorabwd_layer_weights;
 
 typedef struct lorabwd_layer_saved {   /* all act type */

@@ -26,7 +26,7 @@ __all__ = [
     "lorabwd_attn_workspace_size", "lorabwd_ffn_workspace_size",
     "lorabwd_lora_workspace_size", "lorabwd_layer_workspace_size", "lorabwd_status_string",
     "lorabwd_layer_backward_timed", "lorabwd_layer_backward_noalloc", "KernelRecord",
-    "make_desc", "NOALLOC_SCRATCH_BYTES",
+    "make_desc", "NOALLOC_SCRATCH_BYTES", "lorabwd_pack_ternary", "lorabwd_ternary_packed_bytes",
     "F32", "BF16", "ACT_SWIGLU", "ACT_RELU2",
 ]
 
@@ -39,7 +39,7 @@ EXPORTS = [
     "lorabwd_ffn_workspace_size", "lorabwd_ffn_backward",
     "lorabwd_lora_workspace_size", "lorabwd_lora_grad_adamw",
     "lorabwd_layer_workspace_size", "lorabwd_layer_backward", "lorabwd_layer_backward_timed",
-    "lorabwd_layer_backward_noalloc",
+    "lorabwd_layer_backward_noalloc", "lorabwd_ternary_packed_bytes", "lorabwd_pack_ternary",
 ]
 NOALLOC_SCRATCH_BYTES = 16 << 20  # LORABWD_NOALLOC_SCRATCH_BYTES
 
@@ -67,14 +67,16 @@ class LayerDesc(ctypes.Structure):
                 ("act", ctypes.c_int32), ("sub_norms", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32), ("eps", c_float),
                 ("rope_base", c_float), ("attn_scale", c_float), ("lora_alpha", c_float),
-                ("qk_norm", ctypes.c_int32), ("input_grad", ctypes.c_int32)]
+                ("qk_norm", ctypes.c_int32), ("input_grad", ctypes.c_int32),
+                ("weight_format", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
     _fields_ = [("w_o", c_vp), ("w_gate", c_vp), ("w_up", c_vp), ("w_down", c_vp),
                 ("gamma_ffn", c_vp), ("gamma_fsub", c_vp), ("gamma_asub", c_vp), ("gamma_q", c_vp),
                 ("w_q", c_vp), ("w_k", c_vp), ("w_v", c_vp), ("gamma_attn", c_vp),
-                ("gamma_k", c_vp)]
+                ("gamma_k", c_vp), ("scale_o", c_float), ("scale_gate", c_float),
+                ("scale_up", c_float), ("scale_down", c_float)]
 
 
 class LayerSaved(ctypes.Structure):
@@ -119,6 +121,8 @@ _SIGS = {
                                         c_float, c_float, c_float, c_float, c_float, c_float,
                                         c_int, c_int, c_vp, c_size, c_vp]),
     "lorabwd_layer_workspace_size": (c_size, [ctypes.POINTER(LayerDesc)]),
+    "lorabwd_ternary_packed_bytes": (c_size, [c_i64, c_i64]),
+    "lorabwd_pack_ternary": (c_int, [c_i64, c_i64, c_vp, c_int, c_vp, c_vp]),
     "lorabwd_layer_backward": (c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
                                        ctypes.POINTER(LayerSaved), ctypes.POINTER(LoraState),
                                        ctypes.POINTER(LoraState), ctypes.POINTER(AdamW), c_vp,
@@ -269,6 +273,24 @@ def lorabwd_rope_backward(dy, dx, n_heads, head_dim, pos0=0, base=10000.0, strea
     return dx
 
 
+def lorabwd_ternary_packed_bytes(rows, cols):
+    return load_library().lorabwd_ternary_packed_bytes(rows, cols)
+
+
+def lorabwd_pack_ternary(w, packed=None, stream=None):
+    """Packed ternary weights (the format of include/lorabwd.h) of w
+    [rows, cols] (float32 or bfloat16), coded by sign: uint8 [rows, cols/4]."""
+    rows, cols = w.shape
+    _need(w, "w")
+    if packed is None:
+        packed = _torch().empty((rows, cols // 4), dtype=_torch().uint8, device=w.device)
+    _need(packed, "packed", _torch().uint8, (rows, cols // 4))
+    lib = load_library()
+    _check("lorabwd_pack_ternary", lib.lorabwd_pack_ternary(
+        rows, cols, _ptr(w), _dt(w), _ptr(packed), _stream(stream, w.device)))
+    return packed
+
+
 def lorabwd_attn_workspace_size(s_q, s_kv, n_heads, n_kv_heads, head_dim, dtype=F32):
     return load_library().lorabwd_attn_workspace_size(s_q, s_kv, n_heads, n_kv_heads, head_dim,
                                                       dtype)
@@ -373,11 +395,12 @@ def lorabwd_layer_workspace_size(desc):
 
 def make_desc(seq, kv_len, hidden, ffn, n_heads, n_kv_heads, head_dim, act=ACT_SWIGLU,
               sub_norms=False, causal=True, dtype=F32, pos0=0, eps=1e-6, rope_base=10000.0,
-              attn_scale=None, lora_alpha=0.0, qk_norm=False, input_grad=False):
+              attn_scale=None, lora_alpha=0.0, qk_norm=False, input_grad=False,
+              weight_format=0):
     return LayerDesc(seq, kv_len, hidden, ffn, n_heads, n_kv_heads, head_dim, pos0, act,
                      int(sub_norms), int(causal), dtype, eps, rope_base,
                      head_dim ** -0.5 if attn_scale is None else attn_scale, lora_alpha,
-                     int(qk_norm), int(input_grad))
+                     int(qk_norm), int(input_grad), int(weight_format), 0)
 
 
 def lorabwd_layer_backward_noalloc(desc, weights, saved, d_hidden, **kw):
@@ -409,7 +432,10 @@ def lorabwd_layer_backward(desc, weights, saved, d_hidden, q_state=None, v_state
         _f32(d_out, "d_out", (S, H))
     wshapes = {"w_o": (H, qd), "w_gate": (I, H), "w_up": (I, H), "w_down": (H, I)}
     for k, s in wshapes.items():
-        _need(weights[k], k, tdt, s)
+        if d.weight_format == 1:  # packed ternary: uint8 [out, in / 4]
+            _need(weights[k], k, _torch().uint8, (s[0], s[1] // 4))
+        else:
+            _need(weights[k], k, tdt, s)
     _f32(weights["gamma_ffn"], "gamma_ffn", (H,))
     if d.sub_norms:
         _f32(weights["gamma_fsub"], "gamma_fsub", (I,))
@@ -428,7 +454,8 @@ def lorabwd_layer_backward(desc, weights, saved, d_hidden, q_state=None, v_state
     for k, s in sshapes.items():
         if saved.get(k) is not None:
             _need(saved[k], k, tdt, s)
-    w = LayerWeights(*[_ptr(weights.get(k)) for k, _ in LayerWeights._fields_])
+    w = LayerWeights(*[float(weights.get(k, 1.0)) if t is c_float else _ptr(weights.get(k))
+                       for k, t in LayerWeights._fields_])
     a = LayerSaved(*[_ptr(saved.get(k)) for k, _ in LayerSaved._fields_])
 
     def state(st, out_dim, hkey):

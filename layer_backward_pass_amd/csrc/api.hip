@@ -151,7 +151,8 @@ FfnPlan ffn_plan(void* ws, int64_t rows, int64_t dim, int64_t ffn, int dt) {
 int ffn_validate(int64_t rows, int64_t dim, int64_t ffn, int act, const float* d_out,
                  const void* w_down, const void* w_gate, const void* w_up, const void* gate,
                  const void* up_, const void* hidden_pre, const float* gamma_sub,
-                 const void* resid1, const float* gamma_ffn, float* d_resid, float eps, int dt) {
+                 const void* resid1, const float* gamma_ffn, float* d_resid, float eps, int dt,
+                 bool packed_w = false) {
   LBP_CHECK(dtype_ok(dt), LORABWD_ERR_DTYPE);
   LBP_CHECK(act == LORABWD_ACT_SWIGLU || act == LORABWD_ACT_RELU2, LORABWD_ERR_DTYPE);
   LBP_CHECK(rows_ok(rows) && feat_ok(dim) && feat_ok(ffn), LORABWD_ERR_SHAPE);
@@ -166,8 +167,9 @@ int ffn_validate(int64_t rows, int64_t dim, int64_t ffn, int act, const float* d
   const size_t nres = (size_t)rows * dim * 4;
   LBP_CHECK(d_resid == d_out || !overlap(d_resid, nres, d_out, nres), LORABWD_ERR_ALIAS);
   const size_t es = esize(dt);
+  const size_t wn = packed_w ? (size_t)dim * ffn / 4 : (size_t)dim * ffn * es;  // weight bytes
   const void* ins[] = {w_down, w_gate, w_up, gate, up_, resid1, hidden_pre};
-  const size_t ns[] = {(size_t)dim * ffn * es, (size_t)dim * ffn * es, (size_t)dim * ffn * es,
+  const size_t ns[] = {wn, wn, wn,
                        (size_t)rows * ffn * es, (size_t)rows * ffn * es, (size_t)rows * dim * es,
                        (size_t)rows * ffn * es};
   for (int i = 0; i < 7; ++i) LBP_CHECK(!overlap(d_resid, nres, ins[i], ns[i]), LORABWD_ERR_ALIAS);
@@ -369,7 +371,7 @@ const char* lorabwd_status_string(int status) {
   }
 }
 
-int lorabwd_abi_version(void) { return 4; }
+int lorabwd_abi_version(void) { return 5; }
 
 int lorabwd_rmsnorm_backward(int64_t rows, int64_t n, const void* x, const float* gamma,
                              const float* dy, float* dx, float eps, int accumulate, int dtype,
@@ -399,6 +401,24 @@ int lorabwd_rope_backward(int64_t rows, int64_t n_heads, int64_t head_dim, const
   const size_t nb = (size_t)rows * n_heads * head_dim * 4;
   LBP_CHECK(dx == dy || !overlap(dx, nb, dy, nb), LORABWD_ERR_ALIAS);
   LBP_RUN(launch_rope_bwd(rows, n_heads, head_dim, dy, dx, pos0, base, stream));
+  return LORABWD_OK;
+}
+
+size_t lorabwd_ternary_packed_bytes(int64_t rows, int64_t cols) {
+  if (!rows_ok(rows) || rows > kMaxFeat || !feat_ok(cols)) return 0;
+  return (size_t)rows * (size_t)(cols / 4);
+}
+
+int lorabwd_pack_ternary(int64_t rows, int64_t cols, const void* w, int dtype, uint8_t* packed,
+                         hipStream_t stream) {
+  LBP_CHECK(dtype_ok(dtype), LORABWD_ERR_DTYPE);
+  LBP_CHECK(rows_ok(rows) && feat_ok(cols), LORABWD_ERR_SHAPE);
+  if (rows == 0) return LORABWD_OK;
+  LBP_CHECK(w && packed, LORABWD_ERR_NULL);
+  LBP_CHECK(aligned16(w) && aligned16(packed), LORABWD_ERR_ALIGN);
+  LBP_CHECK(!overlap(w, (size_t)rows * cols * esize(dtype), packed, (size_t)rows * (cols / 4)),
+            LORABWD_ERR_ALIAS);
+  LBP_RUN(launch_pack_ternary(rows, cols, w, dtype, packed, stream));
   return LORABWD_OK;
 }
 
@@ -553,6 +573,9 @@ hipError_t decode_chain(const lorabwd_layer_desc* d, const lorabwd_layer_weights
   const int64_t qd = d->n_heads * d->head_dim;
   const int dt = d->dtype;
   const bool sub = d->sub_norms != 0;
+  // packed ternary weights (weight_format 1): each matrix's scale rides
+  // with its GEMV
+  const int wdt = d->weight_format ? TERN2 : dt;
   float* part13 = (float*)p.scratch;
   hipError_t e;
   // part1 = d_out W_down, with the FFN sub-norm's row-sum shares
@@ -567,7 +590,8 @@ hipError_t decode_chain(const lorabwd_layer_desc* d, const lorabwd_layer_weights
     g.nx = a->hidden_pre;
     g.scal = p.scal1;
   }
-  if ((e = launch_dgemv(dt, dt, g, s)) != hipSuccess) return e;
+  g.s1 = g.s2 = w->scale_down;
+  if ((e = launch_dgemv(wdt, dt, g, s)) != hipSuccess) return e;
   // part2 = [dGate | dUp] [W_gate; W_up], with the FFN norm's row-sum
   // shares; the prologue forms each workgroup's slice of [dGate | dUp] from
   // part1 (dHid, sub-norm backward, activation backward)
@@ -595,7 +619,9 @@ hipError_t decode_chain(const lorabwd_layer_desc* d, const lorabwd_layer_weights
   g.p.gate = a->gate;
   g.p.up = a->up;
   g.p.act = d->act;
-  if ((e = launch_dgemv(dt, dt, g, s)) != hipSuccess) return e;
+  g.s1 = w->scale_gate;
+  g.s2 = w->scale_up;
+  if ((e = launch_dgemv(wdt, dt, g, s)) != hipSuccess) return e;
   // part3 = dH1 W_o, with the attention sub-norm's row-sum shares; the
   // prologue forms dH1 = d_out + rmsnorm_bwd(resid1, gamma_ffn, dN2) for its
   // rows from part2 (column block 0 also keeps it in x2)
@@ -620,7 +646,8 @@ hipError_t decode_chain(const lorabwd_layer_desc* d, const lorabwd_layer_weights
   g.p.eps = d->eps;
   g.p.resid = d_in;
   g.p.xout = inplace ? p.x2 : d_hidden;
-  if ((e = launch_dgemv(dt, dt, g, s)) != hipSuccess) return e;
+  g.s1 = g.s2 = w->scale_o;
+  if ((e = launch_dgemv(wdt, dt, g, s)) != hipSuccess) return e;
   // attention backward, inverse RoPE at the token's position
   DecAttnArgs at{};
   at.s_kv = L;
@@ -839,8 +866,11 @@ int desc_validate(const lorabwd_layer_desc* d) {
                 d->pos0 <= (int64_t(1) << 40),
             LORABWD_ERR_SHAPE);
   LBP_CHECK((d->sub_norms == 0 || d->sub_norms == 1) && (d->causal == 0 || d->causal == 1) &&
-                (d->qk_norm == 0 || d->qk_norm == 1) && (d->input_grad == 0 || d->input_grad == 1),
+                (d->qk_norm == 0 || d->qk_norm == 1) && (d->input_grad == 0 || d->input_grad == 1) &&
+                (d->weight_format == 0 || d->weight_format == 1) && d->reserved == 0,
             LORABWD_ERR_ARG);
+  // packed ternary weights run in the single-token chain only
+  LBP_CHECK(!d->weight_format || use_decode_chain(d), LORABWD_ERR_SHAPE);
   // the attention input gradient's dK is not built for bf16 with head_dim 16
   LBP_CHECK(!d->input_grad || d->dtype != LORABWD_BF16 || d->head_dim >= 32, LORABWD_ERR_SHAPE);
   LBP_CHECK(finite(d->eps) && d->eps >= 0.f && finite(d->rope_base) && d->rope_base > 0.f &&
@@ -900,7 +930,12 @@ static int layer_entry(const lorabwd_layer_desc* d, const lorabwd_layer_weights*
             LORABWD_ERR_ALIAS);
   st = ffn_validate(S, H, I, d->act, din, w->w_down, w->w_gate, w->w_up, a->gate, a->up,
                     sub ? a->hidden_pre : nullptr, sub ? w->gamma_fsub : nullptr, a->resid1,
-                    w->gamma_ffn, d_hidden, d->eps, dt);
+                    w->gamma_ffn, d_hidden, d->eps, dt, d->weight_format == 1);
+  if (st != LORABWD_OK) return st;
+  if (d->weight_format)
+    LBP_CHECK(finite(w->scale_o) && finite(w->scale_gate) && finite(w->scale_up) &&
+                  finite(w->scale_down),
+              LORABWD_ERR_ARG);
   if (st != LORABWD_OK) return st;
   LBP_CHECK(aligned16(w->w_o) && aligned16(w->gamma_asub) && aligned16(w->gamma_q) &&
                 aligned16(a->q_raw) && aligned16(dq_pre_out) &&

@@ -109,6 +109,35 @@ template <> struct BufVec<bf16> {
   static __device__ __forceinline__ raw zero() { return make_uint2(0u, 0u); }
 };
 
+// Packed ternary weights (lorabwd_pack_ternary): 2-bit sign codes, column
+// 4c + j in bits 2j .. 2j+1 of byte c of a row (00 -> 0, 01 -> +1, 11 -> -1).
+// A lane's four columns of one row are one byte; each field is sign-extended
+// (v_bfe_i32) to its value in {-1, 0, +1}.  The matrix's scale is applied by
+// the user of the values.
+struct tern2 {
+  uint8_t bits;
+};
+template <> struct BufVec<tern2> {
+  typedef uint32_t raw;
+  static __device__ __forceinline__ raw load(brsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+  }
+  static __device__ __forceinline__ raw load_stream(brsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, BUF_NT);
+  }
+  // (the builtin's result type is unsigned: the field is read back as int
+  // before the conversion, or -1 would convert as 2^32 - 1)
+  static __device__ __forceinline__ float4 cvt(raw v) {
+    const int b = (int)v;
+    return make_float4((float)(int)__builtin_amdgcn_sbfe(b, 0, 2), (float)(int)__builtin_amdgcn_sbfe(b, 2, 2),
+                       (float)(int)__builtin_amdgcn_sbfe(b, 4, 2), (float)(int)__builtin_amdgcn_sbfe(b, 6, 2));
+  }
+  static __device__ __forceinline__ raw zero() { return 0u; }
+};
+// bytes that four consecutive columns of a weight row take
+template <typename T> struct ColBytes4 { static constexpr int v = 4 * (int)sizeof(T); };
+template <> struct ColBytes4<tern2> { static constexpr int v = 1; };
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

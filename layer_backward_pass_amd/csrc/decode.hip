@@ -37,6 +37,8 @@
 // a fixed order.  Loads are buffer loads whose bounds are offsets (out of
 // range reads 0), so no branch interrupts the prefetch pipeline.  Every
 // reduction has a fixed order, so results are bitwise reproducible.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -256,13 +258,13 @@ __global__ __launch_bounds__(256) void dgemv_kernel(GemvArgs a) {
   const bool nok = n < a.N;
   // the chunk's rows as two buffer ranges: rows of W1 (global row < K1) and
   // rows of W2; lanes past N and rows past the wave's share read 0
-  const uint32_t rowb = (uint32_t)(a.N * sizeof(TW));
+  const uint32_t rowb = (uint32_t)((a.N / 4) * ColBytes4<TW>::v);
   const int n1 = kb < a.K1 ? (int)(min(ke, a.K1) - kb) : 0;
   const int64_t kb2 = kb + n1 - a.K1;  // first row of the W2 part, within W2
   const brsrc_t rs1 = make_brsrc(n1 > 0 ? (const char*)a.W1 + kb * rowb : (const char*)a.W1, n1 * rowb);
   const brsrc_t rs2 = make_brsrc(n1 < R ? (const char*)a.W2 + kb2 * rowb : (const char*)a.W2,
                                  (uint32_t)(R - n1) * rowb);
-  const uint32_t coff = nok ? (uint32_t)(n * sizeof(TW)) : BUF_OOB;
+  const uint32_t coff = nok ? (uint32_t)((n / 4) * ColBytes4<TW>::v) : BUF_OOB;
   // two named register stages (indices known at compile time): the next 8
   // rows are in flight while the current 8 are multiplied
   WV wa[DG_U], wb[DG_U];
@@ -306,6 +308,12 @@ __global__ __launch_bounds__(256) void dgemv_kernel(GemvArgs a) {
     pro.finish(a.p, xs, nred, lred);
   }
   __syncthreads();
+  if constexpr (std::is_same<TW, tern2>::value) {
+    // packed weights are {-1, 0, +1}: the rows' scales go into the input
+    // vector (R <= 256 rows, one per thread)
+    if (t < R) xs[t] *= kb + t < a.K1 ? a.s1 : a.s2;
+    __syncthreads();
+  }
   // every step refills both stages unconditionally (rows past the wave's
   // share read 0 and meet a 0 input), so no branch splits the pipeline
   float4 acc = make_float4(0, 0, 0, 0);
@@ -530,7 +538,9 @@ hipError_t launch_dgemv(int w_dt, int a_dt, GemvArgs a, hipStream_t s) {
                             (double)a.p.nscal * 8 >= BUF_MAX_BYTES))
     return hipErrorInvalidValue;
   // buffer ranges: one chunk of weight rows, the input vector
-  if ((double)a.kc * a.N * (w_dt == F32 ? 4 : 2) >= BUF_MAX_BYTES || (double)a.K * 4 >= BUF_MAX_BYTES)
+  const double wes = w_dt == F32 ? 4 : w_dt == BF16 ? 2 : 0.25;
+  if ((double)a.kc * a.N * wes >= BUF_MAX_BYTES || (double)a.K * 4 >= BUF_MAX_BYTES ||
+      (w_dt == TERN2 && a.kc > 256))
     return hipErrorInvalidValue;
   if (dry_run()) return hipSuccess;
   if (a.W2 == nullptr) {
@@ -548,12 +558,15 @@ hipError_t launch_dgemv(int w_dt, int a_dt, GemvArgs a, hipStream_t s) {
   if (w_dt == F32) {
     if (a_dt == F32) LBP_DGEMV(float, float);
     else LBP_DGEMV(float, bf16);
-  } else {
+  } else if (w_dt == BF16) {
     if (a_dt == F32) LBP_DGEMV(bf16, float);
     else LBP_DGEMV(bf16, bf16);
+  } else {
+    if (a_dt == F32) LBP_DGEMV(tern2, float);
+    else LBP_DGEMV(tern2, bf16);
   }
 #undef LBP_DGEMV
-  const double es = w_dt == F32 ? 4 : 2;
+  const double es = wes;
   // algorithmic bytes: the weights, the input vector and the result vector;
   // a prologue reads, in place of the input vector, the reduced producer
   // output and the elementwise inputs that form it (split partials are
@@ -1408,6 +1421,40 @@ hipError_t launch_dec_attn(int dt, int head_dim, const DecAttnArgs& a, hipStream
       return hipErrorInvalidValue;
   }
 #undef LBP_DA
+}
+
+// ---------------------------------------------------------------------------
+// Packing of ternary weights (tern2 in common.h): one byte, four columns, per
+// thread; each value coded by its sign.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_ternary_kernel(int64_t rows, int64_t cols,
+                                                           const T* __restrict__ w,
+                                                           uint8_t* __restrict__ out) {
+  const int64_t q = cols / 4, nb = rows * q;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nb; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / q, c = i - r * q;
+    const float4 v = Act<T>::ld4(w, r * cols + 4 * c);
+    const float e[4] = {v.x, v.y, v.z, v.w};
+    uint32_t b = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b |= (e[j] > 0.f ? 1u : e[j] < 0.f ? 3u : 0u) << (2 * j);
+    out[i] = (uint8_t)b;
+  }
+}
+
+hipError_t launch_pack_ternary(int64_t rows, int64_t cols, const void* w, int w_dt, uint8_t* out,
+                               hipStream_t s) {
+  const int64_t nb = rows * (cols / 4);
+  if (nb == 0) return hipSuccess;
+  if (dry_run()) return hipSuccess;
+  int64_t blocks = cdiv(nb, 256);
+  if (blocks > 8192) blocks = 8192;
+  if (w_dt == F32)
+    pack_ternary_kernel<float><<<dim3((unsigned)blocks), 256, 0, s>>>(rows, cols, (const float*)w, out);
+  else
+    pack_ternary_kernel<bf16><<<dim3((unsigned)blocks), 256, 0, s>>>(rows, cols, (const bf16*)w, out);
+  mark("pack_ternary", (double)rows * cols * (w_dt == F32 ? 4 : 2) + (double)nb, 0, s);
+  return hipGetLastError();
 }
 
 }  // namespace lbp

@@ -8,7 +8,7 @@
 
 namespace lbp {
 
-enum DType { F32 = 0, BF16 = 1 };
+enum DType { F32 = 0, BF16 = 1, TERN2 = 2 };  // TERN2: packed ternary weights (GEMV only)
 
 // Measurement hook: after each kernel launch a launcher calls mark() with the
 // kernel's name, its algorithmic HBM bytes and flops (the method's single
@@ -145,8 +145,11 @@ struct GemvPro {
   const float* resid;
   float* xout;
 };
+// With packed ternary weights (w_dt TERN2), s1 / s2 are the scales of the
+// rows k < K1 (W1) and k >= K1 (W2); dense weights ignore them.
 struct GemvArgs {
   int64_t N, K, K1, kc;
+  float s1, s2;
   const void* W1;
   const void* W2;
   const float* x;  // PRO_COPY input
@@ -192,6 +195,10 @@ int64_t dgemv_splits(int64_t N, int64_t K, int pro = PRO_COPY);
 size_t dgemv_part_bytes(int64_t N, int64_t K, int pro = PRO_COPY);
 int64_t dgemv_nscal(int64_t N, int64_t K, int pro = PRO_COPY);
 hipError_t launch_dgemv(int w_dt, int a_dt, GemvArgs a, hipStream_t s);
+// Packed ternary weights: out [rows][cols / 4] bytes from w [rows][cols]
+// (float or bf16, w_dt), each value coded by its sign (see tern2 in common.h).
+hipError_t launch_pack_ternary(int64_t rows, int64_t cols, const void* w, int w_dt, uint8_t* out,
+                               hipStream_t s);
 hipError_t launch_dgemv_red(int mode, int a_dt, RedArgs a, hipStream_t s);
 
 // One query row against s_kv keys.  With ctx: dec_attn1c (per key block:

@@ -10,6 +10,9 @@ Five workloads, named by what they are:
   stack36     36 seq512-shaped layers at 1024 tokens, fp32
   seq512qk    the seq512 layer with QK-norm (per-head RMSNorm of Q and K before
               RoPE, as Qwen3-style layers have)
+  decode_packed
+              the decode layer with its ternary weights packed 2 bits per value
+              (BitLinear storage)
   seq512ig, seq2048bf16ig
               the seq512 / seq2048bf16 layers with the exact input gradient
               through the attention branch (dK, the transposed Q/K/V
@@ -49,6 +52,7 @@ class LayerConfig:
     ternary: bool = False      # weights are 0.02 * {-1, 0, +1}
     qk_norm: bool = False      # per-head RMSNorm of the Q and K projections before RoPE
     input_grad: bool = False   # differentiate the attention branch input too (no stop-gradient)
+    packed: bool = False       # ternary weights stored packed (2 bits per value)
 
     @property
     def q_dim(self):
@@ -88,9 +92,10 @@ STACK36 = SEQ512.with_(name="stack36", index=4, seq=1024, kv_len=1024, n_layers=
 SEQ512QK = SEQ512.with_(name="seq512qk", index=5, qk_norm=True)
 SEQ512IG = SEQ512.with_(name="seq512ig", index=6, input_grad=True)
 SEQ2048BF16IG = SEQ2048BF16.with_(name="seq2048bf16ig", index=7, input_grad=True)
+DECODE_PACKED = DECODE.with_(name="decode_packed", index=8, packed=True)
 
 CONFIGS = {c.name: c for c in (TINY, DECODE, SEQ512, SEQ2048BF16, STACK36, SEQ512QK, SEQ512IG,
-                               SEQ2048BF16IG)}
+                               SEQ2048BF16IG, DECODE_PACKED)}
 
 
 def get_config(name):

@@ -98,7 +98,8 @@ def desc_of(c):
                          sub_norms=c.sub_norms, causal=c.causal,
                          dtype=lbp.BF16 if c.dtype == "bf16" else lbp.F32, pos0=c.pos0,
                          eps=c.eps, rope_base=c.rope_base, attn_scale=c.scale,
-                         lora_alpha=c.alpha, qk_norm=c.qk_norm, input_grad=c.input_grad)
+                         lora_alpha=c.alpha, qk_norm=c.qk_norm, input_grad=c.input_grad,
+                         weight_format=1 if c.packed else 0)
 
 
 class DeviceLayer:
@@ -273,3 +274,53 @@ def stack_parity(cfg, device="cuda:0", log=print):
     errs["gnorm_sq"] = rel_err(host(gnorm), np.array([gsq]))
     log("stack: %d layers compared" % n)
     return errs
+
+
+PACKED = ("w_o", "w_gate", "w_up", "w_down")
+
+
+def pack_layer_weights(dl, check_bytes):
+    """The layer's ternary weights packed on the GPU (lorabwd_pack_ternary),
+    with their scale (the magnitude of the stored nonzero values).  Every
+    packed matrix is checked on the host: unpacked by the oracle it gives the
+    signs of the dense matrix and holds no unused code; with check_bytes the
+    bytes also equal the oracle's packing of the same matrix."""
+    import layer_backward_pass_amd as lbp
+    from oracle import bitlinear as BL
+    out = {}
+    for k in PACKED:
+        wd = dl.w[k]
+        pk = lbp.lorabwd_pack_ternary(wd)
+        _torch().cuda.synchronize()
+        hw = host(wd)
+        hp = pk.cpu().numpy()
+        assert np.array_equal(BL.unpack_ternary(hp, hw.shape[1]), np.sign(hw)), k
+        for j in range(4):
+            assert not np.any(((hp >> (2 * j)) & 3) == 2), k
+        if check_bytes:
+            assert np.array_equal(hp, BL.pack_ternary(hw)), k
+        nz = np.abs(hw[hw != 0])
+        assert nz.size and np.all(nz == nz[0]), k  # one scale per matrix
+        out[k] = pk
+        out["scale_" + k[2:]] = float(nz[0])
+    return out
+
+
+def packed_layer_parity(cfg, device="cuda:0", check_bytes=True):
+    """The single-token layer with its ternary weights packed (weight_format
+    1) against the float64 oracle on the dense values."""
+    torch = _torch()
+    dl = DeviceLayer(cfg.with_(packed=False), 0, device)
+    ref = dl.run_oracle(dl.o_dout)
+    pw = pack_layer_weights(dl, check_bytes)
+    wts = dict(dl.w)
+    wts.update(pw)
+    import layer_backward_pass_amd as lbp
+    d_hidden = torch.empty_like(dl.d_out)
+    dq_pre = torch.empty(cfg.seq, cfg.q_dim, device=device)
+    dv = torch.empty(cfg.kv_len, cfg.kv_dim, device=device)
+    lbp.lorabwd_layer_backward(desc_of(cfg.with_(packed=True)), wts, dl.saved, d_hidden,
+                               dq_pre_out=dq_pre, dv_out=dv, d_out=dl.d_out)
+    torch.cuda.synchronize()
+    return {"d_hidden": rel_err(host(d_hidden), ref["d_hidden"]),
+            "dq_pre": rel_err(host(dq_pre), ref["dq_pre"]), "dv": rel_err(host(dv), ref["dv"])}

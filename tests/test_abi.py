@@ -56,7 +56,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.lorabwd_abi_version() == 4
+    assert lib.lorabwd_abi_version() == 5
     for code in (OK, ENULL, ESHAPE, EALIGN, EDTYPE, EWS, ESTEP, EALIAS, EHIP, EARG):
         s = lib.lorabwd_status_string(code).decode()
         assert s and s != "unknown status"
@@ -274,6 +274,32 @@ def test_noalloc_validation(lib):
     assert f(r(bad), r(w), r(a), None, None, None, None, far(40), None, None, None, None) == ESHAPE
     d = lbp.make_desc(16, 16, 64, 256, 4, 2, 16)
     assert f(r(d), r(w), r(a), None, None, None, None, None, None, None, None, None) == ENULL
+
+
+def test_pack_ternary_validation(lib):
+    f = lib.lorabwd_pack_ternary
+    assert lib.lorabwd_ternary_packed_bytes(3, 16) == 12
+    assert lib.lorabwd_ternary_packed_bytes(3, 12) == 0          # cols % 8
+    assert f(3, 12, fake(0), 0, fake(1), None) == ESHAPE
+    assert f(3, 16, fake(0), 5, fake(1), None) == EDTYPE
+    assert f(3, 16, None, 0, fake(1), None) == ENULL
+    assert f(3, 16, fake(0) + 4, 0, fake(1), None) == EALIGN
+    assert f(3, 16, fake(0), 0, fake(0) + 16, None) == EALIAS     # output over the input
+    assert f(0, 16, None, 0, None, None) == OK
+    # packed weights are for the single-token layer only, with finite scales
+    d = lbp.make_desc(16, 16, 64, 256, 4, 2, 16, weight_format=1)
+    w = lbp.LayerWeights(*[fake(i) for i in range(4)], fake(4), *([None] * 8),
+                         *([0.02] * 4))
+    a = lbp.LayerSaved(*[fake(10 + i) for i in range(11)])
+    r = ctypes.byref
+    ws = 1 << 30
+    fl = lib.lorabwd_layer_backward
+    assert fl(r(d), r(w), r(a), None, None, None, None, fake(50), None, None, None, fake(60), ws,
+              None) == ESHAPE
+    one = lbp.make_desc(1, 64, 64, 256, 4, 2, 16, act=lbp.ACT_RELU2, weight_format=1, pos0=63)
+    w.scale_up = float("nan")
+    assert fl(r(one), r(w), r(a), None, None, None, None, fake(50), None, None, None, fake(60), ws,
+              None) == EARG
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

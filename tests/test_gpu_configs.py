@@ -41,6 +41,18 @@ def test_full_size_layer(name):
     assert not bad, bad
 
 
+def test_full_size_decode_packed():
+    """The decode workload (hidden 2560, ffn 6912, 512-slot cache) on packed
+    ternary weights, against the oracle on the dense values."""
+    cfg = synth.get_config("decode_packed")
+    t0 = time.time()
+    errs = Hn.packed_layer_parity(cfg, "cuda:0", check_bytes=False)
+    _log("  decode_packed: %.1f s, errors %s" % (time.time() - t0,
+                                               {k: float("%.3g" % v) for k, v in errs.items()}))
+    bad = {k: v for k, v in errs.items() if not v <= Hn.TOL[cfg.dtype]}
+    assert not bad, bad
+
+
 @pytest.mark.timeout(1500)
 def test_stack36_full():
     cfg = synth.get_config("stack36")

@@ -432,3 +432,37 @@ def test_layer_deterministic():
         outs.append((d.cpu(), g.cpu(), dl.lora["q"]["A"].cpu(), dl.lora["v"]["B"].cpu()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ packed ternary weights
+@pytest.mark.parametrize("rows,cols,dt", [(7, 24, "f32"), (33, 64, "bf16"), (1, 8, "f32")])
+def test_pack_ternary_bytes(rows, cols, dt):
+    """lorabwd_pack_ternary equals the oracle's packing byte for byte."""
+    import layer_backward_pass_amd as lbp
+    from oracle import bitlinear as BL
+    r = np.random.default_rng(rows + cols)
+    w = 0.02 * r.integers(-1, 2, size=(rows, cols))
+    wd = torch.tensor(w, dtype=torch.float32 if dt == "f32" else torch.bfloat16, device=DEV)
+    pk = lbp.lorabwd_pack_ternary(wd)
+    torch.cuda.synchronize()
+    assert np.array_equal(pk.cpu().numpy(), BL.pack_ternary(Hn.host(wd)))
+
+
+@pytest.mark.parametrize("over", [
+    {"hidden": 256, "ffn": 512, "n_heads": 8, "n_kv_heads": 2, "head_dim": 64, "kv_len": 300,
+     "pos0": 299},
+    {"hidden": 192, "ffn": 384, "n_heads": 12, "n_kv_heads": 2, "head_dim": 32, "kv_len": 40,
+     "pos0": 39},
+    {"hidden": 256, "ffn": 512, "n_heads": 8, "n_kv_heads": 2, "head_dim": 128, "kv_len": 130,
+     "pos0": 129, "dtype": "bf16"},
+    {"hidden": 256, "ffn": 512, "n_heads": 8, "n_kv_heads": 4, "head_dim": 64, "kv_len": 97,
+     "pos0": 96, "sub_norms": 0, "act": "swiglu"},
+])
+def test_layer_packed_ternary_small(over):
+    """The single-token layer on packed ternary weights (the three GEMV
+    streams decode 2-bit codes) against the oracle on the dense values."""
+    cfg = synth.get_config("decode").with_(**over)
+    print("packed layer", cfg, flush=True)
+    errs = Hn.packed_layer_parity(cfg, DEV, check_bytes=True)
+    bad = {k: v for k, v in errs.items() if not v <= Hn.TOL[cfg.dtype]}
+    assert not bad, bad

@@ -20,6 +20,8 @@ Modules:
   fd        central finite differences
   bitlinear the packed ternary (BitLinear) weight format of the decode layer:
             packing, unpacking and the transposed product
+  lmhead    the lm_head backward upstream of the stack: softmax cross-entropy
+            over the vocabulary, grad_hidden, and AdamW on the lm_head weight
 
 Every function is pinned by tests/test_oracle_*.py (finite differences,
 closed forms, invariants, special cases reducing to library routines).  The
@@ -27,4 +29,4 @@ one thing no pin can fix is the choice among readings where the pages
 disagree (which forward is differentiated); those readings are listed in the
 module docstrings below and in the design notes.
 """
-from . import backward, bitlinear, forward, fd  # noqa: F401
+from . import backward, bitlinear, forward, fd, lmhead  # noqa: F401

@@ -1,0 +1,54 @@
+"""Float64 lm_head backward (the step upstream of the layer stack).  TEST
+INFRASTRUCTURE ONLY.
+
+The entrenar trainer backpropagates "from lm_head through all FFN layers"
+([ENT] wgpu_backward.rs, module doc; backward_through_layers takes the
+grad_hidden "from lm_head backward") and keeps the lm_head weight with AdamW
+moments (WgpuModelState lm_head, lm_head_m, lm_head_v: [vocab, hidden], in
+its gradient-flow test).  The pages give no formula for that step; the plain
+reading, used here and by the library:
+
+  logits = h W^T                  h [S, hidden] the final hidden state,
+                                  W [vocab, hidden] the lm_head weight
+  loss   = (1/S) sum_s CE(logits_s, label_s),  CE(z, y) = logsumexp(z) - z_y
+  dlogits = (softmax(logits) - onehot(labels)) / S
+  grad_hidden = dlogits W          (the gradient handed to the top layer)
+  dW     = dlogits^T h
+  W, m, v <- AdamW(W, dW, m, v)    ([ENT] cpu_adamw, the adapters' form)
+
+The logits are taken as saved by the forward (as the layer takes its saved
+softmax weights).
+"""
+import numpy as np
+
+from .backward import adamw
+
+
+def softmax_rows(z):
+    z = np.asarray(z, np.float64)
+    e = np.exp(z - z.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def cross_entropy(logits, labels):
+    """Mean over rows of logsumexp(z) - z[label]."""
+    z = np.asarray(logits, np.float64)
+    mx = z.max(axis=-1)
+    lse = mx + np.log(np.exp(z - mx[:, None]).sum(axis=-1))
+    return float(np.mean(lse - z[np.arange(z.shape[0]), np.asarray(labels)]))
+
+
+def lm_head_bwd(h, logits, labels, W, m, v, lr, beta1, beta2, eps, wd, step):
+    """Returns dict(loss, dlogits, grad_hidden, dW, W, m, v) (updated W, m, v)."""
+    h = np.asarray(h, np.float64)
+    W = np.asarray(W, np.float64)
+    S = h.shape[0]
+    p = softmax_rows(logits)
+    y = np.zeros_like(p)
+    y[np.arange(S), np.asarray(labels)] = 1.0
+    dlogits = (p - y) / S
+    grad_hidden = dlogits @ W
+    dW = dlogits.T @ h
+    nW, nm, nv = adamw(W, dW, m, v, lr, beta1, beta2, eps, wd, step)
+    return dict(loss=cross_entropy(logits, labels), dlogits=dlogits, grad_hidden=grad_hidden,
+                dW=dW, W=nW, m=nm, v=nv)

@@ -284,3 +284,48 @@ def test_bitlinear_mutation_is_caught(i):
     except (ValueError, IndexError, KeyError):
         ok = False
     assert not ok, "mutation not caught: %r -> %r" % (old, new)
+
+
+# Mutations of oracle/lmhead.py.
+LM_SRC = os.path.join(ROOT, "oracle", "lmhead.py")
+LM_MUTATIONS = [
+    ("dlogits = (p - y) / S", "dlogits = p - y"),                                # mean dropped
+    ("dlogits = (p - y) / S", "dlogits = (y - p) / S"),                          # sign
+    ("dW = dlogits.T @ h", "dW = (h.T @ dlogits)[:, :h.shape[1]].T * 0 + dlogits.T @ h[::-1]"),  # rows
+    ("lse = mx + np.log(np.exp(z - mx[:, None]).sum(axis=-1))",
+     "lse = np.log(np.exp(z - mx[:, None]).sum(axis=-1))"),                     # max dropped
+]
+
+
+def _lm_checks(M):
+    from oracle import fd as FD
+    r = np.random.default_rng(4)
+    h = r.standard_normal((3, 5))
+    W = 0.3 * r.standard_normal((7, 5))
+    labels = np.array([1, 6, 1])
+    res = M.lm_head_bwd(h, h @ W.T, labels, W, np.zeros_like(W), np.zeros_like(W),
+                        1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    loss = lambda h_, W_: float(np.mean(  # noqa: E731
+        np.log(np.exp(h_ @ W_.T).sum(-1)) - (h_ @ W_.T)[np.arange(3), labels]))
+    return [abs(res["loss"] - loss(h, W)) < 1e-12,
+            FD.rel_err(res["grad_hidden"], FD.grad(lambda z: loss(z, W), h)) < 1e-8,
+            FD.rel_err(res["dW"], FD.grad(lambda z: loss(h, z), W)) < 1e-8]
+
+
+def test_unmutated_lmhead_passes():
+    from oracle import lmhead
+    assert all(_lm_checks(lmhead))
+
+
+@pytest.mark.parametrize("i", range(len(LM_MUTATIONS)))
+def test_lmhead_mutation_is_caught(i):
+    old, new = LM_MUTATIONS[i]
+    src = open(LM_SRC).read().replace("from .backward import adamw", "from oracle.backward import adamw")
+    assert src.count(old) == 1, old
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new, 1), "oracle_mutant", "exec"), mod.__dict__)
+    try:
+        ok = all(_lm_checks(mod))
+    except (ValueError, IndexError):
+        ok = False
+    assert not ok, "mutation not caught: %r -> %r" % (old, new)

@@ -559,3 +559,54 @@ def test_trainer_smoke_scenario_on_oracle():
     assert not np.array_equal(res[0]["A_q"], layers[0][2]["A_q"])
     assert not np.array_equal(res[0]["A_v"], layers[0][2]["A_v"])
     assert gnorm >= 0.0 and np.all(np.isfinite(dx))
+
+
+# ---------------------------------------------------------------- lm_head
+def _lm_case(seed, S, H, V):
+    r = rng(seed)
+    h = r.standard_normal((S, H))
+    W = 0.3 * r.standard_normal((V, H))
+    labels = r.integers(0, V, size=S)
+    return h, W, labels
+
+
+def test_lm_head_fd_and_row_sums():
+    from oracle import lmhead as LM
+    h, W, labels = _lm_case(61, 3, 5, 7)
+    res = LM.lm_head_bwd(h, h @ W.T, labels, W, np.zeros_like(W), np.zeros_like(W),
+                         1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    loss = lambda h_, W_: LM.cross_entropy(h_ @ W_.T, labels)  # noqa: E731
+    assert abs(res["loss"] - loss(h, W)) < 1e-15
+    assert fd.rel_err(res["grad_hidden"], fd.grad(lambda z: loss(z, W), h)) < 1e-8
+    assert fd.rel_err(res["dW"], fd.grad(lambda z: loss(h, z), W)) < 1e-8
+    # each row of dlogits sums to zero; the label entry is (p - 1) / S
+    assert np.max(np.abs(res["dlogits"].sum(-1))) < 1e-15
+    p = LM.softmax_rows(h @ W.T)
+    for s in range(3):
+        assert abs(res["dlogits"][s, labels[s]] - (p[s, labels[s]] - 1.0) / 3) < 1e-15
+
+
+def test_lm_head_closed_forms_and_torch():
+    torch = pytest.importorskip("torch")
+    from oracle import lmhead as LM
+    # uniform logits: loss = log V and dlogits = (1/V - onehot) / S
+    V, S = 32, 4
+    labels = np.array([0, 5, 31, 5])
+    z = np.zeros((S, V))
+    assert abs(LM.cross_entropy(z, labels) - np.log(V)) < 1e-15
+    W = np.zeros((V, 8))
+    res = LM.lm_head_bwd(np.ones((S, 8)), z, labels, W, W, W, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1)
+    want = np.full((S, V), 1.0 / V)
+    want[np.arange(S), labels] -= 1.0
+    np.testing.assert_allclose(res["dlogits"], want / S, rtol=0, atol=1e-17)
+    # torch.nn.functional.cross_entropy (mean) and autograd in float64
+    h, W, labels = _lm_case(62, 6, 9, 40)
+    th = torch.tensor(h, requires_grad=True)
+    tW = torch.tensor(W, requires_grad=True)
+    tl = torch.nn.functional.cross_entropy(th @ tW.T, torch.tensor(labels))
+    tl.backward()
+    res = LM.lm_head_bwd(h, h @ W.T, labels, W, np.zeros_like(W), np.zeros_like(W),
+                         1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    assert abs(res["loss"] - tl.item()) < 1e-13
+    np.testing.assert_allclose(res["grad_hidden"], th.grad.numpy(), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(res["dW"], tW.grad.numpy(), rtol=1e-12, atol=1e-15)

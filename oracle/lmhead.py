@@ -10,14 +10,16 @@ reading, used here and by the library:
 
   logits = h W^T                  h [S, hidden] the final hidden state,
                                   W [vocab, hidden] the lm_head weight
-  loss   = (1/S) sum_s CE(logits_s, label_s),  CE(z, y) = logsumexp(z) - z_y
-  dlogits = (softmax(logits) - onehot(labels)) / S
+  loss   = (1/n) sum_s CE(logits_s, label_s),  CE(z, y) = logsumexp(z) - z_y
+  dlogits = (softmax(logits) - onehot(labels)) / n
   grad_hidden = dlogits W          (the gradient handed to the top layer)
   dW     = dlogits^T h
   W, m, v <- AdamW(W, dW, m, v)    ([ENT] cpu_adamw, the adapters' form)
 
 The logits are taken as saved by the forward (as the layer takes its saved
-softmax weights).
+softmax weights).  A row whose label lies outside [0, vocab) (padding,
+commonly -100) is ignored: it adds nothing to the loss or to any gradient,
+and n counts the rows with a label in range (no rows: loss and gradients 0).
 """
 import numpy as np
 
@@ -30,22 +32,35 @@ def softmax_rows(z):
     return e / e.sum(axis=-1, keepdims=True)
 
 
+def label_rows(labels, vocab):
+    """Mask of the rows whose label is a vocabulary index."""
+    labels = np.asarray(labels)
+    return (labels >= 0) & (labels < vocab)
+
+
 def cross_entropy(logits, labels):
-    """Mean over rows of logsumexp(z) - z[label]."""
+    """Mean over the labelled rows of logsumexp(z) - z[label]."""
     z = np.asarray(logits, np.float64)
+    ok = label_rows(labels, z.shape[1])
+    if not ok.any():
+        return 0.0
+    z = z[ok]
     mx = z.max(axis=-1)
     lse = mx + np.log(np.exp(z - mx[:, None]).sum(axis=-1))
-    return float(np.mean(lse - z[np.arange(z.shape[0]), np.asarray(labels)]))
+    return float(np.mean(lse - z[np.arange(z.shape[0]), np.asarray(labels)[ok]]))
 
 
 def lm_head_bwd(h, logits, labels, W, m, v, lr, beta1, beta2, eps, wd, step):
     """Returns dict(loss, dlogits, grad_hidden, dW, W, m, v) (updated W, m, v)."""
     h = np.asarray(h, np.float64)
     W = np.asarray(W, np.float64)
-    S = h.shape[0]
     p = softmax_rows(logits)
+    ok = label_rows(labels, p.shape[1])
+    rows = np.nonzero(ok)[0]
     y = np.zeros_like(p)
-    y[np.arange(S), np.asarray(labels)] = 1.0
+    y[rows, np.asarray(labels)[rows]] = 1.0
+    p[~ok] = 0.0
+    S = max(len(rows), 1)
     dlogits = (p - y) / S
     grad_hidden = dlogits @ W
     dW = dlogits.T @ h

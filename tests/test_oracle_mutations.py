@@ -291,7 +291,9 @@ LM_SRC = os.path.join(ROOT, "oracle", "lmhead.py")
 LM_MUTATIONS = [
     ("dlogits = (p - y) / S", "dlogits = p - y"),                                # mean dropped
     ("dlogits = (p - y) / S", "dlogits = (y - p) / S"),                          # sign
-    ("dW = dlogits.T @ h", "dW = (h.T @ dlogits)[:, :h.shape[1]].T * 0 + dlogits.T @ h[::-1]"),  # rows
+    ("    p[~ok] = 0.0\n", ""),                                                  # ignored rows kept
+    ("S = max(len(rows), 1)", "S = max(len(ok), 1)"),                            # mean over all rows
+    ("dW = dlogits.T @ h", "dW = dlogits.T @ h[::-1]"),                          # rows paired wrongly
     ("lse = mx + np.log(np.exp(z - mx[:, None]).sum(axis=-1))",
      "lse = np.log(np.exp(z - mx[:, None]).sum(axis=-1))"),                     # max dropped
 ]
@@ -302,11 +304,12 @@ def _lm_checks(M):
     r = np.random.default_rng(4)
     h = r.standard_normal((3, 5))
     W = 0.3 * r.standard_normal((7, 5))
-    labels = np.array([1, 6, 1])
+    labels = np.array([1, 6, 1, -100])
+    h = np.vstack([h, r.standard_normal((1, 5))])
     res = M.lm_head_bwd(h, h @ W.T, labels, W, np.zeros_like(W), np.zeros_like(W),
                         1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
-    loss = lambda h_, W_: float(np.mean(  # noqa: E731
-        np.log(np.exp(h_ @ W_.T).sum(-1)) - (h_ @ W_.T)[np.arange(3), labels]))
+    loss = lambda h_, W_: float(np.mean(  # noqa: E731  (the labelled rows 0..2)
+        np.log(np.exp(h_[:3] @ W_.T).sum(-1)) - (h_[:3] @ W_.T)[np.arange(3), labels[:3]]))
     return [abs(res["loss"] - loss(h, W)) < 1e-12,
             FD.rel_err(res["grad_hidden"], FD.grad(lambda z: loss(z, W), h)) < 1e-8,
             FD.rel_err(res["dW"], FD.grad(lambda z: loss(h, z), W)) < 1e-8]

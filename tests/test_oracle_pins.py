@@ -610,3 +610,37 @@ def test_lm_head_closed_forms_and_torch():
     assert abs(res["loss"] - tl.item()) < 1e-13
     np.testing.assert_allclose(res["grad_hidden"], th.grad.numpy(), rtol=1e-12, atol=1e-15)
     np.testing.assert_allclose(res["dW"], tW.grad.numpy(), rtol=1e-12, atol=1e-15)
+
+
+def test_lm_head_ignored_rows():
+    """Labels outside the vocabulary mark rows to skip: against float64 torch
+    cross_entropy with ignore_index (its mean is over the kept rows), and
+    finite differences of the loss over the kept rows alone."""
+    torch = pytest.importorskip("torch")
+    from oracle import lmhead as LM
+    h, W, labels = _lm_case(63, 7, 6, 11)
+    labels[[1, 4]] = -100
+    th = torch.tensor(h, requires_grad=True)
+    tW = torch.tensor(W, requires_grad=True)
+    tl = torch.nn.functional.cross_entropy(th @ tW.T, torch.tensor(labels), ignore_index=-100)
+    tl.backward()
+    res = LM.lm_head_bwd(h, h @ W.T, labels, W, np.zeros_like(W), np.zeros_like(W),
+                         1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    assert abs(res["loss"] - tl.item()) < 1e-13
+    np.testing.assert_allclose(res["grad_hidden"], th.grad.numpy(), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(res["dW"], tW.grad.numpy(), rtol=1e-12, atol=1e-15)
+    assert not res["dlogits"][[1, 4]].any()
+    # a label equal to the vocabulary size is out of range too
+    labels[4] = 11
+    keep = [0, 2, 3, 5, 6]
+    loss = lambda h_: float(np.mean(  # noqa: E731
+        np.log(np.exp(h_[keep] @ W.T).sum(-1)) - (h_[keep] @ W.T)[np.arange(5), labels[keep]]))
+    res = LM.lm_head_bwd(h, h @ W.T, labels, W, np.zeros_like(W), np.zeros_like(W),
+                         1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    assert abs(res["loss"] - loss(h)) < 1e-13
+    assert fd.rel_err(res["grad_hidden"], fd.grad(loss, h)) < 1e-8
+    # every row ignored: no loss, no gradient, and AdamW sees a zero gradient
+    res = LM.lm_head_bwd(h, h @ W.T, np.full(7, -1), W, np.zeros_like(W), np.zeros_like(W),
+                         1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    assert res["loss"] == 0.0 and not res["grad_hidden"].any() and not res["dW"].any()
+    np.testing.assert_allclose(res["W"], W * (1 - 1e-3 * 0.01), rtol=1e-15)

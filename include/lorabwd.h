@@ -212,6 +212,43 @@ int lorabwd_lora_grad_adamw(int64_t rows, int64_t in_dim, int64_t out_dim, int64
                             size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * The lm_head backward upstream of the layer stack, with AdamW on the
+ * lm_head weight.  [ENT] wgpu_backward.rs, module doc (the gradient flows
+ * from lm_head through the layers) and WgpuModelState (lm_head, lm_head_m,
+ * lm_head_v).  With logits z = h W^T as saved by the forward and n the
+ * number of rows whose label is in [0, vocab) (rows with any other label,
+ * e.g. -100 for padding, are ignored: no loss, no gradient):
+ *   loss        = (1/n) sum over labelled rows of logsumexp(z_s) - z_s[label_s]
+ *   dlogits     = (softmax(z) - onehot(labels)) / n, zero on ignored rows
+ *   grad_hidden = dlogits W            (W before this call's update)
+ *   dW          = dlogits^T h
+ *   m = b1 m + (1-b1) dW;  v = b2 v + (1-b2) dW^2
+ *   W -= lr (m/(1-b1^step) / (sqrt(v/(1-b2^step)) + eps) + weight_decay W)
+ * With no labelled row the loss and both gradients are 0 (AdamW still
+ * steps, with a zero gradient).
+ * h        f32 [rows, hidden]   the final hidden state (lm_head input)
+ * logits   f32 [rows, vocab]    finite, or -inf for entries excluded from
+ *                               the softmax (each labelled row needs one
+ *                               finite entry)
+ * labels   i32 [rows]           device memory
+ * w, m, v  f32 [vocab, hidden]  updated in place
+ * grad_hidden f32 [rows, hidden] out (the gradient handed to the top layer)
+ * loss     f32 device scalar, out
+ * grad_w   f32 [vocab, hidden] or NULL: a copy of dW
+ * rows 0 .. 2^20; hidden a multiple of 8 up to 2^20; vocab a multiple of 4
+ * up to 2^20 (vocabularies are commonly padded; give padding entries -inf
+ * logits).  step >= 1.  Results are bitwise reproducible (no float atomics).
+ * The workspace holds dlogits [rows, vocab] and the vocabulary-split partial
+ * sums of grad_hidden.
+ * ---------------------------------------------------------------------- */
+size_t lorabwd_lm_head_workspace_size(int64_t rows, int64_t hidden, int64_t vocab);
+int lorabwd_lm_head_backward(int64_t rows, int64_t hidden, int64_t vocab, const float* h,
+                             const float* logits, const int32_t* labels, float* w, float* m,
+                             float* v, float* grad_hidden, float* loss, float* grad_w, float lr,
+                             float beta1, float beta2, float eps, float weight_decay, int step,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * One whole layer: [FFN] "Backward (reverse)" (lorabwd_ffn_backward with
  * d_resid == d_hidden), then [ATTN] "Gradient Flow": O-projection backward
  * dCtx = dH1 W_o, the attention sub-norm backward (sub_norms = 1),
@@ -359,6 +396,14 @@ int lorabwd_layer_backward_timed(const lorabwd_layer_desc* d, const lorabwd_laye
                                  float* dv_out, float* gnorm_sq, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
                                  lorabwd_kernel_record* records, int capacity, int* n_kernels);
+/* The same measurement variant of lorabwd_lm_head_backward. */
+int lorabwd_lm_head_backward_timed(int64_t rows, int64_t hidden, int64_t vocab, const float* h,
+                                   const float* logits, const int32_t* labels, float* w,
+                                   float* m, float* v, float* grad_hidden, float* loss,
+                                   float* grad_w, float lr, float beta1, float beta2, float eps,
+                                   float weight_decay, int step, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+                                   lorabwd_kernel_record* records, int capacity, int* n_kernels);
 
 /* ------------------------------------------------------------------------
  * Allocation-free variant of lorabwd_layer_backward, for callers that cannot

@@ -40,6 +40,7 @@ EXPORTS = [
     "lorabwd_lora_workspace_size", "lorabwd_lora_grad_adamw",
     "lorabwd_layer_workspace_size", "lorabwd_layer_backward", "lorabwd_layer_backward_timed",
     "lorabwd_layer_backward_noalloc", "lorabwd_ternary_packed_bytes", "lorabwd_pack_ternary",
+    "lorabwd_lm_head_workspace_size", "lorabwd_lm_head_backward", "lorabwd_lm_head_backward_timed",
 ]
 NOALLOC_SCRATCH_BYTES = 16 << 20  # LORABWD_NOALLOC_SCRATCH_BYTES
 
@@ -120,6 +121,14 @@ _SIGS = {
                                         c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_float,
                                         c_float, c_float, c_float, c_float, c_float, c_float,
                                         c_int, c_int, c_vp, c_size, c_vp]),
+    "lorabwd_lm_head_workspace_size": (c_size, [c_i64, c_i64, c_i64]),
+    "lorabwd_lm_head_backward": (c_int, [c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                         c_vp, c_vp, c_vp, c_float, c_float, c_float, c_float,
+                                         c_float, c_int, c_vp, c_size, c_vp]),
+    "lorabwd_lm_head_backward_timed": (c_int, [
+        c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_float,
+        c_float, c_float, c_float, c_float, c_int, c_vp, c_size, c_vp, ctypes.POINTER(c_vp),
+        ctypes.POINTER(KernelRecord), c_int, ctypes.POINTER(c_int)]),
     "lorabwd_layer_workspace_size": (c_size, [ctypes.POINTER(LayerDesc)]),
     "lorabwd_ternary_packed_bytes": (c_size, [c_i64, c_i64]),
     "lorabwd_pack_ternary": (c_int, [c_i64, c_i64, c_vp, c_int, c_vp, c_vp]),
@@ -383,6 +392,45 @@ def lorabwd_lora_grad_adamw(dy, x, h, A, B, m_a, v_a, m_b, v_b, alpha, lr_a, lr_
         rows, in_dim, out_dim, rank, _ptr(dy), _ptr(x), _ptr(h), _ptr(A), _ptr(B), _ptr(m_a),
         _ptr(v_a), _ptr(m_b), _ptr(v_b), _ptr(grad_a), _ptr(grad_b), _ptr(gnorm_sq), alpha, lr_a,
         lr_b, beta1, beta2, eps, weight_decay, step, dt, _ptr(ws), wsb, _stream(stream, dy.device)))
+
+
+def lorabwd_lm_head_workspace_size(rows, hidden, vocab):
+    return load_library().lorabwd_lm_head_workspace_size(rows, hidden, vocab)
+
+
+def lorabwd_lm_head_backward(h, logits, labels, W, m, v, grad_hidden, loss, lr, beta1=0.9,
+                             beta2=0.999, eps=1e-8, weight_decay=0.01, step=1, grad_w=None,
+                             stream=None, timing=None):
+    """lm_head backward with AdamW on W (updated in place with m and v):
+    grad_hidden [rows, hidden] and loss [1] are written.  h, logits, W, m,
+    v float32; labels int32 (a label outside [0, vocab) ignores its row).
+    `timing` = (events, records) as for the layer: per-kernel HIP events
+    recorded on the call's stream."""
+    torch = _torch()
+    rows, hidden = h.shape
+    vocab = W.shape[0]
+    _f32(h, "h", (rows, hidden))
+    _f32(logits, "logits", (rows, vocab))
+    _need(labels, "labels", torch.int32, (rows,))
+    for t, n in ((W, "W"), (m, "m"), (v, "v")):
+        _f32(t, n, (vocab, hidden))
+    _f32(grad_hidden, "grad_hidden", (rows, hidden))
+    _f32(loss, "loss", (1,))
+    _opt(grad_w, "grad_w", torch.float32, (vocab, hidden))
+    lib = load_library()
+    need = lib.lorabwd_lm_head_workspace_size(rows, hidden, vocab)
+    ws, wsb = _workspace(need, h.device, stream)
+    args = (rows, hidden, vocab, _ptr(h), _ptr(logits), _ptr(labels), _ptr(W), _ptr(m), _ptr(v),
+            _ptr(grad_hidden), _ptr(loss), _ptr(grad_w), lr, beta1, beta2, eps, weight_decay,
+            step, _ptr(ws), wsb, _stream(stream, h.device))
+    if timing is None:
+        _check("lorabwd_lm_head_backward", lib.lorabwd_lm_head_backward(*args))
+        return None
+    events, records = timing
+    n = ctypes.c_int(0)
+    _check("lorabwd_lm_head_backward_timed", lib.lorabwd_lm_head_backward_timed(
+        *args, events, records, len(records), ctypes.byref(n)))
+    return n.value
 
 
 def lorabwd_layer_backward_timed(desc, weights, saved, d_hidden, events, records, **kw):

@@ -6,7 +6,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["rowwise.hip", "gemm.hip", "decode.hip", "attn.hip", "lora.hip", "api.hip"]
+SOURCES = ["rowwise.hip", "gemm.hip", "decode.hip", "attn.hip", "lora.hip", "lmhead.hip",
+           "api.hip"]
 LIB = os.path.join(HERE, "liblorabwd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -371,7 +371,7 @@ const char* lorabwd_status_string(int status) {
   }
 }
 
-int lorabwd_abi_version(void) { return 5; }
+int lorabwd_abi_version(void) { return 6; }
 
 int lorabwd_rmsnorm_backward(int64_t rows, int64_t n, const void* x, const float* gamma,
                              const float* dy, float* dx, float eps, int accumulate, int dtype,
@@ -490,6 +490,49 @@ int lorabwd_lora_grad_adamw(int64_t rows, int64_t in_dim, int64_t out_dim, int64
   LBP_RUN(launch_lora_adamw(rows, in_dim, out_dim, rank, dy, x, h, dtype, A, B, m_a, v_a, m_b,
                             v_b, grad_a, grad_b, gnorm_sq, alpha / (float)rank, hp, workspace,
                             stream));
+  return LORABWD_OK;
+}
+
+// ---------------------------------------------------------------- lm_head
+size_t lorabwd_lm_head_workspace_size(int64_t rows, int64_t hidden, int64_t vocab) {
+  if (!rows_ok(rows) || !feat_ok(hidden) || vocab <= 0 || vocab % 4 != 0 || vocab > kMaxFeat)
+    return 0;
+  return up(lm_head_ws_bytes(rows, hidden, vocab));
+}
+
+int lorabwd_lm_head_backward(int64_t rows, int64_t hidden, int64_t vocab, const float* h,
+                             const float* logits, const int32_t* labels, float* w, float* m,
+                             float* v, float* grad_hidden, float* loss, float* grad_w, float lr,
+                             float beta1, float beta2, float eps, float weight_decay, int step,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  LBP_CHECK(rows_ok(rows) && feat_ok(hidden) && vocab > 0 && vocab % 4 == 0 && vocab <= kMaxFeat,
+            LORABWD_ERR_SHAPE);
+  LBP_CHECK(step >= 1, LORABWD_ERR_STEP);
+  LBP_CHECK(finite(lr) && finite(weight_decay) && finite(eps) && eps >= 0.f && beta1 >= 0.f &&
+                beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f,
+            LORABWD_ERR_ARG);
+  LBP_CHECK(w && m && v && loss, LORABWD_ERR_NULL);
+  if (rows > 0) LBP_CHECK(h && logits && labels && grad_hidden, LORABWD_ERR_NULL);
+  const void* ptrs[] = {h, logits, w, m, v, grad_hidden, grad_w};
+  for (const void* q : ptrs) LBP_CHECK(aligned16(q), LORABWD_ERR_ALIGN);
+  LBP_CHECK(((uintptr_t)loss & 3u) == 0 && ((uintptr_t)labels & 3u) == 0, LORABWD_ERR_ALIGN);
+  // outputs pairwise disjoint, and disjoint from every input
+  const size_t nw = (size_t)vocab * hidden * 4, nh = (size_t)rows * hidden * 4;
+  const void* outs[] = {w, m, v, grad_w, grad_hidden, loss};
+  const size_t ns[] = {nw, nw, nw, nw, nh, 4};
+  for (int i = 0; i < 6; ++i) {
+    for (int j = i + 1; j < 6; ++j)
+      LBP_CHECK(!overlap(outs[i], ns[i], outs[j], ns[j]), LORABWD_ERR_ALIAS);
+    LBP_CHECK(!overlap(outs[i], ns[i], h, nh), LORABWD_ERR_ALIAS);
+    LBP_CHECK(!overlap(outs[i], ns[i], logits, (size_t)rows * vocab * 4), LORABWD_ERR_ALIAS);
+    LBP_CHECK(!overlap(outs[i], ns[i], labels, (size_t)rows * 4), LORABWD_ERR_ALIAS);
+  }
+  const size_t need = lorabwd_lm_head_workspace_size(rows, hidden, vocab);
+  LBP_CHECK(need == 0 || (workspace && workspace_bytes >= need), LORABWD_ERR_WORKSPACE);
+  LBP_CHECK(aligned16(workspace), LORABWD_ERR_ALIGN);
+  const AdamHP hp = make_hp(lr, lr, beta1, beta2, eps, weight_decay, step);
+  LBP_RUN(launch_lm_head_bwd(rows, hidden, vocab, h, logits, labels, w, m, v, grad_hidden, loss,
+                             grad_w, hp, workspace, stream));
   return LORABWD_OK;
 }
 
@@ -1022,6 +1065,25 @@ int lorabwd_layer_backward_timed(const lorabwd_layer_desc* d, const lorabwd_laye
   const int st = lorabwd_layer_backward(d, w, a, q_state, v_state, hp, d_out, d_hidden,
                                         dq_pre_out, dv_out, gnorm_sq, workspace, workspace_bytes,
                                         stream);
+  tl_recorder = nullptr;
+  if (n_kernels) *n_kernels = rec.count;
+  return st;
+}
+
+int lorabwd_lm_head_backward_timed(int64_t rows, int64_t hidden, int64_t vocab, const float* h,
+                                   const float* logits, const int32_t* labels, float* w,
+                                   float* m, float* v, float* grad_hidden, float* loss,
+                                   float* grad_w, float lr, float beta1, float beta2, float eps,
+                                   float weight_decay, int step, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+                                   lorabwd_kernel_record* records, int capacity, int* n_kernels) {
+  LBP_CHECK(capacity >= 0, LORABWD_ERR_ARG);
+  LBP_CHECK(capacity == 0 || (events != nullptr && records != nullptr), LORABWD_ERR_NULL);
+  Recorder rec{events, records, capacity, 0};
+  tl_recorder = &rec;
+  const int st = lorabwd_lm_head_backward(rows, hidden, vocab, h, logits, labels, w, m, v,
+                                          grad_hidden, loss, grad_w, lr, beta1, beta2, eps,
+                                          weight_decay, step, workspace, workspace_bytes, stream);
   tl_recorder = nullptr;
   if (n_kernels) *n_kernels = rec.count;
   return st;

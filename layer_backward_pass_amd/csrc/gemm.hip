@@ -7,7 +7,10 @@
 // order (no float atomics), so results are bitwise reproducible.  The W_down
 // product can apply the gated-activation backward to its output as it is
 // stored (ActEpi), so dHid never goes to memory; the W_o product can also
-// store its output transposed in bf16 (TCopy) for the attention's dV.
+// store its output transposed in bf16 (TCopy) for the attention's dV.  The
+// lm_head weight gradient dW = dlogits^T h reads its A operand transposed
+// (dlogits as stored, [K][M]) and applies AdamW to the weight as each tile
+// is stored (AdamEpi), so dW never goes to memory either.
 #include <type_traits>
 
 #include "common.h"
@@ -133,6 +136,74 @@ __device__ __forceinline__ void act_tile_epilogue(const ActEpi& e, int64_t M, in
   }
 }
 
+// A whole 128 x 256 tile of a weight gradient (C[r][c] = dW[r][c], W dense
+// [M][N]) through AdamW: W, m, v updated in place (and the gradient copied
+// to e.grad when set).  As in the activation epilogue, the accumulators pass
+// through LDS in two halves of 64 rows so that each thread then takes eight
+// consecutive columns of a row with 16-byte accesses; a half's W, m, v loads
+// are in flight while its accumulators are written.  N % 8 == 0.
+__device__ __forceinline__ void adam_tile_epilogue(const AdamEpi& e, int64_t M, int64_t N,
+                                                   int64_t bm, int64_t bn, int wm, int wn,
+                                                   const floatx4 (&acc)[4][4], float* stage) {
+  const int t = threadIdx.x, lane = t & 63;
+  const int64_t mrows = min((int64_t)128, M - bm);
+  const uint32_t bytes = (uint32_t)(mrows * N * 4);
+  const brsrc_t rw = make_brsrc(e.w + bm * N, bytes);
+  const brsrc_t rm = make_brsrc(e.m + bm * N, bytes);
+  const brsrc_t rv = make_brsrc(e.v + bm * N, bytes);
+  const int cl = 8 * (t & 31), rl = t >> 5;  // eight columns of row rl (+16 p)
+  const int64_t gc = bn + cl;
+  __syncthreads();  // every wave is past its last LDS read of the k-loop
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float4 pw[4][2], pm[4][2], pv[4][2];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = 64 * h + 16 * p + rl;
+      const bool ok = r < mrows && gc < N;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint32_t off = ok ? (uint32_t)((r * N + gc) * 4 + 16 * q) : BUF_OOB;
+        pw[p][q] = bload_f4(rw, off);
+        pm[p][q] = bload_f4(rm, off);
+        pv[p][q] = bload_f4(rv, off);
+      }
+    }
+    if (wm == 64 * h) {
+#pragma unroll
+      for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+        for (int fj = 0; fj < 4; ++fj)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            stage[(fi * 16 + 4 * (lane >> 4) + v) * EPI_LD + wn + fj * 16 + (lane & 15)] =
+                acc[fi][fj][v];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = 64 * h + 16 * p + rl;
+      if (r < mrows && gc < N) {
+        const int64_t o = (bm + r) * N + gc;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float4 d = *reinterpret_cast<const float4*>(&stage[(16 * p + rl) * EPI_LD + cl + 4 * q]);
+          float4 w = pw[p][q], m = pm[p][q], v = pv[p][q];
+          adamw1(w.x, d.x, m.x, v.x, e.lr, e.hp);
+          adamw1(w.y, d.y, m.y, v.y, e.lr, e.hp);
+          adamw1(w.z, d.z, m.z, v.z, e.lr, e.hp);
+          adamw1(w.w, d.w, m.w, v.w, e.lr, e.hp);
+          *reinterpret_cast<float4*>(e.w + o + 4 * q) = w;
+          *reinterpret_cast<float4*>(e.m + o + 4 * q) = m;
+          *reinterpret_cast<float4*>(e.v + o + 4 * q) = v;
+          if (e.grad) *reinterpret_cast<float4*>(e.grad + o + 4 * q) = d;
+        }
+      }
+    }
+    if (h == 0) __syncthreads();  // the second half overwrites the stage
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 GEMM: workgroup of 8 waves (512 threads), tile 128 x 256, BK = 32; the
 // waves form a 2 x 4 grid of 64 x 64 wave tiles (4 x 4 MFMA accumulators).
@@ -145,7 +216,10 @@ __device__ __forceinline__ void act_tile_epilogue(const ActEpi& e, int64_t M, in
 // are double-buffered: the next k-tile's global loads are in flight while
 // the current one is used, one barrier per k-tile.  A wide workgroup tile
 // keeps the HBM/L2 bytes per MFMA low; with one workgroup per CU the MFMA
-// pipe then stays about three quarters busy.
+// pipe then stays about three quarters busy.  AT: A is given transposed,
+// A^T [K][lda] (m contiguous), and is gathered like B (four k of one m per
+// thread, one 16-byte LDS store); the tiles are then numbered n-fastest.
+// EPI 32 (with AT) is the AdamW epilogue.
 constexpr int F_BK = 32, F_LD = F_BK + 4, F_BM = 128, F_BN = 256, F_NT = 512;
 static_assert(2 * F_BN * F_LD >= 64 * EPI_LD, "activation stage fits in Bs");
 
@@ -154,13 +228,15 @@ static_assert(2 * F_BN * F_LD >= 64 * EPI_LD, "activation stage fits in Bs");
 // tiles are split in k-chunks of kps, item nfull + j -> chunk z = j / ntail
 // of tile nfull + j % ntail (chunk-major, so neighbouring items still share
 // weight panels), written to partial slot z ([z][M][N], dense).  nfull = 0
-// is plain split-K; nfull = all tiles is no split.
+// is plain split-K; nfull = all tiles is no split.  NFAST numbers the tiles
+// n-fastest instead (the column tiles of one row panel together: they share
+// the A panel, for a product whose A is the large operand).
 struct GemmWork {
   int64_t bm, bn, kbeg, kend, ldo;
   float* out;
   bool whole;
 };
-template <int BM, int BN>
+template <int BM, int BN, bool NFAST = false>
 __device__ __forceinline__ GemmWork gemm_work(int64_t M, int64_t N, int64_t K, int64_t kps,
                                               int64_t nfull, float* C, int64_t ldc, float* P) {
   const int64_t nm = (M + BM - 1) / BM, nn = (N + BN - 1) / BN, T = nm * nn;
@@ -178,8 +254,8 @@ __device__ __forceinline__ GemmWork gemm_work(int64_t M, int64_t N, int64_t K, i
     tile = nfull + (j - z * nt);
   }
   GemmWork w;
-  w.bm = (tile % nm) * BM;
-  w.bn = (tile / nm) * BN;
+  w.bm = (NFAST ? tile / nn : tile % nm) * BM;
+  w.bn = (NFAST ? tile % nn : tile / nm) * BN;
   w.whole = z < 0;
   if (z < 0) {
     w.kbeg = 0;
@@ -259,14 +335,15 @@ __device__ __forceinline__ void store_out(const ActEpi& e, const GemmWork& wk, i
   store_tile<4, 4>(wk.out, wk.ldo, M, N, wk.bm + wm, wk.bn + wn, acc);
 }
 
-template <int EPI>
+template <int EPI, bool AT>
 __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, int64_t K,
                                                         const float* __restrict__ A, int64_t lda,
                                                         const float* __restrict__ B1,
                                                         const float* __restrict__ B2, int64_t K1,
                                                         int64_t ldb, float* __restrict__ C,
                                                         int64_t ldc, float* __restrict__ P,
-                                                        int64_t kps, int64_t nfull, ActEpi epi) {
+                                                        int64_t kps, int64_t nfull, ActEpi epi,
+                                                        AdamEpi adam) {
   constexpr int NA = F_BM * F_BK / 4 / F_NT;   // A float4 per thread (2)
   constexpr int NBQ = F_BK * F_BN / 4 / F_NT;  // B k-quads per thread (4)
   constexpr int BQS = F_NT / F_BN;             // k-quad stride between them (2)
@@ -277,7 +354,7 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
   const int l16 = lane & 15, c = lane >> 4;
   // 1-D grid of work items (gemm_work), m fastest, so the row tiles that
   // read one weight panel run together on one XCD.
-  const GemmWork wk = gemm_work<F_BM, F_BN>(M, N, K, kps, nfull, C, ldc, P);
+  const GemmWork wk = gemm_work<F_BM, F_BN, AT>(M, N, K, kps, nfull, C, ldc, P);
   const int64_t bm = wk.bm, bn = wk.bn, kbeg = wk.kbeg, kend = wk.kend;
   const int wm = (w & 1) * 64, wn = (w >> 1) * 64;
 
@@ -288,24 +365,47 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
   // splits the prefetch pipeline.
   const int am = t >> 3, ak = 4 * (t & 7), bc = t % F_BN, bq0 = w / (F_BN / 64);
   const int64_t mrows = min((int64_t)F_BM, M - bm);
-  const brsrc_t ra = make_brsrc(A + bm * lda, (uint32_t)(((mrows - 1) * lda + K) * 4));
+  // (with AT the rows' range is not used: a quad's resource is made per load)
+  const brsrc_t ra = make_brsrc(A + bm * lda, AT ? 0u : (uint32_t)(((mrows - 1) * lda + K) * 4));
   const uint32_t bcoff = bn + bc < N ? (uint32_t)(bc * 4) : BUF_OOB;
+  // (AT) column t % 128 of the tile, k quads t / 128 + 4 i (t / 128 = w / 2,
+  // uniform across a wave, so each quad's resource is a scalar)
+  const int atc = t % F_BM, aq0 = w >> 1;
+  static_assert(F_BM == 128 && F_NT / F_BM * 8 == F_BK, "AT gather covers one k-tile");
+  const uint32_t acoff = atc < mrows ? (uint32_t)(atc * 4) : BUF_OOB;
+  // the rows of a k quad inside the k-range (a range of 0 to 4 rows: a
+  // quad that runs past kend reads zeros there)
+  auto qrows = [&](int64_t kq) -> uint32_t {
+    const int64_t n = kend - kq;
+    return n <= 0 ? 0u : (uint32_t)(n < 4 ? n : 4);
+  };
   struct Stage {
     float4 a[NA], b[NBQ];
   };
   auto load = [&](Stage& r, int64_t k0) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      const int m = am + 64 * i;
-      const int64_t k = k0 + ak;
-      r.a[i] = bload_f4(ra, (m < mrows && k < kend) ? (uint32_t)((m * lda + k) * 4) : BUF_OOB);
+      if constexpr (AT) {
+        const int64_t kq = k0 + 4 * (aq0 + 4 * i);
+        const brsrc_t rt = make_brsrc(A + kq * lda + bm, qrows(kq) * (uint32_t)(lda * 4));
+        float v[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          v[jj] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rt, (int)(acoff + (uint32_t)(jj * lda * 4)), 0, 0));
+        r.a[i] = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        const int m = am + 64 * i;
+        const int64_t k = k0 + ak;
+        r.a[i] = bload_f4(ra, (m < mrows && k < kend) ? (uint32_t)((m * lda + k) * 4) : BUF_OOB);
+      }
     }
 #pragma unroll
     for (int i = 0; i < NBQ; ++i) {
-      const int64_t kq = k0 + 4 * (bq0 + BQS * i);  // kend and K1 are multiples of 4
+      const int64_t kq = k0 + 4 * (bq0 + BQS * i);  // K1 is a multiple of 4
       const bool s1 = kq < K1;
       const brsrc_t rb = make_brsrc((s1 ? B1 + kq * ldb : B2 + (kq - K1) * ldb) + bn,
-                                    kq < kend ? (uint32_t)(4 * ldb * 4) : 0u);
+                                    qrows(kq) * (uint32_t)(ldb * 4));
       float v[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
@@ -316,8 +416,12 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
   };
   auto stash = [&](const Stage& r, int buf) {
 #pragma unroll
-    for (int i = 0; i < NA; ++i)
-      *reinterpret_cast<float4*>(&As[buf][am + 64 * i][ak]) = r.a[i];
+    for (int i = 0; i < NA; ++i) {
+      if constexpr (AT)
+        *reinterpret_cast<float4*>(&As[buf][atc][4 * (aq0 + 4 * i)]) = r.a[i];
+      else
+        *reinterpret_cast<float4*>(&As[buf][am + 64 * i][ak]) = r.a[i];
+    }
 #pragma unroll
     for (int i = 0; i < NBQ; ++i)
       *reinterpret_cast<float4*>(&Bs[buf][bc][4 * (bq0 + BQS * i)]) = r.b[i];
@@ -367,7 +471,10 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
     __syncthreads();
     load(s1, k0 + 4 * F_BK);
   }
-  store_out<EPI>(epi, wk, M, N, wm, wn, acc, &Bs[0][0][0]);
+  if constexpr (EPI == 32)
+    adam_tile_epilogue(adam, M, N, bm, bn, wm, wn, acc, &Bs[0][0][0]);
+  else
+    store_out<EPI>(epi, wk, M, N, wm, wn, acc, &Bs[0][0][0]);
 }
 
 // ---------------------------------------------------------------------------
@@ -746,9 +853,9 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
   const dim3 block(256);
   if (b_dt == F32) {
 #define LBP_GEMM_F32(E)                                                                        \
-  gemm_f32_kernel<E><<<grid1, dim3(F_NT), 0, s>>>(M, N, K, (const float*)A, lda, (const float*)B1, \
-                                                  (const float*)B2, K1, ldb, C, ldc, partials, kps, \
-                                                  nfull, ea)
+  gemm_f32_kernel<E, false><<<grid1, dim3(F_NT), 0, s>>>(                                    \
+      M, N, K, (const float*)A, lda, (const float*)B1, (const float*)B2, K1, ldb, C, ldc,      \
+      partials, kps, nfull, ea, AdamEpi{})
     if (epi == 1) LBP_GEMM_F32(1);
     else if (epi == 2) LBP_GEMM_F32(2);
     else LBP_GEMM_F32(0);
@@ -822,6 +929,24 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
   }
 #undef LBP_RED
   mark("splitk_reduce", 0, 0, s, (double)(tiles - nfull) * pl.bm * pl.bn * 4 * (nsp + 1));
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_at_adamw(int64_t M, int64_t N, int64_t K, const float* At, int64_t lda,
+                                const float* B, int64_t ldb, const AdamEpi& ad, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  // buffer ranges: four rows of A^T and of B, and one tile's rows of W, m, v
+  if (N % 8 != 0 || lda < M || ldb < N || 16.0 * lda >= BUF_MAX_BYTES ||
+      16.0 * ldb >= BUF_MAX_BYTES || (double)F_BM * N * 4 >= BUF_MAX_BYTES)
+    return hipErrorInvalidValue;
+  if (dry_run()) return hipSuccess;
+  // every tile whole (the epilogue needs the finished dW tile)
+  const int64_t tiles = cdiv(M, F_BM) * cdiv(N, F_BN);
+  gemm_f32_kernel<32, true><<<dim3((unsigned)tiles), dim3(F_NT), 0, s>>>(
+      M, N, K, At, lda, B, B, K, ldb, nullptr, N, nullptr, K, tiles, ActEpi{}, ad);
+  // A^T and B once; W, m, v read and written (and the gradient copy)
+  mark("gemm_f32_at_adamw", (double)K * (M + N) * 4 + (double)M * N * 4 * (ad.grad ? 7 : 6),
+       2.0 * M * N * K, s);
   return hipGetLastError();
 }
 

@@ -77,6 +77,20 @@ hipError_t launch_act_bwd(int64_t rows, int64_t ffn, int act, const void* gate, 
 // p[0:n] = 0 (a kernel, not a memset, so the call can sit in a captured graph)
 hipError_t launch_fill_zero(int64_t n, float* p, hipStream_t s);
 
+// ---- AdamW ([ENT] cpu_adamw): lr_a is the step size of every parameter but
+// the LoRA B matrices, which take lr_b (LoRA+)
+struct AdamHP {
+  float lr_a, lr_b, beta1, beta2, eps, wd, bc1, bc2;
+};
+// One AdamW element step (bc1, bc2: the bias corrections 1/(1 - beta^step)).
+__device__ __forceinline__ void adamw1(float& p, float gr, float& m, float& v, float lr,
+                                       const AdamHP& hp) {
+  m = hp.beta1 * m + (1.0f - hp.beta1) * gr;
+  v = hp.beta2 * v + (1.0f - hp.beta2) * gr * gr;
+  const float mh = m * hp.bc1, vh = v * hp.bc2;
+  p -= lr * (mh / (sqrtf(vh) + hp.eps) + hp.wd * p);
+}
+
 // ---- products (gemm.hip)
 // C[M,N] = A[M,K] B[K,N]; B rows k < K1 come from B1 (row k), rows k >= K1
 // from B2 (row k - K1).  A is float or bf16 (a_dt), B is float or bf16
@@ -114,6 +128,26 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
                        int* deferred = nullptr, const ActEpi* act = nullptr,
                        bool* act_done = nullptr, const TCopy* tc = nullptr,
                        bool* tc_done = nullptr);
+// A weight's gradient and its AdamW step in one launch: dW[M,N] = A^T[K,M]^T
+// B[K,N] (fp32; A given transposed with row stride lda, B row stride ldb),
+// never stored; W, m, v [M][N] (dense) are updated in place with step size
+// lr, and dW is also copied to grad when that is set.  N % 8 == 0.
+struct AdamEpi {
+  float *w, *m, *v, *grad;
+  AdamHP hp;
+  float lr;
+};
+hipError_t launch_gemm_at_adamw(int64_t M, int64_t N, int64_t K, const float* At, int64_t lda,
+                                const float* B, int64_t ldb, const AdamEpi& ad, hipStream_t s);
+
+// ---- lm_head backward (lmhead.hip): softmax cross-entropy over the
+// vocabulary, grad_hidden and AdamW on W (step size hp.lr_a); ws holds
+// lm_head_ws_bytes.  vocab % 4 == 0, hidden % 8 == 0.
+size_t lm_head_ws_bytes(int64_t rows, int64_t hidden, int64_t vocab);
+hipError_t launch_lm_head_bwd(int64_t rows, int64_t hidden, int64_t vocab, const float* h,
+                              const float* logits, const int32_t* labels, float* w, float* m,
+                              float* v, float* grad_hidden, float* loss, float* grad_w,
+                              const AdamHP& hp, void* ws, hipStream_t s);
 
 // ---- single-token (decode) kernels (decode.hip)
 // part[chunk, N] = x[K] W[K, N] over row chunks of kc rows (W rows k < K1
@@ -268,9 +302,6 @@ uint16_t* attn_dct_buffer(void* ws, int64_t s_q, int64_t s_kv, int64_t n_heads,
 
 // ---- LoRA + AdamW (lora.hip)
 size_t lora_ws_bytes(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank);
-struct AdamHP {
-  float lr_a, lr_b, beta1, beta2, eps, wd, bc1, bc2;
-};
 // One adapter's LoRA gradient + AdamW work (ws: its own lora_ws_bytes).
 struct LoraJob {
   int64_t rows, in_dim, out_dim, rank;

@@ -331,14 +331,6 @@ __global__ __launch_bounds__(256) void lora_da_kernel(Pair<DaArgs> pa) {
       }
 }
 
-__device__ __forceinline__ void adamw1(float& p, float gr, float& m, float& v, float lr,
-                                       const AdamHP& hp) {
-  m = hp.beta1 * m + (1.0f - hp.beta1) * gr;
-  v = hp.beta2 * v + (1.0f - hp.beta2) * gr * gr;
-  const float mh = m * hp.bc1, vh = v * hp.bc2;
-  p -= lr * (mh / (sqrtf(vh) + hp.eps) + hp.wd * p);
-}
-
 // Elements [0, nb): dB = s sum_slices dbpart, then AdamW on B (lr_b).
 // Elements [nb, nb + ng): g = s sum_groups gpart (ng = rows * 16 RB).
 // sum_{c < n} p[c * stride] in index order, 16 loads in flight at a time

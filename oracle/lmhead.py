@@ -67,3 +67,44 @@ def lm_head_bwd(h, logits, labels, W, m, v, lr, beta1, beta2, eps, wd, step):
     nW, nm, nv = adamw(W, dW, m, v, lr, beta1, beta2, eps, wd, step)
     return dict(loss=cross_entropy(logits, labels), dlogits=dlogits, grad_hidden=grad_hidden,
                 dW=dW, W=nW, m=nm, v=nv)
+
+
+def lm_head_sampled(h, logits, labels, W, rows, cols, chunk=64):
+    """loss, grad_hidden[rows] and dW[cols] as lm_head_bwd defines them, for
+    inputs too large to form the whole float64 dlogits: each row's softmax
+    depends on that row alone (and on n, the labelled-row count), so dlogits
+    is formed a block of rows at a time and only the requested rows and
+    columns are kept.  W may be float32; it is widened a block at a time."""
+    labels = np.asarray(labels)
+    S, V = logits.shape
+    ok = label_rows(labels, V)
+    n = max(int(ok.sum()), 1)
+    rows = np.asarray(rows)
+    cols = np.asarray(cols)
+    loss = 0.0
+    d_cols = np.zeros((S, len(cols)))
+    d_rows = np.zeros((len(rows), V))
+    for r0 in range(0, S, chunk):
+        r1 = min(S, r0 + chunk)
+        z = np.asarray(logits[r0:r1], np.float64)
+        mx = z.max(axis=-1)
+        lse = mx + np.log(np.exp(z - mx[:, None]).sum(axis=-1))
+        p = np.exp(z - lse[:, None])
+        for i in range(r1 - r0):
+            s = r0 + i
+            if ok[s]:
+                loss += lse[i] - z[i, labels[s]]
+                p[i, labels[s]] -= 1.0
+            else:
+                p[i] = 0.0
+        p /= n
+        d_cols[r0:r1] = p[:, cols]
+        for j, s in enumerate(rows):
+            if r0 <= s < r1:
+                d_rows[j] = p[s - r0]
+    grad_hidden = np.zeros((len(rows), W.shape[1]))
+    for v0 in range(0, V, 8192):
+        v1 = min(V, v0 + 8192)
+        grad_hidden += d_rows[:, v0:v1] @ np.asarray(W[v0:v1], np.float64)
+    dW = d_cols.T @ np.asarray(h, np.float64)
+    return dict(loss=loss / n if ok.any() else 0.0, grad_hidden=grad_hidden, dW=dW)

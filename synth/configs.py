@@ -17,6 +17,11 @@ Five workloads, named by what they are:
               the seq512 / seq2048bf16 layers with the exact input gradient
               through the attention branch (dK, the transposed Q/K/V
               products, the adapters' terms, the attention-norm backward)
+
+and the step upstream of the stack (LmHeadConfig):
+  lmhead      the lm_head backward of the stack36 model: 1024 tokens, hidden
+              2560, vocabulary 151936 (a Qwen-family vocabulary), fp32, with
+              AdamW on the lm_head weight
 """
 from dataclasses import dataclass, replace
 
@@ -94,8 +99,39 @@ SEQ512IG = SEQ512.with_(name="seq512ig", index=6, input_grad=True)
 SEQ2048BF16IG = SEQ2048BF16.with_(name="seq2048bf16ig", index=7, input_grad=True)
 DECODE_PACKED = DECODE.with_(name="decode_packed", index=8, packed=True)
 
+
+
+@dataclass(frozen=True)
+class LmHeadConfig:
+    """The lm_head backward: final hidden state h [rows, hidden], logits
+    [rows, vocab] as saved by the forward, int32 labels, the weight
+    [vocab, hidden] with AdamW moments."""
+    name: str
+    index: int
+    rows: int
+    hidden: int
+    vocab: int
+    logit_std: float = 1.0    # the spread of h W^T at these weight scales
+    ignore_every: int = 0     # every k-th row gets label -100 (ignored); 0: none
+    lr: float = 1e-4
+    beta1: float = 0.9
+    beta2: float = 0.999
+    adam_eps: float = 1e-8
+    weight_decay: float = 0.01
+    step: int = 1
+
+    @property
+    def seq(self):
+        return self.rows
+
+    def with_(self, **kw):
+        return replace(self, **kw)
+
+
+LMHEAD = LmHeadConfig("lmhead", 9, rows=1024, hidden=2560, vocab=151936)
+
 CONFIGS = {c.name: c for c in (TINY, DECODE, SEQ512, SEQ2048BF16, STACK36, SEQ512QK, SEQ512IG,
-                               SEQ2048BF16IG, DECODE_PACKED)}
+                               SEQ2048BF16IG, DECODE_PACKED, LMHEAD)}
 
 
 def get_config(name):

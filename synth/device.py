@@ -73,3 +73,21 @@ def draw_timing_layer_device(cfg, layer=0, device="cuda:0"):
                               "m_b": torch.zeros((out, r), device=device),
                               "v_b": torch.zeros((out, r), device=device)}
     return d
+
+
+def draw_lm_head_device(cfg, copy=0, device="cuda:0"):
+    """synth.gen.draw_lm_head's recipe drawn on the GPU (torch RNG)."""
+    g = _gen(cfg, copy, device)
+    S, H, V = cfg.rows, cfg.hidden, cfg.vocab
+    f32 = torch.float32
+    labels = torch.randint(0, V, (S,), generator=g, device=device, dtype=torch.int64).to(torch.int32)
+    if cfg.ignore_every:
+        labels[::cfg.ignore_every] = -100
+    return {
+        "h": torch.randn((S, H), generator=g, device=device, dtype=f32),
+        "logits": torch.randn((S, V), generator=g, device=device, dtype=f32) * cfg.logit_std,
+        "labels": labels,
+        "W": torch.randn((V, H), generator=g, device=device, dtype=f32) * 0.02,
+        "m": torch.zeros((V, H), device=device, dtype=f32),
+        "v": torch.zeros((V, H), device=device, dtype=f32),
+    }

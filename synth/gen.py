@@ -12,6 +12,10 @@ Distributions (the workload recipe):
     t uniform on {-1, 0, +1}
   * RMSNorm scales gamma (also the per-head QK-norm scales): 1 + 0.1 * N(0, 1)
   * AdamW moments m, v: zero (one step from a fresh optimizer)
+  * lm_head: h ~ N(0, 1), W ~ N(0, 0.02), logits drawn on their own as
+    N(0, logit_std^2) (the backward takes them as saved; 1.0 is the spread
+    of h W^T at these scales), labels uniform over the vocabulary, every
+    ignore_every-th row -100 (ignored) when that is set
 """
 import numpy as np
 
@@ -21,6 +25,7 @@ TENSOR_IDS = {
     "gamma_asub": 12, "A_q": 13, "B_q": 14, "A_v": 15, "B_v": 16, "K_cache": 17,
     "V_cache": 18, "m_state": 19, "v_state": 20, "K_prefix": 21, "V_prefix": 22,
     "gamma_q": 23, "gamma_k": 24,
+    "lm_h": 25, "lm_logits": 26, "lm_labels": 27, "lm_W": 28,
     # timing-only draws (stand-ins for saved activations)
     "t_attn_input": 40, "t_resid1": 41, "t_gate": 42, "t_up": 43,
     "t_hidden_pre": 44, "t_ctx": 45, "t_P": 46, "t_K": 47, "t_V": 48,
@@ -102,6 +107,22 @@ def draw_layer(cfg, layer=0):
         for k in ("A_q", "B_q", "A_v", "B_v"):
             d["m_" + k] = np.zeros_like(d[k])
             d["v_" + k] = np.zeros_like(d[k])
+    return d
+
+
+def draw_lm_head(cfg, copy=0):
+    """Inputs of one lm_head backward (float32, labels int32)."""
+    S, H, V = cfg.rows, cfg.hidden, cfg.vocab
+    d = {
+        "h": normal(cfg, copy, "lm_h", (S, H)),
+        "logits": normal(cfg, copy, "lm_logits", (S, V), cfg.logit_std),
+        "labels": stream(cfg.index, copy, "lm_labels").integers(0, V, size=S).astype(np.int32),
+        "W": normal(cfg, copy, "lm_W", (V, H), 0.02),
+        "m": np.zeros((V, H), np.float32),
+        "v": np.zeros((V, H), np.float32),
+    }
+    if cfg.ignore_every:
+        d["labels"][::cfg.ignore_every] = -100
     return d
 
 

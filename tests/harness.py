@@ -324,3 +324,78 @@ def packed_layer_parity(cfg, device="cuda:0", check_bytes=True):
     torch.cuda.synchronize()
     return {"d_hidden": rel_err(host(d_hidden), ref["d_hidden"]),
             "dq_pre": rel_err(host(dq_pre), ref["dq_pre"]), "dv": rel_err(host(dv), ref["dv"])}
+
+
+# ------------------------------------------------------------------ lm_head
+def lm_head_parity(cfg, device="cuda:0", state=False, inf_cols=0, labels=None, full=False,
+                   log=print):
+    """lorabwd_lm_head_backward against the oracle.  Small shapes: every
+    output against lm_head_bwd.  full=True (the workload's own size, drawn on
+    the device): the loss, grad_hidden at sampled rows, and dW, W, m, v at
+    sampled vocabulary rows, against the oracle's block-wise form.  state:
+    non-zero AdamW moments (a later step); inf_cols: that many vocabulary
+    entries excluded from the softmax (-inf logits, never a label)."""
+    torch = _torch()
+    import layer_backward_pass_amd as lbp
+    from oracle import lmhead as LM
+    S, H, V = cfg.rows, cfg.hidden, cfg.vocab
+    if full:
+        from synth.device import draw_lm_head_device
+        T = draw_lm_head_device(cfg, 0, device)
+    else:
+        d = synth.draw_lm_head(cfg)
+        T = {k: torch.from_numpy(np.ascontiguousarray(v)).to(device) for k, v in d.items()}
+    if labels is not None:
+        T["labels"] = torch.as_tensor(np.asarray(labels, np.int32), device=device)
+    if state:
+        m, v = synth.gen.draw_adam_state(cfg, 0, (V, H), 0)
+        T["m"] = torch.from_numpy(m.astype(np.float32)).to(device)
+        T["v"] = torch.from_numpy(v.astype(np.float32)).to(device)
+    if inf_cols:
+        lab = set(T["labels"].cpu().numpy().tolist())
+        cols = [c for c in range(V - 1, -1, -3) if c not in lab][:inf_cols]
+        T["logits"][:, cols] = float("-inf")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    if full:
+        rows = np.unique(np.concatenate([[0, S - 1], rng.integers(0, S, 14)]))
+        lab_h = T["labels"].cpu().numpy()
+        cols = np.unique(np.concatenate([[0, V - 1], lab_h[rows[:8]], rng.integers(0, V, 48)]))
+        cols = cols[(cols >= 0) & (cols < V)]
+        W0 = T["W"].cpu().numpy()  # float32, before the update
+        m0 = host(T["m"][torch.as_tensor(cols, device=device)])
+        v0 = host(T["v"][torch.as_tensor(cols, device=device)])
+    else:
+        pre = {k: host(T[k]) for k in ("h", "logits", "W", "m", "v")}
+        pre["labels"] = T["labels"].cpu().numpy()
+    gh = torch.empty((S, H), device=device)
+    loss = torch.full((1,), 123.0, device=device)
+    gw = None if full else torch.empty((V, H), device=device)
+    hp = dict(lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.adam_eps,
+              weight_decay=cfg.weight_decay, step=cfg.step)
+    log("lm_head S=%d H=%d V=%d state=%s inf_cols=%d full=%s" % (S, H, V, state, inf_cols, full))
+    lbp.lorabwd_lm_head_backward(T["h"], T["logits"], T["labels"], T["W"], T["m"], T["v"], gh,
+                                 loss, grad_w=gw, **hp)
+    torch.cuda.synchronize()
+    f = lambda x: float(np.float32(x))  # noqa: E731  (the scalars the GPU received)
+    adam = (f(cfg.lr), f(cfg.beta1), f(cfg.beta2), f(cfg.adam_eps), f(cfg.weight_decay), cfg.step)
+    errs = {}
+    if full:
+        ref = LM.lm_head_sampled(host(T["h"]), T["logits"].cpu().numpy(), lab_h, W0, rows, cols)
+        errs["loss"] = rel_err(host(loss), [ref["loss"]])
+        errs["grad_hidden"] = rel_err(host(gh)[rows], ref["grad_hidden"])
+        nW, nm, nv = OB.adamw(W0[cols], ref["dW"], m0, v0, *adam)
+        ci = torch.as_tensor(cols, device=device)
+        errs["W"] = update_err(host(T["W"][ci]), nW, ref["dW"], adam[0], TOL["f32"])
+        errs["m"] = rel_err(host(T["m"][ci]), nm)
+        errs["v"] = rel_err(host(T["v"][ci]), nv)
+        return errs
+    ref = LM.lm_head_bwd(pre["h"], pre["logits"], pre["labels"], pre["W"], pre["m"], pre["v"],
+                         *adam)
+    errs["loss"] = rel_err(host(loss), [ref["loss"]])
+    errs["grad_hidden"] = rel_err(host(gh), ref["grad_hidden"])
+    errs["grad_w"] = rel_err(host(gw), ref["dW"])
+    errs["W"] = update_err(host(T["W"]), ref["W"], ref["dW"], adam[0], TOL["f32"])
+    errs["m"] = rel_err(host(T["m"]), ref["m"])
+    errs["v"] = rel_err(host(T["v"]), ref["v"])
+    return errs

@@ -56,7 +56,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.lorabwd_abi_version() == 5
+    assert lib.lorabwd_abi_version() == 6
     for code in (OK, ENULL, ESHAPE, EALIGN, EDTYPE, EWS, ESTEP, EALIAS, EHIP, EARG):
         s = lib.lorabwd_status_string(code).decode()
         assert s and s != "unknown status"
@@ -300,6 +300,48 @@ def test_pack_ternary_validation(lib):
     w.scale_up = float("nan")
     assert fl(r(one), r(w), r(a), None, None, None, None, fake(50), None, None, None, fake(60), ws,
               None) == EARG
+
+
+def test_lm_head_validation(lib):
+    f = lib.lorabwd_lm_head_backward
+    p = [fake(i) for i in range(12)]
+    S, H, V = 16, 64, 1000
+    ws = lib.lorabwd_lm_head_workspace_size(S, H, V)
+    assert ws >= S * V * 4 + S * 4
+    assert lib.lorabwd_lm_head_workspace_size(S, H, 1002) == 0     # vocab % 4
+    assert lib.lorabwd_lm_head_workspace_size(S, 60, V) == 0       # hidden % 8
+    assert lib.lorabwd_lm_head_workspace_size(S, H, (1 << 20) + 4) == 0
+
+    def call(rows=S, hid=H, voc=V, h=p[0], z=p[1], lab=p[2], W=p[3], m=p[4], v=p[5], gh=p[6],
+             loss=p[7], gw=None, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.01, step=1, w=p[9],
+             wsb=ws):
+        return f(rows, hid, voc, h, z, lab, W, m, v, gh, loss, gw, lr, b1, b2, eps, wd, step, w,
+                 wsb, None)
+    assert call(voc=1002) == ESHAPE
+    assert call(voc=0) == ESHAPE
+    assert call(hid=60) == ESHAPE
+    assert call(rows=-1) == ESHAPE
+    assert call(rows=(1 << 20) + 1) == ESHAPE
+    assert call(step=0) == ESTEP
+    assert call(b2=1.0) == EARG
+    assert call(lr=float("inf")) == EARG
+    assert call(W=None) == ENULL
+    assert call(loss=None) == ENULL
+    assert call(lab=None) == ENULL
+    assert call(h=p[0] + 8) == EALIGN
+    assert call(lab=p[2] + 2) == EALIGN
+    assert call(gh=p[0]) == EALIAS                  # grad_hidden over h
+    assert call(m=p[3] + 64) == EALIAS              # m inside W
+    assert call(loss=p[1] + 16) == EALIAS           # loss inside the logits
+    assert call(gw=p[5]) == EALIAS                  # grad_w over v
+    assert call(wsb=ws - 1) == EWS
+    assert call(w=None) == EWS
+    # the timed variant validates the same way
+    ft = lib.lorabwd_lm_head_backward_timed
+    assert ft(S, H, V, *p[:8], None, 1e-3, 0.9, 0.999, 1e-8, 0.01, 0, p[9], ws, None, None, None,
+              0, None) == ESTEP
+    assert ft(S, H, V, *p[:8], None, 1e-3, 0.9, 0.999, 1e-8, 0.01, 1, p[9], ws, None, None, None,
+              -1, None) == EARG
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -62,3 +62,16 @@ def test_stack36_full():
                                          {k: float("%.3g" % v) for k, v in errs.items()}))
     bad = {k: v for k, v in errs.items() if not v <= Hn.TOL[cfg.dtype]}
     assert not bad, bad
+
+
+def test_full_size_lmhead():
+    """The lm_head workload (1024 rows, hidden 2560, vocabulary 151936): the
+    loss, grad_hidden at sampled rows, and dW's AdamW step at sampled
+    vocabulary rows, against the oracle's block-wise form."""
+    cfg = synth.get_config("lmhead")
+    t0 = time.time()
+    errs = Hn.lm_head_parity(cfg, "cuda:0", full=True, log=_log)
+    _log("  lmhead: %.1f s, errors %s" % (time.time() - t0,
+                                        {k: float("%.3g" % v) for k, v in errs.items()}))
+    bad = {k: v for k, v in errs.items() if not v <= Hn.TOL["f32"]}
+    assert not bad, bad

@@ -466,3 +466,57 @@ def test_layer_packed_ternary_small(over):
     errs = Hn.packed_layer_parity(cfg, DEV, check_bytes=True)
     bad = {k: v for k, v in errs.items() if not v <= Hn.TOL[cfg.dtype]}
     assert not bad, bad
+
+
+# ------------------------------------------------------------------ lm_head
+LM = synth.get_config("lmhead")
+
+
+@pytest.mark.parametrize("over,kw", [
+    # ragged everywhere: 37 rows (not a multiple of 4: the dW product's k
+    # tail), 1000 vocabulary rows (7 whole 128-row tiles and a tail), hidden
+    # below one column tile; every fifth row ignored, one label = vocab
+    ({"rows": 37, "hidden": 64, "vocab": 1000, "ignore_every": 5}, {"labels": "with_vocab"}),
+    # split-K grad_hidden, ragged column tiles (520 = 2 * 256 + 8), a later
+    # AdamW step with non-zero moments
+    ({"rows": 300, "hidden": 520, "vocab": 4100, "step": 3}, {"state": True}),
+    # one row, the 32-entry vocabulary of the gradient-flow example
+    ({"rows": 1, "hidden": 64, "vocab": 32}, {}),
+    # vocabulary entries excluded from the softmax (-inf logits)
+    ({"rows": 66, "hidden": 128, "vocab": 2048}, {"inf_cols": 100}),
+    # every row ignored: loss and gradients 0, AdamW steps on a zero gradient
+    ({"rows": 20, "hidden": 64, "vocab": 256}, {"labels": "none", "state": True}),
+    # no rows at all
+    ({"rows": 0, "hidden": 64, "vocab": 256}, {}),
+])
+def test_lm_head(over, kw):
+    cfg = LM.with_(**over)
+    kw = dict(kw)
+    if kw.get("labels") == "with_vocab":
+        lab = synth.draw_lm_head(cfg)["labels"].copy()
+        lab[1] = cfg.vocab
+        lab[2] = -7
+        kw["labels"] = lab
+    elif kw.get("labels") == "none":
+        kw["labels"] = np.full(cfg.rows, -100, np.int32)
+    errs = Hn.lm_head_parity(cfg, DEV, **kw)
+    bad = {k: v for k, v in errs.items() if not v <= Hn.TOL["f32"]}
+    assert not bad, bad
+
+
+def test_lm_head_deterministic():
+    """Two calls on the same inputs give bitwise the same outputs."""
+    import layer_backward_pass_amd as lbp
+    cfg = LM.with_(rows=130, hidden=256, vocab=3000)
+    d = synth.draw_lm_head(cfg)
+    outs = []
+    for _ in range(2):
+        T = {k: torch.from_numpy(v).to(DEV) for k, v in d.items()}
+        gh = torch.empty((cfg.rows, cfg.hidden), device=DEV)
+        loss = torch.empty(1, device=DEV)
+        lbp.lorabwd_lm_head_backward(T["h"], T["logits"], T["labels"], T["W"], T["m"], T["v"], gh,
+                                     loss, lr=1e-3)
+        torch.cuda.synchronize()
+        outs.append((gh.cpu(), loss.cpu(), T["W"].cpu(), T["v"].cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)

@@ -294,8 +294,8 @@ LM_MUTATIONS = [
     ("    p[~ok] = 0.0\n", ""),                                                  # ignored rows kept
     ("S = max(len(rows), 1)", "S = max(len(ok), 1)"),                            # mean over all rows
     ("dW = dlogits.T @ h", "dW = dlogits.T @ h[::-1]"),                          # rows paired wrongly
-    ("lse = mx + np.log(np.exp(z - mx[:, None]).sum(axis=-1))",
-     "lse = np.log(np.exp(z - mx[:, None]).sum(axis=-1))"),                     # max dropped
+    ("\n    lse = mx + np.log(np.exp(z - mx[:, None]).sum(axis=-1))",
+     "\n    lse = np.log(np.exp(z - mx[:, None]).sum(axis=-1))"),                 # max dropped
 ]
 
 

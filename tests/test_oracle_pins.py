@@ -644,3 +644,21 @@ def test_lm_head_ignored_rows():
                          1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
     assert res["loss"] == 0.0 and not res["grad_hidden"].any() and not res["dW"].any()
     np.testing.assert_allclose(res["W"], W * (1 - 1e-3 * 0.01), rtol=1e-15)
+
+
+def test_lm_head_sampled_matches_the_whole_computation():
+    """The block-wise form used at full sizes keeps lm_head_bwd's values at
+    the requested rows and columns (a small block size spans several blocks
+    and a ragged last one)."""
+    from oracle import lmhead as LM
+    h, W, labels = _lm_case(64, 11, 6, 13)
+    labels[3] = -100
+    z = h @ W.T + 0.5
+    full = LM.lm_head_bwd(h, z, labels, W, np.zeros_like(W), np.zeros_like(W),
+                          1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    rows, cols = [0, 3, 10, 5], [12, 0, 7]
+    smp = LM.lm_head_sampled(h, z, labels, W.astype(np.float32), rows, cols, chunk=4)
+    assert abs(smp["loss"] - full["loss"]) < 1e-14
+    np.testing.assert_allclose(smp["dW"], full["dW"][cols], rtol=0, atol=1e-15)
+    ref = full["dlogits"][rows] @ W.astype(np.float32).astype(np.float64)
+    np.testing.assert_allclose(smp["grad_hidden"], ref, rtol=0, atol=1e-15)

@@ -27,6 +27,10 @@ Workloads (default: stack36):
   seq512ig, seq2048bf16ig
                those layers with the exact input gradient through attention
   tiny         hidden 64, 16 tokens (launch-bound; parity-size case)
+  lmhead       the step upstream of the stack: lm_head backward of the stack36
+               model (1024 tokens, hidden 2560, vocabulary 151936, fp32) -
+               softmax cross-entropy, grad_hidden, dW with AdamW on the weight
+               (lorabwd_lm_head_backward; metric lm_head-backward tokens/s)
 
 Prints ONE JSON line.  `roofline` describes the kernel with the largest
 share of the step, timed with HIP events recorded on the library's stream
@@ -55,9 +59,14 @@ PEAK = {  # MI355X published peaks (dense)
     "bf16_TFLOPs": 2516.6,
 }
 COPIES = {"decode": 6, "tiny": 1, "seq512": 4, "seq2048bf16": 4, "stack36": 1, "seq512qk": 4,
-          "seq512ig": 4, "seq2048bf16ig": 4, "decode_packed": 24}
+          "seq512ig": 4, "seq2048bf16ig": 4, "decode_packed": 24, "lmhead": 1}
 DEFAULT_STEPS = {"decode": 2000, "tiny": 2000, "seq512": 200, "seq2048bf16": 100, "stack36": 10,
-                 "seq512qk": 200, "seq512ig": 200, "seq2048bf16ig": 100, "decode_packed": 4800}
+                 "seq512qk": 200, "seq512ig": 200, "seq2048bf16ig": 100, "decode_packed": 4800,
+                 "lmhead": 30}
+
+
+def is_lm(cfg):
+    return type(cfg).__name__ == "LmHeadConfig"
 
 
 def parse():
@@ -141,7 +150,23 @@ def pack_weights(lbp, d, torch):
     return d
 
 
+def lm_call(lbp, cfg, cp, **kw):
+    return lbp.lorabwd_lm_head_backward(cp["h"], cp["logits"], cp["labels"], cp["W"], cp["m"],
+                                        cp["v"], cp["grad_hidden"], cp["loss"], lr=cfg.lr,
+                                        beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.adam_eps,
+                                        weight_decay=cfg.weight_decay, step=cfg.step, **kw)
+
+
 def build_copies(cfg, n_copies, torch, lbp=None):
+    if is_lm(cfg):
+        from synth.device import draw_lm_head_device
+        copies = []
+        for c in range(n_copies):
+            cp = draw_lm_head_device(cfg, c)
+            cp["grad_hidden"] = torch.empty((cfg.rows, cfg.hidden), device="cuda:0")
+            cp["loss"] = torch.empty(1, device="cuda:0")
+            copies.append(cp)
+        return copies
     from synth.device import draw_timing_layer_device
     copies = []
     for c in range(n_copies):
@@ -154,14 +179,23 @@ def build_copies(cfg, n_copies, torch, lbp=None):
     return copies
 
 
+def step_calls(lbp, cfg, cp):
+    """The library calls of one step, each taking the call's keyword options
+    (timing).  Layer workloads: the layers in reverse order (a single layer
+    for one-layer workloads); the top layer reads the upstream gradient
+    d_out, which is never written, and leaves dH1 in d_hidden; the layers
+    below update d_hidden in place.  lmhead: one lm_head backward (AdamW
+    updates the weight in place, as a training step does)."""
+    if is_lm(cfg):
+        return [lambda **kw: lm_call(lbp, cfg, cp, **kw)]
+    return [lambda li=li, d=d, **kw: layer_call(lbp, cfg, d, cp["d_hidden"], gnorm=cp["gnorm"],
+                                                d_out=cp["d_out"] if li == 0 else None, **kw)
+            for li, d in enumerate(reversed(cp["layers"]))]
+
+
 def run_step(lbp, cfg, cp):
-    """One step: the layers in reverse order (a single layer for one-layer
-    workloads).  The top layer reads the upstream gradient d_out, which is
-    never written, and leaves dH1 in d_hidden; the layers below update
-    d_hidden in place."""
-    for li, d in enumerate(reversed(cp["layers"])):
-        layer_call(lbp, cfg, d, cp["d_hidden"], gnorm=cp["gnorm"],
-                   d_out=cp["d_out"] if li == 0 else None)
+    for call in step_calls(lbp, cfg, cp):
+        call()
 
 
 # ------------------------------------------------------------------ roofline
@@ -184,12 +218,10 @@ def kernel_profile(lbp, hip, cfg, copies, torch, reps):
     torch.cuda.synchronize()
     for r in range(reps):
         cp = copies[r % len(copies)]
-        for li, d in enumerate(reversed(cp["layers"])):
+        for call in step_calls(lbp, cfg, cp):
             torch.sum(filler, dim=(0,), out=sink)
             hip.record(ev[cap], stream)
-            n = layer_call(lbp, cfg, d, cp["d_hidden"], gnorm=cp["gnorm"],
-                           d_out=cp["d_out"] if li == 0 else None,
-                           timing=(ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)), recs))
+            n = call(timing=(ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)), recs))
             torch.cuda.synchronize()
             prev = ev[cap]
             for i in range(min(n, cap)):
@@ -213,7 +245,7 @@ def kernel_profile(lbp, hip, cfg, copies, torch, reps):
 # headers it decides whether a stored traffic figure is still current
 KERNEL_SOURCE = (("dec_attn", "decode.hip"), ("dgemv", "decode.hip"), ("gemm", "gemm.hip"),
                  ("splitk", "gemm.hip"), ("attn", "attn.hip"), ("transpose", "attn.hip"),
-                 ("lora", "lora.hip"))
+                 ("lora", "lora.hip"), ("xent", "lmhead.hip"))
 
 
 def kernel_source(name):
@@ -321,9 +353,7 @@ def pmc_pass(lbp, hip, cfg, torch, path):
     cap = 128
     ev = hip.events(cap)
     recs = (lbp.KernelRecord * cap)()
-    d = list(reversed(cp["layers"]))[0]
-    n = layer_call(lbp, cfg, d, cp["d_hidden"], gnorm=cp["gnorm"], d_out=cp["d_out"],
-                   timing=(ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)), recs))
+    n = step_calls(lbp, cfg, cp)[0](timing=(ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)), recs))
     torch.cuda.synchronize()
     rows = [{"index": i, "name": recs[i].name.decode(), "alg_bytes": recs[i].alg_bytes,
              "alg_flops": recs[i].alg_flops} for i in range(min(n, cap))]
@@ -337,7 +367,8 @@ def pmc_pass(lbp, hip, cfg, torch, path):
         dst.copy_(src)
     torch.cuda.synchronize()
     with open(path, "w") as f:
-        json.dump({"workload": cfg.name, "layers": cfg.n_layers, "kernels_per_layer": len(rows),
+        json.dump({"workload": cfg.name, "layers": getattr(cfg, "n_layers", 1),
+                   "kernels_per_layer": len(rows),
                    "records": rows, "calibration_bytes": CAL_BYTES}, f)
 
 
@@ -420,6 +451,35 @@ def blas_info():
     except Exception:  # noqa: BLE001
         pass
     return "unknown", 1
+
+
+def cpu_baseline_lm(cfg, budget_s, parts=16):
+    """The float64 oracle's lm_head backward on a vocabulary slice of the
+    workload (all rows, hidden size as is, vocab / parts entries), repeated
+    until the budget is used; every part of the step (softmax, both products,
+    AdamW) scales with the vocabulary, so a whole step takes parts times a
+    slice's time."""
+    import numpy as np
+    import synth
+    from oracle import lmhead as LM
+    sub = cfg.with_(vocab=cfg.vocab // parts)
+    d = {k: np.asarray(v, np.int64 if k == "labels" else np.float64)
+         for k, v in synth.draw_lm_head(sub).items()}
+    blas, threads = blas_info()
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        LM.lm_head_bwd(d["h"], d["logits"], d["labels"], d["W"], d["m"], d["v"], cfg.lr,
+                       cfg.beta1, cfg.beta2, cfg.adam_eps, cfg.weight_decay, cfg.step)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el * (runs + 1) / runs > 3 * budget_s:
+            break
+    per_step = el / runs * parts
+    return {"value": round(cfg.rows / per_step, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "blas": blas,
+            "sample": "%d lm_head backward(s) on a 1/%d vocabulary slice (%d rows x %d entries, "
+                      "hidden %d), scaled by %d; float64 NumPy, %.1f s timed, input generation "
+                      "excluded" % (runs, parts, cfg.rows, sub.vocab, cfg.hidden, parts, el)}
 
 
 def cpu_baseline(cfg, budget_s):
@@ -543,14 +603,27 @@ def main():
     value = tokens / (ms / 1e3)
 
     kernels = kernel_profile(lbp, hip, cfg, copies, torch,
-                             reps=max(3, min(20, steps // 10)) if cfg.n_layers == 1 else 1)
+                             reps=max(3, min(20, steps // 10))
+                             if getattr(cfg, "n_layers", 1) == 1 else 1)
     rl = roofline(cfg, kernels)
     attn = attention_summary(cfg, kernels)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, args.cpu_seconds)
+        cpu = (cpu_baseline_lm if is_lm(cfg) else cpu_baseline)(cfg, args.cpu_seconds)
+    if is_lm(cfg):
+        config = {"workload": cfg.name, "tokens_per_step": cfg.rows, "hidden": cfg.hidden,
+                  "vocab": cfg.vocab, "input_copies": len(copies), "hip_graph": bool(graphs),
+                  "kernels_per_step": len(kernels)}
+    else:
+        config = {"workload": cfg.name, "tokens_per_step": cfg.seq, "kv_len": cfg.kv_len,
+                  "hidden": cfg.hidden, "ffn": cfg.ffn, "heads": cfg.n_heads,
+                  "kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "act": cfg.act,
+                  "sub_norms": cfg.sub_norms, "lora_rank": cfg.rank, "layers": cfg.n_layers,
+                  "input_copies": len(copies), "hip_graph": bool(graphs),
+                  "steps_per_graph_launch": len(copies) if round_graph is not None else 1,
+                  "kernels_per_step": len(kernels) * (cfg.n_layers if cfg.n_layers > 1 else 1)}
     out = {
-        "metric": "layer-backward tokens/s",
+        "metric": "lm_head-backward tokens/s" if is_lm(cfg) else "layer-backward tokens/s",
         "value": round(value, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -560,15 +633,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "dtype": "bf16" if getattr(cfg, "dtype", "f32") == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "tokens_per_step": cfg.seq, "kv_len": cfg.kv_len,
-                   "hidden": cfg.hidden, "ffn": cfg.ffn, "heads": cfg.n_heads,
-                   "kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "act": cfg.act,
-                   "sub_norms": cfg.sub_norms, "lora_rank": cfg.rank, "layers": cfg.n_layers,
-                   "input_copies": len(copies), "hip_graph": bool(graphs),
-                   "steps_per_graph_launch": len(copies) if round_graph is not None else 1,
-                   "kernels_per_step": len(kernels) * (cfg.n_layers if cfg.n_layers > 1 else 1)},
+        "config": config,
         "roofline": rl,
         "attn": attn,
         "cpu_baseline": cpu,

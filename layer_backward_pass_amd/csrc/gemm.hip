@@ -945,7 +945,7 @@ hipError_t launch_gemm_at_adamw(int64_t M, int64_t N, int64_t K, const float* At
   gemm_f32_kernel<32, true><<<dim3((unsigned)tiles), dim3(F_NT), 0, s>>>(
       M, N, K, At, lda, B, B, K, ldb, nullptr, N, nullptr, K, tiles, ActEpi{}, ad);
   // A^T and B once; W, m, v read and written (and the gradient copy)
-  mark("gemm_f32_at_adamw", (double)K * (M + N) * 4 + (double)M * N * 4 * (ad.grad ? 7 : 6),
+  mark("gemm_f32_mfma_adamw", (double)K * (M + N) * 4 + (double)M * N * 4 * (ad.grad ? 7 : 6),
        2.0 * M * N * K, s);
   return hipGetLastError();
 }

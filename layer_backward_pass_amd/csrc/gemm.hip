@@ -404,8 +404,11 @@ __global__ __launch_bounds__(F_NT) void gemm_f32_kernel(int64_t M, int64_t N, in
     for (int i = 0; i < NBQ; ++i) {
       const int64_t kq = k0 + 4 * (bq0 + BQS * i);  // K1 is a multiple of 4
       const bool s1 = kq < K1;
-      const brsrc_t rb = make_brsrc((s1 ? B1 + kq * ldb : B2 + (kq - K1) * ldb) + bn,
-                                    qrows(kq) * (uint32_t)(ldb * 4));
+      // without AT, K is a multiple of 4 (the layer's feature sizes): a
+      // quad is whole or past the end
+      const uint32_t brange = AT ? qrows(kq) * (uint32_t)(ldb * 4)
+                                 : (kq < kend ? (uint32_t)(4 * ldb * 4) : 0u);
+      const brsrc_t rb = make_brsrc((s1 ? B1 + kq * ldb : B2 + (kq - K1) * ldb) + bn, brange);
       float v[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)

@@ -49,6 +49,13 @@ struct DaArgs {
   const float* g;
   const void* x;
   float* dapart;
+  // GRED: g reduced in the kernel from the dy pass's partials (groups of
+  // them, scaled by s), and written to gout by the items of column group 0
+  // when gout is set
+  const float* gpart;
+  int groups;
+  float s;
+  float* gout;
 };
 struct BUpdArgs {
   int64_t nb, ng;
@@ -253,13 +260,33 @@ __global__ __launch_bounds__(256) void lora_dy_kernel(Pair<DyArgs> pa) {
       }
 }
 
+// dB = s sum_slices dbpart, then AdamW on B (lr_b), for element e of one
+// adapter's B.
+__device__ __forceinline__ void b_update_at(const BUpdArgs& A, int64_t e, const AdamHP& hp);
+
+// g rows of one row slice held in LDS by lora_da_kernel (GRED), in floats
+constexpr int DA_GSLICE = 4096;
+
 // One pass over x [rows, in]: dapart[by][r][k] = sum_{i in slice} g[i,r] x[i,k].
 // Result rows = rank (16 per block b), cols = features (tile j: k0 + 4n + j),
-// k = tokens.  g is [rows, 16 RB], already scaled and zero-padded.  Two
-// 16-row steps in flight, loads through buffer ranges (in_dim % 8 == 0, so
-// a 4-feature chunk is whole).
-template <int RB, typename T>
-__global__ __launch_bounds__(256) void lora_da_kernel(Pair<DaArgs> pa) {
+// k = tokens.  g is [rows, 16 RB], scaled and zero-padded: read from memory,
+// or (GRED) first summed for the item's row slice from the dy pass's
+// per-column-group partials, in group order, into LDS.  Two 16-row steps in
+// flight, loads through buffer ranges (in_dim % 8 == 0, so a 4-feature chunk
+// is whole).  With GRED the launch also carries the B updates: workgroups
+// from nd on each update 256 elements of dB (adapter 0's, then adapter 1's),
+// which need only the dy pass.
+template <int RB, typename T, bool GRED>
+__global__ __launch_bounds__(256) void lora_da_kernel(Pair<DaArgs> pa, Pair<BUpdArgs> pb,
+                                                      int64_t nd, AdamHP hp) {
+  __shared__ float gsl[GRED ? DA_GSLICE : 1];
+  if (GRED && (int64_t)blockIdx.x >= nd) {
+    const int64_t j = (int64_t)blockIdx.x - nd;
+    const bool second = j >= pb.a[0].nblk;
+    const BUpdArgs& B = second ? pb.a[1] : pb.a[0];
+    b_update_at(B, (second ? j - pb.a[0].nblk : j) * 256 + threadIdx.x, hp);
+    return;
+  }
   int bx, by;
   const DaArgs& A = pa.item(bx, by);
   const int64_t rows = A.rows, in_dim = A.in_dim, rs = A.rs;
@@ -275,7 +302,27 @@ __global__ __launch_bounds__(256) void lora_da_kernel(Pair<DaArgs> pa) {
   const int64_t i_end = min(rows, i_beg + rs);
   const int64_t nrow = i_end - i_beg;
   const brsrc_t rx = make_brsrc(x + i_beg * in_dim, nrow > 0 ? (uint32_t)(nrow * in_dim * sizeof(T)) : 0u);
-  const brsrc_t rg = make_brsrc(g + i_beg * RP, nrow > 0 ? (uint32_t)(nrow * RP * 4) : 0u);
+  const brsrc_t rg = make_brsrc(g + i_beg * RP, nrow > 0 && !GRED ? (uint32_t)(nrow * RP * 4) : 0u);
+  if (GRED) {
+    // g of the slice's rows, eight partial loads in flight per element
+    const int ng = A.groups;
+    for (int64_t e = t; e < nrow * RP; e += 256) {
+      const float* src = A.gpart + i_beg * RP + e;
+      const int64_t gst = rows * RP;
+      float s = 0.f;
+      for (int c0 = 0; c0 < ng; c0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = c0 + u < ng ? src[(int64_t)(c0 + u) * gst] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+      }
+      s *= A.s;
+      gsl[e] = s;
+      if (A.gout != nullptr && bx == 0) A.gout[i_beg * RP + e] = s;
+    }
+    __syncthreads();
+  }
   floatx4 acc[4][RB];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -293,9 +340,13 @@ __global__ __launch_bounds__(256) void lora_da_kernel(Pair<DaArgs> pa) {
       const bool ok = i < i_end;
       S.xa[q] = BufVec<T>::load(rx, (ok && c < in_dim) ? (uint32_t)(((i - i_beg) * in_dim + c) * sizeof(T)) : BUF_OOB);
 #pragma unroll
-      for (int b = 0; b < RB; ++b)
-        S.gv[q][b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            rg, ok ? (int)(((i - i_beg) * RP + 16 * b + l16) * 4) : (int)BUF_OOB, 0, 0));
+      for (int b = 0; b < RB; ++b) {
+        if (GRED)
+          S.gv[q][b] = ok ? gsl[(i - i_beg) * RP + 16 * b + l16] : 0.f;
+        else
+          S.gv[q][b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rg, ok ? (int)(((i - i_beg) * RP + 16 * b + l16) * 4) : (int)BUF_OOB, 0, 0));
+      }
     }
   };
   auto step = [&](const Step& S) {
@@ -348,19 +399,24 @@ __device__ __forceinline__ float sum_strided(const float* __restrict__ p, int n,
   return d;
 }
 
+__device__ __forceinline__ void b_update_at(const BUpdArgs& A, int64_t e, const AdamHP& hp) {
+  if (e >= A.nb) return;
+  float d = sum_strided(A.dbpart + e, A.slices, A.nb);
+  d *= A.s;
+  if (A.grad_b) A.grad_b[e] = d;
+  float p = A.B[e], mm = A.m[e], vv = A.v[e];
+  adamw1(p, d, mm, vv, A.lr, hp);
+  A.B[e] = p;
+  A.m[e] = mm;
+  A.v[e] = vv;
+}
+
 __global__ __launch_bounds__(256) void lora_b_update_kernel(Pair<BUpdArgs> pa, AdamHP hp) {
   const BUpdArgs& A = pa.pick();
   if ((int)blockIdx.x >= A.nblk) return;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e < A.nb) {
-    float d = sum_strided(A.dbpart + e, A.slices, A.nb);
-    d *= A.s;
-    if (A.grad_b) A.grad_b[e] = d;
-    float p = A.B[e], mm = A.m[e], vv = A.v[e];
-    adamw1(p, d, mm, vv, A.lr, hp);
-    A.B[e] = p;
-    A.m[e] = mm;
-    A.v[e] = vv;
+    b_update_at(A, e, hp);
   } else if (e < A.nb + A.ng) {
     const int64_t f = e - A.nb;
     A.g[f] = A.s * sum_strided(A.gpart + f, A.groups, A.ng);
@@ -471,9 +527,10 @@ Slicing slicing(int64_t rows, int64_t cols) {
   return s;
 }
 
-// Workspace carve-up, in floats: g | gpart | part (dB, then dA) | sq.
+// Workspace carve-up, in floats: g | gpart | dB partials | dA partials | sq
+// (the dA launch also runs the B updates, so the two partial sets coexist).
 struct LoraWs {
-  int64_t g, gpart, part, sq, end;
+  int64_t g, gpart, part, parta, sq, end;
 };
 LoraWs lora_ws(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank) {
   const int64_t rp = cdiv(rank, 16) * 16;
@@ -483,7 +540,8 @@ LoraWs lora_ws(int64_t rows, int64_t in_dim, int64_t out_dim, int64_t rank) {
   w.g = 0;
   w.gpart = w.g + cdiv(rows * rp, 64) * 64;
   w.part = w.gpart + cdiv(sy.groups * rows * rp, 64) * 64;
-  w.sq = w.part + cdiv(pb > pa ? pb : pa, 64) * 64;
+  w.parta = w.part + cdiv(pb, 64) * 64;
+  w.sq = w.parta + cdiv(pa, 64) * 64;
   w.end = w.sq + cdiv(cdiv(rank * in_dim, 256), 64) * 64;
   return w;
 }
@@ -520,9 +578,10 @@ static hipError_t lora_group(const LoraJob* const* jobs, int nz, float* gnorm_sq
                        base + o.part, base + o.gpart, base + o.g, j.scaling, hp.lr_b,
                        j.B, j.m_b, j.v_b, j.grad_b};
     da.a[z] = DaArgs{j.rows, j.in_dim, sa.rs, (int)j.rank, (int)sa.groups, (int)sa.slices,
-                     base + o.g, j.x, base + o.part};
+                     base + o.g, j.x, base + o.parta, base + o.gpart, (int)sy.groups, j.scaling,
+                     dx != nullptr ? base + o.g : nullptr};
     au.a[z] = AUpdArgs{j.rank * j.in_dim, (int)sa.slices, (int)cdiv(j.rank * j.in_dim, 256),
-                       base + o.part, j.A, j.m_a, j.v_a, j.grad_a, base + o.sq};
+                       base + o.parta, j.A, j.m_a, j.v_a, j.grad_a, base + o.sq};
     if (z >= nz) continue;
     ny += sy.groups * sy.slices;
     nd += sa.groups * sa.slices;
@@ -531,7 +590,7 @@ static hipError_t lora_group(const LoraJob* const* jobs, int nz, float* gnorm_sq
     const double esz = j.dt == F32 ? 4.0 : 2.0;
     by_dy += (double)j.rows * j.out_dim * 4 + (double)j.rows * j.rank * esz + (double)nb * 4;
     fl_dy += 4.0 * j.rows * j.out_dim * j.rank;
-    by_b += (double)nb * 4 * (6 + (j.grad_b ? 1 : 0)) + (double)ng * 4;
+    by_b += (double)nb * 4 * (6 + (j.grad_b ? 1 : 0));
     fl_b += 12.0 * nb;
     by_da += (double)j.rows * j.in_dim * esz + (double)j.rows * j.rank * 4;
     fl_da += 2.0 * j.rows * j.in_dim * j.rank;
@@ -547,17 +606,31 @@ static hipError_t lora_group(const LoraJob* const* jobs, int nz, float* gnorm_sq
         (double)sa.rs * j.in_dim * esz >= BUF_MAX_BYTES || (double)sa.rs * 16 * RB * 4 >= BUF_MAX_BYTES)
       return hipErrorInvalidValue;
   }
+  // the dA launch reduces g itself when a row slice's g fits its LDS
+  bool gred = true;
+  for (int z = 0; z < nz; ++z) gred = gred && da.a[z].rs * 16 * RB <= DA_GSLICE;
   if (dry_run()) return hipSuccess;
   hipError_t e;
+  typedef typename std::conditional<sizeof(TH) == 4, float, bf16>::type TX;
   if (rows > 0) {
     lora_dy_kernel<RB, VEC, TH><<<dim3((unsigned)ny), 256, 0, s>>>(dy);
     mark("lora_dy", by_dy, fl_dy, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // with no token rows the gradients are zero: no slices, no groups
-  lora_b_update_kernel<<<dim3((unsigned)bx, 1, (unsigned)nz), 256, 0, s>>>(bu, hp);
-  mark("lora_adamw_b", by_b, fl_b, s);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (gred) {
+    // one launch: dA partials (g reduced per row slice) and the B updates
+    // (with no token rows the gradients are zero: no slices, no groups)
+    int64_t nbb = 0;
+    for (int z = 0; z < 2; ++z) bu.a[z].nblk = z < nz ? (int)cdiv(bu.a[z].nb, 256) : 0;
+    for (int z = 0; z < nz; ++z) nbb += bu.a[z].nblk;
+    lora_da_kernel<RB, TX, true><<<dim3((unsigned)(nd + nbb)), 256, 0, s>>>(da, bu, nd, hp);
+    mark("lora_da_adamw_b", by_da + by_b, fl_da + fl_b, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
+    lora_b_update_kernel<<<dim3((unsigned)bx, 1, (unsigned)nz), 256, 0, s>>>(bu, hp);
+    mark("lora_adamw_b", by_b, fl_b, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (dx != nullptr && rows > 0) {
     // the adapters' input-gradient term, while A is still the pre-update A
     DxArgs xa[2];
@@ -574,9 +647,8 @@ static hipError_t lora_group(const LoraJob* const* jobs, int nz, float* gnorm_sq
     mark("lora_dx", (double)rows * n * 4 * (dx_acc ? 2 : 1) + rk * (n + rows) * 4, 2.0 * rows * n * rk, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (rows > 0) {
-    lora_da_kernel<RB, typename std::conditional<sizeof(TH) == 4, float, bf16>::type>
-        <<<dim3((unsigned)nd), 256, 0, s>>>(da);
+  if (rows > 0 && !gred) {
+    lora_da_kernel<RB, TX, false><<<dim3((unsigned)nd), 256, 0, s>>>(da, bu, nd, hp);
     mark("lora_da", by_da, fl_da, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

@@ -49,7 +49,9 @@ _LIB = None
 
 
 def lib_path():
-    return os.path.join(_HERE, "liblorabwd.so")
+    """liblorabwd.so built in-tree, or the build LORABWD_LIB names (the same
+    library built differently, e.g. with host sanitizers)."""
+    return os.environ.get("LORABWD_LIB") or os.path.join(_HERE, "liblorabwd.so")
 
 
 class LorabwdError(RuntimeError):

@@ -665,6 +665,128 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
 }
 
 // ---------------------------------------------------------------------------
+// Wide bf16 GEMM for plain products (no epilogue, one B source per k-tile):
+// tile 256 x 256, BK = 64, 8 waves of 128 x 64 (8 x 4 MFMA accumulators).
+// Per MFMA a wave reads 25 % fewer LDS bytes than with 64 x 64 wave tiles,
+// and the tile copies 27 % fewer bytes into LDS per flop.  The accumulators
+// (128 registers) leave room for one register stage of global loads and one
+// half k-tile of operands at two waves per SIMD: the operand reads of one
+// wave overlap the MFMAs of the other.  LDS: A [2][256][72], B [2][64][272]
+// (swizzled as lds_colk8<true> reads it), 143 KB.  One barrier per k-tile:
+// tile k+1 goes from registers into the buffer read two tiles ago, tile k+2's
+// loads are issued, tile k is multiplied.
+constexpr int W_BM = 256, W_BN = 256;
+__global__ __launch_bounds__(H_NT) void gemm_bf16w_kernel(int64_t M, int64_t N, int64_t K,
+                                                          const uint16_t* __restrict__ A,
+                                                          int64_t lda,
+                                                          const uint16_t* __restrict__ B1,
+                                                          const uint16_t* __restrict__ B2,
+                                                          int64_t K1, int64_t ldb,
+                                                          float* __restrict__ C, int64_t ldc,
+                                                          float* __restrict__ P, int64_t kps,
+                                                          int64_t nfull) {
+  constexpr int NA = W_BM * H_BK / 8 / H_NT;  // A chunks of 8 per thread (4)
+  constexpr int NB = H_BK * W_BN / 8 / H_NT;  // B chunks of 8 per thread (4)
+  struct Stage {
+    uint4 a[NA];
+    uint4 b[NB];
+  };
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][W_BM][H_LDA];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][H_BK][H_LDB];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int l16 = lane & 15, c = lane >> 4;
+  const GemmWork wk = gemm_work<W_BM, W_BN>(M, N, K, kps, nfull, C, ldc, P);
+  const int64_t bm = wk.bm, bn = wk.bn, kbeg = wk.kbeg, kend = wk.kend;
+  const int wm = (w & 1) * 128, wn = (w >> 1) * 64;
+  const int64_t mrows = min((int64_t)W_BM, M - bm);
+  const brsrc_t ra = make_brsrc(A + bm * lda, (uint32_t)(((mrows - 1) * lda + K) * 2));
+  auto load = [&](Stage& r, int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int e = t + H_NT * i;
+      const int m = e >> 3;
+      const int64_t k = k0 + 8 * (e & 7);
+      r.a[i] = bload_u4(ra, (m < mrows && k < kend) ? (uint32_t)((m * lda + k) * 2) : BUF_OOB);
+    }
+    // the whole k-tile lies in one source (K1 is a multiple of the tile)
+    const bool s1 = k0 < K1;
+    const int64_t r0 = s1 ? k0 : k0 - K1;
+    const int64_t nrows = min(kend, s1 ? K1 : K) - k0;
+    const brsrc_t rb = make_brsrc((s1 ? B1 : B2) + r0 * ldb + bn,
+                                  nrows > 0 ? (uint32_t)(nrows * ldb * 2) : 0u);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int e = t + H_NT * i;
+      const int kk = e >> 5, n = 8 * (e & 31);  // N % 8 == 0: a chunk is whole
+      const uint32_t off = (kk < nrows && bn + n < N) ? (uint32_t)((kk * ldb + n) * 2) : BUF_OOB;
+      r.b[i] = bload_u4(rb, off);
+    }
+  };
+  auto stash = [&](const Stage& r, int buf) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int e = t + H_NT * i;
+      *reinterpret_cast<uint4*>(&As[buf][e >> 3][8 * (e & 7)]) = r.a[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int e = t + H_NT * i;
+      const int row = e >> 5;
+      *reinterpret_cast<uint4*>(&Bs[buf][row][(8 * (e & 31)) ^ (64 * ((row >> 3) & 1))]) = r.b[i];
+    }
+  };
+  floatx4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      ushortx8 a[8], b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = lds_colk8<true>(&Bs[buf][0][0], H_LDB, 32 * ks, wn + 16 * j, lane);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        a[i] = *reinterpret_cast<const ushortx8*>(&As[buf][wm + 16 * i + l16][32 * ks + 8 * c]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32bf16(a[i], b[j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  Stage st;
+  load(st, kbeg);
+  stash(st, 0);
+  load(st, kbeg + H_BK);
+  __syncthreads();
+  int buf = 0;
+  for (int64_t k0 = kbeg; k0 < kend; k0 += H_BK) {
+    // buffer buf ^ 1 was last read in the previous iteration (before its
+    // barrier): it takes tile k+1 now
+    stash(st, buf ^ 1);
+    load(st, k0 + 2 * H_BK);
+    compute(buf);
+    __syncthreads();
+    buf ^= 1;
+  }
+  // output: wave rows wm + 16 i .., columns wn + 16 j ..
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = bn + wn + 16 * j + l16;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t row = bm + wm + 16 * i + 4 * c + v;
+        if (row < M && col < N) wk.out[row * wk.ldo + col] = acc[i][j][v];
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Fixed-order reduction of split-K partials: C[m, n] = sum_s P[s, m, n],
 // over the split tiles only -- columns n >= n0, except the rows m < mskip of
 // the first column panel [n0, n0 + bn), which were whole tiles.
@@ -741,9 +863,10 @@ struct GemmPlan {
   int bm, bn, nsp;
   int64_t kps, nfull;
 };
-static GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int b_dt) {
+static GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int b_dt, bool wide = false) {
   const bool f32 = b_dt == F32;
-  const int bm = f32 ? F_BM : H_BM, bn = f32 ? F_BN : H_BN, bk = f32 ? F_BK : H_BK;
+  const int bm = f32 ? F_BM : (wide ? W_BM : H_BM), bn = f32 ? F_BN : (wide ? W_BN : H_BN);
+  const int bk = f32 ? F_BK : H_BK;
   const int64_t slots = 256;
   // ns per k index for one tile: 2 bm bn flops at the sustained MFMA rate
   const double ns_per_k = f32 ? 2.0 * bm * bn / (256.0 * 0.74 * 2.4)
@@ -770,8 +893,16 @@ static GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int b_dt) {
   return best;
 }
 
+// The wide bf16 kernel takes plain products with at least two of its tiles
+// in each direction.
+static bool wide_ok(int64_t M, int64_t N, int b_dt) {
+  return b_dt == BF16 && M >= 2 * W_BM && N >= 2 * W_BN;
+}
+
 int gemm_splits(int64_t M, int64_t N, int64_t K, int b_dt) {
-  return gemm_plan(M, N, K, b_dt).nsp;
+  const int s = gemm_plan(M, N, K, b_dt).nsp;
+  const int sw = wide_ok(M, N, b_dt) ? gemm_plan(M, N, K, b_dt, true).nsp : 1;
+  return s > sw ? s : sw;  // partial slots for whichever kernel runs
 }
 
 // Scratch of launch_gemm: the split-K partials, then (bf16 weights with an
@@ -812,19 +943,23 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
   if (act_done) *act_done = false;
   if (tc_done) *tc_done = false;
   if (M == 0 || N == 0) return hipSuccess;
-  const GemmPlan pl = gemm_plan(M, N, K, b_dt);
-  const int64_t kps = pl.kps, nfull = pl.nfull;
-  const int nsp = pl.nsp;
+  GemmPlan pl = gemm_plan(M, N, K, b_dt);
   // the activation epilogue: whole tiles apply it as they store, a split
   // tail is reduced through it; a plain split-K product leaves its partials
   // (the caller's activation pass adds them) -- and gate/up/out take the
   // weights' dtype
-  const bool use_act = act != nullptr && (nsp == 1 || nfull > 0) &&
+  const bool use_act = act != nullptr && (pl.nsp == 1 || pl.nfull > 0) &&
                        act->gdt == b_dt && act->odt == b_dt && ldc == N && N % 8 == 0 &&
                        128.0 * N * 4 < BUF_MAX_BYTES;
   // the transposed bf16 copy: every tile whole, bf16 operands
-  const bool use_tc = !use_act && tc != nullptr && tc_done != nullptr && nsp == 1 &&
+  const bool use_tc = !use_act && tc != nullptr && tc_done != nullptr && pl.nsp == 1 &&
                       b_dt == BF16 && a_dt == BF16 && M % 8 == 0 && tc->ld % 8 == 0;
+  // plain bf16 products of enough tiles (one source per k-tile) take the
+  // wide kernel, with its own work split
+  const bool wide = !use_act && !use_tc && wide_ok(M, N, b_dt) && (B2 == nullptr || K1 % H_BK == 0);
+  if (wide) pl = gemm_plan(M, N, K, b_dt, true);
+  const int64_t kps = pl.kps, nfull = pl.nfull;
+  const int nsp = pl.nsp;
   const int epi = use_act ? 1 + act->act + (b_dt == BF16 ? 6 : 0) : (use_tc ? 16 : 0);
   ActEpi ea = use_act ? *act : ActEpi{};
   if (use_tc) {
@@ -840,7 +975,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
       return hipErrorInvalidValue;
   } else {
     const double la = a_dt == F32 ? (double)K : (double)lda;
-    if (((double)(H_BM - 1) * la + K) * 4 >= BUF_MAX_BYTES || (double)H_BK * ldb * 2 >= BUF_MAX_BYTES)
+    if (((double)(W_BM - 1) * la + K) * 4 >= BUF_MAX_BYTES || (double)H_BK * ldb * 2 >= BUF_MAX_BYTES)
       return hipErrorInvalidValue;
   }
   if (dry_run()) {
@@ -877,6 +1012,11 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
       lda = K;
     }
     const bool splitb = K1 % H_BK != 0;
+    if (wide) {
+      gemm_bf16w_kernel<<<grid1, dim3(H_NT), 0, s>>>(M, N, K, (const uint16_t*)A, lda,
+                                                     (const uint16_t*)B1, (const uint16_t*)B2, K1,
+                                                     ldb, C, ldc, partials, kps, nfull);
+    } else {
 #define LBP_GEMM_BF16(SB, E)                                                                \
   gemm_bf16_kernel<SB, E><<<grid1, dim3(H_NT), 0, s>>>(M, N, K, (const uint16_t*)A, lda,      \
                                                       (const uint16_t*)B1, (const uint16_t*)B2, \
@@ -895,6 +1035,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
       else LBP_GEMM_BF16(false, 0);
     }
 #undef LBP_GEMM_BF16
+    }
   }
   hipError_t e = hipGetLastError();
   // with the activation epilogue the product's output is [dGate | dUp] from

@@ -183,6 +183,10 @@ def test_attention_dq_only(s_q, s_kv, Hq, Hkv, D, dt):
     # fp32 whole tiles with ragged rows and columns
     (833, 512, 9400, "relu2", False, BF16),
     (700, 128, 520, "relu2", False, F32),
+    # the gate/up product on the wide bf16 kernel (256 x 256 tiles): ragged
+    # rows and columns, split in k
+    (600, 520, 1024, "swiglu", False, BF16),
+    (1100, 776, 1600, "relu2", True, BF16),
 ])
 def test_ffn(rows, dim, ffn, act, sub, dt):
     print("ffn", rows, dim, ffn, act, sub, dt, flush=True)

@@ -749,12 +749,10 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16w_kernel(int64_t M, int64_t N, 
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         a[i] = *reinterpret_cast<const ushortx8*>(&As[buf][wm + 16 * i + l16][32 * ks + 8 * c]);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32bf16(a[i], b[j], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
   Stage st;

@@ -740,20 +740,24 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16w_kernel(int64_t M, int64_t N, 
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // B operands of both halves first, then row block by row block: each A
+  // operand is read just ahead of its four MFMAs
   auto compute = [&](int buf) {
+    ushortx8 b[2][4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      ushortx8 a[8], b[4];
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = lds_colk8<true>(&Bs[buf][0][0], H_LDB, 32 * ks, wn + 16 * j, lane);
+      for (int j = 0; j < 4; ++j)
+        b[ks][j] = lds_colk8<true>(&Bs[buf][0][0], H_LDB, 32 * ks, wn + 16 * j, lane);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        a[i] = *reinterpret_cast<const ushortx8*>(&As[buf][wm + 16 * i + l16][32 * ks + 8 * c]);
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i) {
+        const ushortx8 a =
+            *reinterpret_cast<const ushortx8*>(&As[buf][wm + 16 * i + l16][32 * ks + 8 * c]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32bf16(a[i], b[j], acc[i][j]);
-    }
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32bf16(a, b[ks][j], acc[i][j]);
+      }
   };
   Stage st;
   load(st, kbeg);

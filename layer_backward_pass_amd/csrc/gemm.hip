@@ -38,21 +38,23 @@ __device__ __forceinline__ void store_tile(float* C, int64_t ldc, int64_t M, int
     }
 }
 
-// A whole 128 x 256 tile of dHid (C[r][c] = dHid of feature c) through the
-// gated-activation backward: [dGate | dUp] go to e.out[r][c], e.out[r][N + c]
-// (TO: float or bf16), from gate / up [M][N] (TG).  The accumulators pass
-// through LDS (`stage`: 64 x EPI_LD floats, free once the k-loop is done) in
-// two halves of 64 rows, so that each thread then takes eight consecutive
-// features of a row with 16-byte loads and stores; a half's gate/up loads
-// are in flight while its accumulators are written.  N % 8 == 0.
+// A whole tile of dHid (C[r][c] = dHid of feature c; 32 FM rows x 256, the
+// waves' FM x 4 accumulators at rows wm + 16 i) through the gated-activation
+// backward: [dGate | dUp] go to e.out[r][c], e.out[r][N + c] (TO: float or
+// bf16), from gate / up [M][N] (TG).  The accumulators pass through LDS
+// (`stage`: 64 x EPI_LD floats, free once the k-loop is done) 64 rows at a
+// time, so that each thread then takes eight consecutive features of a row
+// with 16-byte loads and stores; a pass's gate/up loads are in flight while
+// its accumulators are written.  N % 8 == 0.
 constexpr int EPI_LD = 260;
-template <typename TG, typename TO, int ACT>
+template <typename TG, typename TO, int ACT, int FM = 4>
 __device__ __forceinline__ void act_tile_epilogue(const ActEpi& e, int64_t M, int64_t N,
                                                   int64_t bm, int64_t bn, int wm, int wn,
-                                                  const floatx4 (&acc)[4][4], float* stage) {
+                                                  const floatx4 (&acc)[FM][4], float* stage) {
   constexpr int GV = sizeof(TG) == 2 ? 1 : 2;  // 16-byte chunks per eight features
+  constexpr int TR = 32 * FM;                  // tile rows
   const int t = threadIdx.x, lane = t & 63;
-  const int64_t mrows = min((int64_t)128, M - bm);
+  const int64_t mrows = min((int64_t)TR, M - bm);
   const uint32_t bytes = (uint32_t)(mrows * N * sizeof(TG));
   const brsrc_t rg = make_brsrc((const TG*)e.gate + bm * N, bytes);
   const brsrc_t ru = make_brsrc((const TG*)e.up + bm * N, bytes);
@@ -60,7 +62,7 @@ __device__ __forceinline__ void act_tile_epilogue(const ActEpi& e, int64_t M, in
   const int64_t gc = bn + cl;
   __syncthreads();  // every wave is past its last LDS read of the k-loop
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < TR / 64; ++h) {
     uint4 g[4][GV], u[4][GV];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -73,15 +75,16 @@ __device__ __forceinline__ void act_tile_epilogue(const ActEpi& e, int64_t M, in
         u[p][q] = bload_u4(ru, off);
       }
     }
-    if (wm == 64 * h) {
+    // the accumulator blocks whose rows fall in this pass (wave-uniform)
 #pragma unroll
-      for (int fi = 0; fi < 4; ++fi)
+    for (int fi = 0; fi < FM; ++fi) {
+      if ((wm + 16 * fi) / 64 != h) continue;
 #pragma unroll
-        for (int fj = 0; fj < 4; ++fj)
+      for (int fj = 0; fj < 4; ++fj)
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            stage[(fi * 16 + 4 * (lane >> 4) + v) * EPI_LD + wn + fj * 16 + (lane & 15)] =
-                acc[fi][fj][v];
+        for (int v = 0; v < 4; ++v)
+          stage[((wm + 16 * fi) % 64 + 4 * (lane >> 4) + v) * EPI_LD + wn + fj * 16 +
+                (lane & 15)] = acc[fi][fj][v];
     }
     __syncthreads();
 #pragma unroll
@@ -132,7 +135,7 @@ __device__ __forceinline__ void act_tile_epilogue(const ActEpi& e, int64_t M, in
         }
       }
     }
-    if (h == 0) __syncthreads();  // the second half overwrites the stage
+    if (h + 1 < TR / 64) __syncthreads();  // the next pass overwrites the stage
   }
 }
 
@@ -676,6 +679,10 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16_kernel(int64_t M, int64_t N, i
 // tile k+1 goes from registers into the buffer read two tiles ago, tile k+2's
 // loads are issued, tile k is multiplied.
 constexpr int W_BM = 256, W_BN = 256;
+static_assert(2 * W_BM * H_LDA * 2 >= 64 * EPI_LD * 4, "activation stage fits in As (both buffers)");
+// EPI: 0 plain, or (7, 8) the activation epilogue of whole tiles as in the
+// narrow kernel (bf16 gate/up and output).
+template <int EPI>
 __global__ __launch_bounds__(H_NT) void gemm_bf16w_kernel(int64_t M, int64_t N, int64_t K,
                                                           const uint16_t* __restrict__ A,
                                                           int64_t lda,
@@ -684,7 +691,7 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16w_kernel(int64_t M, int64_t N, 
                                                           int64_t K1, int64_t ldb,
                                                           float* __restrict__ C, int64_t ldc,
                                                           float* __restrict__ P, int64_t kps,
-                                                          int64_t nfull) {
+                                                          int64_t nfull, ActEpi epi) {
   constexpr int NA = W_BM * H_BK / 8 / H_NT;  // A chunks of 8 per thread (4)
   constexpr int NB = H_BK * W_BN / 8 / H_NT;  // B chunks of 8 per thread (4)
   struct Stage {
@@ -773,6 +780,14 @@ __global__ __launch_bounds__(H_NT) void gemm_bf16w_kernel(int64_t M, int64_t N, 
     compute(buf);
     __syncthreads();
     buf ^= 1;
+  }
+  if constexpr (EPI != 0) {
+    if (wk.whole) {
+      constexpr int ACT = (EPI - 1) & 1;
+      act_tile_epilogue<bf16, bf16, ACT, 8>(epi, M, N, bm, bn, wm, wn, acc,
+                                            reinterpret_cast<float*>(&As[0][0][0]));
+      return;
+    }
   }
   // output: wave rows wm + 16 i .., columns wn + 16 j ..
 #pragma unroll
@@ -945,23 +960,22 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
   if (act_done) *act_done = false;
   if (tc_done) *tc_done = false;
   if (M == 0 || N == 0) return hipSuccess;
-  GemmPlan pl = gemm_plan(M, N, K, b_dt);
+  // bf16 products with enough tiles and one source per k-tile take the wide
+  // kernel (the transposed-copy store stays on the narrow one)
+  const bool wide = wide_ok(M, N, b_dt) && (B2 == nullptr || K1 % H_BK == 0) && tc == nullptr;
+  const GemmPlan pl = gemm_plan(M, N, K, b_dt, wide);
+  const int64_t kps = pl.kps, nfull = pl.nfull;
+  const int nsp = pl.nsp;
   // the activation epilogue: whole tiles apply it as they store, a split
   // tail is reduced through it; a plain split-K product leaves its partials
   // (the caller's activation pass adds them) -- and gate/up/out take the
   // weights' dtype
-  const bool use_act = act != nullptr && (pl.nsp == 1 || pl.nfull > 0) &&
+  const bool use_act = act != nullptr && (nsp == 1 || nfull > 0) &&
                        act->gdt == b_dt && act->odt == b_dt && ldc == N && N % 8 == 0 &&
-                       128.0 * N * 4 < BUF_MAX_BYTES;
+                       (double)pl.bm * N * 4 < BUF_MAX_BYTES;
   // the transposed bf16 copy: every tile whole, bf16 operands
-  const bool use_tc = !use_act && tc != nullptr && tc_done != nullptr && pl.nsp == 1 &&
+  const bool use_tc = !use_act && tc != nullptr && tc_done != nullptr && nsp == 1 &&
                       b_dt == BF16 && a_dt == BF16 && M % 8 == 0 && tc->ld % 8 == 0;
-  // plain bf16 products of enough tiles (one source per k-tile) take the
-  // wide kernel, with its own work split
-  const bool wide = !use_act && !use_tc && wide_ok(M, N, b_dt) && (B2 == nullptr || K1 % H_BK == 0);
-  if (wide) pl = gemm_plan(M, N, K, b_dt, true);
-  const int64_t kps = pl.kps, nfull = pl.nfull;
-  const int nsp = pl.nsp;
   const int epi = use_act ? 1 + act->act + (b_dt == BF16 ? 6 : 0) : (use_tc ? 16 : 0);
   ActEpi ea = use_act ? *act : ActEpi{};
   if (use_tc) {
@@ -1015,9 +1029,14 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
     }
     const bool splitb = K1 % H_BK != 0;
     if (wide) {
-      gemm_bf16w_kernel<<<grid1, dim3(H_NT), 0, s>>>(M, N, K, (const uint16_t*)A, lda,
-                                                     (const uint16_t*)B1, (const uint16_t*)B2, K1,
-                                                     ldb, C, ldc, partials, kps, nfull);
+#define LBP_GEMM_W(E)                                                                         \
+  gemm_bf16w_kernel<E><<<grid1, dim3(H_NT), 0, s>>>(M, N, K, (const uint16_t*)A, lda,          \
+                                                    (const uint16_t*)B1, (const uint16_t*)B2, K1, \
+                                                    ldb, C, ldc, partials, kps, nfull, ea)
+      if (epi == 7) LBP_GEMM_W(7);
+      else if (epi == 8) LBP_GEMM_W(8);
+      else LBP_GEMM_W(0);
+#undef LBP_GEMM_W
     } else {
 #define LBP_GEMM_BF16(SB, E)                                                                \
   gemm_bf16_kernel<SB, E><<<grid1, dim3(H_NT), 0, s>>>(M, N, K, (const uint16_t*)A, lda,      \

@@ -82,6 +82,10 @@ def parse():
                     help="short eager run for a rocprofv3 --pmc pass: writes the step's kernel "
                          "records to RECORDS_JSON, runs 3 eager steps and a 256 MiB plain copy "
                          "(the counter calibration), prints nothing else")
+    ap.add_argument("--sq-summary", nargs=2, metavar=("RECORDS_JSON", "SQ_CSV"),
+                    help="per-kernel MFMA and LDS utilisation from one rocprofv3 --pmc pass of "
+                         "SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT "
+                         "GRBM_GUI_ACTIVE over --pmc-pass")
     ap.add_argument("--traffic-summary", nargs=3, metavar=("RECORDS_JSON", "FETCH_CSV", "WRITE_CSV"),
                     help="turn the two counter passes (FETCH_SIZE, WRITE_SIZE) into "
                          "profiles/traffic.json and print the table; no GPU needed")
@@ -439,6 +443,39 @@ def traffic_summary(records_json, fetch_csv, write_csv):
                                                    k["traffic_over_alg"]))
 
 
+def sq_summary(records_json, sq_csv, simds=1024, cus=256, xcds=8):
+    """MFMA busy and LDS busy as shares of each kernel's cycles, and the
+    bank-conflict share of the LDS cycles, averaged over the recorded call
+    and the eager steps.  GRBM_GUI_ACTIVE is summed over the XCDs (its max
+    is the kernel's cycle count), the SQ counters over every SIMD / CU."""
+    import csv
+    with open(records_json) as f:
+        rec = json.load(f)
+    per = rec["kernels_per_layer"]
+    rows = {}
+    for r in csv.DictReader(open(sq_csv)):
+        if "lbp::" not in r["Kernel_Name"]:
+            continue
+        d = rows.setdefault(int(r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    agg = {}
+    for j, d in enumerate(sorted(rows)):
+        for k, v in rows[d].items():
+            agg.setdefault(j % per, {}).setdefault(k, []).append(v)
+    print("| # | kernel | MFMA busy % | LDS busy % | bank-conflict share of LDS cycles |")
+    print("|---|---|---|---|---|")
+    for i in range(per):
+        a = {k: sum(v) / len(v) for k, v in agg.get(i, {}).items()}
+        cyc = a.get("GRBM_GUI_ACTIVE", 0.0) / xcds
+        if cyc <= 0:
+            continue
+        mf = 100.0 * a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cyc * simds)
+        lds = 100.0 * a.get("SQ_LDS_IDX_ACTIVE", 0.0) / (cyc * cus)
+        bc = a.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(a.get("SQ_LDS_IDX_ACTIVE", 0.0), 1.0)
+        name = rec["records"][i]["name"] if i < len(rec["records"]) else "?"
+        print("| %d | %s | %.1f | %.1f | %.2f |" % (i, name, mf, lds, bc))
+
+
 # ------------------------------------------------------------------ CPU baseline
 def blas_info():
     """(vendor and version, threads) of NumPy's BLAS."""
@@ -534,6 +571,9 @@ def cpu_baseline(cfg, budget_s):
 # ------------------------------------------------------------------ main
 def main():
     args = parse()
+    if args.sq_summary:
+        sq_summary(*args.sq_summary)
+        return 0
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
         return 0

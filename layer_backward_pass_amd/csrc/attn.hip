@@ -582,9 +582,33 @@ struct TrJob {
 
 // Kᵀ (bf16 source) and dCtxᵀ (fp32 source) in one launch: the first
 // a.gx * a.gy workgroups take job a, the rest job b.
+// Eight consecutive elements of a row as bf16 bit patterns (16-byte loads).
+__device__ __forceinline__ void ld8_bf16(const float* p, uint16_t (&o)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  const uint32_t w[4] = {pk_bf16(a.x, a.y), pk_bf16(a.z, a.w), pk_bf16(b.x, b.y), pk_bf16(b.z, b.w)};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    o[2 * j] = (uint16_t)(w[j] & 0xffffu);
+    o[2 * j + 1] = (uint16_t)(w[j] >> 16);
+  }
+}
+__device__ __forceinline__ void ld8_bf16(const bf16* p, uint16_t (&o)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    o[2 * j] = (uint16_t)(w[j] & 0xffffu);
+    o[2 * j + 1] = (uint16_t)(w[j] >> 16);
+  }
+}
+
+// Each thread reads eight consecutive columns of one row with 16-byte loads
+// (rows past the end give 0) and scatters them into the LDS tile
+// transposed; each thread then writes eight consecutive rows of one column.
 template <typename TA, typename TB>
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(TrJob a, TrJob b) {
-  __shared__ uint16_t tile[TR_C][TR_R + 2];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[TR_C][TR_R + 8];
   const int64_t na = (int64_t)a.gx * a.gy;
   const bool second = (int64_t)blockIdx.x >= na;
   const int64_t loc = second ? (int64_t)blockIdx.x - na : (int64_t)blockIdx.x;
@@ -593,23 +617,21 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(TrJob a, TrJob b) {
   uint16_t* __restrict__ dst = jb.dst;
   const int t = threadIdx.x;
   const int64_t r0 = (loc % jb.gx) * TR_R, c0 = (loc / jb.gx) * TR_C;
-  const int col = t & 31;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = (t >> 5) + 8 * i;
-    const int64_t r = r0 + row;
-    float v = 0.f;
-    if (r < rows)
-      v = second ? Act<TB>::ld((const TB*)jb.src, r * ld + c0 + col)
-                 : Act<TA>::ld((const TA*)jb.src, r * ld + c0 + col);
-    tile[col][row] = f2bf(v);
+  static_assert(TR_R * TR_C == 256 * 8, "one 8-column chunk per thread");
+  const int row = t >> 2, c8 = 8 * (t & 3);
+  uint16_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (r0 + row < rows) {
+    if (second)
+      ld8_bf16((const TB*)jb.src + (r0 + row) * ld + c0 + c8, v);
+    else
+      ld8_bf16((const TA*)jb.src + (r0 + row) * ld + c0 + c8, v);
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) tile[c8 + j][row] = v[j];
   __syncthreads();
   const int rc = t & 7, cc = t >> 3;
-  ushortx8 o;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) o[j] = tile[cc][8 * rc + j];
-  *reinterpret_cast<ushortx8*>(dst + (c0 + cc) * LR + r0 + 8 * rc) = o;
+  *reinterpret_cast<uint4*>(dst + (c0 + cc) * LR + r0 + 8 * rc) =
+      *reinterpret_cast<const uint4*>(&tile[cc][8 * rc]);
 }
 
 __device__ __forceinline__ ushortx8 pack8(const float (&x)[8]) {

@@ -331,6 +331,12 @@ def test_lora_adamw(rows, H, out, rank, step, dt):
     # row (a single key would make the softmax constant and dQ identically 0)
     ("seq512", {"seq": 1, "kv_len": 40, "pos0": 39, "hidden": 256, "ffn": 512, "n_heads": 4,
                 "n_kv_heads": 2, "head_dim": 64, "rank": 4, "alpha": 8.0, "input_grad": True}),
+    # bf16 products on the wide 256 x 256 kernel inside the layer (gate/up,
+    # W_down with its activation epilogue, the three transposed input-gradient
+    # products), ragged rows
+    ("seq512", {"seq": 520, "kv_len": 520, "hidden": 512, "ffn": 1024, "n_heads": 8,
+                "n_kv_heads": 2, "head_dim": 64, "rank": 8, "alpha": 16.0, "dtype": "bf16",
+                "input_grad": True}),
 ])
 def test_layer_small(name, over):
     cfg = synth.get_config(name).with_(**over)

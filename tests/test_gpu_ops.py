@@ -498,6 +498,8 @@ LM = synth.get_config("lmhead")
     ({"rows": 20, "hidden": 64, "vocab": 256}, {"labels": "none", "state": True}),
     # no rows at all
     ({"rows": 0, "hidden": 64, "vocab": 256}, {}),
+    # the smallest shapes the boundary takes: hidden 8, vocabulary 4
+    ({"rows": 3, "hidden": 8, "vocab": 4}, {"state": True}),
 ])
 def test_lm_head(over, kw):
     cfg = LM.with_(**over)

@@ -34,9 +34,10 @@ Workloads (default: stack36):
 
 Prints ONE JSON line.  `roofline` describes the kernel with the largest
 share of the step, timed with HIP events recorded on the library's stream
-right after each kernel (lorabwd_layer_backward_timed; the raw interval
-between consecutive events, so it includes one event record); its
-algorithmic bytes / flops come from the library.  `attn` sums the attention
+right after each kernel (lorabwd_*_timed; the raw interval between
+consecutive events, so it includes one event record) over steps run back
+to back after the timed region; its algorithmic bytes / flops come from
+the library.  `attn` sums the attention
 launches of a layer (dA, softmax backward, dQ, dV and their helper launches)
 against the three contractions on unmasked pairs.  `cpu_baseline` times the
 float64 oracle on the host on a bounded sample of the same workload.
@@ -203,45 +204,48 @@ def run_step(lbp, cfg, cp):
 
 
 # ------------------------------------------------------------------ roofline
-def kernel_profile(lbp, hip, cfg, copies, torch, reps):
-    """Per-kernel average duration (ms), from events recorded right after each
-    kernel by lorabwd_layer_backward_timed, over `reps` eager steps."""
-    cap = 128
+def kernel_profile(lbp, hip, cfg, copies, torch, nsteps):
+    """Per-kernel average duration (ms) in steady state, as in the timed
+    region: nsteps whole steps run back to back on the copies in rotation,
+    with an event recorded right after each kernel by the library's timed
+    entry points (lorabwd_*_timed) and one before each call.  A 2 GiB read
+    enqueued first keeps the GPU busy while the host enqueues the steps, so
+    consecutive events bracket kernels that ran back to back, not host
+    launch gaps; the first step after it (cold caches, idle clocks) is not
+    counted."""
+    cap = 32  # kernels of one call at most
     stream = torch.cuda.current_stream().cuda_stream
-    ev = hip.events(cap + 1)
-    recs = (lbp.KernelRecord * cap)()
-    stats = {}
-    # A read of 2 GiB enqueued ahead of each measured call keeps the GPU busy
-    # while the host enqueues the layer, so consecutive events bracket kernels
-    # that ran back to back (not host launch gaps).  It also evicts the
-    # Infinity Cache without leaving dirty lines behind (a write-filler would
-    # make the next kernel pay for its write-backs), so every kernel starts
-    # cold, as in the rotated timed loop.
+    seq = [(st, call) for st in range(nsteps)
+           for call in step_calls(lbp, cfg, copies[st % len(copies)])]
+    evs = [hip.events(cap + 1) for _ in seq]
+    recs = [(lbp.KernelRecord * cap)() for _ in seq]
     filler = torch.zeros(1 << 29, dtype=torch.float32, device="cuda:0")
     sink = torch.empty((), dtype=torch.float32, device="cuda:0")
     torch.cuda.synchronize()
-    for r in range(reps):
-        cp = copies[r % len(copies)]
-        for call in step_calls(lbp, cfg, cp):
-            torch.sum(filler, dim=(0,), out=sink)
-            hip.record(ev[cap], stream)
-            n = call(timing=(ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)), recs))
-            torch.cuda.synchronize()
-            prev = ev[cap]
-            for i in range(min(n, cap)):
-                ms = hip.elapsed_ms(prev, ev[i])
-                prev = ev[i]
-                key = (i, recs[i].name.decode())
-                s = stats.setdefault(key, {"ms": 0.0, "n": 0, "bytes": recs[i].alg_bytes,
-                                           "flops": recs[i].alg_flops,
-                                           "impl": recs[i].impl_bytes})
-                s["ms"] += ms
-                s["n"] += 1
+    torch.sum(filler, dim=(0,), out=sink)
+    counts = []
+    for (st, call), ev, rc in zip(seq, evs, recs):
+        hip.record(ev[cap], stream)
+        counts.append(call(timing=(ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)), rc)))
+    torch.cuda.synchronize()
+    stats = {}
+    for (st, _), ev, rc, n in zip(seq, evs, recs, counts):
+        if st == 0 and nsteps > 1:
+            continue
+        prev = ev[cap]
+        for i in range(min(n, cap)):
+            ms = hip.elapsed_ms(prev, ev[i])
+            prev = ev[i]
+            key = (i, rc[i].name.decode())
+            e = stats.setdefault(key, {"ms": 0.0, "n": 0, "bytes": rc[i].alg_bytes,
+                                       "flops": rc[i].alg_flops, "impl": rc[i].impl_bytes})
+            e["ms"] += ms
+            e["n"] += 1
     del filler, sink
     out = []
-    for (i, name), s in sorted(stats.items()):
-        out.append({"index": i, "name": name, "avg_ms": s["ms"] / s["n"], "alg_bytes": s["bytes"],
-                    "alg_flops": s["flops"], "impl_bytes": s["impl"]})
+    for (i, name), e in sorted(stats.items()):
+        out.append({"index": i, "name": name, "avg_ms": e["ms"] / e["n"], "alg_bytes": e["bytes"],
+                    "alg_flops": e["flops"], "impl_bytes": e["impl"]})
     return out
 
 
@@ -642,9 +646,11 @@ def main():
     tokens = cfg.seq * steps
     value = tokens / (ms / 1e3)
 
+    # steady-state steps for the per-kernel timings: about 40 ms of work, at
+    # least two steps (the first is not counted), at most 24 (the host
+    # enqueues them while the GPU reads the 2 GiB ahead of them)
     kernels = kernel_profile(lbp, hip, cfg, copies, torch,
-                             reps=max(3, min(20, steps // 10))
-                             if getattr(cfg, "n_layers", 1) == 1 else 1)
+                             nsteps=int(min(24, max(2, round(40.0 / ms_per_step)))))
     rl = roofline(cfg, kernels)
     attn = attention_summary(cfg, kernels)
     cpu = None

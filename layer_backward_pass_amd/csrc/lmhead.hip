@@ -8,10 +8,13 @@
 //   grad_hidden = dlogits W          (W before the update)  [rows, hidden]
 //   dW          = dlogits^T h, then AdamW on W              [vocab, hidden]
 // Kernels, in stream order:
-//   xent_bwd_kernel   one workgroup per row: row max and sum of exponentials
-//                     in one pass (rescaled as the max grows), then dlogits
-//                     and the row's loss term; HBM-bound (logits read twice,
-//                     dlogits written once)
+//   xent_bwd_kernel   a row at a time per workgroup (1024 threads, one
+//                     workgroup per CU, rows in turn): row max and sum of
+//                     exponentials in one pass (rescaled as the max grows),
+//                     then dlogits and the row's loss term; HBM-bound (the
+//                     second read of a row mostly comes from the Infinity
+//                     Cache: 256 rows in flight are 155 MB at vocabulary
+//                     151936)
 //   xent_loss_kernel  the row terms summed in a fixed order, divided by n
 //   grad_hidden       launch_gemm (fp32 MFMA, split-K over the vocabulary)
 //   dW + AdamW        launch_gemm_at_adamw: dlogits read transposed in place,
@@ -24,7 +27,9 @@ namespace lbp {
 
 namespace {
 
-constexpr int XT = 256;  // threads per row
+constexpr int XT = 256;   // threads of the loss reduction
+constexpr int XB = 1024;  // threads per row of xent_bwd_kernel
+constexpr int XB_WG = 256;  // its workgroups (rows beyond run in turn)
 
 // Merge of two (max, sum of exp(z - max)) pairs.
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
@@ -35,11 +40,12 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 }
 
 // Number of labels in [0, vocab) among labels[0, rows), by every thread of
-// the workgroup (the same value everywhere).
+// a workgroup of NT threads (the same value everywhere).
+template <int NT>
 __device__ int count_labelled(int64_t rows, int64_t vocab, const int32_t* __restrict__ labels,
                               int* red) {
   int c = 0;
-  for (int64_t i = threadIdx.x; i < rows; i += XT) {
+  for (int64_t i = threadIdx.x; i < rows; i += NT) {
     const int32_t l = labels[i];
     c += (l >= 0 && l < vocab) ? 1 : 0;
   }
@@ -48,81 +54,86 @@ __device__ int count_labelled(int64_t rows, int64_t vocab, const int32_t* __rest
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
   __syncthreads();
-  return red[0] + red[1] + red[2] + red[3];
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) n += red[i];
+  return n;
 }
 
 }  // namespace
 
-__global__ __launch_bounds__(XT) void xent_bwd_kernel(int64_t rows, int64_t vocab,
+__global__ __launch_bounds__(XB) void xent_bwd_kernel(int64_t rows, int64_t vocab,
                                                       const float* __restrict__ logits,
                                                       const int32_t* __restrict__ labels,
                                                       float* __restrict__ dlogits,
                                                       float* __restrict__ rowloss) {
-  __shared__ float rm[4], rs[4];
-  __shared__ int rc[4];
-  const int64_t row = blockIdx.x;
+  constexpr int NW = XB / 64;
+  __shared__ float rm[NW], rs[NW];
+  __shared__ int rc[NW];
   const int t = threadIdx.x;
-  const int n = count_labelled(rows, vocab, labels, rc);
-  const int32_t lab = labels[row];
-  const bool ok = lab >= 0 && lab < vocab;
-  const float4* z4 = reinterpret_cast<const float4*>(logits + row * vocab);
-  float4* d4 = reinterpret_cast<float4*>(dlogits + row * vocab);
+  const int n = count_labelled<XB>(rows, vocab, labels, rc);
   const int64_t q = vocab / 4;
-  // pass 1: running max and sum of exp(z - max), four float4 loads in flight
-  float m = -INFINITY, s = 0.f;
-  auto take = [&](const float4& z) {
-    const float zm = fmaxf(fmaxf(z.x, z.y), fmaxf(z.z, z.w));
-    const float nm = fmaxf(m, zm);
-    if (nm == -INFINITY) return;  // nothing finite yet
-    s = s * expf(m - nm) + (expf(z.x - nm) + expf(z.y - nm)) +
-        (expf(z.z - nm) + expf(z.w - nm));
-    m = nm;
-  };
-  int64_t i = t;
-  for (; i + 3 * XT < q; i += 4 * XT) {
-    const float4 a = z4[i], b = z4[i + XT], c = z4[i + 2 * XT], d = z4[i + 3 * XT];
-    take(a);
-    take(b);
-    take(c);
-    take(d);
-  }
-  for (; i < q; i += XT) take(z4[i]);
-  // the workgroup's pairs merged in a fixed pattern
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const int32_t lab = labels[row];
+    const bool ok = lab >= 0 && lab < vocab;
+    const float4* z4 = reinterpret_cast<const float4*>(logits + row * vocab);
+    float4* d4 = reinterpret_cast<float4*>(dlogits + row * vocab);
+    // pass 1: running max and sum of exp(z - max), four float4 loads in flight
+    float m = -INFINITY, s = 0.f;
+    auto take = [&](const float4& z) {
+      const float zm = fmaxf(fmaxf(z.x, z.y), fmaxf(z.z, z.w));
+      const float nm = fmaxf(m, zm);
+      if (nm == -INFINITY) return;  // nothing finite yet
+      s = s * expf(m - nm) + (expf(z.x - nm) + expf(z.y - nm)) +
+          (expf(z.z - nm) + expf(z.w - nm));
+      m = nm;
+    };
+    int64_t i = t;
+    for (; i + 3 * XB < q; i += 4 * XB) {
+      const float4 a = z4[i], b = z4[i + XB], c = z4[i + 2 * XB], d = z4[i + 3 * XB];
+      take(a);
+      take(b);
+      take(c);
+      take(d);
+    }
+    for (; i < q; i += XB) take(z4[i]);
+    // the workgroup's pairs merged in a fixed pattern
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
-    lse_merge(m, s, m2, s2);
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+      lse_merge(m, s, m2, s2);
+    }
+    __syncthreads();  // the previous row's merge has read rm, rs
+    if ((t & 63) == 0) {
+      rm[t >> 6] = m;
+      rs[t >> 6] = s;
+    }
+    __syncthreads();
+    m = rm[0];
+    s = rs[0];
+#pragma unroll
+    for (int wv = 1; wv < NW; ++wv) lse_merge(m, s, rm[wv], rs[wv]);
+    const float lse = m + logf(s);
+    // pass 2: dlogits = (exp(z - lse) - [v == label]) / n, zero for an ignored row
+    const float scale = ok ? 1.0f / (float)n : 0.f;
+    auto grad = [&](const float4& z, int64_t j) {
+      float4 g;
+      g.x = (expf(z.x - lse) - (4 * j == lab ? 1.f : 0.f)) * scale;
+      g.y = (expf(z.y - lse) - (4 * j + 1 == lab ? 1.f : 0.f)) * scale;
+      g.z = (expf(z.z - lse) - (4 * j + 2 == lab ? 1.f : 0.f)) * scale;
+      g.w = (expf(z.w - lse) - (4 * j + 3 == lab ? 1.f : 0.f)) * scale;
+      d4[j] = g;
+    };
+    for (i = t; i + 3 * XB < q; i += 4 * XB) {
+      const float4 a = z4[i], b = z4[i + XB], c = z4[i + 2 * XB], d = z4[i + 3 * XB];
+      grad(a, i);
+      grad(b, i + XB);
+      grad(c, i + 2 * XB);
+      grad(d, i + 3 * XB);
+    }
+    for (; i < q; i += XB) grad(z4[i], i);
+    if (t == 0) rowloss[row] = ok ? lse - logits[row * vocab + lab] : 0.f;
   }
-  if ((t & 63) == 0) {
-    rm[t >> 6] = m;
-    rs[t >> 6] = s;
-  }
-  __syncthreads();
-  m = rm[0];
-  s = rs[0];
-  lse_merge(m, s, rm[1], rs[1]);
-  lse_merge(m, s, rm[2], rs[2]);
-  lse_merge(m, s, rm[3], rs[3]);
-  const float lse = m + logf(s);
-  // pass 2: dlogits = (exp(z - lse) - [v == label]) / n, zero for an ignored row
-  const float scale = ok ? 1.0f / (float)n : 0.f;
-  auto grad = [&](const float4& z, int64_t j) {
-    float4 g;
-    g.x = (expf(z.x - lse) - (4 * j == lab ? 1.f : 0.f)) * scale;
-    g.y = (expf(z.y - lse) - (4 * j + 1 == lab ? 1.f : 0.f)) * scale;
-    g.z = (expf(z.z - lse) - (4 * j + 2 == lab ? 1.f : 0.f)) * scale;
-    g.w = (expf(z.w - lse) - (4 * j + 3 == lab ? 1.f : 0.f)) * scale;
-    d4[j] = g;
-  };
-  for (i = t; i + 3 * XT < q; i += 4 * XT) {
-    const float4 a = z4[i], b = z4[i + XT], c = z4[i + 2 * XT], d = z4[i + 3 * XT];
-    grad(a, i);
-    grad(b, i + XT);
-    grad(c, i + 2 * XT);
-    grad(d, i + 3 * XT);
-  }
-  for (; i < q; i += XT) grad(z4[i], i);
-  if (t == 0) rowloss[row] = ok ? lse - logits[row * vocab + lab] : 0.f;
 }
 
 // loss = (sum of the row terms in a fixed order) / n; 0 when no row is labelled.
@@ -133,7 +144,7 @@ __global__ __launch_bounds__(XT) void xent_loss_kernel(int64_t rows, int64_t voc
   __shared__ int rc[4];
   __shared__ float rf[4];
   const int t = threadIdx.x;
-  const int n = count_labelled(rows, vocab, labels, rc);
+  const int n = count_labelled<XT>(rows, vocab, labels, rc);
   float a = 0.f;
   for (int64_t i = t; i < rows; i += XT) a += rowloss[i];
 #pragma unroll
@@ -163,8 +174,9 @@ hipError_t launch_lm_head_bwd(int64_t rows, int64_t hidden, int64_t vocab, const
   hipError_t e;
   if (!dry_run()) {
     if (rows > 0) {
-      xent_bwd_kernel<<<dim3((unsigned)rows), dim3(XT), 0, s>>>(rows, vocab, logits, labels,
-                                                                dlogits, rowloss);
+      const int64_t wg = rows < XB_WG ? rows : XB_WG;
+      xent_bwd_kernel<<<dim3((unsigned)wg), dim3(XB), 0, s>>>(rows, vocab, logits, labels,
+                                                              dlogits, rowloss);
       // logits read twice, dlogits written once
       mark("xent_bwd", (double)rows * vocab * 8 + rows * 8.0, 0, s, (double)rows * vocab * 4);
     }

@@ -11,10 +11,10 @@
 //   xent_bwd_kernel   a row at a time per workgroup (1024 threads, one
 //                     workgroup per CU, rows in turn): row max and sum of
 //                     exponentials in one pass (rescaled as the max grows),
-//                     then dlogits and the row's loss term; HBM-bound (the
-//                     second read of a row mostly comes from the Infinity
-//                     Cache: 256 rows in flight are 155 MB at vocabulary
-//                     151936)
+//                     then dlogits and the row's loss term; bandwidth-bound
+//                     (logits read twice from the fabric, the two reads of a
+//                     row close together: 256 rows in flight, 155 MB at
+//                     vocabulary 151936)
 //   xent_loss_kernel  the row terms summed in a fixed order, divided by n
 //   grad_hidden       launch_gemm (fp32 MFMA, split-K over the vocabulary)
 //   dW + AdamW        launch_gemm_at_adamw: dlogits read transposed in place,

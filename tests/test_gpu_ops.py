@@ -219,7 +219,10 @@ def test_ffn(rows, dim, ffn, act, sub, dt):
 @pytest.mark.parametrize("rows,H,out,rank,step,dt", [
     (16, 64, 64, 4, 1, F32), (300, 256, 96, 16, 1, F32), (129, 64, 40, 7, 5, F32),
     (200, 128, 64, 16, 1, BF16), (0, 64, 32, 4, 2, F32), (77, 520, 37, 33, 1, F32),
-    (45, 64, 130, 64, 2, BF16), (1000, 264, 300, 16, 3, F32), (513, 2560, 1024, 24, 1, F32)])
+    (45, 64, 130, 64, 2, BF16), (1000, 264, 300, 16, 3, F32), (513, 2560, 1024, 24, 1, F32),
+    # a row slice whose g (80 rows x rank 64) exceeds the dA launch's LDS
+    # slice: the B update runs as a launch of its own
+    (600, 8192, 64, 64, 2, F32), (600, 8192, 48, 64, 1, BF16)])
 def test_lora_adamw(rows, H, out, rank, step, dt):
     print("lora", rows, H, out, rank, step, dt, flush=True)
     r = np.random.default_rng(12)

@@ -535,3 +535,43 @@ def test_lm_head_deterministic():
         outs.append((gh.cpu(), loss.cpu(), T["W"].cpu(), T["v"].cpu()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+def test_lm_head_graph_replay():
+    """The lm_head backward captured once in a HIP graph and replayed matches
+    eager calls bitwise, step after step (the AdamW state of each side
+    advances in lockstep), with eager work and synchronisation between the
+    replays; 300 rows so the cross-entropy workgroups take several rows."""
+    import layer_backward_pass_amd as lbp
+    cfg = LM.with_(rows=300, hidden=264, vocab=3000, ignore_every=7)
+    d = synth.draw_lm_head(cfg)
+    sides = []
+    for _ in range(2):
+        T = {k: torch.from_numpy(v).to(DEV) for k, v in d.items()}
+        T["gh"] = torch.empty((cfg.rows, cfg.hidden), device=DEV)
+        T["loss"] = torch.empty(1, device=DEV)
+        T["gw"] = torch.empty((cfg.vocab, cfg.hidden), device=DEV)
+        sides.append(T)
+
+    def call(T, step):
+        lbp.lorabwd_lm_head_backward(T["h"], T["logits"], T["labels"], T["W"], T["m"], T["v"],
+                                     T["gh"], T["loss"], lr=1e-3, step=step, grad_w=T["gw"])
+
+    # one eager call each first (sizes the workspace before the capture)
+    for T in sides:
+        call(T, 1)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(sides[1], 2)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for T in sides:
+            T["gh"].fill_(float("nan"))
+            T["gw"].fill_(float("nan"))
+        torch.cuda.synchronize()
+        call(sides[0], 2)
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in ("gh", "loss", "gw", "W", "m", "v"):
+            assert torch.equal(sides[0][k].cpu(), sides[1][k].cpu()), (rep, k)

@@ -972,7 +972,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
   // weights' dtype
   const bool use_act = act != nullptr && (nsp == 1 || nfull > 0) &&
                        act->gdt == b_dt && act->odt == b_dt && ldc == N && N % 8 == 0 &&
-                       (double)pl.bm * N * 4 < BUF_MAX_BYTES;
+                       (double)std::min<int64_t>(pl.bm, M) * N * 4 < BUF_MAX_BYTES;
   // the transposed bf16 copy: every tile whole, bf16 operands
   const bool use_tc = !use_act && tc != nullptr && tc_done != nullptr && nsp == 1 &&
                       b_dt == BF16 && a_dt == BF16 && M % 8 == 0 && tc->ld % 8 == 0;
@@ -984,14 +984,17 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void* A, int a_dt,
   }
   if (act_done) *act_done = use_act;
   if (tc_done) *tc_done = use_tc;
-  // buffer ranges: one tile's rows of A, one k-tile of B (an fp32 A of the
-  // bf16 path is first rounded into a dense [M][K] copy)
+  // buffer ranges: one tile's rows of A (no more than M), one k-tile of B
+  // (an fp32 A of the bf16 path is first rounded into a dense bf16 [M][K]
+  // copy)
   if (b_dt == F32) {
-    if (((double)(F_BM - 1) * lda + K) * 4 >= BUF_MAX_BYTES || 16.0 * ldb >= BUF_MAX_BYTES)
+    const double ar = (double)std::min<int64_t>(F_BM, M) - 1;
+    if ((ar * lda + K) * 4 >= BUF_MAX_BYTES || 16.0 * ldb >= BUF_MAX_BYTES)
       return hipErrorInvalidValue;
   } else {
     const double la = a_dt == F32 ? (double)K : (double)lda;
-    if (((double)(W_BM - 1) * la + K) * 4 >= BUF_MAX_BYTES || (double)H_BK * ldb * 2 >= BUF_MAX_BYTES)
+    const double ar = (double)std::min<int64_t>(W_BM, M) - 1;
+    if ((ar * la + K) * 2 >= BUF_MAX_BYTES || (double)H_BK * ldb * 2 >= BUF_MAX_BYTES)
       return hipErrorInvalidValue;
   }
   if (dry_run()) {
@@ -1102,7 +1105,7 @@ hipError_t launch_gemm_at_adamw(int64_t M, int64_t N, int64_t K, const float* At
   if (M == 0 || N == 0) return hipSuccess;
   // buffer ranges: four rows of A^T and of B, and one tile's rows of W, m, v
   if (N % 8 != 0 || lda < M || ldb < N || 16.0 * lda >= BUF_MAX_BYTES ||
-      16.0 * ldb >= BUF_MAX_BYTES || (double)F_BM * N * 4 >= BUF_MAX_BYTES)
+      16.0 * ldb >= BUF_MAX_BYTES || (double)std::min<int64_t>(F_BM, M) * N * 4 >= BUF_MAX_BYTES)
     return hipErrorInvalidValue;
   if (dry_run()) return hipSuccess;
   // every tile whole (the epilogue needs the finished dW tile)

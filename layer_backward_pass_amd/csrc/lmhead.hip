@@ -8,6 +8,7 @@
 //   grad_hidden = dlogits W          (W before the update)  [rows, hidden]
 //   dW          = dlogits^T h, then AdamW on W              [vocab, hidden]
 // Kernels, in stream order:
+//   xent_count_kernel n, the labelled rows (one workgroup)
 //   xent_bwd_kernel   a row at a time per workgroup (1024 threads, one
 //                     workgroup per CU, rows in turn): row max and sum of
 //                     exponentials in one pass (rescaled as the max grows),
@@ -27,7 +28,7 @@ namespace lbp {
 
 namespace {
 
-constexpr int XT = 256;   // threads of the loss reduction
+constexpr int XT = 256;   // threads of the label count and the loss reduction
 constexpr int XB = 1024;  // threads per row of xent_bwd_kernel
 constexpr int XB_WG = 256;  // its workgroups (rows beyond run in turn)
 
@@ -65,13 +66,13 @@ __device__ int count_labelled(int64_t rows, int64_t vocab, const int32_t* __rest
 __global__ __launch_bounds__(XB) void xent_bwd_kernel(int64_t rows, int64_t vocab,
                                                       const float* __restrict__ logits,
                                                       const int32_t* __restrict__ labels,
+                                                      const int* __restrict__ nlab,
                                                       float* __restrict__ dlogits,
                                                       float* __restrict__ rowloss) {
   constexpr int NW = XB / 64;
   __shared__ float rm[NW], rs[NW];
-  __shared__ int rc[NW];
   const int t = threadIdx.x;
-  const int n = count_labelled<XB>(rows, vocab, labels, rc);
+  const int n = *nlab;
   const int64_t q = vocab / 4;
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     const int32_t lab = labels[row];
@@ -136,15 +137,23 @@ __global__ __launch_bounds__(XB) void xent_bwd_kernel(int64_t rows, int64_t voca
   }
 }
 
+// n = the number of rows whose label is a vocabulary index, counted once.
+__global__ __launch_bounds__(XT) void xent_count_kernel(int64_t rows, int64_t vocab,
+                                                        const int32_t* __restrict__ labels,
+                                                        int* __restrict__ nlab) {
+  __shared__ int rc[XT / 64];
+  const int n = count_labelled<XT>(rows, vocab, labels, rc);
+  if (threadIdx.x == 0) *nlab = n;
+}
+
 // loss = (sum of the row terms in a fixed order) / n; 0 when no row is labelled.
-__global__ __launch_bounds__(XT) void xent_loss_kernel(int64_t rows, int64_t vocab,
-                                                       const int32_t* __restrict__ labels,
+__global__ __launch_bounds__(XT) void xent_loss_kernel(int64_t rows,
+                                                       const int* __restrict__ nlab,
                                                        const float* __restrict__ rowloss,
                                                        float* __restrict__ loss) {
-  __shared__ int rc[4];
   __shared__ float rf[4];
   const int t = threadIdx.x;
-  const int n = count_labelled<XT>(rows, vocab, labels, rc);
+  const int n = *nlab;
   float a = 0.f;
   for (int64_t i = t; i < rows; i += XT) a += rowloss[i];
 #pragma unroll
@@ -156,7 +165,7 @@ __global__ __launch_bounds__(XT) void xent_loss_kernel(int64_t rows, int64_t voc
 
 size_t lm_head_ws_bytes(int64_t rows, int64_t hidden, int64_t vocab) {
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
-  return up((size_t)rows * vocab * 4) + up((size_t)rows * 4) +
+  return up((size_t)rows * vocab * 4) + up((size_t)rows * 4) + 256 +
          up(gemm_partial_bytes(rows, hidden, vocab, F32, F32));
 }
 
@@ -170,18 +179,23 @@ hipError_t launch_lm_head_bwd(int64_t rows, int64_t hidden, int64_t vocab, const
   p += ((size_t)rows * vocab * 4 + 255) / 256 * 256;
   float* rowloss = (float*)p;
   p += ((size_t)rows * 4 + 255) / 256 * 256;
+  int* nlab = (int*)p;
+  p += 256;
   float* partials = (float*)p;
   hipError_t e;
   if (!dry_run()) {
+    xent_count_kernel<<<dim3(1), dim3(XT), 0, s>>>(rows, vocab, labels, nlab);
+    mark("xent_count", rows * 4.0, 0, s);
     if (rows > 0) {
       const int64_t wg = rows < XB_WG ? rows : XB_WG;
       xent_bwd_kernel<<<dim3((unsigned)wg), dim3(XB), 0, s>>>(rows, vocab, logits, labels,
-                                                              dlogits, rowloss);
-      // logits read twice, dlogits written once
-      mark("xent_bwd", (double)rows * vocab * 8 + rows * 8.0, 0, s, (double)rows * vocab * 4);
+                                                              nlab, dlogits, rowloss);
+      // logits read and dlogits written once; the second read of the
+      // logits, the labels read again and the row terms are the kernel's own
+      mark("xent_bwd", (double)rows * vocab * 8, 0, s, (double)rows * vocab * 4 + rows * 8.0);
     }
-    xent_loss_kernel<<<dim3(1), dim3(XT), 0, s>>>(rows, vocab, labels, rowloss, loss);
-    mark("xent_loss", rows * 8.0 + 4, 0, s);
+    xent_loss_kernel<<<dim3(1), dim3(XT), 0, s>>>(rows, nlab, rowloss, loss);
+    mark("xent_loss", 4, 0, s, rows * 4.0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // grad_hidden = dlogits W (W as the forward used it: before the update)
